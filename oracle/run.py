@@ -1,0 +1,191 @@
+"""Oracle iteration manager: blocks, refreshes and denoising steps of one request.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).
+
+Structure (dInfer abstract: model, diffusion iteration manager, decoding
+strategy, KV-cache manager; Sangam abstract: a masked response is denoised
+block by block, cached KV is refreshed and reused across the decodes in
+between; dInfer news article, section "削减计算成本：邻近KV缓存刷新": each
+iteration recomputes KV only for the current block and a small neighbourhood
+and leaves distant entries as they are):
+
+  for each block [bs, be) of the response, left to right:
+      full refresh: every position's K, V recomputed from hard embeddings
+      credit, tracked ids and smoothing state reset
+      while the block holds MASK:
+          window [max(0, bs-w), min(L, be+w)) runs through every layer with its
+          K, V scattered into the cache first; block rows -> final norm -> LM
+          head -> vocab stats -> credit -> commit -> smoothing state
+
+Requests are independent; a batch is a loop over requests.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .decode import (F32, vocab_stats, credit_update, select_commits, smoothing_state,
+                     soft_embedding)
+from .model import OracleModel
+
+
+class OracleRun:
+    """Decode state of one request driven step by step."""
+
+    def __init__(self, model: OracleModel, dcfg, tokens, prompt_len, gen_len, plant_id,
+                 plant_bias, router_bias=None):
+        self.model = model
+        self.m = model.m
+        self.d = dcfg
+        self.P = int(prompt_len)
+        self.G = int(gen_len)
+        self.L = self.P + self.G
+        self.tokens = np.array(tokens[: self.L], dtype=np.int64)
+        self.plant_id = np.array(plant_id[: self.L], dtype=np.int64)
+        self.plant_bias = float(plant_bias)
+        self.router_bias = None if router_bias is None else np.asarray(router_bias, dtype=np.float64)
+        self.B = dcfg.block_len
+        self.n_blocks = self.G // self.B
+        self.cache = model.new_cache(self.L)
+        self.block = -1
+        self.steps = []            # steps per finished block
+        self.records = []          # per-step details
+        self._k = dcfg.smooth_topk
+
+    # --- block bookkeeping ------------------------------------------------
+    @property
+    def bs(self):
+        return self.P + self.block * self.B
+
+    @property
+    def be(self):
+        return self.bs + self.B
+
+    def window(self):
+        w = self.d.vicinity_w
+        return max(0, self.bs - w), min(self.L, self.be + w)
+
+    def _router_bias_block(self):
+        if self.router_bias is None:
+            return None
+        return self.router_bias[:, self.block, :]
+
+    def block_masked(self):
+        return self.tokens[self.bs:self.be] == self.m.mask_id
+
+    def start_block(self, k):
+        """Full refresh at the block start, then reset the per-block decode state."""
+        self.block = k
+        pos = np.arange(self.L)
+        e = self.model.embed(self.tokens[pos])
+        self.model.forward_rows(self.cache, pos, e, self.L, self._router_bias_block())
+        B, kk = self.B, self._k
+        self.credit = np.zeros(B, dtype=F32)
+        self.tracked = np.full(B, -1, dtype=np.int64)
+        self.smooth_valid = np.zeros(B, dtype=bool)
+        self.smooth_ids = np.zeros((B, kk), dtype=np.int64)
+        self.smooth_p = np.zeros((B, kk), dtype=np.float64)
+        self.block_steps = 0
+
+    # --- one denoising step ------------------------------------------------
+    def window_embeddings(self, lo, hi):
+        """Hard embeddings, except soft ones for still-masked block rows with state."""
+        e = self.model.embed(self.tokens[lo:hi])
+        alpha = self.d.smooth_alpha
+        if alpha != 0.0:
+            masked = self.block_masked()
+            soft = np.nonzero(masked & self.smooth_valid)[0]
+            if len(soft):
+                e_mask = self.model.embed([self.m.mask_id])[0]
+                e_ids = self.model.embed(self.smooth_ids[soft].reshape(-1)).reshape(
+                    len(soft), self._k, -1)
+                e[soft + (self.bs - lo)] = soft_embedding(e_mask, e_ids, self.smooth_p[soft], alpha)
+        return e
+
+    def denoise_logits(self):
+        """Vicinity step over the current window; returns fp64 logits of the block rows."""
+        lo, hi = self.window()
+        pos = np.arange(lo, hi)
+        e = self.window_embeddings(lo, hi)
+        h = self.model.forward_rows(self.cache, pos, e, self.L, self._router_bias_block())
+        hb = h[self.bs - lo: self.be - lo]
+        return self.model.logits(hb)
+
+    def stats(self, logits):
+        return vocab_stats(logits, self.plant_id[self.bs:self.be], self.plant_bias,
+                           self.m.mask_id, self._k)
+
+    def commit(self, st):
+        """Credit update, selection, token writes and smoothing state for one step."""
+        d = self.d
+        masked = self.block_masked()
+        self.credit, self.tracked = credit_update(self.credit, self.tracked, st["argmax"],
+                                                  st["conf"], masked, d.credit_decay,
+                                                  d.credit_weight)
+        T, fallback = select_commits(masked, st["conf"], self.credit, d.tau, d.credit_kappa,
+                                     d.hierarchical)
+        self.tokens[self.bs + T] = st["argmax"][T]
+        still = self.block_masked()
+        ids, pt = smoothing_state(st["topk_id"], st["topk_p"])
+        self.smooth_ids = np.where(still[:, None], ids, self.smooth_ids)
+        self.smooth_p = np.where(still[:, None], pt, self.smooth_p)
+        self.smooth_valid = still.copy()
+        self.block_steps += 1
+        rec = {"block": self.block, "commits": T.copy(), "fallback": fallback,
+               "margin": decision_margin(st, masked, self.credit, d, T)}
+        self.records.append(rec)
+        return T, fallback
+
+    def step(self):
+        logits = self.denoise_logits()
+        st = self.stats(logits)
+        self.commit(st)
+        return logits, st
+
+    def run(self, max_steps_per_block=None):
+        cap = self.B if max_steps_per_block is None else max_steps_per_block
+        for k in range(self.n_blocks):
+            self.start_block(k)
+            while self.block_masked().any():
+                if self.block_steps >= cap:
+                    raise RuntimeError("block did not finish within its step cap")
+                self.step()
+            self.steps.append(self.block_steps)
+        return self.tokens
+
+
+def decision_margin(st, masked, credit, d, committed):
+    """Smallest relative distance of this step's decisions from flipping.
+
+    Reported, not gated.  Over the candidates: |conf - tau| / tau,
+    |credit - kappa| / kappa, the relative gap between the best and second-best
+    confidence (decides the fallback), and each committed row's top-1 minus
+    top-2 logit (decides the committed id).
+    """
+    from .decode import candidates
+    C = candidates(masked, d.hierarchical)
+    if len(C) == 0:
+        return np.inf
+    conf = st["conf"][C].astype(np.float64)
+    c = credit[C].astype(np.float64)
+    m = float(np.min(np.abs(conf - d.tau)) / d.tau)
+    if d.credit_weight != 0.0:
+        m = min(m, float(np.min(np.abs(c - d.credit_kappa)) / d.credit_kappa))
+    if len(C) > 1:
+        s = np.sort(conf)[::-1]
+        m = min(m, float((s[0] - s[1]) / s[0]))
+    tp = st["topk_p"][committed]
+    if tp.shape[1] > 1 and len(committed):
+        gap = np.log(tp[:, 0]) - np.log(tp[:, 1])
+        m = min(m, float(np.min(gap)))
+    return float(m)
+
+
+def run_request(mcfg, dcfg, weights, req, r=0, model=None):
+    """Run request r of a synth request batch to completion; returns the OracleRun."""
+    model = model or OracleModel(mcfg, weights)
+    rb = None if req.get("router_bias") is None else req["router_bias"][r].numpy()
+    run = OracleRun(model, dcfg, req["tokens"][r].numpy(), int(req["prompt_len"][r]),
+                    int(req["gen_len"][r]), req["plant_id"][r].numpy(),
+                    float(req["plant_bias"][r]), rb)
+    run.run()
+    return run
