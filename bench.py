@@ -1,0 +1,292 @@
+#!/usr/bin/env python3
+"""Benchmark: committed tokens/s of masked-diffusion decoding on one MI355X.
+
+Workload (default): the dense 8B-shaped dLLM in bf16 at batch 1 -- 32 layers,
+d 4096, 32 heads x 128, SwiGLU FFN 12288, vocab 126464, a prompt of 512
+random ids and 256 generated positions in blocks of 32, vicinity w 16,
+tau 0.9, credit on, smoothing alpha 0.3 over the top-8, planting +8 with
+probability 0.75.  Weights N(0, 0.02) drawn on the GPU; all inputs resident in
+HBM before the timed region.
+
+One bench step = one whole generation of the batch (every block: full KV
+refresh, then denoise+commit steps replayed from a HIP graph until the block
+is committed).  value = committed tokens / wall time over the timed steps.
+
+Also reported:
+  step_latency_ms: one denoise+commit step, event-timed over graph replays.
+  roofline: the dominant kernel (the skinny bf16 GEMM that runs the QKV and
+    gate|up projections of every layer), timed with HIP events on the stream it
+    is launched on, over rotating layers so every launch streams its weights
+    from HBM; algorithmic bytes = weights + input activations + fp32 output.
+  cpu_baseline: the CPU oracle on a bounded sample (one layer's refresh and
+    one layer's window step plus the LM head / vocab stats / commit of one
+    step), scaled to the run's layer, refresh and step counts.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+KERNEL = "gemm_skinny_kernel<bf16, MT=4, NT=2>"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_skinny_qkv_gateup_dense8b_traffic.json")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def source_hash() -> str:
+    p = os.path.join(ROOT, "diffusion_vicinity_kv_amd", "csrc", "gemm.hip")
+    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+
+
+def dominant_kernel_timing(wc, weights, iters=40, with_events=True):
+    """Average launch time and bytes of the QKV / gate|up projections at the
+    step's row count, alternating over rotating layers."""
+    import torch
+    from diffusion_vicinity_kv_amd import binding as B
+    m = wc.model
+    d, F = m.d_model, m.ffn_dim
+    rows = min(wc.max_len, wc.decode.block_len + 2 * wc.decode.vicinity_w) * wc.batch
+    A = (torch.randn(rows, d, device="cuda") * 0.5).to(torch.bfloat16)
+    lib = B.load()
+    out = torch.empty(max(lib.dinfer_linear_out_elems(rows, 3 * d, d, B.BF16),
+                          lib.dinfer_linear_out_elems(rows, 2 * F, d, B.BF16)), device="cuda")
+    layers = [L for L in weights["layers"] if L is not None]
+    shapes = []
+    for i in range(iters):
+        L = layers[i % len(layers)]
+        W = L["wqkv"] if i % 2 == 0 else L["w_gate_up"]
+        shapes.append(W)
+    for W in shapes[:4]:
+        B.linear(A, W, out)
+    torch.cuda.synchronize()
+    st = torch.cuda.current_stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in shapes]
+    nbytes = 0
+    for W, (e0, e1) in zip(shapes, evs):
+        N = W.shape[0]
+        e0.record(st)
+        B.linear(A, W, out)
+        e1.record(st)
+        nbytes += N * d * 2 + rows * d * 2 + rows * N * 4
+    torch.cuda.synchronize()
+    ms = [e0.elapsed_time(e1) for e0, e1 in evs]
+    avg_ms = sum(ms) / len(ms)
+    avg_bytes = nbytes / len(shapes)
+    return avg_ms, avg_bytes, rows
+
+
+def cpu_baseline(wc, gpu_refreshes_per_run, gpu_steps_per_run, committed_per_run):
+    """Oracle timed on a bounded sample of the workload, scaled to one run."""
+    import numpy as np
+    import oracle
+    import synth
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()
+                       if i.get("user_api") == "blas"] or [os.cpu_count()])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count()
+    m = wc.model
+    w = synth.make_weights(m, wc.seed, device="cpu", layers=[0])
+    req = synth.make_requests(wc)
+    om = oracle.OracleModel(m, w, layers=[0])
+    run = oracle.OracleRun(om, wc.decode, req["tokens"][0].numpy(), int(req["prompt_len"][0]),
+                           int(req["gen_len"][0]), req["plant_id"][0].numpy(),
+                           float(req["plant_bias"][0]))
+    t0 = time.perf_counter()
+    run.start_block(0)                           # one layer of the full refresh
+    t_ref_layer = time.perf_counter() - t0
+    lo, hi = run.window()
+    t0 = time.perf_counter()
+    e = run.window_embeddings(lo, hi)
+    h = om.forward_rows(run.cache, np.arange(lo, hi), e, run.L)
+    t_step_layer = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    logits = om.logits(h[run.bs - lo: run.be - lo])
+    st = run.stats(logits)
+    run.commit(st)
+    t_head = time.perf_counter() - t0
+    nl = m.n_layers
+    t_refresh = nl * t_ref_layer
+    t_step = nl * t_step_layer + t_head
+    t_run = gpu_refreshes_per_run * t_refresh + gpu_steps_per_run * t_step
+    sample_s = t_ref_layer + t_step_layer + t_head
+    return {"value": round(committed_per_run / t_run, 4), "unit": "tokens/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": (f"fp64 NumPy oracle: 1 of {nl} layers of the full refresh "
+                       f"({run.L} rows, {t_ref_layer:.2f} s), 1 layer of one window step "
+                       f"({hi - lo} rows, {t_step_layer:.2f} s), the LM head + vocab stats + "
+                       f"commit of one step ({t_head:.2f} s); scaled to {nl} layers, "
+                       f"{gpu_refreshes_per_run} refreshes and {gpu_steps_per_run} steps per run "
+                       f"({t_run:.1f} s projected; {sample_s:.1f} s measured)"),
+            "step_s": round(t_step, 3), "refresh_s": round(t_refresh, 3)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--workload", default="dense8b_b1")
+    ap.add_argument("--unroll", type=int, default=8)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--kernel-only", action="store_true",
+                    help="only the dominant-kernel timing loop (for counter runs)")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="one plain 1 GiB device copy (counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this library runs on one GPU; --gpus {args.gpus} is not supported "
+              "(the multi-GPU layout is described in the design notes, not built)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import synth
+    from diffusion_vicinity_kv_amd.engine import Engine
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    wc = synth.preset(args.workload)
+    m = wc.model
+
+    if args.calib_copy:
+        n = 1 << 28                                   # 1 GiB of fp32
+        src = torch.ones(n, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"calib copy: {n * 4} bytes read, {n * 4} bytes written")
+        return
+
+    log(f"[bench] drawing {m.n_layers}-layer weights on the GPU ({args.workload})")
+    w = synth.make_weights(m, wc.seed, device="cuda")
+    req = synth.make_requests(wc)
+    torch.cuda.synchronize()
+
+    if args.kernel_only:
+        avg_ms, avg_bytes, rows = dominant_kernel_timing(wc, w, iters=64)
+        log(f"[bench] kernel-only: {avg_ms * 1e3:.1f} us/launch, {avg_bytes / avg_ms / 1e6:.0f} GB/s")
+        return
+
+    max_len = req["tokens"].shape[1]
+    eng = Engine(m, wc.decode, w, wc.batch, max_len, graph_unroll=args.unroll)
+    tokens0 = req["tokens"].cuda().contiguous()
+    tokens = tokens0.clone()
+    plant_id = req["plant_id"].cuda().contiguous()
+    plant_bias = req["plant_bias"].cuda().contiguous()
+    P, G = req["prompt_len"].tolist(), req["gen_len"].tolist()
+
+    def one_run():
+        tokens.copy_(tokens0)
+        eng.set_batch(tokens, P, G, plant_id, plant_bias)
+        return eng.run_to_completion()
+
+    for i in range(args.warmup):
+        s = one_run()
+        log(f"[bench] warmup {i}: {s}")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    runs = []
+    for i in range(args.steps):
+        runs.append(one_run())
+        log(f"[bench] step {i}: {runs[-1]}")
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    committed = sum(r["committed"] for r in runs)
+    value = committed / elapsed
+
+    # denoise-step latency: graph replays of the first block, event-timed
+    tokens.copy_(tokens0)
+    eng.set_batch(tokens, P, G, plant_id, plant_bias)
+    eng.refresh_kv()
+    n_lat = max(args.unroll, (wc.decode.block_len // args.unroll) * args.unroll)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    st = torch.cuda.current_stream()
+    eng.step_graph(args.unroll)                     # graph captured, block warmed
+    tokens.copy_(tokens0)
+    eng.set_batch(tokens, P, G, plant_id, plant_bias)
+    eng.refresh_kv()
+    torch.cuda.synchronize()
+    e0.record(st)
+    eng.step_graph(n_lat)
+    e1.record(st)
+    torch.cuda.synchronize()
+    step_ms = e0.elapsed_time(e1) / n_lat
+
+    avg_ms, avg_bytes, rows = dominant_kernel_timing(wc, w)
+    achieved = avg_bytes / (avg_ms * 1e-3) / 1e9
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        t = json.load(open(TRAFFIC_FILE))
+        if t.get("source_hash") == source_hash():
+            traffic = t.get("bytes_per_launch")
+
+    steps_per_run = sum(r["steps"] for r in runs) / len(runs)
+    refreshes_per_run = sum(r["refreshes"] for r in runs) / len(runs)
+    committed_per_run = committed / len(runs)
+    # weights once + KV read once per layer + window KV write, per step
+    d, F, V, nl = m.d_model, m.ffn_dim, m.vocab, m.n_layers
+    weight_bytes = (nl * (3 * d * d + d * d + 3 * d * F) + V * d) * 2
+    kv_bytes = nl * wc.batch * 2 * (wc.max_len * d * 2 + rows // wc.batch * d * 2)
+    step_bytes = weight_bytes + kv_bytes
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline (bounded oracle sample)")
+        cpu = cpu_baseline(wc, int(round(refreshes_per_run)), int(round(steps_per_run)),
+                           committed_per_run)
+
+    out = {
+        "metric": "committed tokens/s (batch 1, dense 8B-shaped dLLM, bf16)",
+        "value": round(value, 3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(elapsed / args.steps * 1e3, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: N(0,0.02) random-init weights of the dense 8B shape, random prompt ids, "
+                "seeded planting",
+        "config": {"workload": args.workload, "batch": wc.batch, "prompt_len": wc.prompt_len[0],
+                   "gen_len": wc.gen_len, "block_len": wc.decode.block_len,
+                   "vicinity_w": wc.decode.vicinity_w, "layers": nl, "d_model": d,
+                   "vocab": V, "graph_unroll": args.unroll},
+        "step_latency_ms": round(step_ms, 4),
+        "steps_per_run": steps_per_run,
+        "refreshes_per_run": refreshes_per_run,
+        "refresh_ms_per_run": round(sum(r["refresh_ms"] for r in runs) / len(runs), 3),
+        "step_roofline": {"bound": "hbm", "bytes": step_bytes,
+                          "achieved": round(step_bytes / (step_ms * 1e-3) / 1e9, 1),
+                          "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                          "frac": round(step_bytes / (step_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+        "roofline": {"bound": "hbm", "kernel": KERNEL, "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "avg_launch_us": round(avg_ms * 1e3, 2),
+                     "bytes_per_launch": int(avg_bytes)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,141 @@
+// Parallel-decode commit of one step (dInfer news article, section
+// "解码的艺术"; classic top-1 decoding from the section on the three
+// bottlenecks): one wave64 per request, lane j = block offset j.
+//
+//   credit  : every still-masked position, c <- (argmax == tracked ? gamma*c : 0)
+//             + lambda*p with one fp32 rounding per operation, tracked <- argmax
+//   candidates: all masked positions, or with the hierarchical order the
+//             midpoints lo + (hi-lo-1)/2 of the maximal masked runs [lo, hi)
+//             of the block (found from the wave's ballot of masked lanes)
+//   gate    : commit every candidate with p >= tau or c >= kappa; if none
+//             passes, the candidate of highest p (lowest offset on ties)
+//   smoothing: each position still masked afterwards keeps its top-8 ids with
+//             probabilities renormalised to sum 1 for the next step's soft
+//             embedding
+//   block_done: set when no MASK remains in the block
+#include "common.h"
+#include "kernels.h"
+
+namespace dinfer {
+
+namespace {
+
+__global__ __launch_bounds__(64) void commit_kernel(CommitArgs a) {
+  const int r = blockIdx.x;
+  const int j = threadIdx.x;
+  const int B = a.B;
+  const int row = r * B + j;
+  const bool inb = j < B;
+  if (!a.req_active[r] || a.block_done[r]) {
+    if (inb) a.commit_mask[row] = 0;
+    return;
+  }
+  const int bs = a.req_bs[r];
+  int* tok = a.tokens + (size_t)r * a.max_len + bs;
+  const bool masked = inb && tok[j] == a.mask_id;
+  const int am = inb ? a.argmax[row] : 0;
+  const float p = inb ? a.conf[row] : 0.f;
+  float c = inb ? a.credit[row] : 0.f;
+  if (masked) {
+    const float keep = (am == a.tracked[row]) ? __fmul_rn(a.gamma, c) : 0.f;
+    c = __fadd_rn(keep, __fmul_rn(a.lambda, p));
+    a.credit[row] = c;
+    a.tracked[row] = am;
+  }
+
+  const unsigned long long mb = __ballot(masked);
+  bool cand = masked;
+  if (a.hierarchical && masked) {
+    // run containing j: lo = one past the highest unmasked offset below j,
+    // hi = the lowest unmasked offset above j (offsets >= B count as unmasked)
+    const unsigned long long below = (~mb) & ((1ull << j) - 1ull);
+    const int lo = below ? 64 - __clzll(below) : 0;
+    const unsigned long long above = (j == 63) ? 0ull : ((~mb) & ~((2ull << j) - 1ull));
+    int hi = above ? __ffsll((long long)above) - 1 : 64;
+    if (hi > B) hi = B;
+    cand = (j == lo + (hi - lo - 1) / 2);
+  }
+  const bool pass = cand && (p >= a.tau || c >= a.kappa);
+  const unsigned long long pb = __ballot(pass);
+  bool commit = pass;
+  if (pb == 0ull) {
+    // fallback: highest p among candidates, lowest offset on ties
+    float bv = cand ? p : -1.f;
+    int bj = cand ? j : 64;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const float ov = __shfl_xor(bv, o, 64);
+      const int oj = __shfl_xor(bj, o, 64);
+      if (ov > bv || (ov == bv && oj < bj)) {
+        bv = ov;
+        bj = oj;
+      }
+    }
+    commit = cand && j == bj;
+  }
+  if (commit) tok[j] = am;
+  if (inb) a.commit_mask[row] = commit ? 1 : 0;
+  const bool still = masked && !commit;
+  if (inb) {
+    if (still) {
+      const float* tp = a.topk_p + (size_t)row * 8;
+      const int* ti = a.topk_id + (size_t)row * 8;
+      float s = 0.f;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) s += tp[k];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        a.smooth_id[(size_t)row * 8 + k] = ti[k];
+        a.smooth_p[(size_t)row * 8 + k] = tp[k] / s;
+      }
+    }
+    a.smooth_valid[row] = still ? 1 : 0;
+  }
+  const unsigned long long sb = __ballot(still);
+  const unsigned long long cb = __ballot(commit);
+  if (j == 0) {
+    a.step_count[r] += 1;
+    a.commit_count[r] += __popcll(cb);
+    if (sb == 0ull) a.block_done[r] = 1;
+  }
+}
+
+// Block start for the selected requests: clear credit, tracked ids,
+// smoothing state and the done flag.
+__global__ __launch_bounds__(64) void block_reset_kernel(int B, const int* __restrict__ req_mask,
+                                                         float* credit, int* tracked,
+                                                         uint8_t* smooth_valid,
+                                                         uint8_t* commit_mask, int* block_done,
+                                                         int* step_count) {
+  const int r = blockIdx.x;
+  const int j = threadIdx.x;
+  if (!req_mask[r]) return;
+  if (j < B) {
+    credit[r * B + j] = 0.f;
+    tracked[r * B + j] = -1;
+    smooth_valid[r * B + j] = 0;
+    commit_mask[r * B + j] = 0;
+  }
+  if (j == 0) {
+    block_done[r] = 0;
+    step_count[r] = 0;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_commit(const CommitArgs& a, hipStream_t st) {
+  if (a.B > 64) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(commit_kernel, dim3(a.batch), dim3(64), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_block_reset(int batch, int B, const int* req_mask, float* credit, int* tracked,
+                              uint8_t* smooth_valid, uint8_t* commit_mask, int* block_done,
+                              int* step_count, hipStream_t st) {
+  hipLaunchKernelGGL(block_reset_kernel, dim3(batch), dim3(64), 0, st, B, req_mask, credit,
+                     tracked, smooth_valid, commit_mask, block_done, step_count);
+  return hipGetLastError();
+}
+
+}  // namespace dinfer

@@ -1,0 +1,129 @@
+// Device-side building blocks shared by the gfx950 kernels: element types,
+// 16-byte vector loads, MFMA wrappers with one operand layout for fp32 and
+// bf16, and wave64 reductions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef __bf16 bf16;
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float floatx4;
+
+// 16 bytes seen as 8 bf16, 4 floats or 4 dwords.
+union V16 {
+  uint4 u;
+  bf16x8 b;
+  floatx4 f;
+};
+
+__device__ __forceinline__ V16 ld16(const void* p) {
+  V16 v;
+  v.u = *reinterpret_cast<const uint4*>(p);
+  return v;
+}
+__device__ __forceinline__ void st16(void* p, const V16& v) { *reinterpret_cast<uint4*>(p) = v.u; }
+__device__ __forceinline__ V16 zero16() {
+  V16 v;
+  v.u = make_uint4(0, 0, 0, 0);
+  return v;
+}
+
+__device__ __forceinline__ float to_f(float x) { return x; }
+__device__ __forceinline__ float to_f(bf16 x) { return static_cast<float>(x); }
+template <typename T> __device__ __forceinline__ T from_f(float x);
+template <> __device__ __forceinline__ float from_f<float>(float x) { return x; }
+template <> __device__ __forceinline__ bf16 from_f<bf16>(float x) { return static_cast<bf16>(x); }
+
+// Element i of a 16-byte vector of T.
+template <typename T> __device__ __forceinline__ float v16_get(const V16& v, int i);
+template <> __device__ __forceinline__ float v16_get<float>(const V16& v, int i) { return v.f[i]; }
+template <> __device__ __forceinline__ float v16_get<bf16>(const V16& v, int i) {
+  return static_cast<float>(v.b[i]);
+}
+
+// ---------------------------------------------------------------------------
+// MFMA 16x16 tiles with fp32 accumulation.
+//
+// Operand layout used everywhere: with lane = 16*g + c (g = lane/16, c = lane%16)
+// each lane supplies one 16-byte vector of A row c and one of B column c, at
+// K offset g*VEC inside a "vector step" of KSTEP = 4*VEC elements.  For bf16
+// (VEC 8) that is exactly one v_mfma_f32_16x16x32_bf16.  For fp32 (VEC 4) it
+// is four v_mfma_f32_16x16x4_f32, the i-th consuming element i of both
+// vectors: the K index is permuted identically on both operands, which leaves
+// the dot product unchanged.  The 16x16 result lives as acc[i] =
+// C[row 4*g + i][col c].
+// ---------------------------------------------------------------------------
+template <typename T> struct Mfma;
+
+template <> struct Mfma<bf16> {
+  static constexpr int VEC = 8;
+  static constexpr int KSTEP = 32;
+  __device__ __forceinline__ static void mac(floatx4& acc, const V16& a, const V16& b) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.b, b.b, acc, 0, 0, 0);
+  }
+};
+
+template <> struct Mfma<float> {
+  static constexpr int VEC = 4;
+  static constexpr int KSTEP = 16;
+  __device__ __forceinline__ static void mac(floatx4& acc, const V16& a, const V16& b) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.f[0], b.f[0], acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.f[1], b.f[1], acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.f[2], b.f[2], acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.f[3], b.f[3], acc, 0, 0, 0);
+  }
+};
+
+// Four-element K step used by attention's P*V product: a[4], b[4] hold A row c
+// at K = 4*g .. 4*g+3 and B column c at the same K.
+template <typename T> struct Mfma4;
+template <> struct Mfma4<bf16> {
+  __device__ __forceinline__ static void mac(floatx4& acc, const float* a, const float* b) {
+    bf16x4 av, bv;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      av[i] = static_cast<bf16>(a[i]);
+      bv[i] = static_cast<bf16>(b[i]);
+    }
+    acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, bv, acc, 0, 0, 0);
+  }
+};
+template <> struct Mfma4<float> {
+  __device__ __forceinline__ static void mac(floatx4& acc, const float* a, const float* b) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i], b[i], acc, 0, 0, 0);
+  }
+};
+
+// ---------------------------------------------------------------------------
+// wave64 / block reductions
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+// Sum over a block of NW waves; `red` is __shared__ float[NW].  Every thread
+// gets the total.
+template <int NW>
+__device__ __forceinline__ float block_sum(float v, float* red) {
+  v = wave_sum(v);
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __syncthreads();
+  float t = 0.f;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) t += red[i];
+  __syncthreads();
+  return t;
+}
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }

@@ -1,0 +1,111 @@
+// Host-side launchers of the gfx950 kernels (one declaration per kernel
+// family).  Every launcher enqueues on `st` and returns the launch status.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace dinfer {
+
+enum class DType : int { F32 = 0, BF16 = 1 };
+
+inline size_t dtype_size(DType t) { return t == DType::F32 ? 4 : 2; }
+
+// Row table of one pass (a vicinity step or a full refresh).  Rows of request
+// r occupy [req_row_off[r], req_row_off[r] + req_nrows[r]) and hold the
+// consecutive positions starting at row_pos[req_row_off[r]].
+struct PassTable {
+  const int* nrows;        // [1]   rows in the pass (<= the pass's row capacity)
+  const int* row_req;      // [rows] request of each row
+  const int* row_pos;      // [rows] position of each row in its request
+  const int* req_row_off;  // [batch]
+  const int* req_nrows;    // [batch] 0 = request not in this pass
+  const int* req_len;      // [batch] L_r: keys each row attends over
+  const int* req_bs;       // [batch] current block start position
+  const int* req_active;   // [batch] request takes part in denoise/commit
+};
+
+// ---- GEMM: out[s][m][n] = sum over K-slice s of A[m][k] * W[n][k] ---------
+struct GemmPlan {
+  int kind;      // 0 = skinny (rows <= 128), 1 = fat
+  int mt, nt;    // skinny: 16-row tiles and 64-column groups per workgroup
+  int splits;    // K splits (skinny only; fat = 1)
+  int grid;
+};
+GemmPlan plan_gemm(DType t, int m_cap, int N, int K, int target_wgs);
+hipError_t launch_gemm(const GemmPlan& p, DType t, const void* A, const void* W, float* out,
+                       const int* m_dev, int m_cap, int N, int K, hipStream_t st);
+bool gemm_shape_ok(DType t, int N, int K);
+
+// ---- row-wise kernels ------------------------------------------------------
+hipError_t launch_embed(DType t, PassTable tb, int m_cap, const int* tokens, int max_len,
+                        const void* emb, int d, int V, int mask_id, float alpha, const int* smooth_id,
+                        const float* smooth_p, const uint8_t* smooth_valid, int B, float* x,
+                        hipStream_t st);
+// x[m] += sum_s P[s][m]; a[m] = rmsnorm(x[m]) * g   (S = 0: no partials)
+hipError_t launch_add_rmsnorm(DType t, const int* nrows, int m_cap, float* x, const float* P,
+                              int S, size_t p_stride, const void* g, float eps, void* a, int d,
+                              hipStream_t st);
+hipError_t launch_qkv_rope_scatter(DType t, PassTable tb, int m_cap, const float* P, int S,
+                                   size_t p_stride, int d, int H, int hd, const float* rope_cs,
+                                   void* q_out, void* kc, void* vc, int max_len, hipStream_t st);
+hipError_t launch_swiglu(DType t, const int* nrows, int m_cap, const float* P, int S,
+                         size_t p_stride, int F, void* act, hipStream_t st);
+// block rows of the window -> x + sum_s P[s] -> rmsnorm * g -> out[r*B + j];
+// also gathers each block row's planting (row_plant_id / row_plant_bias).
+hipError_t launch_final_norm(DType t, PassTable tb, int batch, int B, const float* x,
+                             const float* P, int S, size_t p_stride, const void* g, float eps,
+                             void* out, int d, const int* plant_id, const float* plant_bias,
+                             int max_len, int* row_plant_id, float* row_plant_bias,
+                             hipStream_t st);
+
+// ---- attention ---------------------------------------------------------------
+struct AttnPlan {
+  int q_tiles, n_split, keys_per_split;
+};
+AttnPlan plan_attention(int batch, int max_rows_per_req, int max_keys, int H, int target_wgs);
+hipError_t launch_attention(DType t, const AttnPlan& p, PassTable tb, int batch, int m_cap,
+                            const void* q, const void* kc, const void* vc, int H, int hd,
+                            int max_len, float* o_part, float* ml_part, void* o,
+                            hipStream_t st);
+
+// ---- vocab statistics ---------------------------------------------------------
+struct VocabPlan {
+  int n_split, chunk;
+};
+VocabPlan plan_vocab(int rows, int V, int target_wgs);
+size_t vocab_scratch_bytes(const VocabPlan& p, int rows);
+// plant_id [rows] (-1 none) and plant_bias [rows] may be null.
+hipError_t launch_vocab_stats(const VocabPlan& p, const float* logits, int rows, int V,
+                              const int* plant_id, const float* plant_bias, int mask_id,
+                              void* scratch, int* argmax, float* conf, float* lse, int* topk_id,
+                              float* topk_p, hipStream_t st);
+
+// ---- decode state ---------------------------------------------------------------
+struct CommitArgs {
+  int batch, B, max_len, mask_id, hierarchical;
+  float tau, kappa, gamma, lambda;
+  const int* req_bs;
+  const int* req_active;
+  int* tokens;
+  const int* argmax;
+  const float* conf;
+  const int* topk_id;
+  const float* topk_p;
+  float* credit;
+  int* tracked;
+  int* smooth_id;
+  float* smooth_p;
+  uint8_t* smooth_valid;
+  uint8_t* commit_mask;
+  int* block_done;
+  int* step_count;
+  int* commit_count;
+};
+hipError_t launch_commit(const CommitArgs& a, hipStream_t st);
+hipError_t launch_block_reset(int batch, int B, const int* req_mask, float* credit, int* tracked,
+                              uint8_t* smooth_valid, uint8_t* commit_mask, int* block_done,
+                              int* step_count, hipStream_t st);
+
+}  // namespace dinfer

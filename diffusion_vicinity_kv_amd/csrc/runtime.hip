@@ -1,0 +1,840 @@
+// Host runtime behind the C ABI of include/dinfer.h: configuration checks,
+// workspace carve-up, per-pass row tables, the launch sequence of a refresh
+// and of a denoising step, block bookkeeping, and HIP-graph replay of several
+// steps per host wait (dInfer news article, section "系统级压榨": loop
+// unrolling removes the bubbles between iterations; dLLM-serving
+// characterisation, "GPU vs. CPU overhead": CPU dispatch dominates a
+// single request's wall time).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <chrono>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/dinfer.h"
+#include "kernels.h"
+
+using namespace dinfer;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+dinfer_status fail(dinfer_status s, const std::string& msg) {
+  g_last_error = msg;
+  return s;
+}
+
+#define HIP_TRY(expr)                                                                   \
+  do {                                                                                  \
+    hipError_t e_ = (expr);                                                             \
+    if (e_ != hipSuccess)                                                               \
+      return fail(DINFER_E_HIP, std::string(#expr) + ": " + hipGetErrorString(e_));     \
+  } while (0)
+
+constexpr size_t kAlign = 256;
+inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// Row capacities and buffer sizes derived from the configuration.
+struct Layout {
+  int d, H, hd, F, V, nl, B, w;
+  int max_batch, max_len;
+  int m_step, m_ref, m_all;     // row capacities: step pass, refresh pass, either
+  int lm_rows;                  // max_batch * B
+  DType dt;
+  GemmPlan g_qkv_s, g_o_s, g_gu_s, g_d_s, g_lm;   // step pass
+  GemmPlan g_qkv_r, g_o_r, g_gu_r, g_d_r;         // refresh pass
+  AttnPlan a_step, a_ref;
+  VocabPlan vp;
+  size_t part_elems, attn_o_elems, attn_ml_elems;
+  // byte offsets
+  size_t off_rope, off_kvk, off_kvv, off_x, off_a, off_q, off_o, off_act, off_part, off_ao,
+      off_aml, off_hf, off_logits, off_rpid, off_rpb, off_vscr, off_argmax, off_conf, off_lse,
+      off_tid, off_tp, off_credit, off_tracked, off_sid, off_sp, off_sv, off_cm, off_done,
+      off_steps, off_ccount, off_tab_step, off_tab_ref, off_mask, off_misc, total;
+  size_t kv_layer_elems;        // elements of one layer's K (or V) cache
+  int tab_ints_step, tab_ints_ref;
+};
+
+int table_ints(int m_cap, int mb) { return 16 + 2 * m_cap + 6 * mb; }
+
+bool make_layout(const dinfer_model_cfg* m, const dinfer_decode_cfg* dc, int max_batch,
+                 int max_len, Layout* L, std::string* why) {
+  auto bad = [&](const char* s) {
+    if (why) *why = s;
+    return false;
+  };
+  if (!m || !dc) return bad("null config");
+  if (m->dtype != DINFER_F32 && m->dtype != DINFER_BF16) return bad("dtype must be F32 or BF16");
+  if (m->n_layers < 1 || m->d_model < 1 || m->n_heads < 1 || m->head_dim < 1 || m->vocab < 2)
+    return bad("model dimensions must be positive");
+  if (m->n_heads * m->head_dim != m->d_model) return bad("n_heads * head_dim must equal d_model");
+  if (m->head_dim != 64 && m->head_dim != 128) return bad("head_dim must be 64 or 128");
+  if (m->mask_id < 0 || m->mask_id >= m->vocab) return bad("mask_id out of range");
+  if (m->n_experts != 0) return bad("MoE layers are not supported by this build");
+  if (m->ffn_dim < 1) return bad("ffn_dim must be positive");
+  if (m->d_model > 8192) return bad("d_model above 8192");
+  if (m->vocab % 4 != 0) return bad("vocab must be a multiple of 4");
+  if (dc->block_len < 1 || dc->block_len > 64) return bad("block_len must be in 1..64");
+  if (dc->vicinity_w < 0) return bad("vicinity_w must be >= 0");
+  if (dc->smooth_topk != 8) return bad("smooth_topk must be 8");
+  if (dc->graph_unroll < 0 || dc->graph_unroll > 64) return bad("graph_unroll must be in 0..64");
+  if (max_batch < 1 || max_len < 1) return bad("max_batch and max_len must be positive");
+  const DType dt = m->dtype == DINFER_F32 ? DType::F32 : DType::BF16;
+  const int d = m->d_model, F = m->ffn_dim, V = m->vocab;
+  if (!gemm_shape_ok(dt, 3 * d, d) || !gemm_shape_ok(dt, d, d) || !gemm_shape_ok(dt, 2 * F, d) ||
+      !gemm_shape_ok(dt, d, F) || !gemm_shape_ok(dt, V, d))
+    return bad("GEMM shapes must have N % 128 == 0 and K % 256 (bf16) / 128 (f32) == 0");
+
+  Layout& l = *L;
+  l.dt = dt;
+  l.d = d;
+  l.H = m->n_heads;
+  l.hd = m->head_dim;
+  l.F = F;
+  l.V = V;
+  l.nl = m->n_layers;
+  l.B = dc->block_len;
+  l.w = dc->vicinity_w;
+  l.max_batch = max_batch;
+  l.max_len = max_len;
+  const int win = std::min(max_len, l.B + 2 * l.w);
+  l.m_step = max_batch * win;
+  l.m_ref = max_batch * max_len;
+  l.m_all = std::max(l.m_step, l.m_ref);
+  l.lm_rows = max_batch * l.B;
+  const int tw = 512;
+  l.g_qkv_s = plan_gemm(dt, l.m_step, 3 * d, d, tw);
+  l.g_o_s = plan_gemm(dt, l.m_step, d, d, tw);
+  l.g_gu_s = plan_gemm(dt, l.m_step, 2 * F, d, tw);
+  l.g_d_s = plan_gemm(dt, l.m_step, d, F, tw);
+  l.g_lm = plan_gemm(dt, l.lm_rows, V, d, tw);
+  if (l.g_lm.kind == 0 && l.g_lm.splits != 1) l.g_lm.splits = 1, l.g_lm.grid = V / (64 * l.g_lm.nt);
+  l.g_qkv_r = plan_gemm(dt, l.m_ref, 3 * d, d, tw);
+  l.g_o_r = plan_gemm(dt, l.m_ref, d, d, tw);
+  l.g_gu_r = plan_gemm(dt, l.m_ref, 2 * F, d, tw);
+  l.g_d_r = plan_gemm(dt, l.m_ref, d, F, tw);
+  auto pe = [](const GemmPlan& g, int m_cap, int N) { return (size_t)g.splits * m_cap * N; };
+  l.part_elems = std::max({pe(l.g_qkv_s, l.m_step, 3 * d), pe(l.g_o_s, l.m_step, d),
+                           pe(l.g_gu_s, l.m_step, 2 * F), pe(l.g_d_s, l.m_step, d),
+                           pe(l.g_qkv_r, l.m_ref, 3 * d), pe(l.g_o_r, l.m_ref, d),
+                           pe(l.g_gu_r, l.m_ref, 2 * F), pe(l.g_d_r, l.m_ref, d)});
+  l.a_step = plan_attention(max_batch, win, max_len, l.H, 512);
+  l.a_ref = plan_attention(max_batch, max_len, max_len, l.H, 512);
+  l.attn_o_elems = std::max((size_t)l.a_step.n_split * l.m_step, (size_t)l.a_ref.n_split * l.m_ref) *
+                   l.H * l.hd;
+  l.attn_ml_elems = l.attn_o_elems / l.hd * 2;
+  l.vp = plan_vocab(l.lm_rows, V, 1024);
+  l.tab_ints_step = table_ints(l.m_step, max_batch);
+  l.tab_ints_ref = table_ints(l.m_ref, max_batch);
+  l.kv_layer_elems = (size_t)max_batch * l.H * max_len * l.hd;
+
+  const size_t es = dtype_size(dt);
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = o;
+    o = align_up(o + bytes);
+    return at;
+  };
+  l.off_rope = take((size_t)max_len * l.hd * 4);
+  l.off_kvk = take(l.kv_layer_elems * l.nl * es);
+  l.off_kvv = take(l.kv_layer_elems * l.nl * es);
+  l.off_x = take((size_t)l.m_all * d * 4);
+  l.off_a = take((size_t)l.m_all * d * es);
+  l.off_q = take((size_t)l.m_all * d * es);
+  l.off_o = take((size_t)l.m_all * d * es);
+  l.off_act = take((size_t)l.m_all * F * es);
+  l.off_part = take(l.part_elems * 4);
+  l.off_ao = take(l.attn_o_elems * 4);
+  l.off_aml = take(l.attn_ml_elems * 4);
+  l.off_hf = take((size_t)l.lm_rows * d * es);
+  l.off_logits = take((size_t)l.lm_rows * V * 4);
+  l.off_rpid = take((size_t)l.lm_rows * 4);
+  l.off_rpb = take((size_t)l.lm_rows * 4);
+  l.off_vscr = take(vocab_scratch_bytes(l.vp, l.lm_rows));
+  l.off_argmax = take((size_t)l.lm_rows * 4);
+  l.off_conf = take((size_t)l.lm_rows * 4);
+  l.off_lse = take((size_t)l.lm_rows * 4);
+  l.off_tid = take((size_t)l.lm_rows * 8 * 4);
+  l.off_tp = take((size_t)l.lm_rows * 8 * 4);
+  l.off_credit = take((size_t)l.lm_rows * 4);
+  l.off_tracked = take((size_t)l.lm_rows * 4);
+  l.off_sid = take((size_t)l.lm_rows * 8 * 4);
+  l.off_sp = take((size_t)l.lm_rows * 8 * 4);
+  l.off_sv = take((size_t)l.lm_rows);
+  l.off_cm = take((size_t)l.lm_rows);
+  l.off_done = take((size_t)max_batch * 4);
+  l.off_steps = take((size_t)max_batch * 4);
+  l.off_ccount = take((size_t)max_batch * 4);
+  l.off_tab_step = take((size_t)l.tab_ints_step * 4);
+  l.off_tab_ref = take((size_t)l.tab_ints_ref * 4);
+  l.off_mask = take((size_t)max_batch * 4);
+  l.off_misc = take(64);
+  l.total = o;
+  return true;
+}
+
+PassTable table_view(int* base, int m_cap, int mb) {
+  PassTable t;
+  t.nrows = base;
+  t.row_req = base + 16;
+  t.row_pos = base + 16 + m_cap;
+  t.req_row_off = base + 16 + 2 * m_cap;
+  t.req_nrows = t.req_row_off + mb;
+  t.req_len = t.req_nrows + mb;
+  t.req_bs = t.req_len + mb;
+  t.req_active = t.req_bs + mb;
+  return t;
+}
+
+}  // namespace
+
+struct dinfer_ctx {
+  dinfer_model_cfg m;
+  dinfer_decode_cfg dc;
+  Layout L;
+  hipStream_t stream = nullptr;   // caller's stream
+  hipStream_t st = nullptr;       // stream kernels go to (the capture stream while capturing)
+  hipStream_t cap_stream = nullptr;
+  // weights
+  const void* tok_emb = nullptr;
+  const void* final_norm = nullptr;
+  const void* lm_head = nullptr;
+  std::vector<const void*> attn_norm, wqkv, wo, ffn_norm, wgu, wd;
+  // workspace
+  char* ws = nullptr;
+  // batch
+  int batch = 0;
+  int* tokens = nullptr;
+  const int* plant_id = nullptr;
+  const float* plant_bias = nullptr;
+  std::vector<int> P, G, Lr, blk, nblk;
+  std::vector<uint8_t> finished, refreshed;
+  // host staging (pinned) for the row tables
+  int* h_tab_step = nullptr;
+  int* h_tab_ref = nullptr;
+  int* h_misc = nullptr;
+  hipEvent_t ev_step_upload = nullptr, ev_ref_upload = nullptr;
+  bool step_dirty = true;
+  int state = 0;                  // 0 init, 1 batch bound
+  bool stats_ready = false;
+  // graph
+  hipGraphExec_t graph = nullptr;
+  int graph_steps = 0;
+  hipEvent_t ev0 = nullptr, ev1 = nullptr;
+
+  template <typename T> T* at(size_t off) const { return reinterpret_cast<T*>(ws + off); }
+};
+
+namespace {
+
+dinfer_status upload_step_table(dinfer_ctx* c) {
+  const Layout& L = c->L;
+  HIP_TRY(hipEventSynchronize(c->ev_step_upload));
+  int* t = c->h_tab_step;
+  const int mb = L.max_batch;
+  int* row_req = t + 16;
+  int* row_pos = t + 16 + L.m_step;
+  int* off = t + 16 + 2 * L.m_step;
+  int* nr = off + mb;
+  int* len = nr + mb;
+  int* bs = len + mb;
+  int* act = bs + mb;
+  int rows = 0;
+  for (int r = 0; r < mb; ++r) {
+    off[r] = rows;
+    nr[r] = 0;
+    len[r] = 0;
+    bs[r] = 0;
+    act[r] = 0;
+    if (r >= c->batch) continue;
+    len[r] = c->Lr[r];
+    bs[r] = c->P[r] + c->blk[r] * L.B;
+    if (c->finished[r] || !c->refreshed[r]) continue;
+    const int lo = std::max(0, bs[r] - L.w);
+    const int hi = std::min(c->Lr[r], bs[r] + L.B + L.w);
+    act[r] = 1;
+    nr[r] = hi - lo;
+    for (int i = 0; i < hi - lo; ++i) {
+      row_req[rows + i] = r;
+      row_pos[rows + i] = lo + i;
+    }
+    rows += hi - lo;
+  }
+  t[0] = rows;
+  t[1] = c->batch * L.B;   // LM-head rows
+  HIP_TRY(hipMemcpyAsync(c->at<int>(L.off_tab_step), t, (size_t)L.tab_ints_step * 4,
+                         hipMemcpyHostToDevice, c->stream));
+  HIP_TRY(hipEventRecord(c->ev_step_upload, c->stream));
+  c->step_dirty = false;
+  return DINFER_OK;
+}
+
+// One pass of the model over the rows of a table: embed, every layer with the
+// KV scatter before attention, and for a step the final norm, LM head and
+// vocab statistics.
+dinfer_status run_pass(dinfer_ctx* c, bool step) {
+  const Layout& L = c->L;
+  const DType dt = L.dt;
+  const size_t es = dtype_size(dt);
+  hipStream_t st = c->st;
+  const int m_cap = step ? L.m_step : L.m_ref;
+  int* tab = c->at<int>(step ? L.off_tab_step : L.off_tab_ref);
+  const PassTable tb = table_view(tab, m_cap, L.max_batch);
+  const GemmPlan& gq = step ? L.g_qkv_s : L.g_qkv_r;
+  const GemmPlan& go = step ? L.g_o_s : L.g_o_r;
+  const GemmPlan& gg = step ? L.g_gu_s : L.g_gu_r;
+  const GemmPlan& gd = step ? L.g_d_s : L.g_d_r;
+  const AttnPlan& ap = step ? L.a_step : L.a_ref;
+  const int d = L.d, F = L.F;
+  float* x = c->at<float>(L.off_x);
+  void* a = c->at<char>(L.off_a);
+  void* q = c->at<char>(L.off_q);
+  void* o = c->at<char>(L.off_o);
+  void* act = c->at<char>(L.off_act);
+  float* part = c->at<float>(L.off_part);
+  const size_t stride_q = (size_t)m_cap * 3 * d, stride_d = (size_t)m_cap * d,
+               stride_g = (size_t)m_cap * 2 * F;
+
+  HIP_TRY(launch_embed(dt, tb, m_cap, c->tokens, L.max_len, c->tok_emb, d, L.V, c->m.mask_id,
+                       step ? c->dc.smooth_alpha : 0.f, c->at<int>(L.off_sid),
+                       c->at<float>(L.off_sp), c->at<uint8_t>(L.off_sv), L.B, x, st));
+  for (int l = 0; l < L.nl; ++l) {
+    const bool last = l == L.nl - 1;
+    HIP_TRY(launch_add_rmsnorm(dt, tb.nrows, m_cap, x, part, l == 0 ? 0 : gd.splits, stride_d,
+                               c->attn_norm[l], c->m.rms_eps, a, d, st));
+    HIP_TRY(launch_gemm(gq, dt, a, c->wqkv[l], part, tb.nrows, m_cap, 3 * d, d, st));
+    char* kvk = c->at<char>(L.off_kvk) + (size_t)l * L.kv_layer_elems * es;
+    char* kvv = c->at<char>(L.off_kvv) + (size_t)l * L.kv_layer_elems * es;
+    HIP_TRY(launch_qkv_rope_scatter(dt, tb, m_cap, part, gq.splits, stride_q, d, L.H, L.hd,
+                                    c->at<float>(L.off_rope), q, kvk, kvv, L.max_len, st));
+    if (!step && last) break;   // a refresh needs only the caches
+    HIP_TRY(launch_attention(dt, ap, tb, L.max_batch, m_cap, q, kvk, kvv, L.H, L.hd, L.max_len,
+                             c->at<float>(L.off_ao), c->at<float>(L.off_aml), o, st));
+    HIP_TRY(launch_gemm(go, dt, o, c->wo[l], part, tb.nrows, m_cap, d, d, st));
+    HIP_TRY(launch_add_rmsnorm(dt, tb.nrows, m_cap, x, part, go.splits, stride_d, c->ffn_norm[l],
+                               c->m.rms_eps, a, d, st));
+    HIP_TRY(launch_gemm(gg, dt, a, c->wgu[l], part, tb.nrows, m_cap, 2 * F, d, st));
+    HIP_TRY(launch_swiglu(dt, tb.nrows, m_cap, part, gg.splits, stride_g, F, act, st));
+    HIP_TRY(launch_gemm(gd, dt, act, c->wd[l], part, tb.nrows, m_cap, d, F, st));
+  }
+  if (!step) return DINFER_OK;
+  void* hf = c->at<char>(L.off_hf);
+  HIP_TRY(launch_final_norm(dt, tb, L.max_batch, L.B, x, part, gd.splits, stride_d, c->final_norm,
+                            c->m.rms_eps, hf, d, c->plant_id, c->plant_bias, L.max_len,
+                            c->at<int>(L.off_rpid), c->at<float>(L.off_rpb), st));
+  float* logits = c->at<float>(L.off_logits);
+  HIP_TRY(launch_gemm(L.g_lm, dt, hf, c->lm_head, logits, tab + 1, L.lm_rows, L.V, d, st));
+  HIP_TRY(launch_vocab_stats(L.vp, logits, c->batch * L.B, L.V, c->at<int>(L.off_rpid),
+                             c->at<float>(L.off_rpb), c->m.mask_id, c->at<char>(L.off_vscr),
+                             c->at<int>(L.off_argmax), c->at<float>(L.off_conf),
+                             c->at<float>(L.off_lse), c->at<int>(L.off_tid),
+                             c->at<float>(L.off_tp), st));
+  return DINFER_OK;
+}
+
+dinfer_status launch_commit_step(dinfer_ctx* c) {
+  const Layout& L = c->L;
+  const PassTable tb = table_view(c->at<int>(L.off_tab_step), L.m_step, L.max_batch);
+  CommitArgs a{};
+  a.batch = c->batch;
+  a.B = L.B;
+  a.max_len = L.max_len;
+  a.mask_id = c->m.mask_id;
+  a.hierarchical = c->dc.hierarchical;
+  a.tau = c->dc.tau;
+  a.kappa = c->dc.credit_kappa;
+  a.gamma = c->dc.credit_decay;
+  a.lambda = c->dc.credit_weight;
+  a.req_bs = tb.req_bs;
+  a.req_active = tb.req_active;
+  a.tokens = c->tokens;
+  a.argmax = c->at<int>(L.off_argmax);
+  a.conf = c->at<float>(L.off_conf);
+  a.topk_id = c->at<int>(L.off_tid);
+  a.topk_p = c->at<float>(L.off_tp);
+  a.credit = c->at<float>(L.off_credit);
+  a.tracked = c->at<int>(L.off_tracked);
+  a.smooth_id = c->at<int>(L.off_sid);
+  a.smooth_p = c->at<float>(L.off_sp);
+  a.smooth_valid = c->at<uint8_t>(L.off_sv);
+  a.commit_mask = c->at<uint8_t>(L.off_cm);
+  a.block_done = c->at<int>(L.off_done);
+  a.step_count = c->at<int>(L.off_steps);
+  a.commit_count = c->at<int>(L.off_ccount);
+  HIP_TRY(launch_commit(a, c->st));
+  return DINFER_OK;
+}
+
+int unfinished(const dinfer_ctx* c) {
+  int n = 0;
+  for (int r = 0; r < c->batch; ++r) n += !c->finished[r];
+  return n;
+}
+
+int active_count(const dinfer_ctx* c) {
+  int n = 0;
+  for (int r = 0; r < c->batch; ++r) n += (!c->finished[r] && c->refreshed[r]);
+  return n;
+}
+
+}  // namespace
+
+// ----------------------------------------------------------------------------
+extern "C" {
+
+const char* dinfer_status_str(dinfer_status s) {
+  switch (s) {
+    case DINFER_OK: return "DINFER_OK";
+    case DINFER_E_ARG: return "DINFER_E_ARG";
+    case DINFER_E_WORKSPACE: return "DINFER_E_WORKSPACE";
+    case DINFER_E_STATE: return "DINFER_E_STATE";
+    case DINFER_E_HIP: return "DINFER_E_HIP";
+    case DINFER_E_UNSUPPORTED: return "DINFER_E_UNSUPPORTED";
+  }
+  return "DINFER_E_UNKNOWN";
+}
+
+const char* dinfer_last_error(void) { return g_last_error.c_str(); }
+
+size_t dinfer_workspace_bytes(const dinfer_model_cfg* m, const dinfer_decode_cfg* dc,
+                              int32_t max_batch, int32_t max_len) {
+  Layout L;
+  if (!make_layout(m, dc, max_batch, max_len, &L, nullptr)) return 0;
+  return L.total;
+}
+
+dinfer_status dinfer_step_init(const dinfer_model_cfg* m, const dinfer_decode_cfg* dc,
+                               const dinfer_weights* w, int32_t max_batch, int32_t max_len,
+                               void* d_workspace, size_t ws_bytes, void* stream,
+                               dinfer_ctx** out) {
+  if (!out) return fail(DINFER_E_ARG, "out is null");
+  *out = nullptr;
+  std::string why;
+  Layout L;
+  if (!make_layout(m, dc, max_batch, max_len, &L, &why)) {
+    const bool unsup = why.find("not supported") != std::string::npos ||
+                       why.find("must be 64 or 128") != std::string::npos ||
+                       why.find("GEMM shapes") != std::string::npos;
+    return fail(unsup ? DINFER_E_UNSUPPORTED : DINFER_E_ARG, why);
+  }
+  if (!w || !w->tok_emb || !w->final_norm || !w->lm_head || !w->attn_norm || !w->wqkv || !w->wo ||
+      !w->ffn_norm || !w->w_gate_up || !w->w_down)
+    return fail(DINFER_E_ARG, "missing weight pointers");
+  for (int l = 0; l < m->n_layers; ++l)
+    if (!w->attn_norm[l] || !w->wqkv[l] || !w->wo[l] || !w->ffn_norm[l] || !w->w_gate_up[l] ||
+        !w->w_down[l])
+      return fail(DINFER_E_ARG, "missing per-layer weight pointer at layer " + std::to_string(l));
+  if (!d_workspace) return fail(DINFER_E_WORKSPACE, "workspace is null");
+  if (reinterpret_cast<uintptr_t>(d_workspace) % kAlign != 0)
+    return fail(DINFER_E_WORKSPACE, "workspace must be 256-byte aligned");
+  if (ws_bytes < L.total)
+    return fail(DINFER_E_WORKSPACE, "workspace too small: need " + std::to_string(L.total) +
+                                        " bytes, got " + std::to_string(ws_bytes));
+
+  dinfer_ctx* c = new dinfer_ctx();
+  c->m = *m;
+  c->dc = *dc;
+  c->L = L;
+  c->stream = static_cast<hipStream_t>(stream);
+  c->st = c->stream;
+  c->ws = static_cast<char*>(d_workspace);
+  c->tok_emb = w->tok_emb;
+  c->final_norm = w->final_norm;
+  c->lm_head = w->lm_head;
+  c->attn_norm.assign(w->attn_norm, w->attn_norm + m->n_layers);
+  c->wqkv.assign(w->wqkv, w->wqkv + m->n_layers);
+  c->wo.assign(w->wo, w->wo + m->n_layers);
+  c->ffn_norm.assign(w->ffn_norm, w->ffn_norm + m->n_layers);
+  c->wgu.assign(w->w_gate_up, w->w_gate_up + m->n_layers);
+  c->wd.assign(w->w_down, w->w_down + m->n_layers);
+
+  auto cleanup = [&](dinfer_status s) {
+    dinfer_destroy(c);
+    return s;
+  };
+  if (hipHostMalloc(&c->h_tab_step, (size_t)L.tab_ints_step * 4) != hipSuccess ||
+      hipHostMalloc(&c->h_tab_ref, (size_t)L.tab_ints_ref * 4) != hipSuccess ||
+      hipHostMalloc(&c->h_misc, 64 * 4) != hipSuccess)
+    return cleanup(fail(DINFER_E_HIP, "pinned host staging allocation failed"));
+  if (hipEventCreateWithFlags(&c->ev_step_upload, hipEventDisableTiming) != hipSuccess ||
+      hipEventCreateWithFlags(&c->ev_ref_upload, hipEventDisableTiming) != hipSuccess ||
+      hipEventCreate(&c->ev0) != hipSuccess || hipEventCreate(&c->ev1) != hipSuccess)
+    return cleanup(fail(DINFER_E_HIP, "event creation failed"));
+  std::memset(c->h_tab_step, 0, (size_t)L.tab_ints_step * 4);
+  std::memset(c->h_tab_ref, 0, (size_t)L.tab_ints_ref * 4);
+
+  // RoPE table [pos][cos(0..hd/2) | sin(0..hd/2)], angles in fp64.
+  std::vector<float> cs((size_t)max_len * L.hd);
+  const int half = L.hd / 2;
+  for (int p = 0; p < max_len; ++p)
+    for (int j = 0; j < half; ++j) {
+      const double ang = (double)p * std::pow((double)m->rope_theta, -2.0 * j / L.hd);
+      cs[(size_t)p * L.hd + j] = (float)std::cos(ang);
+      cs[(size_t)p * L.hd + half + j] = (float)std::sin(ang);
+    }
+  if (hipMemcpyAsync(c->at<float>(L.off_rope), cs.data(), cs.size() * 4, hipMemcpyHostToDevice,
+                     c->stream) != hipSuccess ||
+      hipMemsetAsync(c->at<char>(L.off_done), 0, (size_t)max_batch * 4, c->stream) != hipSuccess ||
+      hipMemsetAsync(c->at<char>(L.off_steps), 0, (size_t)max_batch * 4, c->stream) != hipSuccess ||
+      hipMemsetAsync(c->at<char>(L.off_ccount), 0, (size_t)max_batch * 4, c->stream) != hipSuccess ||
+      hipMemsetAsync(c->at<char>(L.off_tab_step), 0, (size_t)L.tab_ints_step * 4, c->stream) !=
+          hipSuccess ||
+      hipMemsetAsync(c->at<char>(L.off_tab_ref), 0, (size_t)L.tab_ints_ref * 4, c->stream) !=
+          hipSuccess ||
+      hipStreamSynchronize(c->stream) != hipSuccess)
+    return cleanup(fail(DINFER_E_HIP, "workspace initialisation failed"));
+  *out = c;
+  return DINFER_OK;
+}
+
+dinfer_status dinfer_set_batch(dinfer_ctx* c, int32_t batch, int32_t* d_tokens,
+                               const int32_t* h_prompt_len, const int32_t* h_gen_len,
+                               const int32_t* d_plant_id, const float* d_plant_bias,
+                               const float* d_router_bias) {
+  if (!c) return fail(DINFER_E_ARG, "ctx is null");
+  if (batch < 1 || batch > c->L.max_batch) return fail(DINFER_E_ARG, "batch out of range");
+  if (!d_tokens || !h_prompt_len || !h_gen_len) return fail(DINFER_E_ARG, "null batch pointer");
+  if (d_router_bias) return fail(DINFER_E_UNSUPPORTED, "router bias given for a dense model");
+  const int B = c->L.B;
+  for (int r = 0; r < batch; ++r) {
+    if (h_prompt_len[r] < 0 || h_gen_len[r] < B || h_gen_len[r] % B != 0)
+      return fail(DINFER_E_ARG, "gen_len must be a positive multiple of block_len");
+    if (h_prompt_len[r] + h_gen_len[r] > c->L.max_len)
+      return fail(DINFER_E_ARG, "prompt_len + gen_len exceeds max_len");
+  }
+  if (c->graph && (batch != c->batch || d_tokens != c->tokens || d_plant_id != c->plant_id ||
+                   d_plant_bias != c->plant_bias)) {
+    // kernel arguments captured in the graph change with these
+    (void)hipGraphExecDestroy(c->graph);
+    c->graph = nullptr;
+    c->graph_steps = 0;
+  }
+  c->batch = batch;
+  c->tokens = d_tokens;
+  c->plant_id = d_plant_id;
+  c->plant_bias = d_plant_bias;
+  c->P.assign(h_prompt_len, h_prompt_len + batch);
+  c->G.assign(h_gen_len, h_gen_len + batch);
+  c->Lr.resize(batch);
+  c->blk.assign(batch, 0);
+  c->nblk.resize(batch);
+  for (int r = 0; r < batch; ++r) {
+    c->Lr[r] = c->P[r] + c->G[r];
+    c->nblk[r] = c->G[r] / B;
+  }
+  c->finished.assign(batch, 0);
+  c->refreshed.assign(batch, 0);
+  c->step_dirty = true;
+  c->stats_ready = false;
+  c->state = 1;
+  const Layout& L = c->L;
+  HIP_TRY(hipMemsetAsync(c->at<char>(L.off_done), 0, (size_t)L.max_batch * 4, c->stream));
+  HIP_TRY(hipMemsetAsync(c->at<char>(L.off_steps), 0, (size_t)L.max_batch * 4, c->stream));
+  HIP_TRY(hipMemsetAsync(c->at<char>(L.off_ccount), 0, (size_t)L.max_batch * 4, c->stream));
+  return upload_step_table(c);
+}
+
+dinfer_status dinfer_refresh_kv(dinfer_ctx* c, const uint8_t* h_req_mask) {
+  if (!c) return fail(DINFER_E_ARG, "ctx is null");
+  if (c->state < 1) return fail(DINFER_E_STATE, "refresh_kv before set_batch");
+  const Layout& L = c->L;
+  HIP_TRY(hipEventSynchronize(c->ev_ref_upload));
+  int* t = c->h_tab_ref;
+  const int mb = L.max_batch;
+  int* row_req = t + 16;
+  int* row_pos = t + 16 + L.m_ref;
+  int* off = t + 16 + 2 * L.m_ref;
+  int* nr = off + mb;
+  int* len = nr + mb;
+  int* bs = len + mb;
+  int* act = bs + mb;
+  int* mask = c->h_misc;
+  int rows = 0, nsel = 0;
+  for (int r = 0; r < mb; ++r) {
+    off[r] = rows;
+    nr[r] = len[r] = bs[r] = act[r] = 0;
+    mask[r] = 0;
+    if (r >= c->batch || c->finished[r]) continue;
+    if (h_req_mask && !h_req_mask[r]) continue;
+    mask[r] = 1;
+    ++nsel;
+    len[r] = c->Lr[r];
+    bs[r] = c->P[r] + c->blk[r] * L.B;
+    act[r] = 1;
+    nr[r] = c->Lr[r];
+    for (int i = 0; i < c->Lr[r]; ++i) {
+      row_req[rows + i] = r;
+      row_pos[rows + i] = i;
+    }
+    rows += c->Lr[r];
+  }
+  if (nsel == 0) return DINFER_OK;
+  t[0] = rows;
+  HIP_TRY(hipMemcpyAsync(c->at<int>(L.off_tab_ref), t, (size_t)L.tab_ints_ref * 4,
+                         hipMemcpyHostToDevice, c->stream));
+  HIP_TRY(hipMemcpyAsync(c->at<int>(L.off_mask), mask, (size_t)mb * 4, hipMemcpyHostToDevice,
+                         c->stream));
+  HIP_TRY(hipEventRecord(c->ev_ref_upload, c->stream));
+  c->st = c->stream;
+  dinfer_status s = run_pass(c, false);
+  if (s != DINFER_OK) return s;
+  HIP_TRY(launch_block_reset(mb, L.B, c->at<int>(L.off_mask), c->at<float>(L.off_credit),
+                             c->at<int>(L.off_tracked), c->at<uint8_t>(L.off_sv),
+                             c->at<uint8_t>(L.off_cm), c->at<int>(L.off_done),
+                             c->at<int>(L.off_steps), c->stream));
+  for (int r = 0; r < c->batch; ++r)
+    if (mask[r]) c->refreshed[r] = 1;
+  c->step_dirty = true;
+  return DINFER_OK;
+}
+
+dinfer_status dinfer_denoise_step(dinfer_ctx* c) {
+  if (!c) return fail(DINFER_E_ARG, "ctx is null");
+  if (c->state < 1) return fail(DINFER_E_STATE, "denoise_step before set_batch");
+  if (active_count(c) == 0) return fail(DINFER_E_STATE, "no refreshed request with an open block");
+  if (c->step_dirty) {
+    dinfer_status s = upload_step_table(c);
+    if (s != DINFER_OK) return s;
+  }
+  c->st = c->stream;
+  dinfer_status s = run_pass(c, true);
+  if (s == DINFER_OK) c->stats_ready = true;
+  return s;
+}
+
+dinfer_status dinfer_commit(dinfer_ctx* c) {
+  if (!c) return fail(DINFER_E_ARG, "ctx is null");
+  if (!c->stats_ready) return fail(DINFER_E_STATE, "commit without a preceding denoise_step");
+  c->st = c->stream;
+  dinfer_status s = launch_commit_step(c);
+  if (s == DINFER_OK) c->stats_ready = false;
+  return s;
+}
+
+dinfer_status dinfer_advance_blocks(dinfer_ctx* c, uint8_t* h_needs_refresh, int32_t* h_unfinished) {
+  if (!c) return fail(DINFER_E_ARG, "ctx is null");
+  if (c->state < 1) return fail(DINFER_E_STATE, "advance_blocks before set_batch");
+  std::vector<int> done(c->batch);
+  HIP_TRY(hipMemcpyAsync(done.data(), c->at<int>(c->L.off_done), (size_t)c->batch * 4,
+                         hipMemcpyDeviceToHost, c->stream));
+  HIP_TRY(hipStreamSynchronize(c->stream));
+  for (int r = 0; r < c->batch; ++r) {
+    if (h_needs_refresh) h_needs_refresh[r] = 0;
+    if (c->finished[r] || !c->refreshed[r] || !done[r]) continue;
+    c->blk[r] += 1;
+    c->refreshed[r] = 0;
+    c->step_dirty = true;
+    if (c->blk[r] >= c->nblk[r]) {
+      c->finished[r] = 1;
+      c->blk[r] = c->nblk[r] - 1;
+    } else if (h_needs_refresh) {
+      h_needs_refresh[r] = 1;
+    }
+  }
+  if (h_unfinished) *h_unfinished = unfinished(c);
+  return DINFER_OK;
+}
+
+static dinfer_status capture_graph(dinfer_ctx* c, int U) {
+  if (c->graph) {
+    (void)hipGraphExecDestroy(c->graph);
+    c->graph = nullptr;
+  }
+  if (!c->cap_stream) HIP_TRY(hipStreamCreateWithFlags(&c->cap_stream, hipStreamNonBlocking));
+  HIP_TRY(hipStreamBeginCapture(c->cap_stream, hipStreamCaptureModeThreadLocal));
+  c->st = c->cap_stream;
+  dinfer_status s = DINFER_OK;
+  for (int u = 0; u < U && s == DINFER_OK; ++u) {
+    s = run_pass(c, true);
+    if (s == DINFER_OK) s = launch_commit_step(c);
+  }
+  hipGraph_t g = nullptr;
+  hipError_t e = hipStreamEndCapture(c->cap_stream, &g);
+  c->st = c->stream;
+  if (s != DINFER_OK) {
+    if (g) (void)hipGraphDestroy(g);
+    return s;
+  }
+  if (e != hipSuccess) return fail(DINFER_E_HIP, std::string("graph capture: ") + hipGetErrorString(e));
+  e = hipGraphInstantiate(&c->graph, g, nullptr, nullptr, 0);
+  (void)hipGraphDestroy(g);
+  if (e != hipSuccess) return fail(DINFER_E_HIP, std::string("graph instantiate: ") + hipGetErrorString(e));
+  c->graph_steps = U;
+  return DINFER_OK;
+}
+
+dinfer_status dinfer_step_graph(dinfer_ctx* c, int32_t n_steps) {
+  if (!c) return fail(DINFER_E_ARG, "ctx is null");
+  const int U = c->dc.graph_unroll;
+  if (U <= 0) return fail(DINFER_E_STATE, "graph_unroll is 0: no step graph");
+  if (n_steps < 0 || n_steps % U != 0)
+    return fail(DINFER_E_ARG, "n_steps must be a non-negative multiple of graph_unroll");
+  if (c->state < 1) return fail(DINFER_E_STATE, "step_graph before set_batch");
+  if (active_count(c) == 0) return fail(DINFER_E_STATE, "no refreshed request with an open block");
+  if (c->step_dirty) {
+    dinfer_status s = upload_step_table(c);
+    if (s != DINFER_OK) return s;
+  }
+  if (!c->graph || c->graph_steps != U) {
+    dinfer_status s = capture_graph(c, U);
+    if (s != DINFER_OK) return s;
+  }
+  for (int i = 0; i < n_steps / U; ++i) HIP_TRY(hipGraphLaunch(c->graph, c->stream));
+  c->stats_ready = false;
+  return DINFER_OK;
+}
+
+dinfer_status dinfer_run_to_completion(dinfer_ctx* c, int32_t max_steps, dinfer_run_stats* h_stats) {
+  if (!c) return fail(DINFER_E_ARG, "ctx is null");
+  if (c->state < 1) return fail(DINFER_E_STATE, "run_to_completion before set_batch");
+  const auto t0 = std::chrono::steady_clock::now();
+  dinfer_run_stats stats{};
+  double refresh_ms = 0.0;
+  std::vector<uint8_t> need(c->batch);
+  auto refresh = [&](const uint8_t* mask) -> dinfer_status {
+    int n = 0;
+    for (int r = 0; r < c->batch; ++r) n += (!c->finished[r] && !c->refreshed[r] && (!mask || mask[r]));
+    if (n == 0) return DINFER_OK;
+    std::vector<uint8_t> sel(c->batch);
+    for (int r = 0; r < c->batch; ++r) sel[r] = (!c->finished[r] && !c->refreshed[r] && (!mask || mask[r]));
+    HIP_TRY(hipEventRecord(c->ev0, c->stream));
+    dinfer_status s = dinfer_refresh_kv(c, sel.data());
+    if (s != DINFER_OK) return s;
+    HIP_TRY(hipEventRecord(c->ev1, c->stream));
+    HIP_TRY(hipEventSynchronize(c->ev1));
+    float ms = 0.f;
+    HIP_TRY(hipEventElapsedTime(&ms, c->ev0, c->ev1));
+    refresh_ms += ms;
+    stats.refreshes += n;
+    return DINFER_OK;
+  };
+  dinfer_status s = refresh(nullptr);
+  if (s != DINFER_OK) return s;
+  const int U = c->dc.graph_unroll;
+  while (unfinished(c) > 0) {
+    if (stats.steps >= max_steps) return fail(DINFER_E_STATE, "max_steps reached before completion");
+    if (c->step_dirty) {
+      s = upload_step_table(c);
+      if (s != DINFER_OK) return s;
+    }
+    if (U > 0) {
+      if (!c->graph || c->graph_steps != U) {
+        s = capture_graph(c, U);
+        if (s != DINFER_OK) return s;
+      }
+      HIP_TRY(hipGraphLaunch(c->graph, c->stream));
+      stats.steps += U;
+    } else {
+      s = dinfer_denoise_step(c);
+      if (s == DINFER_OK) s = dinfer_commit(c);
+      if (s != DINFER_OK) return s;
+      stats.steps += 1;
+    }
+    s = dinfer_advance_blocks(c, need.data(), nullptr);
+    if (s != DINFER_OK) return s;
+    s = refresh(need.data());
+    if (s != DINFER_OK) return s;
+  }
+  std::vector<int> cc(c->batch);
+  HIP_TRY(hipMemcpyAsync(cc.data(), c->at<int>(c->L.off_ccount), (size_t)c->batch * 4,
+                         hipMemcpyDeviceToHost, c->stream));
+  HIP_TRY(hipStreamSynchronize(c->stream));
+  for (int r = 0; r < c->batch; ++r) stats.committed += cc[r];
+  stats.wall_ms = std::chrono::duration<double, std::milli>(std::chrono::steady_clock::now() - t0).count();
+  stats.refresh_ms = refresh_ms;
+  if (h_stats) *h_stats = stats;
+  return DINFER_OK;
+}
+
+dinfer_status dinfer_get_step_view(const dinfer_ctx* c, dinfer_step_view* v) {
+  if (!c || !v) return fail(DINFER_E_ARG, "null argument");
+  const Layout& L = c->L;
+  v->batch = c->batch;
+  v->block_len = L.B;
+  v->vocab = L.V;
+  v->topk = 8;
+  v->logits = c->at<float>(L.off_logits);
+  v->argmax = c->at<int>(L.off_argmax);
+  v->conf = c->at<float>(L.off_conf);
+  v->lse = c->at<float>(L.off_lse);
+  v->topk_id = c->at<int>(L.off_tid);
+  v->topk_p = c->at<float>(L.off_tp);
+  v->credit = c->at<float>(L.off_credit);
+  v->tracked = c->at<int>(L.off_tracked);
+  v->smooth_id = c->at<int>(L.off_sid);
+  v->smooth_p = c->at<float>(L.off_sp);
+  v->smooth_valid = c->at<uint8_t>(L.off_sv);
+  v->commit_mask = c->at<uint8_t>(L.off_cm);
+  v->block_done = c->at<int>(L.off_done);
+  v->step_count = c->at<int>(L.off_steps);
+  v->commit_count = c->at<int>(L.off_ccount);
+  v->kv_k = c->at<char>(L.off_kvk);
+  v->kv_v = c->at<char>(L.off_kvv);
+  return DINFER_OK;
+}
+
+size_t dinfer_linear_out_elems(int32_t M, int32_t N, int32_t K, int32_t dtype) {
+  if (M < 1 || (dtype != DINFER_F32 && dtype != DINFER_BF16)) return 0;
+  const DType dt = dtype == DINFER_F32 ? DType::F32 : DType::BF16;
+  if (!gemm_shape_ok(dt, N, K)) return 0;
+  const GemmPlan p = plan_gemm(dt, M, N, K, 512);
+  return (size_t)p.splits * M * N;
+}
+
+dinfer_status dinfer_linear(const void* d_A, const void* d_W, float* d_out, int32_t M, int32_t N,
+                            int32_t K, int32_t dtype, int32_t* h_splits, void* stream) {
+  if (!d_A || !d_W || !d_out) return fail(DINFER_E_ARG, "null pointer");
+  if (M < 1) return fail(DINFER_E_ARG, "M must be positive");
+  if (dtype != DINFER_F32 && dtype != DINFER_BF16) return fail(DINFER_E_ARG, "bad dtype");
+  const DType dt = dtype == DINFER_F32 ? DType::F32 : DType::BF16;
+  if (!gemm_shape_ok(dt, N, K)) return fail(DINFER_E_UNSUPPORTED, "N % 128 or K chunk multiple");
+  const GemmPlan p = plan_gemm(dt, M, N, K, 512);
+  if (h_splits) *h_splits = p.splits;
+  HIP_TRY(launch_gemm(p, dt, d_A, d_W, d_out, nullptr, M, N, K, static_cast<hipStream_t>(stream)));
+  return DINFER_OK;
+}
+
+size_t dinfer_vocab_stats_scratch_bytes(int32_t rows, int32_t vocab) {
+  if (rows < 1 || vocab < 2) return 0;
+  return vocab_scratch_bytes(plan_vocab(rows, vocab, 1024), rows);
+}
+
+dinfer_status dinfer_vocab_stats(const float* d_logits, int32_t rows, int32_t vocab,
+                                 const int32_t* d_plant_id, const float* d_plant_bias,
+                                 int32_t mask_id, int32_t* d_argmax, float* d_conf, float* d_lse,
+                                 int32_t* d_topk_id, float* d_topk_p, void* d_scratch,
+                                 size_t scratch_bytes, void* stream) {
+  if (!d_logits || !d_argmax || !d_conf || !d_lse || !d_topk_id || !d_topk_p)
+    return fail(DINFER_E_ARG, "null output or input pointer");
+  if (rows < 1 || vocab < 2) return fail(DINFER_E_ARG, "rows and vocab must be positive");
+  if (vocab % 4 != 0) return fail(DINFER_E_UNSUPPORTED, "vocab must be a multiple of 4");
+  if (mask_id < -1 || mask_id >= vocab) return fail(DINFER_E_ARG, "mask_id out of range");
+  const VocabPlan p = plan_vocab(rows, vocab, 1024);
+  if (!d_scratch || scratch_bytes < vocab_scratch_bytes(p, rows))
+    return fail(DINFER_E_WORKSPACE, "scratch too small");
+  HIP_TRY(launch_vocab_stats(p, d_logits, rows, vocab, d_plant_id, d_plant_bias, mask_id, d_scratch,
+                             d_argmax, d_conf, d_lse, d_topk_id, d_topk_p,
+                             static_cast<hipStream_t>(stream)));
+  return DINFER_OK;
+}
+
+void dinfer_destroy(dinfer_ctx* c) {
+  if (!c) return;
+  if (c->graph) (void)hipGraphExecDestroy(c->graph);
+  if (c->cap_stream) (void)hipStreamDestroy(c->cap_stream);
+  if (c->ev_step_upload) (void)hipEventDestroy(c->ev_step_upload);
+  if (c->ev_ref_upload) (void)hipEventDestroy(c->ev_ref_upload);
+  if (c->ev0) (void)hipEventDestroy(c->ev0);
+  if (c->ev1) (void)hipEventDestroy(c->ev1);
+  if (c->h_tab_step) (void)hipHostFree(c->h_tab_step);
+  if (c->h_tab_ref) (void)hipHostFree(c->h_tab_ref);
+  if (c->h_misc) (void)hipHostFree(c->h_misc);
+  delete c;
+}
+
+}  // extern "C"

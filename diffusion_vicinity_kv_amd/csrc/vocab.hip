@@ -1,0 +1,287 @@
+// Vocab statistics of the block rows: planting bias, MASK exclusion, argmax
+// (lowest id on ties), max softmax probability, log-sum-exp and top-8 --
+// everything the decoding strategy consumes (dInfer news article, section
+// "扩散模型的“理论翅膀”与“现实枷锁”": confidence of the most likely token;
+// section "解码的艺术": the probability distribution kept for iteration
+// smoothing).
+//
+// HBM-bound: one pass over the fp32 logits.  The vocabulary of a row is split
+// across workgroups so that a few rows still fill the chip; each thread keeps
+// an online (max, sum of exp) and a sorted top-8 in registers, a workgroup
+// merges them with wave64 exchanges, and a second kernel merges the splits of
+// a row (one wave per row) in split order.
+#include "common.h"
+#include "kernels.h"
+
+#include <climits>
+
+namespace dinfer {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kTop = 8;
+constexpr float kLog2e = 1.4426950408889634f;
+
+// Order used everywhere: larger value first, then smaller id.
+__device__ __forceinline__ bool better(float va, int ia, float vb, int ib) {
+  return va > vb || (va == vb && ia < ib);
+}
+
+// Wave-wide best (value, id) pair.
+__device__ __forceinline__ void wave_best(float& v, int& id) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float ov = __shfl_xor(v, o, 64);
+    const int oi = __shfl_xor(id, o, 64);
+    if (better(ov, oi, v, id)) {
+      v = ov;
+      id = oi;
+    }
+  }
+}
+
+// Extract the wave's top-8 from per-lane sorted lists (pop-front on the
+// winning lane).  Results are uniform across the wave.
+__device__ __forceinline__ void wave_top8(float (&tv)[kTop], int (&ti)[kTop], float (&ov)[kTop],
+                                          int (&oi)[kTop]) {
+#pragma unroll
+  for (int k = 0; k < kTop; ++k) {
+    float v = tv[0];
+    int id = ti[0];
+    wave_best(v, id);
+    ov[k] = v;
+    oi[k] = id;
+    if (tv[0] == v && ti[0] == id) {
+#pragma unroll
+      for (int j = 0; j < kTop - 1; ++j) {
+        tv[j] = tv[j + 1];
+        ti[j] = ti[j + 1];
+      }
+      tv[kTop - 1] = -INFINITY;
+      ti[kTop - 1] = INT_MAX;
+    }
+  }
+}
+
+__device__ __forceinline__ void insert_top8(float (&tv)[kTop], int (&ti)[kTop], float v, int id) {
+  // ids reach a thread in increasing order, so an equal value never displaces
+  // an entry already kept (that entry has the smaller id).
+  if (!(v > tv[kTop - 1])) return;
+  bool carry = false;
+  float cv = v;
+  int ci = id;
+#pragma unroll
+  for (int k = 0; k < kTop; ++k) {
+    const bool take = carry || cv > tv[k];
+    if (take) {
+      const float tvk = tv[k];
+      const int tik = ti[k];
+      tv[k] = cv;
+      ti[k] = ci;
+      cv = tvk;
+      ci = tik;
+      carry = true;
+    }
+  }
+}
+
+// part_f [rows][n_split][2 + 8] = (max, sum exp(z - max), top-8 values);
+// part_i [rows][n_split][8] = top-8 ids.
+__global__ __launch_bounds__(kThreads) void vocab_partial_kernel(
+    const float* __restrict__ logits, int V, int n_split, int chunk, const int* __restrict__ plant_id,
+    const float* __restrict__ plant_bias, int mask_id, float* __restrict__ part_f,
+    int* __restrict__ part_i) {
+  __shared__ float s_m[kThreads / 64], s_s[kThreads / 64];
+  __shared__ float s_tv[kThreads / 64][kTop];
+  __shared__ int s_ti[kThreads / 64][kTop];
+  const int split = blockIdx.x;
+  const int row = blockIdx.y;
+  const int c0 = split * chunk;
+  const int c1 = min(V, c0 + chunk);
+  const int pid = plant_id ? plant_id[row] : -1;
+  const float pb = plant_bias ? plant_bias[row] : 0.f;
+  const float* z = logits + (size_t)row * V;
+
+  float m = -INFINITY, s = 0.f;
+  float tv[kTop];
+  int ti[kTop];
+#pragma unroll
+  for (int k = 0; k < kTop; ++k) {
+    tv[k] = -INFINITY;
+    ti[k] = INT_MAX;
+  }
+  for (int base = c0 + 4 * threadIdx.x; base < c1; base += 4 * kThreads) {
+    float4 x4;
+    if (base + 3 < c1) {
+      x4 = *reinterpret_cast<const float4*>(z + base);
+    } else {
+      x4.x = z[base];
+      x4.y = base + 1 < c1 ? z[base + 1] : -INFINITY;
+      x4.z = base + 2 < c1 ? z[base + 2] : -INFINITY;
+      x4.w = -INFINITY;
+    }
+    float xs[4] = {x4.x, x4.y, x4.z, x4.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int id = base + e;
+      float v = xs[e];
+      if (id == pid) v += pb;
+      if (id == mask_id || id >= c1) v = -INFINITY;
+      if (v == -INFINITY) continue;
+      if (v > m) {
+        s = s * exp2f((m - v) * kLog2e) + 1.f;
+        m = v;
+      } else {
+        s += exp2f((v - m) * kLog2e);
+      }
+      insert_top8(tv, ti, v, id);
+    }
+  }
+  // workgroup merge: (max, sum) then top-8
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  float wm = wave_max(m);
+  float ws = (m == -INFINITY) ? 0.f : s * exp2f((m - wm) * kLog2e);
+  ws = wave_sum(ws);
+  float ov[kTop];
+  int oi[kTop];
+  wave_top8(tv, ti, ov, oi);
+  if (lane == 0) {
+    s_m[wave] = wm;
+    s_s[wave] = ws;
+#pragma unroll
+    for (int k = 0; k < kTop; ++k) {
+      s_tv[wave][k] = ov[k];
+      s_ti[wave][k] = oi[k];
+    }
+  }
+  __syncthreads();
+  if (wave != 0) return;
+  float bm = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < kThreads / 64; ++w) bm = fmaxf(bm, s_m[w]);
+  float bs = 0.f;
+#pragma unroll
+  for (int w = 0; w < kThreads / 64; ++w)
+    if (s_m[w] != -INFINITY) bs += s_s[w] * exp2f((s_m[w] - bm) * kLog2e);
+  // 32 candidates, one per lane (lanes 32..63 empty): extract 8 in order
+  float cv = -INFINITY;
+  int ci = INT_MAX;
+  if (lane < (kThreads / 64) * kTop) {
+    cv = s_tv[lane / kTop][lane % kTop];
+    ci = s_ti[lane / kTop][lane % kTop];
+  }
+  float* pf = part_f + ((size_t)row * n_split + split) * (2 + kTop);
+  int* pi = part_i + ((size_t)row * n_split + split) * kTop;
+#pragma unroll
+  for (int k = 0; k < kTop; ++k) {
+    float v = cv;
+    int id = ci;
+    wave_best(v, id);
+    if (cv == v && ci == id) {
+      cv = -INFINITY;
+      ci = INT_MAX;
+    }
+    if (lane == 0) {
+      pf[2 + k] = v;
+      pi[k] = id;
+    }
+  }
+  if (lane == 0) {
+    pf[0] = bm;
+    pf[1] = bs;
+  }
+}
+
+// One wave per row: merge the splits (lane = split) and emit the statistics.
+__global__ __launch_bounds__(64) void vocab_merge_kernel(int rows, int n_split,
+                                                         const float* __restrict__ part_f,
+                                                         const int* __restrict__ part_i,
+                                                         int* __restrict__ argmax,
+                                                         float* __restrict__ conf,
+                                                         float* __restrict__ lse,
+                                                         int* __restrict__ topk_id,
+                                                         float* __restrict__ topk_p) {
+  const int row = blockIdx.x;
+  const int lane = threadIdx.x;
+  float m = -INFINITY, s = 0.f;
+  float tv[kTop];
+  int ti[kTop];
+#pragma unroll
+  for (int k = 0; k < kTop; ++k) {
+    tv[k] = -INFINITY;
+    ti[k] = INT_MAX;
+  }
+  if (lane < n_split) {
+    const float* pf = part_f + ((size_t)row * n_split + lane) * (2 + kTop);
+    const int* pi = part_i + ((size_t)row * n_split + lane) * kTop;
+    m = pf[0];
+    s = pf[1];
+#pragma unroll
+    for (int k = 0; k < kTop; ++k) {
+      tv[k] = pf[2 + k];
+      ti[k] = pi[k];
+    }
+  }
+  const float M = wave_max(m);
+  const float Z = wave_sum(m == -INFINITY ? 0.f : s * exp2f((m - M) * kLog2e));
+  float ov[kTop];
+  int oi[kTop];
+  wave_top8(tv, ti, ov, oi);
+  if (lane < kTop) {
+    float v = ov[0];
+    int id = oi[0];
+#pragma unroll
+    for (int k = 1; k < kTop; ++k)
+      if (lane == k) {
+        v = ov[k];
+        id = oi[k];
+      }
+    topk_id[(size_t)row * kTop + lane] = id;
+    topk_p[(size_t)row * kTop + lane] = exp2f((v - M) * kLog2e) / Z;
+  }
+  if (lane == 0) {
+    argmax[row] = oi[0];
+    conf[row] = 1.f / Z;
+    lse[row] = M + logf(Z);
+  }
+}
+
+}  // namespace
+
+VocabPlan plan_vocab(int rows, int V, int target_wgs) {
+  VocabPlan p{};
+  int ns = (target_wgs + rows - 1) / rows;
+  const int max_ns = (V + 2047) / 2048;        // at least ~2K entries per split
+  if (ns > max_ns) ns = max_ns;
+  if (ns > 64) ns = 64;
+  if (ns < 1) ns = 1;
+  int chunk = (V + ns - 1) / ns;
+  chunk = (chunk + 3) / 4 * 4;                 // float4-aligned splits
+  p.chunk = chunk;
+  p.n_split = (V + chunk - 1) / chunk;
+  return p;
+}
+
+size_t vocab_scratch_bytes(const VocabPlan& p, int rows) {
+  return (size_t)rows * p.n_split * ((2 + kTop) * sizeof(float) + kTop * sizeof(int));
+}
+
+hipError_t launch_vocab_stats(const VocabPlan& p, const float* logits, int rows, int V,
+                              const int* plant_id, const float* plant_bias, int mask_id,
+                              void* scratch, int* argmax, float* conf, float* lse, int* topk_id,
+                              float* topk_p, hipStream_t st) {
+  if (rows <= 0) return hipSuccess;
+  float* part_f = static_cast<float*>(scratch);
+  int* part_i = reinterpret_cast<int*>(part_f + (size_t)rows * p.n_split * (2 + kTop));
+  hipLaunchKernelGGL(vocab_partial_kernel, dim3(p.n_split, rows), dim3(kThreads), 0, st, logits, V,
+                     p.n_split, p.chunk, plant_id, plant_bias, mask_id, part_f, part_i);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(vocab_merge_kernel, dim3(rows), dim3(64), 0, st, rows, p.n_split, part_f,
+                     part_i, argmax, conf, lse, topk_id, topk_p);
+  return hipGetLastError();
+}
+
+}  // namespace dinfer

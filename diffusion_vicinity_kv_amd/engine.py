@@ -1,0 +1,182 @@
+"""Engine: one libdinfer context over torch-owned device memory.
+
+PyTorch only allocates device memory and provides the stream; every step of
+the method runs in the HIP library behind the C ABI.
+"""
+from __future__ import annotations
+
+import ctypes as C
+
+import torch
+
+from . import binding as B
+
+
+def _model_struct(m) -> B.ModelCfg:
+    s = B.ModelCfg()
+    for f in ("n_layers", "d_model", "n_heads", "head_dim", "ffn_dim", "vocab", "mask_id",
+              "n_experts", "top_k", "expert_ffn", "shared_ffn"):
+        setattr(s, f, int(getattr(m, f)))
+    s.rope_theta = float(m.rope_theta)
+    s.rms_eps = float(m.rms_eps)
+    s.dtype = B.F32 if m.dtype == "f32" else B.BF16
+    return s
+
+
+def _decode_struct(d, graph_unroll: int) -> B.DecodeCfg:
+    s = B.DecodeCfg()
+    s.block_len = int(d.block_len)
+    s.vicinity_w = int(d.vicinity_w)
+    s.tau = float(d.tau)
+    s.credit_weight = float(d.credit_weight)
+    s.credit_decay = float(d.credit_decay)
+    s.credit_kappa = float(d.credit_kappa)
+    s.smooth_alpha = float(d.smooth_alpha)
+    s.smooth_topk = int(d.smooth_topk)
+    s.hierarchical = int(bool(d.hierarchical))
+    s.graph_unroll = int(graph_unroll)
+    return s
+
+
+class Engine:
+    """A denoising-step context.
+
+    weights: dict in the library's layouts (see include/dinfer.h), device tensors.
+    """
+
+    def __init__(self, model_cfg, decode_cfg, weights, max_batch, max_len, graph_unroll=0,
+                 stream=None):
+        self.lib = B.load()
+        self.m = model_cfg
+        self.d = decode_cfg
+        self.max_batch = int(max_batch)
+        self.max_len = int(max_len)
+        self.stream = stream if stream is not None else torch.cuda.current_stream()
+        self._mc = _model_struct(model_cfg)
+        self._dc = _decode_struct(decode_cfg, graph_unroll)
+        self._weights = weights
+        nl = model_cfg.n_layers
+        arr = C.c_void_p * nl
+
+        def per_layer(key):
+            vals = [B.ptr(weights["layers"][i].get(key)) if weights["layers"][i] else 0
+                    for i in range(nl)]
+            return arr(*vals)
+
+        self._arrays = {k: per_layer(k) for k in ("attn_norm", "wqkv", "wo", "ffn_norm",
+                                                  "w_gate_up", "w_down")}
+        w = B.Weights()
+        w.tok_emb = B.ptr(weights["tok_emb"])
+        w.final_norm = B.ptr(weights["final_norm"])
+        w.lm_head = B.ptr(weights["lm_head"])
+        for k, a in self._arrays.items():
+            setattr(w, k, C.cast(a, B._PP))
+        self._w = w
+        nbytes = self.lib.dinfer_workspace_bytes(C.byref(self._mc), C.byref(self._dc),
+                                                 self.max_batch, self.max_len)
+        if nbytes == 0:
+            raise B.DinferError(B.E_ARG, "dinfer_workspace_bytes", "configuration rejected")
+        self.ws_bytes = int(nbytes)
+        raw = torch.empty(self.ws_bytes + 256, dtype=torch.uint8, device="cuda")
+        off = (-raw.data_ptr()) % 256
+        self._raw = raw
+        self.workspace = raw[off: off + self.ws_bytes]
+        ctx = C.c_void_p()
+        st = self.lib.dinfer_step_init(C.byref(self._mc), C.byref(self._dc), C.byref(self._w),
+                                       self.max_batch, self.max_len, B.ptr(self.workspace),
+                                       self.ws_bytes, B.stream_handle(self.stream), C.byref(ctx))
+        B.check(st, "dinfer_step_init")
+        self.ctx = ctx
+        self.batch = 0
+
+    # -- calls ---------------------------------------------------------------
+    def set_batch(self, tokens, prompt_len, gen_len, plant_id=None, plant_bias=None,
+                  router_bias=None):
+        """tokens: device int32 [batch][max_len] (updated in place)."""
+        assert tokens.dtype == torch.int32 and tokens.is_cuda and tokens.is_contiguous()
+        assert tokens.shape[1] == self.max_len
+        batch = tokens.shape[0]
+        P = (C.c_int32 * batch)(*[int(x) for x in prompt_len])
+        G = (C.c_int32 * batch)(*[int(x) for x in gen_len])
+        self._batch_refs = (tokens, plant_id, plant_bias, router_bias)
+        st = self.lib.dinfer_set_batch(self.ctx, batch, B.ptr(tokens), P, G, B.ptr(plant_id),
+                                       B.ptr(plant_bias), B.ptr(router_bias))
+        B.check(st, "dinfer_set_batch")
+        self.batch = batch
+        self.tokens = tokens
+
+    def refresh_kv(self, mask=None):
+        m = None if mask is None else (C.c_uint8 * self.batch)(*[1 if x else 0 for x in mask])
+        B.check(self.lib.dinfer_refresh_kv(self.ctx, m), "dinfer_refresh_kv")
+
+    def denoise_step(self):
+        B.check(self.lib.dinfer_denoise_step(self.ctx), "dinfer_denoise_step")
+
+    def commit(self):
+        B.check(self.lib.dinfer_commit(self.ctx), "dinfer_commit")
+
+    def advance_blocks(self):
+        need = (C.c_uint8 * max(self.batch, 1))()
+        unf = C.c_int32()
+        B.check(self.lib.dinfer_advance_blocks(self.ctx, need, C.byref(unf)),
+                "dinfer_advance_blocks")
+        return [bool(need[i]) for i in range(self.batch)], int(unf.value)
+
+    def step_graph(self, n_steps):
+        B.check(self.lib.dinfer_step_graph(self.ctx, int(n_steps)), "dinfer_step_graph")
+
+    def run_to_completion(self, max_steps=1 << 30):
+        s = B.RunStats()
+        B.check(self.lib.dinfer_run_to_completion(self.ctx, int(max_steps), C.byref(s)),
+                "dinfer_run_to_completion")
+        return {"steps": s.steps, "refreshes": s.refreshes, "committed": s.committed,
+                "wall_ms": s.wall_ms, "refresh_ms": s.refresh_ms}
+
+    # -- state views -----------------------------------------------------------
+    def view(self):
+        """Torch views (no copies) of the context's state buffers."""
+        v = B.StepView()
+        B.check(self.lib.dinfer_get_step_view(self.ctx, C.byref(v)), "dinfer_get_step_view")
+        base = self.workspace.data_ptr()
+        R = self.batch * v.block_len
+        K = v.topk
+
+        def t(addr, n, dtype, shape):
+            off = addr - base
+            nb = n * torch.tensor([], dtype=dtype).element_size()
+            return self.workspace[off: off + nb].view(dtype).view(*shape)
+
+        es = 4 if self.m.dtype == "f32" else 2
+        kvdt = torch.float32 if es == 4 else torch.bfloat16
+        kv_n = self.m.n_layers * self.max_batch * self.m.n_heads * self.max_len * self.m.head_dim
+        kv_shape = (self.m.n_layers, self.max_batch, self.m.n_heads, self.max_len, self.m.head_dim)
+        return {
+            "logits": t(v.logits, R * v.vocab, torch.float32, (R, v.vocab)),
+            "argmax": t(v.argmax, R, torch.int32, (R,)),
+            "conf": t(v.conf, R, torch.float32, (R,)),
+            "lse": t(v.lse, R, torch.float32, (R,)),
+            "topk_id": t(v.topk_id, R * K, torch.int32, (R, K)),
+            "topk_p": t(v.topk_p, R * K, torch.float32, (R, K)),
+            "credit": t(v.credit, R, torch.float32, (R,)),
+            "tracked": t(v.tracked, R, torch.int32, (R,)),
+            "smooth_id": t(v.smooth_id, R * K, torch.int32, (R, K)),
+            "smooth_p": t(v.smooth_p, R * K, torch.float32, (R, K)),
+            "smooth_valid": t(v.smooth_valid, R, torch.uint8, (R,)),
+            "commit_mask": t(v.commit_mask, R, torch.uint8, (R,)),
+            "block_done": t(v.block_done, self.batch, torch.int32, (self.batch,)),
+            "step_count": t(v.step_count, self.batch, torch.int32, (self.batch,)),
+            "commit_count": t(v.commit_count, self.batch, torch.int32, (self.batch,)),
+            "kv_k": t(v.kv_k, kv_n, kvdt, kv_shape),
+            "kv_v": t(v.kv_v, kv_n, kvdt, kv_shape),
+        }
+
+    def close(self):
+        if getattr(self, "ctx", None) is not None and self.ctx.value:
+            self.lib.dinfer_destroy(self.ctx)
+            self.ctx = C.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

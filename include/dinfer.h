@@ -1,0 +1,263 @@
+/*
+ * dinfer.h -- C ABI of the MI355X (gfx950) denoising-step library.
+ *
+ * One denoising iteration of a masked-diffusion LM over the current block:
+ * vicinity KV refresh, bidirectional attention over the full cached KV, the
+ * LM head with fused vocab softmax / max-probability / argmax / top-k, and the
+ * parallel-decode commit (threshold, credit, top-1 fallback, optional
+ * hierarchical midpoint order, iteration smoothing).
+ *
+ * Sources (page titles; sections):
+ *   dInfer abstract, "dInfer: An Efficient Inference Framework for Diffusion
+ *     Language Models": four components -- model, diffusion iteration manager,
+ *     decoding strategy, KV-cache manager.  The calls below follow them:
+ *     model + KV manager -> dinfer_refresh_kv / dinfer_denoise_step,
+ *     decoding strategy -> dinfer_commit, iteration manager ->
+ *     dinfer_advance_blocks / dinfer_run_to_completion.
+ *   dInfer news article (aigc.bar), section "削减计算成本：邻近KV缓存刷新"
+ *     (vicinity KV refresh), section "解码的艺术" (hierarchical, credit,
+ *     smoothing), section "系统级压榨" (loop unrolling against iteration
+ *     bubbles: dinfer_run_to_completion replays several steps per graph).
+ *   Sangam abstract, "Sangam: Efficiently Serving Diffusion LLMs with the AR
+ *     Stack": cached KV is refreshed and reused across block-sized decodes.
+ *
+ * Conventions for every call:
+ *   - Pointers named d_* are device pointers, h_* are host pointers.
+ *   - The library never allocates device memory: the caller owns the weights,
+ *     token buffer and workspace, which must outlive the context.  The
+ *     library borrows them.
+ *   - Calls enqueue work on the context's stream and return without waiting,
+ *     except dinfer_advance_blocks and dinfer_run_to_completion, which wait.
+ *   - Errors are returned as dinfer_status; no exception or abort crosses the
+ *     ABI.  A kernel fault surfaces as DINFER_E_HIP at the next waiting call.
+ *   - A context is used from one host thread at a time.
+ *
+ * Layouts (row-major, no padding):
+ *   Linear weights are [out][in].  tok_emb, lm_head [V][d]; wqkv [3d][d] with
+ *   rows q | k | v, head-major (head h owns rows h*hd .. h*hd+hd-1 of each);
+ *   w_gate_up [2F][d] with rows gate | up; w_down [d][F]; norms [d].
+ *   MoE: router [E][d], exp_gate_up [E][2Fe][d], exp_down [E][d][Fe],
+ *   shared_gate_up [2Fs][d], shared_down [d][Fs].
+ *   Element type: float for DINFER_F32, bfloat16 for DINFER_BF16 (all
+ *   weights of one model share it).
+ */
+#ifndef DINFER_H
+#define DINFER_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct dinfer_ctx dinfer_ctx;
+
+typedef enum {
+  DINFER_OK = 0,
+  DINFER_E_ARG = 1,          /* bad argument (null, out of range, inconsistent) */
+  DINFER_E_WORKSPACE = 2,    /* workspace too small or misaligned               */
+  DINFER_E_STATE = 3,        /* call out of order (e.g. denoise before refresh) */
+  DINFER_E_HIP = 4,          /* a HIP runtime call failed                       */
+  DINFER_E_UNSUPPORTED = 5   /* shape or option this build does not support     */
+} dinfer_status;
+
+typedef enum { DINFER_F32 = 0, DINFER_BF16 = 1 } dinfer_dtype;
+
+/* Model: a bidirectional (non-causal) pre-norm transformer with RoPE,
+ * RMSNorm and SwiGLU; n_experts == 0 selects the dense FFN. */
+typedef struct {
+  int32_t n_layers, d_model, n_heads, head_dim, ffn_dim, vocab, mask_id;
+  int32_t n_experts, top_k, expert_ffn, shared_ffn;
+  float rope_theta, rms_eps;
+  int32_t dtype;             /* dinfer_dtype */
+} dinfer_model_cfg;
+
+/* Decoding strategy (dInfer news article, section "解码的艺术"). */
+typedef struct {
+  int32_t block_len;         /* B: positions per block, 1..64                    */
+  int32_t vicinity_w;        /* w: window = [max(0,bs-w), min(L,be+w))           */
+  float tau;                 /* confidence threshold, inclusive                  */
+  float credit_weight;       /* lambda; 0 = plain threshold decoding             */
+  float credit_decay;        /* gamma                                            */
+  float credit_kappa;        /* credit gate, inclusive                           */
+  float smooth_alpha;        /* 0 = no iteration smoothing                       */
+  int32_t smooth_topk;       /* must be 8                                        */
+  int32_t hierarchical;      /* 1 = only run midpoints are candidates            */
+  int32_t graph_unroll;      /* steps per captured graph in run_to_completion;
+                                0 = launch eagerly                               */
+} dinfer_decode_cfg;
+
+/* Device pointers to the weights (borrowed).  Per-layer entries are host
+ * arrays of n_layers device pointers; unused families may be NULL. */
+typedef struct {
+  const void* tok_emb;
+  const void* final_norm;
+  const void* lm_head;
+  const void* const* attn_norm;
+  const void* const* wqkv;
+  const void* const* wo;
+  const void* const* ffn_norm;
+  const void* const* w_gate_up;
+  const void* const* w_down;
+  const void* const* router;
+  const void* const* exp_gate_up;
+  const void* const* exp_down;
+  const void* const* shared_gate_up;
+  const void* const* shared_down;
+} dinfer_weights;
+
+typedef struct {
+  int64_t steps;             /* denoise+commit steps launched                    */
+  int64_t refreshes;         /* per-request block-start refreshes                */
+  int64_t committed;         /* tokens committed over all requests               */
+  double wall_ms;            /* wall time of the call                            */
+  double refresh_ms;         /* part of wall_ms spent in refreshes (event-timed) */
+} dinfer_run_stats;
+
+/* Device pointers into the context's state, for inspection and tests.  All
+ * buffers are indexed by request r < batch and block offset j < block_len:
+ * row index = r * block_len + j. */
+typedef struct {
+  int32_t batch, block_len, vocab, topk;
+  float* logits;             /* [batch*B][V] fp32 logits of the block rows (before
+                                planting bias and MASK exclusion)               */
+  int32_t* argmax;           /* [batch*B]                                        */
+  float* conf;               /* [batch*B] max softmax probability                */
+  float* lse;                /* [batch*B] log-sum-exp                            */
+  int32_t* topk_id;          /* [batch*B][8]                                     */
+  float* topk_p;             /* [batch*B][8] softmax probabilities               */
+  float* credit;             /* [batch*B]                                        */
+  int32_t* tracked;          /* [batch*B] argmax tracked by credit (-1 = none)   */
+  int32_t* smooth_id;        /* [batch*B][8] smoothing ids                       */
+  float* smooth_p;           /* [batch*B][8] renormalised smoothing probs        */
+  uint8_t* smooth_valid;     /* [batch*B]                                        */
+  uint8_t* commit_mask;      /* [batch*B] 1 = committed by the last commit       */
+  int32_t* block_done;       /* [batch] 1 once the current block has no MASK     */
+  int32_t* step_count;       /* [batch] steps taken in the current block         */
+  int32_t* commit_count;     /* [batch] tokens committed in total                */
+  void* kv_k;                /* [n_layers][max_batch][H][max_len][hd] K, RoPE'd */
+  void* kv_v;                /* [n_layers][max_batch][H][max_len][hd]            */
+} dinfer_step_view;
+
+/* Bytes of workspace dinfer_step_init needs for these shapes (0 on bad args). */
+size_t dinfer_workspace_bytes(const dinfer_model_cfg* model, const dinfer_decode_cfg* dec,
+                              int32_t max_batch, int32_t max_len);
+
+/* Validate the configuration, carve the caller's workspace (256-byte aligned,
+ * at least dinfer_workspace_bytes), build the RoPE tables and bind the
+ * stream (a hipStream_t; NULL = the default stream).  *out receives the
+ * context.  Model and KV-cache manager set-up (dInfer abstract). */
+dinfer_status dinfer_step_init(const dinfer_model_cfg* model, const dinfer_decode_cfg* dec,
+                               const dinfer_weights* weights, int32_t max_batch, int32_t max_len,
+                               void* d_workspace, size_t ws_bytes, void* stream,
+                               dinfer_ctx** out);
+
+/* Bind a batch of requests.  d_tokens [batch][max_len] int32 holds each
+ * request's prompt then MASK positions and is updated in place by commits.
+ * h_prompt_len / h_gen_len [batch]: gen_len must be a multiple of block_len
+ * and prompt_len + gen_len <= max_len.  d_plant_id [batch][max_len] int32
+ * (-1 = no planting) and d_plant_bias [batch] float: the planted target of a
+ * position gets +bias on its raw logit before the vocab statistics.
+ * d_router_bias (MoE only, else NULL): [batch][n_layers][gen_len/B][E] float
+ * added to the router logits of every row during that block.
+ * Every request starts at block 0; call dinfer_refresh_kv next. */
+dinfer_status dinfer_set_batch(dinfer_ctx* ctx, int32_t batch, int32_t* d_tokens,
+                               const int32_t* h_prompt_len, const int32_t* h_gen_len,
+                               const int32_t* d_plant_id, const float* d_plant_bias,
+                               const float* d_router_bias);
+
+/* KV-cache manager, full refresh (Sangam abstract: cached KV is refreshed and
+ * reused across the decodes in between).  For every selected request
+ * (h_req_mask[r] != 0; NULL = every request with an unfinished block):
+ * recompute K and V of all its positions from hard embeddings, and start its
+ * current block (credit, tracked ids and smoothing state cleared). */
+dinfer_status dinfer_refresh_kv(dinfer_ctx* ctx, const uint8_t* h_req_mask);
+
+/* Model + vicinity refresh (dInfer news article, section
+ * "削减计算成本：邻近KV缓存刷新"): for every active request, the window rows
+ * run through all layers; per layer their fresh K,V are written into the
+ * cache before they attend over all cached positions (no causal mask).  The
+ * block rows then go through the final norm, the LM head and the vocab
+ * statistics (planting bias, MASK excluded, argmax lowest id on ties,
+ * max-probability, log-sum-exp, top-8).  Results: dinfer_get_step_view. */
+dinfer_status dinfer_denoise_step(dinfer_ctx* ctx);
+
+/* Decoding strategy (dInfer news article, section "解码的艺术"): per active
+ * request, credit update of every still-masked block position
+ * c <- (argmax == tracked ? gamma*c : 0) + lambda*p (fp32, two roundings),
+ * candidates (all masked positions, or the midpoints of maximal masked runs
+ * when hierarchical), commit every candidate with p >= tau or c >= kappa,
+ * else the single candidate of highest p (lowest position on ties); write
+ * the committed ids into d_tokens; keep each still-masked position's top-8
+ * (renormalised) for the next step's soft embedding; set block_done when the
+ * block holds no MASK. */
+dinfer_status dinfer_commit(dinfer_ctx* ctx);
+
+/* Iteration manager, block bookkeeping: waits for the stream, then for every
+ * request whose block is done moves to its next block (or marks it
+ * finished).  h_needs_refresh[r] (may be NULL) is set to 1 for requests that
+ * moved to a new block and must be refreshed before the next step.
+ * *h_unfinished (may be NULL) receives the number of unfinished requests. */
+dinfer_status dinfer_advance_blocks(dinfer_ctx* ctx, uint8_t* h_needs_refresh,
+                                    int32_t* h_unfinished);
+
+/* Iteration manager: run every request of the batch to completion --
+ * refresh at each block start, then denoise+commit steps replayed
+ * graph_unroll at a time from a captured HIP graph (one host wait per
+ * replay), until every block of every request is committed or max_steps
+ * steps ran (DINFER_E_STATE then).  h_stats may be NULL. */
+dinfer_status dinfer_run_to_completion(dinfer_ctx* ctx, int32_t max_steps,
+                                       dinfer_run_stats* h_stats);
+
+/* Fill *out with device pointers into the context's state. */
+dinfer_status dinfer_get_step_view(const dinfer_ctx* ctx, dinfer_step_view* out);
+
+/* Launch n_steps denoise+commit steps without waiting and without block
+ * bookkeeping: the captured graph of graph_unroll steps (captured on first
+ * use) is replayed n_steps / graph_unroll times (n_steps must be a multiple
+ * of graph_unroll, graph_unroll > 0).  Requests whose block completes
+ * mid-way stop committing (their window is still recomputed).  The loop
+ * unrolling of the dInfer news article, section "系统级压榨". */
+dinfer_status dinfer_step_graph(dinfer_ctx* ctx, int32_t n_steps);
+
+/* Standalone projection, the Linear layer every step runs (dtype as the
+ * model's): out[s][m][n] = sum over the s-th K slice of A[m][k] * W[n][k],
+ * A [M][K] and W [N][K] row-major device arrays, out fp32 [splits][M][N]; the
+ * product A W^T is the sum of the splits (taken in split order by the
+ * library's own consumers).  *h_splits (may be NULL) receives the split
+ * count, which dinfer_linear_out_elems also returns through its result:
+ * out must hold dinfer_linear_out_elems(M, N, K, dtype) floats.  Requires
+ * N % 128 == 0 and K % 256 == 0 (bf16) / K % 128 == 0 (f32).  Same kernels
+ * and launch plan as the step for the same M. */
+size_t dinfer_linear_out_elems(int32_t M, int32_t N, int32_t K, int32_t dtype);
+dinfer_status dinfer_linear(const void* d_A, const void* d_W, float* d_out, int32_t M, int32_t N,
+                            int32_t K, int32_t dtype, int32_t* h_splits, void* stream);
+
+/* Standalone vocab statistics over fp32 logits d_logits [rows][vocab]
+ * (the fused LM-head epilogue of dinfer_denoise_step, exposed on its own):
+ * d_plant_id [rows] (-1 none) and d_plant_bias [rows] add the planting bias;
+ * mask_id is excluded (-1 = none).  Outputs: d_argmax [rows], d_conf [rows],
+ * d_lse [rows], d_topk_id [rows][8], d_topk_p [rows][8].  d_scratch must hold
+ * dinfer_vocab_stats_scratch_bytes(rows, vocab) bytes.  Enqueued on stream. */
+size_t dinfer_vocab_stats_scratch_bytes(int32_t rows, int32_t vocab);
+dinfer_status dinfer_vocab_stats(const float* d_logits, int32_t rows, int32_t vocab,
+                                 const int32_t* d_plant_id, const float* d_plant_bias,
+                                 int32_t mask_id, int32_t* d_argmax, float* d_conf,
+                                 float* d_lse, int32_t* d_topk_id, float* d_topk_p,
+                                 void* d_scratch, size_t scratch_bytes, void* stream);
+
+/* Human-readable name of a status; the last error message of the calling
+ * thread is appended by dinfer_last_error. */
+const char* dinfer_status_str(dinfer_status s);
+const char* dinfer_last_error(void);
+
+/* Release the context (host memory, streams and graphs it created).  The
+ * caller's device buffers are untouched. */
+void dinfer_destroy(dinfer_ctx* ctx);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DINFER_H */

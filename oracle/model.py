@@ -102,7 +102,10 @@ class OracleModel:
         self.m = mcfg
         self.n_layers = mcfg.n_layers
         self.layer_ids = list(range(mcfg.n_layers)) if layers is None else list(layers)
-        self.tok_emb = weights.get("tok_emb")     # gathered row by row, upcast on use
+        emb = weights.get("tok_emb")              # gathered row by row, upcast on use
+        if hasattr(emb, "detach"):
+            emb = emb.detach().cpu()
+        self.tok_emb = emb
         self.final_norm = _f64(weights["final_norm"])
         self.lm_head = _f64(weights.get("lm_head"))
         self.layers = {}

@@ -131,7 +131,7 @@ class OracleRun:
         self.smooth_valid = still.copy()
         self.block_steps += 1
         rec = {"block": self.block, "commits": T.copy(), "fallback": fallback,
-               "margin": decision_margin(st, masked, self.credit, d, T)}
+               "margin": decision_margin(st, masked, self.credit, d, T, still)}
         self.records.append(rec)
         return T, fallback
 
@@ -153,30 +153,31 @@ class OracleRun:
         return self.tokens
 
 
-def decision_margin(st, masked, credit, d, committed):
-    """Smallest relative distance of this step's decisions from flipping.
-
-    Reported, not gated.  Over the candidates: |conf - tau| / tau,
-    |credit - kappa| / kappa, the relative gap between the best and second-best
-    confidence (decides the fallback), and each committed row's top-1 minus
-    top-2 logit (decides the committed id).
-    """
+def decision_margin(st, masked, credit, d, committed, still=None):
+    """Smallest distance, in logit (natural-log) units, of this step's decisions
+    from flipping.  Reported, not used by the method.  Over the candidates:
+    |ln p - ln tau|, |ln c - ln kappa| (credit on), ln p1 - ln p2 between the
+    best and second-best confidence (decides the fallback); over committed rows
+    the top-1 minus top-2 logit (decides the committed id); with smoothing on,
+    over rows still masked the 8th minus 9th logit (decides the kept top-8)."""
     from .decode import candidates
     C = candidates(masked, d.hierarchical)
     if len(C) == 0:
         return np.inf
+    tiny = 1e-30
     conf = st["conf"][C].astype(np.float64)
-    c = credit[C].astype(np.float64)
-    m = float(np.min(np.abs(conf - d.tau)) / d.tau)
+    m = float(np.min(np.abs(np.log(conf) - np.log(d.tau))))
     if d.credit_weight != 0.0:
-        m = min(m, float(np.min(np.abs(c - d.credit_kappa)) / d.credit_kappa))
+        c = np.maximum(credit[C].astype(np.float64), tiny)
+        m = min(m, float(np.min(np.abs(np.log(c) - np.log(d.credit_kappa)))))
     if len(C) > 1:
         s = np.sort(conf)[::-1]
-        m = min(m, float((s[0] - s[1]) / s[0]))
+        m = min(m, float(np.log(s[0]) - np.log(max(s[1], tiny))))
     tp = st["topk_p"][committed]
     if tp.shape[1] > 1 and len(committed):
-        gap = np.log(tp[:, 0]) - np.log(tp[:, 1])
-        m = min(m, float(np.min(gap)))
+        m = min(m, float(np.min(np.log(tp[:, 0]) - np.log(np.maximum(tp[:, 1], tiny)))))
+    if d.smooth_alpha != 0.0 and still is not None and still.any() and "kth_gap" in st:
+        m = min(m, float(np.min(st["kth_gap"][still])))
     return float(m)
 
 

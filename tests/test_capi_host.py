@@ -1,0 +1,108 @@
+"""Host-only checks of the C ABI: the library loads, exports every function
+include/dinfer.h declares, and rejects bad configurations before touching a
+GPU (no compute call runs here)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+import synth
+from diffusion_vicinity_kv_amd import binding as B
+from diffusion_vicinity_kv_amd.engine import _decode_struct, _model_struct
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    names = set()
+    for fn in os.listdir(os.path.join(ROOT, "include")):
+        if not fn.endswith(".h"):
+            continue
+        text = open(os.path.join(ROOT, "include", fn)).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        for m in re.finditer(r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?\b(dinfer_\w+)\s*\(", text, re.M):
+            names.add(m.group(1))
+    return names
+
+
+def test_library_exports_every_declared_function():
+    lib = B.load()
+    declared = _declared_functions()
+    assert {"dinfer_step_init", "dinfer_refresh_kv", "dinfer_denoise_step", "dinfer_commit",
+            "dinfer_run_to_completion"} <= declared
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert declared == set(B.EXPORTS)
+
+
+def test_status_strings():
+    for s, name in [(0, "DINFER_OK"), (1, "DINFER_E_ARG"), (2, "DINFER_E_WORKSPACE"),
+                    (3, "DINFER_E_STATE"), (4, "DINFER_E_HIP"), (5, "DINFER_E_UNSUPPORTED")]:
+        assert B.status_name(s) == name
+
+
+def _structs(name="tiny_f32", **mkw):
+    wc = synth.preset(name)
+    m = wc.model if not mkw else wc.with_model(**mkw).model
+    return _model_struct(m), _decode_struct(wc.decode, 0), wc
+
+
+@pytest.mark.parametrize("name", synth.PRESET_ORDER)
+def test_workspace_bytes_positive_for_dense_presets(name):
+    mc, dc, wc = _structs(name)
+    n = B.load().dinfer_workspace_bytes(C.byref(mc), C.byref(dc), wc.batch, wc.max_len)
+    if wc.model.is_moe:
+        assert n == 0          # MoE is rejected by this build
+    else:
+        assert n > 0 and n % 256 == 0
+        # the KV cache alone: 2 * layers * batch * heads * max_len * hd * element size
+        m = wc.model
+        es = 4 if m.dtype == "f32" else 2
+        assert n >= 2 * m.n_layers * wc.batch * m.n_heads * wc.max_len * m.head_dim * es
+
+
+def test_workspace_bytes_rejects_bad_shapes():
+    lib = B.load()
+    for kw in [dict(head_dim=96, d_model=4 * 96), dict(vocab=4098, mask_id=4097),
+               dict(n_heads=3)]:
+        mc, dc, wc = _structs(**kw)
+        assert lib.dinfer_workspace_bytes(C.byref(mc), C.byref(dc), 1, 128) == 0
+    mc, dc, wc = _structs()
+    dc.block_len = 65
+    assert lib.dinfer_workspace_bytes(C.byref(mc), C.byref(dc), 1, 128) == 0
+
+
+def test_step_init_argument_errors_without_gpu():
+    lib = B.load()
+    mc, dc, wc = _structs()
+    w = B.Weights()
+    ctx = C.c_void_p()
+    # null out pointer
+    assert lib.dinfer_step_init(C.byref(mc), C.byref(dc), C.byref(w), 1, 128, None, 0, None,
+                                None) == B.E_ARG
+    # MoE model: unsupported in this build
+    mc2, dc2, _ = _structs(n_experts=64, top_k=8, expert_ffn=1024, shared_ffn=2048)
+    assert lib.dinfer_step_init(C.byref(mc2), C.byref(dc2), C.byref(w), 1, 128, None, 0, None,
+                                C.byref(ctx)) == B.E_UNSUPPORTED
+    # missing weights
+    assert lib.dinfer_step_init(C.byref(mc), C.byref(dc), C.byref(w), 1, 128, None, 0, None,
+                                C.byref(ctx)) == B.E_ARG
+    assert b"weight" in lib.dinfer_last_error()
+
+
+def test_vocab_stats_argument_errors_without_gpu():
+    lib = B.load()
+    assert lib.dinfer_vocab_stats(None, 4, 4096, None, None, -1, None, None, None, None, None,
+                                  None, 0, None) == B.E_ARG
+    assert lib.dinfer_vocab_stats_scratch_bytes(32, 126464) > 0
+    assert lib.dinfer_vocab_stats_scratch_bytes(0, 126464) == 0
+
+
+def test_calls_on_null_context_fail_cleanly():
+    lib = B.load()
+    assert lib.dinfer_denoise_step(None) == B.E_ARG
+    assert lib.dinfer_commit(None) == B.E_ARG
+    assert lib.dinfer_refresh_kv(None, None) == B.E_ARG
+    assert lib.dinfer_run_to_completion(None, 1, None) == B.E_ARG
+    lib.dinfer_destroy(None)

@@ -1,0 +1,241 @@
+"""GPU parity: the HIP library through its C ABI against the CPU oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from diffusion_vicinity_kv_amd import binding as B
+from oracle.decode import credit_update, select_commits, smoothing_state, vocab_stats
+
+from gpu_util import build, compare_cache, lockstep, note, oracle_runs, small_workload
+
+pytestmark = pytest.mark.gpu
+
+
+# --------------------------------------------------------------- vocab stats (K3)
+@pytest.mark.parametrize("rows,V,ties", [(32, 4096, 0), (37, 4096, 3), (32, 126464, 0),
+                                         (512, 126464, 2), (64, 157184, 0), (5, 1000, 0)])
+def test_vocab_stats_parity(rows, V, ties):
+    note(f"vocab_stats rows={rows} V={V} ties={ties}")
+    z = synth.make_logits(rows, V, seed=rows + V, ties=ties, device="cuda")
+    g = torch.Generator().manual_seed(rows)
+    pid = torch.where(torch.rand(rows, generator=g) < 0.6,
+                      torch.randint(0, V - 1, (rows,), generator=g), torch.full((rows,), -1))
+    pid = pid.to(torch.int32)
+    pb = torch.full((rows,), 8.0)
+    pb[::3] = 2.5
+    mask_id = V - 1
+    z[:, mask_id] = 50.0                     # the MASK column must never win
+    lib = B.load()
+    scratch = torch.empty(lib.dinfer_vocab_stats_scratch_bytes(rows, V), dtype=torch.uint8,
+                          device="cuda")
+    out = {"argmax": torch.empty(rows, dtype=torch.int32, device="cuda"),
+           "conf": torch.empty(rows, device="cuda"), "lse": torch.empty(rows, device="cuda"),
+           "topk_id": torch.empty(rows, 8, dtype=torch.int32, device="cuda"),
+           "topk_p": torch.empty(rows, 8, device="cuda")}
+    B.vocab_stats(z, pid.cuda(), pb.cuda(), mask_id, out, scratch)
+    torch.cuda.synchronize()
+    want = vocab_stats(z.cpu().numpy(), pid.numpy(), pb.numpy(), mask_id, 8)
+    assert np.array_equal(out["argmax"].cpu().numpy(), want["argmax"])
+    assert np.array_equal(out["topk_id"].cpu().numpy(), want["topk_id"])
+    assert np.allclose(out["conf"].cpu().numpy(), want["conf"], rtol=2e-5, atol=0)
+    assert np.allclose(out["lse"].cpu().numpy(), want["lse"], rtol=0, atol=2e-5 * np.abs(want["lse"]).max())
+    assert np.allclose(out["topk_p"].cpu().numpy(), want["topk_p"], rtol=2e-5, atol=1e-12)
+
+
+# --------------------------------------------------------------- commit (K8)
+@pytest.mark.parametrize("hier", [False, True])
+@pytest.mark.parametrize("B_len", [32, 64, 7])
+def test_commit_parity_on_synthetic_stats(hier, B_len):
+    """Selector bit-exactness: both sides get the same synthetic stats, credit,
+    tracked ids and masked patterns (exact threshold values and ties included)."""
+    note(f"commit hier={hier} B={B_len}")
+    wc = small_workload(batch=3, B=B_len, gen=B_len * 2, prompt=(70, 70), hier=hier, w=4)
+    eng, w, req, tokens = build(wc)
+    rng = np.random.default_rng(B_len + 10 * hier)
+    tau, kappa = np.float32(wc.decode.tau), np.float32(wc.decode.credit_kappa)
+    mask_id = wc.model.mask_id
+    for trial in range(25):
+        eng.refresh_kv()
+        eng.denoise_step()
+        torch.cuda.synchronize()
+        v = eng.view()
+        R = wc.batch * B_len
+        masked = rng.random((wc.batch, B_len)) < rng.choice([0.2, 0.6, 1.0])
+        if trial % 5 == 0:
+            masked[0] = False                  # a block with nothing left
+        am = rng.integers(0, 5, R).astype(np.int32)
+        choices = np.float32([tau, np.nextafter(tau, np.float32(0)), 0.5, 0.3, 0.95, 0.05, 0.3])
+        conf = rng.choice(choices, R).astype(np.float32)
+        credit = rng.choice(np.float32([0.0, 1.2, kappa, np.nextafter(kappa, np.float32(0)), 0.8]),
+                            R).astype(np.float32)
+        tracked = np.where(rng.random(R) < 0.5, am, rng.integers(-1, 5, R)).astype(np.int32)
+        tid = rng.integers(0, wc.model.vocab - 1, (R, 8)).astype(np.int32)
+        tp = np.sort(rng.random((R, 8)).astype(np.float32), axis=1)[:, ::-1].copy()
+        bs = 70
+        tok = tokens.cpu().numpy()
+        blk = np.where(masked, mask_id, rng.integers(0, 100, masked.shape)).astype(np.int32)
+        tok[:, bs:bs + B_len] = blk
+        tokens.copy_(torch.from_numpy(tok))
+        v["argmax"].copy_(torch.from_numpy(am))
+        v["conf"].copy_(torch.from_numpy(conf))
+        v["credit"].copy_(torch.from_numpy(credit))
+        v["tracked"].copy_(torch.from_numpy(tracked))
+        v["topk_id"].copy_(torch.from_numpy(tid))
+        v["topk_p"].copy_(torch.from_numpy(tp))
+        eng.commit()
+        torch.cuda.synchronize()
+        gt = tokens.cpu().numpy()
+        for r in range(wc.batch):
+            sl = slice(r * B_len, (r + 1) * B_len)
+            c2, t2 = credit_update(credit[sl], tracked[sl], am[sl], conf[sl], masked[r],
+                                   wc.decode.credit_decay, wc.decode.credit_weight)
+            T, fb = select_commits(masked[r], conf[sl], c2, tau, kappa, hier)
+            want_tok = blk[r].copy()
+            want_tok[T] = am[sl][T]
+            assert np.array_equal(gt[r, bs:bs + B_len], want_tok), (trial, r)
+            gm = v["commit_mask"].cpu().numpy()[sl]
+            om = np.zeros(B_len, np.uint8)
+            om[T] = 1
+            assert np.array_equal(gm, om), (trial, r)
+            assert np.array_equal(v["credit"].cpu().numpy()[sl].view(np.uint32),
+                                  c2.view(np.uint32)), (trial, r)
+            assert np.array_equal(v["tracked"].cpu().numpy()[sl], t2), (trial, r)
+            still = masked[r].copy()
+            still[T] = False
+            assert np.array_equal(v["smooth_valid"].cpu().numpy()[sl].astype(bool), still)
+            ids, pt = smoothing_state(tid[sl], tp[sl])
+            gs = v["smooth_p"].cpu().numpy()[sl]
+            gi = v["smooth_id"].cpu().numpy()[sl]
+            assert np.array_equal(gi[still], ids[still])
+            assert np.allclose(gs[still], pt[still], rtol=1e-6)
+            done = int(v["block_done"].cpu().numpy()[r])
+            assert done == int(not still.any())
+
+
+# ----------------------------------------------------- one step and full runs
+def test_tiny_refresh_cache_and_first_step_logits():
+    note("tiny fp32: refresh cache + first step")
+    wc = synth.preset("tiny_f32")
+    eng, w, req, tokens = build(wc)
+    runs = oracle_runs(wc, w, req)
+    runs[0].start_block(0)
+    eng.refresh_kv()
+    compare_cache(wc, eng, runs)
+    eng.denoise_step()
+    torch.cuda.synchronize()
+    ol = runs[0].denoise_logits()
+    gl = eng.view()["logits"].cpu().numpy()
+    err = np.max(np.abs(gl - ol)) / np.sqrt(np.mean(ol ** 2))
+    assert err < 1e-5, err
+    compare_cache(wc, eng, runs)
+
+
+@pytest.mark.parametrize("variant", ["literal", "confident", "credit", "hier"])
+def test_tiny_lockstep_run(variant):
+    note(f"tiny fp32 lockstep {variant}")
+    wc = synth.preset("tiny_f32")
+    if variant == "confident":       # planted p ~ 0.99: the threshold fires
+        wc = wc.with_(plant_bias=6.0 + float(np.log(4094.0)))
+    elif variant == "credit":        # planted p in the credit band below tau
+        wc = wc.with_(plant_bias=6.0 + float(np.log(4094.0)) - 3.3)
+    elif variant == "hier":
+        wc = wc.with_(plant_bias=6.0 + float(np.log(4094.0))).with_decode(hierarchical=True)
+    eng, w, req, tokens = build(wc)
+    runs = oracle_runs(wc, w, req)
+    rep = lockstep(wc, eng, tokens, runs, logit_tol=1e-5, check_cache=True)
+    note(f"  {rep}")
+    assert rep["diverged"] is None
+    assert np.array_equal(tokens.cpu().numpy()[0][: runs[0].L], runs[0].tokens)
+
+
+@pytest.mark.parametrize("unroll", [0, 1, 4])
+def test_tiny_run_to_completion_matches_oracle(unroll):
+    note(f"tiny fp32 run_to_completion unroll={unroll}")
+    wc = synth.preset("tiny_f32")
+    eng, w, req, tokens = build(wc, graph_unroll=unroll)
+    stats = eng.run_to_completion()
+    torch.cuda.synchronize()
+    run = oracle.run_request(wc.model, wc.decode, w, req)
+    assert np.array_equal(tokens.cpu().numpy()[0][: run.L], run.tokens)
+    assert stats["committed"] == wc.gen_len
+    assert stats["refreshes"] == wc.gen_len // wc.decode.block_len
+    assert stats["steps"] >= sum(run.steps)
+
+
+def test_batched_tiny_run_matches_per_request_oracle():
+    note("tiny fp32 batch 3, ragged prompts, graph")
+    wc = small_workload(batch=3, prompt=(40, 90), gen=64, bias=6.0 + float(np.log(4094.0)) - 2.0,
+                        prob=(0.5, 0.9), seed=3)
+    eng, w, req, tokens = build(wc, graph_unroll=3)
+    eng.run_to_completion()
+    torch.cuda.synchronize()
+    for r in range(wc.batch):
+        run = oracle.run_request(wc.model, wc.decode, w, req, r=r)
+        assert np.array_equal(tokens.cpu().numpy()[r][: run.L], run.tokens), r
+
+
+@pytest.mark.parametrize("alpha", [0.0, 0.3])
+def test_bf16_small_lockstep(alpha):
+    note(f"bf16 small lockstep alpha={alpha}")
+    wc = small_workload(dtype="bf16", d=256, H=2, hd=128, F=768, V=4096, batch=2,
+                        prompt=(60, 100), gen=64, w=8, bias=8.0, prob=(0.75, 0.75), seed=5,
+                        alpha=alpha)
+    eng, w, req, tokens = build(wc)
+    runs = oracle_runs(wc, w, req)
+    rep = lockstep(wc, eng, tokens, runs, logit_tol=2e-2, check_cache=True)
+    note(f"  {rep}")
+    assert rep["steps"] >= (16 if alpha == 0.0 else 1)
+
+
+def test_bf16_batch16_fat_step_path_lockstep():
+    note("bf16 batch 16 (fat GEMM in the step) lockstep")
+    wc = small_workload(dtype="bf16", d=512, H=4, hd=128, F=1024, V=8192, batch=16,
+                        prompt=(16, 96), gen=64, B=32, w=16, bias=8.0, prob=(0.5, 0.9), seed=7,
+                        alpha=0.0)
+    eng, w, req, tokens = build(wc)
+    runs = oracle_runs(wc, w, req)
+    rep = lockstep(wc, eng, tokens, runs, logit_tol=2e-2, max_steps=12)
+    note(f"  {rep}")
+    assert rep["steps"] >= 1
+
+
+@pytest.mark.parametrize("preset", ["dense8b_b1"])
+def test_full_width_two_layer_parity(preset):
+    """Full width of the dense 8B shape (d 4096, 32 heads, F 12288, V 126464),
+    two layers: every per-layer kernel runs in the launch configuration of the
+    32-layer benchmark.  Refresh cache and two steps against the oracle."""
+    note(f"full-width 2-layer {preset}")
+    wc = synth.preset(preset).with_model(n_layers=2).with_decode(smooth_alpha=0.0)
+    eng, w, req, tokens = build(wc)
+    runs = oracle_runs(wc, w, req)
+    rep = lockstep(wc, eng, tokens, runs, logit_tol=2e-2, max_steps=2, check_cache=False)
+    note(f"  {rep}")
+    compare_cache(wc, eng, runs)
+    assert rep["steps"] >= 1
+
+
+# --------------------------------------------------------------- linear (K1)
+@pytest.mark.parametrize("M,N,K,dt", [(64, 24576, 4096, "bf16"), (64, 12288, 4096, "bf16"),
+                                      (48, 4096, 12288, "bf16"), (37, 4096, 4096, "bf16"),
+                                      (128, 1024, 2048, "bf16"), (300, 384, 512, "bf16"),
+                                      (1024, 1536, 1024, "bf16"), (48, 768, 256, "f32"),
+                                      (200, 256, 768, "f32")])
+def test_linear_parity(M, N, K, dt):
+    """Projection = A W^T (plain fp64 matmul as the reference), skinny and fat
+    kernels, ragged row counts."""
+    note(f"linear M={M} N={N} K={K} {dt}")
+    tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+    g = torch.Generator(device="cuda").manual_seed(M * 7 + N)
+    A = torch.randn(M, K, device="cuda", generator=g).to(tdt)
+    W = (torch.randn(N, K, device="cuda", generator=g) * 0.02).to(tdt)
+    lib = B.load()
+    n_out = lib.dinfer_linear_out_elems(M, N, K, B.BF16 if dt == "bf16" else B.F32)
+    out = torch.full((n_out,), float("nan"), device="cuda")
+    S = B.linear(A, W, out)
+    torch.cuda.synchronize()
+    got = out.cpu().double().numpy().reshape(S, M, N).sum(0)
+    want = A.cpu().double().numpy() @ W.cpu().double().numpy().T
+    err = np.max(np.abs(got - want)) / np.sqrt(np.mean(want ** 2))
+    assert err < 2e-5, err
