@@ -131,13 +131,14 @@ def stream_handle(stream=None) -> int:
 
 def linear(A, W, out, stream=None) -> int:
     """dinfer_linear on torch device tensors; returns the split count.
-    A [M][K], W [N][K] (same dtype, f32 or bf16), out fp32 with at least
+    A fp32 [M][K], W [N][K] (f32 or bf16), out fp32 with at least
     dinfer_linear_out_elems(M, N, K, dtype) elements."""
     import torch
     lib = load()
+    assert A.dtype == torch.float32
     M, K = A.shape
     N = W.shape[0]
-    dt = F32 if A.dtype == torch.float32 else BF16
+    dt = F32 if W.dtype == torch.float32 else BF16
     need = lib.dinfer_linear_out_elems(M, N, K, dt)
     if need == 0 or out.numel() < need:
         raise DinferError(E_ARG, "dinfer_linear", f"out needs {need} floats")

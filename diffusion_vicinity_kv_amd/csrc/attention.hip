@@ -12,6 +12,10 @@
 // lanes that hold its output column.  Softmax runs in fp32 in the log2
 // domain.  Each split writes (m, l, unnormalised O) in fp32; a merge kernel
 // combines the splits of a query in split order.
+//
+// Queries stay fp32 and the probabilities are fp32: with a bf16 cache both
+// enter the bf16 MFMAs as hi + lo halves, so the only rounding left in the
+// attention is the cache's own storage of K and V.
 #include "common.h"
 #include "kernels.h"
 
@@ -24,7 +28,7 @@ constexpr int KT = 64;   // keys per LDS chunk
 
 template <typename T, int HD>
 __global__ __launch_bounds__(256) void attn_split_kernel(
-    PassTable tb, int q_tiles, int keys_per_split, int m_cap, const T* __restrict__ q,
+    PassTable tb, int q_tiles, int keys_per_split, int m_cap, const float* __restrict__ q,
     const T* __restrict__ kc, const T* __restrict__ vc, int H, int max_len, float scale_log2,
     float* __restrict__ o_part, float* __restrict__ ml_part) {
   using MF = Mfma<T>;
@@ -58,10 +62,24 @@ __global__ __launch_bounds__(256) void attn_split_kernel(
   const int qrow = tb.req_row_off[r] + qloc;
   const int d = H * HD;
 
-  V16 qf[QV];
+  using SO = SplitOperand<T>;
+  constexpr int QP = SO::PARTS;
+  V16 qf[QV][QP];
 #pragma unroll
-  for (int kk = 0; kk < QV; ++kk)
-    qf[kk] = qvalid ? ld16(q + (size_t)qrow * d + h * HD + kk * KSTEP + lg * VEC) : zero16();
+  for (int kk = 0; kk < QV; ++kk) {
+    float qv[VEC];
+#pragma unroll
+    for (int e = 0; e < VEC; e += 4) {
+      const float4 x = qvalid ? *reinterpret_cast<const float4*>(
+                                    q + (size_t)qrow * d + h * HD + kk * KSTEP + lg * VEC + e)
+                              : make_float4(0.f, 0.f, 0.f, 0.f);
+      qv[e] = x.x;
+      qv[e + 1] = x.y;
+      qv[e + 2] = x.z;
+      qv[e + 3] = x.w;
+    }
+    SO::make(qv, qf[kk]);
+  }
 
   floatx4 o[HT];
 #pragma unroll
@@ -95,7 +113,8 @@ __global__ __launch_bounds__(256) void attn_split_kernel(
 #pragma unroll
       for (int kk = 0; kk < QV; ++kk) {
         const V16 a = *reinterpret_cast<const V16*>(&Ks[(t * 16 + lc) * KSTR + kk * KSTEP + lg * VEC]);
-        MF::mac(s[t], a, qf[kk]);
+#pragma unroll
+        for (int p = 0; p < QP; ++p) MF::mac(s[t], a, qf[kk][p]);
       }
     }
     float mx = -INFINITY;
@@ -138,7 +157,7 @@ __global__ __launch_bounds__(256) void attn_split_kernel(
       for (int ht = 0; ht < HT; ++ht) {
         const T* vr = &Vt[(ht * 16 + lc) * VSTR + t * 16 + lg * 4];
         float av[4] = {to_f(vr[0]), to_f(vr[1]), to_f(vr[2]), to_f(vr[3])};
-        Mfma4<T>::mac(o[ht], av, pv);
+        Mfma4<T>::mac_split_b(o[ht], av, pv);
       }
     }
   }
@@ -158,12 +177,12 @@ __global__ __launch_bounds__(256) void attn_split_kernel(
 
 // Combine the key splits of each (row, head): out = sum_s 2^(m_s - M) O_s /
 // sum_s 2^(m_s - M) l_s, splits taken in order.
-template <typename T, int HD>
+template <int HD>
 __global__ __launch_bounds__(64) void attn_merge_kernel(PassTable tb, int keys_per_split,
                                                         int n_split, int m_cap,
                                                         const float* __restrict__ o_part,
                                                         const float* __restrict__ ml_part, int H,
-                                                        T* __restrict__ out) {
+                                                        float* __restrict__ out) {
   const int m = blockIdx.x;
   const int h = blockIdx.y;
   if (m >= min(*tb.nrows, m_cap)) return;
@@ -185,24 +204,24 @@ __global__ __launch_bounds__(64) void attn_merge_kernel(PassTable tb, int keys_p
     for (int e = 0; e < HD / 64; ++e) acc[e] += w * o_part[base * HD + threadIdx.x + 64 * e];
   }
   const float inv = 1.f / lsum;
-  T* orow = out + (size_t)m * H * HD + h * HD;
+  float* orow = out + (size_t)m * H * HD + h * HD;
 #pragma unroll
-  for (int e = 0; e < HD / 64; ++e) orow[threadIdx.x + 64 * e] = from_f<T>(acc[e] * inv);
+  for (int e = 0; e < HD / 64; ++e) orow[threadIdx.x + 64 * e] = acc[e] * inv;
 }
 
 template <typename T, int HD>
-hipError_t run(const AttnPlan& p, PassTable tb, int batch, int m_cap, const void* q,
+hipError_t run(const AttnPlan& p, PassTable tb, int batch, int m_cap, const float* q,
                const void* kc, const void* vc, int H, int max_len, float* o_part, float* ml_part,
-               void* o, hipStream_t st) {
+               float* o, hipStream_t st) {
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)HD);
   dim3 grid(p.n_split, H, batch * p.q_tiles);
   hipLaunchKernelGGL((attn_split_kernel<T, HD>), grid, dim3(256), 0, st, tb, p.q_tiles,
-                     p.keys_per_split, m_cap, static_cast<const T*>(q), static_cast<const T*>(kc),
+                     p.keys_per_split, m_cap, q, static_cast<const T*>(kc),
                      static_cast<const T*>(vc), H, max_len, scale_log2, o_part, ml_part);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((attn_merge_kernel<T, HD>), dim3(m_cap, H), dim3(64), 0, st, tb,
-                     p.keys_per_split, p.n_split, m_cap, o_part, ml_part, H, static_cast<T*>(o));
+  hipLaunchKernelGGL((attn_merge_kernel<HD>), dim3(m_cap, H), dim3(64), 0, st, tb,
+                     p.keys_per_split, p.n_split, m_cap, o_part, ml_part, H, o);
   return hipGetLastError();
 }
 
@@ -224,8 +243,8 @@ AttnPlan plan_attention(int batch, int max_rows_per_req, int max_keys, int H, in
 }
 
 hipError_t launch_attention(DType t, const AttnPlan& p, PassTable tb, int batch, int m_cap,
-                            const void* q, const void* kc, const void* vc, int H, int hd,
-                            int max_len, float* o_part, float* ml_part, void* o,
+                            const float* q, const void* kc, const void* vc, int H, int hd,
+                            int max_len, float* o_part, float* ml_part, float* o,
                             hipStream_t st) {
   if (t == DType::F32) {
     if (hd == 64) return run<float, 64>(p, tb, batch, m_cap, q, kc, vc, H, max_len, o_part, ml_part, o, st);

@@ -1,17 +1,24 @@
 // Linear layers of the denoising step on gfx950 MFMA: out = A * W^T with A
-// [M][K] activations and W [N][K] weights (Linear storage), fp32 accumulation.
+// [M][K] fp32 activations and W [N][K] weights (Linear storage, fp32 or bf16),
+// fp32 accumulation.
+//
+// Activations stay fp32 between kernels.  With bf16 weights each activation
+// is split into hi = bf16(a) and lo = bf16(a - hi) and both halves go through
+// the bf16 MFMA against the same weight fragment: the product then carries
+// the weights' own precision only (no activation rounding), for one extra
+// MFMA per weight fragment -- free wherever the layer is a weight stream.
 //
 // Two kernels:
-//  * skinny (M <= 128): the vicinity window holds tens of rows, so each layer
-//    is a weight stream.  A workgroup owns 64*NT output columns over all rows
-//    and one K slice; its activations are staged in LDS chunk by chunk and
-//    shared by four waves, while every wave streams its own weight rows
-//    straight into registers (one 16-byte load per lane per MFMA B operand),
-//    issued ahead of the LDS staging so their latency overlaps it.  K splits
-//    raise the workgroup count; each split writes an fp32 partial that the
-//    consumer kernel sums in split order (deterministic).
+//  * skinny (M <= 128): the vicinity window holds tens of rows, so a layer is
+//    a weight stream.  A workgroup owns 64*NT output columns over all rows and
+//    one K slice.  Each wave streams its own weight rows straight into
+//    registers (one 16-byte load per lane per MFMA B operand), double-buffered
+//    one K chunk ahead; the activation chunk is split into hi/lo planes in
+//    LDS, double-buffered, and shared by the four waves.  K splits raise the
+//    workgroup count; each split writes an fp32 partial that the consumer
+//    kernel sums in split order (deterministic).
 //  * fat (M > 128: block-start refresh, batched steps): 128x128 output tiles,
-//    128-byte K slabs of both operands double-buffered in LDS, four waves each
+//    64-byte K slabs of both operands double-buffered in LDS, four waves each
 //    computing 64x64 with 16x16 MFMA tiles.
 #include "common.h"
 #include "kernels.h"
@@ -20,23 +27,50 @@ namespace dinfer {
 
 namespace {
 
+template <typename TW> struct ASplit;
+// bf16 weights: two LDS planes (hi, lo) of bf16 activations.
+template <> struct ASplit<bf16> {
+  static constexpr int PLANES = 2;
+  __device__ __forceinline__ static void store4(bf16* hi, bf16* lo, const float4& x) {
+    const float v[4] = {x.x, x.y, x.z, x.w};
+    bf16x4 h, l;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      h[i] = static_cast<bf16>(v[i]);
+      l[i] = static_cast<bf16>(v[i] - static_cast<float>(h[i]));
+    }
+    *reinterpret_cast<bf16x4*>(hi) = h;
+    *reinterpret_cast<bf16x4*>(lo) = l;
+  }
+};
+// fp32 weights: one plane of fp32 activations.
+template <> struct ASplit<float> {
+  static constexpr int PLANES = 1;
+  __device__ __forceinline__ static void store4(float* p, float*, const float4& x) {
+    *reinterpret_cast<float4*>(p) = x;
+  }
+};
+
 // ---------------------------------------------------------------------------
-template <typename T, int MT, int NT>
-__global__ __launch_bounds__(256) void gemm_skinny_kernel(const T* __restrict__ A,
-                                                          const T* __restrict__ W,
+template <typename TW, int MT, int NT>
+__global__ __launch_bounds__(256) void gemm_skinny_kernel(const float* __restrict__ A,
+                                                          const TW* __restrict__ W,
                                                           float* __restrict__ P,
                                                           const int* __restrict__ m_dev,
                                                           int m_cap, int N, int K, int n_tiles,
                                                           int S) {
-  using MF = Mfma<T>;
+  using MF = Mfma<TW>;
+  using AS = ASplit<TW>;
+  constexpr int PL = AS::PLANES;
   constexpr int VEC = MF::VEC;
   constexpr int KSTEP = MF::KSTEP;
-  constexpr int KC = 512 / sizeof(T);             // K elements per LDS chunk (512 B / row)
-  constexpr int U = KC / KSTEP;                   // vector steps per chunk
+  constexpr int U = 4;                          // vector steps per K chunk
+  constexpr int KC = U * KSTEP;                 // 128 (bf16) / 64 (fp32) K per chunk
   constexpr int ROWS = 16 * MT;
-  constexpr int STR = KC + 16 / sizeof(T);        // LDS row stride, +16 B against bank conflicts
-  constexpr int VPR = KC / VEC;                   // 16-byte vectors per staged row (32)
-  __shared__ __attribute__((aligned(16))) T As[ROWS * STR];
+  constexpr int STR = KC + 16 / sizeof(TW);     // LDS row stride (+16 B)
+  constexpr int F4R = KC / 4;                   // float4 of A per chunk row
+  constexpr int AV = (ROWS * F4R + 255) / 256;  // float4 of A per thread per chunk
+  __shared__ __attribute__((aligned(16))) TW As[2][PL][ROWS * STR];
 
   const int bid = blockIdx.x;
   const int tile = bid % n_tiles;
@@ -57,35 +91,75 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(const T* __restrict__ 
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  const T* wrow[NT];
+  const TW* wrow[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) wrow[nt] = W + (size_t)(n0 + nt * 16 + lc) * K + lg * VEC;
 
-  for (int c = c_begin; c < c_end; ++c) {
-    const int kb = c * KC;
-    V16 b[U][NT];
+  V16 bcur[U][NT], bnext[U][NT];
+  float4 areg[AV];
+  auto load_w = [&](V16 (&b)[U][NT], int c) {
 #pragma unroll
     for (int j = 0; j < U; ++j)
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) b[j][nt] = ld16(wrow[nt] + kb + j * KSTEP);
-    __syncthreads();  // every wave is done reading the previous chunk
-    for (int v = threadIdx.x; v < ROWS * VPR; v += 256) {
-      const int r = v / VPR;
-      const int cv = v % VPR;
-      const V16 x = (r < M) ? ld16(A + (size_t)r * K + kb + cv * VEC) : zero16();
-      st16(&As[r * STR + cv * VEC], x);
+      for (int nt = 0; nt < NT; ++nt) b[j][nt] = ld16(wrow[nt] + c * KC + j * KSTEP);
+  };
+  auto load_a = [&](int c) {
+#pragma unroll
+    for (int i = 0; i < AV; ++i) {
+      const int v = threadIdx.x + 256 * i;
+      const int r = v / F4R;
+      const int cv = v % F4R;
+      areg[i] = (v < ROWS * F4R && r < M)
+                    ? *reinterpret_cast<const float4*>(A + (size_t)r * K + c * KC + cv * 4)
+                    : make_float4(0.f, 0.f, 0.f, 0.f);
     }
-    __syncthreads();
+  };
+  auto store_a = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < AV; ++i) {
+      const int v = threadIdx.x + 256 * i;
+      const int r = v / F4R;
+      const int cv = v % F4R;
+      if (v < ROWS * F4R)
+        AS::store4(&As[buf][0][r * STR + cv * 4], &As[buf][PL - 1][r * STR + cv * 4], areg[i]);
+    }
+  };
+
+  if (c_begin < c_end) {
+    load_w(bcur, c_begin);
+    load_a(c_begin);
+    store_a(0);
+  }
+  __syncthreads();
+  for (int c = c_begin; c < c_end; ++c) {
+    const int buf = (c - c_begin) & 1;
+    const bool more = c + 1 < c_end;
+    if (more) {
+      load_w(bnext, c + 1);
+      load_a(c + 1);
+    }
 #pragma unroll
     for (int j = 0; j < U; ++j) {
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         if (mt * 16 < M) {
-          const V16 a = *reinterpret_cast<const V16*>(&As[(mt * 16 + lc) * STR + j * KSTEP + lg * VEC]);
 #pragma unroll
-          for (int nt = 0; nt < NT; ++nt) MF::mac(acc[mt][nt], a, b[j][nt]);
+          for (int p = 0; p < PL; ++p) {
+            const V16 a = *reinterpret_cast<const V16*>(
+                &As[buf][p][(mt * 16 + lc) * STR + j * KSTEP + lg * VEC]);
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) MF::mac(acc[mt][nt], a, bcur[j][nt]);
+          }
         }
       }
+    }
+    if (more) store_a(buf ^ 1);
+    __syncthreads();
+    if (more) {
+#pragma unroll
+      for (int j = 0; j < U; ++j)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) bcur[j][nt] = bnext[j][nt];
     }
   }
 
@@ -102,21 +176,25 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(const T* __restrict__ 
 }
 
 // ---------------------------------------------------------------------------
-template <typename T>
-__global__ __launch_bounds__(256) void gemm_fat_kernel(const T* __restrict__ A,
-                                                       const T* __restrict__ W,
+template <typename TW>
+__global__ __launch_bounds__(256) void gemm_fat_kernel(const float* __restrict__ A,
+                                                       const TW* __restrict__ W,
                                                        float* __restrict__ Cout,
                                                        const int* __restrict__ m_dev, int m_cap,
                                                        int N, int K) {
-  using MF = Mfma<T>;
+  using MF = Mfma<TW>;
+  using AS = ASplit<TW>;
+  constexpr int PL = AS::PLANES;
   constexpr int VEC = MF::VEC;
   constexpr int KSTEP = MF::KSTEP;
-  constexpr int BK = 128 / sizeof(T);      // K elements per slab (128 B per row)
-  constexpr int STEPS = BK / KSTEP;
-  constexpr int STR = BK + 16 / sizeof(T);
-  constexpr int VPR = BK / VEC;            // 8 vectors per slab row
-  __shared__ __attribute__((aligned(16))) T As[2][128 * STR];
-  __shared__ __attribute__((aligned(16))) T Bs[2][128 * STR];
+  constexpr int BK = KSTEP;                    // one vector step (64 bytes of W) per slab
+  constexpr int STR = BK + 16 / sizeof(TW);
+  constexpr int F4R = BK / 4;                  // float4 of A per slab row
+  constexpr int AV = 128 * F4R / 256;          // float4 of A per thread per slab
+  constexpr int WVR = BK / VEC;                // 16-byte W vectors per slab row (4)
+  constexpr int BV = 128 * WVR / 256;          // W vectors per thread per slab (2)
+  __shared__ __attribute__((aligned(16))) TW As[2][PL][128 * STR];
+  __shared__ __attribute__((aligned(16))) TW Bs[2][128 * STR];
 
   const int M = m_dev ? min(*m_dev, m_cap) : m_cap;
   const int m0 = blockIdx.y * 128;
@@ -135,24 +213,39 @@ __global__ __launch_bounds__(256) void gemm_fat_kernel(const T* __restrict__ A,
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  V16 ra[4], rb[4];
+  float4 ra[AV];
+  V16 rb[BV];
   auto gload = [&](int kt) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < AV; ++i) {
       const int v = threadIdx.x + 256 * i;
-      const int r = v / VPR;
-      const int cv = v % VPR;
-      ra[i] = (m0 + r < M) ? ld16(A + (size_t)(m0 + r) * K + kt * BK + cv * VEC) : zero16();
+      const int r = v / F4R;
+      const int cv = v % F4R;
+      ra[i] = (m0 + r < M)
+                  ? *reinterpret_cast<const float4*>(A + (size_t)(m0 + r) * K + kt * BK + cv * 4)
+                  : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int i = 0; i < BV; ++i) {
+      const int v = threadIdx.x + 256 * i;
+      const int r = v / WVR;
+      const int cv = v % WVR;
       rb[i] = (n0 + r < N) ? ld16(W + (size_t)(n0 + r) * K + kt * BK + cv * VEC) : zero16();
     }
   };
   auto sstore = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < AV; ++i) {
       const int v = threadIdx.x + 256 * i;
-      const int r = v / VPR;
-      const int cv = v % VPR;
-      st16(&As[buf][r * STR + cv * VEC], ra[i]);
+      const int r = v / F4R;
+      const int cv = v % F4R;
+      AS::store4(&As[buf][0][r * STR + cv * 4], &As[buf][PL - 1][r * STR + cv * 4], ra[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < BV; ++i) {
+      const int v = threadIdx.x + 256 * i;
+      const int r = v / WVR;
+      const int cv = v % WVR;
       st16(&Bs[buf][r * STR + cv * VEC], rb[i]);
     }
   };
@@ -164,21 +257,19 @@ __global__ __launch_bounds__(256) void gemm_fat_kernel(const T* __restrict__ A,
   for (int kt = 0; kt < nk; ++kt) {
     const int cur = kt & 1;
     if (kt + 1 < nk) gload(kt + 1);
+    V16 b[4];
 #pragma unroll
-    for (int s = 0; s < STEPS; ++s) {
-      V16 a[4], b[4];
+    for (int nt = 0; nt < 4; ++nt)
+      b[nt] = *reinterpret_cast<const V16*>(&Bs[cur][(wn * 64 + nt * 16 + lc) * STR + lg * VEC]);
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-        a[mt] = *reinterpret_cast<const V16*>(
-            &As[cur][(wm * 64 + mt * 16 + lc) * STR + s * KSTEP + lg * VEC]);
+    for (int p = 0; p < PL; ++p) {
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt)
-        b[nt] = *reinterpret_cast<const V16*>(
-            &Bs[cur][(wn * 64 + nt * 16 + lc) * STR + s * KSTEP + lg * VEC]);
+      for (int mt = 0; mt < 4; ++mt) {
+        const V16 a = *reinterpret_cast<const V16*>(
+            &As[cur][p][(wm * 64 + mt * 16 + lc) * STR + lg * VEC]);
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt) MF::mac(acc[mt][nt], a[mt], b[nt]);
+        for (int nt = 0; nt < 4; ++nt) MF::mac(acc[mt][nt], a, b[nt]);
+      }
     }
     if (kt + 1 < nk) sstore(cur ^ 1);
     __syncthreads();
@@ -196,50 +287,51 @@ __global__ __launch_bounds__(256) void gemm_fat_kernel(const T* __restrict__ A,
       }
 }
 
-template <typename T, int MT, int NT>
-hipError_t run_skinny(const GemmPlan& p, const void* A, const void* W, float* out,
+template <typename TW, int MT, int NT>
+hipError_t run_skinny(const GemmPlan& p, const float* A, const void* W, float* out,
                       const int* m_dev, int m_cap, int N, int K, hipStream_t st) {
   const int n_tiles = N / (64 * NT);
-  hipLaunchKernelGGL((gemm_skinny_kernel<T, MT, NT>), dim3(n_tiles * p.splits), dim3(256), 0, st,
-                     static_cast<const T*>(A), static_cast<const T*>(W), out, m_dev, m_cap, N, K,
-                     n_tiles, p.splits);
+  hipLaunchKernelGGL((gemm_skinny_kernel<TW, MT, NT>), dim3(n_tiles * p.splits), dim3(256), 0,
+                     st, A, static_cast<const TW*>(W), out, m_dev, m_cap, N, K, n_tiles,
+                     p.splits);
   return hipGetLastError();
 }
 
-template <typename T, int NT>
-hipError_t dispatch_mt(const GemmPlan& p, const void* A, const void* W, float* out,
+template <typename TW, int NT>
+hipError_t dispatch_mt(const GemmPlan& p, const float* A, const void* W, float* out,
                        const int* m_dev, int m_cap, int N, int K, hipStream_t st) {
   switch (p.mt) {
-    case 1: return run_skinny<T, 1, NT>(p, A, W, out, m_dev, m_cap, N, K, st);
-    case 2: return run_skinny<T, 2, NT>(p, A, W, out, m_dev, m_cap, N, K, st);
-    case 3: return run_skinny<T, 3, NT>(p, A, W, out, m_dev, m_cap, N, K, st);
-    case 4: return run_skinny<T, 4, NT>(p, A, W, out, m_dev, m_cap, N, K, st);
-    case 5: return run_skinny<T, 5, NT>(p, A, W, out, m_dev, m_cap, N, K, st);
-    case 6: return run_skinny<T, 6, NT>(p, A, W, out, m_dev, m_cap, N, K, st);
-    case 7: return run_skinny<T, 7, NT>(p, A, W, out, m_dev, m_cap, N, K, st);
-    case 8: return run_skinny<T, 8, NT>(p, A, W, out, m_dev, m_cap, N, K, st);
+    case 1: return run_skinny<TW, 1, NT>(p, A, W, out, m_dev, m_cap, N, K, st);
+    case 2: return run_skinny<TW, 2, NT>(p, A, W, out, m_dev, m_cap, N, K, st);
+    case 3: return run_skinny<TW, 3, NT>(p, A, W, out, m_dev, m_cap, N, K, st);
+    case 4: return run_skinny<TW, 4, NT>(p, A, W, out, m_dev, m_cap, N, K, st);
+    case 5: return run_skinny<TW, 5, NT>(p, A, W, out, m_dev, m_cap, N, K, st);
+    case 6: return run_skinny<TW, 6, NT>(p, A, W, out, m_dev, m_cap, N, K, st);
+    case 7: return run_skinny<TW, 7, NT>(p, A, W, out, m_dev, m_cap, N, K, st);
+    case 8: return run_skinny<TW, 8, NT>(p, A, W, out, m_dev, m_cap, N, K, st);
     default: return hipErrorInvalidValue;
   }
 }
 
-template <typename T>
-hipError_t dispatch(const GemmPlan& p, const void* A, const void* W, float* out, const int* m_dev,
-                    int m_cap, int N, int K, hipStream_t st) {
+template <typename TW>
+hipError_t dispatch(const GemmPlan& p, const float* A, const void* W, float* out,
+                    const int* m_dev, int m_cap, int N, int K, hipStream_t st) {
   if (p.kind == 1) {
     dim3 grid((N + 127) / 128, (m_cap + 127) / 128);
-    hipLaunchKernelGGL((gemm_fat_kernel<T>), grid, dim3(256), 0, st, static_cast<const T*>(A),
-                       static_cast<const T*>(W), out, m_dev, m_cap, N, K);
+    hipLaunchKernelGGL((gemm_fat_kernel<TW>), grid, dim3(256), 0, st, A,
+                       static_cast<const TW*>(W), out, m_dev, m_cap, N, K);
     return hipGetLastError();
   }
-  return p.nt == 2 ? dispatch_mt<T, 2>(p, A, W, out, m_dev, m_cap, N, K, st)
-                   : dispatch_mt<T, 1>(p, A, W, out, m_dev, m_cap, N, K, st);
+  return p.nt == 2 ? dispatch_mt<TW, 2>(p, A, W, out, m_dev, m_cap, N, K, st)
+                   : dispatch_mt<TW, 1>(p, A, W, out, m_dev, m_cap, N, K, st);
 }
 
 }  // namespace
 
+int gemm_k_chunk(DType t) { return t == DType::F32 ? 64 : 128; }
+
 bool gemm_shape_ok(DType t, int N, int K) {
-  const int kc = t == DType::F32 ? 128 : 256;   // skinny chunk; the fat slab divides it
-  return N > 0 && K > 0 && N % 128 == 0 && K % kc == 0;
+  return N > 0 && K > 0 && N % 128 == 0 && K % gemm_k_chunk(t) == 0;
 }
 
 GemmPlan plan_gemm(DType t, int m_cap, int N, int K, int target_wgs) {
@@ -254,8 +346,7 @@ GemmPlan plan_gemm(DType t, int m_cap, int N, int K, int target_wgs) {
   p.kind = 0;
   p.mt = (m_cap + 15) / 16;
   if (p.mt < 1) p.mt = 1;
-  const int kc = t == DType::F32 ? 128 : 256;
-  const int chunks = K / kc;
+  const int chunks = K / gemm_k_chunk(t);
   p.nt = (N / 128 >= target_wgs / 2) ? 2 : 1;
   const int n_tiles = N / (64 * p.nt);
   int s = (target_wgs + n_tiles - 1) / n_tiles;
@@ -266,7 +357,7 @@ GemmPlan plan_gemm(DType t, int m_cap, int N, int K, int target_wgs) {
   return p;
 }
 
-hipError_t launch_gemm(const GemmPlan& p, DType t, const void* A, const void* W, float* out,
+hipError_t launch_gemm(const GemmPlan& p, DType t, const float* A, const void* W, float* out,
                        const int* m_dev, int m_cap, int N, int K, hipStream_t st) {
   if (t == DType::F32) return dispatch<float>(p, A, W, out, m_dev, m_cap, N, K, st);
   return dispatch<bf16>(p, A, W, out, m_dev, m_cap, N, K, st);

@@ -34,9 +34,11 @@ struct GemmPlan {
   int grid;
 };
 GemmPlan plan_gemm(DType t, int m_cap, int N, int K, int target_wgs);
-hipError_t launch_gemm(const GemmPlan& p, DType t, const void* A, const void* W, float* out,
+// A is fp32 (split into hi/lo bf16 halves in-kernel for bf16 weights).
+hipError_t launch_gemm(const GemmPlan& p, DType t, const float* A, const void* W, float* out,
                        const int* m_dev, int m_cap, int N, int K, hipStream_t st);
 bool gemm_shape_ok(DType t, int N, int K);
+int gemm_k_chunk(DType t);
 
 // ---- row-wise kernels ------------------------------------------------------
 hipError_t launch_embed(DType t, PassTable tb, int m_cap, const int* tokens, int max_len,
@@ -45,18 +47,18 @@ hipError_t launch_embed(DType t, PassTable tb, int m_cap, const int* tokens, int
                         hipStream_t st);
 // x[m] += sum_s P[s][m]; a[m] = rmsnorm(x[m]) * g   (S = 0: no partials)
 hipError_t launch_add_rmsnorm(DType t, const int* nrows, int m_cap, float* x, const float* P,
-                              int S, size_t p_stride, const void* g, float eps, void* a, int d,
+                              int S, size_t p_stride, const void* g, float eps, float* a, int d,
                               hipStream_t st);
 hipError_t launch_qkv_rope_scatter(DType t, PassTable tb, int m_cap, const float* P, int S,
                                    size_t p_stride, int d, int H, int hd, const float* rope_cs,
-                                   void* q_out, void* kc, void* vc, int max_len, hipStream_t st);
-hipError_t launch_swiglu(DType t, const int* nrows, int m_cap, const float* P, int S,
-                         size_t p_stride, int F, void* act, hipStream_t st);
+                                   float* q_out, void* kc, void* vc, int max_len, hipStream_t st);
+hipError_t launch_swiglu(const int* nrows, int m_cap, const float* P, int S, size_t p_stride,
+                         int F, float* act, hipStream_t st);
 // block rows of the window -> x + sum_s P[s] -> rmsnorm * g -> out[r*B + j];
 // also gathers each block row's planting (row_plant_id / row_plant_bias).
 hipError_t launch_final_norm(DType t, PassTable tb, int batch, int B, const float* x,
                              const float* P, int S, size_t p_stride, const void* g, float eps,
-                             void* out, int d, const int* plant_id, const float* plant_bias,
+                             float* out, int d, const int* plant_id, const float* plant_bias,
                              int max_len, int* row_plant_id, float* row_plant_bias,
                              hipStream_t st);
 
@@ -66,8 +68,8 @@ struct AttnPlan {
 };
 AttnPlan plan_attention(int batch, int max_rows_per_req, int max_keys, int H, int target_wgs);
 hipError_t launch_attention(DType t, const AttnPlan& p, PassTable tb, int batch, int m_cap,
-                            const void* q, const void* kc, const void* vc, int H, int hd,
-                            int max_len, float* o_part, float* ml_part, void* o,
+                            const float* q, const void* kc, const void* vc, int H, int hd,
+                            int max_len, float* o_part, float* ml_part, float* o,
                             hipStream_t st);
 
 // ---- vocab statistics ---------------------------------------------------------

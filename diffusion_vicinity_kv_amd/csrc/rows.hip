@@ -60,7 +60,7 @@ __global__ __launch_bounds__(kThreads) void add_rmsnorm_kernel(const int* __rest
                                                                const float* __restrict__ P, int S,
                                                                size_t p_stride,
                                                                const T* __restrict__ g, float eps,
-                                                               T* __restrict__ a, int d) {
+                                                               float* __restrict__ a, int d) {
   constexpr int MAXE = 32;   // d <= 8192
   __shared__ float red[kThreads / 64];
   const int m = blockIdx.x;
@@ -81,11 +81,11 @@ __global__ __launch_bounds__(kThreads) void add_rmsnorm_kernel(const int* __rest
   }
   const float tot = block_sum<kThreads / 64>(ss, red);
   const float inv = 1.f / sqrtf(tot / d + eps);
-  T* ar = a + (size_t)m * d;
+  float* ar = a + (size_t)m * d;
 #pragma unroll
   for (int e = 0; e < MAXE; ++e) {
     const int i = threadIdx.x + e * kThreads;
-    if (i < d) ar[i] = from_f<T>(v[e] * inv * to_f(g[i]));
+    if (i < d) ar[i] = v[e] * inv * to_f(g[i]);
   }
 }
 
@@ -97,7 +97,7 @@ __global__ __launch_bounds__(kThreads) void add_rmsnorm_kernel(const int* __rest
 template <typename T>
 __global__ __launch_bounds__(kThreads) void qkv_rope_scatter_kernel(
     PassTable tb, int m_cap, const float* __restrict__ P, int S, size_t p_stride, int d, int H,
-    int hd, const float* __restrict__ rope_cs, T* __restrict__ q_out, T* __restrict__ kc,
+    int hd, const float* __restrict__ rope_cs, float* __restrict__ q_out, T* __restrict__ kc,
     T* __restrict__ vc, int max_len) {
   const int m = blockIdx.x;
   if (m >= min(*tb.nrows, m_cap)) return;
@@ -124,9 +124,9 @@ __global__ __launch_bounds__(kThreads) void qkv_rope_scatter_kernel(
     }
     const float c = cs[j];
     const float sn = cs[half + j];
-    T* qr = q_out + (size_t)m * d;
-    qr[c0] = from_f<T>(q0 * c - q1 * sn);
-    qr[c1] = from_f<T>(q1 * c + q0 * sn);
+    float* qr = q_out + (size_t)m * d;
+    qr[c0] = q0 * c - q1 * sn;
+    qr[c1] = q1 * c + q0 * sn;
     const size_t cb = (((size_t)r * H + h) * max_len + pos) * hd;
     kc[cb + j] = from_f<T>(k0 * c - k1 * sn);
     kc[cb + j + half] = from_f<T>(k1 * c + k0 * sn);
@@ -137,11 +137,10 @@ __global__ __launch_bounds__(kThreads) void qkv_rope_scatter_kernel(
 
 // act[m][f] = silu(gate) * up with gate, up summed over the split-K partials
 // of the fused [gate | up] projection.
-template <typename T>
 __global__ __launch_bounds__(kThreads) void swiglu_kernel(const int* __restrict__ nrows, int m_cap,
                                                           const float* __restrict__ P, int S,
                                                           size_t p_stride, int F,
-                                                          T* __restrict__ act) {
+                                                          float* __restrict__ act) {
   const int M = min(*nrows, m_cap);
   const size_t total = (size_t)M * F;
   for (size_t idx = (size_t)blockIdx.x * kThreads + threadIdx.x; idx < total;
@@ -154,7 +153,7 @@ __global__ __launch_bounds__(kThreads) void swiglu_kernel(const int* __restrict_
       g += pr[s * p_stride + f];
       u += pr[s * p_stride + F + f];
     }
-    act[idx] = from_f<T>(g / (1.f + expf(-g)) * u);
+    act[idx] = g / (1.f + expf(-g)) * u;
   }
 }
 
@@ -163,7 +162,7 @@ __global__ __launch_bounds__(kThreads) void swiglu_kernel(const int* __restrict_
 template <typename T>
 __global__ __launch_bounds__(kThreads) void final_norm_kernel(
     PassTable tb, int B, const float* __restrict__ x, const float* __restrict__ P, int S,
-    size_t p_stride, const T* __restrict__ g, float eps, T* __restrict__ out, int d,
+    size_t p_stride, const T* __restrict__ g, float eps, float* __restrict__ out, int d,
     const int* __restrict__ plant_id, const float* __restrict__ plant_bias, int max_len,
     int* __restrict__ row_plant_id, float* __restrict__ row_plant_bias) {
   constexpr int MAXE = 32;
@@ -171,9 +170,9 @@ __global__ __launch_bounds__(kThreads) void final_norm_kernel(
   const int rr = blockIdx.x;
   const int r = rr / B;
   const int j = rr % B;
-  T* orow = out + (size_t)rr * d;
+  float* orow = out + (size_t)rr * d;
   if (!tb.req_active[r] || tb.req_nrows[r] == 0) {
-    for (int i = threadIdx.x; i < d; i += kThreads) orow[i] = from_f<T>(0.f);
+    for (int i = threadIdx.x; i < d; i += kThreads) orow[i] = 0.f;
     if (threadIdx.x == 0) {
       row_plant_id[rr] = -1;
       row_plant_bias[rr] = 0.f;
@@ -201,7 +200,7 @@ __global__ __launch_bounds__(kThreads) void final_norm_kernel(
 #pragma unroll
   for (int e = 0; e < MAXE; ++e) {
     const int i = threadIdx.x + e * kThreads;
-    if (i < d) orow[i] = from_f<T>(v[e] * inv * to_f(g[i]));
+    if (i < d) orow[i] = v[e] * inv * to_f(g[i]);
   }
   if (threadIdx.x == 0) {
     row_plant_id[rr] = plant_id ? plant_id[(size_t)r * max_len + bs + j] : -1;
@@ -231,44 +230,44 @@ hipError_t launch_embed(DType t, PassTable tb, int m_cap, const int* tokens, int
 }
 
 hipError_t launch_add_rmsnorm(DType t, const int* nrows, int m_cap, float* x, const float* P,
-                              int S, size_t p_stride, const void* g, float eps, void* a, int d,
+                              int S, size_t p_stride, const void* g, float eps, float* a, int d,
                               hipStream_t st) {
   if (d > 32 * kThreads) return hipErrorInvalidValue;
   DISPATCH_T(t, hipLaunchKernelGGL((add_rmsnorm_kernel<T>), dim3(m_cap), dim3(kThreads), 0, st,
                                    nrows, m_cap, x, P, S, p_stride, static_cast<const T*>(g), eps,
-                                   static_cast<T*>(a), d));
+                                   a, d));
   return hipGetLastError();
 }
 
 hipError_t launch_qkv_rope_scatter(DType t, PassTable tb, int m_cap, const float* P, int S,
                                    size_t p_stride, int d, int H, int hd, const float* rope_cs,
-                                   void* q_out, void* kc, void* vc, int max_len, hipStream_t st) {
+                                   float* q_out, void* kc, void* vc, int max_len, hipStream_t st) {
   DISPATCH_T(t, hipLaunchKernelGGL((qkv_rope_scatter_kernel<T>), dim3(m_cap), dim3(kThreads), 0,
-                                   st, tb, m_cap, P, S, p_stride, d, H, hd, rope_cs,
-                                   static_cast<T*>(q_out), static_cast<T*>(kc),
+                                   st, tb, m_cap, P, S, p_stride, d, H, hd, rope_cs, q_out,
+                                   static_cast<T*>(kc),
                                    static_cast<T*>(vc), max_len));
   return hipGetLastError();
 }
 
-hipError_t launch_swiglu(DType t, const int* nrows, int m_cap, const float* P, int S,
-                         size_t p_stride, int F, void* act, hipStream_t st) {
+hipError_t launch_swiglu(const int* nrows, int m_cap, const float* P, int S, size_t p_stride,
+                         int F, float* act, hipStream_t st) {
   size_t total = (size_t)m_cap * F;
   int blocks = (int)((total + kThreads - 1) / kThreads);
   if (blocks > 4096) blocks = 4096;
-  DISPATCH_T(t, hipLaunchKernelGGL((swiglu_kernel<T>), dim3(blocks), dim3(kThreads), 0, st, nrows,
-                                   m_cap, P, S, p_stride, F, static_cast<T*>(act)));
+  hipLaunchKernelGGL(swiglu_kernel, dim3(blocks), dim3(kThreads), 0, st, nrows, m_cap, P, S,
+                     p_stride, F, act);
   return hipGetLastError();
 }
 
 hipError_t launch_final_norm(DType t, PassTable tb, int batch, int B, const float* x,
                              const float* P, int S, size_t p_stride, const void* g, float eps,
-                             void* out, int d, const int* plant_id, const float* plant_bias,
+                             float* out, int d, const int* plant_id, const float* plant_bias,
                              int max_len, int* row_plant_id, float* row_plant_bias,
                              hipStream_t st) {
   if (d > 32 * kThreads) return hipErrorInvalidValue;
   DISPATCH_T(t, hipLaunchKernelGGL((final_norm_kernel<T>), dim3(batch * B), dim3(kThreads), 0, st,
                                    tb, B, x, P, S, p_stride, static_cast<const T*>(g), eps,
-                                   static_cast<T*>(out), d, plant_id, plant_bias, max_len,
+                                   out, d, plant_id, plant_bias, max_len,
                                    row_plant_id, row_plant_bias));
   return hipGetLastError();
 }

@@ -88,7 +88,7 @@ bool make_layout(const dinfer_model_cfg* m, const dinfer_decode_cfg* dc, int max
   const int d = m->d_model, F = m->ffn_dim, V = m->vocab;
   if (!gemm_shape_ok(dt, 3 * d, d) || !gemm_shape_ok(dt, d, d) || !gemm_shape_ok(dt, 2 * F, d) ||
       !gemm_shape_ok(dt, d, F) || !gemm_shape_ok(dt, V, d))
-    return bad("GEMM shapes must have N % 128 == 0 and K % 256 (bf16) / 128 (f32) == 0");
+    return bad("GEMM shapes must have N % 128 == 0 and K % 128 (bf16) / 64 (f32) == 0");
 
   Layout& l = *L;
   l.dt = dt;
@@ -144,14 +144,14 @@ bool make_layout(const dinfer_model_cfg* m, const dinfer_decode_cfg* dc, int max
   l.off_kvk = take(l.kv_layer_elems * l.nl * es);
   l.off_kvv = take(l.kv_layer_elems * l.nl * es);
   l.off_x = take((size_t)l.m_all * d * 4);
-  l.off_a = take((size_t)l.m_all * d * es);
-  l.off_q = take((size_t)l.m_all * d * es);
-  l.off_o = take((size_t)l.m_all * d * es);
-  l.off_act = take((size_t)l.m_all * F * es);
+  l.off_a = take((size_t)l.m_all * d * 4);
+  l.off_q = take((size_t)l.m_all * d * 4);
+  l.off_o = take((size_t)l.m_all * d * 4);
+  l.off_act = take((size_t)l.m_all * F * 4);
   l.off_part = take(l.part_elems * 4);
   l.off_ao = take(l.attn_o_elems * 4);
   l.off_aml = take(l.attn_ml_elems * 4);
-  l.off_hf = take((size_t)l.lm_rows * d * es);
+  l.off_hf = take((size_t)l.lm_rows * d * 4);
   l.off_logits = take((size_t)l.lm_rows * V * 4);
   l.off_rpid = take((size_t)l.lm_rows * 4);
   l.off_rpb = take((size_t)l.lm_rows * 4);
@@ -292,10 +292,10 @@ dinfer_status run_pass(dinfer_ctx* c, bool step) {
   const AttnPlan& ap = step ? L.a_step : L.a_ref;
   const int d = L.d, F = L.F;
   float* x = c->at<float>(L.off_x);
-  void* a = c->at<char>(L.off_a);
-  void* q = c->at<char>(L.off_q);
-  void* o = c->at<char>(L.off_o);
-  void* act = c->at<char>(L.off_act);
+  float* a = c->at<float>(L.off_a);
+  float* q = c->at<float>(L.off_q);
+  float* o = c->at<float>(L.off_o);
+  float* act = c->at<float>(L.off_act);
   float* part = c->at<float>(L.off_part);
   const size_t stride_q = (size_t)m_cap * 3 * d, stride_d = (size_t)m_cap * d,
                stride_g = (size_t)m_cap * 2 * F;
@@ -319,11 +319,11 @@ dinfer_status run_pass(dinfer_ctx* c, bool step) {
     HIP_TRY(launch_add_rmsnorm(dt, tb.nrows, m_cap, x, part, go.splits, stride_d, c->ffn_norm[l],
                                c->m.rms_eps, a, d, st));
     HIP_TRY(launch_gemm(gg, dt, a, c->wgu[l], part, tb.nrows, m_cap, 2 * F, d, st));
-    HIP_TRY(launch_swiglu(dt, tb.nrows, m_cap, part, gg.splits, stride_g, F, act, st));
+    HIP_TRY(launch_swiglu(tb.nrows, m_cap, part, gg.splits, stride_g, F, act, st));
     HIP_TRY(launch_gemm(gd, dt, act, c->wd[l], part, tb.nrows, m_cap, d, F, st));
   }
   if (!step) return DINFER_OK;
-  void* hf = c->at<char>(L.off_hf);
+  float* hf = c->at<float>(L.off_hf);
   HIP_TRY(launch_final_norm(dt, tb, L.max_batch, L.B, x, part, gd.splits, stride_d, c->final_norm,
                             c->m.rms_eps, hf, d, c->plant_id, c->plant_bias, L.max_len,
                             c->at<int>(L.off_rpid), c->at<float>(L.off_rpb), st));
@@ -786,7 +786,7 @@ size_t dinfer_linear_out_elems(int32_t M, int32_t N, int32_t K, int32_t dtype) {
   return (size_t)p.splits * M * N;
 }
 
-dinfer_status dinfer_linear(const void* d_A, const void* d_W, float* d_out, int32_t M, int32_t N,
+dinfer_status dinfer_linear(const float* d_A, const void* d_W, float* d_out, int32_t M, int32_t N,
                             int32_t K, int32_t dtype, int32_t* h_splits, void* stream) {
   if (!d_A || !d_W || !d_out) return fail(DINFER_E_ARG, "null pointer");
   if (M < 1) return fail(DINFER_E_ARG, "M must be positive");

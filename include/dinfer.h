@@ -221,17 +221,19 @@ dinfer_status dinfer_get_step_view(const dinfer_ctx* ctx, dinfer_step_view* out)
  * unrolling of the dInfer news article, section "系统级压榨". */
 dinfer_status dinfer_step_graph(dinfer_ctx* ctx, int32_t n_steps);
 
-/* Standalone projection, the Linear layer every step runs (dtype as the
- * model's): out[s][m][n] = sum over the s-th K slice of A[m][k] * W[n][k],
- * A [M][K] and W [N][K] row-major device arrays, out fp32 [splits][M][N]; the
+/* Standalone projection, the Linear layer every step runs:
+ * out[s][m][n] = sum over the s-th K slice of A[m][k] * W[n][k], with A an fp32
+ * [M][K] row-major device array (activations are fp32 throughout the step)
+ * and W [N][K] in the model dtype (weights); out fp32 [splits][M][N].  The
  * product A W^T is the sum of the splits (taken in split order by the
- * library's own consumers).  *h_splits (may be NULL) receives the split
- * count, which dinfer_linear_out_elems also returns through its result:
- * out must hold dinfer_linear_out_elems(M, N, K, dtype) floats.  Requires
- * N % 128 == 0 and K % 256 == 0 (bf16) / K % 128 == 0 (f32).  Same kernels
- * and launch plan as the step for the same M. */
+ * library's own consumers).  With bf16 weights each activation enters the
+ * MFMA as hi = bf16(a) plus lo = bf16(a - hi), so only the weights' rounding
+ * remains.  *h_splits (may be NULL) receives the split count; out must hold
+ * dinfer_linear_out_elems(M, N, K, dtype) floats.  Requires N % 128 == 0 and
+ * K % 128 == 0 (bf16) / K % 64 == 0 (f32).  Same kernels and launch plan as
+ * the step for the same M. */
 size_t dinfer_linear_out_elems(int32_t M, int32_t N, int32_t K, int32_t dtype);
-dinfer_status dinfer_linear(const void* d_A, const void* d_W, float* d_out, int32_t M, int32_t N,
+dinfer_status dinfer_linear(const float* d_A, const void* d_W, float* d_out, int32_t M, int32_t N,
                             int32_t K, int32_t dtype, int32_t* h_splits, void* stream);
 
 /* Standalone vocab statistics over fp32 logits d_logits [rows][vocab]
