@@ -10,13 +10,15 @@
 //
 // Two kernels:
 //  * skinny (M <= 128): the vicinity window holds tens of rows, so a layer is
-//    a weight stream.  A workgroup owns 64*NT output columns over all rows and
-//    one K slice.  Each wave streams its own weight rows straight into
-//    registers (one 16-byte load per lane per MFMA B operand), double-buffered
-//    one K chunk ahead; the activation chunk is split into hi/lo planes in
-//    LDS, double-buffered, and shared by the four waves.  K splits raise the
-//    workgroup count; each split writes an fp32 partial that the consumer
-//    kernel sums in split order (deterministic).
+//    a weight stream.  A workgroup of NW waves owns 16*NT*NW output columns
+//    (64 to 256) over all rows and one K slice.  Each wave streams its own
+//    weight rows straight into registers (one 16-byte load per lane per MFMA
+//    B operand), two K chunks ahead; the activation chunk is
+//    split into hi/lo planes in LDS, double-buffered, and shared by the
+//    waves -- wide column groups keep that fp32 re-read small next to the
+//    weights.  K splits bring the workgroup count to about one per CU; each
+//    split writes an fp32 partial that the consumer kernel sums in split
+//    order (deterministic; the kernel boundary orders the writes).
 //  * fat (M > 128: block-start refresh, batched steps): 128x128 output tiles,
 //    64-byte K slabs of both operands double-buffered in LDS, four waves each
 //    computing 64x64 with 16x16 MFMA tiles.
@@ -52,8 +54,12 @@ template <> struct ASplit<float> {
 };
 
 // ---------------------------------------------------------------------------
-template <typename TW, int MT, int NT>
-__global__ __launch_bounds__(256) void gemm_skinny_kernel(const float* __restrict__ A,
+// GUARD = false: A has at least 16*MT readable rows (rows >= M hold anything
+// finite or not -- they only feed output rows that are never stored), so the
+// activation loads and MFMAs carry no per-row conditions.  GUARD = true: rows
+// >= M are read as zeros (exact-size operands of the standalone entry point).
+template <typename TW, int MT, int NT, int NW, bool GUARD>
+__global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(const float* __restrict__ A,
                                                           const TW* __restrict__ W,
                                                           float* __restrict__ P,
                                                           const int* __restrict__ m_dev,
@@ -68,8 +74,10 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(const float* __restric
   constexpr int KC = U * KSTEP;                 // 128 (bf16) / 64 (fp32) K per chunk
   constexpr int ROWS = 16 * MT;
   constexpr int STR = KC + 16 / sizeof(TW);     // LDS row stride (+16 B)
+  constexpr int NTH = NW * 64;                  // threads per workgroup
   constexpr int F4R = KC / 4;                   // float4 of A per chunk row
-  constexpr int AV = (ROWS * F4R + 255) / 256;  // float4 of A per thread per chunk
+  constexpr int AV = ROWS * F4R / NTH;          // float4 of A per thread per chunk
+  static_assert(ROWS * F4R % NTH == 0, "activation chunk must split evenly");
   __shared__ __attribute__((aligned(16))) TW As[2][PL][ROWS * STR];
 
   const int bid = blockIdx.x;
@@ -83,7 +91,7 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(const float* __restric
   const int wave = threadIdx.x >> 6;
   const int lc = lane & 15;
   const int lg = lane >> 4;
-  const int n0 = tile * (64 * NT) + wave * (16 * NT);
+  const int n0 = tile * (16 * NT * NW) + wave * (16 * NT);
 
   floatx4 acc[MT][NT];
 #pragma unroll
@@ -95,72 +103,84 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(const float* __restric
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) wrow[nt] = W + (size_t)(n0 + nt * 16 + lc) * K + lg * VEC;
 
-  V16 bcur[U][NT], bnext[U][NT];
-  float4 areg[AV];
+  // Weight fragments and raw activations of three consecutive chunks live in
+  // registers.  At chunk c the loads of chunk c+2 are issued (activations
+  // first), chunk c is multiplied from LDS, and the activations of chunk c+1
+  // -- loaded one chunk earlier -- are split into LDS for the next chunk.
+  // Memory operations complete in issue order, so that wait leaves the
+  // weights of c+1 and everything of c+2 in flight.  The loop is unrolled
+  // three times so buffers change roles without register copies (a copy
+  // would wait for loads just issued).
+  V16 b0[U][NT], b1[U][NT], b2[U][NT];
+  float4 a0[AV], a1[AV], a2[AV];
   auto load_w = [&](V16 (&b)[U][NT], int c) {
 #pragma unroll
     for (int j = 0; j < U; ++j)
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) b[j][nt] = ld16(wrow[nt] + c * KC + j * KSTEP);
   };
-  auto load_a = [&](int c) {
+  auto load_a = [&](float4 (&areg)[AV], int c) {
 #pragma unroll
     for (int i = 0; i < AV; ++i) {
-      const int v = threadIdx.x + 256 * i;
+      const int v = threadIdx.x + NTH * i;
       const int r = v / F4R;
       const int cv = v % F4R;
-      areg[i] = (v < ROWS * F4R && r < M)
-                    ? *reinterpret_cast<const float4*>(A + (size_t)r * K + c * KC + cv * 4)
-                    : make_float4(0.f, 0.f, 0.f, 0.f);
+      if (GUARD)
+        areg[i] = r < M ? *reinterpret_cast<const float4*>(A + (size_t)r * K + c * KC + cv * 4)
+                        : make_float4(0.f, 0.f, 0.f, 0.f);
+      else
+        areg[i] = *reinterpret_cast<const float4*>(A + (size_t)r * K + c * KC + cv * 4);
     }
   };
-  auto store_a = [&](int buf) {
+  auto store_a = [&](const float4 (&areg)[AV], int buf) {
 #pragma unroll
     for (int i = 0; i < AV; ++i) {
-      const int v = threadIdx.x + 256 * i;
+      const int v = threadIdx.x + NTH * i;
       const int r = v / F4R;
       const int cv = v % F4R;
-      if (v < ROWS * F4R)
-        AS::store4(&As[buf][0][r * STR + cv * 4], &As[buf][PL - 1][r * STR + cv * 4], areg[i]);
+      AS::store4(&As[buf][0][r * STR + cv * 4], &As[buf][PL - 1][r * STR + cv * 4], areg[i]);
     }
   };
-
-  if (c_begin < c_end) {
-    load_w(bcur, c_begin);
-    load_a(c_begin);
-    store_a(0);
-  }
-  __syncthreads();
-  for (int c = c_begin; c < c_end; ++c) {
+  // bc/ac: chunk c (weights; activations already staged), an: activations of
+  // c+1 (to stage), bl/al: targets of the chunk c+2 loads.
+  auto step = [&](int c, V16 (&bc)[U][NT], float4 (&an)[AV], V16 (&bl)[U][NT],
+                  float4 (&al)[AV]) {
     const int buf = (c - c_begin) & 1;
-    const bool more = c + 1 < c_end;
-    if (more) {
-      load_w(bnext, c + 1);
-      load_a(c + 1);
+    if (c + 2 < c_end) {
+      load_a(al, c + 2);
+      load_w(bl, c + 2);
     }
 #pragma unroll
     for (int j = 0; j < U; ++j) {
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        if (mt * 16 < M) {
 #pragma unroll
-          for (int p = 0; p < PL; ++p) {
-            const V16 a = *reinterpret_cast<const V16*>(
-                &As[buf][p][(mt * 16 + lc) * STR + j * KSTEP + lg * VEC]);
+        for (int p = 0; p < PL; ++p) {
+          const V16 a = *reinterpret_cast<const V16*>(
+              &As[buf][p][(mt * 16 + lc) * STR + j * KSTEP + lg * VEC]);
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt) MF::mac(acc[mt][nt], a, bcur[j][nt]);
-          }
+          for (int nt = 0; nt < NT; ++nt) MF::mac(acc[mt][nt], a, bc[j][nt]);
         }
       }
     }
-    if (more) store_a(buf ^ 1);
+    if (c + 1 < c_end) store_a(an, buf ^ 1);
     __syncthreads();
-    if (more) {
-#pragma unroll
-      for (int j = 0; j < U; ++j)
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) bcur[j][nt] = bnext[j][nt];
+  };
+
+  if (c_begin < c_end) {
+    load_a(a0, c_begin);
+    load_w(b0, c_begin);
+    if (c_begin + 1 < c_end) {
+      load_a(a1, c_begin + 1);
+      load_w(b1, c_begin + 1);
     }
+    store_a(a0, 0);
+  }
+  __syncthreads();
+  for (int c = c_begin; c < c_end; c += 3) {
+    step(c, b0, a1, b2, a2);
+    if (c + 1 < c_end) step(c + 1, b1, a2, b0, a0);
+    if (c + 2 < c_end) step(c + 2, b2, a0, b1, a1);
   }
 
   float* out = P + (size_t)split * m_cap * N;
@@ -287,28 +307,33 @@ __global__ __launch_bounds__(256) void gemm_fat_kernel(const float* __restrict__
       }
 }
 
-template <typename TW, int MT, int NT>
+template <typename TW, int MT, int NT, int NW>
 hipError_t run_skinny(const GemmPlan& p, const float* A, const void* W, float* out,
                       const int* m_dev, int m_cap, int N, int K, hipStream_t st) {
-  const int n_tiles = N / (64 * NT);
-  hipLaunchKernelGGL((gemm_skinny_kernel<TW, MT, NT>), dim3(n_tiles * p.splits), dim3(256), 0,
-                     st, A, static_cast<const TW*>(W), out, m_dev, m_cap, N, K, n_tiles,
-                     p.splits);
+  const int n_tiles = N / (16 * NT * NW);
+  if (p.guard)
+    hipLaunchKernelGGL((gemm_skinny_kernel<TW, MT, NT, NW, true>), dim3(n_tiles * p.splits),
+                       dim3(NW * 64), 0, st, A, static_cast<const TW*>(W), out, m_dev, m_cap, N,
+                       K, n_tiles, p.splits);
+  else
+    hipLaunchKernelGGL((gemm_skinny_kernel<TW, MT, NT, NW, false>), dim3(n_tiles * p.splits),
+                       dim3(NW * 64), 0, st, A, static_cast<const TW*>(W), out, m_dev, m_cap, N,
+                       K, n_tiles, p.splits);
   return hipGetLastError();
 }
 
-template <typename TW, int NT>
+template <typename TW, int NT, int NW>
 hipError_t dispatch_mt(const GemmPlan& p, const float* A, const void* W, float* out,
                        const int* m_dev, int m_cap, int N, int K, hipStream_t st) {
   switch (p.mt) {
-    case 1: return run_skinny<TW, 1, NT>(p, A, W, out, m_dev, m_cap, N, K, st);
-    case 2: return run_skinny<TW, 2, NT>(p, A, W, out, m_dev, m_cap, N, K, st);
-    case 3: return run_skinny<TW, 3, NT>(p, A, W, out, m_dev, m_cap, N, K, st);
-    case 4: return run_skinny<TW, 4, NT>(p, A, W, out, m_dev, m_cap, N, K, st);
-    case 5: return run_skinny<TW, 5, NT>(p, A, W, out, m_dev, m_cap, N, K, st);
-    case 6: return run_skinny<TW, 6, NT>(p, A, W, out, m_dev, m_cap, N, K, st);
-    case 7: return run_skinny<TW, 7, NT>(p, A, W, out, m_dev, m_cap, N, K, st);
-    case 8: return run_skinny<TW, 8, NT>(p, A, W, out, m_dev, m_cap, N, K, st);
+    case 1: return run_skinny<TW, 1, NT, NW>(p, A, W, out, m_dev, m_cap, N, K, st);
+    case 2: return run_skinny<TW, 2, NT, NW>(p, A, W, out, m_dev, m_cap, N, K, st);
+    case 3: return run_skinny<TW, 3, NT, NW>(p, A, W, out, m_dev, m_cap, N, K, st);
+    case 4: return run_skinny<TW, 4, NT, NW>(p, A, W, out, m_dev, m_cap, N, K, st);
+    case 5: return run_skinny<TW, 5, NT, NW>(p, A, W, out, m_dev, m_cap, N, K, st);
+    case 6: return run_skinny<TW, 6, NT, NW>(p, A, W, out, m_dev, m_cap, N, K, st);
+    case 7: return run_skinny<TW, 7, NT, NW>(p, A, W, out, m_dev, m_cap, N, K, st);
+    case 8: return run_skinny<TW, 8, NT, NW>(p, A, W, out, m_dev, m_cap, N, K, st);
     default: return hipErrorInvalidValue;
   }
 }
@@ -322,8 +347,12 @@ hipError_t dispatch(const GemmPlan& p, const float* A, const void* W, float* out
                        static_cast<const TW*>(W), out, m_dev, m_cap, N, K);
     return hipGetLastError();
   }
-  return p.nt == 2 ? dispatch_mt<TW, 2>(p, A, W, out, m_dev, m_cap, N, K, st)
-                   : dispatch_mt<TW, 1>(p, A, W, out, m_dev, m_cap, N, K, st);
+  if constexpr (sizeof(TW) == 2) {   // 8-wave groups: bf16 weights only
+    if (p.nw == 8 && p.nt == 3) return dispatch_mt<TW, 3, 8>(p, A, W, out, m_dev, m_cap, N, K, st);
+    if (p.nw == 8) return dispatch_mt<TW, 2, 8>(p, A, W, out, m_dev, m_cap, N, K, st);
+  }
+  return p.nt == 2 ? dispatch_mt<TW, 2, 4>(p, A, W, out, m_dev, m_cap, N, K, st)
+                   : dispatch_mt<TW, 1, 4>(p, A, W, out, m_dev, m_cap, N, K, st);
 }
 
 }  // namespace
@@ -334,11 +363,14 @@ bool gemm_shape_ok(DType t, int N, int K) {
   return N > 0 && K > 0 && N % 128 == 0 && K % gemm_k_chunk(t) == 0;
 }
 
+// Skinny plan: a column group per workgroup as wide as still gives at least
+// 16 groups (256 columns = 8 waves x 32, else 128 = 4 x 32, else 64 = 4 x 16),
+// then K splits so that the grid is about target_wgs workgroups.
 GemmPlan plan_gemm(DType t, int m_cap, int N, int K, int target_wgs) {
   GemmPlan p{};
   if (m_cap > 128) {
     p.kind = 1;
-    p.mt = p.nt = 0;
+    p.mt = p.nt = p.nw = 0;
     p.splits = 1;
     p.grid = ((N + 127) / 128) * ((m_cap + 127) / 128);
     return p;
@@ -346,10 +378,20 @@ GemmPlan plan_gemm(DType t, int m_cap, int N, int K, int target_wgs) {
   p.kind = 0;
   p.mt = (m_cap + 15) / 16;
   if (p.mt < 1) p.mt = 1;
+  p.guard = (m_cap % 16) != 0;   // exact-size operands with ragged rows only
   const int chunks = K / gemm_k_chunk(t);
-  p.nt = (N / 128 >= target_wgs / 2) ? 2 : 1;
-  const int n_tiles = N / (64 * p.nt);
-  int s = (target_wgs + n_tiles - 1) / n_tiles;
+  if (t == DType::BF16 && N % 256 == 0 && N / 256 >= 32 && p.mt <= 4) {
+    p.nt = 2;
+    p.nw = 8;
+  } else if (N % 128 == 0 && N / 128 >= 16) {
+    p.nt = 2;
+    p.nw = 4;
+  } else {
+    p.nt = 1;
+    p.nw = 4;
+  }
+  const int n_tiles = N / (16 * p.nt * p.nw);
+  int s = (target_wgs + n_tiles / 2) / n_tiles;
   if (s < 1) s = 1;
   if (s > chunks) s = chunks;
   p.splits = s;

@@ -29,7 +29,9 @@ struct PassTable {
 // ---- GEMM: out[s][m][n] = sum over K-slice s of A[m][k] * W[n][k] ---------
 struct GemmPlan {
   int kind;      // 0 = skinny (rows <= 128), 1 = fat
-  int mt, nt;    // skinny: 16-row tiles and 64-column groups per workgroup
+  int mt, nt;    // skinny: 16-row tiles; 16-column tiles per wave
+  int nw;        // skinny: waves per workgroup
+  int guard;     // skinny: 1 = A has exactly m_cap rows; 0 = A readable up to 16*mt rows
   int splits;    // K splits (skinny only; fat = 1)
   int grid;
 };

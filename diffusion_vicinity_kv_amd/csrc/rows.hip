@@ -53,39 +53,66 @@ __global__ __launch_bounds__(kThreads) void embed_kernel(PassTable tb, const int
   }
 }
 
+// init + sum over s < S of p[s * stride] (float4), in split order.  Up to
+// eight partials are loaded before any is added so that their latencies
+// overlap.
+__device__ __forceinline__ float4 add_partials4(float4 acc, const float* p, size_t stride, int S) {
+  for (int s0 = 0; s0 < S; s0 += 8) {
+    const int n = min(8, S - s0);
+    float4 v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      if (k < n) v[k] = *reinterpret_cast<const float4*>(p + (s0 + k) * stride);
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      if (k < n) {
+        acc.x += v[k].x;
+        acc.y += v[k].y;
+        acc.z += v[k].z;
+        acc.w += v[k].w;
+      }
+  }
+  return acc;
+}
+
+constexpr int kNormThreads = 1024;
+
 // x[m] += sum_s P[s][m] (split order); a[m] = x[m] / sqrt(mean(x^2) + eps) * g.
+// One workgroup of 1024 threads per row, one float4 (d <= 4096) or two per
+// thread.
 template <typename T>
-__global__ __launch_bounds__(kThreads) void add_rmsnorm_kernel(const int* __restrict__ nrows, int m_cap,
-                                                               float* __restrict__ x,
-                                                               const float* __restrict__ P, int S,
-                                                               size_t p_stride,
-                                                               const T* __restrict__ g, float eps,
-                                                               float* __restrict__ a, int d) {
-  constexpr int MAXE = 32;   // d <= 8192
-  __shared__ float red[kThreads / 64];
+__global__ __launch_bounds__(kNormThreads) void add_rmsnorm_kernel(
+    const int* __restrict__ nrows, int m_cap, float* __restrict__ x, const float* __restrict__ P,
+    int S, size_t p_stride, const T* __restrict__ g, float eps, float* __restrict__ a, int d) {
+  constexpr int MAXV = 2;   // d <= 8192
+  __shared__ float red[kNormThreads / 64];
   const int m = blockIdx.x;
   if (m >= min(*nrows, m_cap)) return;
-  float v[MAXE];
+  const int d4 = d / 4;
+  float4* xr = reinterpret_cast<float4*>(x + (size_t)m * d);
+  float4 v[MAXV];
   float ss = 0.f;
-  float* xr = x + (size_t)m * d;
 #pragma unroll
-  for (int e = 0; e < MAXE; ++e) {
-    const int i = threadIdx.x + e * kThreads;
-    if (i < d) {
-      float xv = xr[i];
-      for (int s = 0; s < S; ++s) xv += P[s * p_stride + (size_t)m * d + i];
+  for (int e = 0; e < MAXV; ++e) {
+    const int i = threadIdx.x + e * kNormThreads;
+    if (i < d4) {
+      float4 xv = add_partials4(xr[i], P + (size_t)m * d + 4 * i, p_stride, S);
       if (S > 0) xr[i] = xv;
       v[e] = xv;
-      ss += xv * xv;
+      ss += xv.x * xv.x + xv.y * xv.y + xv.z * xv.z + xv.w * xv.w;
     }
   }
-  const float tot = block_sum<kThreads / 64>(ss, red);
+  const float tot = block_sum<kNormThreads / 64>(ss, red);
   const float inv = 1.f / sqrtf(tot / d + eps);
-  float* ar = a + (size_t)m * d;
+  float4* ar = reinterpret_cast<float4*>(a + (size_t)m * d);
 #pragma unroll
-  for (int e = 0; e < MAXE; ++e) {
-    const int i = threadIdx.x + e * kThreads;
-    if (i < d) ar[i] = v[e] * inv * to_f(g[i]);
+  for (int e = 0; e < MAXV; ++e) {
+    const int i = threadIdx.x + e * kNormThreads;
+    if (i < d4) {
+      const T* gi = g + 4 * i;
+      ar[i] = make_float4(v[e].x * inv * to_f(gi[0]), v[e].y * inv * to_f(gi[1]),
+                          v[e].z * inv * to_f(gi[2]), v[e].w * inv * to_f(gi[3]));
+    }
   }
 }
 
@@ -94,8 +121,10 @@ __global__ __launch_bounds__(kThreads) void add_rmsnorm_kernel(const int* __rest
 // attention and scatter k, v into the cache at the row's position -- before
 // any query of this layer reads the cache (dInfer news article, section
 // "削减计算成本：邻近KV缓存刷新": only the window's KV is recomputed).
+constexpr int kQkvThreads = 512;
+
 template <typename T>
-__global__ __launch_bounds__(kThreads) void qkv_rope_scatter_kernel(
+__global__ __launch_bounds__(kQkvThreads) void qkv_rope_scatter_kernel(
     PassTable tb, int m_cap, const float* __restrict__ P, int S, size_t p_stride, int d, int H,
     int hd, const float* __restrict__ rope_cs, float* __restrict__ q_out, T* __restrict__ kc,
     T* __restrict__ vc, int max_len) {
@@ -104,75 +133,89 @@ __global__ __launch_bounds__(kThreads) void qkv_rope_scatter_kernel(
   const int r = tb.row_req[m];
   const int pos = tb.row_pos[m];
   const int half = hd / 2;
-  const int N3 = 3 * d;
-  const float* pr = P + (size_t)m * N3;
+  const int hq = half / 4;                         // float4 groups per half head
+  const float* pr = P + (size_t)m * 3 * d;
   const float* cs = rope_cs + (size_t)pos * hd;   // [pos][cos half | sin half]
-  for (int i = threadIdx.x; i < H * half; i += kThreads) {
-    const int h = i / half;
-    const int j = i % half;
+  const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int i = threadIdx.x; i < H * hq; i += kQkvThreads) {
+    const int h = i / hq;
+    const int j = (i % hq) * 4;
     const int c0 = h * hd + j;
     const int c1 = c0 + half;
-    float q0 = 0.f, q1 = 0.f, k0 = 0.f, k1 = 0.f, v0 = 0.f, v1 = 0.f;
-    for (int s = 0; s < S; ++s) {
-      const float* ps = pr + s * p_stride;
-      q0 += ps[c0];
-      q1 += ps[c1];
-      k0 += ps[d + c0];
-      k1 += ps[d + c1];
-      v0 += ps[2 * d + c0];
-      v1 += ps[2 * d + c1];
-    }
-    const float c = cs[j];
-    const float sn = cs[half + j];
+    const float4 q0 = add_partials4(z4, pr + c0, p_stride, S);
+    const float4 q1 = add_partials4(z4, pr + c1, p_stride, S);
+    const float4 k0 = add_partials4(z4, pr + d + c0, p_stride, S);
+    const float4 k1 = add_partials4(z4, pr + d + c1, p_stride, S);
+    const float4 v0 = add_partials4(z4, pr + 2 * d + c0, p_stride, S);
+    const float4 v1 = add_partials4(z4, pr + 2 * d + c1, p_stride, S);
+    const float4 c = *reinterpret_cast<const float4*>(cs + j);
+    const float4 sn = *reinterpret_cast<const float4*>(cs + half + j);
     float* qr = q_out + (size_t)m * d;
-    qr[c0] = q0 * c - q1 * sn;
-    qr[c1] = q1 * c + q0 * sn;
+    *reinterpret_cast<float4*>(qr + c0) =
+        make_float4(q0.x * c.x - q1.x * sn.x, q0.y * c.y - q1.y * sn.y, q0.z * c.z - q1.z * sn.z,
+                    q0.w * c.w - q1.w * sn.w);
+    *reinterpret_cast<float4*>(qr + c1) =
+        make_float4(q1.x * c.x + q0.x * sn.x, q1.y * c.y + q0.y * sn.y, q1.z * c.z + q0.z * sn.z,
+                    q1.w * c.w + q0.w * sn.w);
     const size_t cb = (((size_t)r * H + h) * max_len + pos) * hd;
-    kc[cb + j] = from_f<T>(k0 * c - k1 * sn);
-    kc[cb + j + half] = from_f<T>(k1 * c + k0 * sn);
-    vc[cb + j] = from_f<T>(v0);
-    vc[cb + j + half] = from_f<T>(v1);
+    T* kp = kc + cb;
+    T* vp = vc + cb;
+    const float ka[4] = {k0.x * c.x - k1.x * sn.x, k0.y * c.y - k1.y * sn.y,
+                         k0.z * c.z - k1.z * sn.z, k0.w * c.w - k1.w * sn.w};
+    const float kb[4] = {k1.x * c.x + k0.x * sn.x, k1.y * c.y + k0.y * sn.y,
+                         k1.z * c.z + k0.z * sn.z, k1.w * c.w + k0.w * sn.w};
+    const float va[4] = {v0.x, v0.y, v0.z, v0.w};
+    const float vb[4] = {v1.x, v1.y, v1.z, v1.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      kp[j + e] = from_f<T>(ka[e]);
+      kp[j + half + e] = from_f<T>(kb[e]);
+      vp[j + e] = from_f<T>(va[e]);
+      vp[j + half + e] = from_f<T>(vb[e]);
+    }
   }
 }
 
 // act[m][f] = silu(gate) * up with gate, up summed over the split-K partials
-// of the fused [gate | up] projection.
+// of the fused [gate | up] projection (float4 per thread).
 __global__ __launch_bounds__(kThreads) void swiglu_kernel(const int* __restrict__ nrows, int m_cap,
                                                           const float* __restrict__ P, int S,
                                                           size_t p_stride, int F,
                                                           float* __restrict__ act) {
   const int M = min(*nrows, m_cap);
-  const size_t total = (size_t)M * F;
+  const int F4 = F / 4;
+  const size_t total = (size_t)M * F4;
+  const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
   for (size_t idx = (size_t)blockIdx.x * kThreads + threadIdx.x; idx < total;
        idx += (size_t)gridDim.x * kThreads) {
-    const size_t m = idx / F;
-    const size_t f = idx % F;
+    const size_t m = idx / F4;
+    const size_t f = (idx % F4) * 4;
     const float* pr = P + m * 2 * F;
-    float g = 0.f, u = 0.f;
-    for (int s = 0; s < S; ++s) {
-      g += pr[s * p_stride + f];
-      u += pr[s * p_stride + F + f];
-    }
-    act[idx] = g / (1.f + expf(-g)) * u;
+    const float4 g = add_partials4(z4, pr + f, p_stride, S);
+    const float4 u = add_partials4(z4, pr + F + f, p_stride, S);
+    *reinterpret_cast<float4*>(act + m * F + f) =
+        make_float4(g.x / (1.f + expf(-g.x)) * u.x, g.y / (1.f + expf(-g.y)) * u.y,
+                    g.z / (1.f + expf(-g.z)) * u.z, g.w / (1.f + expf(-g.w)) * u.w);
   }
 }
 
 // Block rows only: residual add of the last layer, final RMSNorm, and the
 // row's planting for the vocab statistics.
 template <typename T>
-__global__ __launch_bounds__(kThreads) void final_norm_kernel(
+__global__ __launch_bounds__(kNormThreads) void final_norm_kernel(
     PassTable tb, int B, const float* __restrict__ x, const float* __restrict__ P, int S,
     size_t p_stride, const T* __restrict__ g, float eps, float* __restrict__ out, int d,
     const int* __restrict__ plant_id, const float* __restrict__ plant_bias, int max_len,
     int* __restrict__ row_plant_id, float* __restrict__ row_plant_bias) {
-  constexpr int MAXE = 32;
-  __shared__ float red[kThreads / 64];
+  constexpr int MAXV = 2;
+  __shared__ float red[kNormThreads / 64];
   const int rr = blockIdx.x;
   const int r = rr / B;
   const int j = rr % B;
-  float* orow = out + (size_t)rr * d;
+  const int d4 = d / 4;
+  float4* orow = reinterpret_cast<float4*>(out + (size_t)rr * d);
   if (!tb.req_active[r] || tb.req_nrows[r] == 0) {
-    for (int i = threadIdx.x; i < d; i += kThreads) orow[i] = 0.f;
+    for (int i = threadIdx.x; i < d4; i += kNormThreads) orow[i] = make_float4(0.f, 0.f, 0.f, 0.f);
     if (threadIdx.x == 0) {
       row_plant_id[rr] = -1;
       row_plant_bias[rr] = 0.f;
@@ -183,24 +226,28 @@ __global__ __launch_bounds__(kThreads) void final_norm_kernel(
   const int lo = tb.row_pos[off];
   const int bs = tb.req_bs[r];
   const int m = off + (bs - lo) + j;
-  float v[MAXE];
+  const float4* xr = reinterpret_cast<const float4*>(x + (size_t)m * d);
+  float4 v[MAXV];
   float ss = 0.f;
 #pragma unroll
-  for (int e = 0; e < MAXE; ++e) {
-    const int i = threadIdx.x + e * kThreads;
-    if (i < d) {
-      float xv = x[(size_t)m * d + i];
-      for (int s = 0; s < S; ++s) xv += P[s * p_stride + (size_t)m * d + i];
+  for (int e = 0; e < MAXV; ++e) {
+    const int i = threadIdx.x + e * kNormThreads;
+    if (i < d4) {
+      const float4 xv = add_partials4(xr[i], P + (size_t)m * d + 4 * i, p_stride, S);
       v[e] = xv;
-      ss += xv * xv;
+      ss += xv.x * xv.x + xv.y * xv.y + xv.z * xv.z + xv.w * xv.w;
     }
   }
-  const float tot = block_sum<kThreads / 64>(ss, red);
+  const float tot = block_sum<kNormThreads / 64>(ss, red);
   const float inv = 1.f / sqrtf(tot / d + eps);
 #pragma unroll
-  for (int e = 0; e < MAXE; ++e) {
-    const int i = threadIdx.x + e * kThreads;
-    if (i < d) orow[i] = v[e] * inv * to_f(g[i]);
+  for (int e = 0; e < MAXV; ++e) {
+    const int i = threadIdx.x + e * kNormThreads;
+    if (i < d4) {
+      const T* gi = g + 4 * i;
+      orow[i] = make_float4(v[e].x * inv * to_f(gi[0]), v[e].y * inv * to_f(gi[1]),
+                            v[e].z * inv * to_f(gi[2]), v[e].w * inv * to_f(gi[3]));
+    }
   }
   if (threadIdx.x == 0) {
     row_plant_id[rr] = plant_id ? plant_id[(size_t)r * max_len + bs + j] : -1;
@@ -232,8 +279,8 @@ hipError_t launch_embed(DType t, PassTable tb, int m_cap, const int* tokens, int
 hipError_t launch_add_rmsnorm(DType t, const int* nrows, int m_cap, float* x, const float* P,
                               int S, size_t p_stride, const void* g, float eps, float* a, int d,
                               hipStream_t st) {
-  if (d > 32 * kThreads) return hipErrorInvalidValue;
-  DISPATCH_T(t, hipLaunchKernelGGL((add_rmsnorm_kernel<T>), dim3(m_cap), dim3(kThreads), 0, st,
+  if (d > 8 * kNormThreads || d % 4 != 0) return hipErrorInvalidValue;
+  DISPATCH_T(t, hipLaunchKernelGGL((add_rmsnorm_kernel<T>), dim3(m_cap), dim3(kNormThreads), 0, st,
                                    nrows, m_cap, x, P, S, p_stride, static_cast<const T*>(g), eps,
                                    a, d));
   return hipGetLastError();
@@ -242,7 +289,7 @@ hipError_t launch_add_rmsnorm(DType t, const int* nrows, int m_cap, float* x, co
 hipError_t launch_qkv_rope_scatter(DType t, PassTable tb, int m_cap, const float* P, int S,
                                    size_t p_stride, int d, int H, int hd, const float* rope_cs,
                                    float* q_out, void* kc, void* vc, int max_len, hipStream_t st) {
-  DISPATCH_T(t, hipLaunchKernelGGL((qkv_rope_scatter_kernel<T>), dim3(m_cap), dim3(kThreads), 0,
+  DISPATCH_T(t, hipLaunchKernelGGL((qkv_rope_scatter_kernel<T>), dim3(m_cap), dim3(kQkvThreads), 0,
                                    st, tb, m_cap, P, S, p_stride, d, H, hd, rope_cs, q_out,
                                    static_cast<T*>(kc),
                                    static_cast<T*>(vc), max_len));
@@ -251,9 +298,10 @@ hipError_t launch_qkv_rope_scatter(DType t, PassTable tb, int m_cap, const float
 
 hipError_t launch_swiglu(const int* nrows, int m_cap, const float* P, int S, size_t p_stride,
                          int F, float* act, hipStream_t st) {
-  size_t total = (size_t)m_cap * F;
+  if (F % 4 != 0) return hipErrorInvalidValue;
+  size_t total = (size_t)m_cap * F / 4;
   int blocks = (int)((total + kThreads - 1) / kThreads);
-  if (blocks > 4096) blocks = 4096;
+  if (blocks > 8192) blocks = 8192;
   hipLaunchKernelGGL(swiglu_kernel, dim3(blocks), dim3(kThreads), 0, st, nrows, m_cap, P, S,
                      p_stride, F, act);
   return hipGetLastError();
@@ -264,8 +312,8 @@ hipError_t launch_final_norm(DType t, PassTable tb, int batch, int B, const floa
                              float* out, int d, const int* plant_id, const float* plant_bias,
                              int max_len, int* row_plant_id, float* row_plant_bias,
                              hipStream_t st) {
-  if (d > 32 * kThreads) return hipErrorInvalidValue;
-  DISPATCH_T(t, hipLaunchKernelGGL((final_norm_kernel<T>), dim3(batch * B), dim3(kThreads), 0, st,
+  if (d > 8 * kNormThreads || d % 4 != 0) return hipErrorInvalidValue;
+  DISPATCH_T(t, hipLaunchKernelGGL((final_norm_kernel<T>), dim3(batch * B), dim3(kNormThreads), 0, st,
                                    tb, B, x, P, S, p_stride, static_cast<const T*>(g), eps,
                                    out, d, plant_id, plant_bias, max_len,
                                    row_plant_id, row_plant_bias));

@@ -105,25 +105,30 @@ bool make_layout(const dinfer_model_cfg* m, const dinfer_decode_cfg* dc, int max
   const int win = std::min(max_len, l.B + 2 * l.w);
   l.m_step = max_batch * win;
   l.m_ref = max_batch * max_len;
-  l.m_all = std::max(l.m_step, l.m_ref);
+  l.m_all = (std::max(l.m_step, l.m_ref) + 15) / 16 * 16;   // 16-row padded buffers
   l.lm_rows = max_batch * l.B;
-  const int tw = 512;
+  const int tw = 256;   // about one skinny workgroup per CU
   l.g_qkv_s = plan_gemm(dt, l.m_step, 3 * d, d, tw);
   l.g_o_s = plan_gemm(dt, l.m_step, d, d, tw);
   l.g_gu_s = plan_gemm(dt, l.m_step, 2 * F, d, tw);
   l.g_d_s = plan_gemm(dt, l.m_step, d, F, tw);
   l.g_lm = plan_gemm(dt, l.lm_rows, V, d, tw);
-  if (l.g_lm.kind == 0 && l.g_lm.splits != 1) l.g_lm.splits = 1, l.g_lm.grid = V / (64 * l.g_lm.nt);
+  if (l.g_lm.kind == 0 && l.g_lm.splits != 1)
+    l.g_lm.splits = 1, l.g_lm.grid = V / (16 * l.g_lm.nt * l.g_lm.nw);
+  // the step's activation buffers hold at least 16*mt rows: no row guards
+  for (GemmPlan* g : {&l.g_qkv_s, &l.g_o_s, &l.g_gu_s, &l.g_d_s, &l.g_lm}) g->guard = 0;
   l.g_qkv_r = plan_gemm(dt, l.m_ref, 3 * d, d, tw);
   l.g_o_r = plan_gemm(dt, l.m_ref, d, d, tw);
   l.g_gu_r = plan_gemm(dt, l.m_ref, 2 * F, d, tw);
   l.g_d_r = plan_gemm(dt, l.m_ref, d, F, tw);
+  for (GemmPlan* g : {&l.g_qkv_r, &l.g_o_r, &l.g_gu_r, &l.g_d_r}) g->guard = 0;
   auto pe = [](const GemmPlan& g, int m_cap, int N) { return (size_t)g.splits * m_cap * N; };
   l.part_elems = std::max({pe(l.g_qkv_s, l.m_step, 3 * d), pe(l.g_o_s, l.m_step, d),
                            pe(l.g_gu_s, l.m_step, 2 * F), pe(l.g_d_s, l.m_step, d),
                            pe(l.g_qkv_r, l.m_ref, 3 * d), pe(l.g_o_r, l.m_ref, d),
                            pe(l.g_gu_r, l.m_ref, 2 * F), pe(l.g_d_r, l.m_ref, d)});
-  l.a_step = plan_attention(max_batch, win, max_len, l.H, 512);
+  // about one workgroup per CU: more key splits only add fp32 partial traffic
+  l.a_step = plan_attention(max_batch, win, max_len, l.H, 256);
   l.a_ref = plan_attention(max_batch, max_len, max_len, l.H, 512);
   l.attn_o_elems = std::max((size_t)l.a_step.n_split * l.m_step, (size_t)l.a_ref.n_split * l.m_ref) *
                    l.H * l.hd;
@@ -151,7 +156,7 @@ bool make_layout(const dinfer_model_cfg* m, const dinfer_decode_cfg* dc, int max
   l.off_part = take(l.part_elems * 4);
   l.off_ao = take(l.attn_o_elems * 4);
   l.off_aml = take(l.attn_ml_elems * 4);
-  l.off_hf = take((size_t)l.lm_rows * d * 4);
+  l.off_hf = take((size_t)(l.lm_rows + 15) / 16 * 16 * d * 4);
   l.off_logits = take((size_t)l.lm_rows * V * 4);
   l.off_rpid = take((size_t)l.lm_rows * 4);
   l.off_rpb = take((size_t)l.lm_rows * 4);
@@ -782,7 +787,7 @@ size_t dinfer_linear_out_elems(int32_t M, int32_t N, int32_t K, int32_t dtype) {
   if (M < 1 || (dtype != DINFER_F32 && dtype != DINFER_BF16)) return 0;
   const DType dt = dtype == DINFER_F32 ? DType::F32 : DType::BF16;
   if (!gemm_shape_ok(dt, N, K)) return 0;
-  const GemmPlan p = plan_gemm(dt, M, N, K, 512);
+  const GemmPlan p = plan_gemm(dt, M, N, K, 256);
   return (size_t)p.splits * M * N;
 }
 
@@ -793,7 +798,7 @@ dinfer_status dinfer_linear(const float* d_A, const void* d_W, float* d_out, int
   if (dtype != DINFER_F32 && dtype != DINFER_BF16) return fail(DINFER_E_ARG, "bad dtype");
   const DType dt = dtype == DINFER_F32 ? DType::F32 : DType::BF16;
   if (!gemm_shape_ok(dt, N, K)) return fail(DINFER_E_UNSUPPORTED, "N % 128 or K chunk multiple");
-  const GemmPlan p = plan_gemm(dt, M, N, K, 512);
+  const GemmPlan p = plan_gemm(dt, M, N, K, 256);
   if (h_splits) *h_splits = p.splits;
   HIP_TRY(launch_gemm(p, dt, d_A, d_W, d_out, nullptr, M, N, K, static_cast<hipStream_t>(stream)));
   return DINFER_OK;
