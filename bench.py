@@ -39,6 +39,9 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 KERNEL = "gemm_skinny_kernel<bf16, MT=4, NT=2>"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_skinny_qkv_gateup_dense8b_traffic.json")
+MODEL_NAMES = {"dense8b_b1": "dense 8B-shaped dLLM", "dense8b_b16": "dense 8B-shaped dLLM",
+               "dense8b_long_b4": "dense 8B-shaped dLLM, 8K prompt",
+               "moe_b1": "MoE dLLM (64 experts top-8 + shared)", "tiny_f32": "tiny dLLM"}
 
 
 def log(msg):
@@ -56,7 +59,9 @@ def dominant_kernel_timing(wc, weights, iters=40, with_events=True):
     import torch
     from diffusion_vicinity_kv_amd import binding as B
     m = wc.model
-    d, F = m.d_model, m.ffn_dim
+    d = m.d_model
+    F = m.shared_ffn if m.is_moe else m.ffn_dim
+    gu_key = "shared_gate_up" if m.is_moe else "w_gate_up"
     rows = min(wc.max_len, wc.decode.block_len + 2 * wc.decode.vicinity_w) * wc.batch
     A = torch.randn(rows, d, device="cuda")
     lib = B.load()
@@ -66,7 +71,7 @@ def dominant_kernel_timing(wc, weights, iters=40, with_events=True):
     shapes = []
     for i in range(iters):
         L = layers[i % len(layers)]
-        W = L["wqkv"] if i % 2 == 0 else L["w_gate_up"]
+        W = L["wqkv"] if i % 2 == 0 else L[gu_key]
         shapes.append(W)
     for W in shapes[:4]:
         B.linear(A, W, out)
@@ -103,16 +108,17 @@ def cpu_baseline(wc, gpu_refreshes_per_run, gpu_steps_per_run, committed_per_run
     w = synth.make_weights(m, wc.seed, device="cpu", layers=[0])
     req = synth.make_requests(wc)
     om = oracle.OracleModel(m, w, layers=[0])
+    rb = req.get("router_bias")
     run = oracle.OracleRun(om, wc.decode, req["tokens"][0].numpy(), int(req["prompt_len"][0]),
                            int(req["gen_len"][0]), req["plant_id"][0].numpy(),
-                           float(req["plant_bias"][0]))
+                           float(req["plant_bias"][0]), None if rb is None else rb[0].numpy())
     t0 = time.perf_counter()
     run.start_block(0)                           # one layer of the full refresh
     t_ref_layer = time.perf_counter() - t0
     lo, hi = run.window()
     t0 = time.perf_counter()
     e = run.window_embeddings(lo, hi)
-    h = om.forward_rows(run.cache, np.arange(lo, hi), e, run.L)
+    h = om.forward_rows(run.cache, np.arange(lo, hi), e, run.L, run._router_bias_block())
     t_step_layer = time.perf_counter() - t0
     t0 = time.perf_counter()
     logits = om.logits(h[run.bs - lo: run.be - lo])
@@ -192,10 +198,15 @@ def main():
     plant_id = req["plant_id"].cuda().contiguous()
     plant_bias = req["plant_bias"].cuda().contiguous()
     P, G = req["prompt_len"].tolist(), req["gen_len"].tolist()
+    rb = req.get("router_bias")
+    router_bias = None if rb is None else rb.cuda().contiguous()
+
+    def bind():
+        tokens.copy_(tokens0)
+        eng.set_batch(tokens, P, G, plant_id, plant_bias, router_bias)
 
     def one_run():
-        tokens.copy_(tokens0)
-        eng.set_batch(tokens, P, G, plant_id, plant_bias)
+        bind()
         return eng.run_to_completion()
 
     for i in range(args.warmup):
@@ -213,15 +224,13 @@ def main():
     value = committed / elapsed
 
     # denoise-step latency: graph replays of the first block, event-timed
-    tokens.copy_(tokens0)
-    eng.set_batch(tokens, P, G, plant_id, plant_bias)
+    bind()
     eng.refresh_kv()
     n_lat = max(args.unroll, (wc.decode.block_len // args.unroll) * args.unroll)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     st = torch.cuda.current_stream()
     eng.step_graph(args.unroll)                     # graph captured, block warmed
-    tokens.copy_(tokens0)
-    eng.set_batch(tokens, P, G, plant_id, plant_bias)
+    bind()
     eng.refresh_kv()
     torch.cuda.synchronize()
     e0.record(st)
@@ -241,9 +250,14 @@ def main():
     steps_per_run = sum(r["steps"] for r in runs) / len(runs)
     refreshes_per_run = sum(r["refreshes"] for r in runs) / len(runs)
     committed_per_run = committed / len(runs)
-    # weights once + KV read once per layer + window KV write, per step
-    d, F, V, nl = m.d_model, m.ffn_dim, m.vocab, m.n_layers
-    weight_bytes = (nl * (3 * d * d + d * d + 3 * d * F) + V * d) * 2
+    # weights once + KV read once per layer + window KV write, per step.  MoE:
+    # every expert counts (a 64+-row window routes rows to nearly all of them)
+    d, V, nl = m.d_model, m.vocab, m.n_layers
+    if m.is_moe:
+        ffn_w = m.n_experts * (3 * d * m.expert_ffn + d) + 3 * d * m.shared_ffn
+    else:
+        ffn_w = 3 * d * m.ffn_dim
+    weight_bytes = (nl * (3 * d * d + d * d + ffn_w) + V * d) * 2
     kv_bytes = nl * wc.batch * 2 * (wc.max_len * d * 2 + rows // wc.batch * d * 2)
     step_bytes = weight_bytes + kv_bytes
 
@@ -254,7 +268,7 @@ def main():
                            committed_per_run)
 
     out = {
-        "metric": "committed tokens/s (batch 1, dense 8B-shaped dLLM, bf16)",
+        "metric": f"committed tokens/s (batch {wc.batch}, {MODEL_NAMES.get(args.workload, args.workload)}, bf16)",
         "value": round(value, 3),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -265,8 +279,9 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
-        "data": "synthetic: N(0,0.02) random-init weights of the dense 8B shape, random prompt ids, "
-                "seeded planting",
+        "data": f"synthetic: N(0,0.02) random-init weights of the "
+                f"{MODEL_NAMES.get(args.workload, args.workload)} shape, random prompt ids, "
+                "seeded planting" + (", seeded per-block router preference bias" if m.is_moe else ""),
         "config": {"workload": args.workload, "batch": wc.batch, "prompt_len": wc.prompt_len[0],
                    "gen_len": wc.gen_len, "block_len": wc.decode.block_len,
                    "vicinity_w": wc.decode.vicinity_w, "layers": nl, "d_model": d,

@@ -58,7 +58,9 @@ class StepView(C.Structure):
         (n, C.c_void_p) for n in ("logits", "argmax", "conf", "lse", "topk_id", "topk_p", "credit",
                                   "tracked", "smooth_id", "smooth_p", "smooth_valid",
                                   "commit_mask", "block_done", "step_count", "commit_count",
-                                  "kv_k", "kv_v")]
+                                  "kv_k", "kv_v")] + [
+        ("moe_top_k", C.c_int32), ("moe_sel", C.c_void_p), ("moe_gate", C.c_void_p),
+        ("moe_experts", C.c_int32), ("moe_logits", C.c_void_p), ("ffn_in", C.c_void_p)]
 
 
 class DinferError(RuntimeError):

@@ -58,13 +58,16 @@ template <> struct ASplit<float> {
 // finite or not -- they only feed output rows that are never stored), so the
 // activation loads and MFMAs carry no per-row conditions.  GUARD = true: rows
 // >= M are read as zeros (exact-size operands of the standalone entry point).
+//
+// One workgroup's tile: rows [0, M) of A (row r at A + (arow ? arow[r] : r) * K)
+// times weight rows [n_tile, n_tile + 16*NT*NW) of W over K chunks
+// [c_begin, c_end), written to out[row * ldo + column].
 template <typename TW, int MT, int NT, int NW, bool GUARD>
-__global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(const float* __restrict__ A,
-                                                          const TW* __restrict__ W,
-                                                          float* __restrict__ P,
-                                                          const int* __restrict__ m_dev,
-                                                          int m_cap, int N, int K, int n_tiles,
-                                                          int S) {
+__device__ __forceinline__ void skinny_tile(const float* __restrict__ A,
+                                            const int* __restrict__ arow, int M,
+                                            const TW* __restrict__ W, int K,
+                                            float* __restrict__ out, int ldo, int n_tile,
+                                            int c_begin, int c_end) {
   using MF = Mfma<TW>;
   using AS = ASplit<TW>;
   constexpr int PL = AS::PLANES;
@@ -80,18 +83,11 @@ __global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(const float* __res
   static_assert(ROWS * F4R % NTH == 0, "activation chunk must split evenly");
   __shared__ __attribute__((aligned(16))) TW As[2][PL][ROWS * STR];
 
-  const int bid = blockIdx.x;
-  const int tile = bid % n_tiles;
-  const int split = bid / n_tiles;
-  const int C = K / KC;
-  const int c_begin = (split * C) / S;
-  const int c_end = ((split + 1) * C) / S;
-  const int M = m_dev ? min(*m_dev, m_cap) : m_cap;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int lc = lane & 15;
   const int lg = lane >> 4;
-  const int n0 = tile * (16 * NT * NW) + wave * (16 * NT);
+  const int n0 = n_tile + wave * (16 * NT);
 
   floatx4 acc[MT][NT];
 #pragma unroll
@@ -125,11 +121,12 @@ __global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(const float* __res
       const int v = threadIdx.x + NTH * i;
       const int r = v / F4R;
       const int cv = v % F4R;
+      const size_t ar = arow ? (size_t)arow[GUARD ? min(r, M - 1) : r] : (size_t)r;
       if (GUARD)
-        areg[i] = r < M ? *reinterpret_cast<const float4*>(A + (size_t)r * K + c * KC + cv * 4)
+        areg[i] = r < M ? *reinterpret_cast<const float4*>(A + ar * K + c * KC + cv * 4)
                         : make_float4(0.f, 0.f, 0.f, 0.f);
       else
-        areg[i] = *reinterpret_cast<const float4*>(A + (size_t)r * K + c * KC + cv * 4);
+        areg[i] = *reinterpret_cast<const float4*>(A + ar * K + c * KC + cv * 4);
     }
   };
   auto store_a = [&](const float4 (&areg)[AV], int buf) {
@@ -183,7 +180,6 @@ __global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(const float* __res
     if (c + 2 < c_end) step(c + 2, b2, a0, b1, a1);
   }
 
-  float* out = P + (size_t)split * m_cap * N;
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -191,9 +187,51 @@ __global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(const float* __res
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int row = mt * 16 + lg * 4 + i;
-        if (row < M) out[(size_t)row * N + n0 + nt * 16 + lc] = acc[mt][nt][i];
+        if (row < M) out[(size_t)row * ldo + n0 + nt * 16 + lc] = acc[mt][nt][i];
       }
 }
+
+template <typename TW, int MT, int NT, int NW, bool GUARD>
+__global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(const float* __restrict__ A,
+                                                              const TW* __restrict__ W,
+                                                              float* __restrict__ P,
+                                                              const int* __restrict__ m_dev,
+                                                              int m_cap, int N, int K,
+                                                              int n_tiles, int S) {
+  constexpr int KC = 4 * Mfma<TW>::KSTEP;
+  const int bid = blockIdx.x;
+  const int tile = bid % n_tiles;
+  const int split = bid / n_tiles;
+  const int C = K / KC;
+  const int M = m_dev ? min(*m_dev, m_cap) : m_cap;
+  skinny_tile<TW, MT, NT, NW, GUARD>(A, nullptr, M, W, K, P + (size_t)split * m_cap * N, N,
+                                     tile * (16 * NT * NW), (split * C) / S, ((split + 1) * C) / S);
+}
+
+// Grouped projection of the MoE experts: workgroup (expert e, column group,
+// 64-row tile) multiplies rows [off_e + 64 t, min(off_e + count_e, +64)) of
+// the packed assignment list -- gathered from A through row_of[] when given,
+// else read in place -- with expert e's weights W + e*N*K.
+template <typename TW, int NT, int NW>
+__global__ __launch_bounds__(NW * 64) void gemm_grouped_kernel(
+    const float* __restrict__ A, const int* __restrict__ row_of, const int* __restrict__ e_count,
+    const int* __restrict__ e_off, const TW* __restrict__ W, float* __restrict__ out, int N, int K,
+    int n_tiles, int m_tiles) {
+  constexpr int KC = 4 * Mfma<TW>::KSTEP;
+  const int bid = blockIdx.x;
+  const int tile = bid % n_tiles;
+  const int mt = (bid / n_tiles) % m_tiles;
+  const int e = bid / (n_tiles * m_tiles);
+  const int cnt = e_count[e];
+  const int M = min(64, cnt - mt * 64);
+  if (M <= 0) return;
+  const int base = e_off[e] + mt * 64;
+  const float* a = row_of ? A : A + (size_t)base * K;
+  const int* ar = row_of ? row_of + base : nullptr;
+  skinny_tile<TW, 4, NT, NW, true>(a, ar, M, W + (size_t)e * N * K, K, out + (size_t)base * N, N,
+                                   tile * (16 * NT * NW), 0, K / KC);
+}
+
 
 // ---------------------------------------------------------------------------
 template <typename TW>
@@ -358,6 +396,22 @@ hipError_t dispatch(const GemmPlan& p, const float* A, const void* W, float* out
 }  // namespace
 
 int gemm_k_chunk(DType t) { return t == DType::F32 ? 64 : 128; }
+
+hipError_t launch_gemm_grouped(DType t, const float* A, const int* row_of, const int* e_count,
+                               const int* e_off, int E, int max_rows, const void* W, float* out,
+                               int N, int K, hipStream_t st) {
+  if (N % 128 != 0 || K % gemm_k_chunk(t) != 0) return hipErrorInvalidValue;
+  const int n_tiles = N / 128;                 // 4 waves x 32 columns
+  const int m_tiles = (max_rows + 63) / 64;
+  const dim3 grid(E * n_tiles * m_tiles);
+  if (t == DType::F32)
+    hipLaunchKernelGGL((gemm_grouped_kernel<float, 2, 4>), grid, dim3(256), 0, st, A, row_of,
+                       e_count, e_off, static_cast<const float*>(W), out, N, K, n_tiles, m_tiles);
+  else
+    hipLaunchKernelGGL((gemm_grouped_kernel<bf16, 2, 4>), grid, dim3(256), 0, st, A, row_of,
+                       e_count, e_off, static_cast<const bf16*>(W), out, N, K, n_tiles, m_tiles);
+  return hipGetLastError();
+}
 
 bool gemm_shape_ok(DType t, int N, int K) {
   return N > 0 && K > 0 && N % 128 == 0 && K % gemm_k_chunk(t) == 0;

@@ -24,6 +24,7 @@ struct PassTable {
   const int* req_len;      // [batch] L_r: keys each row attends over
   const int* req_bs;       // [batch] current block start position
   const int* req_active;   // [batch] request takes part in denoise/commit
+  const int* req_blk;      // [batch] index of the current block
 };
 
 // ---- GEMM: out[s][m][n] = sum over K-slice s of A[m][k] * W[n][k] ---------
@@ -41,6 +42,11 @@ hipError_t launch_gemm(const GemmPlan& p, DType t, const float* A, const void* W
                        const int* m_dev, int m_cap, int N, int K, hipStream_t st);
 bool gemm_shape_ok(DType t, int N, int K);
 int gemm_k_chunk(DType t);
+// MoE experts: out[off_e + i] = A[row_of ? row_of[off_e + i] : off_e + i] * W[e]^T for
+// i < e_count[e]; W holds E experts of [N][K]; max_rows bounds any e_count.
+hipError_t launch_gemm_grouped(DType t, const float* A, const int* row_of, const int* e_count,
+                               const int* e_off, int E, int max_rows, const void* W, float* out,
+                               int N, int K, hipStream_t st);
 
 // ---- row-wise kernels ------------------------------------------------------
 hipError_t launch_embed(DType t, PassTable tb, int m_cap, const int* tokens, int max_len,
@@ -85,6 +91,18 @@ hipError_t launch_vocab_stats(const VocabPlan& p, const float* logits, int rows,
                               const int* plant_id, const float* plant_bias, int mask_id,
                               void* scratch, int* argmax, float* conf, float* lse, int* topk_id,
                               float* topk_p, hipStream_t st);
+
+// ---- mixture of experts -------------------------------------------------------
+hipError_t launch_moe_route(DType t, PassTable tb, int m_cap, const float* f, int d,
+                            const void* Wr, int E, int top_k, const float* router_bias,
+                            int n_layers, int n_blocks, int layer, int* sel, float* gate,
+                            float* rlog, hipStream_t st);
+hipError_t launch_moe_plan(const int* nrows, int m_cap, const int* sel, int E, int top_k,
+                           int* e_count, int* e_off, int* row_of, int* pos, int* n_assign,
+                           hipStream_t st);
+hipError_t launch_moe_combine(const int* nrows, int m_cap, float* x, const float* P, int S,
+                              size_t p_stride, const float* Y, const int* pos, const float* gate,
+                              int top_k, int d, hipStream_t st);
 
 // ---- decode state ---------------------------------------------------------------
 struct CommitArgs {

@@ -48,6 +48,10 @@ struct Layout {
   DType dt;
   GemmPlan g_qkv_s, g_o_s, g_gu_s, g_d_s, g_lm;   // step pass
   GemmPlan g_qkv_r, g_o_r, g_gu_r, g_d_r;         // refresh pass
+  // MoE: shared-expert plans (step, refresh); experts use the grouped GEMM
+  bool moe;
+  int E, topk, Fe, Fs, assign_cap;
+  GemmPlan g_sgu_s, g_sd_s, g_sgu_r, g_sd_r;
   AttnPlan a_step, a_ref;
   VocabPlan vp;
   size_t part_elems, attn_o_elems, attn_ml_elems;
@@ -55,12 +59,14 @@ struct Layout {
   size_t off_rope, off_kvk, off_kvv, off_x, off_a, off_q, off_o, off_act, off_part, off_ao,
       off_aml, off_hf, off_logits, off_rpid, off_rpb, off_vscr, off_argmax, off_conf, off_lse,
       off_tid, off_tp, off_credit, off_tracked, off_sid, off_sp, off_sv, off_cm, off_done,
-      off_steps, off_ccount, off_tab_step, off_tab_ref, off_mask, off_misc, total;
+      off_steps, off_ccount, off_tab_step, off_tab_ref, off_mask, off_misc, off_sel, off_gate,
+      off_pos, off_rowof, off_ecount, off_eoff, off_nassign, off_egu, off_eact, off_ey, off_rlog,
+      total;
   size_t kv_layer_elems;        // elements of one layer's K (or V) cache
   int tab_ints_step, tab_ints_ref;
 };
 
-int table_ints(int m_cap, int mb) { return 16 + 2 * m_cap + 6 * mb; }
+int table_ints(int m_cap, int mb) { return 16 + 2 * m_cap + 7 * mb; }
 
 bool make_layout(const dinfer_model_cfg* m, const dinfer_decode_cfg* dc, int max_batch,
                  int max_len, Layout* L, std::string* why) {
@@ -75,8 +81,15 @@ bool make_layout(const dinfer_model_cfg* m, const dinfer_decode_cfg* dc, int max
   if (m->n_heads * m->head_dim != m->d_model) return bad("n_heads * head_dim must equal d_model");
   if (m->head_dim != 64 && m->head_dim != 128) return bad("head_dim must be 64 or 128");
   if (m->mask_id < 0 || m->mask_id >= m->vocab) return bad("mask_id out of range");
-  if (m->n_experts != 0) return bad("MoE layers are not supported by this build");
-  if (m->ffn_dim < 1) return bad("ffn_dim must be positive");
+  const bool moe = m->n_experts > 0;
+  if (moe) {
+    if (m->top_k < 1 || m->top_k > m->n_experts) return bad("top_k must be in 1..n_experts");
+    if (m->n_experts > 64) return bad("n_experts above 64 is not supported");
+    if (m->top_k > 8) return bad("top_k above 8 is not supported");
+    if (m->expert_ffn < 1 || m->shared_ffn < 1) return bad("expert_ffn and shared_ffn must be positive");
+  } else if (m->ffn_dim < 1) {
+    return bad("ffn_dim must be positive");
+  }
   if (m->d_model > 8192) return bad("d_model above 8192");
   if (m->vocab % 4 != 0) return bad("vocab must be a multiple of 4");
   if (dc->block_len < 1 || dc->block_len > 64) return bad("block_len must be in 1..64");
@@ -86,9 +99,14 @@ bool make_layout(const dinfer_model_cfg* m, const dinfer_decode_cfg* dc, int max
   if (max_batch < 1 || max_len < 1) return bad("max_batch and max_len must be positive");
   const DType dt = m->dtype == DINFER_F32 ? DType::F32 : DType::BF16;
   const int d = m->d_model, F = m->ffn_dim, V = m->vocab;
-  if (!gemm_shape_ok(dt, 3 * d, d) || !gemm_shape_ok(dt, d, d) || !gemm_shape_ok(dt, 2 * F, d) ||
-      !gemm_shape_ok(dt, d, F) || !gemm_shape_ok(dt, V, d))
-    return bad("GEMM shapes must have N % 128 == 0 and K % 128 (bf16) / 64 (f32) == 0");
+  const int Fe = m->expert_ffn, Fs = m->shared_ffn;
+  bool shapes = gemm_shape_ok(dt, 3 * d, d) && gemm_shape_ok(dt, d, d) && gemm_shape_ok(dt, V, d);
+  if (moe)
+    shapes = shapes && gemm_shape_ok(dt, 2 * Fe, d) && gemm_shape_ok(dt, d, Fe) &&
+             gemm_shape_ok(dt, 2 * Fs, d) && gemm_shape_ok(dt, d, Fs);
+  else
+    shapes = shapes && gemm_shape_ok(dt, 2 * F, d) && gemm_shape_ok(dt, d, F);
+  if (!shapes) return bad("GEMM shapes must have N % 128 == 0 and K % 128 (bf16) / 64 (f32) == 0");
 
   Layout& l = *L;
   l.dt = dt;
@@ -107,11 +125,17 @@ bool make_layout(const dinfer_model_cfg* m, const dinfer_decode_cfg* dc, int max
   l.m_ref = max_batch * max_len;
   l.m_all = (std::max(l.m_step, l.m_ref) + 15) / 16 * 16;   // 16-row padded buffers
   l.lm_rows = max_batch * l.B;
+  l.moe = moe;
+  l.E = m->n_experts;
+  l.topk = moe ? m->top_k : 0;
+  l.Fe = Fe;
+  l.Fs = Fs;
   const int tw = 256;   // about one skinny workgroup per CU
+  const int Fd = moe ? Fs : F;   // the dense FFN, or the shared expert
   l.g_qkv_s = plan_gemm(dt, l.m_step, 3 * d, d, tw);
   l.g_o_s = plan_gemm(dt, l.m_step, d, d, tw);
-  l.g_gu_s = plan_gemm(dt, l.m_step, 2 * F, d, tw);
-  l.g_d_s = plan_gemm(dt, l.m_step, d, F, tw);
+  l.g_gu_s = plan_gemm(dt, l.m_step, 2 * Fd, d, tw);
+  l.g_d_s = plan_gemm(dt, l.m_step, d, Fd, tw);
   l.g_lm = plan_gemm(dt, l.lm_rows, V, d, tw);
   if (l.g_lm.kind == 0 && l.g_lm.splits != 1)
     l.g_lm.splits = 1, l.g_lm.grid = V / (16 * l.g_lm.nt * l.g_lm.nw);
@@ -119,14 +143,14 @@ bool make_layout(const dinfer_model_cfg* m, const dinfer_decode_cfg* dc, int max
   for (GemmPlan* g : {&l.g_qkv_s, &l.g_o_s, &l.g_gu_s, &l.g_d_s, &l.g_lm}) g->guard = 0;
   l.g_qkv_r = plan_gemm(dt, l.m_ref, 3 * d, d, tw);
   l.g_o_r = plan_gemm(dt, l.m_ref, d, d, tw);
-  l.g_gu_r = plan_gemm(dt, l.m_ref, 2 * F, d, tw);
-  l.g_d_r = plan_gemm(dt, l.m_ref, d, F, tw);
+  l.g_gu_r = plan_gemm(dt, l.m_ref, 2 * Fd, d, tw);
+  l.g_d_r = plan_gemm(dt, l.m_ref, d, Fd, tw);
   for (GemmPlan* g : {&l.g_qkv_r, &l.g_o_r, &l.g_gu_r, &l.g_d_r}) g->guard = 0;
   auto pe = [](const GemmPlan& g, int m_cap, int N) { return (size_t)g.splits * m_cap * N; };
   l.part_elems = std::max({pe(l.g_qkv_s, l.m_step, 3 * d), pe(l.g_o_s, l.m_step, d),
-                           pe(l.g_gu_s, l.m_step, 2 * F), pe(l.g_d_s, l.m_step, d),
+                           pe(l.g_gu_s, l.m_step, 2 * Fd), pe(l.g_d_s, l.m_step, d),
                            pe(l.g_qkv_r, l.m_ref, 3 * d), pe(l.g_o_r, l.m_ref, d),
-                           pe(l.g_gu_r, l.m_ref, 2 * F), pe(l.g_d_r, l.m_ref, d)});
+                           pe(l.g_gu_r, l.m_ref, 2 * Fd), pe(l.g_d_r, l.m_ref, d)});
   // about one workgroup per CU: more key splits only add fp32 partial traffic
   l.a_step = plan_attention(max_batch, win, max_len, l.H, 256);
   l.a_ref = plan_attention(max_batch, max_len, max_len, l.H, 512);
@@ -152,7 +176,7 @@ bool make_layout(const dinfer_model_cfg* m, const dinfer_decode_cfg* dc, int max
   l.off_a = take((size_t)l.m_all * d * 4);
   l.off_q = take((size_t)l.m_all * d * 4);
   l.off_o = take((size_t)l.m_all * d * 4);
-  l.off_act = take((size_t)l.m_all * F * 4);
+  l.off_act = take((size_t)l.m_all * Fd * 4);
   l.off_part = take(l.part_elems * 4);
   l.off_ao = take(l.attn_o_elems * 4);
   l.off_aml = take(l.attn_ml_elems * 4);
@@ -179,6 +203,19 @@ bool make_layout(const dinfer_model_cfg* m, const dinfer_decode_cfg* dc, int max
   l.off_tab_ref = take((size_t)l.tab_ints_ref * 4);
   l.off_mask = take((size_t)max_batch * 4);
   l.off_misc = take(64);
+  l.assign_cap = l.m_all * l.topk;
+  const size_t ac = moe ? (size_t)l.assign_cap : 0;
+  l.off_sel = take(ac * 4);
+  l.off_gate = take(ac * 4);
+  l.off_pos = take(ac * 4);
+  l.off_rowof = take(ac * 4);
+  l.off_ecount = take((size_t)(moe ? l.E : 0) * 4);
+  l.off_eoff = take((size_t)(moe ? l.E : 0) * 4);
+  l.off_nassign = take(64);
+  l.off_egu = take(ac * 2 * Fe * 4);
+  l.off_eact = take(ac * Fe * 4);
+  l.off_ey = take(ac * d * 4);
+  l.off_rlog = take((size_t)(moe ? l.m_all * l.E : 0) * 4);
   l.total = o;
   return true;
 }
@@ -193,6 +230,7 @@ PassTable table_view(int* base, int m_cap, int mb) {
   t.req_len = t.req_nrows + mb;
   t.req_bs = t.req_len + mb;
   t.req_active = t.req_bs + mb;
+  t.req_blk = t.req_active + mb;
   return t;
 }
 
@@ -210,6 +248,7 @@ struct dinfer_ctx {
   const void* final_norm = nullptr;
   const void* lm_head = nullptr;
   std::vector<const void*> attn_norm, wqkv, wo, ffn_norm, wgu, wd;
+  std::vector<const void*> router, egu, ed, sgu, sd;   // MoE
   // workspace
   char* ws = nullptr;
   // batch
@@ -217,6 +256,8 @@ struct dinfer_ctx {
   int* tokens = nullptr;
   const int* plant_id = nullptr;
   const float* plant_bias = nullptr;
+  const float* router_bias = nullptr;
+  int n_bias_blocks = 0;                 // blocks per request in the router bias array
   std::vector<int> P, G, Lr, blk, nblk;
   std::vector<uint8_t> finished, refreshed;
   // host staging (pinned) for the row tables
@@ -249,6 +290,7 @@ dinfer_status upload_step_table(dinfer_ctx* c) {
   int* len = nr + mb;
   int* bs = len + mb;
   int* act = bs + mb;
+  int* blk = act + mb;
   int rows = 0;
   for (int r = 0; r < mb; ++r) {
     off[r] = rows;
@@ -256,7 +298,9 @@ dinfer_status upload_step_table(dinfer_ctx* c) {
     len[r] = 0;
     bs[r] = 0;
     act[r] = 0;
+    blk[r] = 0;
     if (r >= c->batch) continue;
+    blk[r] = c->blk[r];
     len[r] = c->Lr[r];
     bs[r] = c->P[r] + c->blk[r] * L.B;
     if (c->finished[r] || !c->refreshed[r]) continue;
@@ -295,7 +339,10 @@ dinfer_status run_pass(dinfer_ctx* c, bool step) {
   const GemmPlan& gg = step ? L.g_gu_s : L.g_gu_r;
   const GemmPlan& gd = step ? L.g_d_s : L.g_d_r;
   const AttnPlan& ap = step ? L.a_step : L.a_ref;
-  const int d = L.d, F = L.F;
+  const int d = L.d;
+  const int F = L.moe ? L.Fs : L.F;   // dense FFN, or the MoE layer's shared expert
+  // partial splits the next reader of x still has to add (0 after an MoE combine)
+  const int x_splits = L.moe ? 0 : gd.splits;
   float* x = c->at<float>(L.off_x);
   float* a = c->at<float>(L.off_a);
   float* q = c->at<float>(L.off_q);
@@ -310,7 +357,7 @@ dinfer_status run_pass(dinfer_ctx* c, bool step) {
                        c->at<float>(L.off_sp), c->at<uint8_t>(L.off_sv), L.B, x, st));
   for (int l = 0; l < L.nl; ++l) {
     const bool last = l == L.nl - 1;
-    HIP_TRY(launch_add_rmsnorm(dt, tb.nrows, m_cap, x, part, l == 0 ? 0 : gd.splits, stride_d,
+    HIP_TRY(launch_add_rmsnorm(dt, tb.nrows, m_cap, x, part, l == 0 ? 0 : x_splits, stride_d,
                                c->attn_norm[l], c->m.rms_eps, a, d, st));
     HIP_TRY(launch_gemm(gq, dt, a, c->wqkv[l], part, tb.nrows, m_cap, 3 * d, d, st));
     char* kvk = c->at<char>(L.off_kvk) + (size_t)l * L.kv_layer_elems * es;
@@ -323,13 +370,42 @@ dinfer_status run_pass(dinfer_ctx* c, bool step) {
     HIP_TRY(launch_gemm(go, dt, o, c->wo[l], part, tb.nrows, m_cap, d, d, st));
     HIP_TRY(launch_add_rmsnorm(dt, tb.nrows, m_cap, x, part, go.splits, stride_d, c->ffn_norm[l],
                                c->m.rms_eps, a, d, st));
-    HIP_TRY(launch_gemm(gg, dt, a, c->wgu[l], part, tb.nrows, m_cap, 2 * F, d, st));
+    if (!L.moe) {
+      HIP_TRY(launch_gemm(gg, dt, a, c->wgu[l], part, tb.nrows, m_cap, 2 * F, d, st));
+      HIP_TRY(launch_swiglu(tb.nrows, m_cap, part, gg.splits, stride_g, F, act, st));
+      HIP_TRY(launch_gemm(gd, dt, act, c->wd[l], part, tb.nrows, m_cap, d, F, st));
+      continue;
+    }
+    // MoE layer: route, plan the expert row lists, grouped expert projections,
+    // the shared expert, then combine into the residual.
+    const int E = L.E, K8 = L.topk, Fe = L.Fe;
+    int* sel = c->at<int>(L.off_sel);
+    float* gate = c->at<float>(L.off_gate);
+    int* pos = c->at<int>(L.off_pos);
+    int* row_of = c->at<int>(L.off_rowof);
+    int* e_count = c->at<int>(L.off_ecount);
+    int* e_off = c->at<int>(L.off_eoff);
+    int* n_assign = c->at<int>(L.off_nassign);
+    float* egu = c->at<float>(L.off_egu);
+    float* eact = c->at<float>(L.off_eact);
+    float* ey = c->at<float>(L.off_ey);
+    HIP_TRY(launch_moe_route(dt, tb, m_cap, a, d, c->router[l], E, K8, c->router_bias, L.nl,
+                             c->n_bias_blocks, l, sel, gate, c->at<float>(L.off_rlog), st));
+    HIP_TRY(launch_moe_plan(tb.nrows, m_cap, sel, E, K8, e_count, e_off, row_of, pos, n_assign, st));
+    HIP_TRY(launch_gemm_grouped(dt, a, row_of, e_count, e_off, E, m_cap, c->egu[l], egu, 2 * Fe, d,
+                                st));
+    HIP_TRY(launch_swiglu(n_assign, m_cap * K8, egu, 1, 0, Fe, eact, st));
+    HIP_TRY(launch_gemm_grouped(dt, eact, nullptr, e_count, e_off, E, m_cap, c->ed[l], ey, d, Fe,
+                                st));
+    HIP_TRY(launch_gemm(gg, dt, a, c->sgu[l], part, tb.nrows, m_cap, 2 * F, d, st));
     HIP_TRY(launch_swiglu(tb.nrows, m_cap, part, gg.splits, stride_g, F, act, st));
-    HIP_TRY(launch_gemm(gd, dt, act, c->wd[l], part, tb.nrows, m_cap, d, F, st));
+    HIP_TRY(launch_gemm(gd, dt, act, c->sd[l], part, tb.nrows, m_cap, d, F, st));
+    HIP_TRY(launch_moe_combine(tb.nrows, m_cap, x, part, gd.splits, stride_d, ey, pos, gate, K8, d,
+                               st));
   }
   if (!step) return DINFER_OK;
   float* hf = c->at<float>(L.off_hf);
-  HIP_TRY(launch_final_norm(dt, tb, L.max_batch, L.B, x, part, gd.splits, stride_d, c->final_norm,
+  HIP_TRY(launch_final_norm(dt, tb, L.max_batch, L.B, x, part, x_splits, stride_d, c->final_norm,
                             c->m.rms_eps, hf, d, c->plant_id, c->plant_bias, L.max_len,
                             c->at<int>(L.off_rpid), c->at<float>(L.off_rpb), st));
   float* logits = c->at<float>(L.off_logits);
@@ -428,12 +504,20 @@ dinfer_status dinfer_step_init(const dinfer_model_cfg* m, const dinfer_decode_cf
     return fail(unsup ? DINFER_E_UNSUPPORTED : DINFER_E_ARG, why);
   }
   if (!w || !w->tok_emb || !w->final_norm || !w->lm_head || !w->attn_norm || !w->wqkv || !w->wo ||
-      !w->ffn_norm || !w->w_gate_up || !w->w_down)
+      !w->ffn_norm)
     return fail(DINFER_E_ARG, "missing weight pointers");
-  for (int l = 0; l < m->n_layers; ++l)
-    if (!w->attn_norm[l] || !w->wqkv[l] || !w->wo[l] || !w->ffn_norm[l] || !w->w_gate_up[l] ||
-        !w->w_down[l])
-      return fail(DINFER_E_ARG, "missing per-layer weight pointer at layer " + std::to_string(l));
+  if (L.moe ? (!w->router || !w->exp_gate_up || !w->exp_down || !w->shared_gate_up || !w->shared_down)
+            : (!w->w_gate_up || !w->w_down))
+    return fail(DINFER_E_ARG, "missing FFN weight pointers");
+  for (int l = 0; l < m->n_layers; ++l) {
+    bool ok = w->attn_norm[l] && w->wqkv[l] && w->wo[l] && w->ffn_norm[l];
+    if (L.moe)
+      ok = ok && w->router[l] && w->exp_gate_up[l] && w->exp_down[l] && w->shared_gate_up[l] &&
+           w->shared_down[l];
+    else
+      ok = ok && w->w_gate_up[l] && w->w_down[l];
+    if (!ok) return fail(DINFER_E_ARG, "missing per-layer weight pointer at layer " + std::to_string(l));
+  }
   if (!d_workspace) return fail(DINFER_E_WORKSPACE, "workspace is null");
   if (reinterpret_cast<uintptr_t>(d_workspace) % kAlign != 0)
     return fail(DINFER_E_WORKSPACE, "workspace must be 256-byte aligned");
@@ -455,8 +539,16 @@ dinfer_status dinfer_step_init(const dinfer_model_cfg* m, const dinfer_decode_cf
   c->wqkv.assign(w->wqkv, w->wqkv + m->n_layers);
   c->wo.assign(w->wo, w->wo + m->n_layers);
   c->ffn_norm.assign(w->ffn_norm, w->ffn_norm + m->n_layers);
-  c->wgu.assign(w->w_gate_up, w->w_gate_up + m->n_layers);
-  c->wd.assign(w->w_down, w->w_down + m->n_layers);
+  if (L.moe) {
+    c->router.assign(w->router, w->router + m->n_layers);
+    c->egu.assign(w->exp_gate_up, w->exp_gate_up + m->n_layers);
+    c->ed.assign(w->exp_down, w->exp_down + m->n_layers);
+    c->sgu.assign(w->shared_gate_up, w->shared_gate_up + m->n_layers);
+    c->sd.assign(w->shared_down, w->shared_down + m->n_layers);
+  } else {
+    c->wgu.assign(w->w_gate_up, w->w_gate_up + m->n_layers);
+    c->wd.assign(w->w_down, w->w_down + m->n_layers);
+  }
 
   auto cleanup = [&](dinfer_status s) {
     dinfer_destroy(c);
@@ -504,7 +596,7 @@ dinfer_status dinfer_set_batch(dinfer_ctx* c, int32_t batch, int32_t* d_tokens,
   if (!c) return fail(DINFER_E_ARG, "ctx is null");
   if (batch < 1 || batch > c->L.max_batch) return fail(DINFER_E_ARG, "batch out of range");
   if (!d_tokens || !h_prompt_len || !h_gen_len) return fail(DINFER_E_ARG, "null batch pointer");
-  if (d_router_bias) return fail(DINFER_E_UNSUPPORTED, "router bias given for a dense model");
+  if (d_router_bias && !c->L.moe) return fail(DINFER_E_ARG, "router bias given for a dense model");
   const int B = c->L.B;
   for (int r = 0; r < batch; ++r) {
     if (h_prompt_len[r] < 0 || h_gen_len[r] < B || h_gen_len[r] % B != 0)
@@ -519,10 +611,19 @@ dinfer_status dinfer_set_batch(dinfer_ctx* c, int32_t batch, int32_t* d_tokens,
     c->graph = nullptr;
     c->graph_steps = 0;
   }
+  int nb = 0;
+  for (int r = 0; r < batch; ++r) nb = std::max(nb, h_gen_len[r] / B);
+  if (c->graph && (d_router_bias != c->router_bias || nb != c->n_bias_blocks)) {
+    (void)hipGraphExecDestroy(c->graph);
+    c->graph = nullptr;
+    c->graph_steps = 0;
+  }
   c->batch = batch;
   c->tokens = d_tokens;
   c->plant_id = d_plant_id;
   c->plant_bias = d_plant_bias;
+  c->router_bias = d_router_bias;
+  c->n_bias_blocks = nb;
   c->P.assign(h_prompt_len, h_prompt_len + batch);
   c->G.assign(h_gen_len, h_gen_len + batch);
   c->Lr.resize(batch);
@@ -558,16 +659,18 @@ dinfer_status dinfer_refresh_kv(dinfer_ctx* c, const uint8_t* h_req_mask) {
   int* len = nr + mb;
   int* bs = len + mb;
   int* act = bs + mb;
+  int* blk = act + mb;
   int* mask = c->h_misc;
   int rows = 0, nsel = 0;
   for (int r = 0; r < mb; ++r) {
     off[r] = rows;
-    nr[r] = len[r] = bs[r] = act[r] = 0;
+    nr[r] = len[r] = bs[r] = act[r] = blk[r] = 0;
     mask[r] = 0;
     if (r >= c->batch || c->finished[r]) continue;
     if (h_req_mask && !h_req_mask[r]) continue;
     mask[r] = 1;
     ++nsel;
+    blk[r] = c->blk[r];
     len[r] = c->Lr[r];
     bs[r] = c->P[r] + c->blk[r] * L.B;
     act[r] = 1;
@@ -780,6 +883,12 @@ dinfer_status dinfer_get_step_view(const dinfer_ctx* c, dinfer_step_view* v) {
   v->commit_count = c->at<int>(L.off_ccount);
   v->kv_k = c->at<char>(L.off_kvk);
   v->kv_v = c->at<char>(L.off_kvv);
+  v->moe_top_k = L.moe ? L.topk : 0;
+  v->moe_sel = L.moe ? c->at<int>(L.off_sel) : nullptr;
+  v->moe_gate = L.moe ? c->at<float>(L.off_gate) : nullptr;
+  v->moe_experts = L.moe ? L.E : 0;
+  v->moe_logits = L.moe ? c->at<float>(L.off_rlog) : nullptr;
+  v->ffn_in = c->at<float>(L.off_a);
   return DINFER_OK;
 }
 

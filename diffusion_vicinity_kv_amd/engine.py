@@ -63,8 +63,12 @@ class Engine:
                     for i in range(nl)]
             return arr(*vals)
 
-        self._arrays = {k: per_layer(k) for k in ("attn_norm", "wqkv", "wo", "ffn_norm",
-                                                  "w_gate_up", "w_down")}
+        keys = ["attn_norm", "wqkv", "wo", "ffn_norm"]
+        if int(model_cfg.n_experts) > 0:
+            keys += ["router", "exp_gate_up", "exp_down", "shared_gate_up", "shared_down"]
+        else:
+            keys += ["w_gate_up", "w_down"]
+        self._arrays = {k: per_layer(k) for k in keys}
         w = B.Weights()
         w.tok_emb = B.ptr(weights["tok_emb"])
         w.final_norm = B.ptr(weights["final_norm"])
@@ -92,8 +96,15 @@ class Engine:
     # -- calls ---------------------------------------------------------------
     def set_batch(self, tokens, prompt_len, gen_len, plant_id=None, plant_bias=None,
                   router_bias=None):
-        """tokens: device int32 [batch][max_len] (updated in place)."""
+        """tokens: device int32 [batch][max_len] (updated in place).
+
+        router_bias (MoE): device float32 [batch][n_layers][n_blocks][E].
+        """
         assert tokens.dtype == torch.int32 and tokens.is_cuda and tokens.is_contiguous()
+        if router_bias is not None:
+            assert router_bias.dtype == torch.float32 and router_bias.is_cuda
+            assert router_bias.is_contiguous() and router_bias.dim() == 4
+            assert router_bias.shape[0] == tokens.shape[0]
         assert tokens.shape[1] == self.max_len
         batch = tokens.shape[0]
         P = (C.c_int32 * batch)(*[int(x) for x in prompt_len])
@@ -150,7 +161,17 @@ class Engine:
         kvdt = torch.float32 if es == 4 else torch.bfloat16
         kv_n = self.m.n_layers * self.max_batch * self.m.n_heads * self.max_len * self.m.head_dim
         kv_shape = (self.m.n_layers, self.max_batch, self.m.n_heads, self.max_len, self.m.head_dim)
-        return {
+        out = {}
+        if v.moe_top_k > 0:
+            # the last pass's rows; the widest pass is a refresh of max_batch * max_len rows
+            n = self.max_batch * self.max_len
+            out["moe_sel"] = t(v.moe_sel, n * v.moe_top_k, torch.int32, (n, v.moe_top_k))
+            out["moe_gate"] = t(v.moe_gate, n * v.moe_top_k, torch.float32, (n, v.moe_top_k))
+            out["moe_logits"] = t(v.moe_logits, n * v.moe_experts, torch.float32,
+                                  (n, v.moe_experts))
+        n = self.max_batch * self.max_len
+        out["ffn_in"] = t(v.ffn_in, n * self.m.d_model, torch.float32, (n, self.m.d_model))
+        return out | {
             "logits": t(v.logits, R * v.vocab, torch.float32, (R, v.vocab)),
             "argmax": t(v.argmax, R, torch.int32, (R,)),
             "conf": t(v.conf, R, torch.float32, (R,)),

@@ -138,6 +138,20 @@ typedef struct {
   int32_t* commit_count;     /* [batch] tokens committed in total                */
   void* kv_k;                /* [n_layers][max_batch][H][max_len][hd] K, RoPE'd */
   void* kv_v;                /* [n_layers][max_batch][H][max_len][hd]            */
+  /* MoE only (else 0 / NULL): routing of the last layer whose FFN the last
+   * pass ran (a step runs every layer; a refresh stops before the last
+   * layer's FFN), one row per pass row in pass order (request by request,
+   * positions ascending: a step's window, or every position of each refreshed
+   * request).  Row m holds its top_k experts (router logit descending, lower
+   * id first on ties) and their gates renormalised over the selection. */
+  int32_t moe_top_k;
+  int32_t* moe_sel;          /* [rows][moe_top_k]                                */
+  float* moe_gate;           /* [rows][moe_top_k]                                */
+  int32_t moe_experts;       /* E                                                */
+  float* moe_logits;         /* [rows][E] router logits incl. the block's bias   */
+  /* After a step: [rows][d] fp32 normalised FFN input of the last layer, rows
+   * in pass order (after a refresh it holds other intermediate values). */
+  float* ffn_in;
 } dinfer_step_view;
 
 /* Bytes of workspace dinfer_step_init needs for these shapes (0 on bad args). */
@@ -159,8 +173,11 @@ dinfer_status dinfer_step_init(const dinfer_model_cfg* model, const dinfer_decod
  * and prompt_len + gen_len <= max_len.  d_plant_id [batch][max_len] int32
  * (-1 = no planting) and d_plant_bias [batch] float: the planted target of a
  * position gets +bias on its raw logit before the vocab statistics.
- * d_router_bias (MoE only, else NULL): [batch][n_layers][gen_len/B][E] float
- * added to the router logits of every row during that block.
+ * d_router_bias (MoE only, else NULL; a dense model rejects it with
+ * DINFER_E_ARG): [batch][n_layers][nb][E] float with nb = max over the batch
+ * of gen_len/B; entry [r][l][k] is added to the router logits of layer l for
+ * every row of request r while r works on block k (refresh and steps).  The
+ * array stays owned by the caller and must live until the next set_batch.
  * Every request starts at block 0; call dinfer_refresh_kv next. */
 dinfer_status dinfer_set_batch(dinfer_ctx* ctx, int32_t batch, int32_t* d_tokens,
                                const int32_t* h_prompt_len, const int32_t* h_gen_len,

@@ -92,6 +92,23 @@ def moe_ffn(f, router, bias, exp_gate_up, exp_down, shared_gate_up, shared_down,
     return out, order, gsel
 
 
+def router_logits(f, router, bias):
+    """Router logits f W_r^T + bias of every row (reported alongside routing)."""
+    r = f @ router.T
+    return r if bias is None else r + bias[None, :]
+
+
+def route_margin(f, router, bias, top_k):
+    """Per row, the router-logit gap between the top_k-th and the next expert:
+    how far the row's expert choice is from flipping.  Reported, not used by
+    the method; inf when every expert is selected."""
+    r = router_logits(f, router, bias)
+    if top_k >= r.shape[1]:
+        return np.full(r.shape[0], np.inf)
+    s = -np.sort(-r, axis=-1)
+    return s[:, top_k - 1] - s[:, top_k]
+
+
 class OracleModel:
     """fp64 copy of the weights plus one request's KV cache.
 
@@ -158,6 +175,10 @@ class OracleModel:
                                          W["shared_gate_up"], W["shared_down"], m.top_k)
                 if record is not None:
                     record.setdefault("experts", {})[li] = order
+                    record.setdefault("gates", {})[li] = gsel
+                    record.setdefault("route_margin", {})[li] = route_margin(
+                        f, W["router"], rb, m.top_k)
+                    record.setdefault("router_logits", {})[li] = router_logits(f, W["router"], rb)
                 h = h + y
             else:
                 h = h + swiglu(f, W["w_gate_up"], W["w_down"])

@@ -50,6 +50,10 @@ class OracleRun:
         self.steps = []            # steps per finished block
         self.records = []          # per-step details
         self._k = dcfg.smooth_topk
+        self.refresh_route_margin = np.inf        # MoE routing near-ties (reported)
+        self.step_route_margin_rows = None
+        self.step_route_margin_window = np.inf
+        self.refresh_record = self.step_record = None   # MoE: experts, route_margin per layer
 
     # --- block bookkeeping ------------------------------------------------
     @property
@@ -77,7 +81,11 @@ class OracleRun:
         self.block = k
         pos = np.arange(self.L)
         e = self.model.embed(self.tokens[pos])
-        self.model.forward_rows(self.cache, pos, e, self.L, self._router_bias_block())
+        rec = {} if self.m.is_moe else None
+        self.model.forward_rows(self.cache, pos, e, self.L, self._router_bias_block(), rec)
+        # routing near-ties of layers whose output feeds a later layer's cache
+        self.refresh_route_margin = _min_route_margin(rec, self.model.layer_ids[:-1])
+        self.refresh_record = rec
         B, kk = self.B, self._k
         self.credit = np.zeros(B, dtype=F32)
         self.tracked = np.full(B, -1, dtype=np.int64)
@@ -106,7 +114,15 @@ class OracleRun:
         lo, hi = self.window()
         pos = np.arange(lo, hi)
         e = self.window_embeddings(lo, hi)
-        h = self.model.forward_rows(self.cache, pos, e, self.L, self._router_bias_block())
+        rec = {} if self.m.is_moe else None
+        h = self.model.forward_rows(self.cache, pos, e, self.L, self._router_bias_block(), rec)
+        if rec is not None:
+            # per block row: its own routing in every layer; any window row's
+            # routing below the last layer also reaches every row through the cache
+            own = np.min(np.stack([rec["route_margin"][li] for li in self.model.layer_ids]), axis=0)
+            self.step_route_margin_rows = own[self.bs - lo: self.be - lo]
+            self.step_route_margin_window = _min_route_margin(rec, self.model.layer_ids[:-1])
+            self.step_record = rec
         hb = h[self.bs - lo: self.be - lo]
         return self.model.logits(hb)
 
@@ -151,6 +167,12 @@ class OracleRun:
                 self.step()
             self.steps.append(self.block_steps)
         return self.tokens
+
+
+def _min_route_margin(rec, layer_ids):
+    if not rec or not layer_ids:
+        return np.inf
+    return float(min(np.min(rec["route_margin"][li]) for li in layer_ids))
 
 
 def decision_margin(st, masked, credit, d, committed, still=None):

@@ -18,13 +18,16 @@ def note(msg):
 
 def small_workload(name="small", *, n_layers=2, d=256, H=4, hd=64, F=768, V=4096, dtype="f32",
                    batch=1, prompt=(64, 64), gen=64, B=32, w=8, tau=0.9, credit=1.0,
-                   alpha=0.3, hier=False, bias=6.0, prob=(0.7, 0.7), seed=0):
+                   alpha=0.3, hier=False, bias=6.0, prob=(0.7, 0.7), seed=0,
+                   experts=0, top_k=0, Fe=0, Fs=0, pref_bias=0.0, pref_count=0):
     m = synth.ModelCfg(n_layers=n_layers, d_model=d, n_heads=H, head_dim=hd, ffn_dim=F, vocab=V,
-                       mask_id=V - 1, dtype=dtype)
+                       mask_id=V - 1, dtype=dtype, n_experts=experts, top_k=top_k,
+                       expert_ffn=Fe, shared_ffn=Fs)
     dc = synth.DecodeCfg(block_len=B, vicinity_w=w, tau=tau, credit_weight=credit,
                          smooth_alpha=alpha, hierarchical=hier)
     return synth.WorkloadCfg(name=name, model=m, decode=dc, batch=batch, prompt_len=prompt,
-                             gen_len=gen, plant_bias=bias, plant_prob=prob, seed=seed)
+                             gen_len=gen, plant_bias=bias, plant_prob=prob, seed=seed,
+                             router_pref_bias=pref_bias, router_pref_count=pref_count or top_k)
 
 
 def build(wc, graph_unroll=0, weights=None, req=None):
@@ -33,8 +36,10 @@ def build(wc, graph_unroll=0, weights=None, req=None):
     max_len = req["tokens"].shape[1]
     eng = Engine(wc.model, wc.decode, w, wc.batch, max_len, graph_unroll=graph_unroll)
     tokens = req["tokens"].cuda().contiguous()
+    rb = req.get("router_bias")
     eng.set_batch(tokens, req["prompt_len"].tolist(), req["gen_len"].tolist(),
-                  req["plant_id"].cuda().contiguous(), req["plant_bias"].cuda().contiguous())
+                  req["plant_id"].cuda().contiguous(), req["plant_bias"].cuda().contiguous(),
+                  None if rb is None else rb.cuda().contiguous())
     return eng, w, req, tokens
 
 
@@ -42,14 +47,16 @@ def oracle_runs(wc, w, req, layers=None):
     om = OracleModel(wc.model, w, layers=layers)
     runs = []
     for r in range(wc.batch):
+        rb = req.get("router_bias")
         runs.append(oracle.OracleRun(om, wc.decode, req["tokens"][r].numpy(),
                                      int(req["prompt_len"][r]), int(req["gen_len"][r]),
-                                     req["plant_id"][r].numpy(), float(req["plant_bias"][r])))
+                                     req["plant_id"][r].numpy(), float(req["plant_bias"][r]),
+                                     None if rb is None else rb[r].numpy()))
     return runs
 
 
 def lockstep(wc, eng, tokens, runs, logit_tol, max_steps=10_000, max_blocks=None,
-             check_cache=False):
+             check_cache=False, route_band=0.0):
     """Drive GPU and oracle step by step.  Per step: block-row logits within
     logit_tol * RMS(oracle logits); commits, tokens and smoothing ids identical.
     Every decision of a step (committed ids, threshold/credit gates, fallback
@@ -60,7 +67,15 @@ def lockstep(wc, eng, tokens, runs, logit_tol, max_steps=10_000, max_blocks=None
     is below that band and the two sides decided differently, the trajectories
     part legitimately and the lockstep stops there (reported as "diverged");
     near-ties decided alike are counted and the lockstep goes on.  Decisions
-    that differ with a margin above the band fail the test."""
+    that differ with a margin above the band fail the test.
+
+    MoE routing is such a decision too, taken inside the forward pass: the
+    oracle reports each row's gap between its top_k-th and next router logit.
+    route_band bounds the router-logit error of the HIP path.  A block row
+    whose logits miss logit_tol is accepted only when its own routing, or any
+    routing that reaches it through the cache (a window row below the last
+    layer, or the block's refresh), was within route_band of flipping: the
+    lockstep then stops there as "diverged"."""
     B = wc.decode.block_len
     batch = wc.batch
     rep = {"steps": 0, "max_rel_logit_err": 0.0, "diverged": None, "min_margin": np.inf,
@@ -88,9 +103,23 @@ def lockstep(wc, eng, tokens, runs, logit_tol, max_steps=10_000, max_blocks=None
                 continue
             ol = run.denoise_logits()
             rms = float(np.sqrt(np.mean(ol ** 2)))
-            err_abs = float(np.max(np.abs(glog[r] - ol)))
-            err_step[r] = err_abs
-            err = err_abs / rms
+            row_err = np.max(np.abs(glog[r] - ol), axis=1) / rms
+            if wc.model.is_moe:
+                shared = min(run.refresh_route_margin, run.step_route_margin_window)
+                near = (run.step_route_margin_rows < route_band) | (shared < route_band)
+                rep["route_near_ties"] = rep.get("route_near_ties", 0) + int(near.sum())
+                bad = row_err > logit_tol
+                if bad.any():
+                    assert near[bad].all(), (
+                        f"request {r} step {steps}: logits rel err {row_err.max():.3e} > "
+                        f"{logit_tol} on rows {np.nonzero(bad & ~near)[0].tolist()} whose "
+                        f"routing margins are >= {route_band}")
+                    rep["diverged"] = {"request": r, "step": steps, "route_rows":
+                                       np.nonzero(bad)[0].tolist(), "row_err": float(row_err.max())}
+                    rep["steps"] = steps
+                    return rep
+            err = float(row_err.max())
+            err_step[r] = err * rms
             rep["max_rel_logit_err"] = max(rep["max_rel_logit_err"], err)
             assert err <= logit_tol, f"request {r} step {steps}: logits rel err {err:.3e} > {logit_tol}"
             ostats[r] = run.stats(ol)

@@ -49,17 +49,19 @@ def _structs(name="tiny_f32", **mkw):
 
 
 @pytest.mark.parametrize("name", synth.PRESET_ORDER)
-def test_workspace_bytes_positive_for_dense_presets(name):
+def test_workspace_bytes_positive_for_presets(name):
     mc, dc, wc = _structs(name)
     n = B.load().dinfer_workspace_bytes(C.byref(mc), C.byref(dc), wc.batch, wc.max_len)
-    if wc.model.is_moe:
-        assert n == 0          # MoE is rejected by this build
-    else:
-        assert n > 0 and n % 256 == 0
-        # the KV cache alone: 2 * layers * batch * heads * max_len * hd * element size
-        m = wc.model
-        es = 4 if m.dtype == "f32" else 2
-        assert n >= 2 * m.n_layers * wc.batch * m.n_heads * wc.max_len * m.head_dim * es
+    assert n > 0 and n % 256 == 0
+    # the KV cache alone: 2 * layers * batch * heads * max_len * hd * element size
+    m = wc.model
+    es = 4 if m.dtype == "f32" else 2
+    kv = 2 * m.n_layers * wc.batch * m.n_heads * wc.max_len * m.head_dim * es
+    assert n >= kv
+    if m.is_moe:
+        # plus the packed expert activations: rows * top_k * (2 Fe + Fe + d) floats
+        rows = wc.batch * wc.max_len
+        assert n >= kv + rows * m.top_k * (3 * m.expert_ffn + m.d_model) * 4
 
 
 def test_workspace_bytes_rejects_bad_shapes():
@@ -71,6 +73,11 @@ def test_workspace_bytes_rejects_bad_shapes():
     mc, dc, wc = _structs()
     dc.block_len = 65
     assert lib.dinfer_workspace_bytes(C.byref(mc), C.byref(dc), 1, 128) == 0
+    moe = dict(n_experts=64, top_k=8, expert_ffn=1024, shared_ffn=2048)
+    for kw in [dict(moe, n_experts=65), dict(moe, top_k=9), dict(moe, top_k=0),
+               dict(moe, expert_ffn=1000)]:
+        mc, dc, wc = _structs(**kw)
+        assert lib.dinfer_workspace_bytes(C.byref(mc), C.byref(dc), 1, 128) == 0, kw
 
 
 def test_step_init_argument_errors_without_gpu():
@@ -81,10 +88,21 @@ def test_step_init_argument_errors_without_gpu():
     # null out pointer
     assert lib.dinfer_step_init(C.byref(mc), C.byref(dc), C.byref(w), 1, 128, None, 0, None,
                                 None) == B.E_ARG
-    # MoE model: unsupported in this build
-    mc2, dc2, _ = _structs(n_experts=64, top_k=8, expert_ffn=1024, shared_ffn=2048)
+    # more experts or a wider top-k than the router kernel handles
+    mc2, dc2, _ = _structs(n_experts=128, top_k=8, expert_ffn=1024, shared_ffn=2048)
     assert lib.dinfer_step_init(C.byref(mc2), C.byref(dc2), C.byref(w), 1, 128, None, 0, None,
                                 C.byref(ctx)) == B.E_UNSUPPORTED
+    # MoE model with dense FFN weights only
+    mc3, dc3, _ = _structs(n_experts=64, top_k=8, expert_ffn=1024, shared_ffn=2048)
+    nl = mc3.n_layers
+    arr = (C.c_void_p * nl)(*([16] * nl))
+    w3 = B.Weights()
+    w3.tok_emb = w3.final_norm = w3.lm_head = 16
+    for k in ("attn_norm", "wqkv", "wo", "ffn_norm", "w_gate_up", "w_down"):
+        setattr(w3, k, C.cast(arr, B._PP))
+    assert lib.dinfer_step_init(C.byref(mc3), C.byref(dc3), C.byref(w3), 1, 128, None, 0, None,
+                                C.byref(ctx)) == B.E_ARG
+    assert b"FFN weight" in lib.dinfer_last_error()
     # missing weights
     assert lib.dinfer_step_init(C.byref(mc), C.byref(dc), C.byref(w), 1, 128, None, 0, None,
                                 C.byref(ctx)) == B.E_ARG

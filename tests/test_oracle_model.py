@@ -104,6 +104,28 @@ def test_moe_matches_row_by_row_bruteforce_with_ties():
     assert np.allclose(got, _moe_bruteforce(f, router, bias, egu, ed, sgu, sd, k), atol=1e-12)
 
 
+def test_route_margin_is_gap_between_kept_and_first_dropped_expert():
+    from oracle.model import route_margin
+    E, d, k = 6, 8, 3
+    f = RNG.standard_normal((7, d))
+    router = RNG.standard_normal((E, d))
+    bias = RNG.standard_normal(E)
+    got = route_margin(f, router, bias, k)
+    for r in range(f.shape[0]):
+        logits = sorted((float(f[r] @ router[e] + bias[e]) for e in range(E)), reverse=True)
+        assert abs(got[r] - (logits[k - 1] - logits[k])) < 1e-12
+    # a tie at the boundary has margin 0; keeping every expert has no boundary
+    router[4] = router[1]
+    bias[:] = 0.0
+    g2 = route_margin(f, router, bias, k)
+    _, order, _ = moe_ffn(f, router, bias, RNG.standard_normal((E, 4, d)),
+                          RNG.standard_normal((E, d, 2)), None, None, k)
+    for r in range(f.shape[0]):
+        if (1 in order[r]) != (4 in order[r]):
+            assert g2[r] == 0.0
+    assert np.all(np.isinf(route_margin(f, router, None, E)))
+
+
 def test_moe_single_expert_is_dense_ffn():
     d, F = 8, 6
     f = RNG.standard_normal((4, d))
