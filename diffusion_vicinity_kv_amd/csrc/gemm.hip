@@ -138,39 +138,63 @@ __device__ __forceinline__ void skinny_tile(const float* __restrict__ A,
       AS::store4(&As[buf][0][r * STR + cv * 4], &As[buf][PL - 1][r * STR + cv * 4], areg[i]);
     }
   };
+  // Activation fragments of one vector step for every row tile and plane,
+  // read from LDS one vector step ahead of the MFMAs that use them.
+  auto read_frags = [&](V16 (&f)[MT][PL], int buf, int j) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int p = 0; p < PL; ++p)
+        f[mt][p] = *reinterpret_cast<const V16*>(
+            &As[buf][p][(mt * 16 + lc) * STR + j * KSTEP + lg * VEC]);
+  };
   // bc/ac: chunk c (weights; activations already staged), an: activations of
-  // c+1 (to stage), bl/al: targets of the chunk c+2 loads.
+  // c+1 (to stage), bl/al: targets of the chunk c+2 loads.  Every step issues
+  // its loads, clamped to the last chunk near the end (a repeated read of
+  // data just fetched): loads under a condition make the compiler's wait
+  // counts at the join points assume the short path and drain the prefetch.
   auto step = [&](int c, V16 (&bc)[U][NT], float4 (&an)[AV], V16 (&bl)[U][NT],
                   float4 (&al)[AV]) {
     const int buf = (c - c_begin) & 1;
-    if (c + 2 < c_end) {
-      load_a(al, c + 2);
-      load_w(bl, c + 2);
-    }
+    const int cl = min(c + 2, c_end - 1);
+    load_a(al, cl);
+    load_w(bl, cl);
+    if constexpr (MT * PL <= 12) {
+      V16 af[2][MT][PL];
+      read_frags(af[0], buf, 0);
 #pragma unroll
-    for (int j = 0; j < U; ++j) {
+      for (int j = 0; j < U; ++j) {
+        if (j + 1 < U) read_frags(af[(j + 1) & 1], buf, j + 1);
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
+        for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int p = 0; p < PL; ++p) {
-          const V16 a = *reinterpret_cast<const V16*>(
-              &As[buf][p][(mt * 16 + lc) * STR + j * KSTEP + lg * VEC]);
+          for (int p = 0; p < PL; ++p)
 #pragma unroll
-          for (int nt = 0; nt < NT; ++nt) MF::mac(acc[mt][nt], a, bc[j][nt]);
-        }
+            for (int nt = 0; nt < NT; ++nt) MF::mac(acc[mt][nt], af[j & 1][mt][p], bc[j][nt]);
       }
+    } else {   // many row tiles: no registers to spare for a fragment buffer
+#pragma unroll
+      for (int j = 0; j < U; ++j)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int p = 0; p < PL; ++p) {
+            const V16 a = *reinterpret_cast<const V16*>(
+                &As[buf][p][(mt * 16 + lc) * STR + j * KSTEP + lg * VEC]);
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) MF::mac(acc[mt][nt], a, bc[j][nt]);
+          }
     }
-    if (c + 1 < c_end) store_a(an, buf ^ 1);
+    store_a(an, buf ^ 1);   // past the end: staged into a buffer nobody reads
     __syncthreads();
   };
 
   if (c_begin < c_end) {
     load_a(a0, c_begin);
     load_w(b0, c_begin);
-    if (c_begin + 1 < c_end) {
-      load_a(a1, c_begin + 1);
-      load_w(b1, c_begin + 1);
-    }
+    const int c1 = min(c_begin + 1, c_end - 1);
+    load_a(a1, c1);
+    load_w(b1, c1);
     store_a(a0, 0);
   }
   __syncthreads();
@@ -368,11 +392,18 @@ hipError_t dispatch_mt(const GemmPlan& p, const float* A, const void* W, float* 
     case 2: return run_skinny<TW, 2, NT, NW>(p, A, W, out, m_dev, m_cap, N, K, st);
     case 3: return run_skinny<TW, 3, NT, NW>(p, A, W, out, m_dev, m_cap, N, K, st);
     case 4: return run_skinny<TW, 4, NT, NW>(p, A, W, out, m_dev, m_cap, N, K, st);
-    case 5: return run_skinny<TW, 5, NT, NW>(p, A, W, out, m_dev, m_cap, N, K, st);
-    case 6: return run_skinny<TW, 6, NT, NW>(p, A, W, out, m_dev, m_cap, N, K, st);
-    case 7: return run_skinny<TW, 7, NT, NW>(p, A, W, out, m_dev, m_cap, N, K, st);
-    case 8: return run_skinny<TW, 8, NT, NW>(p, A, W, out, m_dev, m_cap, N, K, st);
-    default: return hipErrorInvalidValue;
+    default: break;
+  }
+  if constexpr (NW == 8) {
+    return hipErrorInvalidValue;   // 8-wave groups: at most 64 rows
+  } else {
+    switch (p.mt) {
+      case 5: return run_skinny<TW, 5, NT, NW>(p, A, W, out, m_dev, m_cap, N, K, st);
+      case 6: return run_skinny<TW, 6, NT, NW>(p, A, W, out, m_dev, m_cap, N, K, st);
+      case 7: return run_skinny<TW, 7, NT, NW>(p, A, W, out, m_dev, m_cap, N, K, st);
+      case 8: return run_skinny<TW, 8, NT, NW>(p, A, W, out, m_dev, m_cap, N, K, st);
+      default: return hipErrorInvalidValue;
+    }
   }
 }
 
@@ -386,7 +417,6 @@ hipError_t dispatch(const GemmPlan& p, const float* A, const void* W, float* out
     return hipGetLastError();
   }
   if constexpr (sizeof(TW) == 2) {   // 8-wave groups: bf16 weights only
-    if (p.nw == 8 && p.nt == 3) return dispatch_mt<TW, 3, 8>(p, A, W, out, m_dev, m_cap, N, K, st);
     if (p.nw == 8) return dispatch_mt<TW, 2, 8>(p, A, W, out, m_dev, m_cap, N, K, st);
   }
   return p.nt == 2 ? dispatch_mt<TW, 2, 4>(p, A, W, out, m_dev, m_cap, N, K, st)
@@ -445,7 +475,9 @@ GemmPlan plan_gemm(DType t, int m_cap, int N, int K, int target_wgs) {
     p.nw = 4;
   }
   const int n_tiles = N / (16 * p.nt * p.nw);
-  int s = (target_wgs + n_tiles / 2) / n_tiles;
+  // as many K splits as still fit one round of target_wgs workgroups: a
+  // partial round costs a whole round, and each split adds an fp32 partial
+  int s = target_wgs / n_tiles;
   if (s < 1) s = 1;
   if (s > chunks) s = chunks;
   p.splits = s;
