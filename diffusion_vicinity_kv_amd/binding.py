@@ -60,7 +60,8 @@ class StepView(C.Structure):
                                   "commit_mask", "block_done", "step_count", "commit_count",
                                   "kv_k", "kv_v")] + [
         ("moe_top_k", C.c_int32), ("moe_sel", C.c_void_p), ("moe_gate", C.c_void_p),
-        ("moe_experts", C.c_int32), ("moe_logits", C.c_void_p), ("ffn_in", C.c_void_p)]
+        ("moe_experts", C.c_int32), ("moe_logits", C.c_void_p), ("ffn_in", C.c_void_p),
+        ("kv_len", C.c_int32)]
 
 
 class DinferError(RuntimeError):

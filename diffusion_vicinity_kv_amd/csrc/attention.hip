@@ -2,20 +2,34 @@
 // their request (no causal mask: every position attends to every position;
 // dInfer news article, section "扩散模型的“理论翅膀”与“现实枷锁”").
 //
-// Split-KV flash attention on gfx950 MFMA.  A workgroup takes one (request,
-// head, 64-query tile, key range); each of its four waves owns 16 queries.
-// Per 64-key chunk, K is staged in LDS as [key][hd] and V transposed as
-// [hd][key].  Scores are computed transposed, S^T = K Q^T, so that a lane
-// holds the scores of query (lane % 16) for keys 4*(lane/16)+i: exactly the
-// B-operand layout of the next product O^T = V^T P^T, which therefore needs no
-// data movement; the online-softmax statistics of a query also live in the
-// lanes that hold its output column.  Softmax runs in fp32 in the log2
-// domain.  Each split writes (m, l, unnormalised O) in fp32; a merge kernel
-// combines the splits of a query in split order.
+// Cache layouts (per layer): K [request][head][Lp][hd] -- one key's head
+// vector contiguous -- and V in transposed tiles of 32 keys,
+// [request][head][Lp/32][hd][32] -- within a tile one head dimension's values
+// over consecutive keys are contiguous, and a whole tile (8 KB in bf16) is
+// contiguous; Lp = max_len rounded up to 64.  Every MFMA operand of both
+// products is then a 16-byte piece of memory in its fragment layout.
 //
-// Queries stay fp32 and the probabilities are fp32: with a bf16 cache both
-// enter the bf16 MFMAs as hi + lo halves, so the only rounding left in the
-// attention is the cache's own storage of K and V.
+// A workgroup takes (request, head, block of 64 * QTW queries, key range);
+// each of its four waves owns QTW tiles of 16 queries.  Per step of KS keys
+// (32 for bf16, 16 for fp32) the step's K and V fragments (NF kilobytes) are
+// loaded once for the workgroup -- a quarter by each wave, two steps ahead,
+// through registers -- and stored to LDS in fragment order, so that every
+// wave reads each fragment as one contiguous, conflict-free 16-byte-per-lane
+// load.  Then:
+//   S^T = K Q^T with the keys as MFMA rows.  For bf16 the two 16-key tiles
+//   take their rows in the order key(t, j) = 8*(j/4) + 4t + j%4, so lane
+//   (query c, group g) ends up holding the scores of keys 8g..8g+7;
+//   O^T += V^T P^T then takes those eight probabilities as its B operand
+//   directly, against eight consecutive keys of a V^T tile row.
+// Softmax is fp32 in the log2 domain.  Each lane keeps its own partial sum
+// of probabilities (reduced across lanes once, at the end), and the scale m
+// shared by a query's lanes is raised only when some score passes it by more
+// than kSlack (so most steps need no cross-lane reduction; probabilities stay
+// below 2^kSlack).  Queries (fp32) and probabilities enter the bf16 MFMAs as
+// hi + lo halves, so the only rounding left is the cache's own storage.  With
+// one key split the kernel writes the output; otherwise each split writes
+// (m, l, unnormalised O) and a merge kernel combines the splits of a row in
+// split order.
 #include "common.h"
 #include "kernels.h"
 
@@ -23,235 +37,318 @@ namespace dinfer {
 
 namespace {
 
-constexpr int QT = 64;   // queries per workgroup
-constexpr int KT = 64;   // keys per LDS chunk
+constexpr float kSlack = 8.f;
 
-template <typename T, int HD>
-__global__ __launch_bounds__(256) void attn_split_kernel(
-    PassTable tb, int q_tiles, int keys_per_split, int m_cap, const float* __restrict__ q,
-    const T* __restrict__ kc, const T* __restrict__ vc, int H, int max_len, float scale_log2,
-    float* __restrict__ o_part, float* __restrict__ ml_part) {
+template <typename T, int HD, int QTW>
+__global__ __launch_bounds__(256) void attn_kernel(
+    PassTable tb, int q_blocks, int keys_per_split, int n_split, int m_cap,
+    const float* __restrict__ q, const T* __restrict__ kc, const T* __restrict__ vt, int H,
+    int Lp, float scale_log2, float* __restrict__ o_part, float* __restrict__ ml_part,
+    float* __restrict__ out) {
   using MF = Mfma<T>;
+  using SO = SplitOperand<T>;
   constexpr int VEC = MF::VEC;
-  constexpr int KSTEP = MF::KSTEP;
-  constexpr int QV = HD / KSTEP;               // vector steps over the head dim
-  constexpr int KSTR = HD + 16 / sizeof(T);    // K rows in LDS
-  constexpr int VSTR = KT + 8;                 // V^T rows in LDS (elements)
-  constexpr int HT = HD / 16;                  // 16-wide output tiles over hd
-  constexpr int VPK = HD / VEC;                // 16-byte vectors per key row
-  __shared__ __attribute__((aligned(16))) T Ks[KT * KSTR];
-  __shared__ __attribute__((aligned(16))) T Vt[HD * VSTR];
+  constexpr int KS = MF::KSTEP;        // keys per step
+  constexpr int NTS = KS / 16;         // 16-key score tiles per step
+  constexpr int QV = HD / KS;          // vector steps over the head dim
+  constexpr int HT = HD / 16;          // 16-row output tiles over the head dim
+  constexpr int PL = SO::PARTS;
+  constexpr int QB = 64 * QTW;         // queries per workgroup
+  constexpr int NK = NTS * QV;         // K fragments per step
+  constexpr int NF = NK + HT;          // K and V fragments per step
+  constexpr int FW = NF / 4;           // fragments each wave loads
+  static_assert(NF % 4 == 0, "fragments must split over four waves");
+  __shared__ V16 frag[2][NF][64];
 
   const int split = blockIdx.x;
   const int h = blockIdx.y;
-  const int r = blockIdx.z / q_tiles;
-  const int qt = blockIdx.z % q_tiles;
+  const int r = blockIdx.z / q_blocks;
+  const int qb = blockIdx.z % q_blocks;
   const int nq = tb.req_nrows[r];
-  if (qt * QT >= nq) return;
+  if (qb * QB >= nq) return;
   const int L = tb.req_len[r];
   const int k0 = split * keys_per_split;
   if (k0 >= L) return;
   const int k1 = min(L, k0 + keys_per_split);
+  const int n_steps = (k1 - k0 + KS - 1) / KS;
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int lc = lane & 15;
   const int lg = lane >> 4;
-  const int qloc = qt * QT + wave * 16 + lc;    // query index inside the request's rows
-  const bool qvalid = qloc < nq;
-  const int qrow = tb.req_row_off[r] + qloc;
   const int d = H * HD;
 
-  using SO = SplitOperand<T>;
-  constexpr int QP = SO::PARTS;
-  V16 qf[QV][QP];
+  // query fragments (B operand of S^T): query lc of each tile, hd g*VEC..
+  V16 qf[QTW][QV][PL];
+  int qrow[QTW];
+  bool qvalid[QTW];
 #pragma unroll
-  for (int kk = 0; kk < QV; ++kk) {
-    float qv[VEC];
+  for (int u = 0; u < QTW; ++u) {
+    const int qloc = qb * QB + (wave * QTW + u) * 16 + lc;
+    qvalid[u] = qloc < nq;
+    qrow[u] = tb.req_row_off[r] + (qvalid[u] ? qloc : 0);
 #pragma unroll
-    for (int e = 0; e < VEC; e += 4) {
-      const float4 x = qvalid ? *reinterpret_cast<const float4*>(
-                                    q + (size_t)qrow * d + h * HD + kk * KSTEP + lg * VEC + e)
-                              : make_float4(0.f, 0.f, 0.f, 0.f);
-      qv[e] = x.x;
-      qv[e + 1] = x.y;
-      qv[e + 2] = x.z;
-      qv[e + 3] = x.w;
+    for (int kk = 0; kk < QV; ++kk) {
+      float qv[VEC];
+#pragma unroll
+      for (int e = 0; e < VEC; e += 4) {
+        const float4 x = qvalid[u] ? *reinterpret_cast<const float4*>(
+                                         q + (size_t)qrow[u] * d + h * HD + kk * KS + lg * VEC + e)
+                                   : make_float4(0.f, 0.f, 0.f, 0.f);
+        qv[e] = x.x;
+        qv[e + 1] = x.y;
+        qv[e + 2] = x.z;
+        qv[e + 3] = x.w;
+      }
+      SO::make(qv, qf[u][kk]);
     }
-    SO::make(qv, qf[kk]);
   }
 
-  floatx4 o[HT];
+  floatx4 o[QTW][HT];
+  float m_run[QTW], l_run[QTW];
 #pragma unroll
-  for (int t = 0; t < HT; ++t) o[t] = floatx4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY;
-  float l_run = 0.f;
+  for (int u = 0; u < QTW; ++u) {
+#pragma unroll
+    for (int t = 0; t < HT; ++t) o[u][t] = floatx4{0.f, 0.f, 0.f, 0.f};
+    m_run[u] = -INFINITY;
+    l_run[u] = 0.f;
+  }
 
-  const size_t head_base = ((size_t)r * H + h) * max_len;
-  for (int kb = k0; kb < k1; kb += KT) {
-    __syncthreads();
-    for (int v = threadIdx.x; v < KT * VPK; v += 256) {
-      const int key = v / VPK;
-      const int cv = v % VPK;
-      V16 kv = zero16(), vv = zero16();
-      if (kb + key < k1) {
-        kv = ld16(kc + (head_base + kb + key) * HD + cv * VEC);
-        vv = ld16(vc + (head_base + kb + key) * HD + cv * VEC);
-      }
-      st16(&Ks[key * KSTR + cv * VEC], kv);
-      const T* ve = reinterpret_cast<const T*>(&vv);
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) Vt[(cv * VEC + e) * VSTR + key] = ve[e];
-    }
-    __syncthreads();
+  const size_t head = (size_t)r * H + h;
+  const T* kbase = kc + head * Lp * HD + lg * VEC;
+  const T* vbase = vt + head * Lp * HD + lc * 32 + lg * VEC;   // tile-major V^T
+  // score-tile row j of tile t holds key key_of(t, j) of the step
+  const int krow0 = NTS == 2 ? 8 * (lc >> 2) + (lc & 3) : lc;
 
-    // S^T tiles: s[t][i] = score(query lc, key kb + 16 t + 4 lg + i)
-    floatx4 s[KT / 16];
+  // fragment f of a step, as lane `lane` holds it: f < NK is K tile t = f /
+  // QV, head-dim step kk = f % QV; the rest are V^T row tiles ht = f - NK
+  auto load = [&](V16 (&reg)[FW], int s) {
+    const int kb = k0 + min(s, n_steps - 1) * KS;   // past the end: repeat the last step
 #pragma unroll
-    for (int t = 0; t < KT / 16; ++t) {
-      s[t] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kk = 0; kk < QV; ++kk) {
-        const V16 a = *reinterpret_cast<const V16*>(&Ks[(t * 16 + lc) * KSTR + kk * KSTEP + lg * VEC]);
-#pragma unroll
-        for (int p = 0; p < QP; ++p) MF::mac(s[t], a, qf[kk][p]);
+    for (int i = 0; i < FW; ++i) {
+      const int f = wave * FW + i;
+      if (f < NK) {
+        const int key = min(kb + krow0 + 4 * (f / QV), L - 1);   // rows past the range are masked
+        reg[i] = ld16(kbase + (size_t)key * HD + (f % QV) * KS);
+      } else {
+        reg[i] = ld16(vbase + (size_t)(kb >> 5) * HD * 32 + (f - NK) * 16 * 32 + (kb & 31));
       }
     }
-    float mx = -INFINITY;
+  };
+  auto store = [&](const V16 (&reg)[FW], int buf) {
 #pragma unroll
-    for (int t = 0; t < KT / 16; ++t)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int key = kb + t * 16 + lg * 4 + i;
-        const float v = key < k1 ? s[t][i] * scale_log2 : -INFINITY;
-        s[t][i] = v;
-        mx = fmaxf(mx, v);
-      }
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float m_new = fmaxf(m_run, mx);      // finite: the chunk holds at least one key
-    const float alpha = exp2f(m_run - m_new);
-    float ps = 0.f;
-#pragma unroll
-    for (int t = 0; t < KT / 16; ++t)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float p = exp2f(s[t][i] - m_new);
-        s[t][i] = p;
-        ps += p;
-      }
-    ps += __shfl_xor(ps, 16, 64);
-    ps += __shfl_xor(ps, 32, 64);
-    l_run = l_run * alpha + ps;
-    m_run = m_new;
-#pragma unroll
-    for (int t = 0; t < HT; ++t)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) o[t][i] *= alpha;
+    for (int i = 0; i < FW; ++i) frag[buf][wave * FW + i][lane] = reg[i];
+  };
 
-    // O^T[hd][q] += V^T[hd][key] * P^T[key][q]
+  auto compute = [&](int buf, int s) {
+    const int kb = k0 + s * KS;
+    V16 kf[NK];
 #pragma unroll
-    for (int t = 0; t < KT / 16; ++t) {
-      float pv[4] = {s[t][0], s[t][1], s[t][2], s[t][3]};
+    for (int f = 0; f < NK; ++f) kf[f] = frag[buf][f][lane];
+#pragma unroll
+    for (int u = 0; u < QTW; ++u) {
+      floatx4 sc[NTS];
+#pragma unroll
+      for (int t = 0; t < NTS; ++t) {
+        sc[t] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < QV; ++kk)
+#pragma unroll
+          for (int p = 0; p < PL; ++p) MF::mac(sc[t], kf[t * QV + kk], qf[u][kk][p]);
+      }
+      // lane (query lc, group lg) holds keys kb + lg*VEC + e, e = 4t + i
+      float pv[VEC];
+      float mloc = -INFINITY;
+#pragma unroll
+      for (int t = 0; t < NTS; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int e = 4 * t + i;
+          const float v = kb + lg * VEC + e < k1 ? sc[t][i] * scale_log2 : -INFINITY;
+          pv[e] = v;
+          mloc = fmaxf(mloc, v);
+        }
+      if (__any(mloc > m_run[u] + kSlack)) {      // wave-uniform: raise the scale
+        float mx = fmaxf(mloc, __shfl_xor(mloc, 16, 64));
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        const float m_new = fmaxf(m_run[u], mx);  // finite after the first step
+        const float alpha = exp2f(m_run[u] - m_new);
+        l_run[u] *= alpha;
+#pragma unroll
+        for (int ht = 0; ht < HT; ++ht)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) o[u][ht][i] *= alpha;
+        m_run[u] = m_new;
+      }
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+        pv[e] = exp2f(pv[e] - m_run[u]);
+        l_run[u] += pv[e];
+      }
+      V16 pf[PL];
+      SO::make(pv, pf);
 #pragma unroll
       for (int ht = 0; ht < HT; ++ht) {
-        const T* vr = &Vt[(ht * 16 + lc) * VSTR + t * 16 + lg * 4];
-        float av[4] = {to_f(vr[0]), to_f(vr[1]), to_f(vr[2]), to_f(vr[3])};
-        Mfma4<T>::mac_split_b(o[ht], av, pv);
+        const V16 vf = frag[buf][NK + ht][lane];
+#pragma unroll
+        for (int p = 0; p < PL; ++p) MF::mac(o[u][ht], vf, pf[p]);
       }
     }
+  };
+
+  // Registers hold the loads of the next two steps; at step s the loads of
+  // s+2 are issued, step s is computed from LDS, the registers of s+1 are
+  // stored to the other LDS buffer, and a barrier ends the step.  Three
+  // register sets rotate through a three-times unrolled loop (a copy would
+  // wait for the loads just issued); every step loads (clamped), so the
+  // waits stay two steps deep on every path.
+  V16 r0[FW], r1[FW], r2[FW];
+  auto step = [&](int s, V16 (&next)[FW], V16 (&ahead)[FW]) {
+    load(ahead, s + 2);
+    compute(s & 1, s);
+    store(next, (s + 1) & 1);
+    __syncthreads();
+  };
+  load(r0, 0);
+  load(r1, 1);
+  store(r0, 0);
+  __syncthreads();
+  for (int s = 0; s < n_steps; s += 3) {
+    step(s, r1, r2);
+    if (s + 1 < n_steps) step(s + 1, r2, r0);
+    if (s + 2 < n_steps) step(s + 2, r0, r1);
   }
 
-  if (!qvalid) return;
-  const size_t base = ((size_t)split * m_cap + qrow) * H + h;
-  float* op = o_part + base * HD;
+  // each lane summed its own keys: total over the query's four lanes
 #pragma unroll
-  for (int ht = 0; ht < HT; ++ht)
+  for (int u = 0; u < QTW; ++u) {
+    l_run[u] += __shfl_xor(l_run[u], 16, 64);
+    l_run[u] += __shfl_xor(l_run[u], 32, 64);
+  }
+
 #pragma unroll
-    for (int i = 0; i < 4; ++i) op[ht * 16 + lg * 4 + i] = o[ht][i];
-  if (lg == 0) {
-    ml_part[base * 2] = m_run;
-    ml_part[base * 2 + 1] = l_run;
+  for (int u = 0; u < QTW; ++u) {
+    if (!qvalid[u]) continue;
+    if (n_split == 1) {
+      const float inv = 1.f / l_run[u];
+      float* orow = out + (size_t)qrow[u] * d + h * HD;
+#pragma unroll
+      for (int ht = 0; ht < HT; ++ht)
+        *reinterpret_cast<float4*>(orow + ht * 16 + lg * 4) =
+            make_float4(o[u][ht][0] * inv, o[u][ht][1] * inv, o[u][ht][2] * inv,
+                        o[u][ht][3] * inv);
+    } else {
+      const size_t base = ((size_t)split * m_cap + qrow[u]) * H + h;
+      float* op = o_part + base * HD;
+#pragma unroll
+      for (int ht = 0; ht < HT; ++ht)
+        *reinterpret_cast<float4*>(op + ht * 16 + lg * 4) =
+            make_float4(o[u][ht][0], o[u][ht][1], o[u][ht][2], o[u][ht][3]);
+      if (lg == 0) {
+        ml_part[base * 2] = m_run[u];
+        ml_part[base * 2 + 1] = l_run[u];
+      }
+    }
   }
 }
 
-// Combine the key splits of each (row, head): out = sum_s 2^(m_s - M) O_s /
-// sum_s 2^(m_s - M) l_s, splits taken in order.
+// Combine the key splits of each row: out = sum_s 2^(m_s - M) O_s /
+// sum_s 2^(m_s - M) l_s per head, splits taken in order.  One float4 of the
+// row per thread.
 template <int HD>
-__global__ __launch_bounds__(64) void attn_merge_kernel(PassTable tb, int keys_per_split,
-                                                        int n_split, int m_cap,
-                                                        const float* __restrict__ o_part,
-                                                        const float* __restrict__ ml_part, int H,
-                                                        float* __restrict__ out) {
+__global__ __launch_bounds__(256) void attn_merge_kernel(PassTable tb, int keys_per_split,
+                                                         int n_split, int m_cap,
+                                                         const float* __restrict__ o_part,
+                                                         const float* __restrict__ ml_part,
+                                                         int H, float* __restrict__ out) {
   const int m = blockIdx.x;
-  const int h = blockIdx.y;
   if (m >= min(*tb.nrows, m_cap)) return;
+  const int i4 = blockIdx.y * 256 + threadIdx.x;
+  if (i4 * 4 >= H * HD) return;
+  const int h = i4 * 4 / HD;
   const int r = tb.row_req[m];
   const int L = tb.req_len[r];
-  int ns = (L + keys_per_split - 1) / keys_per_split;
-  if (ns > n_split) ns = n_split;
+  const int ns = min(n_split, (L + keys_per_split - 1) / keys_per_split);
   float M = -INFINITY;
   for (int s = 0; s < ns; ++s) M = fmaxf(M, ml_part[(((size_t)s * m_cap + m) * H + h) * 2]);
   float lsum = 0.f;
-  float acc[HD / 64];
-#pragma unroll
-  for (int e = 0; e < HD / 64; ++e) acc[e] = 0.f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   for (int s = 0; s < ns; ++s) {
     const size_t base = ((size_t)s * m_cap + m) * H + h;
     const float w = exp2f(ml_part[base * 2] - M);
     lsum += w * ml_part[base * 2 + 1];
-#pragma unroll
-    for (int e = 0; e < HD / 64; ++e) acc[e] += w * o_part[base * HD + threadIdx.x + 64 * e];
+    const float4 v = *reinterpret_cast<const float4*>(o_part + base * HD + (i4 * 4) % HD);
+    acc.x += w * v.x;
+    acc.y += w * v.y;
+    acc.z += w * v.z;
+    acc.w += w * v.w;
   }
   const float inv = 1.f / lsum;
-  float* orow = out + (size_t)m * H * HD + h * HD;
-#pragma unroll
-  for (int e = 0; e < HD / 64; ++e) orow[threadIdx.x + 64 * e] = acc[e] * inv;
+  *reinterpret_cast<float4*>(out + (size_t)m * H * HD + i4 * 4) =
+      make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
 }
 
-template <typename T, int HD>
+template <typename T, int HD, int QTW>
 hipError_t run(const AttnPlan& p, PassTable tb, int batch, int m_cap, const float* q,
-               const void* kc, const void* vc, int H, int max_len, float* o_part, float* ml_part,
+               const void* kc, const void* vt, int H, int Lp, float* o_part, float* ml_part,
                float* o, hipStream_t st) {
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)HD);
-  dim3 grid(p.n_split, H, batch * p.q_tiles);
-  hipLaunchKernelGGL((attn_split_kernel<T, HD>), grid, dim3(256), 0, st, tb, p.q_tiles,
-                     p.keys_per_split, m_cap, q, static_cast<const T*>(kc),
-                     static_cast<const T*>(vc), H, max_len, scale_log2, o_part, ml_part);
+  dim3 grid(p.n_split, H, batch * p.q_blocks);
+  hipLaunchKernelGGL((attn_kernel<T, HD, QTW>), grid, dim3(256), 0, st, tb,
+                     p.q_blocks,
+                     p.keys_per_split, p.n_split, m_cap, q, static_cast<const T*>(kc),
+                     static_cast<const T*>(vt), H, Lp, scale_log2, o_part, ml_part, o);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((attn_merge_kernel<HD>), dim3(m_cap, H), dim3(64), 0, st, tb,
+  if (e != hipSuccess || p.n_split == 1) return e;
+  const int blocks_y = (H * HD / 4 + 255) / 256;
+  hipLaunchKernelGGL((attn_merge_kernel<HD>), dim3(m_cap, blocks_y), dim3(256), 0, st, tb,
                      p.keys_per_split, p.n_split, m_cap, o_part, ml_part, H, o);
   return hipGetLastError();
 }
 
+template <typename T, int HD>
+hipError_t run_q(const AttnPlan& p, PassTable tb, int batch, int m_cap, const float* q,
+                 const void* kc, const void* vt, int H, int Lp, float* o_part, float* ml_part,
+                 float* o, hipStream_t st) {
+  if (p.qtw == 1) return run<T, HD, 1>(p, tb, batch, m_cap, q, kc, vt, H, Lp, o_part, ml_part, o, st);
+  if (p.qtw == 2) return run<T, HD, 2>(p, tb, batch, m_cap, q, kc, vt, H, Lp, o_part, ml_part, o, st);
+  return hipErrorInvalidValue;
+}
+
 }  // namespace
 
+int attn_cache_len(int max_len) { return (max_len + 63) / 64 * 64; }
+
+// Blocks of 64 queries, one 16-query tile per wave (measured faster than two
+// tiles per wave over the same keys, which halves the workgroups).  Then key
+// splits while the grid stays within target_wgs and every split keeps at
+// least 192 keys (shorter splits cost more in fixed work and partials than
+// they gain in parallelism).
 AttnPlan plan_attention(int batch, int max_rows_per_req, int max_keys, int H, int target_wgs) {
   AttnPlan p{};
-  p.q_tiles = (max_rows_per_req + QT - 1) / QT;
-  if (p.q_tiles < 1) p.q_tiles = 1;
-  const int chunks = (max_keys + KT - 1) / KT;
-  const int base = batch * p.q_tiles * H;
-  int ns = (target_wgs + base - 1) / base;
+  p.qtw = 1;
+  p.q_blocks = (max_rows_per_req + 63) / 64;
+  if (p.q_blocks < 1) p.q_blocks = 1;
+  const int steps = (max_keys + 31) / 32;
+  const int base = batch * p.q_blocks * H;
+  int ns = target_wgs / base;
+  if (ns > max_keys / 192) ns = max_keys / 192;
   if (ns < 1) ns = 1;
-  if (ns > chunks) ns = chunks;
-  int kps = (chunks + ns - 1) / ns * KT;
-  p.keys_per_split = kps;
-  p.n_split = (max_keys + kps - 1) / kps;
+  p.keys_per_split = (steps + ns - 1) / ns * 32;
+  p.n_split = (max_keys + p.keys_per_split - 1) / p.keys_per_split;
   return p;
 }
 
 hipError_t launch_attention(DType t, const AttnPlan& p, PassTable tb, int batch, int m_cap,
-                            const float* q, const void* kc, const void* vc, int H, int hd,
-                            int max_len, float* o_part, float* ml_part, float* o,
-                            hipStream_t st) {
+                            const float* q, const void* kc, const void* vt, int H, int hd,
+                            int Lp, float* o_part, float* ml_part, float* o, hipStream_t st) {
+  if (Lp % 64 != 0 || p.keys_per_split % 32 != 0) return hipErrorInvalidValue;
   if (t == DType::F32) {
-    if (hd == 64) return run<float, 64>(p, tb, batch, m_cap, q, kc, vc, H, max_len, o_part, ml_part, o, st);
-    if (hd == 128) return run<float, 128>(p, tb, batch, m_cap, q, kc, vc, H, max_len, o_part, ml_part, o, st);
+    if (hd == 64) return run_q<float, 64>(p, tb, batch, m_cap, q, kc, vt, H, Lp, o_part, ml_part, o, st);
+    if (hd == 128) return run_q<float, 128>(p, tb, batch, m_cap, q, kc, vt, H, Lp, o_part, ml_part, o, st);
   } else {
-    if (hd == 64) return run<bf16, 64>(p, tb, batch, m_cap, q, kc, vc, H, max_len, o_part, ml_part, o, st);
-    if (hd == 128) return run<bf16, 128>(p, tb, batch, m_cap, q, kc, vc, H, max_len, o_part, ml_part, o, st);
+    if (hd == 64) return run_q<bf16, 64>(p, tb, batch, m_cap, q, kc, vt, H, Lp, o_part, ml_part, o, st);
+    if (hd == 128) return run_q<bf16, 128>(p, tb, batch, m_cap, q, kc, vt, H, Lp, o_part, ml_part, o, st);
   }
   return hipErrorInvalidValue;
 }

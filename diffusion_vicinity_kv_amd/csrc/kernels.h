@@ -59,7 +59,7 @@ hipError_t launch_add_rmsnorm(DType t, const int* nrows, int m_cap, float* x, co
                               hipStream_t st);
 hipError_t launch_qkv_rope_scatter(DType t, PassTable tb, int m_cap, const float* P, int S,
                                    size_t p_stride, int d, int H, int hd, const float* rope_cs,
-                                   float* q_out, void* kc, void* vc, int max_len, hipStream_t st);
+                                   float* q_out, void* kc, void* vt, int Lp, hipStream_t st);
 hipError_t launch_swiglu(const int* nrows, int m_cap, const float* P, int S, size_t p_stride,
                          int F, float* act, hipStream_t st);
 // block rows of the window -> x + sum_s P[s] -> rmsnorm * g -> out[r*B + j];
@@ -72,13 +72,15 @@ hipError_t launch_final_norm(DType t, PassTable tb, int batch, int B, const floa
 
 // ---- attention ---------------------------------------------------------------
 struct AttnPlan {
-  int q_tiles, n_split, keys_per_split;
+  int qtw;              // 16-query tiles per wave (query block = 64 * qtw)
+  int q_blocks, n_split, keys_per_split;
 };
+// Padded cache length Lp of K [req][head][Lp][hd] and V^T [req][head][hd][Lp].
+int attn_cache_len(int max_len);
 AttnPlan plan_attention(int batch, int max_rows_per_req, int max_keys, int H, int target_wgs);
 hipError_t launch_attention(DType t, const AttnPlan& p, PassTable tb, int batch, int m_cap,
-                            const float* q, const void* kc, const void* vc, int H, int hd,
-                            int max_len, float* o_part, float* ml_part, float* o,
-                            hipStream_t st);
+                            const float* q, const void* kc, const void* vt, int H, int hd,
+                            int Lp, float* o_part, float* ml_part, float* o, hipStream_t st);
 
 // ---- vocab statistics ---------------------------------------------------------
 struct VocabPlan {

@@ -121,58 +121,79 @@ __global__ __launch_bounds__(kNormThreads) void add_rmsnorm_kernel(
 // attention and scatter k, v into the cache at the row's position -- before
 // any query of this layer reads the cache (dInfer news article, section
 // "削减计算成本：邻近KV缓存刷新": only the window's KV is recomputed).
-constexpr int kQkvThreads = 512;
+// K goes to [request][head][Lp][hd]; V to transposed tiles of 32 positions,
+// [request][head][Lp/32][hd][32], through an LDS tile, so that consecutive
+// threads store consecutive positions.  A workgroup takes 16 rows of one head.
+constexpr int kQkvRows = 16;
+constexpr int kQkvThreads = 256;
 
 template <typename T>
 __global__ __launch_bounds__(kQkvThreads) void qkv_rope_scatter_kernel(
     PassTable tb, int m_cap, const float* __restrict__ P, int S, size_t p_stride, int d, int H,
     int hd, const float* __restrict__ rope_cs, float* __restrict__ q_out, T* __restrict__ kc,
-    T* __restrict__ vc, int max_len) {
-  const int m = blockIdx.x;
-  if (m >= min(*tb.nrows, m_cap)) return;
-  const int r = tb.row_req[m];
-  const int pos = tb.row_pos[m];
+    T* __restrict__ vt, int Lp) {
+  __shared__ float vs[128 * (kQkvRows + 1)];
+  const int m0 = blockIdx.x * kQkvRows;
+  const int h = blockIdx.y;
+  const int M = min(*tb.nrows, m_cap);
+  if (m0 >= M) return;
   const int half = hd / 2;
-  const int hq = half / 4;                         // float4 groups per half head
-  const float* pr = P + (size_t)m * 3 * d;
-  const float* cs = rope_cs + (size_t)pos * hd;   // [pos][cos half | sin half]
+  const int rr = threadIdx.x / 16;                // row of the tile
+  const int m = m0 + rr;
   const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int i = threadIdx.x; i < H * hq; i += kQkvThreads) {
-    const int h = i / hq;
-    const int j = (i % hq) * 4;
-    const int c0 = h * hd + j;
-    const int c1 = c0 + half;
-    const float4 q0 = add_partials4(z4, pr + c0, p_stride, S);
-    const float4 q1 = add_partials4(z4, pr + c1, p_stride, S);
-    const float4 k0 = add_partials4(z4, pr + d + c0, p_stride, S);
-    const float4 k1 = add_partials4(z4, pr + d + c1, p_stride, S);
-    const float4 v0 = add_partials4(z4, pr + 2 * d + c0, p_stride, S);
-    const float4 v1 = add_partials4(z4, pr + 2 * d + c1, p_stride, S);
-    const float4 c = *reinterpret_cast<const float4*>(cs + j);
-    const float4 sn = *reinterpret_cast<const float4*>(cs + half + j);
-    float* qr = q_out + (size_t)m * d;
-    *reinterpret_cast<float4*>(qr + c0) =
-        make_float4(q0.x * c.x - q1.x * sn.x, q0.y * c.y - q1.y * sn.y, q0.z * c.z - q1.z * sn.z,
-                    q0.w * c.w - q1.w * sn.w);
-    *reinterpret_cast<float4*>(qr + c1) =
-        make_float4(q1.x * c.x + q0.x * sn.x, q1.y * c.y + q0.y * sn.y, q1.z * c.z + q0.z * sn.z,
-                    q1.w * c.w + q0.w * sn.w);
-    const size_t cb = (((size_t)r * H + h) * max_len + pos) * hd;
-    T* kp = kc + cb;
-    T* vp = vc + cb;
-    const float ka[4] = {k0.x * c.x - k1.x * sn.x, k0.y * c.y - k1.y * sn.y,
-                         k0.z * c.z - k1.z * sn.z, k0.w * c.w - k1.w * sn.w};
-    const float kb[4] = {k1.x * c.x + k0.x * sn.x, k1.y * c.y + k0.y * sn.y,
-                         k1.z * c.z + k0.z * sn.z, k1.w * c.w + k0.w * sn.w};
-    const float va[4] = {v0.x, v0.y, v0.z, v0.w};
-    const float vb[4] = {v1.x, v1.y, v1.z, v1.w};
+  if (m < M) {
+    const int r = tb.row_req[m];
+    const int pos = tb.row_pos[m];
+    const float* pr = P + (size_t)m * 3 * d;
+    const float* cs = rope_cs + (size_t)pos * hd;   // [pos][cos half | sin half]
+    T* kp = kc + (((size_t)r * H + h) * Lp + pos) * hd;
+    float* qr = q_out + (size_t)m * d + h * hd;
+    for (int j = (threadIdx.x % 16) * 4; j < half; j += 64) {
+      const int c0 = h * hd + j;
+      const int c1 = c0 + half;
+      const float4 q0 = add_partials4(z4, pr + c0, p_stride, S);
+      const float4 q1 = add_partials4(z4, pr + c1, p_stride, S);
+      const float4 k0 = add_partials4(z4, pr + d + c0, p_stride, S);
+      const float4 k1 = add_partials4(z4, pr + d + c1, p_stride, S);
+      const float4 v0 = add_partials4(z4, pr + 2 * d + c0, p_stride, S);
+      const float4 v1 = add_partials4(z4, pr + 2 * d + c1, p_stride, S);
+      const float4 c = *reinterpret_cast<const float4*>(cs + j);
+      const float4 sn = *reinterpret_cast<const float4*>(cs + half + j);
+      *reinterpret_cast<float4*>(qr + j) =
+          make_float4(q0.x * c.x - q1.x * sn.x, q0.y * c.y - q1.y * sn.y,
+                      q0.z * c.z - q1.z * sn.z, q0.w * c.w - q1.w * sn.w);
+      *reinterpret_cast<float4*>(qr + j + half) =
+          make_float4(q1.x * c.x + q0.x * sn.x, q1.y * c.y + q0.y * sn.y,
+                      q1.z * c.z + q0.z * sn.z, q1.w * c.w + q0.w * sn.w);
+      const float ka[4] = {k0.x * c.x - k1.x * sn.x, k0.y * c.y - k1.y * sn.y,
+                           k0.z * c.z - k1.z * sn.z, k0.w * c.w - k1.w * sn.w};
+      const float kb[4] = {k1.x * c.x + k0.x * sn.x, k1.y * c.y + k0.y * sn.y,
+                           k1.z * c.z + k0.z * sn.z, k1.w * c.w + k0.w * sn.w};
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      kp[j + e] = from_f<T>(ka[e]);
-      kp[j + half + e] = from_f<T>(kb[e]);
-      vp[j + e] = from_f<T>(va[e]);
-      vp[j + half + e] = from_f<T>(vb[e]);
+      for (int e = 0; e < 4; ++e) {
+        kp[j + e] = from_f<T>(ka[e]);
+        kp[j + half + e] = from_f<T>(kb[e]);
+      }
+      const float va[4] = {v0.x, v0.y, v0.z, v0.w};
+      const float vb[4] = {v1.x, v1.y, v1.z, v1.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        vs[(j + e) * (kQkvRows + 1) + rr] = va[e];
+        vs[(j + half + e) * (kQkvRows + 1) + rr] = vb[e];
+      }
     }
+  }
+  __syncthreads();
+  // V^T: element (dim hi, tile row rr2), rows fastest
+  for (int e = threadIdx.x; e < hd * kQkvRows; e += kQkvThreads) {
+    const int rr2 = e % kQkvRows;
+    const int hi = e / kQkvRows;
+    const int m2 = m0 + rr2;
+    if (m2 >= M) continue;
+    const int r = tb.row_req[m2];
+    const int pos = tb.row_pos[m2];
+    vt[(((size_t)r * H + h) * Lp + (pos & ~31)) * hd + hi * 32 + (pos & 31)] =
+        from_f<T>(vs[hi * (kQkvRows + 1) + rr2]);
   }
 }
 
@@ -288,11 +309,12 @@ hipError_t launch_add_rmsnorm(DType t, const int* nrows, int m_cap, float* x, co
 
 hipError_t launch_qkv_rope_scatter(DType t, PassTable tb, int m_cap, const float* P, int S,
                                    size_t p_stride, int d, int H, int hd, const float* rope_cs,
-                                   float* q_out, void* kc, void* vc, int max_len, hipStream_t st) {
-  DISPATCH_T(t, hipLaunchKernelGGL((qkv_rope_scatter_kernel<T>), dim3(m_cap), dim3(kQkvThreads), 0,
-                                   st, tb, m_cap, P, S, p_stride, d, H, hd, rope_cs, q_out,
-                                   static_cast<T*>(kc),
-                                   static_cast<T*>(vc), max_len));
+                                   float* q_out, void* kc, void* vt, int Lp, hipStream_t st) {
+  if (hd > 128 || hd % 8 != 0) return hipErrorInvalidValue;
+  const dim3 grid((m_cap + kQkvRows - 1) / kQkvRows, H);
+  DISPATCH_T(t, hipLaunchKernelGGL((qkv_rope_scatter_kernel<T>), grid, dim3(kQkvThreads), 0, st,
+                                   tb, m_cap, P, S, p_stride, d, H, hd, rope_cs, q_out,
+                                   static_cast<T*>(kc), static_cast<T*>(vt), Lp));
   return hipGetLastError();
 }
 

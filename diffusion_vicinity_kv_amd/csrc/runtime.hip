@@ -43,6 +43,7 @@ inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 struct Layout {
   int d, H, hd, F, V, nl, B, w;
   int max_batch, max_len;
+  int Lp;                       // cache length per head row (max_len padded to 64)
   int m_step, m_ref, m_all;     // row capacities: step pass, refresh pass, either
   int lm_rows;                  // max_batch * B
   DType dt;
@@ -152,7 +153,7 @@ bool make_layout(const dinfer_model_cfg* m, const dinfer_decode_cfg* dc, int max
                            pe(l.g_qkv_r, l.m_ref, 3 * d), pe(l.g_o_r, l.m_ref, d),
                            pe(l.g_gu_r, l.m_ref, 2 * Fd), pe(l.g_d_r, l.m_ref, d)});
   // about one workgroup per CU: more key splits only add fp32 partial traffic
-  l.a_step = plan_attention(max_batch, win, max_len, l.H, 256);
+  l.a_step = plan_attention(max_batch, win, max_len, l.H, 512);
   l.a_ref = plan_attention(max_batch, max_len, max_len, l.H, 512);
   l.attn_o_elems = std::max((size_t)l.a_step.n_split * l.m_step, (size_t)l.a_ref.n_split * l.m_ref) *
                    l.H * l.hd;
@@ -160,7 +161,8 @@ bool make_layout(const dinfer_model_cfg* m, const dinfer_decode_cfg* dc, int max
   l.vp = plan_vocab(l.lm_rows, V, 1024);
   l.tab_ints_step = table_ints(l.m_step, max_batch);
   l.tab_ints_ref = table_ints(l.m_ref, max_batch);
-  l.kv_layer_elems = (size_t)max_batch * l.H * max_len * l.hd;
+  l.Lp = attn_cache_len(max_len);
+  l.kv_layer_elems = (size_t)max_batch * l.H * l.Lp * l.hd;
 
   const size_t es = dtype_size(dt);
   size_t o = 0;
@@ -363,9 +365,9 @@ dinfer_status run_pass(dinfer_ctx* c, bool step) {
     char* kvk = c->at<char>(L.off_kvk) + (size_t)l * L.kv_layer_elems * es;
     char* kvv = c->at<char>(L.off_kvv) + (size_t)l * L.kv_layer_elems * es;
     HIP_TRY(launch_qkv_rope_scatter(dt, tb, m_cap, part, gq.splits, stride_q, d, L.H, L.hd,
-                                    c->at<float>(L.off_rope), q, kvk, kvv, L.max_len, st));
+                                    c->at<float>(L.off_rope), q, kvk, kvv, L.Lp, st));
     if (!step && last) break;   // a refresh needs only the caches
-    HIP_TRY(launch_attention(dt, ap, tb, L.max_batch, m_cap, q, kvk, kvv, L.H, L.hd, L.max_len,
+    HIP_TRY(launch_attention(dt, ap, tb, L.max_batch, m_cap, q, kvk, kvv, L.H, L.hd, L.Lp,
                              c->at<float>(L.off_ao), c->at<float>(L.off_aml), o, st));
     HIP_TRY(launch_gemm(go, dt, o, c->wo[l], part, tb.nrows, m_cap, d, d, st));
     HIP_TRY(launch_add_rmsnorm(dt, tb.nrows, m_cap, x, part, go.splits, stride_d, c->ffn_norm[l],
@@ -583,6 +585,12 @@ dinfer_status dinfer_step_init(const dinfer_model_cfg* m, const dinfer_decode_cf
           hipSuccess ||
       hipMemsetAsync(c->at<char>(L.off_tab_ref), 0, (size_t)L.tab_ints_ref * 4, c->stream) !=
           hipSuccess ||
+      // cache padding and positions never written must hold finite values:
+      // the attention multiplies their (zero) probabilities with V
+      hipMemsetAsync(c->at<char>(L.off_kvk), 0, L.kv_layer_elems * L.nl * dtype_size(L.dt),
+                     c->stream) != hipSuccess ||
+      hipMemsetAsync(c->at<char>(L.off_kvv), 0, L.kv_layer_elems * L.nl * dtype_size(L.dt),
+                     c->stream) != hipSuccess ||
       hipStreamSynchronize(c->stream) != hipSuccess)
     return cleanup(fail(DINFER_E_HIP, "workspace initialisation failed"));
   *out = c;
@@ -883,6 +891,7 @@ dinfer_status dinfer_get_step_view(const dinfer_ctx* c, dinfer_step_view* v) {
   v->commit_count = c->at<int>(L.off_ccount);
   v->kv_k = c->at<char>(L.off_kvk);
   v->kv_v = c->at<char>(L.off_kvv);
+  v->kv_len = L.Lp;
   v->moe_top_k = L.moe ? L.topk : 0;
   v->moe_sel = L.moe ? c->at<int>(L.off_sel) : nullptr;
   v->moe_gate = L.moe ? c->at<float>(L.off_gate) : nullptr;

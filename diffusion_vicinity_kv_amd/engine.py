@@ -159,8 +159,11 @@ class Engine:
 
         es = 4 if self.m.dtype == "f32" else 2
         kvdt = torch.float32 if es == 4 else torch.bfloat16
-        kv_n = self.m.n_layers * self.max_batch * self.m.n_heads * self.max_len * self.m.head_dim
-        kv_shape = (self.m.n_layers, self.max_batch, self.m.n_heads, self.max_len, self.m.head_dim)
+        Lp = v.kv_len
+        kv_n = self.m.n_layers * self.max_batch * self.m.n_heads * Lp * self.m.head_dim
+        kv_shape = (self.m.n_layers, self.max_batch, self.m.n_heads, Lp, self.m.head_dim)
+        # V: transposed tiles of 32 positions, [..][H][Lp/32][hd][32]
+        vt_shape = (self.m.n_layers, self.max_batch, self.m.n_heads, Lp // 32, self.m.head_dim, 32)
         out = {}
         if v.moe_top_k > 0:
             # the last pass's rows; the widest pass is a refresh of max_batch * max_len rows
@@ -188,7 +191,7 @@ class Engine:
             "step_count": t(v.step_count, self.batch, torch.int32, (self.batch,)),
             "commit_count": t(v.commit_count, self.batch, torch.int32, (self.batch,)),
             "kv_k": t(v.kv_k, kv_n, kvdt, kv_shape),
-            "kv_v": t(v.kv_v, kv_n, kvdt, kv_shape),
+            "kv_v": t(v.kv_v, kv_n, kvdt, vt_shape),
         }
 
     def close(self):

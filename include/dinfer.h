@@ -136,8 +136,9 @@ typedef struct {
   int32_t* block_done;       /* [batch] 1 once the current block has no MASK     */
   int32_t* step_count;       /* [batch] steps taken in the current block         */
   int32_t* commit_count;     /* [batch] tokens committed in total                */
-  void* kv_k;                /* [n_layers][max_batch][H][max_len][hd] K, RoPE'd */
-  void* kv_v;                /* [n_layers][max_batch][H][max_len][hd]            */
+  void* kv_k;                /* [n_layers][max_batch][H][kv_len][hd] K, RoPE'd  */
+  void* kv_v;                /* [n_layers][max_batch][H][kv_len/32][hd][32] V in
+                                transposed tiles of 32 positions                 */
   /* MoE only (else 0 / NULL): routing of the last layer whose FFN the last
    * pass ran (a step runs every layer; a refresh stops before the last
    * layer's FFN), one row per pass row in pass order (request by request,
@@ -152,6 +153,8 @@ typedef struct {
   /* After a step: [rows][d] fp32 normalised FFN input of the last layer, rows
    * in pass order (after a refresh it holds other intermediate values). */
   float* ffn_in;
+  int32_t kv_len;            /* cache positions per head row: max_len rounded up
+                                to a multiple of 64 (padding holds zeros)        */
 } dinfer_step_view;
 
 /* Bytes of workspace dinfer_step_init needs for these shapes (0 on bad args). */

@@ -184,6 +184,16 @@ def lockstep(wc, eng, tokens, runs, logit_tol, max_steps=10_000, max_blocks=None
     return rep
 
 
+def cache_rows(v, key, layer, r, L):
+    """K or V cache of request r in one layer as [L][H][hd] float32 numpy
+    (K is stored [H][Lp][hd], V in transposed tiles [H][Lp/32][hd][32])."""
+    if key == "k":
+        return v["kv_k"][layer, r, :, :L].float().cpu().numpy().transpose(1, 0, 2)
+    t = v["kv_v"][layer, r].float().cpu().numpy()            # [H][nb][hd][32]
+    H, nb, hd, _ = t.shape
+    return t.transpose(1, 3, 0, 2).reshape(nb * 32, H, hd)[:L]
+
+
 def compare_cache(wc, eng, runs, tol=None):
     """K, V caches of every request against the oracle's.  fp32 caches: max
     |diff| <= tol * RMS.  bf16 caches store each value rounded to bf16, so an
@@ -197,7 +207,7 @@ def compare_cache(wc, eng, runs, tol=None):
     for r, run in enumerate(runs):
         for li in run.cache["k"]:
             for key in ("k", "v"):
-                g = v["kv_" + key][li, r, :, : run.L].float().cpu().numpy().transpose(1, 0, 2)
+                g = cache_rows(v, key, li, r, run.L)
                 o = run.cache[key][li]
                 rms = np.sqrt(np.mean(o ** 2))
                 bound = tol * rms + (0.0 if f32 else 2.0 ** -8 * np.abs(o))

@@ -32,15 +32,18 @@ def test_vicinity_scatter_writes_only_the_window(dense8b):
     eng.refresh_kv()
     torch.cuda.synchronize()
     v = eng.view()
-    before = {li: v["kv_k"][li, 0].clone() for li in (0, 13, 31)}
+    before = {li: (v["kv_k"][li, 0].clone(), v["kv_v"][li, 0].clone()) for li in (0, 13, 31)}
     eng.denoise_step()
     torch.cuda.synchronize()
     P, B, wv = int(req["prompt_len"][0]), wc.decode.block_len, wc.decode.vicinity_w
     lo, hi = max(0, P - wv), min(P + wc.gen_len, P + B + wv)
-    for li, k0 in before.items():
-        changed = (v["kv_k"][li, 0] != k0).any(dim=-1).any(dim=0).nonzero().flatten().cpu().numpy()
-        assert len(changed) > 0
-        assert changed.min() >= lo and changed.max() < hi, (li, changed.min(), changed.max())
+    for li, (k0, v0) in before.items():
+        # K [H][Lp][hd] and V [H][Lp/32][hd][32]: positions whose entries changed
+        for changed in ((v["kv_k"][li, 0] != k0).any(dim=-1).any(dim=0),
+                        (v["kv_v"][li, 0] != v0).any(dim=2).any(dim=0).flatten()):
+            idx = changed.nonzero().flatten().cpu().numpy()
+            assert len(idx) > 0
+            assert idx.min() >= lo and idx.max() < hi, (li, idx.min(), idx.max())
 
 
 def test_vocab_stats_agree_with_step_logits(dense8b):

@@ -16,7 +16,7 @@ import torch
 
 import oracle
 import synth
-from gpu_util import build, lockstep, note, oracle_runs, small_workload
+from gpu_util import build, cache_rows, lockstep, note, oracle_runs, small_workload
 
 pytestmark = pytest.mark.gpu
 
@@ -151,7 +151,7 @@ def test_full_width_moe(n_layers):
         band0, safe_pos = check_routing(eng, run.refresh_record, 0, run.L, K, min_safe=0.5)
         v = eng.view()
         for key in ("k", "v"):
-            g = v["kv_" + key][1, 0, :, : run.L].float().cpu().numpy().transpose(1, 0, 2)
+            g = cache_rows(v, key, 1, 0, run.L)
             o = run.cache[key][1]
             rms = np.sqrt(np.mean(o ** 2))
             excess = (np.abs(g - o) - 2e-2 * rms - 2.0 ** -8 * np.abs(o))[safe_pos]
