@@ -18,11 +18,16 @@ Also reported:
     gate|up projections of every layer), timed with HIP events on the stream it
     is launched on, over rotating layers so every launch streams its weights
     from HBM; algorithmic bytes = weights + input activations + fp32 output.
+    With more than 128 window rows (batch 16, long context) the projections
+    run the fat GEMM instead, priced in TFLOP/s against bf16 MFMA peak.
+  batch16: the same weights on the batch-16 request mix (prompts U{128..1024},
+    ragged), one warm-up and one timed generation (dense 8B workload only).
   cpu_baseline: the CPU oracle on a bounded sample (one layer's refresh and
     one layer's window step plus the LM head / vocab stats / commit of one
     step), scaled to the run's layer, refresh and step counts.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                       [--no-batch16] [--no-cpu-baseline]
 """
 from __future__ import annotations
 
@@ -37,6 +42,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
 KERNEL = "gemm_skinny_kernel<bf16, MT=4, NT=2>"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_skinny_qkv_gateup_dense8b_traffic.json")
 MODEL_NAMES = {"dense8b_b1": "dense 8B-shaped dLLM", "dense8b_b16": "dense 8B-shaped dLLM",
@@ -80,17 +86,18 @@ def dominant_kernel_timing(wc, weights, iters=40, with_events=True):
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in shapes]
     nbytes = 0
+    nflops = 0
     for W, (e0, e1) in zip(shapes, evs):
         N = W.shape[0]
         e0.record(st)
         B.linear(A, W, out)
         e1.record(st)
         nbytes += N * d * 2 + rows * d * 4 + rows * N * 4
+        nflops += 2 * rows * N * d
     torch.cuda.synchronize()
     ms = [e0.elapsed_time(e1) for e0, e1 in evs]
     avg_ms = sum(ms) / len(ms)
-    avg_bytes = nbytes / len(shapes)
-    return avg_ms, avg_bytes, rows
+    return avg_ms, nbytes / len(shapes), nflops / len(shapes), rows
 
 
 def cpu_baseline(wc, gpu_refreshes_per_run, gpu_steps_per_run, committed_per_run):
@@ -116,29 +123,91 @@ def cpu_baseline(wc, gpu_refreshes_per_run, gpu_steps_per_run, committed_per_run
     run.start_block(0)                           # one layer of the full refresh
     t_ref_layer = time.perf_counter() - t0
     lo, hi = run.window()
-    t0 = time.perf_counter()
-    e = run.window_embeddings(lo, hi)
-    h = om.forward_rows(run.cache, np.arange(lo, hi), e, run.L, run._router_bias_block())
-    t_step_layer = time.perf_counter() - t0
-    t0 = time.perf_counter()
-    logits = om.logits(h[run.bs - lo: run.be - lo])
-    st = run.stats(logits)
-    run.commit(st)
-    t_head = time.perf_counter() - t0
+    reps = 12                                    # window steps sampled (averaged)
+    t_step_layer = t_head = 0.0
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        e = run.window_embeddings(lo, hi)
+        h = om.forward_rows(run.cache, np.arange(lo, hi), e, run.L, run._router_bias_block())
+        t_step_layer += (time.perf_counter() - t0) / reps
+        t0 = time.perf_counter()
+        logits = om.logits(h[run.bs - lo: run.be - lo])
+        st = run.stats(logits)
+        run.commit(st)
+        t_head += (time.perf_counter() - t0) / reps
     nl = m.n_layers
     t_refresh = nl * t_ref_layer
     t_step = nl * t_step_layer + t_head
     t_run = gpu_refreshes_per_run * t_refresh + gpu_steps_per_run * t_step
-    sample_s = t_ref_layer + t_step_layer + t_head
+    sample_s = t_ref_layer + reps * (t_step_layer + t_head)
     return {"value": round(committed_per_run / t_run, 4), "unit": "tokens/s", "cores": int(threads),
             "kind": "oracle",
             "sample": (f"fp64 NumPy oracle: 1 of {nl} layers of the full refresh "
-                       f"({run.L} rows, {t_ref_layer:.2f} s), 1 layer of one window step "
-                       f"({hi - lo} rows, {t_step_layer:.2f} s), the LM head + vocab stats + "
-                       f"commit of one step ({t_head:.2f} s); scaled to {nl} layers, "
+                       f"({run.L} rows, {t_ref_layer:.2f} s); {reps} window steps of 1 layer "
+                       f"({hi - lo} rows, {t_step_layer:.2f} s each) with the LM head + vocab "
+                       f"stats + commit ({t_head:.2f} s each); scaled to {nl} layers, "
                        f"{gpu_refreshes_per_run} refreshes and {gpu_steps_per_run} steps per run "
                        f"({t_run:.1f} s projected; {sample_s:.1f} s measured)"),
             "step_s": round(t_step, 3), "refresh_s": round(t_refresh, 3)}
+
+
+def run_workload(wc, w, req, unroll, warmup, steps):
+    """Timed whole generations of one request batch; also the event-timed
+    latency of one denoise+commit step from graph replays of the first block."""
+    import torch
+    from diffusion_vicinity_kv_amd.engine import Engine
+    m = wc.model
+    max_len = req["tokens"].shape[1]
+    eng = Engine(m, wc.decode, w, wc.batch, max_len, graph_unroll=unroll)
+    tokens0 = req["tokens"].cuda().contiguous()
+    tokens = tokens0.clone()
+    plant_id = req["plant_id"].cuda().contiguous()
+    plant_bias = req["plant_bias"].cuda().contiguous()
+    P, G = req["prompt_len"].tolist(), req["gen_len"].tolist()
+    rb = req.get("router_bias")
+    router_bias = None if rb is None else rb.cuda().contiguous()
+
+    def bind():
+        tokens.copy_(tokens0)
+        eng.set_batch(tokens, P, G, plant_id, plant_bias, router_bias)
+
+    def one_run():
+        bind()
+        return eng.run_to_completion()
+
+    for i in range(warmup):
+        s = one_run()
+        log(f"[bench] warmup {i}: {s}")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    runs = []
+    for i in range(steps):
+        runs.append(one_run())
+        log(f"[bench] step {i}: {runs[-1]}")
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    committed = sum(r["committed"] for r in runs)
+    value = committed / elapsed
+
+    # denoise-step latency: graph replays of the first block, event-timed
+    bind()
+    eng.refresh_kv()
+    n_lat = max(unroll, (wc.decode.block_len // unroll) * unroll)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    st = torch.cuda.current_stream()
+    eng.step_graph(unroll)                     # graph captured, block warmed
+    bind()
+    eng.refresh_kv()
+    torch.cuda.synchronize()
+    e0.record(st)
+    eng.step_graph(n_lat)
+    e1.record(st)
+    torch.cuda.synchronize()
+    step_ms = e0.elapsed_time(e1) / n_lat
+
+    eng.close()
+    return {"value": value, "elapsed": elapsed / steps, "step_ms": step_ms, "runs": runs,
+            "committed": committed}
 
 
 def main():
@@ -149,6 +218,8 @@ def main():
     ap.add_argument("--workload", default="dense8b_b1")
     ap.add_argument("--unroll", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-batch16", action="store_true",
+                    help="skip the batch-16 companion figure of the dense 8B workload")
     ap.add_argument("--kernel-only", action="store_true",
                     help="only the dominant-kernel timing loop (for counter runs)")
     ap.add_argument("--calib-copy", action="store_true",
@@ -162,7 +233,6 @@ def main():
 
     import torch
     import synth
-    from diffusion_vicinity_kv_amd.engine import Engine
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -187,65 +257,47 @@ def main():
     torch.cuda.synchronize()
 
     if args.kernel_only:
-        avg_ms, avg_bytes, rows = dominant_kernel_timing(wc, w, iters=64)
+        avg_ms, avg_bytes, _, rows = dominant_kernel_timing(wc, w, iters=64)
         log(f"[bench] kernel-only: {avg_ms * 1e3:.1f} us/launch, {avg_bytes / avg_ms / 1e6:.0f} GB/s")
         return
 
-    max_len = req["tokens"].shape[1]
-    eng = Engine(m, wc.decode, w, wc.batch, max_len, graph_unroll=args.unroll)
-    tokens0 = req["tokens"].cuda().contiguous()
-    tokens = tokens0.clone()
-    plant_id = req["plant_id"].cuda().contiguous()
-    plant_bias = req["plant_bias"].cuda().contiguous()
-    P, G = req["prompt_len"].tolist(), req["gen_len"].tolist()
-    rb = req.get("router_bias")
-    router_bias = None if rb is None else rb.cuda().contiguous()
+    res = run_workload(wc, w, req, args.unroll, args.warmup, args.steps)
+    value, elapsed, step_ms = res["value"], res["elapsed"], res["step_ms"]
+    runs = res["runs"]
+    committed = res["committed"]
+    b16 = None
+    if args.workload == "dense8b_b1" and not args.no_batch16:
+        # the same weights, batch 16 (step-level batching of ragged requests)
+        wc16 = synth.preset("dense8b_b16")
+        log("[bench] batch 16 companion run (dense8b_b16 requests, same weights)")
+        r16 = run_workload(wc16, w, synth.make_requests(wc16), args.unroll, 1, 1)
+        b16 = {"workload": "dense8b_b16", "value": round(r16["value"], 3), "unit": "tokens/s",
+               "batch": wc16.batch, "ms_per_run": round(r16["elapsed"] * 1e3, 1),
+               "step_latency_ms": round(r16["step_ms"], 3),
+               "steps_per_run": r16["runs"][0]["steps"],
+               "refresh_ms_per_run": round(r16["runs"][0]["refresh_ms"], 1)}
+        torch.cuda.empty_cache()
 
-    def bind():
-        tokens.copy_(tokens0)
-        eng.set_batch(tokens, P, G, plant_id, plant_bias, router_bias)
-
-    def one_run():
-        bind()
-        return eng.run_to_completion()
-
-    for i in range(args.warmup):
-        s = one_run()
-        log(f"[bench] warmup {i}: {s}")
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    runs = []
-    for i in range(args.steps):
-        runs.append(one_run())
-        log(f"[bench] step {i}: {runs[-1]}")
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    committed = sum(r["committed"] for r in runs)
-    value = committed / elapsed
-
-    # denoise-step latency: graph replays of the first block, event-timed
-    bind()
-    eng.refresh_kv()
-    n_lat = max(args.unroll, (wc.decode.block_len // args.unroll) * args.unroll)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    st = torch.cuda.current_stream()
-    eng.step_graph(args.unroll)                     # graph captured, block warmed
-    bind()
-    eng.refresh_kv()
-    torch.cuda.synchronize()
-    e0.record(st)
-    eng.step_graph(n_lat)
-    e1.record(st)
-    torch.cuda.synchronize()
-    step_ms = e0.elapsed_time(e1) / n_lat
-
-    avg_ms, avg_bytes, rows = dominant_kernel_timing(wc, w)
-    achieved = avg_bytes / (avg_ms * 1e-3) / 1e9
-    traffic = None
-    if os.path.exists(TRAFFIC_FILE):
-        t = json.load(open(TRAFFIC_FILE))
-        if t.get("source_hash") == source_hash():
-            traffic = t.get("bytes_per_launch")
+    avg_ms, avg_bytes, avg_flops, rows = dominant_kernel_timing(wc, w)
+    if rows <= 128:
+        # skinny path: a weight stream
+        achieved = avg_bytes / (avg_ms * 1e-3) / 1e9
+        traffic = None
+        if args.workload == "dense8b_b1" and os.path.exists(TRAFFIC_FILE):
+            t = json.load(open(TRAFFIC_FILE))
+            if t.get("source_hash") == source_hash():
+                traffic = t.get("bytes_per_launch")
+        roofline = {"bound": "hbm", "kernel": KERNEL, "achieved": round(achieved, 1),
+                    "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                    "traffic": traffic, "avg_launch_us": round(avg_ms * 1e3, 2),
+                    "bytes_per_launch": int(avg_bytes)}
+    else:
+        # fat path (many window rows): a dense contraction, priced against bf16 MFMA
+        tflops = avg_flops / (avg_ms * 1e-3) / 1e12
+        roofline = {"bound": "mfma", "kernel": "gemm_fat_kernel<bf16>", "achieved": round(tflops, 1),
+                    "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                    "avg_launch_us": round(avg_ms * 1e3, 2), "flops_per_launch": int(avg_flops)}
 
     steps_per_run = sum(r["steps"] for r in runs) / len(runs)
     refreshes_per_run = sum(r["refreshes"] for r in runs) / len(runs)
@@ -274,7 +326,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(elapsed / args.steps * 1e3, 3),
+        "ms_per_step": round(elapsed * 1e3, 3),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -294,10 +346,8 @@ def main():
                           "achieved": round(step_bytes / (step_ms * 1e-3) / 1e9, 1),
                           "peak": HBM_PEAK_GBS, "unit": "GB/s",
                           "frac": round(step_bytes / (step_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
-        "roofline": {"bound": "hbm", "kernel": KERNEL, "achieved": round(achieved, 1),
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic, "avg_launch_us": round(avg_ms * 1e3, 2),
-                     "bytes_per_launch": int(avg_bytes)},
+        "roofline": roofline,
+        "batch16": b16,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
