@@ -10,7 +10,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libdinfer.so")
-SOURCES = ["gemm.hip", "rows.hip", "attention.hip", "vocab.hip", "commit.hip", "moe.hip", "runtime.hip"]
+SOURCES = ["gemm.hip", "gemm_fat.hip", "rows.hip", "attention.hip", "vocab.hip", "commit.hip", "moe.hip", "runtime.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
          # packed fp32 instructions stay off (see the build notes)

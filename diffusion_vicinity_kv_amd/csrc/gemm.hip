@@ -8,7 +8,7 @@
 // the weights' own precision only (no activation rounding), for one extra
 // MFMA per weight fragment -- free wherever the layer is a weight stream.
 //
-// Two kernels:
+// Kernels:
 //  * skinny (M <= 128): the vicinity window holds tens of rows, so a layer is
 //    a weight stream.  A workgroup of NW waves owns 16*NT*NW output columns
 //    (64 to 256) over all rows and one K slice.  Each wave streams its own
@@ -19,39 +19,15 @@
 //    weights.  K splits bring the workgroup count to about one per CU; each
 //    split writes an fp32 partial that the consumer kernel sums in split
 //    order (deterministic; the kernel boundary orders the writes).
-//  * fat (M > 128: block-start refresh, batched steps): 128x128 output tiles,
-//    64-byte K slabs of both operands double-buffered in LDS, four waves each
-//    computing 64x64 with 16x16 MFMA tiles.
+//  * fat (M > 128: block-start refresh, batched steps): gemm_fat.hip.
+// Also the grouped projection of the MoE experts, and the plans.
 #include "common.h"
+#include "gemm_split.h"
 #include "kernels.h"
 
 namespace dinfer {
 
 namespace {
-
-template <typename TW> struct ASplit;
-// bf16 weights: two LDS planes (hi, lo) of bf16 activations.
-template <> struct ASplit<bf16> {
-  static constexpr int PLANES = 2;
-  __device__ __forceinline__ static void store4(bf16* hi, bf16* lo, const float4& x) {
-    const float v[4] = {x.x, x.y, x.z, x.w};
-    bf16x4 h, l;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      h[i] = static_cast<bf16>(v[i]);
-      l[i] = static_cast<bf16>(v[i] - static_cast<float>(h[i]));
-    }
-    *reinterpret_cast<bf16x4*>(hi) = h;
-    *reinterpret_cast<bf16x4*>(lo) = l;
-  }
-};
-// fp32 weights: one plane of fp32 activations.
-template <> struct ASplit<float> {
-  static constexpr int PLANES = 1;
-  __device__ __forceinline__ static void store4(float* p, float*, const float4& x) {
-    *reinterpret_cast<float4*>(p) = x;
-  }
-};
 
 // ---------------------------------------------------------------------------
 // GUARD = false: A has at least 16*MT readable rows (rows >= M hold anything
@@ -258,117 +234,6 @@ __global__ __launch_bounds__(NW * 64) void gemm_grouped_kernel(
 
 
 // ---------------------------------------------------------------------------
-template <typename TW>
-__global__ __launch_bounds__(256) void gemm_fat_kernel(const float* __restrict__ A,
-                                                       const TW* __restrict__ W,
-                                                       float* __restrict__ Cout,
-                                                       const int* __restrict__ m_dev, int m_cap,
-                                                       int N, int K) {
-  using MF = Mfma<TW>;
-  using AS = ASplit<TW>;
-  constexpr int PL = AS::PLANES;
-  constexpr int VEC = MF::VEC;
-  constexpr int KSTEP = MF::KSTEP;
-  constexpr int BK = KSTEP;                    // one vector step (64 bytes of W) per slab
-  constexpr int STR = BK + 16 / sizeof(TW);
-  constexpr int F4R = BK / 4;                  // float4 of A per slab row
-  constexpr int AV = 128 * F4R / 256;          // float4 of A per thread per slab
-  constexpr int WVR = BK / VEC;                // 16-byte W vectors per slab row (4)
-  constexpr int BV = 128 * WVR / 256;          // W vectors per thread per slab (2)
-  __shared__ __attribute__((aligned(16))) TW As[2][PL][128 * STR];
-  __shared__ __attribute__((aligned(16))) TW Bs[2][128 * STR];
-
-  const int M = m_dev ? min(*m_dev, m_cap) : m_cap;
-  const int m0 = blockIdx.y * 128;
-  const int n0 = blockIdx.x * 128;
-  if (m0 >= M) return;
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int lc = lane & 15;
-  const int lg = lane >> 4;
-  const int wm = wave >> 1;
-  const int wn = wave & 1;
-
-  floatx4 acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
-
-  float4 ra[AV];
-  V16 rb[BV];
-  auto gload = [&](int kt) {
-#pragma unroll
-    for (int i = 0; i < AV; ++i) {
-      const int v = threadIdx.x + 256 * i;
-      const int r = v / F4R;
-      const int cv = v % F4R;
-      ra[i] = (m0 + r < M)
-                  ? *reinterpret_cast<const float4*>(A + (size_t)(m0 + r) * K + kt * BK + cv * 4)
-                  : make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-#pragma unroll
-    for (int i = 0; i < BV; ++i) {
-      const int v = threadIdx.x + 256 * i;
-      const int r = v / WVR;
-      const int cv = v % WVR;
-      rb[i] = (n0 + r < N) ? ld16(W + (size_t)(n0 + r) * K + kt * BK + cv * VEC) : zero16();
-    }
-  };
-  auto sstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < AV; ++i) {
-      const int v = threadIdx.x + 256 * i;
-      const int r = v / F4R;
-      const int cv = v % F4R;
-      AS::store4(&As[buf][0][r * STR + cv * 4], &As[buf][PL - 1][r * STR + cv * 4], ra[i]);
-    }
-#pragma unroll
-    for (int i = 0; i < BV; ++i) {
-      const int v = threadIdx.x + 256 * i;
-      const int r = v / WVR;
-      const int cv = v % WVR;
-      st16(&Bs[buf][r * STR + cv * VEC], rb[i]);
-    }
-  };
-
-  const int nk = K / BK;
-  gload(0);
-  sstore(0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) gload(kt + 1);
-    V16 b[4];
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt)
-      b[nt] = *reinterpret_cast<const V16*>(&Bs[cur][(wn * 64 + nt * 16 + lc) * STR + lg * VEC]);
-#pragma unroll
-    for (int p = 0; p < PL; ++p) {
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        const V16 a = *reinterpret_cast<const V16*>(
-            &As[cur][p][(wm * 64 + mt * 16 + lc) * STR + lg * VEC]);
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt) MF::mac(acc[mt][nt], a, b[nt]);
-      }
-    }
-    if (kt + 1 < nk) sstore(cur ^ 1);
-    __syncthreads();
-  }
-
-#pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = m0 + wm * 64 + mt * 16 + lg * 4 + i;
-        const int col = n0 + wn * 64 + nt * 16 + lc;
-        if (row < M && col < N) Cout[(size_t)row * N + col] = acc[mt][nt][i];
-      }
-}
-
 template <typename TW, int MT, int NT, int NW>
 hipError_t run_skinny(const GemmPlan& p, const float* A, const void* W, float* out,
                       const int* m_dev, int m_cap, int N, int K, hipStream_t st) {
@@ -410,12 +275,9 @@ hipError_t dispatch_mt(const GemmPlan& p, const float* A, const void* W, float* 
 template <typename TW>
 hipError_t dispatch(const GemmPlan& p, const float* A, const void* W, float* out,
                     const int* m_dev, int m_cap, int N, int K, hipStream_t st) {
-  if (p.kind == 1) {
-    dim3 grid((N + 127) / 128, (m_cap + 127) / 128);
-    hipLaunchKernelGGL((gemm_fat_kernel<TW>), grid, dim3(256), 0, st, A,
-                       static_cast<const TW*>(W), out, m_dev, m_cap, N, K);
-    return hipGetLastError();
-  }
+  if (p.kind == 1)
+    return launch_gemm_fat(sizeof(TW) == 2 ? DType::BF16 : DType::F32, p.nw, A, W, out, m_dev,
+                           m_cap, N, K, st);
   if constexpr (sizeof(TW) == 2) {   // 8-wave groups: bf16 weights only
     if (p.nw == 8) return dispatch_mt<TW, 2, 8>(p, A, W, out, m_dev, m_cap, N, K, st);
   }
@@ -454,9 +316,11 @@ GemmPlan plan_gemm(DType t, int m_cap, int N, int K, int target_wgs) {
   GemmPlan p{};
   if (m_cap > 128) {
     p.kind = 1;
-    p.mt = p.nt = p.nw = 0;
+    p.mt = p.nt = 0;
     p.splits = 1;
-    p.grid = ((N + 127) / 128) * ((m_cap + 127) / 128);
+    const int mtiles = (m_cap + 127) / 128;
+    p.nw = ((N + 255) / 256) * mtiles >= target_wgs ? 4 : 2;
+    p.grid = ((N + 64 * p.nw - 1) / (64 * p.nw)) * mtiles;
     return p;
   }
   p.kind = 0;

@@ -1,0 +1,174 @@
+// Dense projections with many rows (block-start refresh, batched steps) on
+// gfx950 MFMA: out = A * W^T, A [M][K] fp32 activations, W [N][K] weights
+// (fp32 or bf16), fp32 accumulation, no K split.
+#include "common.h"
+#include "gemm_split.h"
+#include "kernels.h"
+
+namespace dinfer {
+
+namespace {
+
+// Fat kernel: 128 x 64*WN output tile per workgroup of 2 x WN waves (each
+// 64 x 64 as 4 x 4 MFMA tiles; WN = 4: two waves per SIMD, used when the grid
+// still has a workgroup per CU, else WN = 2), K slabs of BK = 64 (bf16)
+// / 32 (fp32) elements double-buffered in LDS with the activations split into
+// hi/lo planes on the way in.  Global loads run two slabs ahead through three
+// register sets (a three-times unrolled loop, as in the skinny kernel), all
+// unconditional: rows past M read row M-1 and columns past N read column
+// N-1 (their outputs are not stored).
+constexpr int kFatM = 128;
+
+template <typename TW, int WN>
+__global__ __launch_bounds__(128 * WN) void gemm_fat_kernel(const float* __restrict__ A,
+                                                            const TW* __restrict__ W,
+                                                            float* __restrict__ Cout,
+                                                            const int* __restrict__ m_dev,
+                                                            int m_cap, int N, int K) {
+  constexpr int kFatN = 64 * WN, kFatThreads = 128 * WN;
+  using MF = Mfma<TW>;
+  using AS = ASplit<TW>;
+  constexpr int PL = AS::PLANES;
+  constexpr int VEC = MF::VEC;
+  constexpr int KSTEP = MF::KSTEP;
+  constexpr int KK = 2;                        // vector steps per slab
+  constexpr int BK = KK * KSTEP;               // 64 (bf16) / 32 (fp32) elements
+  constexpr int STR = BK + 16 / sizeof(TW);    // LDS row stride (+16 B)
+  constexpr int F4R = BK / 4;                  // float4 of A per slab row
+  constexpr int AV = kFatM * F4R / kFatThreads;     // float4 of A per thread per slab
+  constexpr int WVR = BK / VEC;                // 16-byte W vectors per slab row
+  constexpr int BV = kFatN * WVR / kFatThreads;     // W vectors per thread per slab
+  __shared__ __attribute__((aligned(16))) TW As[2][PL][kFatM * STR];
+  __shared__ __attribute__((aligned(16))) TW Bs[2][kFatN * STR];
+
+  const int M = m_dev ? min(*m_dev, m_cap) : m_cap;
+  const int m0 = blockIdx.y * kFatM;
+  const int n0 = blockIdx.x * kFatN;
+  if (m0 >= M) return;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int lc = lane & 15;
+  const int lg = lane >> 4;
+  const int wm = wave / WN;                    // 2 row halves
+  const int wn = wave % WN;                    // WN column groups
+  const int nk = K / BK;
+
+  floatx4 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  // row offsets of this thread's slab elements (fixed over K)
+  const float* arow[AV];
+#pragma unroll
+  for (int i = 0; i < AV; ++i) {
+    const int v = threadIdx.x + kFatThreads * i;
+    arow[i] = A + (size_t)min(m0 + v / F4R, M - 1) * K + (v % F4R) * 4;
+  }
+  const TW* wrow[BV];
+#pragma unroll
+  for (int i = 0; i < BV; ++i) {
+    const int v = threadIdx.x + kFatThreads * i;
+    wrow[i] = W + (size_t)min(n0 + v / WVR, N - 1) * K + (v % WVR) * VEC;
+  }
+  auto gload = [&](float4 (&ra)[AV], V16 (&rb)[BV], int kt) {
+    kt = min(kt, nk - 1);   // past the end: repeat the last slab
+#pragma unroll
+    for (int i = 0; i < AV; ++i) ra[i] = *reinterpret_cast<const float4*>(arow[i] + kt * BK);
+#pragma unroll
+    for (int i = 0; i < BV; ++i) rb[i] = ld16(wrow[i] + kt * BK);
+  };
+  auto sstore = [&](const float4 (&ra)[AV], const V16 (&rb)[BV], int buf) {
+#pragma unroll
+    for (int i = 0; i < AV; ++i) {
+      const int v = threadIdx.x + kFatThreads * i;
+      const int r = v / F4R;
+      const int cv = v % F4R;
+      AS::store4(&As[buf][0][r * STR + cv * 4], &As[buf][PL - 1][r * STR + cv * 4], ra[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < BV; ++i) {
+      const int v = threadIdx.x + kFatThreads * i;
+      const int r = v / WVR;
+      const int cv = v % WVR;
+      st16(&Bs[buf][r * STR + cv * VEC], rb[i]);
+    }
+  };
+  auto mma = [&](int buf) {
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      V16 b[4];
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt)
+        b[nt] = *reinterpret_cast<const V16*>(
+            &Bs[buf][(wn * 64 + nt * 16 + lc) * STR + kk * KSTEP + lg * VEC]);
+#pragma unroll
+      for (int p = 0; p < PL; ++p) {
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+          const V16 a = *reinterpret_cast<const V16*>(
+              &As[buf][p][(wm * 64 + mt * 16 + lc) * STR + kk * KSTEP + lg * VEC]);
+#pragma unroll
+          for (int nt = 0; nt < 4; ++nt) MF::mac(acc[mt][nt], a, b[nt]);
+        }
+      }
+    }
+  };
+  // slab kt: issue the loads of kt+2, multiply slab kt from LDS, stage the
+  // registers of kt+1 into the other buffer, barrier
+  float4 a0[AV], a1[AV], a2[AV];
+  V16 b0[BV], b1[BV], b2[BV];
+  auto step = [&](int kt, float4 (&an)[AV], V16 (&bn)[BV], float4 (&al)[AV], V16 (&bl)[BV]) {
+    gload(al, bl, kt + 2);
+    mma(kt & 1);
+    sstore(an, bn, (kt + 1) & 1);
+    __syncthreads();
+  };
+  gload(a0, b0, 0);
+  gload(a1, b1, 1);
+  sstore(a0, b0, 0);
+  __syncthreads();
+  for (int kt = 0; kt < nk; kt += 3) {
+    step(kt, a1, b1, a2, b2);
+    if (kt + 1 < nk) step(kt + 1, a2, b2, a0, b0);
+    if (kt + 2 < nk) step(kt + 2, a0, b0, a1, b1);
+  }
+
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = m0 + wm * 64 + mt * 16 + lg * 4 + i;
+        const int col = n0 + wn * 64 + nt * 16 + lc;
+        if (row < M && col < N) Cout[(size_t)row * N + col] = acc[mt][nt][i];
+      }
+}
+
+}  // namespace
+
+hipError_t launch_gemm_fat(DType t, int wn, const float* A, const void* W, float* out,
+                           const int* m_dev, int m_cap, int N, int K, hipStream_t st) {
+  if (wn != 2 && wn != 4) return hipErrorInvalidValue;
+  const dim3 grid((N + 64 * wn - 1) / (64 * wn), (m_cap + kFatM - 1) / kFatM);
+  if (t == DType::F32) {
+    if (wn == 4)
+      hipLaunchKernelGGL((gemm_fat_kernel<float, 4>), grid, dim3(512), 0, st, A,
+                         static_cast<const float*>(W), out, m_dev, m_cap, N, K);
+    else
+      hipLaunchKernelGGL((gemm_fat_kernel<float, 2>), grid, dim3(256), 0, st, A,
+                         static_cast<const float*>(W), out, m_dev, m_cap, N, K);
+  } else {
+    if (wn == 4)
+      hipLaunchKernelGGL((gemm_fat_kernel<bf16, 4>), grid, dim3(512), 0, st, A,
+                         static_cast<const bf16*>(W), out, m_dev, m_cap, N, K);
+    else
+      hipLaunchKernelGGL((gemm_fat_kernel<bf16, 2>), grid, dim3(256), 0, st, A,
+                         static_cast<const bf16*>(W), out, m_dev, m_cap, N, K);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace dinfer

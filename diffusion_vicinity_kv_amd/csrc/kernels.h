@@ -31,7 +31,7 @@ struct PassTable {
 struct GemmPlan {
   int kind;      // 0 = skinny (rows <= 128), 1 = fat
   int mt, nt;    // skinny: 16-row tiles; 16-column tiles per wave
-  int nw;        // skinny: waves per workgroup
+  int nw;        // skinny: waves per workgroup; fat: column waves (2 or 4)
   int guard;     // skinny: 1 = A has exactly m_cap rows; 0 = A readable up to 16*mt rows
   int splits;    // K splits (skinny only; fat = 1)
   int grid;
@@ -40,6 +40,9 @@ GemmPlan plan_gemm(DType t, int m_cap, int N, int K, int target_wgs);
 // A is fp32 (split into hi/lo bf16 halves in-kernel for bf16 weights).
 hipError_t launch_gemm(const GemmPlan& p, DType t, const float* A, const void* W, float* out,
                        const int* m_dev, int m_cap, int N, int K, hipStream_t st);
+// The fat kernel alone (M > 128): wn = 2 or 4 column waves (128 x 64*wn tiles).
+hipError_t launch_gemm_fat(DType t, int wn, const float* A, const void* W, float* out,
+                           const int* m_dev, int m_cap, int N, int K, hipStream_t st);
 bool gemm_shape_ok(DType t, int N, int K);
 int gemm_k_chunk(DType t);
 // MoE experts: out[off_e + i] = A[row_of ? row_of[off_e + i] : off_e + i] * W[e]^T for

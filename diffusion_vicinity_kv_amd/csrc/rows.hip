@@ -123,9 +123,10 @@ __global__ __launch_bounds__(kNormThreads) void add_rmsnorm_kernel(
 // "削减计算成本：邻近KV缓存刷新": only the window's KV is recomputed).
 // K goes to [request][head][Lp][hd]; V to transposed tiles of 32 positions,
 // [request][head][Lp/32][hd][32], through an LDS tile, so that consecutive
-// threads store consecutive positions.  A workgroup takes 16 rows of one head.
-constexpr int kQkvRows = 16;
-constexpr int kQkvThreads = 256;
+// threads store consecutive positions.  A workgroup takes 8 rows of one head
+// (16 threads per row), so a 64-row window still spreads over 256 workgroups.
+constexpr int kQkvRows = 8;
+constexpr int kQkvThreads = 128;
 
 template <typename T>
 __global__ __launch_bounds__(kQkvThreads) void qkv_rope_scatter_kernel(
