@@ -23,7 +23,13 @@ namespace {
 constexpr int kMaxE = 64;
 constexpr int kMaxTopK = 8;
 
-// One workgroup (256 threads) per row.
+// One workgroup per row.  Each of its four waves takes a quarter of d, lane e
+// accumulating expert e's partial dot product (the row read as wave-uniform
+// float4s, the router row as 16-byte vectors, eight vectors in flight); the
+// quarters are added in order through LDS, then wave 0 picks the top_k by
+// repeated wave argmax.
+constexpr int kRouteUnroll = 8;
+
 template <typename T>
 __global__ __launch_bounds__(256) void moe_route_kernel(PassTable tb, int m_cap,
                                                         const float* __restrict__ f, int d,
@@ -33,28 +39,36 @@ __global__ __launch_bounds__(256) void moe_route_kernel(PassTable tb, int m_cap,
                                                         int* __restrict__ sel,
                                                         float* __restrict__ gate,
                                                         float* __restrict__ rlog) {
-  __shared__ float logit[kMaxE];
-  const int m = blockIdx.x;
-  if (m >= min(*tb.nrows, m_cap)) return;
+  constexpr int VEC = 16 / sizeof(T);          // weights per 16-byte load
+  __shared__ float part[4][kMaxE];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const float* fr = f + (size_t)m * d;
-  for (int e = wave; e < E; e += 4) {
-    const T* w = Wr + (size_t)e * d;
-    float s = 0.f;
-    for (int k = lane * 4; k < d; k += 256) {
-      const float4 x = *reinterpret_cast<const float4*>(fr + k);
-      s += x.x * to_f(w[k]) + x.y * to_f(w[k + 1]) + x.z * to_f(w[k + 2]) + x.w * to_f(w[k + 3]);
-    }
-    s = wave_sum(s);
-    if (lane == 0) logit[e] = s;
+  const int m = blockIdx.x;
+  if (m >= min(*tb.nrows, m_cap)) return;
+  const int dq = d / 4;                        // this wave's quarter of d
+  const float* fr = f + (size_t)m * d + wave * dq;
+  const T* w = Wr + (size_t)min(lane, E - 1) * d + wave * dq;
+  float s = 0.f;
+  for (int k0 = 0; k0 < dq; k0 += kRouteUnroll * VEC) {
+    V16 wv[kRouteUnroll];
+#pragma unroll
+    for (int u = 0; u < kRouteUnroll; ++u) wv[u] = ld16(w + k0 + u * VEC);
+#pragma unroll
+    for (int u = 0; u < kRouteUnroll; ++u)
+#pragma unroll
+      for (int e = 0; e < VEC; e += 4) {
+        const float4 x = *reinterpret_cast<const float4*>(fr + k0 + u * VEC + e);
+        s += x.x * v16_get<T>(wv[u], e) + x.y * v16_get<T>(wv[u], e + 1) +
+             x.z * v16_get<T>(wv[u], e + 2) + x.w * v16_get<T>(wv[u], e + 3);
+      }
   }
+  part[wave][lane] = s;
   __syncthreads();
   if (wave != 0) return;
   const int r = tb.row_req[m];
   float v = -INFINITY;
   if (lane < E) {
-    v = logit[lane];
+    v = ((part[0][lane] + part[1][lane]) + part[2][lane]) + part[3][lane];
     if (router_bias)
       v += router_bias[(((size_t)r * n_layers + layer) * n_blocks + tb.req_blk[r]) * E + lane];
     rlog[(size_t)m * E + lane] = v;
@@ -94,94 +108,101 @@ __global__ __launch_bounds__(256) void moe_route_kernel(PassTable tb, int m_cap,
     }
 }
 
-// One workgroup of E*G threads: thread (e, g) owns expert e over the g-th
-// range of assignments.  Counts per (e, g), an exclusive scan in (e, g)
-// order, then positions: assignments of an expert appear in row order.
-constexpr int kPlanGroups = 16;
+// One workgroup of 16 waves; wave w owns experts w, w+16, w+32, w+48.  The
+// assignment list (row-major [row][slot]) is staged in LDS when it fits.  An
+// expert's assignments are found 64 at a time by ballot; a first pass counts
+// them, an exclusive scan over experts gives the offsets, and a second pass
+// writes each assignment's packed position (its rank among the expert's
+// matches in list order, i.e. row order) -- deterministic.
+constexpr int kPlanWaves = 16;
+constexpr int kPlanLds = 16384;    // assignments staged in LDS (larger lists read global memory)
 
-__global__ __launch_bounds__(kMaxE * kPlanGroups) void moe_plan_kernel(
-    const int* __restrict__ nrows, int m_cap, const int* __restrict__ sel, int E, int top_k,
+__global__ __launch_bounds__(64 * kPlanWaves) void moe_plan_kernel(
+    const int* __restrict__ nrows, int m_cap, const int* __restrict__ sel_g, int E, int top_k,
     int* __restrict__ e_count, int* __restrict__ e_off, int* __restrict__ row_of,
     int* __restrict__ pos, int* __restrict__ n_assign) {
-  __shared__ int cnt[kMaxE * kPlanGroups];
+  __shared__ int sel_s[kPlanLds];
+  __shared__ int cnt[kMaxE];
+  __shared__ int off[kMaxE + 1];
   const int t = threadIdx.x;
-  const int e = t / kPlanGroups;
-  const int g = t % kPlanGroups;
-  const int M = min(*nrows, m_cap);
-  const int total = M * top_k;
-  const int a0 = (int)((long long)total * g / kPlanGroups);
-  const int a1 = (int)((long long)total * (g + 1) / kPlanGroups);
-  int c = 0;
-  if (e < E)
-    for (int a = a0; a < a1; ++a) c += (sel[a] == e);
-  // exclusive scan of the counts in thread order (= (expert, group) order)
-  __shared__ int wsum[kMaxE * kPlanGroups / 64];
   const int lane = t & 63;
   const int wave = t >> 6;
-  int incl = c;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(incl, o, 64);
-    if (lane >= o) incl += y;
+  const int M = min(*nrows, m_cap);
+  const int total = M * top_k;
+  const bool staged = total <= kPlanLds;
+  if (staged)
+    for (int a = t; a < total; a += 64 * kPlanWaves) sel_s[a] = sel_g[a];
+  __syncthreads();
+  const int* sel = staged ? sel_s : sel_g;
+  const unsigned long long below = (1ull << lane) - 1ull;
+  for (int e = wave; e < E; e += kPlanWaves) {
+    int c = 0;
+    for (int a0 = 0; a0 < total; a0 += 64) {
+      const int a = a0 + lane;
+      c += __popcll(__ballot(a < total && sel[a] == e));
+    }
+    if (lane == 0) cnt[e] = c;
   }
-  if (lane == 63) wsum[wave] = incl;
   __syncthreads();
   if (t == 0) {
     int run = 0;
-    for (int w = 0; w < kMaxE * kPlanGroups / 64; ++w) {
-      const int x = wsum[w];
-      wsum[w] = run;
-      run += x;
+    for (int e = 0; e < E; ++e) {
+      off[e] = run;
+      run += cnt[e];
     }
+    off[E] = run;
     *n_assign = run;
   }
   __syncthreads();
-  cnt[t] = wsum[wave] + incl - c;
-  __syncthreads();
-  if (e < E) {
-    int p = cnt[t];
-    if (g == 0) {
-      e_off[e] = p;
-      const int next = (e + 1 < E) ? cnt[(e + 1) * kPlanGroups] : *n_assign;
-      e_count[e] = next - p;
+  for (int e = wave; e < E; e += kPlanWaves) {
+    if (lane == 0) {
+      e_off[e] = off[e];
+      e_count[e] = cnt[e];
     }
-    for (int a = a0; a < a1; ++a)
-      if (sel[a] == e) {
-        row_of[p] = a / top_k;
-        pos[a] = p;
-        ++p;
+    int p = off[e];
+    for (int a0 = 0; a0 < total; a0 += 64) {
+      const int a = a0 + lane;
+      const bool hit = a < total && sel[a] == e;
+      const unsigned long long mask = __ballot(hit);
+      if (hit) {
+        const int q = p + __popcll(mask & below);
+        row_of[q] = a / top_k;
+        pos[a] = q;
       }
+      p += __popcll(mask);
+    }
   }
 }
 
-// x[m] += sum_s P[s][m] + sum_k gate[m][k] * Y[pos[m][k]]  (float4 per thread)
+// x[m] += sum_s P[s][m] + sum_k gate[m][k] * Y[pos[m][k]]: one float4 of one
+// row per thread, partials in split order, experts in slot order.
 __global__ __launch_bounds__(256) void moe_combine_kernel(
     const int* __restrict__ nrows, int m_cap, float* __restrict__ x, const float* __restrict__ P,
     int S, size_t p_stride, const float* __restrict__ Y, const int* __restrict__ pos,
     const float* __restrict__ gate, int top_k, int d) {
-  const int m = blockIdx.x;
-  if (m >= min(*nrows, m_cap)) return;
   const int d4 = d / 4;
-  for (int i = threadIdx.x; i < d4; i += 256) {
-    float4 acc = reinterpret_cast<float4*>(x + (size_t)m * d)[i];
-    for (int s = 0; s < S; ++s) {
-      const float4 v = *reinterpret_cast<const float4*>(P + s * p_stride + (size_t)m * d + 4 * i);
-      acc.x += v.x;
-      acc.y += v.y;
-      acc.z += v.z;
-      acc.w += v.w;
-    }
-    for (int k = 0; k < top_k; ++k) {
-      const float gk = gate[(size_t)m * top_k + k];
-      const float4 v =
-          *reinterpret_cast<const float4*>(Y + (size_t)pos[(size_t)m * top_k + k] * d + 4 * i);
-      acc.x += gk * v.x;
-      acc.y += gk * v.y;
-      acc.z += gk * v.z;
-      acc.w += gk * v.w;
-    }
-    reinterpret_cast<float4*>(x + (size_t)m * d)[i] = acc;
+  const int idx = blockIdx.x * 256 + threadIdx.x;
+  const int m = idx / d4;
+  const int i = idx % d4;
+  if (m >= min(*nrows, m_cap)) return;
+  float4 acc = reinterpret_cast<float4*>(x + (size_t)m * d)[i];
+  for (int s = 0; s < S; ++s) {
+    const float4 v = *reinterpret_cast<const float4*>(P + s * p_stride + (size_t)m * d + 4 * i);
+    acc.x += v.x;
+    acc.y += v.y;
+    acc.z += v.z;
+    acc.w += v.w;
   }
+  for (int k = 0; k < top_k; ++k) {
+    const float gk = gate[(size_t)m * top_k + k];
+    const float4 v =
+        *reinterpret_cast<const float4*>(Y + (size_t)pos[(size_t)m * top_k + k] * d + 4 * i);
+    acc.x += gk * v.x;
+    acc.y += gk * v.y;
+    acc.z += gk * v.z;
+    acc.w += gk * v.w;
+  }
+  reinterpret_cast<float4*>(x + (size_t)m * d)[i] = acc;
 }
 
 }  // namespace
@@ -190,13 +211,15 @@ hipError_t launch_moe_route(DType t, PassTable tb, int m_cap, const float* f, in
                             const void* Wr, int E, int top_k, const float* router_bias,
                             int n_layers, int n_blocks, int layer, int* sel, float* gate,
                             float* rlog, hipStream_t st) {
-  if (E > kMaxE || top_k > kMaxTopK || top_k > E || d % 4 != 0) return hipErrorInvalidValue;
+  if (E > kMaxE || top_k > kMaxTopK || top_k > E || d % (4 * kRouteUnroll * 8) != 0)
+    return hipErrorInvalidValue;
+  const dim3 grid(m_cap);
   if (t == DType::F32)
-    hipLaunchKernelGGL(moe_route_kernel<float>, dim3(m_cap), dim3(256), 0, st, tb, m_cap, f, d,
+    hipLaunchKernelGGL(moe_route_kernel<float>, grid, dim3(256), 0, st, tb, m_cap, f, d,
                        static_cast<const float*>(Wr), E, top_k, router_bias, n_layers, n_blocks,
                        layer, sel, gate, rlog);
   else
-    hipLaunchKernelGGL(moe_route_kernel<bf16>, dim3(m_cap), dim3(256), 0, st, tb, m_cap, f, d,
+    hipLaunchKernelGGL(moe_route_kernel<bf16>, grid, dim3(256), 0, st, tb, m_cap, f, d,
                        static_cast<const bf16*>(Wr), E, top_k, router_bias, n_layers, n_blocks,
                        layer, sel, gate, rlog);
   return hipGetLastError();
@@ -206,7 +229,7 @@ hipError_t launch_moe_plan(const int* nrows, int m_cap, const int* sel, int E, i
                            int* e_count, int* e_off, int* row_of, int* pos, int* n_assign,
                            hipStream_t st) {
   if (E > kMaxE) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(moe_plan_kernel, dim3(1), dim3(kMaxE * kPlanGroups), 0, st, nrows, m_cap, sel,
+  hipLaunchKernelGGL(moe_plan_kernel, dim3(1), dim3(64 * kPlanWaves), 0, st, nrows, m_cap, sel,
                      E, top_k, e_count, e_off, row_of, pos, n_assign);
   return hipGetLastError();
 }
@@ -215,7 +238,8 @@ hipError_t launch_moe_combine(const int* nrows, int m_cap, float* x, const float
                               size_t p_stride, const float* Y, const int* pos, const float* gate,
                               int top_k, int d, hipStream_t st) {
   if (d % 4 != 0) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(moe_combine_kernel, dim3(m_cap), dim3(256), 0, st, nrows, m_cap, x, P, S,
+  const int blocks = (int)(((size_t)m_cap * (d / 4) + 255) / 256);
+  hipLaunchKernelGGL(moe_combine_kernel, dim3(blocks), dim3(256), 0, st, nrows, m_cap, x, P, S,
                      p_stride, Y, pos, gate, top_k, d);
   return hipGetLastError();
 }
