@@ -9,13 +9,13 @@
 // contiguous; Lp = max_len rounded up to 64.  Every MFMA operand of both
 // products is then a 16-byte piece of memory in its fragment layout.
 //
-// A workgroup takes (request, head, block of 64 * QTW queries, key range);
-// each of its four waves owns QTW tiles of 16 queries.  Per step of KS keys
-// (32 for bf16, 16 for fp32) the step's K and V fragments (NF kilobytes) are
-// loaded once for the workgroup -- a quarter by each wave, two steps ahead,
-// through registers -- and stored to LDS in fragment order, so that every
-// wave reads each fragment as one contiguous, conflict-free 16-byte-per-lane
-// load.  Then:
+// A workgroup takes (request, head, block of 64 * QTW queries, key range) on
+// two groups of four waves; each wave owns QTW tiles of 16 queries, and the
+// groups take alternate steps of KS keys (32 for bf16, 16 for fp32) and merge
+// at the end.  A step's K and V fragments (NF kilobytes) are loaded once for
+// the group -- a quarter by each wave, two steps ahead, through registers --
+// and stored to LDS in fragment order, so that every wave reads each fragment
+// as one contiguous, conflict-free 16-byte-per-lane load.  Then:
 //   S^T = K Q^T with the keys as MFMA rows.  For bf16 the two 16-key tiles
 //   take their rows in the order key(t, j) = 8*(j/4) + 4t + j%4, so lane
 //   (query c, group g) ends up holding the scores of keys 8g..8g+7;
@@ -38,9 +38,10 @@ namespace dinfer {
 namespace {
 
 constexpr float kSlack = 8.f;
+constexpr int kKeyGroups = 2;   // groups of four waves taking alternate steps
 
 template <typename T, int HD, int QTW>
-__global__ __launch_bounds__(256) void attn_kernel(
+__global__ __launch_bounds__(256 * kKeyGroups) void attn_kernel(
     PassTable tb, int q_blocks, int keys_per_split, int n_split, int m_cap,
     const float* __restrict__ q, const T* __restrict__ kc, const T* __restrict__ vt, int H,
     int Lp, float scale_log2, float* __restrict__ o_part, float* __restrict__ ml_part,
@@ -57,8 +58,9 @@ __global__ __launch_bounds__(256) void attn_kernel(
   constexpr int NK = NTS * QV;         // K fragments per step
   constexpr int NF = NK + HT;          // K and V fragments per step
   constexpr int FW = NF / 4;           // fragments each wave loads
+  constexpr int KG = kKeyGroups;
   static_assert(NF % 4 == 0, "fragments must split over four waves");
-  __shared__ V16 frag[2][NF][64];
+  __shared__ V16 frag[KG][2][NF][64];
 
   const int split = blockIdx.x;
   const int h = blockIdx.y;
@@ -73,10 +75,12 @@ __global__ __launch_bounds__(256) void attn_kernel(
   const int n_steps = (k1 - k0 + KS - 1) / KS;
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int kg = threadIdx.x >> 8;             // key group: steps kg, kg + KG, ...
+  const int wave = (threadIdx.x >> 6) & 3;     // query tile(s) within the block
   const int lc = lane & 15;
   const int lg = lane >> 4;
   const int d = H * HD;
+  const int n_local = (n_steps + KG - 1) / KG; // steps per group (the last may be empty)
 
   // query fragments (B operand of S^T): query lc of each tile, hd g*VEC..
   V16 qf[QTW][QV][PL];
@@ -122,8 +126,8 @@ __global__ __launch_bounds__(256) void attn_kernel(
 
   // fragment f of a step, as lane `lane` holds it: f < NK is K tile t = f /
   // QV, head-dim step kk = f % QV; the rest are V^T row tiles ht = f - NK
-  auto load = [&](V16 (&reg)[FW], int s) {
-    const int kb = k0 + min(s, n_steps - 1) * KS;   // past the end: repeat the last step
+  auto load = [&](V16 (&reg)[FW], int i) {     // this group's local step i
+    const int kb = k0 + min(kg + i * KG, n_steps - 1) * KS;   // past the end: repeat the last
 #pragma unroll
     for (int i = 0; i < FW; ++i) {
       const int f = wave * FW + i;
@@ -137,14 +141,16 @@ __global__ __launch_bounds__(256) void attn_kernel(
   };
   auto store = [&](const V16 (&reg)[FW], int buf) {
 #pragma unroll
-    for (int i = 0; i < FW; ++i) frag[buf][wave * FW + i][lane] = reg[i];
+    for (int i = 0; i < FW; ++i) frag[kg][buf][wave * FW + i][lane] = reg[i];
   };
 
-  auto compute = [&](int buf, int s) {
+  auto compute = [&](int buf, int i) {
+    const int s = kg + i * KG;
+    if (s >= n_steps) return;                  // this group's slot past the range
     const int kb = k0 + s * KS;
     V16 kf[NK];
 #pragma unroll
-    for (int f = 0; f < NK; ++f) kf[f] = frag[buf][f][lane];
+    for (int f = 0; f < NK; ++f) kf[f] = frag[kg][buf][f][lane];
 #pragma unroll
     for (int u = 0; u < QTW; ++u) {
       floatx4 sc[NTS];
@@ -189,34 +195,35 @@ __global__ __launch_bounds__(256) void attn_kernel(
       SO::make(pv, pf);
 #pragma unroll
       for (int ht = 0; ht < HT; ++ht) {
-        const V16 vf = frag[buf][NK + ht][lane];
+        const V16 vf = frag[kg][buf][NK + ht][lane];
 #pragma unroll
         for (int p = 0; p < PL; ++p) MF::mac(o[u][ht], vf, pf[p]);
       }
     }
   };
 
-  // Registers hold the loads of the next two steps; at step s the loads of
-  // s+2 are issued, step s is computed from LDS, the registers of s+1 are
-  // stored to the other LDS buffer, and a barrier ends the step.  Three
-  // register sets rotate through a three-times unrolled loop (a copy would
-  // wait for the loads just issued); every step loads (clamped), so the
-  // waits stay two steps deep on every path.
+  // Per group, registers hold the loads of its next two steps; at local step
+  // i the loads of i+2 are issued, step i is computed from LDS, the
+  // registers of i+1 are stored to the group's other LDS buffer, and a
+  // barrier (shared by the groups, which advance together) ends the step.
+  // Three register sets rotate through a three-times unrolled loop (a copy
+  // would wait for the loads just issued); every step loads (clamped), so
+  // the waits stay two steps deep on every path.
   V16 r0[FW], r1[FW], r2[FW];
-  auto step = [&](int s, V16 (&next)[FW], V16 (&ahead)[FW]) {
-    load(ahead, s + 2);
-    compute(s & 1, s);
-    store(next, (s + 1) & 1);
+  auto step = [&](int i, V16 (&next)[FW], V16 (&ahead)[FW]) {
+    load(ahead, i + 2);
+    compute(i & 1, i);
+    store(next, (i + 1) & 1);
     __syncthreads();
   };
   load(r0, 0);
   load(r1, 1);
   store(r0, 0);
   __syncthreads();
-  for (int s = 0; s < n_steps; s += 3) {
-    step(s, r1, r2);
-    if (s + 1 < n_steps) step(s + 1, r2, r0);
-    if (s + 2 < n_steps) step(s + 2, r0, r1);
+  for (int i = 0; i < n_local; i += 3) {
+    step(i, r1, r2);
+    if (i + 1 < n_local) step(i + 1, r2, r0);
+    if (i + 2 < n_local) step(i + 2, r0, r1);
   }
 
   // each lane summed its own keys: total over the query's four lanes
@@ -224,6 +231,50 @@ __global__ __launch_bounds__(256) void attn_kernel(
   for (int u = 0; u < QTW; ++u) {
     l_run[u] += __shfl_xor(l_run[u], 16, 64);
     l_run[u] += __shfl_xor(l_run[u], 32, 64);
+  }
+
+  // key groups 1.. hand (m, l, O) to group 0 through the (now idle) fragment
+  // buffers; group 0 merges them in order
+  static_assert((KG - 1) * 4 * QTW * (HT + 1) <= KG * 2 * NF, "merge area fits the fragment buffers");
+  V16* xch = &frag[0][0][0][0];
+  if (kg > 0) {
+#pragma unroll
+    for (int u = 0; u < QTW; ++u) {
+      const int slot = ((kg - 1) * 4 + wave) * QTW + u;
+#pragma unroll
+      for (int ht = 0; ht < HT; ++ht) xch[(slot * (HT + 1) + ht) * 64 + lane].f = o[u][ht];
+      xch[(slot * (HT + 1) + HT) * 64 + lane].f = floatx4{m_run[u], l_run[u], 0.f, 0.f};
+    }
+  }
+  __syncthreads();
+  if (kg > 0) return;
+#pragma unroll
+  for (int u = 0; u < QTW; ++u) {
+    float M = m_run[u];
+#pragma unroll
+    for (int k = 1; k < KG; ++k)
+      M = fmaxf(M, xch[((((k - 1) * 4 + wave) * QTW + u) * (HT + 1) + HT) * 64 + lane].f[0]);
+    const float w0 = M == -INFINITY ? 0.f : exp2f(m_run[u] - M);
+    float l = l_run[u] * w0;
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[u][ht][i] *= w0;
+#pragma unroll
+    for (int k = 1; k < KG; ++k) {
+      const int slot = ((k - 1) * 4 + wave) * QTW + u;
+      const floatx4 ml = xch[(slot * (HT + 1) + HT) * 64 + lane].f;
+      const float w = ml[0] == -INFINITY ? 0.f : exp2f(ml[0] - M);
+      l += w * ml[1];
+#pragma unroll
+      for (int ht = 0; ht < HT; ++ht) {
+        const floatx4 v = xch[(slot * (HT + 1) + ht) * 64 + lane].f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[u][ht][i] += w * v[i];
+      }
+    }
+    m_run[u] = M;
+    l_run[u] = l;
   }
 
 #pragma unroll
@@ -294,7 +345,7 @@ hipError_t run(const AttnPlan& p, PassTable tb, int batch, int m_cap, const floa
                float* o, hipStream_t st) {
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)HD);
   dim3 grid(p.n_split, H, batch * p.q_blocks);
-  hipLaunchKernelGGL((attn_kernel<T, HD, QTW>), grid, dim3(256), 0, st, tb,
+  hipLaunchKernelGGL((attn_kernel<T, HD, QTW>), grid, dim3(256 * kKeyGroups), 0, st, tb,
                      p.q_blocks,
                      p.keys_per_split, p.n_split, m_cap, q, static_cast<const T*>(kc),
                      static_cast<const T*>(vt), H, Lp, scale_log2, o_part, ml_part, o);
@@ -311,7 +362,6 @@ hipError_t run_q(const AttnPlan& p, PassTable tb, int batch, int m_cap, const fl
                  const void* kc, const void* vt, int H, int Lp, float* o_part, float* ml_part,
                  float* o, hipStream_t st) {
   if (p.qtw == 1) return run<T, HD, 1>(p, tb, batch, m_cap, q, kc, vt, H, Lp, o_part, ml_part, o, st);
-  if (p.qtw == 2) return run<T, HD, 2>(p, tb, batch, m_cap, q, kc, vt, H, Lp, o_part, ml_part, o, st);
   return hipErrorInvalidValue;
 }
 
@@ -321,9 +371,9 @@ int attn_cache_len(int max_len) { return (max_len + 63) / 64 * 64; }
 
 // Blocks of 64 queries, one 16-query tile per wave (measured faster than two
 // tiles per wave over the same keys, which halves the workgroups).  Then key
-// splits while the grid stays within target_wgs and every split keeps at
-// least 192 keys (shorter splits cost more in fixed work and partials than
-// they gain in parallelism).
+// splits while the grid stays within target_wgs (256: about one workgroup of
+// eight waves per CU) and every split keeps at least 192 keys (shorter splits
+// cost more in fixed work and partials than they gain in parallelism).
 AttnPlan plan_attention(int batch, int max_rows_per_req, int max_keys, int H, int target_wgs) {
   AttnPlan p{};
   p.qtw = 1;

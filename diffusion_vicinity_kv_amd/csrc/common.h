@@ -76,43 +76,6 @@ template <> struct Mfma<float> {
   }
 };
 
-// Four-element K step used by attention's P*V product: a[4], b[4] hold A row c
-// at K = 4*g .. 4*g+3 and B column c at the same K.
-template <typename T> struct Mfma4;
-template <> struct Mfma4<bf16> {
-  __device__ __forceinline__ static void mac(floatx4& acc, const float* a, const float* b) {
-    bf16x4 av, bv;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      av[i] = static_cast<bf16>(a[i]);
-      bv[i] = static_cast<bf16>(b[i]);
-    }
-    acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, bv, acc, 0, 0, 0);
-  }
-  // b = hi + lo with hi = bf16(b), lo = bf16(b - hi): two bf16 MFMAs, so the
-  // fp32 operand b loses only its 2^-16 relative tail.
-  __device__ __forceinline__ static void mac_split_b(floatx4& acc, const float* a, const float* b) {
-    bf16x4 av, bh, bl;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      av[i] = static_cast<bf16>(a[i]);
-      bh[i] = static_cast<bf16>(b[i]);
-      bl[i] = static_cast<bf16>(b[i] - static_cast<float>(bh[i]));
-    }
-    acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, bh, acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, bl, acc, 0, 0, 0);
-  }
-};
-template <> struct Mfma4<float> {
-  __device__ __forceinline__ static void mac(floatx4& acc, const float* a, const float* b) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i], b[i], acc, 0, 0, 0);
-  }
-  // b given as fp32: already exact for the fp32 MFMA.
-  __device__ __forceinline__ static void mac_split_b(floatx4& acc, const float* a, const float* b) {
-    mac(acc, a, b);
-  }
-};
 // Split an fp32 vector operand of the 16-byte MFMA layout into bf16 hi/lo
 // halves (bf16 MFMA) or pass it through (fp32 MFMA).  src holds VEC floats.
 template <typename T> struct SplitOperand;

@@ -49,10 +49,10 @@ struct Layout {
   DType dt;
   GemmPlan g_qkv_s, g_o_s, g_gu_s, g_d_s, g_lm;   // step pass
   GemmPlan g_qkv_r, g_o_r, g_gu_r, g_d_r;         // refresh pass
-  // MoE: shared-expert plans (step, refresh); experts use the grouped GEMM
+  // MoE: the shared expert reuses the FFN plans (sized for Fs); the experts
+  // use the grouped GEMM
   bool moe;
   int E, topk, Fe, Fs, assign_cap;
-  GemmPlan g_sgu_s, g_sd_s, g_sgu_r, g_sd_r;
   AttnPlan a_step, a_ref;
   VocabPlan vp;
   size_t part_elems, attn_o_elems, attn_ml_elems;
@@ -153,8 +153,8 @@ bool make_layout(const dinfer_model_cfg* m, const dinfer_decode_cfg* dc, int max
                            pe(l.g_qkv_r, l.m_ref, 3 * d), pe(l.g_o_r, l.m_ref, d),
                            pe(l.g_gu_r, l.m_ref, 2 * Fd), pe(l.g_d_r, l.m_ref, d)});
   // about one workgroup per CU: more key splits only add fp32 partial traffic
-  l.a_step = plan_attention(max_batch, win, max_len, l.H, 512);
-  l.a_ref = plan_attention(max_batch, max_len, max_len, l.H, 512);
+  l.a_step = plan_attention(max_batch, win, max_len, l.H, 256);
+  l.a_ref = plan_attention(max_batch, max_len, max_len, l.H, 256);
   l.attn_o_elems = std::max((size_t)l.a_step.n_split * l.m_step, (size_t)l.a_ref.n_split * l.m_ref) *
                    l.H * l.hd;
   l.attn_ml_elems = l.attn_o_elems / l.hd * 2;
