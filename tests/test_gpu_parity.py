@@ -150,6 +150,32 @@ def test_tiny_lockstep_run(variant):
     assert np.array_equal(tokens.cpu().numpy()[0][: runs[0].L], runs[0].tokens)
 
 
+@pytest.mark.parametrize("shape", ["one_key_step", "many_key_splits", "hd128_ragged_length"])
+def test_attention_edge_lockstep(shape):
+    """Attention layouts at the edges of the kernel's tiling, fp32 so every
+    decision must match: a sequence shorter than one key step (the second key
+    group of the workgroup has no step); a long sequence whose window is split
+    over several key ranges merged afterwards, with a ragged last range (the
+    refresh splits too); head dim 128 with a length that is not a multiple of
+    the 32-key V tiles."""
+    note(f"tiny fp32 attention edge case {shape}")
+    if shape == "one_key_step":
+        wc = small_workload(prompt=(4, 4), gen=8, B=8, w=2, bias=6.0 + float(np.log(4094.0)),
+                            seed=21)
+    elif shape == "many_key_splits":
+        wc = small_workload(prompt=(1000, 1000), gen=32, B=16, w=4, alpha=0.3, seed=22)
+    else:
+        wc = small_workload(H=2, hd=128, prompt=(301, 301), gen=32, B=16, w=3, alpha=0.3,
+                            bias=6.0 + float(np.log(4094.0)), seed=23)
+    eng, w, req, tokens = build(wc)
+    runs = oracle_runs(wc, w, req)
+    rep = lockstep(wc, eng, tokens, runs, logit_tol=1e-5, check_cache=True,
+                   max_steps=12 if shape == "many_key_splits" else 10_000)
+    note(f"  {rep}")
+    assert rep["diverged"] is None
+    assert rep["steps"] >= 1
+
+
 @pytest.mark.parametrize("unroll", [0, 1, 4])
 def test_tiny_run_to_completion_matches_oracle(unroll):
     note(f"tiny fp32 run_to_completion unroll={unroll}")
