@@ -13,7 +13,9 @@ namespace {
 // 64 x 64 as 4 x 4 MFMA tiles; WN = 4: two waves per SIMD, used when the grid
 // still has a workgroup per CU, else WN = 2), K slabs of BK = 64 (bf16)
 // / 32 (fp32) elements double-buffered in LDS with the activations split into
-// hi/lo planes on the way in.  Global loads run two slabs ahead through three
+// hi/lo planes on the way in.  LDS rows are unpadded 128-byte lines with an
+// XOR swizzle of their 16-byte chunks (bank-conflict free reads and writes;
+// LDS traffic, not MFMA, bounds this kernel).  Global loads run two slabs ahead through three
 // register sets (a three-times unrolled loop, as in the skinny kernel), all
 // unconditional: rows past M read row M-1 and columns past N read column
 // N-1 (their outputs are not stored).
@@ -33,7 +35,13 @@ __global__ __launch_bounds__(128 * WN) void gemm_fat_kernel(const float* __restr
   constexpr int KSTEP = MF::KSTEP;
   constexpr int KK = 2;                        // vector steps per slab
   constexpr int BK = KK * KSTEP;               // 64 (bf16) / 32 (fp32) elements
-  constexpr int STR = BK + 16 / sizeof(TW);    // LDS row stride (+16 B)
+  constexpr int STR = BK;                      // LDS row: 128 bytes, eight 16-byte chunks
+  constexpr int CH = 16 / sizeof(TW);          // elements per chunk
+  static_assert(BK * sizeof(TW) == 128, "the swizzle assumes eight chunks per row");
+  // Chunk j of row r lives at chunk j ^ ((r >> 1) & 7): the 16 rows of a
+  // fragment read then fall on 16 distinct 16-byte bank groups, and the
+  // rows of a staging write on disjoint halves of the banks.
+  auto sw = [](int r, int e) { return r * STR + ((((e / CH) ^ (r >> 1)) & 7) * CH) + e % CH; };
   constexpr int F4R = BK / 4;                  // float4 of A per slab row
   constexpr int AV = kFatM * F4R / kFatThreads;     // float4 of A per thread per slab
   constexpr int WVR = BK / VEC;                // 16-byte W vectors per slab row
@@ -85,14 +93,14 @@ __global__ __launch_bounds__(128 * WN) void gemm_fat_kernel(const float* __restr
       const int v = threadIdx.x + kFatThreads * i;
       const int r = v / F4R;
       const int cv = v % F4R;
-      AS::store4(&As[buf][0][r * STR + cv * 4], &As[buf][PL - 1][r * STR + cv * 4], ra[i]);
+      AS::store4(&As[buf][0][sw(r, cv * 4)], &As[buf][PL - 1][sw(r, cv * 4)], ra[i]);
     }
 #pragma unroll
     for (int i = 0; i < BV; ++i) {
       const int v = threadIdx.x + kFatThreads * i;
       const int r = v / WVR;
       const int cv = v % WVR;
-      st16(&Bs[buf][r * STR + cv * VEC], rb[i]);
+      st16(&Bs[buf][sw(r, cv * VEC)], rb[i]);
     }
   };
   auto mma = [&](int buf) {
@@ -102,13 +110,13 @@ __global__ __launch_bounds__(128 * WN) void gemm_fat_kernel(const float* __restr
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt)
         b[nt] = *reinterpret_cast<const V16*>(
-            &Bs[buf][(wn * 64 + nt * 16 + lc) * STR + kk * KSTEP + lg * VEC]);
+            &Bs[buf][sw(wn * 64 + nt * 16 + lc, kk * KSTEP + lg * VEC)]);
 #pragma unroll
       for (int p = 0; p < PL; ++p) {
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
           const V16 a = *reinterpret_cast<const V16*>(
-              &As[buf][p][(wm * 64 + mt * 16 + lc) * STR + kk * KSTEP + lg * VEC]);
+              &As[buf][p][sw(wm * 64 + mt * 16 + lc, kk * KSTEP + lg * VEC)]);
 #pragma unroll
           for (int nt = 0; nt < 4; ++nt) MF::mac(acc[mt][nt], a, b[nt]);
         }
