@@ -73,7 +73,9 @@ def dominant_kernel_timing(wc, weights, iters=40, with_events=True):
     lib = B.load()
     out = torch.empty(max(lib.dinfer_linear_out_elems(rows, 3 * d, d, B.BF16),
                           lib.dinfer_linear_out_elems(rows, 2 * F, d, B.BF16)), device="cuda")
-    layers = [L for L in weights["layers"] if L is not None]
+    # the two projections in the packed layout the library reads
+    layers = [{k: B.pack_linear(L[k]) for k in ("wqkv", gu_key)}
+              for L in weights["layers"] if L is not None]
     shapes = []
     for i in range(iters):
         L = layers[i % len(layers)]

@@ -18,7 +18,7 @@ EXPORTS = [
     "dinfer_workspace_bytes", "dinfer_step_init", "dinfer_set_batch", "dinfer_refresh_kv",
     "dinfer_denoise_step", "dinfer_commit", "dinfer_advance_blocks", "dinfer_run_to_completion",
     "dinfer_get_step_view", "dinfer_vocab_stats_scratch_bytes", "dinfer_vocab_stats",
-    "dinfer_step_graph", "dinfer_linear_out_elems", "dinfer_linear",
+    "dinfer_step_graph", "dinfer_pack_linear", "dinfer_linear_out_elems", "dinfer_linear",
     "dinfer_status_str", "dinfer_last_error", "dinfer_destroy",
 ]
 
@@ -97,6 +97,7 @@ def load(path: str = LIB_PATH) -> C.CDLL:
         "dinfer_vocab_stats_scratch_bytes": (sz, [i32, i32]),
         "dinfer_vocab_stats": (i32, [vp, i32, i32, vp, vp, i32, vp, vp, vp, vp, vp, vp, sz, vp]),
         "dinfer_step_graph": (i32, [vp, i32]),
+        "dinfer_pack_linear": (i32, [vp, vp, C.c_int64, i32, i32, vp]),
         "dinfer_linear_out_elems": (sz, [i32, i32, i32, i32]),
         "dinfer_linear": (i32, [vp, vp, vp, i32, i32, i32, i32, C.POINTER(i32), vp]),
         "dinfer_status_str": (C.c_char_p, [i32]),
@@ -132,10 +133,25 @@ def stream_handle(stream=None) -> int:
     return int(s.cuda_stream)
 
 
+def pack_linear(W, stream=None):
+    """dinfer_pack_linear on a contiguous torch device tensor W [N][K] or
+    [E][N][K] (f32 or bf16); returns a new tensor of the same shape and dtype
+    holding the packed layout the projection kernels read."""
+    import torch
+    lib = load()
+    assert W.is_contiguous() and W.dtype in (torch.float32, torch.bfloat16)
+    out = torch.empty_like(W)
+    K = W.shape[-1]
+    check(lib.dinfer_pack_linear(ptr(W), ptr(out), W.numel() // K, K,
+                                 F32 if W.dtype == torch.float32 else BF16,
+                                 stream_handle(stream)), "dinfer_pack_linear")
+    return out
+
+
 def linear(A, W, out, stream=None) -> int:
     """dinfer_linear on torch device tensors; returns the split count.
-    A fp32 [M][K], W [N][K] (f32 or bf16), out fp32 with at least
-    dinfer_linear_out_elems(M, N, K, dtype) elements."""
+    A fp32 [M][K], W [N][K] (f32 or bf16) packed by pack_linear, out fp32 with
+    at least dinfer_linear_out_elems(M, N, K, dtype) elements."""
     import torch
     lib = load()
     assert A.dtype == torch.float32

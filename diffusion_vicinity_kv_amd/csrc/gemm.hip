@@ -8,12 +8,19 @@
 // the weights' own precision only (no activation rounding), for one extra
 // MFMA per weight fragment -- free wherever the layer is a weight stream.
 //
+// Weights are read in a packed layout (pack_linear below): the 1 KB MFMA B
+// operand of every 16 rows x KSTEP columns is stored contiguously, in lane
+// order, so that each weight load of a wave is one contiguous kilobyte --
+// whole 128-byte lines, sequential along K.  Read row-major, each load would
+// touch 64 bytes of 16 different rows and the vector L1 would issue twice as
+// many half-line requests, stalling the address unit.
+//
 // Kernels:
 //  * skinny (M <= 128): the vicinity window holds tens of rows, so a layer is
 //    a weight stream.  A workgroup of NW waves owns 16*NT*NW output columns
 //    (64 to 256) over all rows and one K slice.  Each wave streams its own
-//    weight rows straight into registers (one 16-byte load per lane per MFMA
-//    B operand), two K chunks ahead; the activation chunk is
+//    packed weight blocks straight into registers (one 16-byte load per lane
+//    per MFMA B operand), two K chunks ahead; the activation chunk is
 //    split into hi/lo planes in LDS, double-buffered, and shared by the
 //    waves -- wide column groups keep that fp32 re-read small next to the
 //    weights.  K splits bring the workgroup count to about one per CU; each
@@ -71,9 +78,12 @@ __device__ __forceinline__ void skinny_tile(const float* __restrict__ A,
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = floatx4{0.f, 0.f, 0.f, 0.f};
 
+  // packed weights: block (16-row group, vector step) of 64 * VEC elements
+  constexpr int BE = 64 * VEC;
   const TW* wrow[NT];
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) wrow[nt] = W + (size_t)(n0 + nt * 16 + lc) * K + lg * VEC;
+  for (int nt = 0; nt < NT; ++nt)
+    wrow[nt] = W + (size_t)(n0 / 16 + nt) * (K / KSTEP) * BE + lane * VEC;
 
   // Weight fragments and raw activations of three consecutive chunks live in
   // registers.  At chunk c the loads of chunk c+2 are issued (activations
@@ -89,7 +99,7 @@ __device__ __forceinline__ void skinny_tile(const float* __restrict__ A,
 #pragma unroll
     for (int j = 0; j < U; ++j)
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) b[j][nt] = ld16(wrow[nt] + c * KC + j * KSTEP);
+      for (int nt = 0; nt < NT; ++nt) b[j][nt] = ld16(wrow[nt] + (size_t)(c * U + j) * BE);
   };
   auto load_a = [&](float4 (&areg)[AV], int c) {
 #pragma unroll
@@ -233,6 +243,26 @@ __global__ __launch_bounds__(NW * 64) void gemm_grouped_kernel(
 }
 
 
+// Packs W [N][K] (row-major) into the block layout the GEMMs read: block
+// (g = n / 16, s = k / KSTEP) holds 64 * VEC elements at offset
+// (g * K / KSTEP + s) * 64 * VEC, and its lane 16 * q + c slot holds
+// W[16 g + c][s * KSTEP + q * VEC, + VEC) -- the MFMA operand of that lane.
+// A stack of E matrices [E][N][K] packs as one [E*N][K] matrix.
+template <typename TW>
+__global__ __launch_bounds__(256) void pack_kernel(const TW* __restrict__ W, TW* __restrict__ P,
+                                                   int N, int K) {
+  constexpr int VEC = Mfma<TW>::VEC;
+  constexpr int KSTEP = Mfma<TW>::KSTEP;
+  const int KS = K / KSTEP;
+  const size_t blk = (size_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (blk >= (size_t)(N / 16) * KS) return;
+  const int lane = threadIdx.x & 63;
+  const size_t g = blk / KS;
+  const int s = (int)(blk % KS);
+  st16(P + blk * 64 * VEC + lane * VEC,
+       ld16(W + (g * 16 + (lane & 15)) * K + s * KSTEP + (lane >> 4) * VEC));
+}
+
 // ---------------------------------------------------------------------------
 template <typename TW, int MT, int NT, int NW>
 hipError_t run_skinny(const GemmPlan& p, const float* A, const void* W, float* out,
@@ -302,6 +332,22 @@ hipError_t launch_gemm_grouped(DType t, const float* A, const int* row_of, const
   else
     hipLaunchKernelGGL((gemm_grouped_kernel<bf16, 2, 4>), grid, dim3(256), 0, st, A, row_of,
                        e_count, e_off, static_cast<const bf16*>(W), out, N, K, n_tiles, m_tiles);
+  return hipGetLastError();
+}
+
+hipError_t launch_pack_linear(DType t, const void* W, void* P, size_t N, int K, hipStream_t st) {
+  const int kstep = t == DType::F32 ? Mfma<float>::KSTEP : Mfma<bf16>::KSTEP;
+  if (N % 16 != 0 || N > (size_t)INT32_MAX || K <= 0 || K % kstep != 0)
+    return hipErrorInvalidValue;
+  const size_t wgs = (N / 16 * (K / kstep) + 3) / 4;   // four 1 KB blocks per workgroup
+  if (wgs == 0) return hipSuccess;
+  if (wgs > (size_t)INT32_MAX) return hipErrorInvalidValue;
+  if (t == DType::F32)
+    hipLaunchKernelGGL(pack_kernel<float>, dim3((unsigned)wgs), dim3(256), 0, st,
+                       static_cast<const float*>(W), static_cast<float*>(P), (int)N, K);
+  else
+    hipLaunchKernelGGL(pack_kernel<bf16>, dim3((unsigned)wgs), dim3(256), 0, st,
+                       static_cast<const bf16*>(W), static_cast<bf16*>(P), (int)N, K);
   return hipGetLastError();
 }
 

@@ -1,6 +1,7 @@
 // Dense projections with many rows (block-start refresh, batched steps) on
 // gfx950 MFMA: out = A * W^T, A [M][K] fp32 activations, W [N][K] weights
-// (fp32 or bf16), fp32 accumulation, no K split.
+// (fp32 or bf16) in the packed block layout of launch_pack_linear, fp32
+// accumulation, no K split.
 #include "common.h"
 #include "gemm_split.h"
 #include "kernels.h"
@@ -13,12 +14,14 @@ namespace {
 // 64 x 64 as 4 x 4 MFMA tiles; WN = 4: two waves per SIMD, used when the grid
 // still has a workgroup per CU, else WN = 2), K slabs of BK = 64 (bf16)
 // / 32 (fp32) elements double-buffered in LDS with the activations split into
-// hi/lo planes on the way in.  LDS rows are unpadded 128-byte lines with an
-// XOR swizzle of their 16-byte chunks (bank-conflict free reads and writes;
-// LDS traffic, not MFMA, bounds this kernel).  Global loads run two slabs ahead through three
-// register sets (a three-times unrolled loop, as in the skinny kernel), all
-// unconditional: rows past M read row M-1 and columns past N read column
-// N-1 (their outputs are not stored).
+// hi/lo planes on the way in.  Activation rows in LDS are unpadded 128-byte
+// lines with an XOR swizzle of their 16-byte chunks; the weights keep their
+// packed 1 KB operand blocks, so both are read and written without bank
+// conflicts (LDS traffic, not MFMA, bounds this kernel).  Global loads run
+// two slabs ahead through three register sets (a three-times unrolled loop,
+// as in the skinny kernel), all unconditional: rows past M read row M-1 and
+// columns past N read the last 16-column group (their outputs are not
+// stored).
 constexpr int kFatM = 128;
 
 template <typename TW, int WN>
@@ -44,8 +47,9 @@ __global__ __launch_bounds__(128 * WN) void gemm_fat_kernel(const float* __restr
   auto sw = [](int r, int e) { return r * STR + ((((e / CH) ^ (r >> 1)) & 7) * CH) + e % CH; };
   constexpr int F4R = BK / 4;                  // float4 of A per slab row
   constexpr int AV = kFatM * F4R / kFatThreads;     // float4 of A per thread per slab
-  constexpr int WVR = BK / VEC;                // 16-byte W vectors per slab row
-  constexpr int BV = kFatN * WVR / kFatThreads;     // W vectors per thread per slab
+  constexpr int BE = 64 * VEC;                 // elements of one packed weight block
+  constexpr int BV = (kFatN / 16) * KK * 64 / kFatThreads;   // W vectors per thread per slab
+  static_assert((kFatN / 16) * KK * 64 % kFatThreads == 0, "weight slab must split evenly");
   __shared__ __attribute__((aligned(16))) TW As[2][PL][kFatM * STR];
   __shared__ __attribute__((aligned(16))) TW Bs[2][kFatN * STR];
 
@@ -74,18 +78,21 @@ __global__ __launch_bounds__(128 * WN) void gemm_fat_kernel(const float* __restr
     const int v = threadIdx.x + kFatThreads * i;
     arow[i] = A + (size_t)min(m0 + v / F4R, M - 1) * K + (v % F4R) * 4;
   }
+  // weight vector v of a slab: block v / 64 = (16-column group, vector step),
+  // lane slot v % 64; the slab's blocks sit in LDS in that order
   const TW* wrow[BV];
 #pragma unroll
   for (int i = 0; i < BV; ++i) {
     const int v = threadIdx.x + kFatThreads * i;
-    wrow[i] = W + (size_t)min(n0 + v / WVR, N - 1) * K + (v % WVR) * VEC;
+    const int grp = min(n0 / 16 + (v / 64) / KK, N / 16 - 1);
+    wrow[i] = W + ((size_t)grp * (K / KSTEP) + (v / 64) % KK) * BE + (v % 64) * VEC;
   }
   auto gload = [&](float4 (&ra)[AV], V16 (&rb)[BV], int kt) {
     kt = min(kt, nk - 1);   // past the end: repeat the last slab
 #pragma unroll
     for (int i = 0; i < AV; ++i) ra[i] = *reinterpret_cast<const float4*>(arow[i] + kt * BK);
 #pragma unroll
-    for (int i = 0; i < BV; ++i) rb[i] = ld16(wrow[i] + kt * BK);
+    for (int i = 0; i < BV; ++i) rb[i] = ld16(wrow[i] + (size_t)kt * KK * BE);
   };
   auto sstore = [&](const float4 (&ra)[AV], const V16 (&rb)[BV], int buf) {
 #pragma unroll
@@ -96,12 +103,7 @@ __global__ __launch_bounds__(128 * WN) void gemm_fat_kernel(const float* __restr
       AS::store4(&As[buf][0][sw(r, cv * 4)], &As[buf][PL - 1][sw(r, cv * 4)], ra[i]);
     }
 #pragma unroll
-    for (int i = 0; i < BV; ++i) {
-      const int v = threadIdx.x + kFatThreads * i;
-      const int r = v / WVR;
-      const int cv = v % WVR;
-      st16(&Bs[buf][sw(r, cv * VEC)], rb[i]);
-    }
+    for (int i = 0; i < BV; ++i) st16(&Bs[buf][(threadIdx.x + kFatThreads * i) * VEC], rb[i]);
   };
   auto mma = [&](int buf) {
 #pragma unroll
@@ -109,8 +111,7 @@ __global__ __launch_bounds__(128 * WN) void gemm_fat_kernel(const float* __restr
       V16 b[4];
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt)
-        b[nt] = *reinterpret_cast<const V16*>(
-            &Bs[buf][sw(wn * 64 + nt * 16 + lc, kk * KSTEP + lg * VEC)]);
+        b[nt] = *reinterpret_cast<const V16*>(&Bs[buf][((wn * 4 + nt) * KK + kk) * BE + lane * VEC]);
 #pragma unroll
       for (int p = 0; p < PL; ++p) {
 #pragma unroll

@@ -41,8 +41,13 @@ def _decode_struct(d, graph_unroll: int) -> B.DecodeCfg:
 class Engine:
     """A denoising-step context.
 
-    weights: dict in the library's layouts (see include/dinfer.h), device tensors.
+    weights: dict of row-major device tensors (synth.make_weights layout).  The
+    projection matrices are packed once, at construction, into the layout the
+    library reads (dinfer_pack_linear); the engine holds the packed copies.
     """
+
+    PACKED = ("wqkv", "wo", "w_gate_up", "w_down", "exp_gate_up", "exp_down",
+              "shared_gate_up", "shared_down")
 
     def __init__(self, model_cfg, decode_cfg, weights, max_batch, max_len, graph_unroll=0,
                  stream=None):
@@ -57,10 +62,16 @@ class Engine:
         self._weights = weights
         nl = model_cfg.n_layers
         arr = C.c_void_p * nl
+        # packed projection weights, per layer (None where the layer is absent)
+        self.packed_layers = [
+            {k: B.pack_linear(L[k], self.stream) for k in self.PACKED if L.get(k) is not None}
+            if L else None for L in weights["layers"]]
+        lm = weights.get("lm_head")
+        self.packed_lm_head = None if lm is None else B.pack_linear(lm, self.stream)
 
         def per_layer(key):
-            vals = [B.ptr(weights["layers"][i].get(key)) if weights["layers"][i] else 0
-                    for i in range(nl)]
+            src = self.packed_layers if key in self.PACKED else weights["layers"]
+            vals = [B.ptr(src[i].get(key)) if src[i] else 0 for i in range(nl)]
             return arr(*vals)
 
         keys = ["attn_norm", "wqkv", "wo", "ffn_norm"]
@@ -72,7 +83,7 @@ class Engine:
         w = B.Weights()
         w.tok_emb = B.ptr(weights["tok_emb"])
         w.final_norm = B.ptr(weights["final_norm"])
-        w.lm_head = B.ptr(weights["lm_head"])
+        w.lm_head = B.ptr(self.packed_lm_head)
         for k, a in self._arrays.items():
             setattr(w, k, C.cast(a, B._PP))
         self._w = w

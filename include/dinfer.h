@@ -89,7 +89,11 @@ typedef struct {
 } dinfer_decode_cfg;
 
 /* Device pointers to the weights (borrowed).  Per-layer entries are host
- * arrays of n_layers device pointers; unused families may be NULL. */
+ * arrays of n_layers device pointers; unused families may be NULL.
+ * Projection weights -- lm_head, wqkv, wo, w_gate_up, w_down, exp_gate_up,
+ * exp_down, shared_gate_up, shared_down -- are Linear [out][in] matrices
+ * (experts: [E][out][in]) in the packed layout of dinfer_pack_linear; the
+ * others (tok_emb [V][d], norms [d], router [E][d]) are plain row-major. */
 typedef struct {
   const void* tok_emb;
   const void* final_norm;
@@ -241,10 +245,24 @@ dinfer_status dinfer_get_step_view(const dinfer_ctx* ctx, dinfer_step_view* out)
  * unrolling of the dInfer news article, section "系统级压榨". */
 dinfer_status dinfer_step_graph(dinfer_ctx* ctx, int32_t n_steps);
 
+/* Weight packing (a storage format of this library, not of the method):
+ * copies d_W, a row-major [rows][K] matrix of the given dtype (a stack of E
+ * matrices [E][N][K] is one [E*N][K] matrix), into d_packed (same byte size,
+ * no overlap) in the layout every projection kernel reads.  Each 16-row group
+ * and each run of 32 (bf16) / 16 (f32) columns becomes one contiguous 1 KB
+ * block, blocks ordered by row group then column run; inside a block, 16-byte
+ * slot 16*q + c holds row c of the group, columns q*VEC .. q*VEC+VEC-1 of the
+ * run (VEC = 8 bf16 / 4 f32): the MFMA operand of lane 16*q + c, so that a
+ * wave's weight load is one contiguous kilobyte.  rows % 16 == 0; K a
+ * multiple of 32 (bf16) / 16 (f32).  Enqueued on stream. */
+dinfer_status dinfer_pack_linear(const void* d_W, void* d_packed, int64_t rows, int32_t K,
+                                 int32_t dtype, void* stream);
+
 /* Standalone projection, the Linear layer every step runs:
  * out[s][m][n] = sum over the s-th K slice of A[m][k] * W[n][k], with A an fp32
  * [M][K] row-major device array (activations are fp32 throughout the step)
- * and W [N][K] in the model dtype (weights); out fp32 [splits][M][N].  The
+ * and W [N][K] in the model dtype, packed by dinfer_pack_linear; out fp32
+ * [splits][M][N].  The
  * product A W^T is the sum of the splits (taken in split order by the
  * library's own consumers).  With bf16 weights each activation enters the
  * MFMA as hi = bf16(a) plus lo = bf16(a - hi), so only the weights' rounding

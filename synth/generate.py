@@ -48,7 +48,8 @@ def normal(shape, std, dtype, device, seed, tag, index=0) -> torch.Tensor:
 
 def make_weights(m: ModelCfg, seed: int, device="cpu", layers=None, with_embed=True,
                  with_head=True) -> dict:
-    """Weights in the library's layouts (Linear storage [out][in], row-major).
+    """Weights as row-major tensors (Linear storage [out][in]); the engine packs
+    the projection matrices into the library's own layout.
 
     tok_emb [V][d], final_norm [d], lm_head [V][d]; per layer: attn_norm [d],
     wqkv [3d][d] (rows q | k | v, head-major inside each), wo [d][d],

@@ -245,6 +245,26 @@ def test_full_width_two_layer_parity(preset):
 
 
 # --------------------------------------------------------------- linear (K1)
+@pytest.mark.parametrize("shape,dt", [((48, 256), "bf16"), ((3, 32, 96), "bf16"),
+                                      ((4096, 4096), "bf16"), ((32, 48), "f32"),
+                                      ((2, 16, 64), "f32")])
+def test_pack_linear_layout(shape, dt):
+    """Packed weight layout, bit for bit: 16-row groups x one vector step
+    (32 bf16 / 16 f32 columns) per 1 KB block, blocks by group then step,
+    slot 16q + c = row c of the group, columns [q*VEC, (q+1)*VEC) of the step."""
+    note(f"pack_linear {shape} {dt}")
+    tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+    vec = 8 if dt == "bf16" else 4
+    g = torch.Generator(device="cuda").manual_seed(len(shape) * 100 + shape[-1])
+    W = torch.randn(*shape, device="cuda", generator=g).to(tdt)
+    P = B.pack_linear(W)
+    torch.cuda.synchronize()
+    K = shape[-1]
+    rows = W.numel() // K
+    w = W.reshape(rows // 16, 16, K // (4 * vec), 4, vec).permute(0, 2, 3, 1, 4).contiguous()
+    assert torch.equal(P.reshape(-1).cpu(), w.reshape(-1).cpu())
+
+
 @pytest.mark.parametrize("M,N,K,dt", [(64, 24576, 4096, "bf16"), (64, 12288, 4096, "bf16"),
                                       (48, 4096, 12288, "bf16"), (37, 4096, 4096, "bf16"),
                                       (128, 1024, 2048, "bf16"), (300, 384, 512, "bf16"),
@@ -262,7 +282,7 @@ def test_linear_parity(M, N, K, dt):
     lib = B.load()
     n_out = lib.dinfer_linear_out_elems(M, N, K, B.BF16 if dt == "bf16" else B.F32)
     out = torch.full((n_out,), float("nan"), device="cuda")
-    S = B.linear(A, W, out)
+    S = B.linear(A, B.pack_linear(W), out)
     torch.cuda.synchronize()
     got = out.cpu().double().numpy().reshape(S, M, N).sum(0)
     want = A.cpu().double().numpy() @ W.cpu().double().numpy().T
