@@ -306,6 +306,79 @@ __global__ __launch_bounds__(256 * kKeyGroups) void attn_kernel(
 // Combine the key splits of each row: out = sum_s 2^(m_s - M) O_s /
 // sum_s 2^(m_s - M) l_s per head, splits taken in order.  One float4 of the
 // row per thread.
+// Merge of NS split records (m_s, l_s, o_s) of one (row, head), float4 of
+// the output: weights exp2(m_s - max), in split order.  The fixed-count
+// version issues every load before the first use.
+template <int HD, int NS>
+__device__ __forceinline__ float4 merge_fixed(const float* __restrict__ o_part,
+                                              const float* __restrict__ ml_part, size_t base0,
+                                              size_t sstride, int i4) {
+  float2 ml[NS];
+  float4 v[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    const size_t base = base0 + s * sstride;
+    ml[s] = *reinterpret_cast<const float2*>(ml_part + base * 2);
+    v[s] = *reinterpret_cast<const float4*>(o_part + base * HD + (i4 * 4) % HD);
+  }
+  float M = -INFINITY;
+#pragma unroll
+  for (int s = 0; s < NS; ++s) M = fmaxf(M, ml[s].x);
+  float lsum = 0.f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    const float w = exp2f(ml[s].x - M);
+    lsum += w * ml[s].y;
+    acc.x += w * v[s].x;
+    acc.y += w * v[s].y;
+    acc.z += w * v[s].z;
+    acc.w += w * v[s].w;
+  }
+  const float inv = 1.f / lsum;
+  return make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+}
+
+template <int HD>
+__device__ __forceinline__ float4 merge_fixed_dispatch(int ns, const float* __restrict__ o_part,
+                                                       const float* __restrict__ ml_part,
+                                                       size_t base0, size_t sstride, int i4) {
+  switch (ns) {
+    case 1: return merge_fixed<HD, 1>(o_part, ml_part, base0, sstride, i4);
+    case 2: return merge_fixed<HD, 2>(o_part, ml_part, base0, sstride, i4);
+    case 3: return merge_fixed<HD, 3>(o_part, ml_part, base0, sstride, i4);
+    case 4: return merge_fixed<HD, 4>(o_part, ml_part, base0, sstride, i4);
+    case 5: return merge_fixed<HD, 5>(o_part, ml_part, base0, sstride, i4);
+    case 6: return merge_fixed<HD, 6>(o_part, ml_part, base0, sstride, i4);
+    case 7: return merge_fixed<HD, 7>(o_part, ml_part, base0, sstride, i4);
+    case 8: return merge_fixed<HD, 8>(o_part, ml_part, base0, sstride, i4);
+    default: return make_float4(0.f, 0.f, 0.f, 0.f);   // no split covers the row
+  }
+}
+
+// Any split count (more than eight splits: the long-context plans).
+template <int HD>
+__device__ __forceinline__ float4 merge_loop(int ns, const float* __restrict__ o_part,
+                                             const float* __restrict__ ml_part, size_t base0,
+                                             size_t sstride, int i4) {
+  float M = -INFINITY;
+  for (int s = 0; s < ns; ++s) M = fmaxf(M, ml_part[(base0 + s * sstride) * 2]);
+  float lsum = 0.f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int s = 0; s < ns; ++s) {
+    const size_t base = base0 + s * sstride;
+    const float w = exp2f(ml_part[base * 2] - M);
+    lsum += w * ml_part[base * 2 + 1];
+    const float4 v = *reinterpret_cast<const float4*>(o_part + base * HD + (i4 * 4) % HD);
+    acc.x += w * v.x;
+    acc.y += w * v.y;
+    acc.z += w * v.z;
+    acc.w += w * v.w;
+  }
+  const float inv = 1.f / lsum;
+  return make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+}
+
 template <int HD>
 __global__ __launch_bounds__(256) void attn_merge_kernel(PassTable tb, int keys_per_split,
                                                          int n_split, int m_cap,
@@ -320,23 +393,11 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(PassTable tb, int keys_
   const int r = tb.row_req[m];
   const int L = tb.req_len[r];
   const int ns = min(n_split, (L + keys_per_split - 1) / keys_per_split);
-  float M = -INFINITY;
-  for (int s = 0; s < ns; ++s) M = fmaxf(M, ml_part[(((size_t)s * m_cap + m) * H + h) * 2]);
-  float lsum = 0.f;
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int s = 0; s < ns; ++s) {
-    const size_t base = ((size_t)s * m_cap + m) * H + h;
-    const float w = exp2f(ml_part[base * 2] - M);
-    lsum += w * ml_part[base * 2 + 1];
-    const float4 v = *reinterpret_cast<const float4*>(o_part + base * HD + (i4 * 4) % HD);
-    acc.x += w * v.x;
-    acc.y += w * v.y;
-    acc.z += w * v.z;
-    acc.w += w * v.w;
-  }
-  const float inv = 1.f / lsum;
-  *reinterpret_cast<float4*>(out + (size_t)m * H * HD + i4 * 4) =
-      make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+  const size_t base0 = (size_t)m * H + h;
+  const size_t sstride = (size_t)m_cap * H;   // between splits, in (m, h) records
+  const float4 res = ns <= 8 ? merge_fixed_dispatch<HD>(ns, o_part, ml_part, base0, sstride, i4)
+                             : merge_loop<HD>(ns, o_part, ml_part, base0, sstride, i4);
+  *reinterpret_cast<float4*>(out + (size_t)m * H * HD + i4 * 4) = res;
 }
 
 template <typename T, int HD, int QTW>

@@ -128,3 +128,55 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
 }
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+// ---------------------------------------------------------------------------
+// Split-K partial sums: acc[i] += sum over s < S of p[i][s * stride] (float4),
+// in split order, for NV vectors at once.  The split count is dispatched once
+// and every load of a group of up to eight splits is issued before any add:
+// a load under a runtime condition (or in a loop with a runtime trip count)
+// makes the compiler wait for all earlier loads where the paths join, which
+// turns S independent reads into S round trips.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void add4(float4& a, const float4& v) {
+  a.x += v.x;
+  a.y += v.y;
+  a.z += v.z;
+  a.w += v.w;
+}
+
+template <int NS, int NV>
+__device__ __forceinline__ void sum_splits_fixed(float4 (&acc)[NV], const float* const (&p)[NV],
+                                                 size_t off, size_t stride) {
+  float4 v[NV][NS];
+#pragma unroll
+  for (int k = 0; k < NS; ++k)
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
+      v[i][k] = *reinterpret_cast<const float4*>(p[i] + off + (size_t)k * stride);
+#pragma unroll
+  for (int i = 0; i < NV; ++i)
+#pragma unroll
+    for (int k = 0; k < NS; ++k) add4(acc[i], v[i][k]);
+}
+
+// G: most splits loaded at once (8, or less to bound the registers a
+// kernel with many vectors holds for the largest case).
+template <int NV, int G = 8>
+__device__ __forceinline__ void add_splits(float4 (&acc)[NV], const float* const (&p)[NV],
+                                           size_t stride, int S) {
+  static_assert(G >= 1 && G <= 8, "group of 1..8 splits");
+  int s = 0;
+  for (; S - s > G; s += G) sum_splits_fixed<G, NV>(acc, p, (size_t)s * stride, stride);
+  const size_t off = (size_t)s * stride;
+  switch (S - s) {
+    case 1: sum_splits_fixed<1, NV>(acc, p, off, stride); break;
+    case 2: if constexpr (G >= 2) sum_splits_fixed<2, NV>(acc, p, off, stride); break;
+    case 3: if constexpr (G >= 3) sum_splits_fixed<3, NV>(acc, p, off, stride); break;
+    case 4: if constexpr (G >= 4) sum_splits_fixed<4, NV>(acc, p, off, stride); break;
+    case 5: if constexpr (G >= 5) sum_splits_fixed<5, NV>(acc, p, off, stride); break;
+    case 6: if constexpr (G >= 6) sum_splits_fixed<6, NV>(acc, p, off, stride); break;
+    case 7: if constexpr (G >= 7) sum_splits_fixed<7, NV>(acc, p, off, stride); break;
+    case 8: if constexpr (G >= 8) sum_splits_fixed<8, NV>(acc, p, off, stride); break;
+    default: break;
+  }
+}

@@ -185,24 +185,34 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(
   const int m = idx / d4;
   const int i = idx % d4;
   if (m >= min(*nrows, m_cap)) return;
-  float4 acc = reinterpret_cast<float4*>(x + (size_t)m * d)[i];
-  for (int s = 0; s < S; ++s) {
-    const float4 v = *reinterpret_cast<const float4*>(P + s * p_stride + (size_t)m * d + 4 * i);
-    acc.x += v.x;
-    acc.y += v.y;
-    acc.z += v.z;
-    acc.w += v.w;
+  float4 acc[1] = {reinterpret_cast<float4*>(x + (size_t)m * d)[i]};
+  const float* const pp[1] = {P + (size_t)m * d + 4 * i};
+  add_splits<1>(acc, pp, p_stride, S);
+  // expert slots: indices and gates first, then every slot's row load, then
+  // the sum in slot order (top_k <= 8; slots past top_k repeat the last one
+  // and are not added)
+  int pk[kMaxTopK];
+  float gk[kMaxTopK];
+#pragma unroll
+  for (int k = 0; k < kMaxTopK; ++k) {
+    const size_t slot = (size_t)m * top_k + min(k, top_k - 1);
+    pk[k] = pos[slot];
+    gk[k] = gate[slot];
   }
-  for (int k = 0; k < top_k; ++k) {
-    const float gk = gate[(size_t)m * top_k + k];
-    const float4 v =
-        *reinterpret_cast<const float4*>(Y + (size_t)pos[(size_t)m * top_k + k] * d + 4 * i);
-    acc.x += gk * v.x;
-    acc.y += gk * v.y;
-    acc.z += gk * v.z;
-    acc.w += gk * v.w;
-  }
-  reinterpret_cast<float4*>(x + (size_t)m * d)[i] = acc;
+  float4 v[kMaxTopK];
+#pragma unroll
+  for (int k = 0; k < kMaxTopK; ++k)
+    v[k] = *reinterpret_cast<const float4*>(Y + (size_t)pk[k] * d + 4 * i);
+  float4 a = acc[0];
+#pragma unroll
+  for (int k = 0; k < kMaxTopK; ++k)
+    if (k < top_k) {
+      a.x += gk[k] * v[k].x;
+      a.y += gk[k] * v[k].y;
+      a.z += gk[k] * v[k].z;
+      a.w += gk[k] * v[k].w;
+    }
+  reinterpret_cast<float4*>(x + (size_t)m * d)[i] = a;
 }
 
 }  // namespace

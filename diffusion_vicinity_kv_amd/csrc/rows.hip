@@ -34,45 +34,50 @@ __global__ __launch_bounds__(kThreads) void embed_kernel(PassTable tb, const int
   const bool soft = alpha != 0.f && tok == mask_id && j >= 0 && j < B &&
                     smooth_valid[r * B + j] != 0;
   float* xr = x + (size_t)m * d;
+  constexpr int EV = 16 / sizeof(T);   // elements per 16-byte vector (d % EV == 0)
   if (!soft) {
     const T* e = emb + (size_t)tok * d;
-    for (int i = threadIdx.x; i < d; i += kThreads) xr[i] = to_f(e[i]);
+    for (int c = threadIdx.x; c < d / EV; c += kThreads) {
+      const V16 v = ld16(e + c * EV);
+#pragma unroll
+      for (int q = 0; q < EV; q += 4)
+        *reinterpret_cast<float4*>(xr + c * EV + q) =
+            make_float4(v16_get<T>(v, q), v16_get<T>(v, q + 1), v16_get<T>(v, q + 2),
+                        v16_get<T>(v, q + 3));
+    }
     return;
   }
+  // an id outside [0, V) contributes nothing: it reads the MASK row with
+  // weight 0, so that the eight rows' loads of a vector are issued together
   const int* ids = smooth_id + (size_t)(r * B + j) * 8;
   const float* ps = smooth_p + (size_t)(r * B + j) * 8;
   const T* em = emb + (size_t)mask_id * d;
-  for (int i = threadIdx.x; i < d; i += kThreads) {
-    float s = 0.f;
+  const T* er[8];
+  float pk[8];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const int id = ids[k];
-      if (id >= 0 && id < V) s += ps[k] * to_f(emb[(size_t)id * d + i]);
+  for (int k = 0; k < 8; ++k) {
+    const int id = ids[k];
+    const bool ok = id >= 0 && id < V;
+    er[k] = emb + (size_t)(ok ? id : mask_id) * d;
+    pk[k] = ok ? ps[k] : 0.f;
+  }
+  for (int c = threadIdx.x; c < d / EV; c += kThreads) {
+    const V16 mv = ld16(em + c * EV);
+    V16 ev[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) ev[k] = ld16(er[k] + c * EV);
+    float o[EV];
+#pragma unroll
+    for (int q = 0; q < EV; ++q) {
+      float sm = 0.f;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) sm += pk[k] * v16_get<T>(ev[k], q);
+      o[q] = (1.f - alpha) * v16_get<T>(mv, q) + alpha * sm;
     }
-    xr[i] = (1.f - alpha) * to_f(em[i]) + alpha * s;
-  }
-}
-
-// init + sum over s < S of p[s * stride] (float4), in split order.  Up to
-// eight partials are loaded before any is added so that their latencies
-// overlap.
-__device__ __forceinline__ float4 add_partials4(float4 acc, const float* p, size_t stride, int S) {
-  for (int s0 = 0; s0 < S; s0 += 8) {
-    const int n = min(8, S - s0);
-    float4 v[8];
 #pragma unroll
-    for (int k = 0; k < 8; ++k)
-      if (k < n) v[k] = *reinterpret_cast<const float4*>(p + (s0 + k) * stride);
-#pragma unroll
-    for (int k = 0; k < 8; ++k)
-      if (k < n) {
-        acc.x += v[k].x;
-        acc.y += v[k].y;
-        acc.z += v[k].z;
-        acc.w += v[k].w;
-      }
+    for (int q = 0; q < EV; q += 4)
+      *reinterpret_cast<float4*>(xr + c * EV + q) = make_float4(o[q], o[q + 1], o[q + 2], o[q + 3]);
   }
-  return acc;
 }
 
 constexpr int kNormThreads = 1024;
@@ -80,40 +85,63 @@ constexpr int kNormThreads = 1024;
 // x[m] += sum_s P[s][m] (split order); a[m] = x[m] / sqrt(mean(x^2) + eps) * g.
 // One workgroup of 1024 threads per row, one float4 (d <= 4096) or two per
 // thread.
-template <typename T>
+// Sum of squares of one row after its split-K partials are added, NV float4
+// per thread (threads past the row end read its last vector and add nothing).
+template <int NV>
+__device__ __forceinline__ float load_row(float4 (&v)[NV], const float* xrow, const float* prow,
+                                          int S, size_t p_stride, int d4) {
+  const float* pp[NV];
+#pragma unroll
+  for (int e = 0; e < NV; ++e) {
+    const int i = min((int)threadIdx.x + e * kNormThreads, d4 - 1);
+    v[e] = reinterpret_cast<const float4*>(xrow)[i];
+    pp[e] = prow + 4 * i;
+  }
+  add_splits<NV>(v, pp, p_stride, S);
+  float ss = 0.f;
+#pragma unroll
+  for (int e = 0; e < NV; ++e)
+    if ((int)threadIdx.x + e * kNormThreads < d4)
+      ss += v[e].x * v[e].x + v[e].y * v[e].y + v[e].z * v[e].z + v[e].w * v[e].w;
+  return ss;
+}
+
+// out[i] = v * inv * g for this thread's in-range vectors
+template <typename T, int NV>
+__device__ __forceinline__ void store_norm(float4* orow, const float4 (&v)[NV], float inv,
+                                           const T* __restrict__ g, int d4) {
+#pragma unroll
+  for (int e = 0; e < NV; ++e) {
+    const int i = threadIdx.x + e * kNormThreads;
+    if (i < d4) {
+      const T* gi = g + 4 * i;
+      orow[i] = make_float4(v[e].x * inv * to_f(gi[0]), v[e].y * inv * to_f(gi[1]),
+                            v[e].z * inv * to_f(gi[2]), v[e].w * inv * to_f(gi[3]));
+    }
+  }
+}
+
+// x[m] += sum_s P[s][m] (split order); a[m] = rmsnorm(x[m]) * g.  One row per
+// workgroup, NV = ceil(d / 4096) float4 per thread.
+template <typename T, int NV>
 __global__ __launch_bounds__(kNormThreads) void add_rmsnorm_kernel(
     const int* __restrict__ nrows, int m_cap, float* __restrict__ x, const float* __restrict__ P,
     int S, size_t p_stride, const T* __restrict__ g, float eps, float* __restrict__ a, int d) {
-  constexpr int MAXV = 2;   // d <= 8192
   __shared__ float red[kNormThreads / 64];
   const int m = blockIdx.x;
   if (m >= min(*nrows, m_cap)) return;
   const int d4 = d / 4;
-  float4* xr = reinterpret_cast<float4*>(x + (size_t)m * d);
-  float4 v[MAXV];
-  float ss = 0.f;
+  float4 v[NV];
+  const float ss = load_row<NV>(v, x + (size_t)m * d, P + (size_t)m * d, S, p_stride, d4);
+  if (S > 0) {
+    float4* xr = reinterpret_cast<float4*>(x + (size_t)m * d);
 #pragma unroll
-  for (int e = 0; e < MAXV; ++e) {
-    const int i = threadIdx.x + e * kNormThreads;
-    if (i < d4) {
-      float4 xv = add_partials4(xr[i], P + (size_t)m * d + 4 * i, p_stride, S);
-      if (S > 0) xr[i] = xv;
-      v[e] = xv;
-      ss += xv.x * xv.x + xv.y * xv.y + xv.z * xv.z + xv.w * xv.w;
-    }
+    for (int e = 0; e < NV; ++e)
+      if ((int)threadIdx.x + e * kNormThreads < d4) xr[threadIdx.x + e * kNormThreads] = v[e];
   }
   const float tot = block_sum<kNormThreads / 64>(ss, red);
   const float inv = 1.f / sqrtf(tot / d + eps);
-  float4* ar = reinterpret_cast<float4*>(a + (size_t)m * d);
-#pragma unroll
-  for (int e = 0; e < MAXV; ++e) {
-    const int i = threadIdx.x + e * kNormThreads;
-    if (i < d4) {
-      const T* gi = g + 4 * i;
-      ar[i] = make_float4(v[e].x * inv * to_f(gi[0]), v[e].y * inv * to_f(gi[1]),
-                          v[e].z * inv * to_f(gi[2]), v[e].w * inv * to_f(gi[3]));
-    }
-  }
+  store_norm<T, NV>(reinterpret_cast<float4*>(a + (size_t)m * d), v, inv, g, d4);
 }
 
 // QKV: sum the split-K partials, rotate q and k (pair (j, j+hd/2) by the
@@ -128,7 +156,7 @@ __global__ __launch_bounds__(kNormThreads) void add_rmsnorm_kernel(
 constexpr int kQkvRows = 8;
 constexpr int kQkvThreads = 128;
 
-template <typename T>
+template <typename T, int G>
 __global__ __launch_bounds__(kQkvThreads) void qkv_rope_scatter_kernel(
     PassTable tb, int m_cap, const float* __restrict__ P, int S, size_t p_stride, int d, int H,
     int hd, const float* __restrict__ rope_cs, float* __restrict__ q_out, T* __restrict__ kc,
@@ -152,12 +180,11 @@ __global__ __launch_bounds__(kQkvThreads) void qkv_rope_scatter_kernel(
     for (int j = (threadIdx.x % 16) * 4; j < half; j += 64) {
       const int c0 = h * hd + j;
       const int c1 = c0 + half;
-      const float4 q0 = add_partials4(z4, pr + c0, p_stride, S);
-      const float4 q1 = add_partials4(z4, pr + c1, p_stride, S);
-      const float4 k0 = add_partials4(z4, pr + d + c0, p_stride, S);
-      const float4 k1 = add_partials4(z4, pr + d + c1, p_stride, S);
-      const float4 v0 = add_partials4(z4, pr + 2 * d + c0, p_stride, S);
-      const float4 v1 = add_partials4(z4, pr + 2 * d + c1, p_stride, S);
+      float4 t[6] = {z4, z4, z4, z4, z4, z4};
+      const float* const pp[6] = {pr + c0, pr + c1, pr + d + c0, pr + d + c1, pr + 2 * d + c0,
+                                  pr + 2 * d + c1};
+      add_splits<6, G>(t, pp, p_stride, S);
+      const float4 q0 = t[0], q1 = t[1], k0 = t[2], k1 = t[3], v0 = t[4], v1 = t[5];
       const float4 c = *reinterpret_cast<const float4*>(cs + j);
       const float4 sn = *reinterpret_cast<const float4*>(cs + half + j);
       *reinterpret_cast<float4*>(qr + j) =
@@ -200,6 +227,7 @@ __global__ __launch_bounds__(kQkvThreads) void qkv_rope_scatter_kernel(
 
 // act[m][f] = silu(gate) * up with gate, up summed over the split-K partials
 // of the fused [gate | up] projection (float4 per thread).
+template <int G>
 __global__ __launch_bounds__(kThreads) void swiglu_kernel(const int* __restrict__ nrows, int m_cap,
                                                           const float* __restrict__ P, int S,
                                                           size_t p_stride, int F,
@@ -213,8 +241,10 @@ __global__ __launch_bounds__(kThreads) void swiglu_kernel(const int* __restrict_
     const size_t m = idx / F4;
     const size_t f = (idx % F4) * 4;
     const float* pr = P + m * 2 * F;
-    const float4 g = add_partials4(z4, pr + f, p_stride, S);
-    const float4 u = add_partials4(z4, pr + F + f, p_stride, S);
+    float4 t[2] = {z4, z4};
+    const float* const pp[2] = {pr + f, pr + F + f};
+    add_splits<2, G>(t, pp, p_stride, S);
+    const float4 g = t[0], u = t[1];
     *reinterpret_cast<float4*>(act + m * F + f) =
         make_float4(g.x / (1.f + expf(-g.x)) * u.x, g.y / (1.f + expf(-g.y)) * u.y,
                     g.z / (1.f + expf(-g.z)) * u.z, g.w / (1.f + expf(-g.w)) * u.w);
@@ -223,13 +253,12 @@ __global__ __launch_bounds__(kThreads) void swiglu_kernel(const int* __restrict_
 
 // Block rows only: residual add of the last layer, final RMSNorm, and the
 // row's planting for the vocab statistics.
-template <typename T>
+template <typename T, int NV>
 __global__ __launch_bounds__(kNormThreads) void final_norm_kernel(
     PassTable tb, int B, const float* __restrict__ x, const float* __restrict__ P, int S,
     size_t p_stride, const T* __restrict__ g, float eps, float* __restrict__ out, int d,
     const int* __restrict__ plant_id, const float* __restrict__ plant_bias, int max_len,
     int* __restrict__ row_plant_id, float* __restrict__ row_plant_bias) {
-  constexpr int MAXV = 2;
   __shared__ float red[kNormThreads / 64];
   const int rr = blockIdx.x;
   const int r = rr / B;
@@ -248,29 +277,11 @@ __global__ __launch_bounds__(kNormThreads) void final_norm_kernel(
   const int lo = tb.row_pos[off];
   const int bs = tb.req_bs[r];
   const int m = off + (bs - lo) + j;
-  const float4* xr = reinterpret_cast<const float4*>(x + (size_t)m * d);
-  float4 v[MAXV];
-  float ss = 0.f;
-#pragma unroll
-  for (int e = 0; e < MAXV; ++e) {
-    const int i = threadIdx.x + e * kNormThreads;
-    if (i < d4) {
-      const float4 xv = add_partials4(xr[i], P + (size_t)m * d + 4 * i, p_stride, S);
-      v[e] = xv;
-      ss += xv.x * xv.x + xv.y * xv.y + xv.z * xv.z + xv.w * xv.w;
-    }
-  }
+  float4 v[NV];
+  const float ss = load_row<NV>(v, x + (size_t)m * d, P + (size_t)m * d, S, p_stride, d4);
   const float tot = block_sum<kNormThreads / 64>(ss, red);
   const float inv = 1.f / sqrtf(tot / d + eps);
-#pragma unroll
-  for (int e = 0; e < MAXV; ++e) {
-    const int i = threadIdx.x + e * kNormThreads;
-    if (i < d4) {
-      const T* gi = g + 4 * i;
-      orow[i] = make_float4(v[e].x * inv * to_f(gi[0]), v[e].y * inv * to_f(gi[1]),
-                            v[e].z * inv * to_f(gi[2]), v[e].w * inv * to_f(gi[3]));
-    }
-  }
+  store_norm<T, NV>(orow, v, inv, g, d4);
   if (threadIdx.x == 0) {
     row_plant_id[rr] = plant_id ? plant_id[(size_t)r * max_len + bs + j] : -1;
     row_plant_bias[rr] = plant_bias ? plant_bias[r] : 0.f;
@@ -292,6 +303,7 @@ hipError_t launch_embed(DType t, PassTable tb, int m_cap, const int* tokens, int
                         const void* emb, int d, int V, int mask_id, float alpha, const int* smooth_id,
                         const float* smooth_p, const uint8_t* smooth_valid, int B, float* x,
                         hipStream_t st) {
+  if (d % 8 != 0) return hipErrorInvalidValue;   // whole 16-byte vectors per row
   DISPATCH_T(t, hipLaunchKernelGGL((embed_kernel<T>), dim3(m_cap), dim3(kThreads), 0, st, tb,
                                    tokens, max_len, static_cast<const T*>(emb), d, V, mask_id, alpha,
                                    smooth_id, smooth_p, smooth_valid, B, x));
@@ -302,9 +314,15 @@ hipError_t launch_add_rmsnorm(DType t, const int* nrows, int m_cap, float* x, co
                               int S, size_t p_stride, const void* g, float eps, float* a, int d,
                               hipStream_t st) {
   if (d > 8 * kNormThreads || d % 4 != 0) return hipErrorInvalidValue;
-  DISPATCH_T(t, hipLaunchKernelGGL((add_rmsnorm_kernel<T>), dim3(m_cap), dim3(kNormThreads), 0, st,
-                                   nrows, m_cap, x, P, S, p_stride, static_cast<const T*>(g), eps,
-                                   a, d));
+  if (d <= 4 * kNormThreads) {
+    DISPATCH_T(t, hipLaunchKernelGGL((add_rmsnorm_kernel<T, 1>), dim3(m_cap), dim3(kNormThreads),
+                                     0, st, nrows, m_cap, x, P, S, p_stride,
+                                     static_cast<const T*>(g), eps, a, d));
+  } else {
+    DISPATCH_T(t, hipLaunchKernelGGL((add_rmsnorm_kernel<T, 2>), dim3(m_cap), dim3(kNormThreads),
+                                     0, st, nrows, m_cap, x, P, S, p_stride,
+                                     static_cast<const T*>(g), eps, a, d));
+  }
   return hipGetLastError();
 }
 
@@ -313,9 +331,16 @@ hipError_t launch_qkv_rope_scatter(DType t, PassTable tb, int m_cap, const float
                                    float* q_out, void* kc, void* vt, int Lp, hipStream_t st) {
   if (hd > 128 || hd % 8 != 0) return hipErrorInvalidValue;
   const dim3 grid((m_cap + kQkvRows - 1) / kQkvRows, H);
-  DISPATCH_T(t, hipLaunchKernelGGL((qkv_rope_scatter_kernel<T>), grid, dim3(kQkvThreads), 0, st,
-                                   tb, m_cap, P, S, p_stride, d, H, hd, rope_cs, q_out,
-                                   static_cast<T*>(kc), static_cast<T*>(vt), Lp));
+  // unsplit input (many-row passes): a small register set keeps occupancy up
+  if (S <= 1) {
+    DISPATCH_T(t, hipLaunchKernelGGL((qkv_rope_scatter_kernel<T, 1>), grid, dim3(kQkvThreads), 0,
+                                     st, tb, m_cap, P, S, p_stride, d, H, hd, rope_cs, q_out,
+                                     static_cast<T*>(kc), static_cast<T*>(vt), Lp));
+  } else {
+    DISPATCH_T(t, hipLaunchKernelGGL((qkv_rope_scatter_kernel<T, 8>), grid, dim3(kQkvThreads), 0,
+                                     st, tb, m_cap, P, S, p_stride, d, H, hd, rope_cs, q_out,
+                                     static_cast<T*>(kc), static_cast<T*>(vt), Lp));
+  }
   return hipGetLastError();
 }
 
@@ -325,8 +350,12 @@ hipError_t launch_swiglu(const int* nrows, int m_cap, const float* P, int S, siz
   size_t total = (size_t)m_cap * F / 4;
   int blocks = (int)((total + kThreads - 1) / kThreads);
   if (blocks > 8192) blocks = 8192;
-  hipLaunchKernelGGL(swiglu_kernel, dim3(blocks), dim3(kThreads), 0, st, nrows, m_cap, P, S,
-                     p_stride, F, act);
+  if (S <= 1)   // unsplit input (many-row passes): fewer registers, more waves
+    hipLaunchKernelGGL(swiglu_kernel<1>, dim3(blocks), dim3(kThreads), 0, st, nrows, m_cap, P, S,
+                       p_stride, F, act);
+  else
+    hipLaunchKernelGGL(swiglu_kernel<8>, dim3(blocks), dim3(kThreads), 0, st, nrows, m_cap, P, S,
+                       p_stride, F, act);
   return hipGetLastError();
 }
 
@@ -336,10 +365,17 @@ hipError_t launch_final_norm(DType t, PassTable tb, int batch, int B, const floa
                              int max_len, int* row_plant_id, float* row_plant_bias,
                              hipStream_t st) {
   if (d > 8 * kNormThreads || d % 4 != 0) return hipErrorInvalidValue;
-  DISPATCH_T(t, hipLaunchKernelGGL((final_norm_kernel<T>), dim3(batch * B), dim3(kNormThreads), 0, st,
-                                   tb, B, x, P, S, p_stride, static_cast<const T*>(g), eps,
-                                   out, d, plant_id, plant_bias, max_len,
-                                   row_plant_id, row_plant_bias));
+  if (d <= 4 * kNormThreads) {
+    DISPATCH_T(t, hipLaunchKernelGGL((final_norm_kernel<T, 1>), dim3(batch * B), dim3(kNormThreads),
+                                     0, st, tb, B, x, P, S, p_stride, static_cast<const T*>(g), eps,
+                                     out, d, plant_id, plant_bias, max_len, row_plant_id,
+                                     row_plant_bias));
+  } else {
+    DISPATCH_T(t, hipLaunchKernelGGL((final_norm_kernel<T, 2>), dim3(batch * B), dim3(kNormThreads),
+                                     0, st, tb, B, x, P, S, p_stride, static_cast<const T*>(g), eps,
+                                     out, d, plant_id, plant_bias, max_len, row_plant_id,
+                                     row_plant_bias));
+  }
   return hipGetLastError();
 }
 

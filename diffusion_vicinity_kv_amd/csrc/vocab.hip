@@ -111,31 +111,36 @@ __global__ __launch_bounds__(kThreads) void vocab_partial_kernel(
     tv[k] = -INFINITY;
     ti[k] = INT_MAX;
   }
-  for (int base = c0 + 4 * threadIdx.x; base < c1; base += 4 * kThreads) {
-    float4 x4;
-    if (base + 3 < c1) {
-      x4 = *reinterpret_cast<const float4*>(z + base);
-    } else {
-      x4.x = z[base];
-      x4.y = base + 1 < c1 ? z[base + 1] : -INFINITY;
-      x4.z = base + 2 < c1 ? z[base + 2] : -INFINITY;
-      x4.w = -INFINITY;
-    }
-    float xs[4] = {x4.x, x4.y, x4.z, x4.w};
+  // c0, c1 and V are multiples of 4, so every float4 lies wholly inside or
+  // outside the split.  Four float4 per thread are loaded before any is used
+  // (clamped into the split; the extra ones are skipped), in increasing id
+  // order per thread.
+  constexpr int kU = 4;
+  for (int b0 = c0 + 4 * threadIdx.x; b0 < c1; b0 += 4 * kThreads * kU) {
+    float4 xv[kU];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int id = base + e;
-      float v = xs[e];
-      if (id == pid) v += pb;
-      if (id == mask_id || id >= c1) v = -INFINITY;
-      if (v == -INFINITY) continue;
-      if (v > m) {
-        s = s * exp2f((m - v) * kLog2e) + 1.f;
-        m = v;
-      } else {
-        s += exp2f((v - m) * kLog2e);
+    for (int u = 0; u < kU; ++u)
+      xv[u] = *reinterpret_cast<const float4*>(z + min(b0 + u * 4 * kThreads, c1 - 4));
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int base = b0 + u * 4 * kThreads;
+      if (base >= c1) break;
+      const float xs[4] = {xv[u].x, xv[u].y, xv[u].z, xv[u].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int id = base + e;
+        float v = xs[e];
+        if (id == pid) v += pb;
+        if (id == mask_id) v = -INFINITY;
+        if (v == -INFINITY) continue;
+        if (v > m) {
+          s = s * exp2f((m - v) * kLog2e) + 1.f;
+          m = v;
+        } else {
+          s += exp2f((v - m) * kLog2e);
+        }
+        insert_top8(tv, ti, v, id);
       }
-      insert_top8(tv, ti, v, id);
     }
   }
   // workgroup merge: (max, sum) then top-8
