@@ -59,7 +59,7 @@ def source_hash() -> str:
     return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
 
 
-def dominant_kernel_timing(wc, weights, iters=40, with_events=True):
+def dominant_kernel_timing(wc, weights, iters=40):
     """Average launch time and bytes of the QKV / gate|up projections at the
     step's row count, alternating over rotating layers."""
     import torch
@@ -84,21 +84,28 @@ def dominant_kernel_timing(wc, weights, iters=40, with_events=True):
     for W in shapes[:4]:
         B.linear(A, W, out)
     torch.cuda.synchronize()
+    # the launches replayed from one captured graph, back to back on one
+    # stream as in the step's own graph: events around the replays time the
+    # kernels, not the host's launch rate (which a profiler slows down)
+    cap = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=cap):
+        for W in shapes:
+            B.linear(A, W, out)
     st = torch.cuda.current_stream()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in shapes]
-    nbytes = 0
-    nflops = 0
-    for W, (e0, e1) in zip(shapes, evs):
-        N = W.shape[0]
-        e0.record(st)
-        B.linear(A, W, out)
-        e1.record(st)
-        nbytes += N * d * 2 + rows * d * 4 + rows * N * 4
-        nflops += 2 * rows * N * d
+    g.replay()
     torch.cuda.synchronize()
-    ms = [e0.elapsed_time(e1) for e0, e1 in evs]
-    avg_ms = sum(ms) / len(ms)
+    reps = 3
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(st)
+    for _ in range(reps):
+        g.replay()
+    e1.record(st)
+    torch.cuda.synchronize()
+    avg_ms = e0.elapsed_time(e1) / (reps * len(shapes))
+    nbytes = sum(W.shape[0] * d * 2 + rows * d * 4 + rows * W.shape[0] * 4 for W in shapes)
+    nflops = sum(2 * rows * W.shape[0] * d for W in shapes)
+    del g
     return avg_ms, nbytes / len(shapes), nflops / len(shapes), rows
 
 

@@ -97,7 +97,7 @@ def load(path: str = LIB_PATH) -> C.CDLL:
         "dinfer_vocab_stats_scratch_bytes": (sz, [i32, i32]),
         "dinfer_vocab_stats": (i32, [vp, i32, i32, vp, vp, i32, vp, vp, vp, vp, vp, vp, sz, vp]),
         "dinfer_step_graph": (i32, [vp, i32]),
-        "dinfer_pack_linear": (i32, [vp, vp, C.c_int64, i32, i32, vp]),
+        "dinfer_pack_linear": (i32, [vp, vp, i32, i32, i32, i32, vp]),
         "dinfer_linear_out_elems": (sz, [i32, i32, i32, i32]),
         "dinfer_linear": (i32, [vp, vp, vp, i32, i32, i32, i32, C.POINTER(i32), vp]),
         "dinfer_status_str": (C.c_char_p, [i32]),
@@ -140,9 +140,10 @@ def pack_linear(W, stream=None):
     import torch
     lib = load()
     assert W.is_contiguous() and W.dtype in (torch.float32, torch.bfloat16)
+    assert W.dim() in (2, 3)
     out = torch.empty_like(W)
-    K = W.shape[-1]
-    check(lib.dinfer_pack_linear(ptr(W), ptr(out), W.numel() // K, K,
+    n_mats = W.shape[0] if W.dim() == 3 else 1
+    check(lib.dinfer_pack_linear(ptr(W), ptr(out), n_mats, W.shape[-2], W.shape[-1],
                                  F32 if W.dtype == torch.float32 else BF16,
                                  stream_handle(stream)), "dinfer_pack_linear")
     return out

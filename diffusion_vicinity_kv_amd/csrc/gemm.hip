@@ -8,12 +8,14 @@
 // the weights' own precision only (no activation rounding), for one extra
 // MFMA per weight fragment -- free wherever the layer is a weight stream.
 //
-// Weights are read in a packed layout (pack_linear below): the 1 KB MFMA B
-// operand of every 16 rows x KSTEP columns is stored contiguously, in lane
-// order, so that each weight load of a wave is one contiguous kilobyte --
-// whole 128-byte lines, sequential along K.  Read row-major, each load would
-// touch 64 bytes of 16 different rows and the vector L1 would issue twice as
-// many half-line requests, stalling the address unit.
+// Weights are read in a packed layout (pack_kernel below; gemm_split.h): the
+// 1 KB MFMA B operand of every 16 rows x KSTEP columns is stored
+// contiguously, in lane order, so that each weight load of a wave is one
+// contiguous kilobyte -- whole 128-byte lines -- and the blocks of a 256-row
+// tile follow each other k-step by k-step, so that a workgroup's weight
+// stream is one sequential run.  Read row-major, each load would touch 64
+// bytes of 16 different rows and the vector L1 would issue twice as many
+// half-line requests, stalling the address unit.
 //
 // Kernels:
 //  * skinny (M <= 128): the vicinity window holds tens of rows, so a layer is
@@ -43,12 +45,12 @@ namespace {
 // >= M are read as zeros (exact-size operands of the standalone entry point).
 //
 // One workgroup's tile: rows [0, M) of A (row r at A + (arow ? arow[r] : r) * K)
-// times weight rows [n_tile, n_tile + 16*NT*NW) of W over K chunks
+// times weight rows [n_tile, n_tile + 16*NT*NW) of W (N rows) over K chunks
 // [c_begin, c_end), written to out[row * ldo + column].
 template <typename TW, int MT, int NT, int NW, bool GUARD>
 __device__ __forceinline__ void skinny_tile(const float* __restrict__ A,
                                             const int* __restrict__ arow, int M,
-                                            const TW* __restrict__ W, int K,
+                                            const TW* __restrict__ W, int N, int K,
                                             float* __restrict__ out, int ldo, int n_tile,
                                             int c_begin, int c_end) {
   using MF = Mfma<TW>;
@@ -78,12 +80,16 @@ __device__ __forceinline__ void skinny_tile(const float* __restrict__ A,
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  // packed weights: block (16-row group, vector step) of 64 * VEC elements
+  // packed weights: block (16-row group, vector step) of 64 * VEC elements;
+  // a wave's groups sit in one tile, so they share the k-step stride
   constexpr int BE = 64 * VEC;
+  const int KS = K / KSTEP;
+  const int NG = N / 16;
+  const size_t wstep = (size_t)packed_kstride(n0 / 16, NG) * BE;
   const TW* wrow[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt)
-    wrow[nt] = W + (size_t)(n0 / 16 + nt) * (K / KSTEP) * BE + lane * VEC;
+    wrow[nt] = W + packed_block(n0 / 16 + nt, 0, KS, NG) * BE + lane * VEC;
 
   // Weight fragments and raw activations of three consecutive chunks live in
   // registers.  At chunk c the loads of chunk c+2 are issued (activations
@@ -99,7 +105,7 @@ __device__ __forceinline__ void skinny_tile(const float* __restrict__ A,
 #pragma unroll
     for (int j = 0; j < U; ++j)
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) b[j][nt] = ld16(wrow[nt] + (size_t)(c * U + j) * BE);
+      for (int nt = 0; nt < NT; ++nt) b[j][nt] = ld16(wrow[nt] + (c * U + j) * wstep);
   };
   auto load_a = [&](float4 (&areg)[AV], int c) {
 #pragma unroll
@@ -214,7 +220,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(const float* __res
   const int split = bid / n_tiles;
   const int C = K / KC;
   const int M = m_dev ? min(*m_dev, m_cap) : m_cap;
-  skinny_tile<TW, MT, NT, NW, GUARD>(A, nullptr, M, W, K, P + (size_t)split * m_cap * N, N,
+  skinny_tile<TW, MT, NT, NW, GUARD>(A, nullptr, M, W, N, K, P + (size_t)split * m_cap * N, N,
                                      tile * (16 * NT * NW), (split * C) / S, ((split + 1) * C) / S);
 }
 
@@ -238,29 +244,31 @@ __global__ __launch_bounds__(NW * 64) void gemm_grouped_kernel(
   const int base = e_off[e] + mt * 64;
   const float* a = row_of ? A : A + (size_t)base * K;
   const int* ar = row_of ? row_of + base : nullptr;
-  skinny_tile<TW, 4, NT, NW, true>(a, ar, M, W + (size_t)e * N * K, K, out + (size_t)base * N, N,
+  skinny_tile<TW, 4, NT, NW, true>(a, ar, M, W + (size_t)e * N * K, N, K, out + (size_t)base * N, N,
                                    tile * (16 * NT * NW), 0, K / KC);
 }
 
 
-// Packs W [N][K] (row-major) into the block layout the GEMMs read: block
-// (g = n / 16, s = k / KSTEP) holds 64 * VEC elements at offset
-// (g * K / KSTEP + s) * 64 * VEC, and its lane 16 * q + c slot holds
-// W[16 g + c][s * KSTEP + q * VEC, + VEC) -- the MFMA operand of that lane.
-// A stack of E matrices [E][N][K] packs as one [E*N][K] matrix.
+// Packs W [N][K] (row-major; blockIdx.y selects one of a stack of such
+// matrices) into the block layout the GEMMs read (packed_block): block
+// (group g = n / 16, k-step s = k / KSTEP) holds 64 * VEC elements and its
+// slot 16 q + c holds W[16 g + c][s * KSTEP + q * VEC, + VEC) -- the MFMA
+// operand of lane 16 q + c.
 template <typename TW>
 __global__ __launch_bounds__(256) void pack_kernel(const TW* __restrict__ W, TW* __restrict__ P,
                                                    int N, int K) {
   constexpr int VEC = Mfma<TW>::VEC;
   constexpr int KSTEP = Mfma<TW>::KSTEP;
   const int KS = K / KSTEP;
-  const size_t blk = (size_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (blk >= (size_t)(N / 16) * KS) return;
+  const int NG = N / 16;
+  const size_t blk = (size_t)blockIdx.x * 4 + (threadIdx.x >> 6);   // source order: g, then s
+  if (blk >= (size_t)NG * KS) return;
+  const size_t mat = (size_t)blockIdx.y * N * K;
   const int lane = threadIdx.x & 63;
-  const size_t g = blk / KS;
+  const int g = (int)(blk / KS);
   const int s = (int)(blk % KS);
-  st16(P + blk * 64 * VEC + lane * VEC,
-       ld16(W + (g * 16 + (lane & 15)) * K + s * KSTEP + (lane >> 4) * VEC));
+  st16(P + mat + packed_block(g, s, KS, NG) * 64 * VEC + lane * VEC,
+       ld16(W + mat + ((size_t)g * 16 + (lane & 15)) * K + s * KSTEP + (lane >> 4) * VEC));
 }
 
 // ---------------------------------------------------------------------------
@@ -335,19 +343,20 @@ hipError_t launch_gemm_grouped(DType t, const float* A, const int* row_of, const
   return hipGetLastError();
 }
 
-hipError_t launch_pack_linear(DType t, const void* W, void* P, size_t N, int K, hipStream_t st) {
+hipError_t launch_pack_linear(DType t, const void* W, void* P, int n_mats, int N, int K,
+                              hipStream_t st) {
   const int kstep = t == DType::F32 ? Mfma<float>::KSTEP : Mfma<bf16>::KSTEP;
-  if (N % 16 != 0 || N > (size_t)INT32_MAX || K <= 0 || K % kstep != 0)
+  if (n_mats < 1 || n_mats > 65535 || N < 16 || N % 16 != 0 || K < kstep || K % kstep != 0)
     return hipErrorInvalidValue;
-  const size_t wgs = (N / 16 * (K / kstep) + 3) / 4;   // four 1 KB blocks per workgroup
-  if (wgs == 0) return hipSuccess;
+  const size_t wgs = ((size_t)(N / 16) * (K / kstep) + 3) / 4;   // four 1 KB blocks per workgroup
   if (wgs > (size_t)INT32_MAX) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)wgs, (unsigned)n_mats);
   if (t == DType::F32)
-    hipLaunchKernelGGL(pack_kernel<float>, dim3((unsigned)wgs), dim3(256), 0, st,
-                       static_cast<const float*>(W), static_cast<float*>(P), (int)N, K);
+    hipLaunchKernelGGL(pack_kernel<float>, grid, dim3(256), 0, st, static_cast<const float*>(W),
+                       static_cast<float*>(P), N, K);
   else
-    hipLaunchKernelGGL(pack_kernel<bf16>, dim3((unsigned)wgs), dim3(256), 0, st,
-                       static_cast<const bf16*>(W), static_cast<bf16*>(P), (int)N, K);
+    hipLaunchKernelGGL(pack_kernel<bf16>, grid, dim3(256), 0, st, static_cast<const bf16*>(W),
+                       static_cast<bf16*>(P), N, K);
   return hipGetLastError();
 }
 

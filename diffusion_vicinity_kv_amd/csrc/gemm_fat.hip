@@ -80,19 +80,23 @@ __global__ __launch_bounds__(128 * WN) void gemm_fat_kernel(const float* __restr
   }
   // weight vector v of a slab: block v / 64 = (16-column group, vector step),
   // lane slot v % 64; the slab's blocks sit in LDS in that order
+  const int KS = K / KSTEP;
+  const int NG = N / 16;
   const TW* wrow[BV];
+  size_t wstep[BV];   // elements between slabs
 #pragma unroll
   for (int i = 0; i < BV; ++i) {
     const int v = threadIdx.x + kFatThreads * i;
-    const int grp = min(n0 / 16 + (v / 64) / KK, N / 16 - 1);
-    wrow[i] = W + ((size_t)grp * (K / KSTEP) + (v / 64) % KK) * BE + (v % 64) * VEC;
+    const int grp = min(n0 / 16 + (v / 64) / KK, NG - 1);
+    wrow[i] = W + packed_block(grp, (v / 64) % KK, KS, NG) * BE + (v % 64) * VEC;
+    wstep[i] = (size_t)KK * packed_kstride(grp, NG) * BE;
   }
   auto gload = [&](float4 (&ra)[AV], V16 (&rb)[BV], int kt) {
     kt = min(kt, nk - 1);   // past the end: repeat the last slab
 #pragma unroll
     for (int i = 0; i < AV; ++i) ra[i] = *reinterpret_cast<const float4*>(arow[i] + kt * BK);
 #pragma unroll
-    for (int i = 0; i < BV; ++i) rb[i] = ld16(wrow[i] + (size_t)kt * KK * BE);
+    for (int i = 0; i < BV; ++i) rb[i] = ld16(wrow[i] + kt * wstep[i]);
   };
   auto sstore = [&](const float4 (&ra)[AV], const V16 (&rb)[BV], int buf) {
 #pragma unroll

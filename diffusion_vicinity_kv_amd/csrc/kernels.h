@@ -44,10 +44,12 @@ hipError_t launch_gemm(const GemmPlan& p, DType t, const float* A, const void* W
 // The fat kernel alone (M > 128): wn = 2 or 4 column waves (128 x 64*wn tiles).
 hipError_t launch_gemm_fat(DType t, int wn, const float* A, const void* W, float* out,
                            const int* m_dev, int m_cap, int N, int K, hipStream_t st);
-// W [N][K] row-major -> the packed block layout every GEMM here reads (16-row
-// groups x one MFMA vector step per 1 KB block, lane order).  N % 16 == 0,
-// K a multiple of the vector step (32 bf16 / 16 fp32); P must not alias W.
-hipError_t launch_pack_linear(DType t, const void* W, void* P, size_t N, int K, hipStream_t st);
+// n_mats matrices W [N][K] row-major -> the packed block layout every GEMM
+// here reads (gemm_split.h: 16-row groups x one MFMA vector step per 1 KB
+// block, 256-row tiles stored k-step by k-step).  N % 16 == 0, K a multiple
+// of the vector step (32 bf16 / 16 fp32); P must not alias W.
+hipError_t launch_pack_linear(DType t, const void* W, void* P, int n_mats, int N, int K,
+                              hipStream_t st);
 bool gemm_shape_ok(DType t, int N, int K);
 int gemm_k_chunk(DType t);
 // MoE experts: out[off_e + i] = A[row_of ? row_of[off_e + i] : off_e + i] * W[e]^T for

@@ -901,20 +901,21 @@ dinfer_status dinfer_get_step_view(const dinfer_ctx* c, dinfer_step_view* v) {
   return DINFER_OK;
 }
 
-dinfer_status dinfer_pack_linear(const void* d_W, void* d_packed, int64_t rows, int32_t K,
-                                 int32_t dtype, void* stream) {
+dinfer_status dinfer_pack_linear(const void* d_W, void* d_packed, int32_t n_mats, int32_t rows,
+                                 int32_t K, int32_t dtype, void* stream) {
   if (!d_W || !d_packed) return fail(DINFER_E_ARG, "null pointer");
   if (d_W == d_packed) return fail(DINFER_E_ARG, "packing in place is not supported");
   if (dtype != DINFER_F32 && dtype != DINFER_BF16) return fail(DINFER_E_ARG, "bad dtype");
   const DType dt = dtype == DINFER_F32 ? DType::F32 : DType::BF16;
   const int kstep = dt == DType::F32 ? 16 : 32;
-  if (rows < 16 || rows % 16 != 0 || rows > INT32_MAX) return fail(DINFER_E_ARG, "rows must be a positive multiple of 16");
+  if (n_mats < 1 || n_mats > 65535) return fail(DINFER_E_ARG, "n_mats must be in 1..65535");
+  if (rows < 16 || rows % 16 != 0) return fail(DINFER_E_ARG, "rows must be a positive multiple of 16");
   if (K < kstep || K % kstep != 0) return fail(DINFER_E_ARG, "K must be a positive multiple of 32 (bf16) / 16 (f32)");
-  const size_t bytes = (size_t)rows * K * dtype_size(dt);
+  const size_t bytes = (size_t)n_mats * rows * K * dtype_size(dt);
   const char* a = static_cast<const char*>(d_W);
   const char* b = static_cast<const char*>(d_packed);
   if (a < b + bytes && b < a + bytes) return fail(DINFER_E_ARG, "source and destination overlap");
-  HIP_TRY(launch_pack_linear(dt, d_W, d_packed, (size_t)rows, K, static_cast<hipStream_t>(stream)));
+  HIP_TRY(launch_pack_linear(dt, d_W, d_packed, n_mats, rows, K, static_cast<hipStream_t>(stream)));
   return DINFER_OK;
 }
 

@@ -246,17 +246,22 @@ dinfer_status dinfer_get_step_view(const dinfer_ctx* ctx, dinfer_step_view* out)
 dinfer_status dinfer_step_graph(dinfer_ctx* ctx, int32_t n_steps);
 
 /* Weight packing (a storage format of this library, not of the method):
- * copies d_W, a row-major [rows][K] matrix of the given dtype (a stack of E
- * matrices [E][N][K] is one [E*N][K] matrix), into d_packed (same byte size,
- * no overlap) in the layout every projection kernel reads.  Each 16-row group
- * and each run of 32 (bf16) / 16 (f32) columns becomes one contiguous 1 KB
- * block, blocks ordered by row group then column run; inside a block, 16-byte
- * slot 16*q + c holds row c of the group, columns q*VEC .. q*VEC+VEC-1 of the
- * run (VEC = 8 bf16 / 4 f32): the MFMA operand of lane 16*q + c, so that a
- * wave's weight load is one contiguous kilobyte.  rows % 16 == 0; K a
- * multiple of 32 (bf16) / 16 (f32).  Enqueued on stream. */
-dinfer_status dinfer_pack_linear(const void* d_W, void* d_packed, int64_t rows, int32_t K,
-                                 int32_t dtype, void* stream);
+ * copies d_W, a stack of n_mats row-major matrices [n_mats][rows][K] of the
+ * given dtype (one Linear [out][in] weight: n_mats = 1; MoE experts [E][N][K]:
+ * n_mats = E), into d_packed (same byte size, no overlap) in the layout every
+ * projection kernel reads; each matrix is packed on its own.  A block is the
+ * 1 KB MFMA operand of 16 rows (a group) x one run of 32 (bf16) / 16 (f32)
+ * columns: its 16-byte slot 16*q + c holds row c of the group, columns
+ * q*VEC .. q*VEC+VEC-1 of the run (VEC = 8 bf16 / 4 f32).  Groups form tiles
+ * of 16 (256 rows; the last tile may hold fewer); tile t's blocks are stored
+ * run by run, the tile's groups in order within a run, tiles one after the
+ * other: block (group g, run s) is at index 16*KS*(g/16) + s*G_t + g%16
+ * with KS = K/32 (bf16) or K/16 (f32) runs and G_t groups in g's tile.  A
+ * wave's weight load is then one contiguous kilobyte and a workgroup's
+ * weight stream one sequential run.  rows % 16 == 0; K a multiple of 32
+ * (bf16) / 16 (f32); n_mats <= 65535.  Enqueued on stream. */
+dinfer_status dinfer_pack_linear(const void* d_W, void* d_packed, int32_t n_mats, int32_t rows,
+                                 int32_t K, int32_t dtype, void* stream);
 
 /* Standalone projection, the Linear layer every step runs:
  * out[s][m][n] = sum over the s-th K slice of A[m][k] * W[n][k], with A an fp32

@@ -121,15 +121,17 @@ def test_pack_linear_argument_errors_without_gpu():
     """Every rejection happens before a launch (addresses are never touched)."""
     lib = B.load()
     a, b = 1 << 20, 1 << 40
-    assert lib.dinfer_pack_linear(None, b, 64, 128, B.BF16, None) == B.E_ARG
-    assert lib.dinfer_pack_linear(a, a, 64, 128, B.BF16, None) == B.E_ARG
-    assert lib.dinfer_pack_linear(a, a + 64 * 128, 64, 128, B.BF16, None) == B.E_ARG   # overlap
-    assert lib.dinfer_pack_linear(a, b, 40, 128, B.BF16, None) == B.E_ARG              # rows % 16
-    assert lib.dinfer_pack_linear(a, b, 0, 128, B.BF16, None) == B.E_ARG
-    assert lib.dinfer_pack_linear(a, b, 64, 48, B.BF16, None) == B.E_ARG               # K % 32
-    assert lib.dinfer_pack_linear(a, b, 64, 24, B.F32, None) == B.E_ARG                # K % 16
-    assert lib.dinfer_pack_linear(a, b, 64, 128, 7, None) == B.E_ARG
-    assert b"multiple" in lib.dinfer_last_error() or b"dtype" in lib.dinfer_last_error()
+    assert lib.dinfer_pack_linear(None, b, 1, 64, 128, B.BF16, None) == B.E_ARG
+    assert lib.dinfer_pack_linear(a, a, 1, 64, 128, B.BF16, None) == B.E_ARG
+    assert lib.dinfer_pack_linear(a, a + 64 * 128, 1, 64, 128, B.BF16, None) == B.E_ARG  # overlap
+    assert lib.dinfer_pack_linear(a, a + 64 * 128 * 2, 2, 64, 128, B.BF16, None) == B.E_ARG
+    assert lib.dinfer_pack_linear(a, b, 1, 40, 128, B.BF16, None) == B.E_ARG            # rows % 16
+    assert lib.dinfer_pack_linear(a, b, 1, 0, 128, B.BF16, None) == B.E_ARG
+    assert lib.dinfer_pack_linear(a, b, 0, 64, 128, B.BF16, None) == B.E_ARG            # n_mats
+    assert lib.dinfer_pack_linear(a, b, 1, 64, 48, B.BF16, None) == B.E_ARG             # K % 32
+    assert lib.dinfer_pack_linear(a, b, 1, 64, 24, B.F32, None) == B.E_ARG              # K % 16
+    assert lib.dinfer_pack_linear(a, b, 1, 64, 128, 7, None) == B.E_ARG
+    assert b"dtype" in lib.dinfer_last_error()
 
 
 def test_calls_on_null_context_fail_cleanly():

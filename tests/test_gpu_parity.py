@@ -246,12 +246,15 @@ def test_full_width_two_layer_parity(preset):
 
 # --------------------------------------------------------------- linear (K1)
 @pytest.mark.parametrize("shape,dt", [((48, 256), "bf16"), ((3, 32, 96), "bf16"),
-                                      ((4096, 4096), "bf16"), ((32, 48), "f32"),
-                                      ((2, 16, 64), "f32")])
+                                      ((4096, 4096), "bf16"), ((384, 128), "bf16"),
+                                      ((2, 400, 64), "bf16"), ((32, 48), "f32"),
+                                      ((2, 272, 64), "f32")])
 def test_pack_linear_layout(shape, dt):
-    """Packed weight layout, bit for bit: 16-row groups x one vector step
-    (32 bf16 / 16 f32 columns) per 1 KB block, blocks by group then step,
-    slot 16q + c = row c of the group, columns [q*VEC, (q+1)*VEC) of the step."""
+    """Packed weight layout, bit for bit, against the layout written out with
+    reshapes: 1 KB blocks of 16 rows x one vector step (32 bf16 / 16 f32
+    columns), slot 16q + c = row c of the group, columns [q*VEC, (q+1)*VEC);
+    tiles of 16 groups stored step by step (the last tile may be short); each
+    matrix of a stack on its own."""
     note(f"pack_linear {shape} {dt}")
     tdt = torch.bfloat16 if dt == "bf16" else torch.float32
     vec = 8 if dt == "bf16" else 4
@@ -259,10 +262,16 @@ def test_pack_linear_layout(shape, dt):
     W = torch.randn(*shape, device="cuda", generator=g).to(tdt)
     P = B.pack_linear(W)
     torch.cuda.synchronize()
-    K = shape[-1]
-    rows = W.numel() // K
-    w = W.reshape(rows // 16, 16, K // (4 * vec), 4, vec).permute(0, 2, 3, 1, 4).contiguous()
-    assert torch.equal(P.reshape(-1).cpu(), w.reshape(-1).cpu())
+    N, K = shape[-2], shape[-1]
+    ks = K // (4 * vec)
+    want = []
+    for w in W.reshape(-1, N, K).cpu():
+        # blocks[g][s] = the (group, step) block in slot order
+        blocks = w.reshape(N // 16, 16, ks, 4, vec).permute(0, 2, 3, 1, 4).reshape(N // 16, ks, -1)
+        for t0 in range(0, N // 16, 16):
+            tile = blocks[t0: t0 + 16]                       # [groups in tile][ks][block]
+            want.append(tile.permute(1, 0, 2).reshape(-1))   # step-major within the tile
+    assert torch.equal(P.reshape(-1).cpu(), torch.cat(want))
 
 
 @pytest.mark.parametrize("M,N,K,dt", [(64, 24576, 4096, "bf16"), (64, 12288, 4096, "bf16"),
