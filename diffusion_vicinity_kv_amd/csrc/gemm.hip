@@ -30,6 +30,8 @@
 //    order (deterministic; the kernel boundary orders the writes).
 //  * fat (M > 128: block-start refresh, batched steps): gemm_fat.hip.
 // Also the grouped projection of the MoE experts, and the plans.
+#include <algorithm>
+
 #include "common.h"
 #include "gemm_split.h"
 #include "kernels.h"
@@ -314,8 +316,8 @@ template <typename TW>
 hipError_t dispatch(const GemmPlan& p, const float* A, const void* W, float* out,
                     const int* m_dev, int m_cap, int N, int K, hipStream_t st) {
   if (p.kind == 1)
-    return launch_gemm_fat(sizeof(TW) == 2 ? DType::BF16 : DType::F32, p.nw, A, W, out, m_dev,
-                           m_cap, N, K, st);
+    return launch_gemm_fat(sizeof(TW) == 2 ? DType::BF16 : DType::F32, p.nw, p.splits, A, W,
+                           out, m_dev, m_cap, N, K, st);
   if constexpr (sizeof(TW) == 2) {   // 8-wave groups: bf16 weights only
     if (p.nw == 8) return dispatch_mt<TW, 2, 8>(p, A, W, out, m_dev, m_cap, N, K, st);
   }
@@ -364,6 +366,15 @@ bool gemm_shape_ok(DType t, int N, int K) {
   return N > 0 && K > 0 && N % 128 == 0 && K % gemm_k_chunk(t) == 0;
 }
 
+// Fat plan: 128 x 256 tiles (128 x 128 when N has a single tile), and the K
+// split count s <= 4 that minimises the estimated time
+//   ceil(tiles * s / target_wgs) / s * K * c_round  +  (s - 1) * M * N * c_part
+// -- rounds of one workgroup per CU, each a 1/s share of the full-K tile work,
+// plus the extra fp32 partial written and read back for each added split
+// (c_round and c_part measured on the dense 8B shapes: a full-K round takes
+// about 112 us at K = 4096; a partial element costs 8 bytes at about 4 TB/s).
+// Splitting pays where the tile count leaves a last round mostly empty.
+//
 // Skinny plan: a column group per workgroup as wide as still gives at least
 // 16 groups (256 columns = 8 waves x 32, else 128 = 4 x 32, else 64 = 4 x 16),
 // then K splits so that the grid is about target_wgs workgroups.
@@ -372,10 +383,22 @@ GemmPlan plan_gemm(DType t, int m_cap, int N, int K, int target_wgs) {
   if (m_cap > 128) {
     p.kind = 1;
     p.mt = p.nt = 0;
-    p.splits = 1;
+    p.nw = N > 128 ? 4 : 2;
     const int mtiles = (m_cap + 127) / 128;
-    p.nw = ((N + 255) / 256) * mtiles >= target_wgs ? 4 : 2;
-    p.grid = ((N + 64 * p.nw - 1) / (64 * p.nw)) * mtiles;
+    const int tiles = ((N + 64 * p.nw - 1) / (64 * p.nw)) * mtiles;
+    const int max_s = std::min(4, K / (t == DType::F32 ? 32 : 64));
+    const double c_round = 112.0 / 4096, c_part = 8.0 / 4e6;   // us per K element; us per partial
+    double best = 0.0;
+    p.splits = 1;
+    for (int s = 1; s <= max_s; ++s) {
+      const double rounds = (double)((tiles * s + target_wgs - 1) / target_wgs);
+      const double cost = rounds / s * K * c_round + (s - 1) * (double)m_cap * N * c_part;
+      if (s == 1 || cost < best) {
+        best = cost;
+        p.splits = s;
+      }
+    }
+    p.grid = tiles * p.splits;
     return p;
   }
   p.kind = 0;

@@ -1,7 +1,8 @@
 // Dense projections with many rows (block-start refresh, batched steps) on
-// gfx950 MFMA: out = A * W^T, A [M][K] fp32 activations, W [N][K] weights
-// (fp32 or bf16) in the packed block layout of launch_pack_linear, fp32
-// accumulation, no K split.
+// gfx950 MFMA: out[s] = A * W^T over the s-th K slice, A [M][K] fp32
+// activations, W [N][K] weights (fp32 or bf16) in the packed block layout of
+// launch_pack_linear, fp32 accumulation.  K splits (grid z) only even out the
+// last round of workgroups; their partials are summed by the consumer.
 #include "common.h"
 #include "gemm_split.h"
 #include "kernels.h"
@@ -63,7 +64,11 @@ __global__ __launch_bounds__(128 * WN) void gemm_fat_kernel(const float* __restr
   const int lg = lane >> 4;
   const int wm = wave / WN;                    // 2 row halves
   const int wn = wave % WN;                    // WN column groups
-  const int nk = K / BK;
+  // this workgroup's K slabs: split blockIdx.z of gridDim.z
+  const int nk_all = K / BK;
+  const int kb = (int)(blockIdx.z * nk_all / gridDim.z);
+  const int nk = (int)((blockIdx.z + 1) * nk_all / gridDim.z) - kb;
+  Cout += (size_t)blockIdx.z * m_cap * N;
 
   floatx4 acc[4][4];
 #pragma unroll
@@ -92,7 +97,7 @@ __global__ __launch_bounds__(128 * WN) void gemm_fat_kernel(const float* __restr
     wstep[i] = (size_t)KK * packed_kstride(grp, NG) * BE;
   }
   auto gload = [&](float4 (&ra)[AV], V16 (&rb)[BV], int kt) {
-    kt = min(kt, nk - 1);   // past the end: repeat the last slab
+    kt = kb + min(kt, nk - 1);   // past the end: repeat the last slab
 #pragma unroll
     for (int i = 0; i < AV; ++i) ra[i] = *reinterpret_cast<const float4*>(arow[i] + kt * BK);
 #pragma unroll
@@ -162,10 +167,11 @@ __global__ __launch_bounds__(128 * WN) void gemm_fat_kernel(const float* __restr
 
 }  // namespace
 
-hipError_t launch_gemm_fat(DType t, int wn, const float* A, const void* W, float* out,
-                           const int* m_dev, int m_cap, int N, int K, hipStream_t st) {
-  if (wn != 2 && wn != 4) return hipErrorInvalidValue;
-  const dim3 grid((N + 64 * wn - 1) / (64 * wn), (m_cap + kFatM - 1) / kFatM);
+hipError_t launch_gemm_fat(DType t, int wn, int splits, const float* A, const void* W,
+                           float* out, const int* m_dev, int m_cap, int N, int K, hipStream_t st) {
+  const int bk = t == DType::F32 ? 32 : 64;   // K per slab
+  if ((wn != 2 && wn != 4) || splits < 1 || splits > K / bk) return hipErrorInvalidValue;
+  const dim3 grid((N + 64 * wn - 1) / (64 * wn), (m_cap + kFatM - 1) / kFatM, splits);
   if (t == DType::F32) {
     if (wn == 4)
       hipLaunchKernelGGL((gemm_fat_kernel<float, 4>), grid, dim3(512), 0, st, A,

@@ -34,16 +34,17 @@ struct GemmPlan {
   int mt, nt;    // skinny: 16-row tiles; 16-column tiles per wave
   int nw;        // skinny: waves per workgroup; fat: column waves (2 or 4)
   int guard;     // skinny: 1 = A has exactly m_cap rows; 0 = A readable up to 16*mt rows
-  int splits;    // K splits (skinny only; fat = 1)
+  int splits;    // K splits (partials out[s][m][n], summed by the consumer)
   int grid;
 };
 GemmPlan plan_gemm(DType t, int m_cap, int N, int K, int target_wgs);
 // A is fp32 (split into hi/lo bf16 halves in-kernel for bf16 weights).
 hipError_t launch_gemm(const GemmPlan& p, DType t, const float* A, const void* W, float* out,
                        const int* m_dev, int m_cap, int N, int K, hipStream_t st);
-// The fat kernel alone (M > 128): wn = 2 or 4 column waves (128 x 64*wn tiles).
-hipError_t launch_gemm_fat(DType t, int wn, const float* A, const void* W, float* out,
-                           const int* m_dev, int m_cap, int N, int K, hipStream_t st);
+// The fat kernel alone (M > 128): wn = 2 or 4 column waves (128 x 64*wn
+// tiles), splits K slices (1 .. K/64 bf16, K/32 fp32) writing out[s][m][n].
+hipError_t launch_gemm_fat(DType t, int wn, int splits, const float* A, const void* W,
+                           float* out, const int* m_dev, int m_cap, int N, int K, hipStream_t st);
 // n_mats matrices W [N][K] row-major -> the packed block layout every GEMM
 // here reads (gemm_split.h: 16-row groups x one MFMA vector step per 1 KB
 // block, 256-row tiles stored k-step by k-step).  N % 16 == 0, K a multiple

@@ -138,8 +138,11 @@ bool make_layout(const dinfer_model_cfg* m, const dinfer_decode_cfg* dc, int max
   l.g_gu_s = plan_gemm(dt, l.m_step, 2 * Fd, d, tw);
   l.g_d_s = plan_gemm(dt, l.m_step, d, Fd, tw);
   l.g_lm = plan_gemm(dt, l.lm_rows, V, d, tw);
-  if (l.g_lm.kind == 0 && l.g_lm.splits != 1)
-    l.g_lm.splits = 1, l.g_lm.grid = V / (16 * l.g_lm.nt * l.g_lm.nw);
+  // the logits are read in place by the vocab statistics: one K slice only
+  if (l.g_lm.splits != 1) {
+    l.g_lm.grid /= l.g_lm.splits;
+    l.g_lm.splits = 1;
+  }
   // the step's activation buffers hold at least 16*mt rows: no row guards
   for (GemmPlan* g : {&l.g_qkv_s, &l.g_o_s, &l.g_gu_s, &l.g_d_s, &l.g_lm}) g->guard = 0;
   l.g_qkv_r = plan_gemm(dt, l.m_ref, 3 * d, d, tw);
@@ -242,6 +245,10 @@ struct dinfer_ctx {
   dinfer_model_cfg m;
   dinfer_decode_cfg dc;
   Layout L;
+  // refresh pass: row capacity and projection plans for the rows of the
+  // current refresh call (the table keeps the full m_ref layout)
+  int ref_mcap = 0;
+  GemmPlan ref_q{}, ref_o{}, ref_g{}, ref_d{};
   hipStream_t stream = nullptr;   // caller's stream
   hipStream_t st = nullptr;       // stream kernels go to (the capture stream while capturing)
   hipStream_t cap_stream = nullptr;
@@ -333,13 +340,13 @@ dinfer_status run_pass(dinfer_ctx* c, bool step) {
   const DType dt = L.dt;
   const size_t es = dtype_size(dt);
   hipStream_t st = c->st;
-  const int m_cap = step ? L.m_step : L.m_ref;
+  const int m_cap = step ? L.m_step : c->ref_mcap;
   int* tab = c->at<int>(step ? L.off_tab_step : L.off_tab_ref);
-  const PassTable tb = table_view(tab, m_cap, L.max_batch);
-  const GemmPlan& gq = step ? L.g_qkv_s : L.g_qkv_r;
-  const GemmPlan& go = step ? L.g_o_s : L.g_o_r;
-  const GemmPlan& gg = step ? L.g_gu_s : L.g_gu_r;
-  const GemmPlan& gd = step ? L.g_d_s : L.g_d_r;
+  const PassTable tb = table_view(tab, step ? L.m_step : L.m_ref, L.max_batch);
+  const GemmPlan& gq = step ? L.g_qkv_s : c->ref_q;
+  const GemmPlan& go = step ? L.g_o_s : c->ref_o;
+  const GemmPlan& gg = step ? L.g_gu_s : c->ref_g;
+  const GemmPlan& gd = step ? L.g_d_s : c->ref_d;
   const AttnPlan& ap = step ? L.a_step : L.a_ref;
   const int d = L.d;
   const int F = L.moe ? L.Fs : L.F;   // dense FFN, or the MoE layer's shared expert
@@ -691,6 +698,24 @@ dinfer_status dinfer_refresh_kv(dinfer_ctx* c, const uint8_t* h_req_mask) {
   }
   if (nsel == 0) return DINFER_OK;
   t[0] = rows;
+  // plans for this call's rows (K splits that suit the actual tile count),
+  // unless their partials would not fit the buffer sized for m_ref
+  {
+    const int d = L.d, Fd = L.moe ? L.Fs : L.F;
+    int m_eff = std::min(L.m_ref, (rows + 15) / 16 * 16);
+    GemmPlan pq = plan_gemm(L.dt, m_eff, 3 * d, d, 256), po = plan_gemm(L.dt, m_eff, d, d, 256),
+             pg = plan_gemm(L.dt, m_eff, 2 * Fd, d, 256), pd = plan_gemm(L.dt, m_eff, d, Fd, 256);
+    auto fits = [&](const GemmPlan& g, int N) {
+      return (size_t)g.splits * m_eff * N <= L.part_elems;
+    };
+    if (!(fits(pq, 3 * d) && fits(po, d) && fits(pg, 2 * Fd) && fits(pd, d))) {
+      m_eff = L.m_ref;
+      pq = L.g_qkv_r, po = L.g_o_r, pg = L.g_gu_r, pd = L.g_d_r;
+    }
+    for (GemmPlan* g : {&pq, &po, &pg, &pd}) g->guard = 0;   // buffers hold m_all rows
+    c->ref_mcap = m_eff;
+    c->ref_q = pq, c->ref_o = po, c->ref_g = pg, c->ref_d = pd;
+  }
   HIP_TRY(hipMemcpyAsync(c->at<int>(L.off_tab_ref), t, (size_t)L.tab_ints_ref * 4,
                          hipMemcpyHostToDevice, c->stream));
   HIP_TRY(hipMemcpyAsync(c->at<int>(L.off_mask), mask, (size_t)mb * 4, hipMemcpyHostToDevice,
