@@ -66,7 +66,9 @@ __device__ __forceinline__ void wave_top8(float (&tv)[kTop], int (&ti)[kTop], fl
 
 __device__ __forceinline__ void insert_top8(float (&tv)[kTop], int (&ti)[kTop], float v, int id) {
   // ids reach a thread in increasing order, so an equal value never displaces
-  // an entry already kept (that entry has the smaller id).
+  // an entry already kept (that entry has the smaller id).  The insertion is
+  // a chain of selects (no per-slot branches): once a slot takes the new
+  // entry, every later slot takes its predecessor.
   if (!(v > tv[kTop - 1])) return;
   bool carry = false;
   float cv = v;
@@ -74,15 +76,13 @@ __device__ __forceinline__ void insert_top8(float (&tv)[kTop], int (&ti)[kTop], 
 #pragma unroll
   for (int k = 0; k < kTop; ++k) {
     const bool take = carry || cv > tv[k];
-    if (take) {
-      const float tvk = tv[k];
-      const int tik = ti[k];
-      tv[k] = cv;
-      ti[k] = ci;
-      cv = tvk;
-      ci = tik;
-      carry = true;
-    }
+    const float tvk = tv[k];
+    const int tik = ti[k];
+    tv[k] = take ? cv : tvk;
+    ti[k] = take ? ci : tik;
+    cv = take ? tvk : cv;
+    ci = take ? tik : ci;
+    carry = take;
   }
 }
 
@@ -132,13 +132,14 @@ __global__ __launch_bounds__(kThreads) void vocab_partial_kernel(
         float v = xs[e];
         if (id == pid) v += pb;
         if (id == mask_id) v = -INFINITY;
-        if (v == -INFINITY) continue;
-        if (v > m) {
-          s = s * exp2f((m - v) * kLog2e) + 1.f;
-          m = v;
-        } else {
-          s += exp2f((v - m) * kLog2e);
-        }
+        // online (max, sum): rescale by exp2(m - mx), add exp2(v - mx) -- one
+        // of the two factors is exactly 1, so this equals the two-branch
+        // update bit for bit without diverging; -inf entries change nothing
+        const bool live = v != -INFINITY;
+        const float mx = fmaxf(m, v);
+        const float sn = s * exp2f((m - mx) * kLog2e) + exp2f((v - mx) * kLog2e);
+        s = live ? sn : s;
+        m = live ? mx : m;
         insert_top8(tv, ti, v, id);
       }
     }
