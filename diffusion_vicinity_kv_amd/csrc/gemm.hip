@@ -11,9 +11,10 @@
 // Weights are read in a packed layout (pack_kernel below; gemm_split.h): the
 // 1 KB MFMA B operand of every 16 rows x KSTEP columns is stored
 // contiguously, in lane order, so that each weight load of a wave is one
-// contiguous kilobyte -- whole 128-byte lines -- and the blocks of a 256-row
-// tile follow each other k-step by k-step, so that a workgroup's weight
-// stream is one sequential run.  Read row-major, each load would touch 64
+// contiguous kilobyte -- whole 128-byte lines -- and the blocks of one k-step
+// of all rows are adjacent, so that the workgroups of a K split, advancing
+// together, stream one narrow window of addresses through the matrix.  Read
+// row-major, each load would touch 64
 // bytes of 16 different rows and the vector L1 would issue twice as many
 // half-line requests, stalling the address unit.
 //

@@ -252,14 +252,14 @@ dinfer_status dinfer_step_graph(dinfer_ctx* ctx, int32_t n_steps);
  * projection kernel reads; each matrix is packed on its own.  A block is the
  * 1 KB MFMA operand of 16 rows (a group) x one run of 32 (bf16) / 16 (f32)
  * columns: its 16-byte slot 16*q + c holds row c of the group, columns
- * q*VEC .. q*VEC+VEC-1 of the run (VEC = 8 bf16 / 4 f32).  Groups form tiles
- * of 16 (256 rows; the last tile may hold fewer); tile t's blocks are stored
- * run by run, the tile's groups in order within a run, tiles one after the
- * other: block (group g, run s) is at index 16*KS*(g/16) + s*G_t + g%16
- * with KS = K/32 (bf16) or K/16 (f32) runs and G_t groups in g's tile.  A
- * wave's weight load is then one contiguous kilobyte and a workgroup's
- * weight stream one sequential run.  rows % 16 == 0; K a multiple of 32
- * (bf16) / 16 (f32); n_mats <= 65535.  Enqueued on stream. */
+ * q*VEC .. q*VEC+VEC-1 of the run (VEC = 8 bf16 / 4 f32).  Blocks are
+ * stored run-major: block (group g, run s) is at index s*(rows/16) + g, with
+ * KS = K/32 (bf16) or K/16 (f32) runs.  A wave's weight load is then one
+ * contiguous kilobyte, a workgroup's column tile one contiguous piece per
+ * run, and the workgroups of one K split read neighbouring pieces as they
+ * advance together (a narrow address window sweeping through the matrix).
+ * rows % 16 == 0; K a multiple of 32 (bf16) / 16 (f32); n_mats <= 65535.
+ * Enqueued on stream. */
 dinfer_status dinfer_pack_linear(const void* d_W, void* d_packed, int32_t n_mats, int32_t rows,
                                  int32_t K, int32_t dtype, void* stream);
 

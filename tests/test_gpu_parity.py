@@ -253,8 +253,8 @@ def test_pack_linear_layout(shape, dt):
     """Packed weight layout, bit for bit, against the layout written out with
     reshapes: 1 KB blocks of 16 rows x one vector step (32 bf16 / 16 f32
     columns), slot 16q + c = row c of the group, columns [q*VEC, (q+1)*VEC);
-    tiles of 16 groups stored step by step (the last tile may be short); each
-    matrix of a stack on its own."""
+    blocks stored step-major (every group of step 0, then of step 1, ...);
+    each matrix of a stack on its own."""
     note(f"pack_linear {shape} {dt}")
     tdt = torch.bfloat16 if dt == "bf16" else torch.float32
     vec = 8 if dt == "bf16" else 4
@@ -268,9 +268,7 @@ def test_pack_linear_layout(shape, dt):
     for w in W.reshape(-1, N, K).cpu():
         # blocks[g][s] = the (group, step) block in slot order
         blocks = w.reshape(N // 16, 16, ks, 4, vec).permute(0, 2, 3, 1, 4).reshape(N // 16, ks, -1)
-        for t0 in range(0, N // 16, 16):
-            tile = blocks[t0: t0 + 16]                       # [groups in tile][ks][block]
-            want.append(tile.permute(1, 0, 2).reshape(-1))   # step-major within the tile
+        want.append(blocks.permute(1, 0, 2).reshape(-1))   # step-major
     assert torch.equal(P.reshape(-1).cpu(), torch.cat(want))
 
 
