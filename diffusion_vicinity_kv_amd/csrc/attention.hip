@@ -144,24 +144,31 @@ __global__ __launch_bounds__(256 * kKeyGroups) void attn_kernel(
     for (int i = 0; i < FW; ++i) frag[kg][buf][wave * FW + i][lane] = reg[i];
   };
 
+  // Scores of every query tile first (each K fragment read from LDS once and
+  // used by all of the wave's tiles), then the softmax update of each tile,
+  // then P V with each V fragment likewise read once.
   auto compute = [&](int buf, int i) {
     const int s = kg + i * KG;
     if (s >= n_steps) return;                  // this group's slot past the range
     const int kb = k0 + s * KS;
-    V16 kf[NK];
+    floatx4 sc[QTW][NTS];
 #pragma unroll
-    for (int f = 0; f < NK; ++f) kf[f] = frag[kg][buf][f][lane];
+    for (int u = 0; u < QTW; ++u)
+#pragma unroll
+      for (int t = 0; t < NTS; ++t) sc[u][t] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int t = 0; t < NTS; ++t)
+#pragma unroll
+      for (int kk = 0; kk < QV; ++kk) {
+        const V16 kf = frag[kg][buf][t * QV + kk][lane];
+#pragma unroll
+        for (int u = 0; u < QTW; ++u)
+#pragma unroll
+          for (int p = 0; p < PL; ++p) MF::mac(sc[u][t], kf, qf[u][kk][p]);
+      }
+    V16 pf[QTW][PL];
 #pragma unroll
     for (int u = 0; u < QTW; ++u) {
-      floatx4 sc[NTS];
-#pragma unroll
-      for (int t = 0; t < NTS; ++t) {
-        sc[t] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kk = 0; kk < QV; ++kk)
-#pragma unroll
-          for (int p = 0; p < PL; ++p) MF::mac(sc[t], kf[t * QV + kk], qf[u][kk][p]);
-      }
       // lane (query lc, group lg) holds keys kb + lg*VEC + e, e = 4t + i
       float pv[VEC];
       float mloc = -INFINITY;
@@ -170,7 +177,7 @@ __global__ __launch_bounds__(256 * kKeyGroups) void attn_kernel(
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int e = 4 * t + i;
-          const float v = kb + lg * VEC + e < k1 ? sc[t][i] * scale_log2 : -INFINITY;
+          const float v = kb + lg * VEC + e < k1 ? sc[u][t][i] * scale_log2 : -INFINITY;
           pv[e] = v;
           mloc = fmaxf(mloc, v);
         }
@@ -191,14 +198,15 @@ __global__ __launch_bounds__(256 * kKeyGroups) void attn_kernel(
         pv[e] = exp2f(pv[e] - m_run[u]);
         l_run[u] += pv[e];
       }
-      V16 pf[PL];
-      SO::make(pv, pf);
+      SO::make(pv, pf[u]);
+    }
 #pragma unroll
-      for (int ht = 0; ht < HT; ++ht) {
-        const V16 vf = frag[kg][buf][NK + ht][lane];
+    for (int ht = 0; ht < HT; ++ht) {
+      const V16 vf = frag[kg][buf][NK + ht][lane];
 #pragma unroll
-        for (int p = 0; p < PL; ++p) MF::mac(o[u][ht], vf, pf[p]);
-      }
+      for (int u = 0; u < QTW; ++u)
+#pragma unroll
+        for (int p = 0; p < PL; ++p) MF::mac(o[u][ht], vf, pf[u][p]);
     }
   };
 
@@ -234,48 +242,49 @@ __global__ __launch_bounds__(256 * kKeyGroups) void attn_kernel(
   }
 
   // key groups 1.. hand (m, l, O) to group 0 through the (now idle) fragment
-  // buffers; group 0 merges them in order
-  static_assert((KG - 1) * 4 * QTW * (HT + 1) <= KG * 2 * NF, "merge area fits the fragment buffers");
+  // buffers, one query tile of each wave per round; group 0 merges them in
+  // order
+  static_assert((KG - 1) * 4 * (HT + 1) <= KG * 2 * NF, "merge area fits the fragment buffers");
   V16* xch = &frag[0][0][0][0];
-  if (kg > 0) {
 #pragma unroll
-    for (int u = 0; u < QTW; ++u) {
-      const int slot = ((kg - 1) * 4 + wave) * QTW + u;
+  for (int u = 0; u < QTW; ++u) {
+    if (u > 0) __syncthreads();   // the previous round's records have been read
+    if (kg > 0) {
+      const int slot = (kg - 1) * 4 + wave;
 #pragma unroll
       for (int ht = 0; ht < HT; ++ht) xch[(slot * (HT + 1) + ht) * 64 + lane].f = o[u][ht];
       xch[(slot * (HT + 1) + HT) * 64 + lane].f = floatx4{m_run[u], l_run[u], 0.f, 0.f};
     }
-  }
-  __syncthreads();
-  if (kg > 0) return;
+    __syncthreads();
+    if (kg == 0) {
+      float M = m_run[u];
 #pragma unroll
-  for (int u = 0; u < QTW; ++u) {
-    float M = m_run[u];
+      for (int k = 1; k < KG; ++k)
+        M = fmaxf(M, xch[(((k - 1) * 4 + wave) * (HT + 1) + HT) * 64 + lane].f[0]);
+      const float w0 = M == -INFINITY ? 0.f : exp2f(m_run[u] - M);
+      float l = l_run[u] * w0;
 #pragma unroll
-    for (int k = 1; k < KG; ++k)
-      M = fmaxf(M, xch[((((k - 1) * 4 + wave) * QTW + u) * (HT + 1) + HT) * 64 + lane].f[0]);
-    const float w0 = M == -INFINITY ? 0.f : exp2f(m_run[u] - M);
-    float l = l_run[u] * w0;
+      for (int ht = 0; ht < HT; ++ht)
 #pragma unroll
-    for (int ht = 0; ht < HT; ++ht)
+        for (int i = 0; i < 4; ++i) o[u][ht][i] *= w0;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) o[u][ht][i] *= w0;
+      for (int k = 1; k < KG; ++k) {
+        const int slot = (k - 1) * 4 + wave;
+        const floatx4 ml = xch[(slot * (HT + 1) + HT) * 64 + lane].f;
+        const float w = ml[0] == -INFINITY ? 0.f : exp2f(ml[0] - M);
+        l += w * ml[1];
 #pragma unroll
-    for (int k = 1; k < KG; ++k) {
-      const int slot = ((k - 1) * 4 + wave) * QTW + u;
-      const floatx4 ml = xch[(slot * (HT + 1) + HT) * 64 + lane].f;
-      const float w = ml[0] == -INFINITY ? 0.f : exp2f(ml[0] - M);
-      l += w * ml[1];
+        for (int ht = 0; ht < HT; ++ht) {
+          const floatx4 v = xch[(slot * (HT + 1) + ht) * 64 + lane].f;
 #pragma unroll
-      for (int ht = 0; ht < HT; ++ht) {
-        const floatx4 v = xch[(slot * (HT + 1) + ht) * 64 + lane].f;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) o[u][ht][i] += w * v[i];
+          for (int i = 0; i < 4; ++i) o[u][ht][i] += w * v[i];
+        }
       }
+      m_run[u] = M;
+      l_run[u] = l;
     }
-    m_run[u] = M;
-    l_run[u] = l;
   }
+  if (kg > 0) return;
 
 #pragma unroll
   for (int u = 0; u < QTW; ++u) {
@@ -423,6 +432,7 @@ hipError_t run_q(const AttnPlan& p, PassTable tb, int batch, int m_cap, const fl
                  const void* kc, const void* vt, int H, int Lp, float* o_part, float* ml_part,
                  float* o, hipStream_t st) {
   if (p.qtw == 1) return run<T, HD, 1>(p, tb, batch, m_cap, q, kc, vt, H, Lp, o_part, ml_part, o, st);
+  if (p.qtw == 2) return run<T, HD, 2>(p, tb, batch, m_cap, q, kc, vt, H, Lp, o_part, ml_part, o, st);
   return hipErrorInvalidValue;
 }
 
@@ -430,15 +440,20 @@ hipError_t run_q(const AttnPlan& p, PassTable tb, int batch, int m_cap, const fl
 
 int attn_cache_len(int max_len) { return (max_len + 63) / 64 * 64; }
 
-// Blocks of 64 queries, one 16-query tile per wave (measured faster than two
-// tiles per wave over the same keys, which halves the workgroups).  Then key
-// splits while the grid stays within target_wgs (256: about one workgroup of
-// eight waves per CU) and every split keeps at least 192 keys (shorter splits
-// cost more in fixed work and partials than they gain in parallelism).
+// Blocks of 64 queries, one 16-query tile per wave, while a request has at
+// most 64 query rows (batch-1 and batch-16 windows of 32 + 2 * 16 positions;
+// measured faster than fewer, wider workgroups there).  With more rows
+// (refresh, wider windows) blocks of 128 queries, two tiles per wave: each
+// K/V fragment is read from the cache and from LDS once for twice the
+// queries (refresh of the 8K-prompt workload 6% faster, its window steps 3%).
+// Then key splits while the grid stays within target_wgs (256: about one
+// workgroup of eight waves per CU) and every split keeps at least 192 keys
+// (shorter splits cost more in fixed work and partials than they gain in
+// parallelism).
 AttnPlan plan_attention(int batch, int max_rows_per_req, int max_keys, int H, int target_wgs) {
   AttnPlan p{};
-  p.qtw = 1;
-  p.q_blocks = (max_rows_per_req + 63) / 64;
+  p.qtw = max_rows_per_req > 64 ? 2 : 1;
+  p.q_blocks = (max_rows_per_req + 64 * p.qtw - 1) / (64 * p.qtw);
   if (p.q_blocks < 1) p.q_blocks = 1;
   const int steps = (max_keys + 31) / 32;
   const int base = batch * p.q_blocks * H;
