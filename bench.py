@@ -55,8 +55,12 @@ def log(msg):
 
 
 def source_hash() -> str:
-    p = os.path.join(ROOT, "diffusion_vicinity_kv_amd", "csrc", "gemm.hip")
-    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+    """Hash of the sources the skinny projection kernel is built from (its
+    recorded HBM traffic is reported only while they are unchanged)."""
+    h = hashlib.sha256()
+    for f in ("gemm.hip", "gemm_split.h", "common.h"):
+        h.update(open(os.path.join(ROOT, "diffusion_vicinity_kv_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
 
 
 def dominant_kernel_timing(wc, weights, iters=40):
