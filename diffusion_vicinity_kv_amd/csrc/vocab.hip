@@ -5,15 +5,17 @@
 // section "解码的艺术": the probability distribution kept for iteration
 // smoothing).
 //
-// HBM-bound: one pass over the fp32 logits.  The vocabulary of a row is split
-// across workgroups so that a few rows still fill the chip; each thread keeps
-// an online (max, sum of exp) and a sorted top-8 in registers, a workgroup
+// One pass over the fp32 logits.  The vocabulary of a row is split across
+// workgroups so that a few rows still fill the chip; each thread keeps an
+// online (max, sum of exp) and a sorted top-8 in registers, fed through a
+// wave-wide threshold so that few entries need an insertion, a workgroup
 // merges them with wave64 exchanges, and a second kernel merges the splits of
 // a row (one wave per row) in split order.
 #include "common.h"
 #include "kernels.h"
 
 #include <climits>
+#include <type_traits>
 
 namespace dinfer {
 
@@ -112,37 +114,93 @@ __global__ __launch_bounds__(kThreads) void vocab_partial_kernel(
     ti[k] = INT_MAX;
   }
   // c0, c1 and V are multiples of 4, so every float4 lies wholly inside or
-  // outside the split.  Four float4 per thread are loaded before any is used
-  // (clamped into the split; the extra ones are skipped), in increasing id
-  // order per thread.
+  // outside the split (c1 > c0 for every launched split).  A thread takes
+  // kE = 4 kU entries per round, kU float4 loaded together; entry i of the
+  // round has id b0 + (i/4) 4 kThreads + i%4 -- increasing in i and over
+  // rounds.
+  //  * softmax: the round's maximum first, then one rescale of the running
+  //    sum and one exp per entry;
+  //  * top-8: an entry can reach the row's top 8 only if it is >= T, the
+  //    largest 8th-best value over the wave's lanes (that lane holds eight
+  //    entries >= T, so anything smaller has eight strictly larger
+  //    entries), and it enters this lane's list only if it beats the list's
+  //    8th entry; after the first rounds few entries pass both tests.
   constexpr int kU = 4;
-  for (int b0 = c0 + 4 * threadIdx.x; b0 < c1; b0 += 4 * kThreads * kU) {
-    float4 xv[kU];
+  constexpr int kE = 4 * kU;
+  // Every lane runs the same number of rounds (the wave-wide threshold is a
+  // cross-lane reduction), rounded up to even; entries past the split are
+  // -inf.  The loads of round r+1 are issued before round r is processed
+  // (two register sets alternate; loads past the split are clamped).
+  float T = -INFINITY;
+  constexpr int kRound = 4 * kThreads * kU;    // entries of the split per round
+  const int rounds = ((c1 - c0 + kRound - 1) / kRound + 1) / 2 * 2;
+  auto issue = [&](float4 (&xv)[kU], int r) {
+    const int b0 = c0 + 4 * threadIdx.x + r * kRound;
 #pragma unroll
     for (int u = 0; u < kU; ++u)
       xv[u] = *reinterpret_cast<const float4*>(z + min(b0 + u * 4 * kThreads, c1 - 4));
+  };
+  auto process = [&](const float4 (&xv)[kU], int r, auto sparse) {
+    const int b0 = c0 + 4 * threadIdx.x + r * kRound;
+    float v[kE];
+    float gm = -INFINITY;
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
       const int base = b0 + u * 4 * kThreads;
-      if (base >= c1) break;
       const float xs[4] = {xv[u].x, xv[u].y, xv[u].z, xv[u].w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int id = base + e;
-        float v = xs[e];
-        if (id == pid) v += pb;
-        if (id == mask_id) v = -INFINITY;
-        // online (max, sum): rescale by exp2(m - mx), add exp2(v - mx) -- one
-        // of the two factors is exactly 1, so this equals the two-branch
-        // update bit for bit without diverging; -inf entries change nothing
-        const bool live = v != -INFINITY;
-        const float mx = fmaxf(m, v);
-        const float sn = s * exp2f((m - mx) * kLog2e) + exp2f((v - mx) * kLog2e);
-        s = live ? sn : s;
-        m = live ? mx : m;
-        insert_top8(tv, ti, v, id);
+        float x = xs[e];
+        if (id == pid) x += pb;
+        if (id == mask_id || base >= c1) x = -INFINITY;
+        v[4 * u + e] = x;
+        gm = fmaxf(gm, x);
       }
     }
+    const float mn = fmaxf(m, gm);
+    if (mn != -INFINITY) {
+      float add = 0.f;
+#pragma unroll
+      for (int i = 0; i < kE; ++i) add += exp2f((v[i] - mn) * kLog2e);
+      s = s * exp2f((m - mn) * kLog2e) + add;
+      m = mn;
+    }
+    if constexpr (decltype(sparse)::value) {
+      // few entries pass: collect them, then insert one at a time in id order
+      unsigned pend = 0;
+#pragma unroll
+      for (int i = 0; i < kE; ++i) pend |= (v[i] > tv[kTop - 1] && v[i] >= T) ? 1u << i : 0u;
+      while (pend != 0) {
+        const int i = __builtin_ctz(pend);
+        pend &= pend - 1;
+        float cv = v[0];
+#pragma unroll
+        for (int j = 1; j < kE; ++j) cv = i == j ? v[j] : cv;
+        insert_top8(tv, ti, cv, b0 + (i >> 2) * 4 * kThreads + (i & 3));
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < kE; ++i)
+        if (v[i] >= T) insert_top8(tv, ti, v[i], b0 + (i >> 2) * 4 * kThreads + (i & 3));
+    }
+    T = wave_max(tv[kTop - 1]);
+  };
+  // The first two rounds fill the lists (most entries enter): each entry is
+  // tried in turn.  Later rounds collect the few passing entries first.
+  using Dense = std::integral_constant<bool, false>;
+  using Sparse = std::integral_constant<bool, true>;
+  float4 xa[kU], xb[kU];
+  issue(xa, 0);
+  issue(xb, 1);
+  process(xa, 0, Dense{});
+  issue(xa, 2);
+  process(xb, 1, Dense{});
+  for (int r = 2; r < rounds; r += 2) {
+    issue(xb, r + 1);
+    process(xa, r, Sparse{});
+    issue(xa, r + 2);
+    process(xb, r + 1, Sparse{});
   }
   // workgroup merge: (max, sum) then top-8
   const int lane = threadIdx.x & 63;
