@@ -66,9 +66,11 @@ __global__ __launch_bounds__(256 * kKeyGroups) void attn_kernel(
   const int h = blockIdx.y;
   const int r = blockIdx.z / q_blocks;
   const int qb = blockIdx.z % q_blocks;
+  // the request's three table entries are loaded together
   const int nq = tb.req_nrows[r];
-  if (qb * QB >= nq) return;
   const int L = tb.req_len[r];
+  const int row_off = tb.req_row_off[r];
+  if (qb * QB >= nq) return;
   const int k0 = split * keys_per_split;
   if (k0 >= L) return;
   const int k1 = min(L, k0 + keys_per_split);
@@ -90,7 +92,7 @@ __global__ __launch_bounds__(256 * kKeyGroups) void attn_kernel(
   for (int u = 0; u < QTW; ++u) {
     const int qloc = qb * QB + (wave * QTW + u) * 16 + lc;
     qvalid[u] = qloc < nq;
-    qrow[u] = tb.req_row_off[r] + (qvalid[u] ? qloc : 0);
+    qrow[u] = row_off + (qvalid[u] ? qloc : 0);
 #pragma unroll
     for (int kk = 0; kk < QV; ++kk) {
       float qv[VEC];
@@ -313,15 +315,17 @@ __global__ __launch_bounds__(256 * kKeyGroups) void attn_kernel(
 }
 
 // Combine the key splits of each row: out = sum_s 2^(m_s - M) O_s /
-// sum_s 2^(m_s - M) l_s per head, splits taken in order.  One float4 of the
-// row per thread.
-// Merge of NS split records (m_s, l_s, o_s) of one (row, head), float4 of
-// the output: weights exp2(m_s - max), in split order.  The fixed-count
-// version issues every load before the first use.
+// sum_s 2^(m_s - M) l_s per head, splits taken in order; float4 of the row
+// per thread.  With at most eight splits every record a row may have is
+// loaded first -- before the row's request and key count are known, which
+// only decide how many of them count (ns) -- so the row's loads take one
+// memory round trip; records past ns are ignored (never read as numbers).
 template <int HD, int NS>
 __device__ __forceinline__ float4 merge_fixed(const float* __restrict__ o_part,
                                               const float* __restrict__ ml_part, size_t base0,
-                                              size_t sstride, int i4) {
+                                              size_t sstride, int i4,
+                                              const int* __restrict__ req_len, int r, int kps,
+                                              bool valid) {
   float2 ml[NS];
   float4 v[NS];
 #pragma unroll
@@ -330,39 +334,30 @@ __device__ __forceinline__ float4 merge_fixed(const float* __restrict__ o_part,
     ml[s] = *reinterpret_cast<const float2*>(ml_part + base * 2);
     v[s] = *reinterpret_cast<const float4*>(o_part + base * HD + (i4 * 4) % HD);
   }
+  // a row past the pass has no request to look up (its table entry may be
+  // anything); its result is not stored
+  const int L = valid ? req_len[r] : 0;
+  const int ns = min(NS, (L + kps - 1) / kps);
+  if (ns <= 0) return make_float4(0.f, 0.f, 0.f, 0.f);   // no split covers the row
   float M = -INFINITY;
 #pragma unroll
-  for (int s = 0; s < NS; ++s) M = fmaxf(M, ml[s].x);
+  for (int s = 0; s < NS; ++s)
+    if (s < ns) M = fmaxf(M, ml[s].x);
   float lsum = 0.f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
-    const float w = exp2f(ml[s].x - M);
-    lsum += w * ml[s].y;
-    acc.x += w * v[s].x;
-    acc.y += w * v[s].y;
-    acc.z += w * v[s].z;
-    acc.w += w * v[s].w;
+    if (s < ns) {
+      const float w = exp2f(ml[s].x - M);
+      lsum += w * ml[s].y;
+      acc.x += w * v[s].x;
+      acc.y += w * v[s].y;
+      acc.z += w * v[s].z;
+      acc.w += w * v[s].w;
+    }
   }
   const float inv = 1.f / lsum;
   return make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
-}
-
-template <int HD>
-__device__ __forceinline__ float4 merge_fixed_dispatch(int ns, const float* __restrict__ o_part,
-                                                       const float* __restrict__ ml_part,
-                                                       size_t base0, size_t sstride, int i4) {
-  switch (ns) {
-    case 1: return merge_fixed<HD, 1>(o_part, ml_part, base0, sstride, i4);
-    case 2: return merge_fixed<HD, 2>(o_part, ml_part, base0, sstride, i4);
-    case 3: return merge_fixed<HD, 3>(o_part, ml_part, base0, sstride, i4);
-    case 4: return merge_fixed<HD, 4>(o_part, ml_part, base0, sstride, i4);
-    case 5: return merge_fixed<HD, 5>(o_part, ml_part, base0, sstride, i4);
-    case 6: return merge_fixed<HD, 6>(o_part, ml_part, base0, sstride, i4);
-    case 7: return merge_fixed<HD, 7>(o_part, ml_part, base0, sstride, i4);
-    case 8: return merge_fixed<HD, 8>(o_part, ml_part, base0, sstride, i4);
-    default: return make_float4(0.f, 0.f, 0.f, 0.f);   // no split covers the row
-  }
 }
 
 // Any split count (more than eight splits: the long-context plans).
@@ -370,6 +365,7 @@ template <int HD>
 __device__ __forceinline__ float4 merge_loop(int ns, const float* __restrict__ o_part,
                                              const float* __restrict__ ml_part, size_t base0,
                                              size_t sstride, int i4) {
+  if (ns <= 0) return make_float4(0.f, 0.f, 0.f, 0.f);
   float M = -INFINITY;
   for (int s = 0; s < ns; ++s) M = fmaxf(M, ml_part[(base0 + s * sstride) * 2]);
   float lsum = 0.f;
@@ -394,18 +390,32 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(PassTable tb, int keys_
                                                          const float* __restrict__ o_part,
                                                          const float* __restrict__ ml_part,
                                                          int H, float* __restrict__ out) {
-  const int m = blockIdx.x;
-  if (m >= min(*tb.nrows, m_cap)) return;
+  const int m = blockIdx.x;                    // < m_cap: every row's records are readable
   const int i4 = blockIdx.y * 256 + threadIdx.x;
   if (i4 * 4 >= H * HD) return;
-  const int h = i4 * 4 / HD;
+  const int nr = *tb.nrows;
   const int r = tb.row_req[m];
-  const int L = tb.req_len[r];
-  const int ns = min(n_split, (L + keys_per_split - 1) / keys_per_split);
+  const bool valid = m < min(nr, m_cap);
+  const int h = i4 * 4 / HD;
   const size_t base0 = (size_t)m * H + h;
   const size_t sstride = (size_t)m_cap * H;   // between splits, in (m, h) records
-  const float4 res = ns <= 8 ? merge_fixed_dispatch<HD>(ns, o_part, ml_part, base0, sstride, i4)
-                             : merge_loop<HD>(ns, o_part, ml_part, base0, sstride, i4);
+  float4 res;
+  switch (n_split) {
+    case 1: res = merge_fixed<HD, 1>(o_part, ml_part, base0, sstride, i4, tb.req_len, r, keys_per_split, valid); break;
+    case 2: res = merge_fixed<HD, 2>(o_part, ml_part, base0, sstride, i4, tb.req_len, r, keys_per_split, valid); break;
+    case 3: res = merge_fixed<HD, 3>(o_part, ml_part, base0, sstride, i4, tb.req_len, r, keys_per_split, valid); break;
+    case 4: res = merge_fixed<HD, 4>(o_part, ml_part, base0, sstride, i4, tb.req_len, r, keys_per_split, valid); break;
+    case 5: res = merge_fixed<HD, 5>(o_part, ml_part, base0, sstride, i4, tb.req_len, r, keys_per_split, valid); break;
+    case 6: res = merge_fixed<HD, 6>(o_part, ml_part, base0, sstride, i4, tb.req_len, r, keys_per_split, valid); break;
+    case 7: res = merge_fixed<HD, 7>(o_part, ml_part, base0, sstride, i4, tb.req_len, r, keys_per_split, valid); break;
+    case 8: res = merge_fixed<HD, 8>(o_part, ml_part, base0, sstride, i4, tb.req_len, r, keys_per_split, valid); break;
+    default: {
+      const int L = valid ? tb.req_len[r] : 0;
+      const int ns = min(n_split, (L + keys_per_split - 1) / keys_per_split);
+      res = merge_loop<HD>(ns, o_part, ml_part, base0, sstride, i4);
+    }
+  }
+  if (!valid) return;
   *reinterpret_cast<float4*>(out + (size_t)m * H * HD + i4 * 4) = res;
 }
 

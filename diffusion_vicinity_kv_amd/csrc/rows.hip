@@ -129,10 +129,13 @@ __global__ __launch_bounds__(kNormThreads) void add_rmsnorm_kernel(
     int S, size_t p_stride, const T* __restrict__ g, float eps, float* __restrict__ a, int d) {
   __shared__ float red[kNormThreads / 64];
   const int m = blockIdx.x;
-  if (m >= min(*nrows, m_cap)) return;
+  // the row count is read together with the row (every row below m_cap is
+  // readable): one memory round trip before the reduction instead of two
+  const int nr = *nrows;
   const int d4 = d / 4;
   float4 v[NV];
   const float ss = load_row<NV>(v, x + (size_t)m * d, P + (size_t)m * d, S, p_stride, d4);
+  if (m >= min(nr, m_cap)) return;
   if (S > 0) {
     float4* xr = reinterpret_cast<float4*>(x + (size_t)m * d);
 #pragma unroll
@@ -162,53 +165,64 @@ __global__ __launch_bounds__(kQkvThreads) void qkv_rope_scatter_kernel(
     int hd, const float* __restrict__ rope_cs, float* __restrict__ q_out, T* __restrict__ kc,
     T* __restrict__ vt, int Lp) {
   __shared__ float vs[128 * (kQkvRows + 1)];
+  __shared__ int s_req[kQkvRows], s_pos[kQkvRows];
   const int m0 = blockIdx.x * kQkvRows;
   const int h = blockIdx.y;
-  const int M = min(*tb.nrows, m_cap);
-  if (m0 >= M) return;
   const int half = hd / 2;
   const int rr = threadIdx.x / 16;                // row of the tile
   const int m = m0 + rr;
+  // The row count, the row's table entries and its partials are loaded
+  // together (rows past the pass read row min(m, m_cap - 1), which is
+  // readable; nothing of theirs is stored).  One vector of each half of the
+  // head per thread (hd <= 128); threads past half load a clamped column.
+  const int nr = *tb.nrows;
+  const int mm = min(m, m_cap - 1);
+  const int r = tb.row_req[mm];
+  const int pos = tb.row_pos[mm];
+  const int j = (threadIdx.x % 16) * 4;
+  const int jj = min(j, half - 4);
+  const float* pr = P + (size_t)mm * 3 * d;
+  const int c0 = h * hd + jj;
+  const int c1 = c0 + half;
   const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
-  if (m < M) {
-    const int r = tb.row_req[m];
-    const int pos = tb.row_pos[m];
-    const float* pr = P + (size_t)m * 3 * d;
+  float4 t[6] = {z4, z4, z4, z4, z4, z4};
+  const float* const pp[6] = {pr + c0, pr + c1, pr + d + c0, pr + d + c1, pr + 2 * d + c0,
+                              pr + 2 * d + c1};
+  add_splits<6, G>(t, pp, p_stride, S);
+  const int M = min(nr, m_cap);
+  if (m0 >= M) return;
+  if (threadIdx.x % 16 == 0) {
+    s_req[rr] = r;
+    s_pos[rr] = pos;
+  }
+  if (m < M && j < half) {
     const float* cs = rope_cs + (size_t)pos * hd;   // [pos][cos half | sin half]
     T* kp = kc + (((size_t)r * H + h) * Lp + pos) * hd;
     float* qr = q_out + (size_t)m * d + h * hd;
-    for (int j = (threadIdx.x % 16) * 4; j < half; j += 64) {
-      const int c0 = h * hd + j;
-      const int c1 = c0 + half;
-      float4 t[6] = {z4, z4, z4, z4, z4, z4};
-      const float* const pp[6] = {pr + c0, pr + c1, pr + d + c0, pr + d + c1, pr + 2 * d + c0,
-                                  pr + 2 * d + c1};
-      add_splits<6, G>(t, pp, p_stride, S);
-      const float4 q0 = t[0], q1 = t[1], k0 = t[2], k1 = t[3], v0 = t[4], v1 = t[5];
-      const float4 c = *reinterpret_cast<const float4*>(cs + j);
-      const float4 sn = *reinterpret_cast<const float4*>(cs + half + j);
-      *reinterpret_cast<float4*>(qr + j) =
-          make_float4(q0.x * c.x - q1.x * sn.x, q0.y * c.y - q1.y * sn.y,
-                      q0.z * c.z - q1.z * sn.z, q0.w * c.w - q1.w * sn.w);
-      *reinterpret_cast<float4*>(qr + j + half) =
-          make_float4(q1.x * c.x + q0.x * sn.x, q1.y * c.y + q0.y * sn.y,
-                      q1.z * c.z + q0.z * sn.z, q1.w * c.w + q0.w * sn.w);
-      const float ka[4] = {k0.x * c.x - k1.x * sn.x, k0.y * c.y - k1.y * sn.y,
-                           k0.z * c.z - k1.z * sn.z, k0.w * c.w - k1.w * sn.w};
-      const float kb[4] = {k1.x * c.x + k0.x * sn.x, k1.y * c.y + k0.y * sn.y,
-                           k1.z * c.z + k0.z * sn.z, k1.w * c.w + k0.w * sn.w};
+    const float4 q0 = t[0], q1 = t[1], k0 = t[2], k1 = t[3], v0 = t[4], v1 = t[5];
+    const float4 c = *reinterpret_cast<const float4*>(cs + j);
+    const float4 sn = *reinterpret_cast<const float4*>(cs + half + j);
+    *reinterpret_cast<float4*>(qr + j) =
+        make_float4(q0.x * c.x - q1.x * sn.x, q0.y * c.y - q1.y * sn.y,
+                    q0.z * c.z - q1.z * sn.z, q0.w * c.w - q1.w * sn.w);
+    *reinterpret_cast<float4*>(qr + j + half) =
+        make_float4(q1.x * c.x + q0.x * sn.x, q1.y * c.y + q0.y * sn.y,
+                    q1.z * c.z + q0.z * sn.z, q1.w * c.w + q0.w * sn.w);
+    const float ka[4] = {k0.x * c.x - k1.x * sn.x, k0.y * c.y - k1.y * sn.y,
+                         k0.z * c.z - k1.z * sn.z, k0.w * c.w - k1.w * sn.w};
+    const float kb[4] = {k1.x * c.x + k0.x * sn.x, k1.y * c.y + k0.y * sn.y,
+                         k1.z * c.z + k0.z * sn.z, k1.w * c.w + k0.w * sn.w};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        kp[j + e] = from_f<T>(ka[e]);
-        kp[j + half + e] = from_f<T>(kb[e]);
-      }
-      const float va[4] = {v0.x, v0.y, v0.z, v0.w};
-      const float vb[4] = {v1.x, v1.y, v1.z, v1.w};
+    for (int e = 0; e < 4; ++e) {
+      kp[j + e] = from_f<T>(ka[e]);
+      kp[j + half + e] = from_f<T>(kb[e]);
+    }
+    const float va[4] = {v0.x, v0.y, v0.z, v0.w};
+    const float vb[4] = {v1.x, v1.y, v1.z, v1.w};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        vs[(j + e) * (kQkvRows + 1) + rr] = va[e];
-        vs[(j + half + e) * (kQkvRows + 1) + rr] = vb[e];
-      }
+    for (int e = 0; e < 4; ++e) {
+      vs[(j + e) * (kQkvRows + 1) + rr] = va[e];
+      vs[(j + half + e) * (kQkvRows + 1) + rr] = vb[e];
     }
   }
   __syncthreads();
@@ -216,11 +230,10 @@ __global__ __launch_bounds__(kQkvThreads) void qkv_rope_scatter_kernel(
   for (int e = threadIdx.x; e < hd * kQkvRows; e += kQkvThreads) {
     const int rr2 = e % kQkvRows;
     const int hi = e / kQkvRows;
-    const int m2 = m0 + rr2;
-    if (m2 >= M) continue;
-    const int r = tb.row_req[m2];
-    const int pos = tb.row_pos[m2];
-    vt[(((size_t)r * H + h) * Lp + (pos & ~31)) * hd + hi * 32 + (pos & 31)] =
+    if (m0 + rr2 >= M) continue;
+    const int r2 = s_req[rr2];
+    const int pos2 = s_pos[rr2];
+    vt[(((size_t)r2 * H + h) * Lp + (pos2 & ~31)) * hd + hi * 32 + (pos2 & 31)] =
         from_f<T>(vs[hi * (kQkvRows + 1) + rr2]);
   }
 }
@@ -232,9 +245,11 @@ __global__ __launch_bounds__(kThreads) void swiglu_kernel(const int* __restrict_
                                                           const float* __restrict__ P, int S,
                                                           size_t p_stride, int F,
                                                           float* __restrict__ act) {
-  const int M = min(*nrows, m_cap);
+  // rows up to m_cap are read (all readable) while the row count loads;
+  // only the pass's rows are stored
+  const int nr = *nrows;
   const int F4 = F / 4;
-  const size_t total = (size_t)M * F4;
+  const size_t total = (size_t)m_cap * F4;
   const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
   for (size_t idx = (size_t)blockIdx.x * kThreads + threadIdx.x; idx < total;
        idx += (size_t)gridDim.x * kThreads) {
@@ -245,9 +260,10 @@ __global__ __launch_bounds__(kThreads) void swiglu_kernel(const int* __restrict_
     const float* const pp[2] = {pr + f, pr + F + f};
     add_splits<2, G>(t, pp, p_stride, S);
     const float4 g = t[0], u = t[1];
-    *reinterpret_cast<float4*>(act + m * F + f) =
-        make_float4(g.x / (1.f + expf(-g.x)) * u.x, g.y / (1.f + expf(-g.y)) * u.y,
-                    g.z / (1.f + expf(-g.z)) * u.z, g.w / (1.f + expf(-g.w)) * u.w);
+    if ((int)m < min(nr, m_cap))
+      *reinterpret_cast<float4*>(act + m * F + f) =
+          make_float4(g.x / (1.f + expf(-g.x)) * u.x, g.y / (1.f + expf(-g.y)) * u.y,
+                      g.z / (1.f + expf(-g.z)) * u.z, g.w / (1.f + expf(-g.w)) * u.w);
   }
 }
 
@@ -329,7 +345,7 @@ hipError_t launch_add_rmsnorm(DType t, const int* nrows, int m_cap, float* x, co
 hipError_t launch_qkv_rope_scatter(DType t, PassTable tb, int m_cap, const float* P, int S,
                                    size_t p_stride, int d, int H, int hd, const float* rope_cs,
                                    float* q_out, void* kc, void* vt, int Lp, hipStream_t st) {
-  if (hd > 128 || hd % 8 != 0) return hipErrorInvalidValue;
+  if (hd > 128 || hd % 8 != 0 || m_cap < 1) return hipErrorInvalidValue;
   const dim3 grid((m_cap + kQkvRows - 1) / kQkvRows, H);
   // unsplit input (many-row passes): a small register set keeps occupancy up
   if (S <= 1) {
