@@ -108,20 +108,112 @@ __global__ __launch_bounds__(256) void moe_route_kernel(PassTable tb, int m_cap,
     }
 }
 
-// One workgroup of 16 waves; wave w owns experts w, w+16, w+32, w+48.  The
-// assignment list (row-major [row][slot]) is staged in LDS when it fits.  An
-// expert's assignments are found 64 at a time by ballot; a first pass counts
-// them, an exclusive scan over experts gives the offsets, and a second pass
-// writes each assignment's packed position (its rank among the expert's
-// matches in list order, i.e. row order) -- deterministic.
+// Plan of the (row, slot) assignments: per-expert counts, offsets (experts
+// in id order) and row lists, rows ascending within an expert -- a stable
+// counting sort, deterministic.  One workgroup of 16 waves; the list
+// (row-major [row][slot]) is staged in LDS in chunks of 64 assignments.
+//  1. each wave takes whole chunks: a lane finds the lanes of its chunk with
+//     the same expert by six ballots over the bits of the expert id (its
+//     rank among them and their count) and the chunk's first such lane
+//     records the count per (chunk, expert);
+//  2. one thread per expert sums its chunk counts in chunk order (its
+//     per-chunk bases); an exclusive scan over experts gives the offsets;
+//  3. each assignment's packed position = offset of its expert + base of its
+//     chunk for that expert + its rank in the chunk.
+// Lists longer than kPlanLds assignments use moe_plan_wide_kernel.
 constexpr int kPlanWaves = 16;
-constexpr int kPlanLds = 16384;    // assignments staged in LDS (larger lists read global memory)
+constexpr int kPlanLds = 16384;                 // assignments staged in LDS
+constexpr int kPlanChunks = kPlanLds / 64;
 
 __global__ __launch_bounds__(64 * kPlanWaves) void moe_plan_kernel(
     const int* __restrict__ nrows, int m_cap, const int* __restrict__ sel_g, int E, int top_k,
     int* __restrict__ e_count, int* __restrict__ e_off, int* __restrict__ row_of,
     int* __restrict__ pos, int* __restrict__ n_assign) {
   __shared__ int sel_s[kPlanLds];
+  __shared__ unsigned short ccnt[kPlanChunks][kMaxE];   // per (chunk, expert): count, then base
+  __shared__ int off[kMaxE + 1];
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int wave = t >> 6;
+  const int M = min(*nrows, m_cap);
+  const int total = M * top_k;                  // <= kPlanLds (checked at launch)
+  const int nch = (total + 63) / 64;
+  for (int a = t; a < total; a += 64 * kPlanWaves) sel_s[a] = sel_g[a];
+  for (int i = t; i < nch * kMaxE; i += 64 * kPlanWaves) ccnt[i / kMaxE][i % kMaxE] = 0;
+  __syncthreads();
+  const unsigned long long below = (1ull << lane) - 1ull;
+  // 1. per-chunk counts and ranks (ranks kept in registers, up to 16 chunks
+  //    per wave)
+  constexpr int kMaxOwn = kPlanChunks / kPlanWaves;
+  int rank[kMaxOwn];
+#pragma unroll
+  for (int i = 0; i < kMaxOwn; ++i) {
+    const int ch = wave + i * kPlanWaves;
+    rank[i] = 0;
+    if (ch >= nch) continue;                     // wave-uniform
+    const int a = ch * 64 + lane;
+    const bool live = a < total;
+    const int e = live ? sel_s[a] : kMaxE;      // kMaxE: no expert (7 bits)
+    unsigned long long peers = ~0ull;
+#pragma unroll
+    for (int b = 0; b < 7; ++b) {
+      const unsigned long long bb = __ballot((e >> b) & 1);
+      peers &= ((e >> b) & 1) ? bb : ~bb;
+    }
+    rank[i] = __popcll(peers & below);
+    if (live && rank[i] == 0) ccnt[ch][e] = (unsigned short)__popcll(peers);
+  }
+  __syncthreads();
+  // 2. per-expert chunk bases (chunk order), then offsets over experts
+  if (t < E) {
+    int run = 0;
+    for (int ch = 0; ch < nch; ++ch) {
+      const int c = ccnt[ch][t];
+      ccnt[ch][t] = (unsigned short)run;
+      run += c;
+    }
+    off[t] = run;                                // count, scanned below
+  }
+  __syncthreads();
+  if (t == 0) {
+    int run = 0;
+    for (int e = 0; e < E; ++e) {
+      const int c = off[e];
+      off[e] = run;
+      run += c;
+    }
+    off[E] = run;
+    *n_assign = run;
+  }
+  __syncthreads();
+  if (t < E) {
+    e_off[t] = off[t];
+    e_count[t] = off[t + 1] - off[t];
+  }
+  // 3. packed positions
+#pragma unroll
+  for (int i = 0; i < kMaxOwn; ++i) {
+    const int ch = wave + i * kPlanWaves;
+    if (ch >= nch) continue;
+    const int a = ch * 64 + lane;
+    if (a >= total) continue;
+    const int e = sel_s[a];
+    const int q = off[e] + ccnt[ch][e] + rank[i];
+    row_of[q] = a / top_k;
+    pos[a] = q;
+  }
+}
+
+// Lists longer than kPlanLds (many-row refreshes of several requests): one
+// workgroup of 16 waves, wave w owns experts w, w+16, ...; an expert's
+// assignments are found 64 at a time by ballot, a first pass counts them,
+// an exclusive scan over experts gives the offsets, a second pass writes
+// each assignment's position (its rank among the expert's matches in list
+// order) -- the same result as moe_plan_kernel.
+__global__ __launch_bounds__(64 * kPlanWaves) void moe_plan_wide_kernel(
+    const int* __restrict__ nrows, int m_cap, const int* __restrict__ sel, int E, int top_k,
+    int* __restrict__ e_count, int* __restrict__ e_off, int* __restrict__ row_of,
+    int* __restrict__ pos, int* __restrict__ n_assign) {
   __shared__ int cnt[kMaxE];
   __shared__ int off[kMaxE + 1];
   const int t = threadIdx.x;
@@ -129,11 +221,6 @@ __global__ __launch_bounds__(64 * kPlanWaves) void moe_plan_kernel(
   const int wave = t >> 6;
   const int M = min(*nrows, m_cap);
   const int total = M * top_k;
-  const bool staged = total <= kPlanLds;
-  if (staged)
-    for (int a = t; a < total; a += 64 * kPlanWaves) sel_s[a] = sel_g[a];
-  __syncthreads();
-  const int* sel = staged ? sel_s : sel_g;
   const unsigned long long below = (1ull << lane) - 1ull;
   for (int e = wave; e < E; e += kPlanWaves) {
     int c = 0;
@@ -239,8 +326,12 @@ hipError_t launch_moe_plan(const int* nrows, int m_cap, const int* sel, int E, i
                            int* e_count, int* e_off, int* row_of, int* pos, int* n_assign,
                            hipStream_t st) {
   if (E > kMaxE) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(moe_plan_kernel, dim3(1), dim3(64 * kPlanWaves), 0, st, nrows, m_cap, sel,
-                     E, top_k, e_count, e_off, row_of, pos, n_assign);
+  if ((size_t)m_cap * top_k <= (size_t)kPlanLds)
+    hipLaunchKernelGGL(moe_plan_kernel, dim3(1), dim3(64 * kPlanWaves), 0, st, nrows, m_cap, sel,
+                       E, top_k, e_count, e_off, row_of, pos, n_assign);
+  else
+    hipLaunchKernelGGL(moe_plan_wide_kernel, dim3(1), dim3(64 * kPlanWaves), 0, st, nrows, m_cap,
+                       sel, E, top_k, e_count, e_off, row_of, pos, n_assign);
   return hipGetLastError();
 }
 
