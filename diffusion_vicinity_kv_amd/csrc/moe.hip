@@ -23,15 +23,14 @@ namespace {
 constexpr int kMaxE = 64;
 constexpr int kMaxTopK = 8;
 
-// One workgroup per row.  Each of its four waves takes a quarter of d, lane e
+// One workgroup per row.  Each of its NW waves takes 1/NW of d, lane e
 // accumulating expert e's partial dot product (the row read as wave-uniform
-// float4s, the router row as 16-byte vectors, eight vectors in flight); the
-// quarters are added in order through LDS, then wave 0 picks the top_k by
-// repeated wave argmax.
-constexpr int kRouteUnroll = 8;
-
-template <typename T>
-__global__ __launch_bounds__(256) void moe_route_kernel(PassTable tb, int m_cap,
+// float4s, the router row as 16-byte vectors, UNR vectors in flight); the
+// parts are added in wave order through LDS, then wave 0 picks the top_k by
+// repeated wave argmax.  Eight waves with sixteen vectors in flight cover a
+// 2048-wide row in two rounds of loads.
+template <typename T, int NW, int UNR>
+__global__ __launch_bounds__(64 * NW) void moe_route_kernel(PassTable tb, int m_cap,
                                                         const float* __restrict__ f, int d,
                                                         const T* __restrict__ Wr, int E, int top_k,
                                                         const float* __restrict__ router_bias,
@@ -40,21 +39,21 @@ __global__ __launch_bounds__(256) void moe_route_kernel(PassTable tb, int m_cap,
                                                         float* __restrict__ gate,
                                                         float* __restrict__ rlog) {
   constexpr int VEC = 16 / sizeof(T);          // weights per 16-byte load
-  __shared__ float part[4][kMaxE];
+  __shared__ float part[NW][kMaxE];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int m = blockIdx.x;
   if (m >= min(*tb.nrows, m_cap)) return;
-  const int dq = d / 4;                        // this wave's quarter of d
+  const int dq = d / NW;                       // this wave's share of d
   const float* fr = f + (size_t)m * d + wave * dq;
   const T* w = Wr + (size_t)min(lane, E - 1) * d + wave * dq;
   float s = 0.f;
-  for (int k0 = 0; k0 < dq; k0 += kRouteUnroll * VEC) {
-    V16 wv[kRouteUnroll];
+  for (int k0 = 0; k0 < dq; k0 += UNR * VEC) {
+    V16 wv[UNR];
 #pragma unroll
-    for (int u = 0; u < kRouteUnroll; ++u) wv[u] = ld16(w + k0 + u * VEC);
+    for (int u = 0; u < UNR; ++u) wv[u] = ld16(w + k0 + u * VEC);
 #pragma unroll
-    for (int u = 0; u < kRouteUnroll; ++u)
+    for (int u = 0; u < UNR; ++u)
 #pragma unroll
       for (int e = 0; e < VEC; e += 4) {
         const float4 x = *reinterpret_cast<const float4*>(fr + k0 + u * VEC + e);
@@ -68,7 +67,9 @@ __global__ __launch_bounds__(256) void moe_route_kernel(PassTable tb, int m_cap,
   const int r = tb.row_req[m];
   float v = -INFINITY;
   if (lane < E) {
-    v = ((part[0][lane] + part[1][lane]) + part[2][lane]) + part[3][lane];
+    v = part[0][lane];
+#pragma unroll
+    for (int q = 1; q < NW; ++q) v += part[q][lane];
     if (router_bias)
       v += router_bias[(((size_t)r * n_layers + layer) * n_blocks + tb.req_blk[r]) * E + lane];
     rlog[(size_t)m * E + lane] = v;
@@ -308,17 +309,31 @@ hipError_t launch_moe_route(DType t, PassTable tb, int m_cap, const float* f, in
                             const void* Wr, int E, int top_k, const float* router_bias,
                             int n_layers, int n_blocks, int layer, int* sel, float* gate,
                             float* rlog, hipStream_t st) {
-  if (E > kMaxE || top_k > kMaxTopK || top_k > E || d % (4 * kRouteUnroll * 8) != 0)
-    return hipErrorInvalidValue;
+  if (E > kMaxE || top_k > kMaxTopK || top_k > E) return hipErrorInvalidValue;
   const dim3 grid(m_cap);
-  if (t == DType::F32)
-    hipLaunchKernelGGL(moe_route_kernel<float>, grid, dim3(256), 0, st, tb, m_cap, f, d,
-                       static_cast<const float*>(Wr), E, top_k, router_bias, n_layers, n_blocks,
-                       layer, sel, gate, rlog);
-  else
-    hipLaunchKernelGGL(moe_route_kernel<bf16>, grid, dim3(256), 0, st, tb, m_cap, f, d,
-                       static_cast<const bf16*>(Wr), E, top_k, router_bias, n_layers, n_blocks,
-                       layer, sel, gate, rlog);
+  const int vec = t == DType::F32 ? 4 : 8;
+  // wide rows: eight waves, sixteen vectors in flight; else four waves, eight
+  if (d % (8 * 16 * vec) == 0) {
+    if (t == DType::F32)
+      hipLaunchKernelGGL((moe_route_kernel<float, 8, 16>), grid, dim3(512), 0, st, tb, m_cap, f, d,
+                         static_cast<const float*>(Wr), E, top_k, router_bias, n_layers,
+                         n_blocks, layer, sel, gate, rlog);
+    else
+      hipLaunchKernelGGL((moe_route_kernel<bf16, 8, 16>), grid, dim3(512), 0, st, tb, m_cap, f, d,
+                         static_cast<const bf16*>(Wr), E, top_k, router_bias, n_layers,
+                         n_blocks, layer, sel, gate, rlog);
+  } else if (d % (4 * 8 * vec) == 0) {
+    if (t == DType::F32)
+      hipLaunchKernelGGL((moe_route_kernel<float, 4, 8>), grid, dim3(256), 0, st, tb, m_cap, f, d,
+                         static_cast<const float*>(Wr), E, top_k, router_bias, n_layers,
+                         n_blocks, layer, sel, gate, rlog);
+    else
+      hipLaunchKernelGGL((moe_route_kernel<bf16, 4, 8>), grid, dim3(256), 0, st, tb, m_cap, f, d,
+                         static_cast<const bf16*>(Wr), E, top_k, router_bias, n_layers,
+                         n_blocks, layer, sel, gate, rlog);
+  } else {
+    return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
