@@ -316,7 +316,7 @@ __global__ __launch_bounds__(256 * kKeyGroups) void attn_kernel(
 
 // Combine the key splits of each row: out = sum_s 2^(m_s - M) O_s /
 // sum_s 2^(m_s - M) l_s per head, splits taken in order; float4 of the row
-// per thread.  With at most eight splits every record a row may have is
+// per thread.  With at most sixteen splits every record a row may have is
 // loaded first -- before the row's request and key count are known, which
 // only decide how many of them count (ns) -- so the row's loads take one
 // memory round trip; records past ns are ignored (never read as numbers).
@@ -360,7 +360,7 @@ __device__ __forceinline__ float4 merge_fixed(const float* __restrict__ o_part,
   return make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
 }
 
-// Any split count (more than eight splits: the long-context plans).
+// Any split count (more than sixteen splits).
 template <int HD>
 __device__ __forceinline__ float4 merge_loop(int ns, const float* __restrict__ o_part,
                                              const float* __restrict__ ml_part, size_t base0,
@@ -409,6 +409,14 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(PassTable tb, int keys_
     case 6: res = merge_fixed<HD, 6>(o_part, ml_part, base0, sstride, i4, tb.req_len, r, keys_per_split, valid); break;
     case 7: res = merge_fixed<HD, 7>(o_part, ml_part, base0, sstride, i4, tb.req_len, r, keys_per_split, valid); break;
     case 8: res = merge_fixed<HD, 8>(o_part, ml_part, base0, sstride, i4, tb.req_len, r, keys_per_split, valid); break;
+    case 9: res = merge_fixed<HD, 9>(o_part, ml_part, base0, sstride, i4, tb.req_len, r, keys_per_split, valid); break;
+    case 10: res = merge_fixed<HD, 10>(o_part, ml_part, base0, sstride, i4, tb.req_len, r, keys_per_split, valid); break;
+    case 11: res = merge_fixed<HD, 11>(o_part, ml_part, base0, sstride, i4, tb.req_len, r, keys_per_split, valid); break;
+    case 12: res = merge_fixed<HD, 12>(o_part, ml_part, base0, sstride, i4, tb.req_len, r, keys_per_split, valid); break;
+    case 13: res = merge_fixed<HD, 13>(o_part, ml_part, base0, sstride, i4, tb.req_len, r, keys_per_split, valid); break;
+    case 14: res = merge_fixed<HD, 14>(o_part, ml_part, base0, sstride, i4, tb.req_len, r, keys_per_split, valid); break;
+    case 15: res = merge_fixed<HD, 15>(o_part, ml_part, base0, sstride, i4, tb.req_len, r, keys_per_split, valid); break;
+    case 16: res = merge_fixed<HD, 16>(o_part, ml_part, base0, sstride, i4, tb.req_len, r, keys_per_split, valid); break;
     default: {
       const int L = valid ? tb.req_len[r] : 0;
       const int ns = min(n_split, (L + keys_per_split - 1) / keys_per_split);
