@@ -23,14 +23,18 @@ namespace {
 constexpr int kMaxE = 64;
 constexpr int kMaxTopK = 8;
 
-// One workgroup per row.  Each of its NW waves takes 1/NW of d, lane e
-// accumulating expert e's partial dot product (the row read as wave-uniform
-// float4s, the router row as 16-byte vectors, UNR vectors in flight); the
-// parts are added in wave order through LDS, then wave 0 picks the top_k by
-// repeated wave argmax.  Eight waves with sixteen vectors in flight cover a
-// 2048-wide row in two rounds of loads.
-template <typename T, int NW, int UNR>
-__global__ __launch_bounds__(64 * NW) void moe_route_kernel(PassTable tb, int m_cap,
+// One workgroup of eight waves per row.  Wave w takes experts
+// [w*epw, (w+1)*epw) (epw = ceil(E/8) <= 8): its lanes walk the row d in
+// 16-byte steps, every lane loading the same stretch of each of the wave's
+// router rows (one contiguous kilobyte per load instruction) and of the
+// activation row, and keeping one partial dot product per expert; the
+// partials are summed across the wave, the logits meet in LDS, and wave 0
+// picks the top_k by repeated wave argmax.  The row count and the row's
+// request are read together with the row.
+constexpr int kRouteWaves = 8;
+
+template <typename T>
+__global__ __launch_bounds__(64 * kRouteWaves) void moe_route_kernel(PassTable tb, int m_cap,
                                                         const float* __restrict__ f, int d,
                                                         const T* __restrict__ Wr, int E, int top_k,
                                                         const float* __restrict__ router_bias,
@@ -39,37 +43,54 @@ __global__ __launch_bounds__(64 * NW) void moe_route_kernel(PassTable tb, int m_
                                                         float* __restrict__ gate,
                                                         float* __restrict__ rlog) {
   constexpr int VEC = 16 / sizeof(T);          // weights per 16-byte load
-  __shared__ float part[NW][kMaxE];
+  constexpr int EPW = kMaxE / kRouteWaves;     // most experts a wave takes
+  __shared__ float logit[kMaxE];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int m = blockIdx.x;
-  if (m >= min(*tb.nrows, m_cap)) return;
-  const int dq = d / NW;                       // this wave's share of d
-  const float* fr = f + (size_t)m * d + wave * dq;
-  const T* w = Wr + (size_t)min(lane, E - 1) * d + wave * dq;
-  float s = 0.f;
-  for (int k0 = 0; k0 < dq; k0 += UNR * VEC) {
-    V16 wv[UNR];
+  const int m = blockIdx.x;                    // < m_cap: the row is readable
+  const int nr = *tb.nrows;
+  const int r = tb.row_req[m];
+  const int epw = (E + kRouteWaves - 1) / kRouteWaves;
+  const int e0 = wave * epw;
+  const float* fr = f + (size_t)m * d;
+  // rows past the wave's experts repeat the last expert (not stored)
+  const T* wr[EPW];
 #pragma unroll
-    for (int u = 0; u < UNR; ++u) wv[u] = ld16(w + k0 + u * VEC);
+  for (int i = 0; i < EPW; ++i) wr[i] = Wr + (size_t)min(e0 + min(i, epw - 1), E - 1) * d;
+  float s[EPW];
 #pragma unroll
-    for (int u = 0; u < UNR; ++u)
+  for (int i = 0; i < EPW; ++i) s[i] = 0.f;
+#pragma unroll 2
+  for (int k0 = lane * VEC; k0 < d; k0 += 64 * VEC) {
+    float xv[VEC];
 #pragma unroll
-      for (int e = 0; e < VEC; e += 4) {
-        const float4 x = *reinterpret_cast<const float4*>(fr + k0 + u * VEC + e);
-        s += x.x * v16_get<T>(wv[u], e) + x.y * v16_get<T>(wv[u], e + 1) +
-             x.z * v16_get<T>(wv[u], e + 2) + x.w * v16_get<T>(wv[u], e + 3);
-      }
+    for (int q = 0; q < VEC; q += 4) {
+      const float4 x = *reinterpret_cast<const float4*>(fr + k0 + q);
+      xv[q] = x.x;
+      xv[q + 1] = x.y;
+      xv[q + 2] = x.z;
+      xv[q + 3] = x.w;
+    }
+    V16 wv[EPW];
+#pragma unroll
+    for (int i = 0; i < EPW; ++i) wv[i] = ld16(wr[i] + k0);
+#pragma unroll
+    for (int i = 0; i < EPW; ++i)
+#pragma unroll
+      for (int q = 0; q < VEC; ++q) s[i] += xv[q] * v16_get<T>(wv[i], q);
   }
-  part[wave][lane] = s;
+#pragma unroll
+  for (int i = 0; i < EPW; ++i) s[i] = wave_sum(s[i]);
+  if (m >= min(nr, m_cap)) return;             // the whole workgroup
+  if (lane == 0)
+#pragma unroll
+    for (int i = 0; i < EPW; ++i)
+      if (i < epw && e0 + i < E) logit[e0 + i] = s[i];
   __syncthreads();
   if (wave != 0) return;
-  const int r = tb.row_req[m];
   float v = -INFINITY;
   if (lane < E) {
-    v = part[0][lane];
-#pragma unroll
-    for (int q = 1; q < NW; ++q) v += part[q][lane];
+    v = logit[lane];
     if (router_bias)
       v += router_bias[(((size_t)r * n_layers + layer) * n_blocks + tb.req_blk[r]) * E + lane];
     rlog[(size_t)m * E + lane] = v;
@@ -309,31 +330,18 @@ hipError_t launch_moe_route(DType t, PassTable tb, int m_cap, const float* f, in
                             const void* Wr, int E, int top_k, const float* router_bias,
                             int n_layers, int n_blocks, int layer, int* sel, float* gate,
                             float* rlog, hipStream_t st) {
-  if (E > kMaxE || top_k > kMaxTopK || top_k > E) return hipErrorInvalidValue;
-  const dim3 grid(m_cap);
   const int vec = t == DType::F32 ? 4 : 8;
-  // wide rows: eight waves, sixteen vectors in flight; else four waves, eight
-  if (d % (8 * 16 * vec) == 0) {
-    if (t == DType::F32)
-      hipLaunchKernelGGL((moe_route_kernel<float, 8, 16>), grid, dim3(512), 0, st, tb, m_cap, f, d,
-                         static_cast<const float*>(Wr), E, top_k, router_bias, n_layers,
-                         n_blocks, layer, sel, gate, rlog);
-    else
-      hipLaunchKernelGGL((moe_route_kernel<bf16, 8, 16>), grid, dim3(512), 0, st, tb, m_cap, f, d,
-                         static_cast<const bf16*>(Wr), E, top_k, router_bias, n_layers,
-                         n_blocks, layer, sel, gate, rlog);
-  } else if (d % (4 * 8 * vec) == 0) {
-    if (t == DType::F32)
-      hipLaunchKernelGGL((moe_route_kernel<float, 4, 8>), grid, dim3(256), 0, st, tb, m_cap, f, d,
-                         static_cast<const float*>(Wr), E, top_k, router_bias, n_layers,
-                         n_blocks, layer, sel, gate, rlog);
-    else
-      hipLaunchKernelGGL((moe_route_kernel<bf16, 4, 8>), grid, dim3(256), 0, st, tb, m_cap, f, d,
-                         static_cast<const bf16*>(Wr), E, top_k, router_bias, n_layers,
-                         n_blocks, layer, sel, gate, rlog);
-  } else {
+  if (E > kMaxE || top_k > kMaxTopK || top_k > E || d % (64 * vec) != 0 || m_cap < 1)
     return hipErrorInvalidValue;
-  }
+  const dim3 grid(m_cap);
+  if (t == DType::F32)
+    hipLaunchKernelGGL(moe_route_kernel<float>, grid, dim3(64 * kRouteWaves), 0, st, tb, m_cap, f,
+                       d, static_cast<const float*>(Wr), E, top_k, router_bias, n_layers, n_blocks,
+                       layer, sel, gate, rlog);
+  else
+    hipLaunchKernelGGL(moe_route_kernel<bf16>, grid, dim3(64 * kRouteWaves), 0, st, tb, m_cap, f,
+                       d, static_cast<const bf16*>(Wr), E, top_k, router_bias, n_layers, n_blocks,
+                       layer, sel, gate, rlog);
   return hipGetLastError();
 }
 

@@ -88,6 +88,9 @@ bool make_layout(const dinfer_model_cfg* m, const dinfer_decode_cfg* dc, int max
     if (m->n_experts > 64) return bad("n_experts above 64 is not supported");
     if (m->top_k > 8) return bad("top_k above 8 is not supported");
     if (m->expert_ffn < 1 || m->shared_ffn < 1) return bad("expert_ffn and shared_ffn must be positive");
+    // the router's lanes walk d in 16-byte steps, 64 lanes at a time
+    if (m->d_model % (m->dtype == DINFER_BF16 ? 512 : 256) != 0)
+      return bad("MoE d_model must be a multiple of 512 (bf16) or 256 (f32)");
   } else if (m->ffn_dim < 1) {
     return bad("ffn_dim must be positive");
   }

@@ -65,7 +65,9 @@ typedef enum {
 typedef enum { DINFER_F32 = 0, DINFER_BF16 = 1 } dinfer_dtype;
 
 /* Model: a bidirectional (non-causal) pre-norm transformer with RoPE,
- * RMSNorm and SwiGLU; n_experts == 0 selects the dense FFN. */
+ * RMSNorm and SwiGLU; n_experts == 0 selects the dense FFN.  Supported:
+ * head_dim 64 or 128; MoE with n_experts <= 64, top_k <= 8 and d_model a
+ * multiple of 512 (bf16) / 256 (f32); others give DINFER_E_ARG at init. */
 typedef struct {
   int32_t n_layers, d_model, n_heads, head_dim, ffn_dim, vocab, mask_id;
   int32_t n_experts, top_k, expert_ffn, shared_ffn;

@@ -36,9 +36,11 @@ def vocab_stats(z, plant_id, plant_bias, mask_id, k=8):
     """Per-row vocab statistics of logits z [R, V].
 
     Returns dict: argmax [R] int64, conf [R] float32 (max softmax probability),
-    lse [R] float64, topk_id [R,k] int64, topk_p [R,k] float64, and kth_gap [R]:
+    lse [R] float64, topk_id [R,k] int64, topk_p [R,k] float64, kth_gap [R]:
     the k-th largest minus the (k+1)-th largest biased logit (how far the
-    top-k set is from changing; reported, not used by the method).
+    top-k set is from changing), and rank_gap [R]: the smallest gap between
+    consecutive logits among the k+1 largest (how far the top-k set or its
+    order is from changing); both reported, not used by the method.
     The biased logits are rounded to fp32 before any order decision; the
     probabilities are then computed in fp64 from those fp32 values.
     """
@@ -60,10 +62,12 @@ def vocab_stats(z, plant_id, plant_bias, mask_id, k=8):
     order = np.argsort(-z32, axis=1, kind="stable")[:, :k + 1]   # value desc, id asc
     kth_gap = (np.take_along_axis(zd, order[:, k - 1:k], axis=1)
                - np.take_along_axis(zd, order[:, k:k + 1], axis=1))[:, 0]
+    ztop = np.take_along_axis(zd, order, axis=1)
+    rank_gap = np.min(ztop[:, :-1] - ztop[:, 1:], axis=1)
     order = order[:, :k]
     topk_p = np.take_along_axis(e, order, axis=1) / Z[:, None]
     return {"argmax": argmax, "conf": conf, "lse": lse, "topk_id": order, "topk_p": topk_p,
-            "logit_max": zmax, "kth_gap": kth_gap}
+            "logit_max": zmax, "kth_gap": kth_gap, "rank_gap": rank_gap}
 
 
 def credit_update(credit, tracked, argmax, conf, masked, gamma, lam):

@@ -181,7 +181,8 @@ def decision_margin(st, masked, credit, d, committed, still=None):
     |ln p - ln tau|, |ln c - ln kappa| (credit on), ln p1 - ln p2 between the
     best and second-best confidence (decides the fallback); over committed rows
     the top-1 minus top-2 logit (decides the committed id); with smoothing on,
-    over rows still masked the 8th minus 9th logit (decides the kept top-8)."""
+    over rows still masked the smallest gap between consecutive logits among
+    the 9 largest (decides the kept top-8 and the order their ids are kept in)."""
     from .decode import candidates
     C = candidates(masked, d.hierarchical)
     if len(C) == 0:
@@ -198,8 +199,8 @@ def decision_margin(st, masked, credit, d, committed, still=None):
     tp = st["topk_p"][committed]
     if tp.shape[1] > 1 and len(committed):
         m = min(m, float(np.min(np.log(tp[:, 0]) - np.log(np.maximum(tp[:, 1], tiny)))))
-    if d.smooth_alpha != 0.0 and still is not None and still.any() and "kth_gap" in st:
-        m = min(m, float(np.min(st["kth_gap"][still])))
+    if d.smooth_alpha != 0.0 and still is not None and still.any() and "rank_gap" in st:
+        m = min(m, float(np.min(st["rank_gap"][still])))
     return float(m)
 
 

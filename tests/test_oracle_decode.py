@@ -49,6 +49,12 @@ def test_argmax_and_topk_bruteforce_with_ties_and_mask():
         assert st["argmax"][r] == want[0]
         assert st["topk_id"][r].tolist() == want
         assert V - 1 not in st["topk_id"][r]
+        # reported gaps, from the brute-force order: k-th minus (k+1)-th, and
+        # the smallest consecutive gap among the k+1 largest
+        top9 = sorted(row, reverse=True)[:9]
+        assert st["kth_gap"][r] == pytest.approx(top9[7] - top9[8], abs=1e-12)
+        assert st["rank_gap"][r] == pytest.approx(min(a - b for a, b in zip(top9, top9[1:])),
+                                                  abs=1e-12)
 
 
 def test_planted_confidence_closed_form():
