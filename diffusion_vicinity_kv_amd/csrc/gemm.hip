@@ -230,17 +230,25 @@ __global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(const float* __res
 // Grouped projection of the MoE experts: workgroup (expert e, column group,
 // 64-row tile) multiplies rows [off_e + 64 t, min(off_e + count_e, +64)) of
 // the packed assignment list -- gathered from A through row_of[] when given,
-// else read in place -- with expert e's weights W + e*N*K.
+// else read in place -- with expert e's weights W + e*N*K.  The row tiles of
+// one (expert, column group) get workgroup ids 8 apart: workgroups are dealt
+// to the eight XCDs in id order, so they run side by side on one XCD and
+// the second reads the weights the first brings into that XCD's L2 (an
+// expert that many rows prefer needs two row tiles).
 template <typename TW, int NT, int NW>
 __global__ __launch_bounds__(NW * 64) void gemm_grouped_kernel(
     const float* __restrict__ A, const int* __restrict__ row_of, const int* __restrict__ e_count,
     const int* __restrict__ e_off, const TW* __restrict__ W, float* __restrict__ out, int N, int K,
-    int n_tiles, int m_tiles) {
+    int n_tiles, int m_tiles, int n_pairs) {
   constexpr int KC = 4 * Mfma<TW>::KSTEP;
   const int bid = blockIdx.x;
-  const int tile = bid % n_tiles;
-  const int mt = (bid / n_tiles) % m_tiles;
-  const int e = bid / (n_tiles * m_tiles);
+  const int grp = bid / (8 * m_tiles);
+  const int rem = bid % (8 * m_tiles);
+  const int mt = rem / 8;
+  const int pair = grp * 8 + rem % 8;          // e * n_tiles + tile
+  if (pair >= n_pairs) return;
+  const int tile = pair % n_tiles;
+  const int e = pair / n_tiles;
   const int cnt = e_count[e];
   const int M = min(64, cnt - mt * 64);
   if (M <= 0) return;
@@ -336,13 +344,16 @@ hipError_t launch_gemm_grouped(DType t, const float* A, const int* row_of, const
   if (N % 128 != 0 || K % gemm_k_chunk(t) != 0) return hipErrorInvalidValue;
   const int n_tiles = N / 128;                 // 4 waves x 32 columns
   const int m_tiles = (max_rows + 63) / 64;
-  const dim3 grid(E * n_tiles * m_tiles);
+  const int n_pairs = E * n_tiles;
+  const dim3 grid((n_pairs + 7) / 8 * 8 * m_tiles);
   if (t == DType::F32)
     hipLaunchKernelGGL((gemm_grouped_kernel<float, 2, 4>), grid, dim3(256), 0, st, A, row_of,
-                       e_count, e_off, static_cast<const float*>(W), out, N, K, n_tiles, m_tiles);
+                       e_count, e_off, static_cast<const float*>(W), out, N, K, n_tiles, m_tiles,
+                       n_pairs);
   else
     hipLaunchKernelGGL((gemm_grouped_kernel<bf16, 2, 4>), grid, dim3(256), 0, st, A, row_of,
-                       e_count, e_off, static_cast<const bf16*>(W), out, N, K, n_tiles, m_tiles);
+                       e_count, e_off, static_cast<const bf16*>(W), out, N, K, n_tiles, m_tiles,
+                       n_pairs);
   return hipGetLastError();
 }
 
