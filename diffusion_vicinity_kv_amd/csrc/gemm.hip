@@ -342,13 +342,21 @@ hipError_t launch_gemm_grouped(DType t, const float* A, const int* row_of, const
                                const int* e_off, int E, int max_rows, const void* W, float* out,
                                int N, int K, hipStream_t st) {
   if (N % 128 != 0 || K % gemm_k_chunk(t) != 0) return hipErrorInvalidValue;
-  const int n_tiles = N / 128;                 // 4 waves x 32 columns
   const int m_tiles = (max_rows + 63) / 64;
+  // bf16 with 256-column groups: eight waves x 32 columns (two waves per
+  // SIMD hide each other's latency; four waves of this tile need one SIMD
+  // each); else four waves x 32 columns
+  const bool wide = t == DType::BF16 && N % 256 == 0;
+  const int n_tiles = N / (wide ? 256 : 128);
   const int n_pairs = E * n_tiles;
   const dim3 grid((n_pairs + 7) / 8 * 8 * m_tiles);
   if (t == DType::F32)
     hipLaunchKernelGGL((gemm_grouped_kernel<float, 2, 4>), grid, dim3(256), 0, st, A, row_of,
                        e_count, e_off, static_cast<const float*>(W), out, N, K, n_tiles, m_tiles,
+                       n_pairs);
+  else if (wide)
+    hipLaunchKernelGGL((gemm_grouped_kernel<bf16, 2, 8>), grid, dim3(512), 0, st, A, row_of,
+                       e_count, e_off, static_cast<const bf16*>(W), out, N, K, n_tiles, m_tiles,
                        n_pairs);
   else
     hipLaunchKernelGGL((gemm_grouped_kernel<bf16, 2, 4>), grid, dim3(256), 0, st, A, row_of,
