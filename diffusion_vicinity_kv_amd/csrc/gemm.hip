@@ -216,14 +216,25 @@ __global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(const float* __res
                                                               float* __restrict__ P,
                                                               const int* __restrict__ m_dev,
                                                               int m_cap, int N, int K,
-                                                              int n_tiles, int S) {
+                                                              int n_tiles, int S, int m_tiles) {
   constexpr int KC = 4 * Mfma<TW>::KSTEP;
+  constexpr int ROWS = 16 * MT;
+  // work item (split, column group) = split * n_tiles + tile; its m_tiles row
+  // tiles get workgroup ids 8 apart, so they run side by side on one XCD and
+  // share the weights through its L2 (ids past the items exit)
   const int bid = blockIdx.x;
-  const int tile = bid % n_tiles;
-  const int split = bid / n_tiles;
+  const int grp = bid / (8 * m_tiles);
+  const int rem = bid % (8 * m_tiles);
+  const int mt = rem / 8;
+  const int item = grp * 8 + rem % 8;
+  if (item >= n_tiles * S) return;
+  const int tile = item % n_tiles;
+  const int split = item / n_tiles;
   const int C = K / KC;
-  const int M = m_dev ? min(*m_dev, m_cap) : m_cap;
-  skinny_tile<TW, MT, NT, NW, GUARD>(A, nullptr, M, W, N, K, P + (size_t)split * m_cap * N, N,
+  const int M = (m_dev ? min(*m_dev, m_cap) : m_cap) - mt * ROWS;
+  if (M <= 0) return;
+  skinny_tile<TW, MT, NT, NW, GUARD>(A + (size_t)mt * ROWS * K, nullptr, min(M, ROWS), W, N, K,
+                                     P + ((size_t)split * m_cap + (size_t)mt * ROWS) * N, N,
                                      tile * (16 * NT * NW), (split * C) / S, ((split + 1) * C) / S);
 }
 
@@ -287,14 +298,17 @@ template <typename TW, int MT, int NT, int NW>
 hipError_t run_skinny(const GemmPlan& p, const float* A, const void* W, float* out,
                       const int* m_dev, int m_cap, int N, int K, hipStream_t st) {
   const int n_tiles = N / (16 * NT * NW);
+  const int mtiles = p.mtiles > 1 ? p.mtiles : 1;
+  if (m_cap > 16 * MT * mtiles) return hipErrorInvalidValue;
+  const dim3 grid((n_tiles * p.splits + 7) / 8 * 8 * mtiles);
   if (p.guard)
-    hipLaunchKernelGGL((gemm_skinny_kernel<TW, MT, NT, NW, true>), dim3(n_tiles * p.splits),
-                       dim3(NW * 64), 0, st, A, static_cast<const TW*>(W), out, m_dev, m_cap, N,
-                       K, n_tiles, p.splits);
+    hipLaunchKernelGGL((gemm_skinny_kernel<TW, MT, NT, NW, true>), grid, dim3(NW * 64), 0, st, A,
+                       static_cast<const TW*>(W), out, m_dev, m_cap, N, K, n_tiles, p.splits,
+                       mtiles);
   else
-    hipLaunchKernelGGL((gemm_skinny_kernel<TW, MT, NT, NW, false>), dim3(n_tiles * p.splits),
-                       dim3(NW * 64), 0, st, A, static_cast<const TW*>(W), out, m_dev, m_cap, N,
-                       K, n_tiles, p.splits);
+    hipLaunchKernelGGL((gemm_skinny_kernel<TW, MT, NT, NW, false>), grid, dim3(NW * 64), 0, st, A,
+                       static_cast<const TW*>(W), out, m_dev, m_cap, N, K, n_tiles, p.splits,
+                       mtiles);
   return hipGetLastError();
 }
 
@@ -402,6 +416,7 @@ GemmPlan plan_gemm(DType t, int m_cap, int N, int K, int target_wgs) {
   GemmPlan p{};
   if (m_cap > 128) {
     p.kind = 1;
+    p.mtiles = 1;
     p.mt = p.nt = 0;
     p.nw = N > 128 ? 4 : 2;
     const int mtiles = (m_cap + 127) / 128;
@@ -424,11 +439,21 @@ GemmPlan plan_gemm(DType t, int m_cap, int N, int K, int target_wgs) {
   p.kind = 0;
   p.mt = (m_cap + 15) / 16;
   if (p.mt < 1) p.mt = 1;
+  p.mtiles = 1;
   p.guard = (m_cap % 16) != 0;   // exact-size operands with ragged rows only
   const int chunks = K / gemm_k_chunk(t);
   if (t == DType::BF16 && N % 256 == 0 && N / 256 >= 32 && p.mt <= 4) {
     p.nt = 2;
     p.nw = 8;
+  } else if (t == DType::BF16 && N % 256 == 0 && p.mt > 4) {
+    // 65..128 rows: two 64-row tiles on eight-wave groups (two waves per
+    // SIMD; one 128-row tile needs four waves of 400+ registers, one per
+    // SIMD), the tiles of a column group sharing its weights through L2
+    p.mt = 4;
+    p.mtiles = 2;
+    p.nt = 2;
+    p.nw = 8;
+    p.guard = (m_cap % 64) != 0;   // the second tile reads rows 64..127
   } else if (N % 128 == 0 && N / 128 >= 16) {
     p.nt = 2;
     p.nw = 4;
@@ -439,11 +464,11 @@ GemmPlan plan_gemm(DType t, int m_cap, int N, int K, int target_wgs) {
   const int n_tiles = N / (16 * p.nt * p.nw);
   // as many K splits as still fit one round of target_wgs workgroups: a
   // partial round costs a whole round, and each split adds an fp32 partial
-  int s = target_wgs / n_tiles;
+  int s = target_wgs / (n_tiles * p.mtiles);
   if (s < 1) s = 1;
   if (s > chunks) s = chunks;
   p.splits = s;
-  p.grid = n_tiles * s;
+  p.grid = n_tiles * s * p.mtiles;
   return p;
 }
 

@@ -35,6 +35,7 @@ struct GemmPlan {
   int nw;        // skinny: waves per workgroup; fat: column waves (2 or 4)
   int guard;     // skinny: 1 = A has exactly m_cap rows; 0 = A readable up to 16*mt rows
   int splits;    // K splits (partials out[s][m][n], summed by the consumer)
+  int mtiles;    // skinny: row tiles of 16*mt rows per (column group, split); 1 or 2
   int grid;
 };
 GemmPlan plan_gemm(DType t, int m_cap, int N, int K, int target_wgs);

@@ -146,8 +146,10 @@ bool make_layout(const dinfer_model_cfg* m, const dinfer_decode_cfg* dc, int max
     l.g_lm.grid /= l.g_lm.splits;
     l.g_lm.splits = 1;
   }
-  // the step's activation buffers hold at least 16*mt rows: no row guards
-  for (GemmPlan* g : {&l.g_qkv_s, &l.g_o_s, &l.g_gu_s, &l.g_d_s, &l.g_lm}) g->guard = 0;
+  // the step's activation buffers hold at least 16*mt rows: no row guards,
+  // except where two row tiles read past the step's rows
+  for (GemmPlan* g : {&l.g_qkv_s, &l.g_o_s, &l.g_gu_s, &l.g_d_s, &l.g_lm})
+    g->guard = g->kind == 0 && g->mtiles > 1 && l.m_step < 16 * g->mt * g->mtiles;
   l.g_qkv_r = plan_gemm(dt, l.m_ref, 3 * d, d, tw);
   l.g_o_r = plan_gemm(dt, l.m_ref, d, d, tw);
   l.g_gu_r = plan_gemm(dt, l.m_ref, 2 * Fd, d, tw);
@@ -715,7 +717,8 @@ dinfer_status dinfer_refresh_kv(dinfer_ctx* c, const uint8_t* h_req_mask) {
       m_eff = L.m_ref;
       pq = L.g_qkv_r, po = L.g_o_r, pg = L.g_gu_r, pd = L.g_d_r;
     }
-    for (GemmPlan* g : {&pq, &po, &pg, &pd}) g->guard = 0;   // buffers hold m_all rows
+    for (GemmPlan* g : {&pq, &po, &pg, &pd})   // buffers hold m_all rows
+      g->guard = g->kind == 0 && g->mtiles > 1 && L.m_all < 16 * g->mt * g->mtiles;
     c->ref_mcap = m_eff;
     c->ref_q = pq, c->ref_o = po, c->ref_g = pg, c->ref_d = pd;
   }

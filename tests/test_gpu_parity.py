@@ -274,7 +274,8 @@ def test_pack_linear_layout(shape, dt):
 
 @pytest.mark.parametrize("M,N,K,dt", [(64, 24576, 4096, "bf16"), (64, 12288, 4096, "bf16"),
                                       (48, 4096, 12288, "bf16"), (37, 4096, 4096, "bf16"),
-                                      (128, 1024, 2048, "bf16"), (300, 384, 512, "bf16"),
+                                      (128, 1024, 2048, "bf16"), (100, 512, 1024, "bf16"),
+                                      (96, 768, 512, "bf16"), (300, 384, 512, "bf16"),
                                       (1024, 1536, 1024, "bf16"), (48, 768, 256, "f32"),
                                       (200, 256, 768, "f32")])
 def test_linear_parity(M, N, K, dt):
