@@ -185,3 +185,37 @@ def test_full_width_moe(n_layers):
         assert safe.sum() >= 16
     if safe.any():
         assert row_err[safe].max() <= 2e-2
+
+
+def test_tiny_moe_long_refresh_wide_plan():
+    """A refresh with more expert assignments than the plan stages in LDS
+    (2112 positions x top-8 of 8 experts = 16896 > 16384) takes the per-expert
+    ballot plan; with every expert chosen by every row there is no routing
+    decision, so the layer-1 cache after the refresh (which every expert's
+    row list feeds) and the next step's logits match the oracle to fp32
+    rounding.  The step's 48 window rows take the staged plan."""
+    note("tiny fp32 MoE, all 8 experts chosen, 2112 positions: wide plan in the refresh")
+    wc = small_workload(F=0, experts=8, top_k=8, Fe=128, Fs=256, pref_bias=1.0, pref_count=2,
+                        prompt=(2080, 2080), gen=32, seed=16)
+    eng, w, req, tokens = build(wc)
+    run = oracle_runs(wc, w, req)[0]
+    assert run.L * wc.model.top_k > 16384
+    run.start_block(0)
+    eng.refresh_kv()
+    torch.cuda.synchronize()
+    v = eng.view()
+    for key in ("k", "v"):
+        g = cache_rows(v, key, 1, 0, run.L)
+        o = run.cache[key][1]
+        rms = float(np.sqrt(np.mean(o ** 2)))
+        err = float(np.max(np.abs(g - o))) / rms
+        note(f"  layer-1 cache {key}: max rel err {err:.2e}")
+        assert err <= 1e-5
+    eng.denoise_step()
+    torch.cuda.synchronize()
+    glog = eng.view()["logits"].cpu().numpy()
+    ol = run.denoise_logits()
+    rms = float(np.sqrt(np.mean(ol ** 2)))
+    err = float(np.max(np.abs(glog[: ol.shape[0]] - ol))) / rms
+    note(f"  step logits: max rel err {err:.2e}")
+    assert err <= 1e-5
