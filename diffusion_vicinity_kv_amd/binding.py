@@ -35,7 +35,7 @@ class DecodeCfg(C.Structure):
                 ("credit_weight", C.c_float), ("credit_decay", C.c_float),
                 ("credit_kappa", C.c_float), ("smooth_alpha", C.c_float),
                 ("smooth_topk", C.c_int32), ("hierarchical", C.c_int32),
-                ("graph_unroll", C.c_int32)]
+                ("graph_unroll", C.c_int32), ("eos_id", C.c_int32)]
 
 
 _PP = C.POINTER(C.c_void_p)

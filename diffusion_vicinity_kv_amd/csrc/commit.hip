@@ -12,7 +12,11 @@
 //   smoothing: each position still masked afterwards keeps its top-8 ids with
 //             probabilities renormalised to sum 1 for the next step's soft
 //             embedding
-//   block_done: set when no MASK remains in the block
+//   end-of-sequence (optional): a committed EOS fixes every still-masked
+//             response position after it to EOS (dInfer news article, section
+//             "系统级压榨": computation after EOS is skipped)
+//   block_done: 1 when no MASK remains in the block, 2 when none remains in
+//             the whole response either (the request is complete)
 #include "common.h"
 #include "kernels.h"
 
@@ -75,7 +79,25 @@ __global__ __launch_bounds__(64) void commit_kernel(CommitArgs a) {
   }
   if (commit) tok[j] = am;
   if (inb) a.commit_mask[row] = commit ? 1 : 0;
-  const bool still = masked && !commit;
+  // end-of-sequence (early stop): a committed EOS at p fixes every
+  // still-masked response position after p to EOS -- the block's lanes here,
+  // the positions past the block by the wave's loop.  There is no EOS below
+  // the lowest one committed now (a masked position after an earlier EOS
+  // would have been filled), so p is the response's first EOS.
+  unsigned long long eb = 0ull;
+  bool filled = false;
+  if (a.eos_id >= 0) {
+    eb = __ballot(commit && am == a.eos_id);
+    if (eb != 0ull) {
+      const int p = __ffsll((long long)eb) - 1;   // block offset
+      filled = masked && !commit && j > p;
+      if (filled) tok[j] = a.eos_id;
+      int* full = a.tokens + (size_t)r * a.max_len;
+      for (int i = bs + B + j; i < a.req_len[r]; i += 64)
+        if (full[i] == a.mask_id) full[i] = a.eos_id;
+    }
+  }
+  const bool still = masked && !commit && !filled;
   if (inb) {
     if (still) {
       const float* tp = a.topk_p + (size_t)row * 8;
@@ -93,10 +115,24 @@ __global__ __launch_bounds__(64) void commit_kernel(CommitArgs a) {
   }
   const unsigned long long sb = __ballot(still);
   const unsigned long long cb = __ballot(commit);
+  // with an EOS id, a finished block also finishes the request when no masked
+  // response position is left after it (2 = request complete): certainly if
+  // this step committed an EOS, else by a scan of the positions past the block
+  bool complete = false;
+  if (a.eos_id >= 0 && sb == 0ull) {
+    if (eb != 0ull) {
+      complete = true;
+    } else {
+      const int* full = a.tokens + (size_t)r * a.max_len;
+      bool left = false;
+      for (int i = bs + B + j; i < a.req_len[r]; i += 64) left = left || full[i] == a.mask_id;
+      complete = !__any(left);
+    }
+  }
   if (j == 0) {
     a.step_count[r] += 1;
     a.commit_count[r] += __popcll(cb);
-    if (sb == 0ull) a.block_done[r] = 1;
+    if (sb == 0ull) a.block_done[r] = complete ? 2 : 1;
   }
 }
 

@@ -121,9 +121,12 @@ hipError_t launch_moe_combine(const int* nrows, int m_cap, float* x, const float
 // ---- decode state ---------------------------------------------------------------
 struct CommitArgs {
   int batch, B, max_len, mask_id, hierarchical;
+  int eos_id;            // -1: none
   float tau, kappa, gamma, lambda;
   const int* req_bs;
   const int* req_active;
+  const int* req_len;    // L_r
+  const int* req_blk;    // current block index (response start = bs - blk * B)
   int* tokens;
   const int* argmax;
   const float* conf;

@@ -100,6 +100,8 @@ bool make_layout(const dinfer_model_cfg* m, const dinfer_decode_cfg* dc, int max
   if (dc->vicinity_w < 0) return bad("vicinity_w must be >= 0");
   if (dc->smooth_topk != 8) return bad("smooth_topk must be 8");
   if (dc->graph_unroll < 0 || dc->graph_unroll > 64) return bad("graph_unroll must be in 0..64");
+  if (dc->eos_id != -1 && (dc->eos_id < 0 || dc->eos_id >= m->vocab || dc->eos_id == m->mask_id))
+    return bad("eos_id must be -1 or a token id in [0, vocab) other than mask_id");
   if (max_batch < 1 || max_len < 1) return bad("max_batch and max_len must be positive");
   const DType dt = m->dtype == DINFER_F32 ? DType::F32 : DType::BF16;
   const int d = m->d_model, F = m->ffn_dim, V = m->vocab;
@@ -447,6 +449,9 @@ dinfer_status launch_commit_step(dinfer_ctx* c) {
   a.lambda = c->dc.credit_weight;
   a.req_bs = tb.req_bs;
   a.req_active = tb.req_active;
+  a.req_len = tb.req_len;
+  a.req_blk = tb.req_blk;
+  a.eos_id = c->dc.eos_id;
   a.tokens = c->tokens;
   a.argmax = c->at<int>(L.off_argmax);
   a.conf = c->at<float>(L.off_conf);
@@ -773,6 +778,12 @@ dinfer_status dinfer_advance_blocks(dinfer_ctx* c, uint8_t* h_needs_refresh, int
   for (int r = 0; r < c->batch; ++r) {
     if (h_needs_refresh) h_needs_refresh[r] = 0;
     if (c->finished[r] || !c->refreshed[r] || !done[r]) continue;
+    if (done[r] == 2) {   // end-of-sequence: no masked response position is left
+      c->finished[r] = 1;
+      c->refreshed[r] = 0;
+      c->step_dirty = true;
+      continue;
+    }
     c->blk[r] += 1;
     c->refreshed[r] = 0;
     c->step_dirty = true;

@@ -35,6 +35,7 @@ def _decode_struct(d, graph_unroll: int) -> B.DecodeCfg:
     s.smooth_topk = int(d.smooth_topk)
     s.hierarchical = int(bool(d.hierarchical))
     s.graph_unroll = int(graph_unroll)
+    s.eos_id = int(getattr(d, "eos_id", -1))
     return s
 
 

@@ -88,6 +88,14 @@ typedef struct {
   int32_t hierarchical;      /* 1 = only run midpoints are candidates            */
   int32_t graph_unroll;      /* steps per captured graph in run_to_completion;
                                 0 = launch eagerly                               */
+  int32_t eos_id;            /* -1 = none.  Else the end-of-sequence token (early
+                                stop, dInfer news article, section "系统级压榨"):
+                                once a request holds it at a response position
+                                p, every still-masked response position after p
+                                takes it, and a request left with no masked
+                                response position is complete (its remaining
+                                blocks get neither refresh nor steps).  Must be
+                                in [0, vocab) and differ from mask_id.          */
 } dinfer_decode_cfg;
 
 /* Device pointers to the weights (borrowed).  Per-layer entries are host
@@ -139,7 +147,8 @@ typedef struct {
   float* smooth_p;           /* [batch*B][8] renormalised smoothing probs        */
   uint8_t* smooth_valid;     /* [batch*B]                                        */
   uint8_t* commit_mask;      /* [batch*B] 1 = committed by the last commit       */
-  int32_t* block_done;       /* [batch] 1 once the current block has no MASK     */
+  int32_t* block_done;       /* [batch] 1 once the current block has no MASK,
+                                2 once the whole response has none (EOS)        */
   int32_t* step_count;       /* [batch] steps taken in the current block         */
   int32_t* commit_count;     /* [batch] tokens committed in total                */
   void* kv_k;                /* [n_layers][max_batch][H][kv_len][hd] K, RoPE'd  */

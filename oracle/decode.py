@@ -129,3 +129,19 @@ def smoothing_state(topk_id, topk_p):
 def soft_embedding(e_mask, e_ids, p_tilde, alpha):
     """(1-alpha) E[MASK] + alpha * sum_j p~_j E[id_j]; e_ids [n, k, d], p_tilde [n, k]."""
     return (1.0 - alpha) * e_mask[None, :] + alpha * np.einsum("nk,nkd->nd", p_tilde, e_ids)
+
+
+def eos_fill(tokens, P, L, mask_id, eos_id):
+    """Early stop at the end-of-sequence token (dInfer news article, section
+    "系统级压榨": computation after EOS is skipped).  Reading: once the
+    response [P, L) holds eos_id at some position, every response position
+    after the first such position that is still MASK becomes eos_id; the
+    positions before it are decoded as usual.  tokens is changed in place;
+    returns True when no MASK is left in the response."""
+    resp = tokens[P:L]
+    if eos_id >= 0:
+        at = np.nonzero(resp == eos_id)[0]
+        if len(at):
+            tail = resp[at[0] + 1:]
+            tail[tail == mask_id] = eos_id
+    return not bool((resp == mask_id).any())

@@ -9,7 +9,9 @@ between; dInfer news article, section "削减计算成本：邻近KV缓存刷新
 iteration recomputes KV only for the current block and a small neighbourhood
 and leaves distant entries as they are):
 
-  for each block [bs, be) of the response, left to right:
+  for each block [bs, be) of the response, left to right, while the
+  response holds MASK (an end-of-sequence token fills the rest; see
+  decode.eos_fill):
       full refresh: every position's K, V recomputed from hard embeddings
       credit, tracked ids and smoothing state reset
       while the block holds MASK:
@@ -24,7 +26,7 @@ from __future__ import annotations
 import numpy as np
 
 from .decode import (F32, vocab_stats, credit_update, select_commits, smoothing_state,
-                     soft_embedding)
+                     soft_embedding, eos_fill)
 from .model import OracleModel
 
 
@@ -49,6 +51,7 @@ class OracleRun:
         self.block = -1
         self.steps = []            # steps per finished block
         self.records = []          # per-step details
+        self.complete = False      # no MASK left in the response (end-of-sequence)
         self._k = dcfg.smooth_topk
         self.refresh_route_margin = np.inf        # MoE routing near-ties (reported)
         self.step_route_margin_rows = None
@@ -140,6 +143,8 @@ class OracleRun:
         T, fallback = select_commits(masked, st["conf"], self.credit, d.tau, d.credit_kappa,
                                      d.hierarchical)
         self.tokens[self.bs + T] = st["argmax"][T]
+        self.complete = eos_fill(self.tokens, self.P, self.L, self.m.mask_id,
+                                 getattr(d, "eos_id", -1))
         still = self.block_masked()
         ids, pt = smoothing_state(st["topk_id"], st["topk_p"])
         self.smooth_ids = np.where(still[:, None], ids, self.smooth_ids)
@@ -159,6 +164,7 @@ class OracleRun:
 
     def run(self, max_steps_per_block=None):
         cap = self.B if max_steps_per_block is None else max_steps_per_block
+        self.complete = False
         for k in range(self.n_blocks):
             self.start_block(k)
             while self.block_masked().any():
@@ -166,6 +172,8 @@ class OracleRun:
                     raise RuntimeError("block did not finish within its step cap")
                 self.step()
             self.steps.append(self.block_steps)
+            if self.complete:      # end-of-sequence: nothing masked is left
+                break
         return self.tokens
 
 

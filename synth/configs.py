@@ -58,6 +58,7 @@ class DecodeCfg:
     smooth_topk: int = 8
     hierarchical: bool = False
     min_commit: int = 1
+    eos_id: int = -1                # -1: no end-of-sequence token (early stop off)
 
 
 @dataclass(frozen=True)

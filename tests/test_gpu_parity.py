@@ -202,6 +202,32 @@ def test_batched_tiny_run_matches_per_request_oracle():
         assert np.array_equal(tokens.cpu().numpy()[r][: run.L], run.tokens), r
 
 
+@pytest.mark.parametrize("unroll", [0, 3])
+def test_eos_early_stop_matches_oracle(unroll):
+    """End-of-sequence early stop: the EOS id is the first token request 0's
+    plain run commits, so that request stops inside its first block (the rest
+    of its response filled with EOS, no further refresh); every request's
+    tokens equal its oracle run with the same EOS id, and the refreshes are
+    the blocks the oracle runs."""
+    note(f"tiny fp32 batch 3 with an EOS id, unroll={unroll}")
+    wc = small_workload(batch=3, prompt=(40, 90), gen=64, bias=6.0 + float(np.log(4094.0)) - 2.0,
+                        prob=(0.5, 0.9), seed=3)
+    w = synth.make_weights(wc.model, wc.seed, device="cuda")
+    req = synth.make_requests(wc)
+    plain = oracle.run_request(wc.model, wc.decode, w, req, r=0)
+    eos = int(plain.tokens[plain.P + int(plain.records[0]["commits"][0])])
+    wce = wc.with_decode(eos_id=eos)
+    eng, _, _, tokens = build(wce, graph_unroll=unroll, weights=w, req=req)
+    stats = eng.run_to_completion()
+    torch.cuda.synchronize()
+    runs = [oracle.run_request(wce.model, wce.decode, w, req, r=r) for r in range(wce.batch)]
+    for r, run in enumerate(runs):
+        assert np.array_equal(tokens.cpu().numpy()[r][: run.L], run.tokens), r
+    assert len(runs[0].steps) < len(plain.steps)
+    assert stats["refreshes"] == sum(len(run.steps) for run in runs)
+    note(f"  refreshes {stats['refreshes']} (oracle blocks {[len(x.steps) for x in runs]})")
+
+
 @pytest.mark.parametrize("alpha", [0.0, 0.3])
 def test_bf16_small_lockstep(alpha):
     note(f"bf16 small lockstep alpha={alpha}")

@@ -89,3 +89,65 @@ def test_batch_requests_are_independent():
     req2["tokens"][2] = 7
     r1b = oracle.run_request(wc.model, wc.decode, w, req2, r=1)
     assert np.array_equal(r1.tokens, r1b.tokens) and r1.steps == r1b.steps
+
+
+def test_eos_fill_cases():
+    """End-of-sequence fill against a brute-force rewrite of the rule: after
+    the first EOS of the response every MASK becomes EOS; MASKs before it,
+    other tokens, and EOS ids in the prompt are left alone."""
+    from oracle.decode import eos_fill
+    M, E, P = 9, 5, 4
+    cases = [[1, 5, 2, 3, M, M, 7, M, M, M],       # EOS only in the prompt
+             [1, 2, 3, 4, M, 5, M, 7, M, 5],       # first response EOS at 5
+             [1, 2, 3, 4, 5, M, M, M, M, M],       # EOS at the response start
+             [1, 2, 3, 4, M, M, M, M, M, M],       # no EOS
+             [1, 2, 3, 4, 6, 7, 8, 5, 1, 2]]       # nothing masked
+    for c in cases:
+        t = np.array(c)
+        want = t.copy()
+        first = next((i for i in range(P, len(c)) if c[i] == E), None)
+        if first is not None:
+            for i in range(first + 1, len(c)):
+                if c[i] == M:
+                    want[i] = E
+        done = eos_fill(t, P, len(c), M, E)
+        assert t.tolist() == want.tolist()
+        assert done == (M not in want[P:].tolist())
+        t2 = np.array(c)
+        eos_fill(t2, P, len(c), M, -1)                # no EOS id: unchanged
+        assert t2.tolist() == c
+
+
+def test_eos_run_stops_after_the_first_eos():
+    """A run whose EOS id is a token the plain run commits early: the run
+    ends once nothing is masked, every response position after the first EOS
+    holds EOS, none before it is MASK, and no block after the EOS's block is
+    run; an EOS id the plain run never commits leaves the run unchanged."""
+    import dataclasses
+    wc = _small_workload(batch=1)
+    w = synth.make_weights(wc.model, wc.seed)
+    req = synth.make_requests(wc)
+
+    def run_with(eos):
+        dc = dataclasses.replace(wc.decode, eos_id=eos)
+        run = oracle.OracleRun(OracleModel(wc.model, w), dc, req["tokens"][0].numpy(),
+                               int(req["prompt_len"][0]), wc.gen_len, req["plant_id"][0].numpy(),
+                               float(req["plant_bias"][0]))
+        run.run()
+        return run
+
+    plain = run_with(-1)
+    P, L = plain.P, plain.L
+    # the first token committed by the plain run (block 0, step 0)
+    T0 = plain.records[0]["commits"]
+    eos = int(plain.tokens[P + int(T0[0])])
+    run = run_with(eos)
+    resp = run.tokens[P:L]
+    first = int(np.nonzero(resp == eos)[0][0])
+    assert (resp[first + 1:] == eos).all()
+    assert (resp[:first] != wc.model.mask_id).all()
+    assert len(run.steps) == first // wc.decode.block_len + 1
+    assert sum(run.steps) < sum(plain.steps)
+    unused = next(i for i in range(wc.model.vocab - 1) if i not in plain.tokens[P:L])
+    same = run_with(unused)
+    assert np.array_equal(same.tokens, plain.tokens) and same.steps == plain.steps
