@@ -21,7 +21,8 @@
 // Kernels:
 //  * skinny (M <= 128): the vicinity window holds tens of rows, so a layer is
 //    a weight stream.  A workgroup of NW waves owns 16*NT*NW output columns
-//    (64 to 256) over all rows and one K slice.  Each wave streams its own
+//    (64 to 256) over all rows (or one of two 64-row tiles, for 65..128 rows)
+//    and one K slice.  Each wave streams its own
 //    packed weight blocks straight into registers (one 16-byte load per lane
 //    per MFMA B operand), two K chunks ahead; the activation chunk is
 //    split into hi/lo planes in LDS, double-buffered, and shared by the
@@ -409,9 +410,11 @@ bool gemm_shape_ok(DType t, int N, int K) {
 // about 112 us at K = 4096; a partial element costs 8 bytes at about 4 TB/s).
 // Splitting pays where the tile count leaves a last round mostly empty.
 //
-// Skinny plan: a column group per workgroup as wide as still gives at least
-// 16 groups (256 columns = 8 waves x 32, else 128 = 4 x 32, else 64 = 4 x 16),
-// then K splits so that the grid is about target_wgs workgroups.
+// Skinny plan: up to 64 rows, 256-column groups (8 waves x 32) where that
+// gives at least 32 groups, else 128 (4 x 32) where it gives 16, else 64
+// (4 x 16); 65..128 rows with N % 256 == 0: two 64-row tiles on 256-column
+// eight-wave groups; then K splits so that the grid is about target_wgs
+// workgroups.
 GemmPlan plan_gemm(DType t, int m_cap, int N, int K, int target_wgs) {
   GemmPlan p{};
   if (m_cap > 128) {
