@@ -19,7 +19,7 @@ EXPORTS = [
     "dinfer_denoise_step", "dinfer_commit", "dinfer_advance_blocks", "dinfer_run_to_completion",
     "dinfer_get_step_view", "dinfer_vocab_stats_scratch_bytes", "dinfer_vocab_stats",
     "dinfer_step_graph", "dinfer_pack_linear", "dinfer_linear_out_elems", "dinfer_linear",
-    "dinfer_status_str", "dinfer_last_error", "dinfer_destroy",
+    "dinfer_status_str", "dinfer_last_error", "dinfer_destroy", "dinfer_refill", "dinfer_finished",
 ]
 
 
@@ -103,6 +103,8 @@ def load(path: str = LIB_PATH) -> C.CDLL:
         "dinfer_status_str": (C.c_char_p, [i32]),
         "dinfer_last_error": (C.c_char_p, []),
         "dinfer_destroy": (None, [vp]),
+        "dinfer_refill": (i32, [vp, i32, i32, i32]),
+        "dinfer_finished": (i32, [vp, C.POINTER(C.c_uint8)]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)

@@ -670,6 +670,39 @@ dinfer_status dinfer_set_batch(dinfer_ctx* c, int32_t batch, int32_t* d_tokens,
   return upload_step_table(c);
 }
 
+dinfer_status dinfer_refill(dinfer_ctx* c, int32_t slot, int32_t prompt_len, int32_t gen_len) {
+  if (!c) return fail(DINFER_E_ARG, "ctx is null");
+  if (c->state < 1) return fail(DINFER_E_STATE, "refill before set_batch");
+  if (slot < 0 || slot >= c->batch) return fail(DINFER_E_ARG, "slot out of range");
+  if (!c->finished[slot]) return fail(DINFER_E_STATE, "slot has not finished");
+  const int B = c->L.B;
+  if (prompt_len < 0 || gen_len < B || gen_len % B != 0)
+    return fail(DINFER_E_ARG, "gen_len must be a positive multiple of block_len");
+  if (prompt_len + gen_len > c->L.max_len)
+    return fail(DINFER_E_ARG, "prompt_len + gen_len exceeds max_len");
+  if (c->router_bias && gen_len / B > c->n_bias_blocks)
+    return fail(DINFER_E_ARG, "more blocks than the router bias holds");
+  c->P[slot] = prompt_len;
+  c->G[slot] = gen_len;
+  c->Lr[slot] = prompt_len + gen_len;
+  c->nblk[slot] = gen_len / B;
+  c->blk[slot] = 0;
+  c->finished[slot] = 0;
+  c->refreshed[slot] = 0;
+  c->step_dirty = true;
+  const Layout& L = c->L;
+  HIP_TRY(hipMemsetAsync(c->at<int>(L.off_done) + slot, 0, 4, c->stream));
+  HIP_TRY(hipMemsetAsync(c->at<int>(L.off_steps) + slot, 0, 4, c->stream));
+  HIP_TRY(hipMemsetAsync(c->at<int>(L.off_ccount) + slot, 0, 4, c->stream));
+  return DINFER_OK;
+}
+
+dinfer_status dinfer_finished(const dinfer_ctx* c, uint8_t* h_finished) {
+  if (!c || !h_finished) return fail(DINFER_E_ARG, "null argument");
+  for (int r = 0; r < c->batch; ++r) h_finished[r] = c->finished[r] ? 1 : 0;
+  return DINFER_OK;
+}
+
 dinfer_status dinfer_refresh_kv(dinfer_ctx* c, const uint8_t* h_req_mask) {
   if (!c) return fail(DINFER_E_ARG, "ctx is null");
   if (c->state < 1) return fail(DINFER_E_STATE, "refresh_kv before set_batch");
@@ -790,10 +823,12 @@ dinfer_status dinfer_advance_blocks(dinfer_ctx* c, uint8_t* h_needs_refresh, int
     if (c->blk[r] >= c->nblk[r]) {
       c->finished[r] = 1;
       c->blk[r] = c->nblk[r] - 1;
-    } else if (h_needs_refresh) {
-      h_needs_refresh[r] = 1;
     }
   }
+  // every unfinished request without a refresh of its current block (one
+  // that moved to a new block, or a refilled slot) needs one
+  if (h_needs_refresh)
+    for (int r = 0; r < c->batch; ++r) h_needs_refresh[r] = !c->finished[r] && !c->refreshed[r];
   if (h_unfinished) *h_unfinished = unfinished(c);
   return DINFER_OK;
 }

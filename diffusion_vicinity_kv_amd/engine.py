@@ -155,6 +155,67 @@ class Engine:
         return {"steps": s.steps, "refreshes": s.refreshes, "committed": s.committed,
                 "wall_ms": s.wall_ms, "refresh_ms": s.refresh_ms}
 
+    def refill(self, slot, prompt_len, gen_len):
+        B.check(self.lib.dinfer_refill(self.ctx, int(slot), int(prompt_len), int(gen_len)),
+                "dinfer_refill")
+
+    def finished(self):
+        f = (C.c_uint8 * max(self.batch, 1))()
+        B.check(self.lib.dinfer_finished(self.ctx, f), "dinfer_finished")
+        return [bool(f[i]) for i in range(self.batch)]
+
+    def run_queue(self, queue, max_steps=1 << 30):
+        """Continuous batching over the bound batch (set_batch holds the first
+        requests): whenever a slot finishes, its response is taken and the next
+        queued request is written into the slot's rows of the bound arrays and
+        restarted (dinfer_refill).  queue: list of dicts with "tokens" (int32
+        [max_len] row: prompt ids then mask_id), "prompt_len", "gen_len",
+        "plant_id" (int32 [max_len] row) and "plant_bias" (float).  Returns
+        {"outputs": [(slot request index, tokens row copy)], "steps",
+        "refreshes"}; request index i >= batch is queue[i - batch]."""
+        tokens, plant_id, plant_bias, router_bias = self._batch_refs
+        assert router_bias is None, "refill of MoE router bias rows is the caller's"
+        U = int(self._dc.graph_unroll)
+        owner = list(range(self.batch))          # request index held by each slot
+        nxt = self.batch
+        outputs, steps, refreshes = [], 0, 0
+        self.refresh_kv()
+        refreshes += self.batch
+        while True:
+            if U > 0:
+                self.step_graph(U)
+                steps += U
+            else:
+                self.denoise_step()
+                self.commit()
+                steps += 1
+            if steps > max_steps:
+                raise RuntimeError("run_queue: max_steps reached")
+            self.advance_blocks()
+            for sl, done in enumerate(self.finished()):
+                if not done or owner[sl] is None:
+                    continue
+                outputs.append((owner[sl], tokens[sl].clone()))
+                if nxt - self.batch < len(queue):
+                    q = queue[nxt - self.batch]
+                    tokens[sl].copy_(q["tokens"])
+                    if plant_id is not None:
+                        plant_id[sl].copy_(q["plant_id"])
+                    if plant_bias is not None:
+                        plant_bias[sl] = float(q["plant_bias"])
+                    self.refill(sl, q["prompt_len"], q["gen_len"])
+                    owner[sl] = nxt
+                    nxt += 1
+                else:
+                    owner[sl] = None
+            need, unfinished = self.advance_blocks()
+            if unfinished == 0:
+                break
+            if any(need):
+                self.refresh_kv(need)
+                refreshes += sum(need)
+        return {"outputs": outputs, "steps": steps, "refreshes": refreshes}
+
     # -- state views -----------------------------------------------------------
     def view(self):
         """Torch views (no copies) of the context's state buffers."""

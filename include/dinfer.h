@@ -231,11 +231,32 @@ dinfer_status dinfer_commit(dinfer_ctx* ctx);
 
 /* Iteration manager, block bookkeeping: waits for the stream, then for every
  * request whose block is done moves to its next block (or marks it
- * finished).  h_needs_refresh[r] (may be NULL) is set to 1 for requests that
- * moved to a new block and must be refreshed before the next step.
+ * finished).  h_needs_refresh[r] (may be NULL) is set to 1 for unfinished
+ * requests whose current block has not been refreshed (moved to a new block,
+ * or a refilled slot): they must be refreshed before the next step.
  * *h_unfinished (may be NULL) receives the number of unfinished requests. */
 dinfer_status dinfer_advance_blocks(dinfer_ctx* ctx, uint8_t* h_needs_refresh,
                                     int32_t* h_unfinished);
+
+/* Iteration manager, continuous batching (serving-characterisation page
+ * "服务掩码扩散大语言模型：来自真实硬件的特征分析与设计原则", section "Design
+ * Principles for Future Systems": step-level parallelism, request admission
+ * and eviction between shared forward passes): restart the finished slot
+ * `slot` with a new request.  Before the call the caller writes the new
+ * request into the slot's rows of the arrays given to dinfer_set_batch:
+ * tokens[slot] (prompt ids, then mask_id over the response), plant
+ * ids[slot] and plant bias[slot], and with an MoE router bias its
+ * [slot] entries.  The slot restarts at block 0, waits for the next
+ * dinfer_refresh_kv that selects it (dinfer_advance_blocks reports it in
+ * h_needs_refresh until then), and its step and commit counters restart at
+ * 0 (a reset enqueued on the context's stream).  DINFER_E_STATE if the slot
+ * has not finished; DINFER_E_ARG for lengths dinfer_set_batch would reject
+ * or, with a router bias, more blocks than dinfer_set_batch sized it for. */
+dinfer_status dinfer_refill(dinfer_ctx* ctx, int32_t slot, int32_t prompt_len, int32_t gen_len);
+
+/* h_finished[r] = 1 for every request r of the batch that has finished
+ * (host bookkeeping of dinfer_advance_blocks; no wait). */
+dinfer_status dinfer_finished(const dinfer_ctx* ctx, uint8_t* h_finished);
 
 /* Iteration manager: run every request of the batch to completion --
  * refresh at each block start, then denoise+commit steps replayed

@@ -5,6 +5,7 @@ import torch
 
 import oracle
 import synth
+from diffusion_vicinity_kv_amd.engine import Engine
 from diffusion_vicinity_kv_amd import binding as B
 from oracle.decode import credit_update, select_commits, smoothing_state, vocab_stats
 
@@ -226,6 +227,36 @@ def test_eos_early_stop_matches_oracle(unroll):
     assert len(runs[0].steps) < len(plain.steps)
     assert stats["refreshes"] == sum(len(run.steps) for run in runs)
     note(f"  refreshes {stats['refreshes']} (oracle blocks {[len(x.steps) for x in runs]})")
+
+
+@pytest.mark.parametrize("unroll", [0, 3])
+def test_continuous_batching_refill_matches_oracle(unroll):
+    """Six requests through two slots: a finished slot takes the next queued
+    request (dinfer_refill) while the other keeps decoding.  Requests are
+    independent, so every response equals its own oracle run."""
+    note(f"tiny fp32: 6 requests through 2 slots, unroll={unroll}")
+    wc = small_workload(batch=6, prompt=(40, 90), gen=64, bias=6.0 + float(np.log(4094.0)) - 2.0,
+                        prob=(0.5, 0.9), seed=5)
+    w = synth.make_weights(wc.model, wc.seed, device="cuda")
+    req = synth.make_requests(wc)
+    max_len = req["tokens"].shape[1]
+    eng = Engine(wc.model, wc.decode, w, 2, max_len, graph_unroll=unroll)
+    tokens = req["tokens"][:2].cuda().contiguous()
+    plant_id = req["plant_id"][:2].cuda().contiguous()
+    plant_bias = req["plant_bias"][:2].cuda().contiguous()
+    P, G = req["prompt_len"].tolist(), req["gen_len"].tolist()
+    eng.set_batch(tokens, P[:2], G[:2], plant_id, plant_bias)
+    queue = [{"tokens": req["tokens"][i].cuda(), "prompt_len": P[i], "gen_len": G[i],
+              "plant_id": req["plant_id"][i].cuda(), "plant_bias": float(req["plant_bias"][i])}
+             for i in range(2, 6)]
+    res = eng.run_queue(queue)
+    torch.cuda.synchronize()
+    got = sorted(i for i, _ in res["outputs"])
+    assert got == list(range(6)), got
+    for i, row in res["outputs"]:
+        run = oracle.run_request(wc.model, wc.decode, w, req, r=i)
+        assert np.array_equal(row.cpu().numpy()[: run.L], run.tokens), i
+    note(f"  steps {res['steps']}, refreshes {res['refreshes']}")
 
 
 @pytest.mark.parametrize("alpha", [0.0, 0.3])
