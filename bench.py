@@ -27,7 +27,7 @@ Also reported:
     step), scaled to the run's layer, refresh and step counts.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                       [--no-batch16] [--no-cpu-baseline]
+                       [--no-batch16] [--no-cpu-baseline] [--queue Q]
 """
 from __future__ import annotations
 
@@ -223,6 +223,36 @@ def run_workload(wc, w, req, unroll, warmup, steps):
             "committed": committed}
 
 
+def run_queue_workload(wc, w, n_requests, unroll):
+    """Continuous batching: n_requests of the workload's request mix through
+    its wc.batch slots (a finished slot takes the next queued request)."""
+    import torch
+    import synth
+    from diffusion_vicinity_kv_amd.engine import Engine
+    req = synth.make_requests(wc.with_(batch=n_requests))
+    max_len = req["tokens"].shape[1]
+    S = wc.batch
+    eng = Engine(wc.model, wc.decode, w, S, max_len, graph_unroll=unroll)
+    tokens = req["tokens"][:S].cuda().contiguous()
+    plant_id = req["plant_id"][:S].cuda().contiguous()
+    plant_bias = req["plant_bias"][:S].cuda().contiguous()
+    P, G = req["prompt_len"].tolist(), req["gen_len"].tolist()
+    eng.set_batch(tokens, P[:S], G[:S], plant_id, plant_bias)
+    queue = [{"tokens": req["tokens"][i].cuda(), "prompt_len": P[i], "gen_len": G[i],
+              "plant_id": req["plant_id"][i].cuda(), "plant_bias": float(req["plant_bias"][i])}
+             for i in range(S, n_requests)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    res = eng.run_queue(queue)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    eng.close()
+    committed = sum(G)        # every response position is committed (no end-of-sequence id)
+    return {"requests": n_requests, "slots": S, "value": round(committed / elapsed, 3),
+            "unit": "tokens/s", "wall_s": round(elapsed, 3), "steps": res["steps"],
+            "refreshes": res["refreshes"]}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -233,6 +263,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-batch16", action="store_true",
                     help="skip the batch-16 companion figure of the dense 8B workload")
+    ap.add_argument("--queue", type=int, default=0,
+                    help="also run this many batch-16-mix requests through the 16 slots with "
+                         "continuous batching (dense 8B workload only)")
     ap.add_argument("--kernel-only", action="store_true",
                     help="only the dominant-kernel timing loop (for counter runs)")
     ap.add_argument("--calib-copy", action="store_true",
@@ -289,6 +322,12 @@ def main():
                "step_latency_ms": round(r16["step_ms"], 3),
                "steps_per_run": r16["runs"][0]["steps"],
                "refresh_ms_per_run": round(r16["runs"][0]["refresh_ms"], 1)}
+        torch.cuda.empty_cache()
+    cb = None
+    if args.workload == "dense8b_b1" and args.queue > 0:
+        wc16 = synth.preset("dense8b_b16")
+        log(f"[bench] continuous batching: {args.queue} requests through {wc16.batch} slots")
+        cb = run_queue_workload(wc16, w, args.queue, args.unroll)
         torch.cuda.empty_cache()
 
     avg_ms, avg_bytes, avg_flops, rows = dominant_kernel_timing(wc, w)
@@ -361,6 +400,7 @@ def main():
                           "frac": round(step_bytes / (step_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
         "roofline": roofline,
         "batch16": b16,
+        "continuous_batching": cb,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
