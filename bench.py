@@ -27,7 +27,7 @@ Also reported:
     step), scaled to the run's layer, refresh and step counts.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                       [--no-batch16] [--no-cpu-baseline] [--queue Q]
+                       [--no-batch16] [--no-cpu-baseline] [--queue Q [--budget T]]
 """
 from __future__ import annotations
 
@@ -223,9 +223,11 @@ def run_workload(wc, w, req, unroll, warmup, steps):
             "committed": committed}
 
 
-def run_queue_workload(wc, w, n_requests, unroll):
+def run_queue_workload(wc, w, n_requests, unroll, budget=None):
     """Continuous batching: n_requests of the workload's request mix through
-    its wc.batch slots (a finished slot takes the next queued request)."""
+    its wc.batch slots (a finished slot takes the next queued request); with a
+    budget (rows per step) the deficit scheduler admits the refreshes.  All
+    requests arrive at the start, so a request's latency is its finish time."""
     import torch
     import synth
     from diffusion_vicinity_kv_amd.engine import Engine
@@ -243,14 +245,17 @@ def run_queue_workload(wc, w, n_requests, unroll):
              for i in range(S, n_requests)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    res = eng.run_queue(queue)
+    res = eng.run_queue(queue, token_budget=budget)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    lat = sorted(t - t0 for t in res["finish_time"].values())
     eng.close()
     committed = sum(G)        # every response position is committed (no end-of-sequence id)
     return {"requests": n_requests, "slots": S, "value": round(committed / elapsed, 3),
             "unit": "tokens/s", "wall_s": round(elapsed, 3), "steps": res["steps"],
-            "refreshes": res["refreshes"]}
+            "refreshes": res["refreshes"], "token_budget_per_step": budget,
+            "mean_latency_s": round(sum(lat) / len(lat), 3),
+            "p90_latency_s": round(lat[int(0.9 * (len(lat) - 1))], 3)}
 
 
 def main():
@@ -266,6 +271,9 @@ def main():
     ap.add_argument("--queue", type=int, default=0,
                     help="also run this many batch-16-mix requests through the 16 slots with "
                          "continuous batching (dense 8B workload only)")
+    ap.add_argument("--budget", type=int, default=0,
+                    help="with --queue: also run the queue with the deficit token-budget "
+                         "scheduler at this many rows per step")
     ap.add_argument("--kernel-only", action="store_true",
                     help="only the dominant-kernel timing loop (for counter runs)")
     ap.add_argument("--calib-copy", action="store_true",
@@ -329,6 +337,11 @@ def main():
         log(f"[bench] continuous batching: {args.queue} requests through {wc16.batch} slots")
         cb = run_queue_workload(wc16, w, args.queue, args.unroll)
         torch.cuda.empty_cache()
+        if args.budget > 0:
+            log(f"[bench] continuous batching, deficit budget {args.budget} rows/step")
+            cb = {"fifo": cb,
+                  "deficit": run_queue_workload(wc16, w, args.queue, args.unroll, args.budget)}
+            torch.cuda.empty_cache()
 
     avg_ms, avg_bytes, avg_flops, rows = dominant_kernel_timing(wc, w)
     if rows <= 128:

@@ -20,6 +20,7 @@ EXPORTS = [
     "dinfer_get_step_view", "dinfer_vocab_stats_scratch_bytes", "dinfer_vocab_stats",
     "dinfer_step_graph", "dinfer_pack_linear", "dinfer_linear_out_elems", "dinfer_linear",
     "dinfer_status_str", "dinfer_last_error", "dinfer_destroy", "dinfer_refill", "dinfer_finished",
+    "dinfer_pending_rows", "dinfer_sched_create", "dinfer_sched_destroy", "dinfer_sched_round",
 ]
 
 
@@ -105,6 +106,11 @@ def load(path: str = LIB_PATH) -> C.CDLL:
         "dinfer_destroy": (None, [vp]),
         "dinfer_refill": (i32, [vp, i32, i32, i32]),
         "dinfer_finished": (i32, [vp, C.POINTER(C.c_uint8)]),
+        "dinfer_pending_rows": (i32, [vp, C.POINTER(i32), C.POINTER(i32)]),
+        "dinfer_sched_create": (i32, [C.c_int64, i32, C.POINTER(vp)]),
+        "dinfer_sched_destroy": (None, [vp]),
+        "dinfer_sched_round": (i32, [vp, C.POINTER(i32), C.POINTER(i32), C.POINTER(C.c_uint8),
+                                     C.POINTER(C.c_int64)]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -180,3 +186,36 @@ def vocab_stats(logits, plant_id, plant_bias, mask_id, out, scratch, stream=None
                                 ptr(out["topk_id"]), ptr(out["topk_p"]), ptr(scratch),
                                 scratch.numel() * scratch.element_size(), stream_handle(stream))
     check(st, "dinfer_vocab_stats")
+
+
+class DeficitScheduler:
+    """dinfer_sched_* (deficit token-budget admission of whole refreshes):
+    owns the host object; round() marshals one round's per-slot rows."""
+
+    def __init__(self, budget: int, n_slots: int):
+        lib = load()
+        h = C.c_void_p()
+        check(lib.dinfer_sched_create(int(budget), int(n_slots), C.byref(h)), "dinfer_sched_create")
+        self._lib, self._h, self.n = lib, h, int(n_slots)
+
+    def round(self, decode_rows, refresh_rows):
+        n = self.n
+        assert len(decode_rows) == n and len(refresh_rows) == n
+        dec = (C.c_int32 * n)(*[int(x) for x in decode_rows])
+        ref = (C.c_int32 * n)(*[int(x) for x in refresh_rows])
+        adm = (C.c_uint8 * n)()
+        deficit = C.c_int64()
+        check(self._lib.dinfer_sched_round(self._h, dec, ref, adm, C.byref(deficit)),
+              "dinfer_sched_round")
+        return [int(adm[i]) for i in range(n)], int(deficit.value)
+
+    def close(self):
+        if self._h:
+            self._lib.dinfer_sched_destroy(self._h)
+            self._h = C.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

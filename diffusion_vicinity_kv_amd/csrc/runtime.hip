@@ -12,6 +12,8 @@
 #include <cmath>
 #include <cstdio>
 #include <cstring>
+#include <deque>
+#include <new>
 #include <string>
 #include <vector>
 
@@ -37,6 +39,7 @@ dinfer_status fail(dinfer_status s, const std::string& msg) {
   } while (0)
 
 constexpr size_t kAlign = 256;
+constexpr int64_t kSchedMaxBudget = int64_t(1) << 62;
 inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 // Row capacities and buffer sizes derived from the configuration.
@@ -700,6 +703,95 @@ dinfer_status dinfer_refill(dinfer_ctx* c, int32_t slot, int32_t prompt_len, int
 dinfer_status dinfer_finished(const dinfer_ctx* c, uint8_t* h_finished) {
   if (!c || !h_finished) return fail(DINFER_E_ARG, "null argument");
   for (int r = 0; r < c->batch; ++r) h_finished[r] = c->finished[r] ? 1 : 0;
+  return DINFER_OK;
+}
+
+dinfer_status dinfer_pending_rows(const dinfer_ctx* c, int32_t* h_decode_rows,
+                                  int32_t* h_refresh_rows) {
+  if (!c || !h_decode_rows || !h_refresh_rows) return fail(DINFER_E_ARG, "null argument");
+  if (c->state < 1) return fail(DINFER_E_STATE, "pending_rows before set_batch");
+  const Layout& L = c->L;
+  for (int r = 0; r < c->batch; ++r) {
+    h_decode_rows[r] = h_refresh_rows[r] = 0;
+    if (c->finished[r]) continue;
+    if (!c->refreshed[r]) {
+      h_refresh_rows[r] = c->Lr[r];
+      continue;
+    }
+    const int bs = c->P[r] + c->blk[r] * L.B;
+    h_decode_rows[r] = std::min(c->Lr[r], bs + L.B + L.w) - std::max(0, bs - L.w);
+  }
+  return DINFER_OK;
+}
+
+// Deficit token-budget admission (host only).  The queue holds the waiting
+// slots first come first served; `queued` mirrors membership.
+struct dinfer_sched {
+  int64_t budget = 0;
+  int n = 0;
+  int64_t deficit = 0;
+  std::deque<int> queue;
+  std::vector<uint8_t> queued;
+};
+
+dinfer_status dinfer_sched_create(int64_t token_budget, int32_t n_slots, dinfer_sched** out) {
+  if (!out) return fail(DINFER_E_ARG, "out is null");
+  *out = nullptr;
+  if (token_budget < 0 || token_budget > kSchedMaxBudget)
+    return fail(DINFER_E_ARG, "token_budget out of [0, 2^62]");
+  if (n_slots < 1) return fail(DINFER_E_ARG, "n_slots < 1");
+  dinfer_sched* s = new (std::nothrow) dinfer_sched;
+  if (!s) return fail(DINFER_E_ARG, "out of host memory");
+  s->budget = token_budget;
+  s->n = n_slots;
+  s->queued.assign(n_slots, 0);
+  *out = s;
+  return DINFER_OK;
+}
+
+void dinfer_sched_destroy(dinfer_sched* s) { delete s; }
+
+dinfer_status dinfer_sched_round(dinfer_sched* s, const int32_t* h_decode_rows,
+                                 const int32_t* h_refresh_rows, uint8_t* h_admit,
+                                 int64_t* h_deficit) {
+  if (!s || !h_decode_rows || !h_refresh_rows || !h_admit) return fail(DINFER_E_ARG, "null argument");
+  int64_t dec = 0;
+  for (int r = 0; r < s->n; ++r) {
+    if (h_decode_rows[r] < 0 || h_refresh_rows[r] < 0)
+      return fail(DINFER_E_ARG, "negative row count");
+    if (h_decode_rows[r] > 0 && h_refresh_rows[r] > 0)
+      return fail(DINFER_E_ARG, "a slot both decodes and waits for a refresh");
+    dec += h_decode_rows[r];
+  }
+  // slots that stopped waiting leave; this round's arrivals join in slot order
+  std::deque<int> q;
+  for (int r : s->queue) {
+    if (h_refresh_rows[r] > 0) q.push_back(r);
+    else s->queued[r] = 0;
+  }
+  for (int r = 0; r < s->n; ++r)
+    if (h_refresh_rows[r] > 0 && !s->queued[r]) {
+      q.push_back(r);
+      s->queued[r] = 1;
+    }
+  // the decodes spend the round's budget first; whole refreshes follow while
+  // the counter covers them (the head once in a round with no decode)
+  s->deficit += s->budget - dec;
+  std::memset(h_admit, 0, (size_t)s->n);
+  bool admitted = false;
+  while (!q.empty()) {
+    const int head = q.front();
+    const int64_t cost = h_refresh_rows[head];
+    if (s->deficit < cost && (dec > 0 || admitted)) break;
+    h_admit[head] = 1;
+    s->deficit -= cost;
+    s->queued[head] = 0;
+    q.pop_front();
+    admitted = true;
+  }
+  if (q.empty()) s->deficit = 0;   // the counter runs only while a refresh waits
+  s->queue.swap(q);
+  if (h_deficit) *h_deficit = s->deficit;
   return DINFER_OK;
 }
 

@@ -6,6 +6,7 @@ the method runs in the HIP library behind the C ABI.
 from __future__ import annotations
 
 import ctypes as C
+import time
 
 import torch
 
@@ -164,31 +165,62 @@ class Engine:
         B.check(self.lib.dinfer_finished(self.ctx, f), "dinfer_finished")
         return [bool(f[i]) for i in range(self.batch)]
 
-    def run_queue(self, queue, max_steps=1 << 30):
+    def pending_rows(self):
+        """dinfer_pending_rows: per slot, rows of its next step (decoding) and
+        of a whole refresh (waiting)."""
+        n = max(self.batch, 1)
+        dec, ref = (C.c_int32 * n)(), (C.c_int32 * n)()
+        B.check(self.lib.dinfer_pending_rows(self.ctx, dec, ref), "dinfer_pending_rows")
+        return [int(dec[i]) for i in range(self.batch)], [int(ref[i]) for i in range(self.batch)]
+
+    def run_queue(self, queue, max_steps=1 << 30, token_budget=None):
         """Continuous batching over the bound batch (set_batch holds the first
         requests): whenever a slot finishes, its response is taken and the next
         queued request is written into the slot's rows of the bound arrays and
         restarted (dinfer_refill).  queue: list of dicts with "tokens" (int32
         [max_len] row: prompt ids then mask_id), "prompt_len", "gen_len",
-        "plant_id" (int32 [max_len] row) and "plant_bias" (float).  Returns
-        {"outputs": [(slot request index, tokens row copy)], "steps",
-        "refreshes"}; request index i >= batch is queue[i - batch]."""
+        "plant_id" (int32 [max_len] row) and "plant_bias" (float).
+
+        Each round runs graph_unroll steps (one without graphs).  Without a
+        token_budget every slot that waits for a refresh (a new request or a
+        block start) is refreshed before the round; with one, the deficit
+        scheduler (dinfer_sched_round, token_budget rows per step) decides
+        which waiting slots are refreshed, and the others wait, not decoding,
+        for a later round.
+
+        Returns {"outputs": [(request index, tokens row copy)], "finish_step":
+        {request index: steps run when it finished}, "finish_time": {request
+        index: time.perf_counter() when it was taken}, "steps", "refreshes",
+        "rounds": [(decode rows, refresh rows, admitted, counter)] with a
+        budget}; request index i >= batch is queue[i - batch]."""
         tokens, plant_id, plant_bias, router_bias = self._batch_refs
         assert router_bias is None, "refill of MoE router bias rows is the caller's"
         U = int(self._dc.graph_unroll)
+        per_round = max(U, 1)
+        sched = None if token_budget is None else B.DeficitScheduler(int(token_budget) * per_round,
+                                                                     self.batch)
         owner = list(range(self.batch))          # request index held by each slot
         nxt = self.batch
-        outputs, steps, refreshes = [], 0, 0
-        self.refresh_kv()
-        refreshes += self.batch
+        outputs, finish_step, finish_time, log = [], {}, {}, []
+        steps, refreshes = 0, 0
+        need = [True] * self.batch               # set_batch: every slot waits
         while True:
+            if sched is None:
+                admit = need
+            else:
+                dec, ref = self.pending_rows()
+                dec = [x * per_round for x in dec]
+                admit, deficit = sched.round(dec, ref)
+                log.append((dec, ref, admit, deficit))
+            if any(admit):
+                self.refresh_kv(admit)
+                refreshes += sum(bool(a) for a in admit)
             if U > 0:
                 self.step_graph(U)
-                steps += U
             else:
                 self.denoise_step()
                 self.commit()
-                steps += 1
+            steps += per_round
             if steps > max_steps:
                 raise RuntimeError("run_queue: max_steps reached")
             self.advance_blocks()
@@ -196,6 +228,8 @@ class Engine:
                 if not done or owner[sl] is None:
                     continue
                 outputs.append((owner[sl], tokens[sl].clone()))
+                finish_step[owner[sl]] = steps
+                finish_time[owner[sl]] = time.perf_counter()   # advance_blocks waited
                 if nxt - self.batch < len(queue):
                     q = queue[nxt - self.batch]
                     tokens[sl].copy_(q["tokens"])
@@ -211,10 +245,11 @@ class Engine:
             need, unfinished = self.advance_blocks()
             if unfinished == 0:
                 break
-            if any(need):
-                self.refresh_kv(need)
-                refreshes += sum(need)
-        return {"outputs": outputs, "steps": steps, "refreshes": refreshes}
+        if sched is not None:
+            sched.close()
+        return {"outputs": outputs, "finish_step": finish_step, "finish_time": finish_time,
+                "steps": steps,
+                "refreshes": refreshes, "rounds": log}
 
     # -- state views -----------------------------------------------------------
     def view(self):

@@ -258,6 +258,47 @@ dinfer_status dinfer_refill(dinfer_ctx* ctx, int32_t slot, int32_t prompt_len, i
  * (host bookkeeping of dinfer_advance_blocks; no wait). */
 dinfer_status dinfer_finished(const dinfer_ctx* ctx, uint8_t* h_finished);
 
+/* Per-slot token cost of the next scheduling round (host bookkeeping, no
+ * wait): h_decode_rows[r] = rows of request r's next denoising step (its
+ * block with the +-w window, clipped to the request) if r is refreshed and
+ * unfinished, else 0; h_refresh_rows[r] = prompt + response length (the rows
+ * of a whole refresh) if r is unfinished and waits for a refresh, else 0.
+ * Both arrays hold `batch` entries.  DINFER_E_STATE before dinfer_set_batch. */
+dinfer_status dinfer_pending_rows(const dinfer_ctx* ctx, int32_t* h_decode_rows,
+                                  int32_t* h_refresh_rows);
+
+/* Deficit token-budget admission of whole KV refreshes ("Sangam: Efficiently
+ * Serving Diffusion LLMs with the AR Stack", abstract: in-flight decodes are
+ * admitted first, a whole refresh -- which bidirectional attention does not
+ * let one split -- only when the token budget accumulated so far covers it,
+ * unused budget carries over).  A host-only object; no GPU work, no context.
+ *
+ * One round per forward pass: the counter gains token_budget, loses the rows
+ * of every decode of the round, and then admits waiting slots first come
+ * first served (slots that start to wait in the same round queue in slot
+ * order) while it covers the head's rows; the head of the queue blocks the
+ * slots behind it.  In a round with no decode the head is admitted even if
+ * the counter does not cover it (the counter goes negative).  When no slot is
+ * left waiting at the end of a round the counter returns to 0, so budget is
+ * carried only while a refresh waits.
+ *
+ * dinfer_sched_create: token_budget in [0, 2^62] rows per round, n_slots >= 1;
+ * *out receives the object (NULL on error).  dinfer_sched_destroy frees it
+ * (NULL is a no-op).  dinfer_sched_round: h_decode_rows[r] > 0 for a slot
+ * decoding in this round, h_refresh_rows[r] > 0 for a slot waiting for a
+ * refresh (n_slots entries each, both >= 0, at most one of the two > 0 per
+ * slot, else DINFER_E_ARG and the state is unchanged); a queued slot whose
+ * refresh_rows becomes 0 leaves the queue.  h_admit[r] = 1 for the slots
+ * admitted in this round; *h_deficit (may be NULL) receives the counter after
+ * the round.  The caller refreshes the admitted slots before the round's
+ * step.  Not thread-safe per object. */
+typedef struct dinfer_sched dinfer_sched;
+dinfer_status dinfer_sched_create(int64_t token_budget, int32_t n_slots, dinfer_sched** out);
+void dinfer_sched_destroy(dinfer_sched* sched);
+dinfer_status dinfer_sched_round(dinfer_sched* sched, const int32_t* h_decode_rows,
+                                 const int32_t* h_refresh_rows, uint8_t* h_admit,
+                                 int64_t* h_deficit);
+
 /* Iteration manager: run every request of the batch to completion --
  * refresh at each block start, then denoise+commit steps replayed
  * graph_unroll at a time from a captured HIP graph (one host wait per

@@ -7,6 +7,7 @@ import oracle
 import synth
 from diffusion_vicinity_kv_amd.engine import Engine
 from diffusion_vicinity_kv_amd import binding as B
+from oracle.sched import DeficitScheduler as OracleSched
 from oracle.decode import credit_update, select_commits, smoothing_state, vocab_stats
 
 from gpu_util import build, compare_cache, lockstep, note, oracle_runs, small_workload
@@ -257,6 +258,47 @@ def test_continuous_batching_refill_matches_oracle(unroll):
         run = oracle.run_request(wc.model, wc.decode, w, req, r=i)
         assert np.array_equal(row.cpu().numpy()[: run.L], run.tokens), i
     note(f"  steps {res['steps']}, refreshes {res['refreshes']}")
+
+
+@pytest.mark.parametrize("unroll,budget", [(0, 200), (3, 64)])
+def test_deficit_budget_admission_matches_oracle(unroll, budget):
+    """Six requests through three slots with the deficit token budget deciding
+    which waiting refreshes (new requests and block starts) run in each round:
+    responses equal their own oracle runs, the library's admissions equal the
+    oracle scheduler's on the same rounds, and the budget defers some refresh
+    that the unbudgeted loop would have run at once."""
+    note(f"tiny fp32: 6 requests through 3 slots, unroll={unroll}, budget={budget} rows/step")
+    wc = small_workload(batch=6, prompt=(40, 90), gen=64, bias=6.0 + float(np.log(4094.0)) - 2.0,
+                        prob=(0.5, 0.9), seed=6)
+    w = synth.make_weights(wc.model, wc.seed, device="cuda")
+    req = synth.make_requests(wc)
+    max_len = req["tokens"].shape[1]
+    S = 3
+    eng = Engine(wc.model, wc.decode, w, S, max_len, graph_unroll=unroll)
+    tokens = req["tokens"][:S].cuda().contiguous()
+    plant_id = req["plant_id"][:S].cuda().contiguous()
+    plant_bias = req["plant_bias"][:S].cuda().contiguous()
+    P, G = req["prompt_len"].tolist(), req["gen_len"].tolist()
+    eng.set_batch(tokens, P[:S], G[:S], plant_id, plant_bias)
+    queue = [{"tokens": req["tokens"][i].cuda(), "prompt_len": P[i], "gen_len": G[i],
+              "plant_id": req["plant_id"][i].cuda(), "plant_bias": float(req["plant_bias"][i])}
+             for i in range(S, 6)]
+    res = eng.run_queue(queue, token_budget=budget)
+    torch.cuda.synchronize()
+    assert sorted(i for i, _ in res["outputs"]) == list(range(6))
+    for i, row in res["outputs"]:
+        run = oracle.run_request(wc.model, wc.decode, w, req, r=i)
+        assert np.array_equal(row.cpu().numpy()[: run.L], run.tokens), i
+    per_round = max(unroll, 1)
+    ora = OracleSched(budget * per_round, S)
+    deferred = 0
+    for dec, ref, admit, deficit in res["rounds"]:
+        assert ora.round(dec, ref) == admit
+        assert ora.deficit == deficit
+        deferred += sum(1 for r in range(S) if ref[r] > 0 and not admit[r])
+    note(f"  rounds {len(res['rounds'])}, steps {res['steps']}, refreshes {res['refreshes']}, "
+         f"deferred waits {deferred}")
+    assert deferred > 0
 
 
 @pytest.mark.parametrize("alpha", [0.0, 0.3])
