@@ -249,13 +249,18 @@ def run_queue_workload(wc, w, n_requests, unroll, budget=None):
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     lat = sorted(t - t0 for t in res["finish_time"].values())
+    rnd = sorted(res["round_s"])
     eng.close()
     committed = sum(G)        # every response position is committed (no end-of-sequence id)
     return {"requests": n_requests, "slots": S, "value": round(committed / elapsed, 3),
             "unit": "tokens/s", "wall_s": round(elapsed, 3), "steps": res["steps"],
             "refreshes": res["refreshes"], "token_budget_per_step": budget,
             "mean_latency_s": round(sum(lat) / len(lat), 3),
-            "p90_latency_s": round(lat[int(0.9 * (len(lat) - 1))], 3)}
+            "p90_latency_s": round(lat[int(0.9 * (len(lat) - 1))], 3),
+            # a round is graph_unroll steps plus the refreshes admitted before
+            # them: the longest rounds are the decode stalls refreshes cause
+            "rounds": len(rnd), "median_round_ms": round(1e3 * rnd[len(rnd) // 2], 2),
+            "max_round_ms": round(1e3 * rnd[-1], 2)}
 
 
 def main():
@@ -271,9 +276,9 @@ def main():
     ap.add_argument("--queue", type=int, default=0,
                     help="also run this many batch-16-mix requests through the 16 slots with "
                          "continuous batching (dense 8B workload only)")
-    ap.add_argument("--budget", type=int, default=0,
+    ap.add_argument("--budget", default="",
                     help="with --queue: also run the queue with the deficit token-budget "
-                         "scheduler at this many rows per step")
+                         "scheduler at these rows per step (comma-separated)")
     ap.add_argument("--kernel-only", action="store_true",
                     help="only the dominant-kernel timing loop (for counter runs)")
     ap.add_argument("--calib-copy", action="store_true",
@@ -337,11 +342,13 @@ def main():
         log(f"[bench] continuous batching: {args.queue} requests through {wc16.batch} slots")
         cb = run_queue_workload(wc16, w, args.queue, args.unroll)
         torch.cuda.empty_cache()
-        if args.budget > 0:
-            log(f"[bench] continuous batching, deficit budget {args.budget} rows/step")
-            cb = {"fifo": cb,
-                  "deficit": run_queue_workload(wc16, w, args.queue, args.unroll, args.budget)}
-            torch.cuda.empty_cache()
+        budgets = [int(b) for b in args.budget.split(",") if b.strip()]
+        if budgets:
+            cb = {"fifo": cb, "deficit": []}
+            for b in budgets:
+                log(f"[bench] continuous batching, deficit budget {b} rows/step")
+                cb["deficit"].append(run_queue_workload(wc16, w, args.queue, args.unroll, b))
+                torch.cuda.empty_cache()
 
     avg_ms, avg_bytes, avg_flops, rows = dominant_kernel_timing(wc, w)
     if rows <= 128:

@@ -190,7 +190,8 @@ class Engine:
 
         Returns {"outputs": [(request index, tokens row copy)], "finish_step":
         {request index: steps run when it finished}, "finish_time": {request
-        index: time.perf_counter() when it was taken}, "steps", "refreshes",
+        index: time.perf_counter() when it was taken}, "round_s": wall time of
+        each round (its refreshes and steps), "steps", "refreshes",
         "rounds": [(decode rows, refresh rows, admitted, counter)] with a
         budget}; request index i >= batch is queue[i - batch]."""
         tokens, plant_id, plant_bias, router_bias = self._batch_refs
@@ -204,6 +205,7 @@ class Engine:
         outputs, finish_step, finish_time, log = [], {}, {}, []
         steps, refreshes = 0, 0
         need = [True] * self.batch               # set_batch: every slot waits
+        round_end = [time.perf_counter()]
         while True:
             if sched is None:
                 admit = need
@@ -224,6 +226,7 @@ class Engine:
             if steps > max_steps:
                 raise RuntimeError("run_queue: max_steps reached")
             self.advance_blocks()
+            round_end.append(time.perf_counter())  # advance_blocks waited for the round
             for sl, done in enumerate(self.finished()):
                 if not done or owner[sl] is None:
                     continue
@@ -248,7 +251,7 @@ class Engine:
         if sched is not None:
             sched.close()
         return {"outputs": outputs, "finish_step": finish_step, "finish_time": finish_time,
-                "steps": steps,
+                "round_s": [b - a for a, b in zip(round_end, round_end[1:])], "steps": steps,
                 "refreshes": refreshes, "rounds": log}
 
     # -- state views -----------------------------------------------------------
