@@ -18,7 +18,8 @@ What it computes, and where each step is stated (page titles; sections):
       decoding, iteration smoothing).
   [S] "Sangam: Efficiently Serving Diffusion LLMs with the AR Stack" (abstract):
       a masked response is denoised; several positions commit per invocation;
-      cached KV is refreshed and reused across decodes; decodes are block-sized.
+      cached KV is refreshed and reused across decodes; decodes are block-sized;
+      a deficit token budget admits whole refreshes (sched.py).
   [T] "TIDE: Efficient and Lossless MoE Diffusion LLM Inference with I/O-aware
       Expert Offload" (abstract): block-level decoding; expert activations are
       stable within a block.
