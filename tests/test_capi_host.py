@@ -141,3 +141,18 @@ def test_calls_on_null_context_fail_cleanly():
     assert lib.dinfer_refresh_kv(None, None) == B.E_ARG
     assert lib.dinfer_run_to_completion(None, 1, None) == B.E_ARG
     lib.dinfer_destroy(None)
+
+
+def test_pending_rows_and_scheduler_argument_errors_without_gpu():
+    lib = B.load()
+    a = (C.c_int32 * 4)()
+    assert lib.dinfer_pending_rows(None, a, a) == B.E_ARG
+    h = C.c_void_p()
+    assert lib.dinfer_sched_create(10, 4, None) == B.E_ARG
+    assert lib.dinfer_sched_create(10, 4, C.byref(h)) == B.OK and h.value
+    adm = (C.c_uint8 * 4)()
+    assert lib.dinfer_sched_round(h, None, a, adm, None) == B.E_ARG
+    assert lib.dinfer_sched_round(h, a, a, None, None) == B.E_ARG
+    assert lib.dinfer_sched_round(h, a, a, adm, None) == B.OK   # nothing decodes or waits
+    lib.dinfer_sched_destroy(h)
+    lib.dinfer_sched_destroy(None)

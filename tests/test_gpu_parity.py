@@ -260,6 +260,29 @@ def test_continuous_batching_refill_matches_oracle(unroll):
     note(f"  steps {res['steps']}, refreshes {res['refreshes']}")
 
 
+def test_pending_rows_report_window_and_refresh_rows():
+    """dinfer_pending_rows: a waiting request costs its full length, a
+    refreshed one its block with the +-w window clipped to the request, a
+    finished one nothing."""
+    note("pending rows of three requests")
+    wc = small_workload(batch=3, prompt=(4, 90), gen=64, w=8, seed=9)
+    eng, w, req, tokens = build(wc)
+    P, G = req["prompt_len"].tolist(), req["gen_len"].tolist()
+    Bl, wv = wc.decode.block_len, wc.decode.vicinity_w
+    dec, ref = eng.pending_rows()
+    assert dec == [0, 0, 0] and ref == [P[r] + G[r] for r in range(3)]
+    eng.refresh_kv([True, False, True])
+    dec, ref = eng.pending_rows()
+    for r in range(3):
+        L, bs = P[r] + G[r], P[r]
+        want = min(L, bs + Bl + wv) - max(0, bs - wv)
+        assert dec[r] == (want if r != 1 else 0), (r, dec)
+        assert ref[r] == (0 if r != 1 else L), (r, ref)
+    eng.run_to_completion()
+    torch.cuda.synchronize()
+    assert eng.pending_rows() == ([0, 0, 0], [0, 0, 0])
+
+
 @pytest.mark.parametrize("unroll,budget", [(0, 200), (3, 64)])
 def test_deficit_budget_admission_matches_oracle(unroll, budget):
     """Six requests through three slots with the deficit token budget deciding
