@@ -198,8 +198,9 @@ class Engine:
         assert router_bias is None, "refill of MoE router bias rows is the caller's"
         U = int(self._dc.graph_unroll)
         per_round = max(U, 1)
-        sched = None if token_budget is None else B.DeficitScheduler(int(token_budget) * per_round,
-                                                                     self.batch)
+        sched = None
+        if token_budget is not None:   # per round; the library caps budgets at 2^62 rows
+            sched = B.DeficitScheduler(min(int(token_budget) * per_round, 1 << 62), self.batch)
         owner = list(range(self.batch))          # request index held by each slot
         nxt = self.batch
         outputs, finish_step, finish_time, log = [], {}, {}, []
