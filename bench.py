@@ -13,7 +13,9 @@ refresh, then denoise+commit steps replayed from a HIP graph until the block
 is committed).  value = committed tokens / wall time over the timed steps.
 
 Also reported:
-  step_latency_ms: one denoise+commit step, event-timed over graph replays.
+  step_latency_ms / step_latency_p90_ms: one denoise+commit step, median and
+    p90 over every graph replay of a run (replay time / graph_unroll,
+    event-timed; block refreshes excluded).
   roofline: the dominant kernel (the skinny bf16 GEMM that runs the QKV and
     gate|up projections of every layer), timed with HIP events on the stream it
     is launched on, over rotating layers so every launch streams its weights
@@ -202,24 +204,34 @@ def run_workload(wc, w, req, unroll, warmup, steps):
     committed = sum(r["committed"] for r in runs)
     value = committed / elapsed
 
-    # denoise-step latency: graph replays of the first block, event-timed
-    bind()
-    eng.refresh_kv()
-    n_lat = max(unroll, (wc.decode.block_len // unroll) * unroll)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # denoise-step latency over every step of one more run: each graph replay
+    # (unroll steps) event-timed on the library's stream (torch's current
+    # stream), block refreshes outside the timed replays
     st = torch.cuda.current_stream()
-    eng.step_graph(unroll)                     # graph captured, block warmed
     bind()
-    eng.refresh_kv()
-    torch.cuda.synchronize()
-    e0.record(st)
-    eng.step_graph(n_lat)
-    e1.record(st)
-    torch.cuda.synchronize()
-    step_ms = e0.elapsed_time(e1) / n_lat
+    need, lat = [True] * wc.batch, []
+    while True:
+        if any(need):
+            eng.refresh_kv(need)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        if unroll > 0:
+            eng.step_graph(unroll)
+        else:
+            eng.denoise_step()
+            eng.commit()
+        e1.record(st)
+        need, unfinished = eng.advance_blocks()    # waits for the stream
+        lat.append(e0.elapsed_time(e1) / max(unroll, 1))
+        if unfinished == 0:
+            break
+    lat.sort()
+    step_ms = lat[len(lat) // 2]
+    step_p90_ms = lat[int(0.9 * (len(lat) - 1))]
 
     eng.close()
-    return {"value": value, "elapsed": elapsed / steps, "step_ms": step_ms, "runs": runs,
+    return {"value": value, "elapsed": elapsed / steps, "step_ms": step_ms,
+            "step_p90_ms": step_p90_ms, "replays": len(lat), "runs": runs,
             "committed": committed}
 
 
@@ -333,6 +345,7 @@ def main():
         b16 = {"workload": "dense8b_b16", "value": round(r16["value"], 3), "unit": "tokens/s",
                "batch": wc16.batch, "ms_per_run": round(r16["elapsed"] * 1e3, 1),
                "step_latency_ms": round(r16["step_ms"], 3),
+               "step_latency_p90_ms": round(r16["step_p90_ms"], 3),
                "steps_per_run": r16["runs"][0]["steps"],
                "refresh_ms_per_run": round(r16["runs"][0]["refresh_ms"], 1)}
         torch.cuda.empty_cache()
@@ -411,6 +424,7 @@ def main():
                    "vicinity_w": wc.decode.vicinity_w, "layers": nl, "d_model": d,
                    "vocab": V, "graph_unroll": args.unroll},
         "step_latency_ms": round(step_ms, 4),
+        "step_latency_p90_ms": round(res["step_p90_ms"], 4), "latency_replays": res["replays"],
         "steps_per_run": steps_per_run,
         "refreshes_per_run": refreshes_per_run,
         "refresh_ms_per_run": round(sum(r["refresh_ms"] for r in runs) / len(runs), 3),
