@@ -324,6 +324,47 @@ def test_deficit_budget_admission_matches_oracle(unroll, budget):
     assert deferred > 0
 
 
+@pytest.mark.parametrize("unroll,budget", [(0, 200), (3, 64)])
+def test_eos_refill_and_budget_admission_match_oracle(unroll, budget):
+    """End-of-sequence stop, slot refill and budgeted admission together: six
+    requests through three slots with an EOS id that ends request 0 inside its
+    first block; a slot freed early takes the next request, whose first
+    refresh waits for the budget like every other.  Every response equals its
+    own oracle run with the same EOS id."""
+    note(f"tiny fp32: EOS + 6 requests through 3 slots, unroll={unroll}, budget={budget}")
+    wc = small_workload(batch=6, prompt=(40, 90), gen=64, bias=6.0 + float(np.log(4094.0)) - 2.0,
+                        prob=(0.5, 0.9), seed=3)
+    w = synth.make_weights(wc.model, wc.seed, device="cuda")
+    req = synth.make_requests(wc)
+    plain = oracle.run_request(wc.model, wc.decode, w, req, r=0)
+    eos = int(plain.tokens[plain.P + int(plain.records[0]["commits"][0])])
+    wce = wc.with_decode(eos_id=eos)
+    max_len = req["tokens"].shape[1]
+    S = 3
+    eng = Engine(wce.model, wce.decode, w, S, max_len, graph_unroll=unroll)
+    tokens = req["tokens"][:S].cuda().contiguous()
+    plant_id = req["plant_id"][:S].cuda().contiguous()
+    plant_bias = req["plant_bias"][:S].cuda().contiguous()
+    P, G = req["prompt_len"].tolist(), req["gen_len"].tolist()
+    eng.set_batch(tokens, P[:S], G[:S], plant_id, plant_bias)
+    queue = [{"tokens": req["tokens"][i].cuda(), "prompt_len": P[i], "gen_len": G[i],
+              "plant_id": req["plant_id"][i].cuda(), "plant_bias": float(req["plant_bias"][i])}
+             for i in range(S, 6)]
+    res = eng.run_queue(queue, token_budget=budget)
+    torch.cuda.synchronize()
+    assert sorted(i for i, _ in res["outputs"]) == list(range(6))
+    runs = {}
+    for i, row in res["outputs"]:
+        runs[i] = oracle.run_request(wce.model, wce.decode, w, req, r=i)
+        assert np.array_equal(row.cpu().numpy()[: runs[i].L], runs[i].tokens), i
+    assert len(runs[0].steps) < len(plain.steps)
+    assert res["refreshes"] == sum(len(r.steps) for r in runs.values())
+    ora = OracleSched(budget * max(unroll, 1), S)
+    for dec, ref, admit, deficit in res["rounds"]:
+        assert ora.round(dec, ref) == admit and ora.deficit == deficit
+    note(f"  rounds {len(res['rounds'])}, steps {res['steps']}, refreshes {res['refreshes']}")
+
+
 @pytest.mark.parametrize("alpha", [0.0, 0.3])
 def test_bf16_small_lockstep(alpha):
     note(f"bf16 small lockstep alpha={alpha}")
