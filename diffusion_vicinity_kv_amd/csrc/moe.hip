@@ -23,15 +23,16 @@ namespace {
 constexpr int kMaxE = 64;
 constexpr int kMaxTopK = 8;
 
-// One workgroup of eight waves per row.  Wave w takes experts
-// [w*epw, (w+1)*epw) (epw = ceil(E/8) <= 8): its lanes walk the row d in
+// One workgroup of sixteen waves per row (measured 0.7% faster on the MoE
+// window step than eight waves of eight experts).  Wave w takes experts
+// [w*epw, (w+1)*epw) (epw = ceil(E/16) <= 4): its lanes walk the row d in
 // 16-byte steps, every lane loading the same stretch of each of the wave's
 // router rows (one contiguous kilobyte per load instruction) and of the
 // activation row, and keeping one partial dot product per expert; the
 // partials are summed across the wave, the logits meet in LDS, and wave 0
 // picks the top_k by repeated wave argmax.  The row count and the row's
 // request are read together with the row.
-constexpr int kRouteWaves = 8;
+constexpr int kRouteWaves = 16;
 
 template <typename T>
 __global__ __launch_bounds__(64 * kRouteWaves) void moe_route_kernel(PassTable tb, int m_cap,
