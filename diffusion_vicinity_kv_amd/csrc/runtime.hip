@@ -39,6 +39,7 @@ dinfer_status fail(dinfer_status s, const std::string& msg) {
   } while (0)
 
 constexpr size_t kAlign = 256;
+
 constexpr int64_t kSchedMaxBudget = int64_t(1) << 62;
 inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -693,6 +694,7 @@ dinfer_status dinfer_refill(dinfer_ctx* c, int32_t slot, int32_t prompt_len, int
   c->finished[slot] = 0;
   c->refreshed[slot] = 0;
   c->step_dirty = true;
+  c->stats_ready = false;
   const Layout& L = c->L;
   HIP_TRY(hipMemsetAsync(c->at<int>(L.off_done) + slot, 0, 4, c->stream));
   HIP_TRY(hipMemsetAsync(c->at<int>(L.off_steps) + slot, 0, 4, c->stream));
@@ -867,6 +869,7 @@ dinfer_status dinfer_refresh_kv(dinfer_ctx* c, const uint8_t* h_req_mask) {
   for (int r = 0; r < c->batch; ++r)
     if (mask[r]) c->refreshed[r] = 1;
   c->step_dirty = true;
+  c->stats_ready = false;   // a refreshed block starts over: the last stats are stale
   return DINFER_OK;
 }
 
@@ -900,6 +903,7 @@ dinfer_status dinfer_advance_blocks(dinfer_ctx* c, uint8_t* h_needs_refresh, int
   HIP_TRY(hipMemcpyAsync(done.data(), c->at<int>(c->L.off_done), (size_t)c->batch * 4,
                          hipMemcpyDeviceToHost, c->stream));
   HIP_TRY(hipStreamSynchronize(c->stream));
+  c->stats_ready = false;   // blocks may move: a commit needs a fresh denoise_step
   for (int r = 0; r < c->batch; ++r) {
     if (h_needs_refresh) h_needs_refresh[r] = 0;
     if (c->finished[r] || !c->refreshed[r] || !done[r]) continue;

@@ -30,6 +30,11 @@
  *     except dinfer_advance_blocks and dinfer_run_to_completion, which wait.
  *   - Errors are returned as dinfer_status; no exception or abort crosses the
  *     ABI.  A kernel fault surfaces as DINFER_E_HIP at the next waiting call.
+ *   - Call order: step_init -> set_batch -> refresh_kv -> (denoise_step ->
+ *     commit)*.  A call out of that order returns DINFER_E_STATE and changes
+ *     nothing: denoise_step or step_graph before set_batch or with no
+ *     refreshed request; commit without a denoise_step since the last
+ *     commit, refresh_kv, advance_blocks, refill or set_batch.
  *   - A context is used from one host thread at a time.
  *
  * Layouts (row-major, no padding):

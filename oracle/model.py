@@ -23,6 +23,12 @@ def _f64(x):
     return np.asarray(x, dtype=np.float64)
 
 
+def _round_bf16(x):
+    """x rounded to the nearest bfloat16 (ties to even), returned as fp64."""
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(x)).to(torch.bfloat16).to(torch.float64).numpy()
+
+
 def rmsnorm(x, g, eps):
     """RMSNorm over the last axis."""
     return x / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps) * g
@@ -50,11 +56,12 @@ def attention(q, K, V, scale):
     Every query sees every cached key ([N] section on the bottlenecks: attention
     is bidirectional, so there is no causal mask).
     """
-    s = np.einsum("nhd,lhd->hnl", q, K) * scale
+    # per head: S = q_h K_h^T (a batched matrix product), row softmax, P V_h
+    s = np.matmul(q.transpose(1, 0, 2), K.transpose(1, 2, 0)) * scale      # [H, n, L]
     s = s - s.max(axis=-1, keepdims=True)
     p = np.exp(s)
     p = p / p.sum(axis=-1, keepdims=True)
-    return np.einsum("hnl,lhd->nhd", p, V)
+    return np.matmul(p, V.transpose(1, 0, 2)).transpose(1, 0, 2)          # [n, H, hd]
 
 
 def silu(x):
@@ -134,10 +141,14 @@ class OracleModel:
         return _f64(self.tok_emb[np.asarray(ids, dtype=np.int64)])
 
     # --- forward ----------------------------------------------------------
-    def new_cache(self, L):
+    def new_cache(self, L, kv_round=None):
+        """Zeroed K, V of L positions per layer.  kv_round="bf16" stores every
+        cached K and V rounded to bfloat16 (nearest even), the storage of a
+        bf16 model's cache; None keeps them in fp64."""
         m = self.m
         z = lambda: np.zeros((L, m.n_heads, m.head_dim))  # noqa: E731
-        return {"k": {li: z() for li in self.layer_ids}, "v": {li: z() for li in self.layer_ids}}
+        return {"k": {li: z() for li in self.layer_ids}, "v": {li: z() for li in self.layer_ids},
+                "round": kv_round}
 
     def forward_rows(self, cache, pos, e, L, router_bias=None, record=None, rope_offset=0):
         """Run every layer over the rows at positions `pos` with inputs e [n, d].
@@ -164,6 +175,8 @@ class OracleModel:
             v = qkv[:, 2 * d:].reshape(n, H, hd)
             q = rope(q, pos + rope_offset, m.rope_theta)
             k = rope(k, pos + rope_offset, m.rope_theta)
+            if cache.get("round") == "bf16":
+                k, v = _round_bf16(k), _round_bf16(v)
             cache["k"][li][pos] = k
             cache["v"][li][pos] = v
             o = attention(q, cache["k"][li][:L], cache["v"][li][:L], 1.0 / np.sqrt(hd))

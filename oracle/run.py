@@ -34,7 +34,7 @@ class OracleRun:
     """Decode state of one request driven step by step."""
 
     def __init__(self, model: OracleModel, dcfg, tokens, prompt_len, gen_len, plant_id,
-                 plant_bias, router_bias=None):
+                 plant_bias, router_bias=None, kv_round=None):
         self.model = model
         self.m = model.m
         self.d = dcfg
@@ -47,7 +47,7 @@ class OracleRun:
         self.router_bias = None if router_bias is None else np.asarray(router_bias, dtype=np.float64)
         self.B = dcfg.block_len
         self.n_blocks = self.G // self.B
-        self.cache = model.new_cache(self.L)
+        self.cache = model.new_cache(self.L, kv_round)
         self.block = -1
         self.steps = []            # steps per finished block
         self.records = []          # per-step details
@@ -152,7 +152,7 @@ class OracleRun:
         self.smooth_valid = still.copy()
         self.block_steps += 1
         rec = {"block": self.block, "commits": T.copy(), "fallback": fallback,
-               "margin": decision_margin(st, masked, self.credit, d, T, still)}
+               "margin": decision_margin(st, masked, self.credit, d, T, still, fallback)}
         self.records.append(rec)
         return T, fallback
 
@@ -183,32 +183,50 @@ def _min_route_margin(rec, layer_ids):
     return float(min(np.min(rec["route_margin"][li]) for li in layer_ids))
 
 
-def decision_margin(st, masked, credit, d, committed, still=None):
-    """Smallest distance, in logit (natural-log) units, of this step's decisions
-    from flipping.  Reported, not used by the method.  Over the candidates:
-    |ln p - ln tau|, |ln c - ln kappa| (credit on), ln p1 - ln p2 between the
-    best and second-best confidence (decides the fallback); over committed rows
-    the top-1 minus top-2 logit (decides the committed id); with smoothing on,
-    over rows still masked the smallest gap between consecutive logits among
-    the 9 largest (decides the kept top-8 and the order their ids are kept in)."""
+def decision_margin(st, masked, credit, d, committed, still=None, fallback=False):
+    """How far this step's float-to-integer decisions are from flipping, as a
+    band on the block rows' logits: if two computations of the same step differ
+    by at most e in every logit, each decision below is taken alike by both
+    whenever the returned margin exceeds 2e.  Reported, not used by the method.
+
+    Under a logit error of at most e a row's log max-probability moves by at most
+    2e (its top logit and its log-sum-exp each by e), a difference of two logits
+    of one row by at most 2e, and a difference of two rows' log-probabilities
+    by at most 4e.  The decisions of a step and their margins:
+      * the threshold gate of every candidate: |ln p - ln tau|;
+      * the credit gate of every candidate (credit on): |ln c - ln kappa| --
+        c = gamma*c_prev + lambda*p moves by at most the factor p does;
+      * the fallback, only when it was taken (no candidate passed a gate): the
+        best against the second-best candidate, (ln p1 - ln p2) / 2;
+      * the id of each committed row, and with credit on the id every masked
+        row passes to the credit state (stable or reset): the row's top-1 minus
+        top-2 logit;
+      * with smoothing on, the set of ids each still-masked row keeps (the soft
+        embedding sums over the set, so the order inside it decides nothing):
+        the row's 8th minus 9th largest logit."""
     from .decode import candidates
     C = candidates(masked, d.hierarchical)
     if len(C) == 0:
         return np.inf
-    tiny = 1e-30
-    conf = st["conf"][C].astype(np.float64)
+    tiny = 1e-300
+    conf = np.maximum(st["conf"][C].astype(np.float64), tiny)
     m = float(np.min(np.abs(np.log(conf) - np.log(d.tau))))
     if d.credit_weight != 0.0:
         c = np.maximum(credit[C].astype(np.float64), tiny)
         m = min(m, float(np.min(np.abs(np.log(c) - np.log(d.credit_kappa)))))
-    if len(C) > 1:
+    if fallback and len(C) > 1:
         s = np.sort(conf)[::-1]
-        m = min(m, float(np.log(s[0]) - np.log(max(s[1], tiny))))
-    tp = st["topk_p"][committed]
-    if tp.shape[1] > 1 and len(committed):
-        m = min(m, float(np.min(np.log(tp[:, 0]) - np.log(np.maximum(tp[:, 1], tiny)))))
-    if d.smooth_alpha != 0.0 and still is not None and still.any() and "rank_gap" in st:
-        m = min(m, float(np.min(st["rank_gap"][still])))
+        m = min(m, 0.5 * float(np.log(s[0]) - np.log(s[1])))
+    tp = np.maximum(np.asarray(st["topk_p"], dtype=np.float64), tiny)
+    top_gap = np.log(tp[:, 0]) - np.log(tp[:, 1])
+    rows = np.zeros(len(masked), dtype=bool)
+    rows[np.asarray(committed, dtype=np.int64)] = True
+    if d.credit_weight != 0.0:
+        rows |= np.asarray(masked, dtype=bool)
+    if rows.any():
+        m = min(m, float(np.min(top_gap[rows])))
+    if d.smooth_alpha != 0.0 and still is not None and np.any(still):
+        m = min(m, float(np.min(st["kth_gap"][np.asarray(still, dtype=bool)])))
     return float(m)
 
 

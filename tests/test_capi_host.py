@@ -156,3 +156,29 @@ def test_pending_rows_and_scheduler_argument_errors_without_gpu():
     assert lib.dinfer_sched_round(h, a, a, adm, None) == B.OK   # nothing decodes or waits
     lib.dinfer_sched_destroy(h)
     lib.dinfer_sched_destroy(None)
+
+
+def test_step_init_workspace_errors_without_gpu():
+    """An absent, misaligned or undersized workspace is rejected before any
+    device call (the weight pointers are placeholders, never dereferenced)."""
+    lib = B.load()
+    mc, dc, wc = _structs()
+    nl = mc.n_layers
+    arr = (C.c_void_p * nl)(*([4096] * nl))
+    w = B.Weights()
+    w.tok_emb = w.final_norm = w.lm_head = 4096
+    for k in ("attn_norm", "wqkv", "wo", "ffn_norm", "w_gate_up", "w_down"):
+        setattr(w, k, C.cast(arr, B._PP))
+    need = lib.dinfer_workspace_bytes(C.byref(mc), C.byref(dc), 1, wc.max_len)
+    assert need > 0
+    ctx = C.c_void_p(1234)
+    base = 1 << 40
+    for ws, nbytes, why in [(None, need, b"null"), (base + 8, need, b"aligned"),
+                            (base + 128, need, b"aligned"), (base, need - 256, b"too small"),
+                            (base, 0, b"too small")]:
+        st = lib.dinfer_step_init(C.byref(mc), C.byref(dc), C.byref(w), 1, wc.max_len, ws,
+                                  nbytes, None, C.byref(ctx))
+        assert st == B.E_WORKSPACE, (ws, nbytes, st)
+        assert why in lib.dinfer_last_error(), lib.dinfer_last_error()
+        assert ctx.value is None            # *out cleared on every failure
+        ctx = C.c_void_p(1234)

@@ -1,8 +1,11 @@
 """Properties of the full dense 8B-shaped model (32 layers, bf16, batch 1) in
-the launch configuration the benchmark times.  The oracle cannot run this
-size, so the checks are properties that hold at any size: the vicinity
+the launch configuration the benchmark times, checked at every step of a
+block or a run without an oracle forward pass (test_gpu_fullshape.py runs the
+oracle's forward at this size for a refresh and two steps): the vicinity
 scatter writes only the window, the vocab statistics agree with the step's own
-logits, the commit rules hold, and graph replays are bit-deterministic."""
+logits, the oracle selector fed the step's own statistics takes the GPU's
+decisions bit for bit, the commit rules hold, and graph replays are
+bit-deterministic."""
 import numpy as np
 import pytest
 import torch
@@ -109,3 +112,34 @@ def test_full_run_commits_every_position(dense8b):
     assert not np.any(t[P:P + wc.gen_len] == wc.model.mask_id)
     assert np.array_equal(t[:P], req["tokens"][0, :P].numpy())
     note(f"  {stats}")
+
+
+def test_selector_bit_exact_on_the_steps_own_statistics(dense8b):
+    """A whole block of the 32-layer model, eager steps: after each step the
+    oracle selector, fed the step's own statistics and the credit state before
+    it, must give the GPU's commit mask, tokens, credit bits, tracked ids and
+    smoothing state; fed the oracle's vocab statistics of the step's logits it
+    must take the same commits except at confidences or credits within 1e-3 of
+    tau or kappa (excluded and counted)."""
+    from gpu_util import _gpu_block_state, selector_check
+    wc, eng, w, req, tokens = dense8b
+    note("full-size: selector on the step's own statistics, one block")
+    tokens.copy_(req["tokens"].cuda())
+    eng.set_batch(tokens, req["prompt_len"].tolist(), req["gen_len"].tolist(),
+                  req["plant_id"].cuda(), req["plant_bias"].cuda())
+    eng.refresh_kv()
+    B = wc.decode.block_len
+    excluded = 0
+    for s in range(B):
+        v = eng.view()
+        tok0 = tokens.cpu().numpy()
+        st0 = _gpu_block_state(v, 1, B)
+        eng.denoise_step()
+        eng.commit()
+        torch.cuda.synchronize()
+        excluded += selector_check(wc, req, tok0, st0, v, tokens.cpu().numpy(), [0], [0])
+        if not (tokens[0, int(req["prompt_len"][0]):int(req["prompt_len"][0]) + B]
+                == wc.model.mask_id).any():
+            break
+    note(f"  {s + 1} steps, {excluded} excluded near tau/kappa")
+    assert s + 1 == B       # one commit per step under the literal planting

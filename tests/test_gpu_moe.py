@@ -98,13 +98,13 @@ def test_tiny_moe_batched_ragged_lockstep():
     runs = oracle_runs(wc, w, req)
     rep = lockstep(wc, eng, tokens, runs, logit_tol=1e-5, route_band=1e-4)
     note(f"  {rep}")
-    # The three requests reach a near-exact tie (two of a row's top-8 logits
-    # within one fp32 ulp, which fixes the order the smoothing state keeps
-    # their ids in) after 40 identical steps: the lockstep stops there, as
-    # designed, because a decision inside the numerical band may differ.  The
-    # run must get that far with every decision identical.
+    # The kept smoothing ids are compared as a set (the soft embedding sums
+    # over it), so a tie inside a row's top eight decides nothing.  The run
+    # ends with every decision identical unless a decision inside the
+    # numerical band (logged) parts the two.
     d = rep["diverged"]
-    assert d is None or (d.get("margin", 0.0) < d.get("band", 1.0) and rep["steps"] >= 32), rep
+    assert d is None or d.get("margin", 0.0) < d.get("band", 1.0), rep
+    assert d is not None or all(getattr(r, "_finished", False) for r in runs)
 
 
 def test_tiny_moe_routing_of_refresh_and_step():

@@ -130,7 +130,8 @@ def test_tiny_refresh_cache_and_first_step_logits():
     ol = runs[0].denoise_logits()
     gl = eng.view()["logits"].cpu().numpy()
     err = np.max(np.abs(gl - ol)) / np.sqrt(np.mean(ol ** 2))
-    assert err < 3e-5, err
+    note(f"  first step: max |dlogit| / RMS = {err:.3e}")
+    assert err < 1e-5, err
     compare_cache(wc, eng, runs)
 
 
@@ -172,10 +173,13 @@ def test_attention_edge_lockstep(shape):
     eng, w, req, tokens = build(wc)
     runs = oracle_runs(wc, w, req)
     rep = lockstep(wc, eng, tokens, runs, logit_tol=1e-5, check_cache=True,
-                   max_steps=12 if shape == "many_key_splits" else 10_000)
+                   max_steps=16 if shape == "many_key_splits" else 10_000)
     note(f"  {rep}")
     assert rep["diverged"] is None
-    assert rep["steps"] >= 1
+    if shape == "many_key_splits":
+        assert rep["steps"] >= 16                     # the whole first block
+    else:
+        assert all(getattr(r, "_finished", False) for r in runs)
 
 
 @pytest.mark.parametrize("unroll", [0, 1, 4])
@@ -375,9 +379,9 @@ def test_bf16_small_lockstep(alpha):
     runs = oracle_runs(wc, w, req)
     rep = lockstep(wc, eng, tokens, runs, logit_tol=2e-2, check_cache=True)
     note(f"  {rep}")
-    # a run may part from the oracle at a genuine near-tie (reported); before
-    # that every step matched
-    assert rep["steps"] >= (8 if alpha == 0.0 else 1)
+    # every step until the run ends matched, unless a genuine near-tie (a
+    # decision inside the numerical band, logged) parts the two earlier
+    assert rep["diverged"] is not None or all(getattr(r, "_finished", False) for r in runs)
 
 
 def test_bf16_batch16_fat_step_path_lockstep():
@@ -387,9 +391,11 @@ def test_bf16_batch16_fat_step_path_lockstep():
                         alpha=0.0)
     eng, w, req, tokens = build(wc)
     runs = oracle_runs(wc, w, req)
-    rep = lockstep(wc, eng, tokens, runs, logit_tol=2e-2, max_steps=12)
+    rep = lockstep(wc, eng, tokens, runs, logit_tol=2e-2, max_steps=40)
     note(f"  {rep}")
-    assert rep["steps"] >= 1
+    # at least the first block (32 steps of one fallback commit each), unless a
+    # logged near-tie parts the two earlier
+    assert rep["diverged"] is not None or rep["steps"] >= 32
 
 
 @pytest.mark.parametrize("preset", ["dense8b_b1"])
@@ -398,13 +404,13 @@ def test_full_width_two_layer_parity(preset):
     two layers: every per-layer kernel runs in the launch configuration of the
     32-layer benchmark.  Refresh cache and two steps against the oracle."""
     note(f"full-width 2-layer {preset}")
-    wc = synth.preset(preset).with_model(n_layers=2).with_decode(smooth_alpha=0.0)
+    wc = synth.preset(preset).with_model(n_layers=2)
     eng, w, req, tokens = build(wc)
     runs = oracle_runs(wc, w, req)
-    rep = lockstep(wc, eng, tokens, runs, logit_tol=2e-2, max_steps=2, check_cache=False)
+    rep = lockstep(wc, eng, tokens, runs, logit_tol=2e-2, max_steps=8, check_cache=False)
     note(f"  {rep}")
     compare_cache(wc, eng, runs)
-    assert rep["steps"] >= 1
+    assert rep["diverged"] is not None or rep["steps"] == 8
 
 
 # --------------------------------------------------------------- linear (K1)

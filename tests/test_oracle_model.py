@@ -246,3 +246,38 @@ def test_vicinity_step_after_refresh_equals_refresh_outputs():
     want = om.logits(h[run.bs:run.be])
     got = run.denoise_logits()
     assert np.allclose(got, want, atol=1e-10)
+
+
+def test_bf16_cache_storage_rounds_to_nearest_even():
+    """kv_round="bf16": the cache keeps K and V rounded to bfloat16 (8
+    significant bits).  Worked cases: 1 + 2^-8 lies halfway between 1 and its
+    neighbour 1 + 2^-7 and goes to the even one, 1; 1 + 3 * 2^-8 lies halfway
+    between 1 + 2^-7 (odd) and 1 + 2^-6 (even) and goes up; anything past a
+    halfway point goes to the nearer neighbour; representable values stay."""
+    from oracle.model import _round_bf16
+    x = np.array([1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, 1.0 + 2.0 ** -8 + 2.0 ** -20,
+                  -(1.0 + 2.0 ** -8 - 2.0 ** -20), 0.75, -96.0, 3.0 * 2.0 ** -130])
+    want = np.array([1.0, 1.0 + 2.0 ** -6, 1.0 + 2.0 ** -7, -1.0, 0.75, -96.0, 3.0 * 2.0 ** -130])
+    assert np.array_equal(_round_bf16(x), want)
+
+
+def test_bf16_cache_option_changes_only_the_stored_precision():
+    wc = synth.preset("tiny_f32").with_model(n_layers=2, d_model=64, n_heads=2, head_dim=32,
+                                             ffn_dim=96, vocab=256, mask_id=255)
+    w = synth.make_weights(wc.model, 3)
+    om = OracleModel(wc.model, w)
+    pos = np.arange(40)
+    e = om.embed(RNG.integers(0, 255, 40))
+    c64, cbf = om.new_cache(40), om.new_cache(40, kv_round="bf16")
+    om.forward_rows(c64, pos, e, 40)
+    om.forward_rows(cbf, pos, e, 40)
+    from oracle.model import _round_bf16
+    # layer 0 sees the same inputs: its K, V are the fp64 ones rounded
+    for key in ("k", "v"):
+        assert np.array_equal(cbf[key][0], _round_bf16(c64[key][0]))
+        # every stored value is a bfloat16: at most half an ulp (2^-8 relative) away
+        rel = np.abs(cbf[key][0] - c64[key][0]) / np.maximum(np.abs(c64[key][0]), 1e-30)
+        assert rel.max() <= 2.0 ** -8
+    # deeper layers see the rounded cache through attention: close, not equal
+    d = np.abs(cbf["k"][1] - c64["k"][1]).max() / np.sqrt(np.mean(c64["k"][1] ** 2))
+    assert 0 < d < 5e-2
