@@ -21,6 +21,7 @@ EXPORTS = [
     "dinfer_step_graph", "dinfer_pack_linear", "dinfer_linear_out_elems", "dinfer_linear",
     "dinfer_status_str", "dinfer_last_error", "dinfer_destroy", "dinfer_refill", "dinfer_finished",
     "dinfer_pending_rows", "dinfer_sched_create", "dinfer_sched_destroy", "dinfer_sched_round",
+    "dinfer_vocab_stats_noalloc",
 ]
 
 
@@ -97,6 +98,7 @@ def load(path: str = LIB_PATH) -> C.CDLL:
         "dinfer_get_step_view": (i32, [vp, C.POINTER(StepView)]),
         "dinfer_vocab_stats_scratch_bytes": (sz, [i32, i32]),
         "dinfer_vocab_stats": (i32, [vp, i32, i32, vp, vp, i32, vp, vp, vp, vp, vp, vp, sz, vp]),
+        "dinfer_vocab_stats_noalloc": (i32, [vp, i32, i32, vp, vp, i32, vp, vp, vp, vp, vp, vp]),
         "dinfer_step_graph": (i32, [vp, i32]),
         "dinfer_pack_linear": (i32, [vp, vp, i32, i32, i32, i32, vp]),
         "dinfer_linear_out_elems": (sz, [i32, i32, i32, i32]),
@@ -186,6 +188,17 @@ def vocab_stats(logits, plant_id, plant_bias, mask_id, out, scratch, stream=None
                                 ptr(out["topk_id"]), ptr(out["topk_p"]), ptr(scratch),
                                 scratch.numel() * scratch.element_size(), stream_handle(stream))
     check(st, "dinfer_vocab_stats")
+
+
+def vocab_stats_noalloc(logits, plant_id, plant_bias, mask_id, out, stream=None):
+    """dinfer_vocab_stats_noalloc (no scratch argument, no allocation)."""
+    lib = load()
+    rows, vocab = logits.shape
+    st = lib.dinfer_vocab_stats_noalloc(ptr(logits), rows, vocab, ptr(plant_id), ptr(plant_bias),
+                                        mask_id, ptr(out["argmax"]), ptr(out["conf"]),
+                                        ptr(out["lse"]), ptr(out["topk_id"]), ptr(out["topk_p"]),
+                                        stream_handle(stream))
+    check(st, "dinfer_vocab_stats_noalloc")
 
 
 class DeficitScheduler:

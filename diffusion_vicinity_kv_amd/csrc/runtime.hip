@@ -13,6 +13,7 @@
 #include <cstdio>
 #include <cstring>
 #include <deque>
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
@@ -40,6 +41,17 @@ dinfer_status fail(dinfer_status s, const std::string& msg) {
 
 constexpr size_t kAlign = 256;
 
+// Scratch of dinfer_vocab_stats_noalloc: the split partials of the vocab
+// statistics live in this fixed device array instead of a caller buffer.
+// Each GPU the library runs on holds its own copy until the process ends.
+constexpr size_t kNoAllocScratchBytes = size_t(2) << 20;
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+// Device address of `scratch` per device, looked up once (with that device
+// current) by hipGetSymbolAddress; host code passes only these addresses to
+// kernels, never the array's name.
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
 constexpr int64_t kSchedMaxBudget = int64_t(1) << 62;
 inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -1132,6 +1144,44 @@ dinfer_status dinfer_vocab_stats(const float* d_logits, int32_t rows, int32_t vo
   if (!d_scratch || scratch_bytes < vocab_scratch_bytes(p, rows))
     return fail(DINFER_E_WORKSPACE, "scratch too small");
   HIP_TRY(launch_vocab_stats(p, d_logits, rows, vocab, d_plant_id, d_plant_bias, mask_id, d_scratch,
+                             d_argmax, d_conf, d_lse, d_topk_id, d_topk_p,
+                             static_cast<hipStream_t>(stream)));
+  return DINFER_OK;
+}
+
+dinfer_status dinfer_vocab_stats_noalloc(const float* d_logits, int32_t rows, int32_t vocab,
+                                         const int32_t* d_plant_id, const float* d_plant_bias,
+                                         int32_t mask_id, int32_t* d_argmax, float* d_conf,
+                                         float* d_lse, int32_t* d_topk_id, float* d_topk_p,
+                                         void* stream) {
+  if (!d_logits || !d_argmax || !d_conf || !d_lse || !d_topk_id || !d_topk_p)
+    return fail(DINFER_E_ARG, "null output or input pointer");
+  if (rows < 1 || vocab < 2) return fail(DINFER_E_ARG, "rows and vocab must be positive");
+  if (vocab % 4 != 0) return fail(DINFER_E_UNSUPPORTED, "vocab must be a multiple of 4");
+  if (mask_id < -1 || mask_id >= vocab) return fail(DINFER_E_ARG, "mask_id out of range");
+  const VocabPlan p = plan_vocab(rows, vocab, 1024);
+  const size_t need = vocab_scratch_bytes(p, rows);
+  if (need > kNoAllocScratchBytes)
+    return fail(DINFER_E_UNSUPPORTED,
+                "rows x vocab splits need " + std::to_string(need) +
+                    " bytes of scratch, above the fixed " +
+                    std::to_string(kNoAllocScratchBytes) + " of the no-allocation entry point");
+  int dev = 0;
+  HIP_TRY(hipGetDevice(&dev));
+  if (dev < 0 || dev >= kMaxDevices) return fail(DINFER_E_UNSUPPORTED, "device index above 63");
+  void* ptr = nullptr;
+  {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+      // first call on this device (it is current): its copy of the array
+      void* a = nullptr;
+      HIP_TRY(hipGetSymbolAddress(&a, HIP_SYMBOL(scratch)));
+      if (!a) return fail(DINFER_E_HIP, "hipGetSymbolAddress returned no address");
+      g_scratch_ptr[dev] = a;
+    }
+    ptr = g_scratch_ptr[dev];
+  }
+  HIP_TRY(launch_vocab_stats(p, d_logits, rows, vocab, d_plant_id, d_plant_bias, mask_id, ptr,
                              d_argmax, d_conf, d_lse, d_topk_id, d_topk_p,
                              static_cast<hipStream_t>(stream)));
   return DINFER_OK;

@@ -370,6 +370,23 @@ dinfer_status dinfer_vocab_stats(const float* d_logits, int32_t rows, int32_t vo
                                  float* d_lse, int32_t* d_topk_id, float* d_topk_p,
                                  void* d_scratch, size_t scratch_bytes, void* stream);
 
+/* dinfer_vocab_stats without a scratch argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the same kernels, with the split partials
+ * in a fixed 2 MiB array of device memory that the library holds on each GPU
+ * it runs on until the process ends.  Makes no allocation.  Returns
+ * DINFER_E_UNSUPPORTED when rows x vocab splits need more than that
+ * (dinfer_vocab_stats_scratch_bytes(rows, vocab) > 2 MiB: about 29000 rows
+ * at vocab 126464).  Calls on one GPU share its array: calls that may overlap
+ * on one GPU (different streams, no ordering between them) race and must not
+ * be issued; calls ordered on one stream are safe.  Other arguments and
+ * errors as dinfer_vocab_stats. */
+dinfer_status dinfer_vocab_stats_noalloc(const float* d_logits, int32_t rows, int32_t vocab,
+                                         const int32_t* d_plant_id, const float* d_plant_bias,
+                                         int32_t mask_id, int32_t* d_argmax, float* d_conf,
+                                         float* d_lse, int32_t* d_topk_id, float* d_topk_p,
+                                         void* stream);
+
 /* Human-readable name of a status; the last error message of the calling
  * thread is appended by dinfer_last_error. */
 const char* dinfer_status_str(dinfer_status s);
