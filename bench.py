@@ -24,6 +24,15 @@ Also reported:
     run the fat GEMM instead, priced in TFLOP/s against bf16 MFMA peak.
   batch16: the same weights on the batch-16 request mix (prompts U{128..1024},
     ragged), one warm-up and one timed generation (dense 8B workload only).
+  decode_accounting: commits through the threshold gate, the credit gate and
+    the fallback, idle graph steps past a block's end, commits-per-step
+    histogram.  Under the workloads' literal planting every step commits one
+    token through the fallback.
+  supplementary_calibrated_planting: the batch-1 and batch-16 workloads (and
+    with --supplementary-long the long-context one) with the planting bias
+    raised by ln(V-1), so that planted positions pass the threshold gate:
+    tokens/s, step latency and the same accounting.  A separate reading of
+    the planting, labelled as such; `value` is always the literal workload.
   cpu_baseline: the CPU oracle on a bounded sample (one layer's refresh and
     one layer's window step plus the LM head / vocab stats / commit of one
     step), scaled to the run's layer, refresh and step counts.
@@ -190,6 +199,14 @@ def run_workload(wc, w, req, unroll, warmup, steps):
         bind()
         return eng.run_to_completion()
 
+    def accounting():
+        """The last run's decode accounting summed over the batch."""
+        ds = eng.view()["decode_stats"].cpu().sum(dim=0).tolist()
+        hist = {k: int(n) for k, n in enumerate(ds[4:69]) if n}
+        return {"threshold_commits": int(ds[0]), "credit_commits": int(ds[1]),
+                "fallback_commits": int(ds[2]), "idle_steps": int(ds[3]),
+                "commits_per_step_hist": hist}
+
     for i in range(warmup):
         s = one_run()
         log(f"[bench] warmup {i}: {s}")
@@ -203,6 +220,7 @@ def run_workload(wc, w, req, unroll, warmup, steps):
     elapsed = time.perf_counter() - t0
     committed = sum(r["committed"] for r in runs)
     value = committed / elapsed
+    acct = accounting()
 
     # denoise-step latency over every step of one more run: each graph replay
     # (unroll steps) event-timed on the library's stream (torch's current
@@ -232,7 +250,30 @@ def run_workload(wc, w, req, unroll, warmup, steps):
     eng.close()
     return {"value": value, "elapsed": elapsed / steps, "step_ms": step_ms,
             "step_p90_ms": step_p90_ms, "replays": len(lat), "runs": runs,
-            "committed": committed}
+            "committed": committed, "accounting": acct}
+
+
+def calibrated(wc):
+    """The supplementary planting reading: bias b' = b + ln(V - 1), so that a
+    planted position's confidence is about e^b / (e^b + 1) (0.9997 at b = 8)
+    whatever the vocabulary size, and the threshold gate fires."""
+    import math
+    return wc.with_(plant_bias=wc.plant_bias + math.log(wc.model.vocab - 1))
+
+
+def supplementary_leg(name, w, unroll):
+    """One warm-up and one timed generation of a workload under calibrated
+    planting, with its decode accounting."""
+    import synth
+    wc = calibrated(synth.preset(name))
+    r = run_workload(wc, w, synth.make_requests(wc), unroll, 1, 1)
+    return {"workload": name, "planting": f"calibrated: bias {wc.plant_bias:.3f} = "
+            f"{synth.preset(name).plant_bias:g} + ln(V-1)", "batch": wc.batch,
+            "hierarchical": bool(wc.decode.hierarchical), "value": round(r["value"], 3),
+            "unit": "tokens/s", "ms_per_run": round(r["elapsed"] * 1e3, 1),
+            "step_latency_ms": round(r["step_ms"], 3), "steps_per_run": r["runs"][0]["steps"],
+            "refreshes_per_run": r["runs"][0]["refreshes"],
+            "refresh_ms_per_run": round(r["runs"][0]["refresh_ms"], 1), **r["accounting"]}
 
 
 def run_queue_workload(wc, w, n_requests, unroll, budget=None):
@@ -291,6 +332,12 @@ def main():
     ap.add_argument("--budget", default="",
                     help="with --queue: also run the queue with the deficit token-budget "
                          "scheduler at these rows per step (comma-separated)")
+    ap.add_argument("--no-supplementary", action="store_true",
+                    help="skip the supplementary calibrated-planting runs of the dense 8B "
+                         "workloads (batch 1 and the batch-16 mix)")
+    ap.add_argument("--supplementary-long", action="store_true",
+                    help="also run the long-context workload (batch 4, 8K prompt, hierarchical) "
+                         "under calibrated planting (about a minute)")
     ap.add_argument("--kernel-only", action="store_true",
                     help="only the dominant-kernel timing loop (for counter runs)")
     ap.add_argument("--calib-copy", action="store_true",
@@ -347,8 +394,18 @@ def main():
                "step_latency_ms": round(r16["step_ms"], 3),
                "step_latency_p90_ms": round(r16["step_p90_ms"], 3),
                "steps_per_run": r16["runs"][0]["steps"],
-               "refresh_ms_per_run": round(r16["runs"][0]["refresh_ms"], 1)}
+               "refresh_ms_per_run": round(r16["runs"][0]["refresh_ms"], 1),
+               **r16["accounting"]}
         torch.cuda.empty_cache()
+    supp = None
+    if args.workload == "dense8b_b1" and not args.no_supplementary:
+        supp = []
+        names = ["dense8b_b1", "dense8b_b16"] + (["dense8b_long_b4"] if args.supplementary_long else [])
+        for name in names:
+            log(f"[bench] supplementary: {name} under calibrated planting")
+            supp.append(supplementary_leg(name, w, args.unroll))
+            log(f"[bench]   {supp[-1]}")
+            torch.cuda.empty_cache()
     cb = None
     if args.workload == "dense8b_b1" and args.queue > 0:
         wc16 = synth.preset("dense8b_b16")
@@ -432,8 +489,10 @@ def main():
                           "achieved": round(step_bytes / (step_ms * 1e-3) / 1e9, 1),
                           "peak": HBM_PEAK_GBS, "unit": "GB/s",
                           "frac": round(step_bytes / (step_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+        "decode_accounting": res["accounting"],
         "roofline": roofline,
         "batch16": b16,
+        "supplementary_calibrated_planting": supp,
         "continuous_batching": cb,
         "cpu_baseline": cpu,
     }

@@ -21,7 +21,7 @@ EXPORTS = [
     "dinfer_step_graph", "dinfer_pack_linear", "dinfer_linear_out_elems", "dinfer_linear",
     "dinfer_status_str", "dinfer_last_error", "dinfer_destroy", "dinfer_refill", "dinfer_finished",
     "dinfer_pending_rows", "dinfer_sched_create", "dinfer_sched_destroy", "dinfer_sched_round",
-    "dinfer_vocab_stats_noalloc",
+    "dinfer_vocab_stats_noalloc", "dinfer_keep_logits",
 ]
 
 
@@ -63,7 +63,7 @@ class StepView(C.Structure):
                                   "kv_k", "kv_v")] + [
         ("moe_top_k", C.c_int32), ("moe_sel", C.c_void_p), ("moe_gate", C.c_void_p),
         ("moe_experts", C.c_int32), ("moe_logits", C.c_void_p), ("ffn_in", C.c_void_p),
-        ("kv_len", C.c_int32)]
+        ("kv_len", C.c_int32), ("decode_stats", C.c_void_p), ("decode_stat_words", C.c_int32)]
 
 
 class DinferError(RuntimeError):
@@ -96,6 +96,7 @@ def load(path: str = LIB_PATH) -> C.CDLL:
         "dinfer_advance_blocks": (i32, [vp, C.POINTER(C.c_uint8), C.POINTER(i32)]),
         "dinfer_run_to_completion": (i32, [vp, i32, C.POINTER(RunStats)]),
         "dinfer_get_step_view": (i32, [vp, C.POINTER(StepView)]),
+        "dinfer_keep_logits": (i32, [vp, i32]),
         "dinfer_vocab_stats_scratch_bytes": (sz, [i32, i32]),
         "dinfer_vocab_stats": (i32, [vp, i32, i32, vp, vp, i32, vp, vp, vp, vp, vp, vp, sz, vp]),
         "dinfer_vocab_stats_noalloc": (i32, [vp, i32, i32, vp, vp, i32, vp, vp, vp, vp, vp, vp]),

@@ -17,6 +17,10 @@
 //             "系统级压榨": computation after EOS is skipped)
 //   block_done: 1 when no MASK remains in the block, 2 when none remains in
 //             the whole response either (the request is complete)
+//   accounting: per request, commits through the threshold gate, through the
+//             credit gate alone, through the fallback, steps that found the
+//             block already done (a graph replays steps past a block's end),
+//             and a histogram of commits per step (statistics only)
 #include "common.h"
 #include "kernels.h"
 
@@ -30,8 +34,10 @@ __global__ __launch_bounds__(64) void commit_kernel(CommitArgs a) {
   const int B = a.B;
   const int row = r * B + j;
   const bool inb = j < B;
+  int* acct = a.decode_stats + (size_t)r * kDecodeStatWords;
   if (!a.req_active[r] || a.block_done[r]) {
     if (inb) a.commit_mask[row] = 0;
+    if (j == 0 && a.req_active[r]) acct[3] += 1;    // idle step: the block is done
     return;
   }
   const int bs = a.req_bs[r];
@@ -129,10 +135,19 @@ __global__ __launch_bounds__(64) void commit_kernel(CommitArgs a) {
       complete = !__any(left);
     }
   }
+  const int n_tau = __popcll(__ballot(commit && pb != 0ull && p >= a.tau));
   if (j == 0) {
+    const int n = __popcll(cb);
     a.step_count[r] += 1;
-    a.commit_count[r] += __popcll(cb);
+    a.commit_count[r] += n;
     if (sb == 0ull) a.block_done[r] = complete ? 2 : 1;
+    if (pb != 0ull) {
+      acct[0] += n_tau;
+      acct[1] += n - n_tau;
+    } else {
+      acct[2] += n;
+    }
+    acct[4 + n] += 1;
   }
 }
 
@@ -158,7 +173,38 @@ __global__ __launch_bounds__(64) void block_reset_kernel(int B, const int* __res
   }
 }
 
+// Head of a denoising step: requests whose block is already done take no
+// part (their row count in the step table goes to 0, so the attention skips
+// them), and when no request has an open block the step's row counts go to
+// 0, so every kernel of the step exits at once.  Such steps arise when a
+// captured graph of several steps runs past a block's end.  The host writes
+// the table afresh whenever blocks move (dinfer_advance_blocks), which
+// restores the counts.
+__global__ __launch_bounds__(64) void step_gate_kernel(int batch, int* nrows, int* lm_rows,
+                                                       int* req_nrows,
+                                                       const int* __restrict__ req_active,
+                                                       const int* __restrict__ block_done) {
+  bool open = false;
+  for (int r = threadIdx.x; r < batch; r += 64) {
+    const bool act = req_active[r] != 0;
+    const bool done = block_done[r] != 0;
+    if (act && done) req_nrows[r] = 0;
+    open = open || (act && !done);
+  }
+  if (!__any(open) && threadIdx.x == 0) {
+    *nrows = 0;
+    *lm_rows = 0;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_step_gate(int batch, int* nrows, int* lm_rows, int* req_nrows,
+                            const int* req_active, const int* block_done, hipStream_t st) {
+  hipLaunchKernelGGL(step_gate_kernel, dim3(1), dim3(64), 0, st, batch, nrows, lm_rows, req_nrows,
+                     req_active, block_done);
+  return hipGetLastError();
+}
 
 hipError_t launch_commit(const CommitArgs& a, hipStream_t st) {
   if (a.B > 64) return hipErrorInvalidValue;

@@ -37,6 +37,7 @@
 #include "common.h"
 #include "gemm_split.h"
 #include "kernels.h"
+#include "vocab_common.h"
 
 namespace dinfer {
 
@@ -51,12 +52,17 @@ namespace {
 // One workgroup's tile: rows [0, M) of A (row r at A + (arow ? arow[r] : r) * K)
 // times weight rows [n_tile, n_tile + 16*NT*NW) of W (N rows) over K chunks
 // [c_begin, c_end), written to out[row * ldo + column].
-template <typename TW, int MT, int NT, int NW, bool GUARD>
+//
+// VS = true (LM head): instead of storing the tile (or besides it, when out
+// is not null) the workgroup stages it in LDS and reduces every row of it to
+// its vocab record (vocab_common.h), rows numbered from vrow0.
+template <typename TW, int MT, int NT, int NW, bool GUARD, bool VS = false>
 __device__ __forceinline__ void skinny_tile(const float* __restrict__ A,
                                             const int* __restrict__ arow, int M,
                                             const TW* __restrict__ W, int N, int K,
                                             float* __restrict__ out, int ldo, int n_tile,
-                                            int c_begin, int c_end) {
+                                            int c_begin, int c_end,
+                                            const VocabEpi* ve = nullptr, int vrow0 = 0) {
   using MF = Mfma<TW>;
   using AS = ASplit<TW>;
   constexpr int PL = AS::PLANES;
@@ -200,15 +206,41 @@ __device__ __forceinline__ void skinny_tile(const float* __restrict__ A,
     if (c + 2 < c_end) step(c + 2, b2, a0, b1, a1);
   }
 
+  if constexpr (VS) {
+    // the logit tile [ROWS][NCOL] in the (now idle) activation staging
+    // buffer; rows padded so the four row groups of a store fall on
+    // different banks
+    constexpr int NCOL = 16 * NT * NW;
+    constexpr int LDZ = NCOL + (sizeof(TW) == 2 ? 16 : 8);
+    static_assert(ROWS * LDZ * sizeof(float) <= sizeof(As), "logit tile fits the staging buffer");
+    float* zt = reinterpret_cast<float*>(&As[0][0][0]);
+    __syncthreads();
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
+    for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
+      for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = mt * 16 + lg * 4 + i;
-        if (row < M) out[(size_t)row * ldo + n0 + nt * 16 + lc] = acc[mt][nt][i];
-      }
+        for (int i = 0; i < 4; ++i) {
+          const int row = mt * 16 + lg * 4 + i;
+          const int col = wave * (16 * NT) + nt * 16 + lc;
+          zt[row * LDZ + col] = acc[mt][nt][i];
+          if (out != nullptr && row < M) out[(size_t)row * ldo + n0 + nt * 16 + lc] = acc[mt][nt][i];
+        }
+    __syncthreads();
+    vocab::tile_records<NCOL, NW>(zt, LDZ, M, vrow0, n_tile, N, n_tile / NCOL, ve->n_tiles,
+                                  ve->row_plant_id, ve->row_plant_bias, ve->mask_id, ve->rec_f,
+                                  ve->rec_i);
+  } else {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int row = mt * 16 + lg * 4 + i;
+          if (row < M) out[(size_t)row * ldo + n0 + nt * 16 + lc] = acc[mt][nt][i];
+        }
+  }
 }
 
 template <typename TW, int MT, int NT, int NW, bool GUARD>
@@ -237,6 +269,29 @@ __global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(const float* __res
   skinny_tile<TW, MT, NT, NW, GUARD>(A + (size_t)mt * ROWS * K, nullptr, min(M, ROWS), W, N, K,
                                      P + ((size_t)split * m_cap + (size_t)mt * ROWS) * N, N,
                                      tile * (16 * NT * NW), (split * C) / S, ((split + 1) * C) / S);
+}
+
+// LM head: the skinny projection of the block rows over the whole
+// vocabulary (one K slice), each workgroup reducing its tile to vocab
+// records instead of storing logits (also stored when ve.logits is set).
+template <typename TW, int MT, int NT, int NW, bool GUARD>
+__global__ __launch_bounds__(NW * 64) void gemm_skinny_lmhead_kernel(
+    const float* __restrict__ A, const TW* __restrict__ W, const int* __restrict__ m_dev,
+    int m_cap, int N, int K, int n_tiles, int m_tiles, VocabEpi ve) {
+  constexpr int KC = 4 * Mfma<TW>::KSTEP;
+  constexpr int ROWS = 16 * MT;
+  const int bid = blockIdx.x;
+  const int grp = bid / (8 * m_tiles);
+  const int rem = bid % (8 * m_tiles);
+  const int mt = rem / 8;
+  const int tile = grp * 8 + rem % 8;
+  if (tile >= n_tiles) return;
+  const int M = (m_dev ? min(*m_dev, m_cap) : m_cap) - mt * ROWS;
+  if (M <= 0) return;
+  skinny_tile<TW, MT, NT, NW, GUARD, true>(
+      A + (size_t)mt * ROWS * K, nullptr, min(M, ROWS), W, N, K,
+      ve.logits ? ve.logits + (size_t)mt * ROWS * N : nullptr, N, tile * (16 * NT * NW), 0,
+      K / KC, &ve, mt * ROWS);
 }
 
 // Grouped projection of the MoE experts: workgroup (expert e, column group,
@@ -311,6 +366,58 @@ hipError_t run_skinny(const GemmPlan& p, const float* A, const void* W, float* o
                        static_cast<const TW*>(W), out, m_dev, m_cap, N, K, n_tiles, p.splits,
                        mtiles);
   return hipGetLastError();
+}
+
+template <typename TW, int MT, int NT, int NW>
+hipError_t run_skinny_lmhead(const GemmPlan& p, const float* A, const void* W, const int* m_dev,
+                             int m_cap, int N, int K, const VocabEpi& e, hipStream_t st) {
+  const int n_tiles = N / (16 * NT * NW);
+  const int mtiles = p.mtiles > 1 ? p.mtiles : 1;
+  if (m_cap > 16 * MT * mtiles || p.splits != 1 || e.n_tiles != n_tiles) return hipErrorInvalidValue;
+  const dim3 grid((n_tiles + 7) / 8 * 8 * mtiles);
+  if (p.guard)
+    hipLaunchKernelGGL((gemm_skinny_lmhead_kernel<TW, MT, NT, NW, true>), grid, dim3(NW * 64), 0,
+                       st, A, static_cast<const TW*>(W), m_dev, m_cap, N, K, n_tiles, mtiles, e);
+  else
+    hipLaunchKernelGGL((gemm_skinny_lmhead_kernel<TW, MT, NT, NW, false>), grid, dim3(NW * 64), 0,
+                       st, A, static_cast<const TW*>(W), m_dev, m_cap, N, K, n_tiles, mtiles, e);
+  return hipGetLastError();
+}
+
+template <typename TW, int NT, int NW>
+hipError_t lmhead_mt(const GemmPlan& p, const float* A, const void* W, const int* m_dev,
+                     int m_cap, int N, int K, const VocabEpi& e, hipStream_t st) {
+  switch (p.mt) {
+    case 1: return run_skinny_lmhead<TW, 1, NT, NW>(p, A, W, m_dev, m_cap, N, K, e, st);
+    case 2: return run_skinny_lmhead<TW, 2, NT, NW>(p, A, W, m_dev, m_cap, N, K, e, st);
+    case 3: return run_skinny_lmhead<TW, 3, NT, NW>(p, A, W, m_dev, m_cap, N, K, e, st);
+    case 4: return run_skinny_lmhead<TW, 4, NT, NW>(p, A, W, m_dev, m_cap, N, K, e, st);
+    default: break;
+  }
+  if constexpr (NW == 8) {
+    return hipErrorInvalidValue;
+  } else {
+    switch (p.mt) {
+      case 5: return run_skinny_lmhead<TW, 5, NT, NW>(p, A, W, m_dev, m_cap, N, K, e, st);
+      case 6: return run_skinny_lmhead<TW, 6, NT, NW>(p, A, W, m_dev, m_cap, N, K, e, st);
+      case 7: return run_skinny_lmhead<TW, 7, NT, NW>(p, A, W, m_dev, m_cap, N, K, e, st);
+      case 8: return run_skinny_lmhead<TW, 8, NT, NW>(p, A, W, m_dev, m_cap, N, K, e, st);
+      default: return hipErrorInvalidValue;
+    }
+  }
+}
+
+template <typename TW>
+hipError_t lmhead_dispatch(const GemmPlan& p, const float* A, const void* W, const int* m_dev,
+                           int m_cap, int N, int K, const VocabEpi& e, hipStream_t st) {
+  if (p.kind == 1)
+    return launch_gemm_fat_lmhead(sizeof(TW) == 2 ? DType::BF16 : DType::F32, p.nw, A, W, m_dev,
+                                  m_cap, N, K, e, st);
+  if constexpr (sizeof(TW) == 2) {
+    if (p.nw == 8) return lmhead_mt<TW, 2, 8>(p, A, W, m_dev, m_cap, N, K, e, st);
+  }
+  return p.nt == 2 ? lmhead_mt<TW, 2, 4>(p, A, W, m_dev, m_cap, N, K, e, st)
+                   : lmhead_mt<TW, 1, 4>(p, A, W, m_dev, m_cap, N, K, e, st);
 }
 
 template <typename TW, int NT, int NW>
@@ -473,6 +580,21 @@ GemmPlan plan_gemm(DType t, int m_cap, int N, int K, int target_wgs) {
   p.splits = s;
   p.grid = n_tiles * s * p.mtiles;
   return p;
+}
+
+int gemm_lmhead_tiles(const GemmPlan& p, int N) {
+  const int cols = p.kind == 1 ? 64 * p.nw : 16 * p.nt * p.nw;
+  return (N + cols - 1) / cols;
+}
+
+hipError_t launch_gemm_lmhead(const GemmPlan& p, DType t, const float* A, const void* W,
+                              const int* m_dev, int m_cap, int N, int K, const VocabEpi& e,
+                              hipStream_t st) {
+  if (!e.row_plant_id || !e.row_plant_bias || !e.rec_f || !e.rec_i ||
+      e.n_tiles != gemm_lmhead_tiles(p, N))
+    return hipErrorInvalidValue;
+  if (t == DType::F32) return lmhead_dispatch<float>(p, A, W, m_dev, m_cap, N, K, e, st);
+  return lmhead_dispatch<bf16>(p, A, W, m_dev, m_cap, N, K, e, st);
 }
 
 hipError_t launch_gemm(const GemmPlan& p, DType t, const float* A, const void* W, float* out,

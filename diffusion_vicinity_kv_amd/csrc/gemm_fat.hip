@@ -6,6 +6,7 @@
 #include "common.h"
 #include "gemm_split.h"
 #include "kernels.h"
+#include "vocab_common.h"
 
 namespace dinfer {
 
@@ -25,12 +26,16 @@ namespace {
 // stored).
 constexpr int kFatM = 128;
 
-template <typename TW, int WN>
+//
+// VS = true (LM head, one K split): the 128 x 64*WN tile is reduced to vocab
+// records (vocab_common.h) through LDS, 64 rows at a time, instead of being
+// stored (stored as well when ve.logits is set).
+template <typename TW, int WN, bool VS>
 __global__ __launch_bounds__(128 * WN) void gemm_fat_kernel(const float* __restrict__ A,
                                                             const TW* __restrict__ W,
                                                             float* __restrict__ Cout,
                                                             const int* __restrict__ m_dev,
-                                                            int m_cap, int N, int K) {
+                                                            int m_cap, int N, int K, VocabEpi ve) {
   constexpr int kFatN = 64 * WN, kFatThreads = 128 * WN;
   using MF = Mfma<TW>;
   using AS = ASplit<TW>;
@@ -51,8 +56,13 @@ __global__ __launch_bounds__(128 * WN) void gemm_fat_kernel(const float* __restr
   constexpr int BE = 64 * VEC;                 // elements of one packed weight block
   constexpr int BV = (kFatN / 16) * KK * 64 / kFatThreads;   // W vectors per thread per slab
   static_assert((kFatN / 16) * KK * 64 % kFatThreads == 0, "weight slab must split evenly");
-  __shared__ __attribute__((aligned(16))) TW As[2][PL][kFatM * STR];
-  __shared__ __attribute__((aligned(16))) TW Bs[2][kFatN * STR];
+  // one LDS block: activation planes, then weight slabs (the LM head's
+  // epilogue reuses all of it)
+  constexpr size_t kAsBytes = (size_t)2 * PL * kFatM * STR * sizeof(TW);
+  constexpr size_t kBsBytes = (size_t)2 * kFatN * STR * sizeof(TW);
+  __shared__ __attribute__((aligned(16))) unsigned char smem[kAsBytes + kBsBytes];
+  auto& As = *reinterpret_cast<TW(*)[2][PL][kFatM * STR]>(smem);
+  auto& Bs = *reinterpret_cast<TW(*)[2][kFatN * STR]>(smem + kAsBytes);
 
   const int M = m_dev ? min(*m_dev, m_cap) : m_cap;
   const int m0 = blockIdx.y * kFatM;
@@ -153,6 +163,31 @@ __global__ __launch_bounds__(128 * WN) void gemm_fat_kernel(const float* __restr
     if (kt + 2 < nk) step(kt + 2, a0, b0, a1, b1);
   }
 
+  if constexpr (VS) {
+    constexpr int LDZ = kFatN + 16;              // padded rows: stores spread over banks
+    static_assert((size_t)64 * LDZ * sizeof(float) <= kAsBytes + kBsBytes, "half tile fits LDS");
+    float* zt = reinterpret_cast<float*>(smem);
+    for (int h = 0; h < 2; ++h) {               // row halves: waves wm == h stage theirs
+      __syncthreads();
+      if (wm == h) {
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+          for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              zt[(mt * 16 + lg * 4 + i) * LDZ + wn * 64 + nt * 16 + lc] = acc[mt][nt][i];
+      }
+      __syncthreads();
+      const int r0 = m0 + h * 64;
+      if (r0 < M)
+        vocab::tile_records<kFatN, 2 * WN>(zt, LDZ, min(64, M - r0), r0, n0, N, blockIdx.x,
+                                           ve.n_tiles, ve.row_plant_id, ve.row_plant_bias,
+                                           ve.mask_id, ve.rec_f, ve.rec_i);
+    }
+    Cout = ve.logits;
+    if (Cout == nullptr) return;
+  }
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
@@ -165,29 +200,43 @@ __global__ __launch_bounds__(128 * WN) void gemm_fat_kernel(const float* __restr
       }
 }
 
-}  // namespace
-
-hipError_t launch_gemm_fat(DType t, int wn, int splits, const float* A, const void* W,
-                           float* out, const int* m_dev, int m_cap, int N, int K, hipStream_t st) {
+template <bool VS>
+hipError_t fat_launch(DType t, int wn, int splits, const float* A, const void* W, float* out,
+                      const int* m_dev, int m_cap, int N, int K, const VocabEpi& ve,
+                      hipStream_t st) {
   const int bk = t == DType::F32 ? 32 : 64;   // K per slab
   if ((wn != 2 && wn != 4) || splits < 1 || splits > K / bk) return hipErrorInvalidValue;
   const dim3 grid((N + 64 * wn - 1) / (64 * wn), (m_cap + kFatM - 1) / kFatM, splits);
   if (t == DType::F32) {
     if (wn == 4)
-      hipLaunchKernelGGL((gemm_fat_kernel<float, 4>), grid, dim3(512), 0, st, A,
-                         static_cast<const float*>(W), out, m_dev, m_cap, N, K);
+      hipLaunchKernelGGL((gemm_fat_kernel<float, 4, VS>), grid, dim3(512), 0, st, A,
+                         static_cast<const float*>(W), out, m_dev, m_cap, N, K, ve);
     else
-      hipLaunchKernelGGL((gemm_fat_kernel<float, 2>), grid, dim3(256), 0, st, A,
-                         static_cast<const float*>(W), out, m_dev, m_cap, N, K);
+      hipLaunchKernelGGL((gemm_fat_kernel<float, 2, VS>), grid, dim3(256), 0, st, A,
+                         static_cast<const float*>(W), out, m_dev, m_cap, N, K, ve);
   } else {
     if (wn == 4)
-      hipLaunchKernelGGL((gemm_fat_kernel<bf16, 4>), grid, dim3(512), 0, st, A,
-                         static_cast<const bf16*>(W), out, m_dev, m_cap, N, K);
+      hipLaunchKernelGGL((gemm_fat_kernel<bf16, 4, VS>), grid, dim3(512), 0, st, A,
+                         static_cast<const bf16*>(W), out, m_dev, m_cap, N, K, ve);
     else
-      hipLaunchKernelGGL((gemm_fat_kernel<bf16, 2>), grid, dim3(256), 0, st, A,
-                         static_cast<const bf16*>(W), out, m_dev, m_cap, N, K);
+      hipLaunchKernelGGL((gemm_fat_kernel<bf16, 2, VS>), grid, dim3(256), 0, st, A,
+                         static_cast<const bf16*>(W), out, m_dev, m_cap, N, K, ve);
   }
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gemm_fat(DType t, int wn, int splits, const float* A, const void* W,
+                           float* out, const int* m_dev, int m_cap, int N, int K, hipStream_t st) {
+  return fat_launch<false>(t, wn, splits, A, W, out, m_dev, m_cap, N, K, VocabEpi{}, st);
+}
+
+hipError_t launch_gemm_fat_lmhead(DType t, int wn, const float* A, const void* W,
+                                  const int* m_dev, int m_cap, int N, int K, const VocabEpi& e,
+                                  hipStream_t st) {
+  if (e.n_tiles != (N + 64 * wn - 1) / (64 * wn)) return hipErrorInvalidValue;
+  return fat_launch<true>(t, wn, 1, A, W, e.logits, m_dev, m_cap, N, K, e, st);
 }
 
 }  // namespace dinfer

@@ -106,6 +106,32 @@ hipError_t launch_vocab_stats(const VocabPlan& p, const float* logits, int rows,
                               void* scratch, int* argmax, float* conf, float* lse, int* topk_id,
                               float* topk_p, hipStream_t st);
 
+// LM head with the vocab statistics fused into its epilogue: the projection
+// kernel reduces each (row, column tile) of its logits to a record (max, sum
+// of exp, top-8) after the planting bias and MASK exclusion; the merge kernel
+// combines a row's records.  Records: rec_f [rows][n_tiles][10] floats, then
+// rec_i [rows][n_tiles][8] ints (vocab_record_bytes).
+struct VocabEpi {
+  const int* row_plant_id;   // [rows] planted id (-1 none)
+  const float* row_plant_bias;
+  int mask_id;
+  float* logits;             // [rows][N] also stored when not null
+  float* rec_f;
+  int* rec_i;
+  int n_tiles;               // column tiles of the plan (gemm_lmhead_tiles)
+};
+int gemm_lmhead_tiles(const GemmPlan& p, int N);
+hipError_t launch_gemm_lmhead(const GemmPlan& p, DType t, const float* A, const void* W,
+                              const int* m_dev, int m_cap, int N, int K, const VocabEpi& e,
+                              hipStream_t st);
+hipError_t launch_gemm_fat_lmhead(DType t, int wn, const float* A, const void* W,
+                                  const int* m_dev, int m_cap, int N, int K, const VocabEpi& e,
+                                  hipStream_t st);
+size_t vocab_record_bytes(int rows, int n_tiles);
+hipError_t launch_vocab_merge_tiles(int rows, int n_tiles, const float* rec_f, const int* rec_i,
+                                    int* argmax, float* conf, float* lse, int* topk_id,
+                                    float* topk_p, hipStream_t st);
+
 // ---- mixture of experts -------------------------------------------------------
 hipError_t launch_moe_route(DType t, PassTable tb, int m_cap, const float* f, int d,
                             const void* Wr, int E, int top_k, const float* router_bias,
@@ -119,6 +145,10 @@ hipError_t launch_moe_combine(const int* nrows, int m_cap, float* x, const float
                               int top_k, int d, hipStream_t st);
 
 // ---- decode state ---------------------------------------------------------------
+// Per-request decode accounting words: [0] threshold commits, [1] credit-only
+// commits, [2] fallback commits, [3] idle steps (block already done), [4 + k]
+// steps that committed k tokens (k = 0..64).
+constexpr int kDecodeStatWords = 72;
 struct CommitArgs {
   int batch, B, max_len, mask_id, hierarchical;
   int eos_id;            // -1: none
@@ -141,8 +171,11 @@ struct CommitArgs {
   int* block_done;
   int* step_count;
   int* commit_count;
+  int* decode_stats;     // [batch][kDecodeStatWords]
 };
 hipError_t launch_commit(const CommitArgs& a, hipStream_t st);
+hipError_t launch_step_gate(int batch, int* nrows, int* lm_rows, int* req_nrows,
+                            const int* req_active, const int* block_done, hipStream_t st);
 hipError_t launch_block_reset(int batch, int B, const int* req_mask, float* credit, int* tracked,
                               uint8_t* smooth_valid, uint8_t* commit_mask, int* block_done,
                               int* step_count, hipStream_t st);

@@ -70,13 +70,13 @@ struct Layout {
   bool moe;
   int E, topk, Fe, Fs, assign_cap;
   AttnPlan a_step, a_ref;
-  VocabPlan vp;
+  int lm_tiles;                 // column tiles of the LM head (vocab records per row)
   size_t part_elems, attn_o_elems, attn_ml_elems;
   // byte offsets
   size_t off_rope, off_kvk, off_kvv, off_x, off_a, off_q, off_o, off_act, off_part, off_ao,
-      off_aml, off_hf, off_logits, off_rpid, off_rpb, off_vscr, off_argmax, off_conf, off_lse,
+      off_aml, off_hf, off_logits, off_lmrec, off_rpid, off_rpb, off_argmax, off_conf, off_lse,
       off_tid, off_tp, off_credit, off_tracked, off_sid, off_sp, off_sv, off_cm, off_done,
-      off_steps, off_ccount, off_tab_step, off_tab_ref, off_mask, off_misc, off_sel, off_gate,
+      off_steps, off_ccount, off_dstat, off_tab_step, off_tab_ref, off_mask, off_misc, off_sel, off_gate,
       off_pos, off_rowof, off_ecount, off_eoff, off_nassign, off_egu, off_eact, off_ey, off_rlog,
       total;
   size_t kv_layer_elems;        // elements of one layer's K (or V) cache
@@ -184,7 +184,7 @@ bool make_layout(const dinfer_model_cfg* m, const dinfer_decode_cfg* dc, int max
   l.attn_o_elems = std::max((size_t)l.a_step.n_split * l.m_step, (size_t)l.a_ref.n_split * l.m_ref) *
                    l.H * l.hd;
   l.attn_ml_elems = l.attn_o_elems / l.hd * 2;
-  l.vp = plan_vocab(l.lm_rows, V, 1024);
+  l.lm_tiles = gemm_lmhead_tiles(l.g_lm, V);
   l.tab_ints_step = table_ints(l.m_step, max_batch);
   l.tab_ints_ref = table_ints(l.m_ref, max_batch);
   l.Lp = attn_cache_len(max_len);
@@ -210,9 +210,9 @@ bool make_layout(const dinfer_model_cfg* m, const dinfer_decode_cfg* dc, int max
   l.off_aml = take(l.attn_ml_elems * 4);
   l.off_hf = take((size_t)(l.lm_rows + 15) / 16 * 16 * d * 4);
   l.off_logits = take((size_t)l.lm_rows * V * 4);
+  l.off_lmrec = take(vocab_record_bytes(l.lm_rows, l.lm_tiles));
   l.off_rpid = take((size_t)l.lm_rows * 4);
   l.off_rpb = take((size_t)l.lm_rows * 4);
-  l.off_vscr = take(vocab_scratch_bytes(l.vp, l.lm_rows));
   l.off_argmax = take((size_t)l.lm_rows * 4);
   l.off_conf = take((size_t)l.lm_rows * 4);
   l.off_lse = take((size_t)l.lm_rows * 4);
@@ -227,6 +227,7 @@ bool make_layout(const dinfer_model_cfg* m, const dinfer_decode_cfg* dc, int max
   l.off_done = take((size_t)max_batch * 4);
   l.off_steps = take((size_t)max_batch * 4);
   l.off_ccount = take((size_t)max_batch * 4);
+  l.off_dstat = take((size_t)max_batch * kDecodeStatWords * 4);
   l.off_tab_step = take((size_t)l.tab_ints_step * 4);
   l.off_tab_ref = take((size_t)l.tab_ints_ref * 4);
   l.off_mask = take((size_t)max_batch * 4);
@@ -300,6 +301,7 @@ struct dinfer_ctx {
   bool step_dirty = true;
   int state = 0;                  // 0 init, 1 batch bound
   bool stats_ready = false;
+  bool keep_logits = false;       // the LM head also stores the fp32 logits
   // graph
   hipGraphExec_t graph = nullptr;
   int graph_steps = 0;
@@ -384,6 +386,9 @@ dinfer_status run_pass(dinfer_ctx* c, bool step) {
   const size_t stride_q = (size_t)m_cap * 3 * d, stride_d = (size_t)m_cap * d,
                stride_g = (size_t)m_cap * 2 * F;
 
+  if (step)
+    HIP_TRY(launch_step_gate(c->batch, tab, tab + 1, const_cast<int*>(tb.req_nrows), tb.req_active,
+                             c->at<int>(L.off_done), st));
   HIP_TRY(launch_embed(dt, tb, m_cap, c->tokens, L.max_len, c->tok_emb, d, L.V, c->m.mask_id,
                        step ? c->dc.smooth_alpha : 0.f, c->at<int>(L.off_sid),
                        c->at<float>(L.off_sp), c->at<uint8_t>(L.off_sv), L.B, x, st));
@@ -440,13 +445,22 @@ dinfer_status run_pass(dinfer_ctx* c, bool step) {
   HIP_TRY(launch_final_norm(dt, tb, L.max_batch, L.B, x, part, x_splits, stride_d, c->final_norm,
                             c->m.rms_eps, hf, d, c->plant_id, c->plant_bias, L.max_len,
                             c->at<int>(L.off_rpid), c->at<float>(L.off_rpb), st));
-  float* logits = c->at<float>(L.off_logits);
-  HIP_TRY(launch_gemm(L.g_lm, dt, hf, c->lm_head, logits, tab + 1, L.lm_rows, L.V, d, st));
-  HIP_TRY(launch_vocab_stats(L.vp, logits, c->batch * L.B, L.V, c->at<int>(L.off_rpid),
-                             c->at<float>(L.off_rpb), c->m.mask_id, c->at<char>(L.off_vscr),
-                             c->at<int>(L.off_argmax), c->at<float>(L.off_conf),
-                             c->at<float>(L.off_lse), c->at<int>(L.off_tid),
-                             c->at<float>(L.off_tp), st));
+  // LM head with the vocab statistics in its epilogue: per-(row, column
+  // tile) records, then one merge per row; the fp32 logits are stored only
+  // while keep_logits is on (inspection)
+  VocabEpi ve{};
+  ve.row_plant_id = c->at<int>(L.off_rpid);
+  ve.row_plant_bias = c->at<float>(L.off_rpb);
+  ve.mask_id = c->m.mask_id;
+  ve.logits = c->keep_logits ? c->at<float>(L.off_logits) : nullptr;
+  ve.rec_f = c->at<float>(L.off_lmrec);
+  ve.rec_i = reinterpret_cast<int*>(ve.rec_f + (size_t)L.lm_rows * L.lm_tiles * (2 + 8));
+  ve.n_tiles = L.lm_tiles;
+  HIP_TRY(launch_gemm_lmhead(L.g_lm, dt, hf, c->lm_head, tab + 1, L.lm_rows, L.V, d, ve, st));
+  HIP_TRY(launch_vocab_merge_tiles(c->batch * L.B, L.lm_tiles, ve.rec_f, ve.rec_i,
+                                   c->at<int>(L.off_argmax), c->at<float>(L.off_conf),
+                                   c->at<float>(L.off_lse), c->at<int>(L.off_tid),
+                                   c->at<float>(L.off_tp), st));
   return DINFER_OK;
 }
 
@@ -482,6 +496,7 @@ dinfer_status launch_commit_step(dinfer_ctx* c) {
   a.block_done = c->at<int>(L.off_done);
   a.step_count = c->at<int>(L.off_steps);
   a.commit_count = c->at<int>(L.off_ccount);
+  a.decode_stats = c->at<int>(L.off_dstat);
   HIP_TRY(launch_commit(a, c->st));
   return DINFER_OK;
 }
@@ -614,6 +629,8 @@ dinfer_status dinfer_step_init(const dinfer_model_cfg* m, const dinfer_decode_cf
       hipMemsetAsync(c->at<char>(L.off_done), 0, (size_t)max_batch * 4, c->stream) != hipSuccess ||
       hipMemsetAsync(c->at<char>(L.off_steps), 0, (size_t)max_batch * 4, c->stream) != hipSuccess ||
       hipMemsetAsync(c->at<char>(L.off_ccount), 0, (size_t)max_batch * 4, c->stream) != hipSuccess ||
+      hipMemsetAsync(c->at<char>(L.off_dstat), 0, (size_t)max_batch * kDecodeStatWords * 4,
+                     c->stream) != hipSuccess ||
       hipMemsetAsync(c->at<char>(L.off_tab_step), 0, (size_t)L.tab_ints_step * 4, c->stream) !=
           hipSuccess ||
       hipMemsetAsync(c->at<char>(L.off_tab_ref), 0, (size_t)L.tab_ints_ref * 4, c->stream) !=
@@ -683,6 +700,8 @@ dinfer_status dinfer_set_batch(dinfer_ctx* c, int32_t batch, int32_t* d_tokens,
   HIP_TRY(hipMemsetAsync(c->at<char>(L.off_done), 0, (size_t)L.max_batch * 4, c->stream));
   HIP_TRY(hipMemsetAsync(c->at<char>(L.off_steps), 0, (size_t)L.max_batch * 4, c->stream));
   HIP_TRY(hipMemsetAsync(c->at<char>(L.off_ccount), 0, (size_t)L.max_batch * 4, c->stream));
+  HIP_TRY(hipMemsetAsync(c->at<char>(L.off_dstat), 0, (size_t)L.max_batch * kDecodeStatWords * 4,
+                         c->stream));
   return upload_step_table(c);
 }
 
@@ -711,6 +730,8 @@ dinfer_status dinfer_refill(dinfer_ctx* c, int32_t slot, int32_t prompt_len, int
   HIP_TRY(hipMemsetAsync(c->at<int>(L.off_done) + slot, 0, 4, c->stream));
   HIP_TRY(hipMemsetAsync(c->at<int>(L.off_steps) + slot, 0, 4, c->stream));
   HIP_TRY(hipMemsetAsync(c->at<int>(L.off_ccount) + slot, 0, 4, c->stream));
+  HIP_TRY(hipMemsetAsync(c->at<int>(L.off_dstat) + (size_t)slot * kDecodeStatWords, 0,
+                         kDecodeStatWords * 4, c->stream));
   return DINFER_OK;
 }
 
@@ -1052,6 +1073,18 @@ dinfer_status dinfer_run_to_completion(dinfer_ctx* c, int32_t max_steps, dinfer_
   return DINFER_OK;
 }
 
+dinfer_status dinfer_keep_logits(dinfer_ctx* c, int32_t on) {
+  if (!c) return fail(DINFER_E_ARG, "ctx is null");
+  if ((on != 0) != c->keep_logits && c->graph) {
+    // the captured step graph holds the LM head's arguments
+    (void)hipGraphExecDestroy(c->graph);
+    c->graph = nullptr;
+    c->graph_steps = 0;
+  }
+  c->keep_logits = on != 0;
+  return DINFER_OK;
+}
+
 dinfer_status dinfer_get_step_view(const dinfer_ctx* c, dinfer_step_view* v) {
   if (!c || !v) return fail(DINFER_E_ARG, "null argument");
   const Layout& L = c->L;
@@ -1074,6 +1107,8 @@ dinfer_status dinfer_get_step_view(const dinfer_ctx* c, dinfer_step_view* v) {
   v->block_done = c->at<int>(L.off_done);
   v->step_count = c->at<int>(L.off_steps);
   v->commit_count = c->at<int>(L.off_ccount);
+  v->decode_stats = c->at<int>(L.off_dstat);
+  v->decode_stat_words = kDecodeStatWords;
   v->kv_k = c->at<char>(L.off_kvk);
   v->kv_v = c->at<char>(L.off_kvv);
   v->kv_len = L.Lp;

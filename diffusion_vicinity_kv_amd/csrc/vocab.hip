@@ -13,6 +13,7 @@
 // a row (one wave per row) in split order.
 #include "common.h"
 #include "kernels.h"
+#include "vocab_common.h"
 
 #include <climits>
 #include <type_traits>
@@ -21,72 +22,9 @@ namespace dinfer {
 
 namespace {
 
+using namespace vocab;
+
 constexpr int kThreads = 256;
-constexpr int kTop = 8;
-constexpr float kLog2e = 1.4426950408889634f;
-
-// Order used everywhere: larger value first, then smaller id.
-__device__ __forceinline__ bool better(float va, int ia, float vb, int ib) {
-  return va > vb || (va == vb && ia < ib);
-}
-
-// Wave-wide best (value, id) pair.
-__device__ __forceinline__ void wave_best(float& v, int& id) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const float ov = __shfl_xor(v, o, 64);
-    const int oi = __shfl_xor(id, o, 64);
-    if (better(ov, oi, v, id)) {
-      v = ov;
-      id = oi;
-    }
-  }
-}
-
-// Extract the wave's top-8 from per-lane sorted lists (pop-front on the
-// winning lane).  Results are uniform across the wave.
-__device__ __forceinline__ void wave_top8(float (&tv)[kTop], int (&ti)[kTop], float (&ov)[kTop],
-                                          int (&oi)[kTop]) {
-#pragma unroll
-  for (int k = 0; k < kTop; ++k) {
-    float v = tv[0];
-    int id = ti[0];
-    wave_best(v, id);
-    ov[k] = v;
-    oi[k] = id;
-    if (tv[0] == v && ti[0] == id) {
-#pragma unroll
-      for (int j = 0; j < kTop - 1; ++j) {
-        tv[j] = tv[j + 1];
-        ti[j] = ti[j + 1];
-      }
-      tv[kTop - 1] = -INFINITY;
-      ti[kTop - 1] = INT_MAX;
-    }
-  }
-}
-
-__device__ __forceinline__ void insert_top8(float (&tv)[kTop], int (&ti)[kTop], float v, int id) {
-  // ids reach a thread in increasing order, so an equal value never displaces
-  // an entry already kept (that entry has the smaller id).  The insertion is
-  // a chain of selects (no per-slot branches): once a slot takes the new
-  // entry, every later slot takes its predecessor.
-  if (!(v > tv[kTop - 1])) return;
-  bool carry = false;
-  float cv = v;
-  int ci = id;
-#pragma unroll
-  for (int k = 0; k < kTop; ++k) {
-    const bool take = carry || cv > tv[k];
-    const float tvk = tv[k];
-    const int tik = ti[k];
-    tv[k] = take ? cv : tvk;
-    ti[k] = take ? ci : tik;
-    cv = take ? tvk : cv;
-    ci = take ? tik : ci;
-    carry = take;
-  }
-}
 
 // part_f [rows][n_split][2 + 8] = (max, sum exp(z - max), top-8 values);
 // part_i [rows][n_split][8] = top-8 ids.
@@ -312,7 +250,113 @@ __global__ __launch_bounds__(64) void vocab_merge_kernel(int rows, int n_split,
   }
 }
 
+// Merge of the LM head's per-(row, column tile) records: one workgroup per
+// row.  Thread t folds tiles t, t + 256, ... (ascending, so ids arrive in
+// increasing order for equal values) into an online (max, sum of exp) and a
+// sorted top-8, the waves merge theirs with wave64 exchanges, and wave 0
+// merges the four waves' and emits the statistics.
+__global__ __launch_bounds__(kThreads) void vocab_merge_tiles_kernel(
+    int n_tiles, const float* __restrict__ rec_f, const int* __restrict__ rec_i,
+    int* __restrict__ argmax, float* __restrict__ conf, float* __restrict__ lse,
+    int* __restrict__ topk_id, float* __restrict__ topk_p) {
+  __shared__ float s_m[kThreads / 64], s_s[kThreads / 64];
+  __shared__ float s_tv[kThreads / 64][kTop];
+  __shared__ int s_ti[kThreads / 64][kTop];
+  const int row = blockIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  float m = -INFINITY, s = 0.f;
+  float tv[kTop];
+  int ti[kTop];
+#pragma unroll
+  for (int k = 0; k < kTop; ++k) {
+    tv[k] = -INFINITY;
+    ti[k] = INT_MAX;
+  }
+  for (int t = threadIdx.x; t < n_tiles; t += kThreads) {
+    const float* pf = rec_f + ((size_t)row * n_tiles + t) * kRecF;
+    const int* pi = rec_i + ((size_t)row * n_tiles + t) * kTop;
+    float f[kRecF];
+    int id[kTop];
+#pragma unroll
+    for (int k = 0; k < kRecF; ++k) f[k] = pf[k];
+#pragma unroll
+    for (int k = 0; k < kTop; ++k) id[k] = pi[k];
+    const float mn = fmaxf(m, f[0]);
+    if (mn != -INFINITY) {
+      s = (m == -INFINITY ? 0.f : s * exp2f((m - mn) * kLog2e)) +
+          (f[0] == -INFINITY ? 0.f : f[1] * exp2f((f[0] - mn) * kLog2e));
+      m = mn;
+    }
+#pragma unroll
+    for (int k = 0; k < kTop; ++k) insert_top8(tv, ti, f[2 + k], id[k]);
+  }
+  const float wm = wave_max(m);
+  float ws = (m == -INFINITY) ? 0.f : s * exp2f((m - wm) * kLog2e);
+  ws = wave_sum(ws);
+  float ov[kTop];
+  int oi[kTop];
+  wave_top8(tv, ti, ov, oi);
+  if (lane == 0) {
+    s_m[wave] = wm;
+    s_s[wave] = ws;
+#pragma unroll
+    for (int k = 0; k < kTop; ++k) {
+      s_tv[wave][k] = ov[k];
+      s_ti[wave][k] = oi[k];
+    }
+  }
+  __syncthreads();
+  if (wave != 0) return;
+  float M = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < kThreads / 64; ++w) M = fmaxf(M, s_m[w]);
+  float Z = 0.f;
+#pragma unroll
+  for (int w = 0; w < kThreads / 64; ++w)
+    if (s_m[w] != -INFINITY) Z += s_s[w] * exp2f((s_m[w] - M) * kLog2e);
+  float cv = -INFINITY;
+  int ci = INT_MAX;
+  if (lane < (kThreads / 64) * kTop) {
+    cv = s_tv[lane / kTop][lane % kTop];
+    ci = s_ti[lane / kTop][lane % kTop];
+  }
+#pragma unroll
+  for (int k = 0; k < kTop; ++k) {
+    float v = cv;
+    int id = ci;
+    wave_best(v, id);
+    if (cv == v && ci == id) {
+      cv = -INFINITY;
+      ci = INT_MAX;
+    }
+    if (lane == 0) {
+      topk_id[(size_t)row * kTop + k] = id;
+      topk_p[(size_t)row * kTop + k] = exp2f((v - M) * kLog2e) / Z;
+      if (k == 0) {
+        argmax[row] = id;
+        conf[row] = 1.f / Z;
+        lse[row] = M + logf(Z);
+      }
+    }
+  }
+}
+
 }  // namespace
+
+hipError_t launch_vocab_merge_tiles(int rows, int n_tiles, const float* rec_f, const int* rec_i,
+                                    int* argmax, float* conf, float* lse, int* topk_id,
+                                    float* topk_p, hipStream_t st) {
+  if (rows <= 0) return hipSuccess;
+  if (n_tiles < 1) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(vocab_merge_tiles_kernel, dim3(rows), dim3(kThreads), 0, st, n_tiles, rec_f,
+                     rec_i, argmax, conf, lse, topk_id, topk_p);
+  return hipGetLastError();
+}
+
+size_t vocab_record_bytes(int rows, int n_tiles) {
+  return (size_t)rows * n_tiles * (vocab::kRecF * sizeof(float) + vocab::kTop * sizeof(int));
+}
 
 VocabPlan plan_vocab(int rows, int V, int target_wgs) {
   VocabPlan p{};

@@ -52,7 +52,7 @@ class Engine:
               "shared_gate_up", "shared_down")
 
     def __init__(self, model_cfg, decode_cfg, weights, max_batch, max_len, graph_unroll=0,
-                 stream=None):
+                 stream=None, keep_logits=False):
         self.lib = B.load()
         self.m = model_cfg
         self.d = decode_cfg
@@ -105,6 +105,11 @@ class Engine:
         B.check(st, "dinfer_step_init")
         self.ctx = ctx
         self.batch = 0
+        self.keep_logits(keep_logits)
+
+    def keep_logits(self, on=True):
+        """dinfer_keep_logits: also store the block rows' fp32 logits (inspection)."""
+        B.check(self.lib.dinfer_keep_logits(self.ctx, 1 if on else 0), "dinfer_keep_logits")
 
     # -- calls ---------------------------------------------------------------
     def set_batch(self, tokens, prompt_len, gen_len, plant_id=None, plant_bias=None,
@@ -302,6 +307,8 @@ class Engine:
             "block_done": t(v.block_done, self.batch, torch.int32, (self.batch,)),
             "step_count": t(v.step_count, self.batch, torch.int32, (self.batch,)),
             "commit_count": t(v.commit_count, self.batch, torch.int32, (self.batch,)),
+            "decode_stats": t(v.decode_stats, self.batch * v.decode_stat_words, torch.int32,
+                              (self.batch, v.decode_stat_words)),
             "kv_k": t(v.kv_k, kv_n, kvdt, kv_shape),
             "kv_v": t(v.kv_v, kv_n, kvdt, vt_shape),
         }

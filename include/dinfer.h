@@ -140,7 +140,9 @@ typedef struct {
 typedef struct {
   int32_t batch, block_len, vocab, topk;
   float* logits;             /* [batch*B][V] fp32 logits of the block rows (before
-                                planting bias and MASK exclusion)               */
+                                planting bias and MASK exclusion), written by
+                                denoise_step only while dinfer_keep_logits is
+                                on (the statistics never read them)             */
   int32_t* argmax;           /* [batch*B]                                        */
   float* conf;               /* [batch*B] max softmax probability                */
   float* lse;                /* [batch*B] log-sum-exp                            */
@@ -175,6 +177,14 @@ typedef struct {
   float* ffn_in;
   int32_t kv_len;            /* cache positions per head row: max_len rounded up
                                 to a multiple of 64 (padding holds zeros)        */
+  /* Decode accounting of each request since set_batch (or its refill):
+   * [batch][decode_stat_words] int32 -- [0] commits through the threshold
+   * gate, [1] through the credit gate alone, [2] through the fallback, [3]
+   * steps that found the request's block already done (graph replays past a
+   * block's end), [4 + k] steps that committed k tokens, k = 0..64.
+   * Statistics only: nothing reads them back. */
+  int32_t* decode_stats;
+  int32_t decode_stat_words;
 } dinfer_step_view;
 
 /* Bytes of workspace dinfer_step_init needs for these shapes (0 on bad args). */
@@ -312,6 +322,15 @@ dinfer_status dinfer_sched_round(dinfer_sched* sched, const int32_t* h_decode_ro
 dinfer_status dinfer_run_to_completion(dinfer_ctx* ctx, int32_t max_steps,
                                        dinfer_run_stats* h_stats);
 
+/* Inspection switch (default off): while on, denoise_step also stores the
+ * block rows' fp32 logits into the step view's logits buffer.  The vocab
+ * statistics are computed in the LM head's epilogue either way (per row and
+ * column tile: planting bias, MASK exclusion, max, sum of exp, top-8; then a
+ * merge per row), so the switch changes no result, only the extra store.
+ * Takes effect at the next denoise_step (a captured step graph is dropped
+ * and captured again). */
+dinfer_status dinfer_keep_logits(dinfer_ctx* ctx, int32_t on);
+
 /* Fill *out with device pointers into the context's state. */
 dinfer_status dinfer_get_step_view(const dinfer_ctx* ctx, dinfer_step_view* out);
 
@@ -357,8 +376,9 @@ size_t dinfer_linear_out_elems(int32_t M, int32_t N, int32_t K, int32_t dtype);
 dinfer_status dinfer_linear(const float* d_A, const void* d_W, float* d_out, int32_t M, int32_t N,
                             int32_t K, int32_t dtype, int32_t* h_splits, void* stream);
 
-/* Standalone vocab statistics over fp32 logits d_logits [rows][vocab]
- * (the fused LM-head epilogue of dinfer_denoise_step, exposed on its own):
+/* Standalone vocab statistics over materialised fp32 logits d_logits
+ * [rows][vocab] -- the statistics dinfer_denoise_step computes in its LM
+ * head's epilogue without storing logits, here as a pass of its own:
  * d_plant_id [rows] (-1 none) and d_plant_bias [rows] add the planting bias;
  * mask_id is excluded (-1 = none).  Outputs: d_argmax [rows], d_conf [rows],
  * d_lse [rows], d_topk_id [rows][8], d_topk_p [rows][8].  d_scratch must hold

@@ -34,7 +34,8 @@ def build(wc, graph_unroll=0, weights=None, req=None):
     w = weights if weights is not None else synth.make_weights(wc.model, wc.seed, device="cuda")
     req = req if req is not None else synth.make_requests(wc)
     max_len = req["tokens"].shape[1]
-    eng = Engine(wc.model, wc.decode, w, wc.batch, max_len, graph_unroll=graph_unroll)
+    eng = Engine(wc.model, wc.decode, w, wc.batch, max_len, graph_unroll=graph_unroll,
+                 keep_logits=True)
     tokens = req["tokens"].cuda().contiguous()
     rb = req.get("router_bias")
     eng.set_batch(tokens, req["prompt_len"].tolist(), req["gen_len"].tolist(),

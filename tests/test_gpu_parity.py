@@ -86,9 +86,11 @@ def test_commit_parity_on_synthetic_stats(hier, B_len):
         v["tracked"].copy_(torch.from_numpy(tracked))
         v["topk_id"].copy_(torch.from_numpy(tid))
         v["topk_p"].copy_(torch.from_numpy(tp))
+        ds0 = v["decode_stats"].cpu().numpy().copy()
         eng.commit()
         torch.cuda.synchronize()
         gt = tokens.cpu().numpy()
+        dds = v["decode_stats"].cpu().numpy() - ds0
         for r in range(wc.batch):
             sl = slice(r * B_len, (r + 1) * B_len)
             c2, t2 = credit_update(credit[sl], tracked[sl], am[sl], conf[sl], masked[r],
@@ -114,6 +116,16 @@ def test_commit_parity_on_synthetic_stats(hier, B_len):
             assert np.allclose(gs[still], pt[still], rtol=1e-6)
             done = int(v["block_done"].cpu().numpy()[r])
             assert done == int(not still.any())
+            # accounting: threshold / credit-only / fallback commits, one step
+            # in the histogram bin of its commit count
+            want = np.zeros(dds.shape[1], np.int64)
+            if fb:
+                want[2] = len(T)
+            else:
+                want[0] = int(np.sum(conf[sl][T] >= tau))
+                want[1] = len(T) - want[0]
+            want[4 + len(T)] = 1
+            assert np.array_equal(dds[r], want), (trial, r, dds[r][:8], want[:8])
 
 
 # ----------------------------------------------------- one step and full runs
