@@ -316,6 +316,68 @@ def run_queue_workload(wc, w, n_requests, unroll, budget=None):
             "max_round_ms": round(1e3 * rnd[-1], 2)}
 
 
+def run_expert_sweep(wc, w, slot_list, intervals, blocks, unroll):
+    """TIDE-style expert cache on the MoE workload: the first `blocks` blocks
+    of its request with `slots` experts per layer in HBM and the rest read
+    from a pinned host store, for each (slots, interval); beside the run with
+    every expert in HBM.  Reports tokens/s, hit rates, bytes moved, and
+    whether the tokens equal the all-in-HBM run's (they must: the cache is
+    lossless)."""
+    import torch
+    import synth
+    from diffusion_vicinity_kv_amd.engine import Engine
+    wcs = wc.with_(gen_len=blocks * wc.decode.block_len)
+    req = synth.make_requests(wcs)
+    max_len = req["tokens"].shape[1]
+    P, G = req["prompt_len"].tolist(), req["gen_len"].tolist()
+    out = []
+
+    def one(slots, interval):
+        eng = Engine(wcs.model, wcs.decode, w, wcs.batch, max_len, graph_unroll=unroll)
+        if slots is not None:
+            eng.expert_offload(slots, interval)
+        tokens = req["tokens"].cuda().contiguous()
+        args = (P, G, req["plant_id"].cuda().contiguous(), req["plant_bias"].cuda().contiguous(),
+                req["router_bias"].cuda().contiguous())
+        eng.set_batch(tokens, *args)                 # warm-up (graph capture)
+        eng.run_to_completion()
+        if slots is not None:
+            eng.expert_report(reset=True)
+        tokens.copy_(req["tokens"].cuda())
+        eng.set_batch(tokens, *args)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        st = eng.run_to_completion()
+        torch.cuda.synchronize()
+        el = time.perf_counter() - t0
+        rep = eng.expert_report() if slots is not None else None
+        toks = tokens.clone()
+        eng.close()
+        del eng
+        torch.cuda.empty_cache()
+        return el, st, rep, toks
+
+    el0, st0, _, tok0 = one(None, 0)
+    out.append({"slots": wc.model.n_experts, "interval": None, "store": "all experts in HBM",
+                "value": round(st0["committed"] / el0, 3), "unit": "tokens/s",
+                "steps": st0["steps"], "refreshes": st0["refreshes"]})
+    log(f"[bench] expert sweep: all in HBM {out[-1]}")
+    for slots in slot_list:
+        for interval in intervals:
+            el, st, rep, toks = one(slots, interval)
+            rows = rep["row_hits"] + rep["row_misses"]
+            ex = rep["expert_hits"] + rep["expert_misses"]
+            out.append({"slots": slots, "interval": interval, "value": round(st["committed"] / el, 3),
+                        "unit": "tokens/s", "steps": st["steps"], "refreshes": st["refreshes"],
+                        "row_hit_rate": round(rep["row_hits"] / max(rows, 1), 4),
+                        "expert_hit_rate": round(rep["expert_hits"] / max(ex, 1), 4),
+                        "placements": rep["placements"], "bytes_placed": rep["bytes_placed"],
+                        "bytes_host_read": rep["bytes_host_read"],
+                        "tokens_equal_all_in_hbm": bool(torch.equal(toks, tok0))})
+            log(f"[bench] expert sweep: {out[-1]}")
+    return {"workload": wc.name, "blocks": blocks, "gen_len": wcs.gen_len, "points": out}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -338,6 +400,14 @@ def main():
     ap.add_argument("--supplementary-long", action="store_true",
                     help="also run the long-context workload (batch 4, 8K prompt, hierarchical) "
                          "under calibrated planting (about a minute)")
+    ap.add_argument("--expert-sweep", default="",
+                    help="MoE workload: comma-separated expert slots per layer for the HBM "
+                         "expert cache over a pinned host store (TIDE-style placement)")
+    ap.add_argument("--expert-interval", default="0",
+                    help="with --expert-sweep: comma-separated placement intervals in steps "
+                         "(0: block starts only)")
+    ap.add_argument("--expert-blocks", type=int, default=2,
+                    help="with --expert-sweep: blocks of the request to run")
     ap.add_argument("--kernel-only", action="store_true",
                     help="only the dominant-kernel timing loop (for counter runs)")
     ap.add_argument("--calib-copy", action="store_true",
@@ -377,6 +447,16 @@ def main():
     if args.kernel_only:
         avg_ms, avg_bytes, _, rows = dominant_kernel_timing(wc, w, iters=64)
         log(f"[bench] kernel-only: {avg_ms * 1e3:.1f} us/launch, {avg_bytes / avg_ms / 1e6:.0f} GB/s")
+        return
+
+    if args.expert_sweep:
+        if not m.is_moe:
+            print("bench.py: --expert-sweep needs an MoE workload", file=sys.stderr)
+            sys.exit(2)
+        sweep = run_expert_sweep(wc, w, [int(x) for x in args.expert_sweep.split(",")],
+                                 [int(x) for x in args.expert_interval.split(",")],
+                                 args.expert_blocks, args.unroll)
+        print(json.dumps({"expert_cache_sweep": sweep}), flush=True)
         return
 
     res = run_workload(wc, w, req, args.unroll, args.warmup, args.steps)

@@ -21,7 +21,8 @@ EXPORTS = [
     "dinfer_step_graph", "dinfer_pack_linear", "dinfer_linear_out_elems", "dinfer_linear",
     "dinfer_status_str", "dinfer_last_error", "dinfer_destroy", "dinfer_refill", "dinfer_finished",
     "dinfer_pending_rows", "dinfer_sched_create", "dinfer_sched_destroy", "dinfer_sched_round",
-    "dinfer_vocab_stats_noalloc", "dinfer_keep_logits",
+    "dinfer_vocab_stats_noalloc", "dinfer_keep_logits", "dinfer_expert_slot_bytes",
+    "dinfer_expert_offload", "dinfer_expert_place", "dinfer_expert_cache_report",
 ]
 
 
@@ -66,6 +67,12 @@ class StepView(C.Structure):
         ("kv_len", C.c_int32), ("decode_stats", C.c_void_p), ("decode_stat_words", C.c_int32)]
 
 
+class ExpertCacheStats(C.Structure):
+    _fields_ = [(n, C.c_int64) for n in ("expert_hits", "expert_misses", "row_hits", "row_misses",
+                                          "bytes_placed", "bytes_host_read", "placements")] + [
+        ("slots", C.c_int32), ("interval", C.c_int32)]
+
+
 class DinferError(RuntimeError):
     def __init__(self, status, what, detail):
         super().__init__(f"{what}: {status_name(status)}: {detail}")
@@ -97,6 +104,10 @@ def load(path: str = LIB_PATH) -> C.CDLL:
         "dinfer_run_to_completion": (i32, [vp, i32, C.POINTER(RunStats)]),
         "dinfer_get_step_view": (i32, [vp, C.POINTER(StepView)]),
         "dinfer_keep_logits": (i32, [vp, i32]),
+        "dinfer_expert_slot_bytes": (sz, [C.POINTER(ModelCfg)]),
+        "dinfer_expert_offload": (i32, [vp, C.POINTER(vp), C.POINTER(vp), i32, i32, vp, sz]),
+        "dinfer_expert_place": (i32, [vp]),
+        "dinfer_expert_cache_report": (i32, [vp, C.POINTER(ExpertCacheStats), i32]),
         "dinfer_vocab_stats_scratch_bytes": (sz, [i32, i32]),
         "dinfer_vocab_stats": (i32, [vp, i32, i32, vp, vp, i32, vp, vp, vp, vp, vp, vp, sz, vp]),
         "dinfer_vocab_stats_noalloc": (i32, [vp, i32, i32, vp, vp, i32, vp, vp, vp, vp, vp, vp]),

@@ -297,7 +297,9 @@ __global__ __launch_bounds__(NW * 64) void gemm_skinny_lmhead_kernel(
 // Grouped projection of the MoE experts: workgroup (expert e, column group,
 // 64-row tile) multiplies rows [off_e + 64 t, min(off_e + count_e, +64)) of
 // the packed assignment list -- gathered from A through row_of[] when given,
-// else read in place -- with expert e's weights W + e*N*K.  The row tiles of
+// else read in place -- with expert e's weights Wtab[e] (one packed [N][K]
+// matrix: in HBM, or in pinned host memory the kernel reads directly when an
+// expert cache holds only some experts in HBM).  The row tiles of
 // one (expert, column group) get workgroup ids 8 apart: workgroups are dealt
 // to the eight XCDs in id order, so they run side by side on one XCD and
 // the second reads the weights the first brings into that XCD's L2 (an
@@ -305,8 +307,8 @@ __global__ __launch_bounds__(NW * 64) void gemm_skinny_lmhead_kernel(
 template <typename TW, int NT, int NW>
 __global__ __launch_bounds__(NW * 64) void gemm_grouped_kernel(
     const float* __restrict__ A, const int* __restrict__ row_of, const int* __restrict__ e_count,
-    const int* __restrict__ e_off, const TW* __restrict__ W, float* __restrict__ out, int N, int K,
-    int n_tiles, int m_tiles, int n_pairs) {
+    const int* __restrict__ e_off, const TW* const* __restrict__ Wtab, float* __restrict__ out,
+    int N, int K, int n_tiles, int m_tiles, int n_pairs) {
   constexpr int KC = 4 * Mfma<TW>::KSTEP;
   const int bid = blockIdx.x;
   const int grp = bid / (8 * m_tiles);
@@ -322,7 +324,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_grouped_kernel(
   const int base = e_off[e] + mt * 64;
   const float* a = row_of ? A : A + (size_t)base * K;
   const int* ar = row_of ? row_of + base : nullptr;
-  skinny_tile<TW, 4, NT, NW, true>(a, ar, M, W + (size_t)e * N * K, N, K, out + (size_t)base * N, N,
+  skinny_tile<TW, 4, NT, NW, true>(a, ar, M, Wtab[e], N, K, out + (size_t)base * N, N,
                                    tile * (16 * NT * NW), 0, K / KC);
 }
 
@@ -461,8 +463,8 @@ hipError_t dispatch(const GemmPlan& p, const float* A, const void* W, float* out
 int gemm_k_chunk(DType t) { return t == DType::F32 ? 64 : 128; }
 
 hipError_t launch_gemm_grouped(DType t, const float* A, const int* row_of, const int* e_count,
-                               const int* e_off, int E, int max_rows, const void* W, float* out,
-                               int N, int K, hipStream_t st) {
+                               const int* e_off, int E, int max_rows, const void* const* Wtab,
+                               float* out, int N, int K, hipStream_t st) {
   if (N % 128 != 0 || K % gemm_k_chunk(t) != 0) return hipErrorInvalidValue;
   const int m_tiles = (max_rows + 63) / 64;
   // bf16 with 256-column groups: eight waves x 32 columns (two waves per
@@ -474,15 +476,15 @@ hipError_t launch_gemm_grouped(DType t, const float* A, const int* row_of, const
   const dim3 grid((n_pairs + 7) / 8 * 8 * m_tiles);
   if (t == DType::F32)
     hipLaunchKernelGGL((gemm_grouped_kernel<float, 2, 4>), grid, dim3(256), 0, st, A, row_of,
-                       e_count, e_off, static_cast<const float*>(W), out, N, K, n_tiles, m_tiles,
+                       e_count, e_off, reinterpret_cast<const float* const*>(Wtab), out, N, K, n_tiles, m_tiles,
                        n_pairs);
   else if (wide)
     hipLaunchKernelGGL((gemm_grouped_kernel<bf16, 2, 8>), grid, dim3(512), 0, st, A, row_of,
-                       e_count, e_off, static_cast<const bf16*>(W), out, N, K, n_tiles, m_tiles,
+                       e_count, e_off, reinterpret_cast<const bf16* const*>(Wtab), out, N, K, n_tiles, m_tiles,
                        n_pairs);
   else
     hipLaunchKernelGGL((gemm_grouped_kernel<bf16, 2, 4>), grid, dim3(256), 0, st, A, row_of,
-                       e_count, e_off, static_cast<const bf16*>(W), out, N, K, n_tiles, m_tiles,
+                       e_count, e_off, reinterpret_cast<const bf16* const*>(Wtab), out, N, K, n_tiles, m_tiles,
                        n_pairs);
   return hipGetLastError();
 }

@@ -54,11 +54,12 @@ hipError_t launch_pack_linear(DType t, const void* W, void* P, int n_mats, int N
                               hipStream_t st);
 bool gemm_shape_ok(DType t, int N, int K);
 int gemm_k_chunk(DType t);
-// MoE experts: out[off_e + i] = A[row_of ? row_of[off_e + i] : off_e + i] * W[e]^T for
-// i < e_count[e]; W holds E experts of [N][K]; max_rows bounds any e_count.
+// MoE experts: out[off_e + i] = A[row_of ? row_of[off_e + i] : off_e + i] * W_e^T for
+// i < e_count[e]; Wtab [E] (device array) points at each expert's packed
+// [N][K] matrix; max_rows bounds any e_count.
 hipError_t launch_gemm_grouped(DType t, const float* A, const int* row_of, const int* e_count,
-                               const int* e_off, int E, int max_rows, const void* W, float* out,
-                               int N, int K, hipStream_t st);
+                               const int* e_off, int E, int max_rows, const void* const* Wtab,
+                               float* out, int N, int K, hipStream_t st);
 
 // ---- row-wise kernels ------------------------------------------------------
 hipError_t launch_embed(DType t, PassTable tb, int m_cap, const int* tokens, int max_len,
@@ -140,6 +141,13 @@ hipError_t launch_moe_route(DType t, PassTable tb, int m_cap, const float* f, in
 hipError_t launch_moe_plan(const int* nrows, int m_cap, const int* sel, int E, int top_k,
                            int* e_count, int* e_off, int* row_of, int* pos, int* n_assign,
                            hipStream_t st);
+// Expert-cache accounting of one routed layer: per expert, its assignment
+// count is added to counts[e] (usage since the last placement); the
+// experts with rows and their rows are split into hits (resident[e] != 0)
+// and misses, added to acct[0..3] = expert hits, expert misses, row hits,
+// row misses (int64).
+hipError_t launch_expert_usage(const int* e_count, int E, const int* resident, int* counts,
+                               long long* acct, hipStream_t st);
 hipError_t launch_moe_combine(const int* nrows, int m_cap, float* x, const float* P, int S,
                               size_t p_stride, const float* Y, const int* pos, const float* gate,
                               int top_k, int d, hipStream_t st);

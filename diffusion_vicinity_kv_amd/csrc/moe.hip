@@ -325,7 +325,41 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(
   reinterpret_cast<float4*>(x + (size_t)m * d)[i] = a;
 }
 
+// One wave: lane e takes expert e (E <= 64).
+__global__ __launch_bounds__(64) void expert_usage_kernel(const int* __restrict__ e_count, int E,
+                                                          const int* __restrict__ resident,
+                                                          int* __restrict__ counts,
+                                                          long long* __restrict__ acct) {
+  const int e = threadIdx.x;
+  const int c = e < E ? e_count[e] : 0;
+  const bool res = e < E && resident[e] != 0;
+  if (e < E) counts[e] += c;
+  const unsigned long long used = __ballot(c > 0);
+  const unsigned long long hit = __ballot(c > 0 && res);
+  int rh = (c > 0 && res) ? c : 0;
+  int rm = (c > 0 && !res) ? c : 0;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    rh += __shfl_xor(rh, o, 64);
+    rm += __shfl_xor(rm, o, 64);
+  }
+  if (e == 0) {
+    acct[0] += __popcll(hit);
+    acct[1] += __popcll(used & ~hit);
+    acct[2] += rh;
+    acct[3] += rm;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_expert_usage(const int* e_count, int E, const int* resident, int* counts,
+                               long long* acct, hipStream_t st) {
+  if (E < 1 || E > kMaxE) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(expert_usage_kernel, dim3(1), dim3(64), 0, st, e_count, E, resident, counts,
+                     acct);
+  return hipGetLastError();
+}
 
 hipError_t launch_moe_route(DType t, PassTable tb, int m_cap, const float* f, int d,
                             const void* Wr, int E, int top_k, const float* router_bias,

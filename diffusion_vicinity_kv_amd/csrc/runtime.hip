@@ -78,6 +78,7 @@ struct Layout {
       off_tid, off_tp, off_credit, off_tracked, off_sid, off_sp, off_sv, off_cm, off_done,
       off_steps, off_ccount, off_dstat, off_tab_step, off_tab_ref, off_mask, off_misc, off_sel, off_gate,
       off_pos, off_rowof, off_ecount, off_eoff, off_nassign, off_egu, off_eact, off_ey, off_rlog,
+      off_wtab, off_resident, off_eusage, off_eacct,
       total;
   size_t kv_layer_elems;        // elements of one layer's K (or V) cache
   int tab_ints_step, tab_ints_ref;
@@ -245,6 +246,13 @@ bool make_layout(const dinfer_model_cfg* m, const dinfer_decode_cfg* dc, int max
   l.off_eact = take(ac * Fe * 4);
   l.off_ey = take(ac * d * 4);
   l.off_rlog = take((size_t)(moe ? l.m_all * l.E : 0) * 4);
+  // MoE expert pointer tables [layer][gate|up, down][E], residency flags,
+  // usage counts since the last placement [layer][E], accounting [layer][4]
+  const size_t ne = moe ? (size_t)l.nl * l.E : 0;
+  l.off_wtab = take(ne * 2 * sizeof(void*));
+  l.off_resident = take(ne * 4);
+  l.off_eusage = take(ne * 4);
+  l.off_eacct = take((moe ? (size_t)l.nl : 0) * 4 * 8);
   l.total = o;
   return true;
 }
@@ -297,6 +305,18 @@ struct dinfer_ctx {
   int* h_tab_step = nullptr;
   int* h_tab_ref = nullptr;
   int* h_misc = nullptr;
+  // MoE expert tables (host staging, pinned) and the expert cache
+  const void** h_wtab = nullptr;      // [layer][2][E]
+  int* h_resident = nullptr;          // [layer][E]
+  bool experts_ready = false;         // every table entry points at weights
+  bool offload = false;
+  int slots = 0, interval = 0;
+  char* d_slots = nullptr;
+  std::vector<const char*> h_gu, h_dn;       // host store, host addresses
+  std::vector<const char*> hd_gu, hd_dn;     // the same, device-accessible
+  std::vector<std::vector<int>> slot_expert; // [layer][slot] -> expert
+  long long bytes_h2d = 0, placements = 0;
+  int steps_since_place = 0;
   hipEvent_t ev_step_upload = nullptr, ev_ref_upload = nullptr;
   bool step_dirty = true;
   int state = 0;                  // 0 init, 1 batch bound
@@ -429,10 +449,14 @@ dinfer_status run_pass(dinfer_ctx* c, bool step) {
     HIP_TRY(launch_moe_route(dt, tb, m_cap, a, d, c->router[l], E, K8, c->router_bias, L.nl,
                              c->n_bias_blocks, l, sel, gate, c->at<float>(L.off_rlog), st));
     HIP_TRY(launch_moe_plan(tb.nrows, m_cap, sel, E, K8, e_count, e_off, row_of, pos, n_assign, st));
-    HIP_TRY(launch_gemm_grouped(dt, a, row_of, e_count, e_off, E, m_cap, c->egu[l], egu, 2 * Fe, d,
-                                st));
+    const void* const* wt = c->at<const void*>(L.off_wtab) + (size_t)l * 2 * E;
+    if (c->offload)
+      HIP_TRY(launch_expert_usage(e_count, E, c->at<int>(L.off_resident) + (size_t)l * E,
+                                  c->at<int>(L.off_eusage) + (size_t)l * E,
+                                  c->at<long long>(L.off_eacct) + (size_t)l * 4, st));
+    HIP_TRY(launch_gemm_grouped(dt, a, row_of, e_count, e_off, E, m_cap, wt, egu, 2 * Fe, d, st));
     HIP_TRY(launch_swiglu(n_assign, m_cap * K8, egu, 1, 0, Fe, eact, st));
-    HIP_TRY(launch_gemm_grouped(dt, eact, nullptr, e_count, e_off, E, m_cap, c->ed[l], ey, d, Fe,
+    HIP_TRY(launch_gemm_grouped(dt, eact, nullptr, e_count, e_off, E, m_cap, wt + E, ey, d, Fe,
                                 st));
     HIP_TRY(launch_gemm(gg, dt, a, c->sgu[l], part, tb.nrows, m_cap, 2 * F, d, st));
     HIP_TRY(launch_swiglu(tb.nrows, m_cap, part, gg.splits, stride_g, F, act, st));
@@ -513,6 +537,87 @@ int active_count(const dinfer_ctx* c) {
   return n;
 }
 
+size_t expert_gu_bytes(const Layout& L) { return (size_t)2 * L.Fe * L.d * dtype_size(L.dt); }
+size_t expert_dn_bytes(const Layout& L) { return (size_t)L.d * L.Fe * dtype_size(L.dt); }
+
+// Expert e of layer l into HBM slot s (host store -> slot copy on the
+// context's stream, after every kernel enqueued before it), and the host
+// staging of its table entries and residency.
+dinfer_status move_expert_in(dinfer_ctx* c, int l, int e, int s) {
+  const Layout& L = c->L;
+  const size_t gu = expert_gu_bytes(L), dn = expert_dn_bytes(L);
+  char* dst = c->d_slots + ((size_t)l * c->slots + s) * (gu + dn);
+  HIP_TRY(hipMemcpyAsync(dst, c->h_gu[l] + e * gu, gu, hipMemcpyHostToDevice, c->stream));
+  HIP_TRY(hipMemcpyAsync(dst + gu, c->h_dn[l] + e * dn, dn, hipMemcpyHostToDevice, c->stream));
+  c->h_wtab[((size_t)l * 2 + 0) * L.E + e] = dst;
+  c->h_wtab[((size_t)l * 2 + 1) * L.E + e] = dst + gu;
+  c->h_resident[(size_t)l * L.E + e] = 1;
+  c->slot_expert[l][s] = e;
+  c->bytes_h2d += (long long)(gu + dn);
+  return DINFER_OK;
+}
+
+// Expert e of layer l back to its host-store address (read by the kernels
+// from pinned host memory).
+void move_expert_out(dinfer_ctx* c, int l, int e) {
+  const Layout& L = c->L;
+  const size_t gu = expert_gu_bytes(L), dn = expert_dn_bytes(L);
+  c->h_wtab[((size_t)l * 2 + 0) * L.E + e] = c->hd_gu[l] + e * gu;
+  c->h_wtab[((size_t)l * 2 + 1) * L.E + e] = c->hd_dn[l] + e * dn;
+  c->h_resident[(size_t)l * L.E + e] = 0;
+}
+
+dinfer_status upload_expert_tables(dinfer_ctx* c) {
+  const Layout& L = c->L;
+  const size_t ne = (size_t)L.nl * L.E;
+  HIP_TRY(hipMemcpyAsync(c->at<char>(L.off_wtab), c->h_wtab, ne * 2 * sizeof(void*),
+                         hipMemcpyHostToDevice, c->stream));
+  HIP_TRY(hipMemcpyAsync(c->at<char>(L.off_resident), c->h_resident, ne * 4,
+                         hipMemcpyHostToDevice, c->stream));
+  HIP_TRY(hipMemsetAsync(c->at<char>(L.off_eusage), 0, ne * 4, c->stream));
+  return DINFER_OK;
+}
+
+// Interval placement (TIDE abstract: expert activations are stable within a
+// block, so the placement is refreshed per interval): per layer, the `slots`
+// experts with the most row assignments since the last placement become
+// resident (ties: the resident one, then the lower id); only the experts that
+// change are copied, each into the slot of an expert that leaves.
+dinfer_status place_experts(dinfer_ctx* c) {
+  const Layout& L = c->L;
+  const int E = L.E, C = c->slots;
+  std::vector<int> cnt((size_t)L.nl * E);
+  HIP_TRY(hipMemcpyAsync(cnt.data(), c->at<int>(L.off_eusage), cnt.size() * 4,
+                         hipMemcpyDeviceToHost, c->stream));
+  HIP_TRY(hipStreamSynchronize(c->stream));   // also: the last table upload has been read
+  for (int l = 0; l < L.nl; ++l) {
+    const int* u = cnt.data() + (size_t)l * E;
+    const int* res = c->h_resident + (size_t)l * E;
+    std::vector<int> order(E);
+    for (int e = 0; e < E; ++e) order[e] = e;
+    std::stable_sort(order.begin(), order.end(), [&](int a, int b) {
+      if (u[a] != u[b]) return u[a] > u[b];
+      return res[a] > res[b];
+    });
+    std::vector<uint8_t> want(E, 0);
+    for (int i = 0; i < C; ++i) want[order[i]] = 1;
+    std::vector<int> in;
+    for (int e = 0; e < E; ++e)
+      if (want[e] && !res[e]) in.push_back(e);
+    size_t k = 0;
+    for (int s = 0; s < C && k < in.size(); ++s) {
+      const int out = c->slot_expert[l][s];
+      if (want[out]) continue;
+      move_expert_out(c, l, out);
+      dinfer_status st = move_expert_in(c, l, in[k++], s);
+      if (st != DINFER_OK) return st;
+    }
+  }
+  c->placements += 1;
+  c->steps_since_place = 0;
+  return upload_expert_tables(c);
+}
+
 }  // namespace
 
 // ----------------------------------------------------------------------------
@@ -556,14 +661,18 @@ dinfer_status dinfer_step_init(const dinfer_model_cfg* m, const dinfer_decode_cf
   if (!w || !w->tok_emb || !w->final_norm || !w->lm_head || !w->attn_norm || !w->wqkv || !w->wo ||
       !w->ffn_norm)
     return fail(DINFER_E_ARG, "missing weight pointers");
-  if (L.moe ? (!w->router || !w->exp_gate_up || !w->exp_down || !w->shared_gate_up || !w->shared_down)
+  // MoE experts may be left out (both arrays NULL) when an expert cache will
+  // hold them (dinfer_expert_offload)
+  const bool have_experts = L.moe && w->exp_gate_up && w->exp_down;
+  if (L.moe ? (!w->router || !w->shared_gate_up || !w->shared_down ||
+               (!w->exp_gate_up != !w->exp_down))
             : (!w->w_gate_up || !w->w_down))
     return fail(DINFER_E_ARG, "missing FFN weight pointers");
   for (int l = 0; l < m->n_layers; ++l) {
     bool ok = w->attn_norm[l] && w->wqkv[l] && w->wo[l] && w->ffn_norm[l];
     if (L.moe)
-      ok = ok && w->router[l] && w->exp_gate_up[l] && w->exp_down[l] && w->shared_gate_up[l] &&
-           w->shared_down[l];
+      ok = ok && w->router[l] && w->shared_gate_up[l] && w->shared_down[l] &&
+           (!have_experts || (w->exp_gate_up[l] && w->exp_down[l]));
     else
       ok = ok && w->w_gate_up[l] && w->w_down[l];
     if (!ok) return fail(DINFER_E_ARG, "missing per-layer weight pointer at layer " + std::to_string(l));
@@ -591,8 +700,10 @@ dinfer_status dinfer_step_init(const dinfer_model_cfg* m, const dinfer_decode_cf
   c->ffn_norm.assign(w->ffn_norm, w->ffn_norm + m->n_layers);
   if (L.moe) {
     c->router.assign(w->router, w->router + m->n_layers);
-    c->egu.assign(w->exp_gate_up, w->exp_gate_up + m->n_layers);
-    c->ed.assign(w->exp_down, w->exp_down + m->n_layers);
+    if (have_experts) {
+      c->egu.assign(w->exp_gate_up, w->exp_gate_up + m->n_layers);
+      c->ed.assign(w->exp_down, w->exp_down + m->n_layers);
+    }
     c->sgu.assign(w->shared_gate_up, w->shared_gate_up + m->n_layers);
     c->sd.assign(w->shared_down, w->shared_down + m->n_layers);
   } else {
@@ -614,6 +725,34 @@ dinfer_status dinfer_step_init(const dinfer_model_cfg* m, const dinfer_decode_cf
     return cleanup(fail(DINFER_E_HIP, "event creation failed"));
   std::memset(c->h_tab_step, 0, (size_t)L.tab_ints_step * 4);
   std::memset(c->h_tab_ref, 0, (size_t)L.tab_ints_ref * 4);
+  if (L.moe) {
+    const size_t ne = (size_t)L.nl * L.E;
+    if (hipHostMalloc(&c->h_wtab, ne * 2 * sizeof(void*)) != hipSuccess ||
+        hipHostMalloc(&c->h_resident, ne * 4) != hipSuccess)
+      return cleanup(fail(DINFER_E_HIP, "pinned host staging allocation failed"));
+    std::memset(c->h_wtab, 0, ne * 2 * sizeof(void*));
+    for (size_t i = 0; i < ne; ++i) c->h_resident[i] = 1;
+    if (have_experts) {
+      // every expert in HBM: expert e of a layer at base + e * (its matrix bytes)
+      const size_t es = dtype_size(L.dt);
+      const size_t gu = (size_t)2 * L.Fe * L.d * es, dn = (size_t)L.d * L.Fe * es;
+      for (int l = 0; l < L.nl; ++l)
+        for (int e = 0; e < L.E; ++e) {
+          c->h_wtab[((size_t)l * 2 + 0) * L.E + e] = static_cast<const char*>(c->egu[l]) + e * gu;
+          c->h_wtab[((size_t)l * 2 + 1) * L.E + e] = static_cast<const char*>(c->ed[l]) + e * dn;
+        }
+      c->experts_ready = true;
+    }
+    if (hipMemcpyAsync(c->at<char>(L.off_wtab), c->h_wtab, ne * 2 * sizeof(void*),
+                       hipMemcpyHostToDevice, c->stream) != hipSuccess ||
+        hipMemcpyAsync(c->at<char>(L.off_resident), c->h_resident, ne * 4, hipMemcpyHostToDevice,
+                       c->stream) != hipSuccess ||
+        hipMemsetAsync(c->at<char>(L.off_eusage), 0, ne * 4, c->stream) != hipSuccess ||
+        hipMemsetAsync(c->at<char>(L.off_eacct), 0, (size_t)L.nl * 4 * 8, c->stream) != hipSuccess)
+      return cleanup(fail(DINFER_E_HIP, "expert table upload failed"));
+  } else {
+    c->experts_ready = true;
+  }
 
   // RoPE table [pos][cos(0..hd/2) | sin(0..hd/2)], angles in fp64.
   std::vector<float> cs((size_t)max_len * L.hd);
@@ -833,6 +972,8 @@ dinfer_status dinfer_sched_round(dinfer_sched* s, const int32_t* h_decode_rows,
 dinfer_status dinfer_refresh_kv(dinfer_ctx* c, const uint8_t* h_req_mask) {
   if (!c) return fail(DINFER_E_ARG, "ctx is null");
   if (c->state < 1) return fail(DINFER_E_STATE, "refresh_kv before set_batch");
+  if (!c->experts_ready)
+    return fail(DINFER_E_STATE, "no expert weights: give them at init or call dinfer_expert_offload");
   const Layout& L = c->L;
   HIP_TRY(hipEventSynchronize(c->ev_ref_upload));
   int* t = c->h_tab_ref;
@@ -1033,7 +1174,9 @@ dinfer_status dinfer_run_to_completion(dinfer_ctx* c, int32_t max_steps, dinfer_
     HIP_TRY(hipEventElapsedTime(&ms, c->ev0, c->ev1));
     refresh_ms += ms;
     stats.refreshes += n;
-    return DINFER_OK;
+    // expert cache: a block start re-places the experts from the routing of
+    // the refresh just run (and of the steps since the last placement)
+    return c->offload ? place_experts(c) : DINFER_OK;
   };
   dinfer_status s = refresh(nullptr);
   if (s != DINFER_OK) return s;
@@ -1057,6 +1200,13 @@ dinfer_status dinfer_run_to_completion(dinfer_ctx* c, int32_t max_steps, dinfer_
       if (s != DINFER_OK) return s;
       stats.steps += 1;
     }
+    if (c->offload && c->interval > 0) {
+      c->steps_since_place += U > 0 ? U : 1;
+      if (c->steps_since_place >= c->interval) {
+        s = place_experts(c);
+        if (s != DINFER_OK) return s;
+      }
+    }
     s = dinfer_advance_blocks(c, need.data(), nullptr);
     if (s != DINFER_OK) return s;
     s = refresh(need.data());
@@ -1070,6 +1220,114 @@ dinfer_status dinfer_run_to_completion(dinfer_ctx* c, int32_t max_steps, dinfer_
   stats.wall_ms = std::chrono::duration<double, std::milli>(std::chrono::steady_clock::now() - t0).count();
   stats.refresh_ms = refresh_ms;
   if (h_stats) *h_stats = stats;
+  return DINFER_OK;
+}
+
+size_t dinfer_expert_slot_bytes(const dinfer_model_cfg* m) {
+  if (!m || m->n_experts < 1 || m->expert_ffn < 1 || m->d_model < 1) return 0;
+  if (m->dtype != DINFER_F32 && m->dtype != DINFER_BF16) return 0;
+  return (size_t)3 * m->expert_ffn * m->d_model * (m->dtype == DINFER_F32 ? 4 : 2);
+}
+
+dinfer_status dinfer_expert_offload(dinfer_ctx* c, const void* const* h_exp_gate_up,
+                                    const void* const* h_exp_down, int32_t slots,
+                                    int32_t interval, void* d_slots, size_t slots_bytes) {
+  if (!c) return fail(DINFER_E_ARG, "ctx is null");
+  const Layout& L = c->L;
+  if (!L.moe) return fail(DINFER_E_ARG, "expert offload needs an MoE model");
+  if (c->offload) return fail(DINFER_E_STATE, "the expert cache is already configured");
+  if (slots < 1 || slots > L.E) return fail(DINFER_E_ARG, "slots must be in 1..n_experts");
+  if (interval < 0) return fail(DINFER_E_ARG, "interval must be >= 0");
+  if (!h_exp_gate_up || !h_exp_down) return fail(DINFER_E_ARG, "null expert store");
+  const size_t one = expert_gu_bytes(L) + expert_dn_bytes(L);
+  if (!d_slots) return fail(DINFER_E_WORKSPACE, "slot buffer is null");
+  if (reinterpret_cast<uintptr_t>(d_slots) % kAlign != 0)
+    return fail(DINFER_E_WORKSPACE, "slot buffer must be 256-byte aligned");
+  if (slots_bytes < (size_t)L.nl * slots * one)
+    return fail(DINFER_E_WORKSPACE, "slot buffer too small: need " +
+                                        std::to_string((size_t)L.nl * slots * one) + " bytes");
+  std::vector<const char*> gu(L.nl), dn(L.nl), dgu(L.nl), ddn(L.nl);
+  for (int l = 0; l < L.nl; ++l) {
+    if (!h_exp_gate_up[l] || !h_exp_down[l]) return fail(DINFER_E_ARG, "null expert store entry");
+    void* a = nullptr;
+    void* b = nullptr;
+    if (hipHostGetDevicePointer(&a, const_cast<void*>(h_exp_gate_up[l]), 0) != hipSuccess ||
+        hipHostGetDevicePointer(&b, const_cast<void*>(h_exp_down[l]), 0) != hipSuccess || !a || !b) {
+      (void)hipGetLastError();
+      return fail(DINFER_E_ARG, "the expert store must be pinned host memory (hipHostMalloc)");
+    }
+    gu[l] = static_cast<const char*>(h_exp_gate_up[l]);
+    dn[l] = static_cast<const char*>(h_exp_down[l]);
+    dgu[l] = static_cast<const char*>(a);
+    ddn[l] = static_cast<const char*>(b);
+  }
+  HIP_TRY(hipStreamSynchronize(c->stream));
+  c->h_gu = gu;
+  c->h_dn = dn;
+  c->hd_gu = dgu;
+  c->hd_dn = ddn;
+  c->d_slots = static_cast<char*>(d_slots);
+  c->slots = slots;
+  c->interval = interval;
+  c->slot_expert.assign(L.nl, std::vector<int>(slots, -1));
+  // start with experts 0..slots-1 of every layer in HBM, the rest in the store
+  for (int l = 0; l < L.nl; ++l)
+    for (int e = 0; e < L.E; ++e) {
+      if (e < slots) {
+        dinfer_status st = move_expert_in(c, l, e, e);
+        if (st != DINFER_OK) return st;
+      } else {
+        move_expert_out(c, l, e);
+      }
+    }
+  dinfer_status st = upload_expert_tables(c);
+  if (st != DINFER_OK) return st;
+  HIP_TRY(hipMemsetAsync(c->at<char>(L.off_eacct), 0, (size_t)L.nl * 4 * 8, c->stream));
+  HIP_TRY(hipStreamSynchronize(c->stream));
+  c->offload = true;
+  c->experts_ready = true;
+  c->steps_since_place = 0;
+  if (c->graph) {   // the step now also records expert usage
+    (void)hipGraphExecDestroy(c->graph);
+    c->graph = nullptr;
+    c->graph_steps = 0;
+  }
+  return DINFER_OK;
+}
+
+dinfer_status dinfer_expert_place(dinfer_ctx* c) {
+  if (!c) return fail(DINFER_E_ARG, "ctx is null");
+  if (!c->offload) return fail(DINFER_E_STATE, "no expert cache (dinfer_expert_offload)");
+  return place_experts(c);
+}
+
+dinfer_status dinfer_expert_cache_report(dinfer_ctx* c, dinfer_expert_cache_stats* out,
+                                         int32_t reset) {
+  if (!c || !out) return fail(DINFER_E_ARG, "null argument");
+  if (!c->offload) return fail(DINFER_E_STATE, "no expert cache (dinfer_expert_offload)");
+  const Layout& L = c->L;
+  std::vector<long long> a((size_t)L.nl * 4);
+  HIP_TRY(hipMemcpyAsync(a.data(), c->at<long long>(L.off_eacct), a.size() * 8,
+                         hipMemcpyDeviceToHost, c->stream));
+  HIP_TRY(hipStreamSynchronize(c->stream));
+  dinfer_expert_cache_stats r{};
+  for (int l = 0; l < L.nl; ++l) {
+    r.expert_hits += a[(size_t)l * 4 + 0];
+    r.expert_misses += a[(size_t)l * 4 + 1];
+    r.row_hits += a[(size_t)l * 4 + 2];
+    r.row_misses += a[(size_t)l * 4 + 3];
+  }
+  r.bytes_placed = c->bytes_h2d;
+  r.bytes_host_read = r.expert_misses * (int64_t)(expert_gu_bytes(L) + expert_dn_bytes(L));
+  r.placements = c->placements;
+  r.slots = c->slots;
+  r.interval = c->interval;
+  *out = r;
+  if (reset) {
+    HIP_TRY(hipMemsetAsync(c->at<char>(L.off_eacct), 0, (size_t)L.nl * 4 * 8, c->stream));
+    c->bytes_h2d = 0;
+    c->placements = 0;
+  }
   return DINFER_OK;
 }
 
@@ -1233,6 +1491,8 @@ void dinfer_destroy(dinfer_ctx* c) {
   if (c->h_tab_step) (void)hipHostFree(c->h_tab_step);
   if (c->h_tab_ref) (void)hipHostFree(c->h_tab_ref);
   if (c->h_misc) (void)hipHostFree(c->h_misc);
+  if (c->h_wtab) (void)hipHostFree(c->h_wtab);
+  if (c->h_resident) (void)hipHostFree(c->h_resident);
   delete c;
 }
 

@@ -107,6 +107,41 @@ class Engine:
         self.batch = 0
         self.keep_logits(keep_logits)
 
+    def expert_offload(self, slots, interval=0):
+        """dinfer_expert_offload: every expert of every layer in a pinned host
+        store (copies of the packed expert weights), `slots` experts per layer
+        also in an HBM slot buffer; placement after each block-start refresh
+        and every `interval` steps (0: block starts only)."""
+        import torch
+        nl = self.m.n_layers
+        gu = [torch.empty(L["exp_gate_up"].shape, dtype=L["exp_gate_up"].dtype, pin_memory=True)
+              for L in self.packed_layers]
+        dn = [torch.empty(L["exp_down"].shape, dtype=L["exp_down"].dtype, pin_memory=True)
+              for L in self.packed_layers]
+        for i, L in enumerate(self.packed_layers):
+            gu[i].copy_(L["exp_gate_up"])
+            dn[i].copy_(L["exp_down"])
+        torch.cuda.synchronize()
+        one = self.lib.dinfer_expert_slot_bytes(C.byref(self._mc))
+        nbytes = nl * int(slots) * one
+        raw = torch.empty(nbytes + 256, dtype=torch.uint8, device="cuda")
+        off = (-raw.data_ptr()) % 256
+        arr = C.c_void_p * nl
+        self._expert_store = (gu, dn, raw, arr(*[B.ptr(t) for t in gu]), arr(*[B.ptr(t) for t in dn]))
+        B.check(self.lib.dinfer_expert_offload(self.ctx, self._expert_store[3],
+                                               self._expert_store[4], int(slots), int(interval),
+                                               raw.data_ptr() + off, nbytes),
+                "dinfer_expert_offload")
+
+    def expert_place(self):
+        B.check(self.lib.dinfer_expert_place(self.ctx), "dinfer_expert_place")
+
+    def expert_report(self, reset=False):
+        r = B.ExpertCacheStats()
+        B.check(self.lib.dinfer_expert_cache_report(self.ctx, C.byref(r), 1 if reset else 0),
+                "dinfer_expert_cache_report")
+        return {k: getattr(r, k) for k, _ in B.ExpertCacheStats._fields_}
+
     def keep_logits(self, on=True):
         """dinfer_keep_logits: also store the block rows' fp32 logits (inspection)."""
         B.check(self.lib.dinfer_keep_logits(self.ctx, 1 if on else 0), "dinfer_keep_logits")

@@ -322,6 +322,53 @@ dinfer_status dinfer_sched_round(dinfer_sched* sched, const int32_t* h_decode_ro
 dinfer_status dinfer_run_to_completion(dinfer_ctx* ctx, int32_t max_steps,
                                        dinfer_run_stats* h_stats);
 
+/* TIDE-style interval expert placement ("TIDE: Efficient and Lossless MoE
+ * Diffusion LLM Inference with I/O-aware Expert Offload", abstract: expert
+ * activations are stable over the steps of a block, so the placement of
+ * experts is refreshed at intervals, moving only what changes, without loss).
+ *
+ * dinfer_expert_offload switches an MoE context to an expert cache: every
+ * expert of every layer lives in a host store (h_exp_gate_up[l],
+ * h_exp_down[l]: per layer the packed [E][2Fe][d] and [E][d][Fe] matrices of
+ * dinfer_pack_linear, in pinned host memory from hipHostMalloc, borrowed),
+ * and `slots` experts per layer are also held in HBM, in d_slots (caller
+ * device memory, 256-byte aligned, at least n_layers * slots *
+ * dinfer_expert_slot_bytes bytes, borrowed).  The grouped expert projection
+ * reads a resident expert from its slot and any other expert directly from
+ * the host store, so every result is bit-identical to the all-in-HBM run;
+ * only the time changes.  The experts given to dinfer_step_init are not used
+ * afterwards (they may be NULL there, both arrays, if this call follows
+ * before the first refresh).  Initially experts 0..slots-1 are resident.
+ * Placement: per layer, the `slots` experts with the most row assignments
+ * since the last placement (ties: the resident one, then the lower id) are
+ * copied into the slots of the experts they replace (on the context's stream,
+ * in order with the kernels).  dinfer_run_to_completion places after every
+ * block-start refresh and, with interval > 0, every `interval` steps (rounded
+ * up to whole graph replays); dinfer_expert_place does it on demand (waits
+ * for the stream).  DINFER_E_STATE if called twice; DINFER_E_WORKSPACE for a
+ * bad slot buffer; DINFER_E_ARG for a dense model or memory that is not
+ * pinned host memory. */
+typedef struct {
+  int64_t expert_hits;       /* (layer, pass, expert) with rows, expert resident */
+  int64_t expert_misses;     /* ... expert read from the host store              */
+  int64_t row_hits;          /* row assignments to resident experts              */
+  int64_t row_misses;        /* row assignments to host-store experts            */
+  int64_t bytes_placed;      /* host -> HBM copies of placements                 */
+  int64_t bytes_host_read;   /* expert_misses x one expert's weight bytes: what
+                                the kernels read from host memory at least       */
+  int64_t placements;
+  int32_t slots, interval;
+} dinfer_expert_cache_stats;
+size_t dinfer_expert_slot_bytes(const dinfer_model_cfg* model);
+dinfer_status dinfer_expert_offload(dinfer_ctx* ctx, const void* const* h_exp_gate_up,
+                                    const void* const* h_exp_down, int32_t slots,
+                                    int32_t interval, void* d_slots, size_t slots_bytes);
+dinfer_status dinfer_expert_place(dinfer_ctx* ctx);
+/* Counters since dinfer_expert_offload (or the last reset); waits for the
+ * stream.  reset != 0 clears them after reading. */
+dinfer_status dinfer_expert_cache_report(dinfer_ctx* ctx, dinfer_expert_cache_stats* out,
+                                         int32_t reset);
+
 /* Inspection switch (default off): while on, denoise_step also stores the
  * block rows' fp32 logits into the step view's logits buffer.  The vocab
  * statistics are computed in the LM head's epilogue either way (per row and
