@@ -23,6 +23,7 @@ EXPORTS = [
     "dinfer_pending_rows", "dinfer_sched_create", "dinfer_sched_destroy", "dinfer_sched_round",
     "dinfer_vocab_stats_noalloc", "dinfer_keep_logits", "dinfer_expert_slot_bytes",
     "dinfer_expert_offload", "dinfer_expert_place", "dinfer_expert_cache_report",
+    "dinfer_set_activation_precision",
 ]
 
 
@@ -104,6 +105,7 @@ def load(path: str = LIB_PATH) -> C.CDLL:
         "dinfer_run_to_completion": (i32, [vp, i32, C.POINTER(RunStats)]),
         "dinfer_get_step_view": (i32, [vp, C.POINTER(StepView)]),
         "dinfer_keep_logits": (i32, [vp, i32]),
+        "dinfer_set_activation_precision": (i32, [vp, C.c_uint32, C.c_uint32]),
         "dinfer_expert_slot_bytes": (sz, [C.POINTER(ModelCfg)]),
         "dinfer_expert_offload": (i32, [vp, C.POINTER(vp), C.POINTER(vp), i32, i32, vp, sz]),
         "dinfer_expert_place": (i32, [vp]),

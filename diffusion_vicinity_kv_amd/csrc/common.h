@@ -129,6 +129,18 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 
+// Pins prefetched registers at their point of use: an empty volatile asm that
+// takes the values and gives them back, ordered with the barriers around it.
+// Without it the scheduler hoists the pure-ALU conversion of a prefetched
+// operand (fp32 -> bf16 hi/lo) above the previous step's barrier, up to just
+// after its load, and the wait for that load then stalls the step that issued
+// it -- two slabs of prefetch collapse to none.
+template <int N>
+__device__ __forceinline__ void hold_regs(float4 (&r)[N]) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) asm volatile("" : "+v"(r[i].x), "+v"(r[i].y), "+v"(r[i].z), "+v"(r[i].w));
+}
+
 // ---------------------------------------------------------------------------
 // Split-K partial sums: acc[i] += sum over s < S of p[i][s * stride] (float4),
 // in split order, for NV vectors at once.  The split count is dispatched once

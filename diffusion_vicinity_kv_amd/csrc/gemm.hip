@@ -56,7 +56,7 @@ namespace {
 // VS = true (LM head): instead of storing the tile (or besides it, when out
 // is not null) the workgroup stages it in LDS and reduces every row of it to
 // its vocab record (vocab_common.h), rows numbered from vrow0.
-template <typename TW, int MT, int NT, int NW, bool GUARD, bool VS = false>
+template <typename TW, int MT, int NT, int NW, bool GUARD, bool VS = false, bool LO = true>
 __device__ __forceinline__ void skinny_tile(const float* __restrict__ A,
                                             const int* __restrict__ arow, int M,
                                             const TW* __restrict__ W, int N, int K,
@@ -64,7 +64,7 @@ __device__ __forceinline__ void skinny_tile(const float* __restrict__ A,
                                             int c_begin, int c_end,
                                             const VocabEpi* ve = nullptr, int vrow0 = 0) {
   using MF = Mfma<TW>;
-  using AS = ASplit<TW>;
+  using AS = ASplit<TW, LO>;
   constexpr int PL = AS::PLANES;
   constexpr int VEC = MF::VEC;
   constexpr int KSTEP = MF::KSTEP;
@@ -200,6 +200,9 @@ __device__ __forceinline__ void skinny_tile(const float* __restrict__ A,
     store_a(a0, 0);
   }
   __syncthreads();
+  // (Whole groups of three unconditional steps with the remainder after the
+  // loop, which keeps the compiler from draining the prefetch at the loop's
+  // join points, measured 3-10% slower here; the fat kernel takes it.)
   for (int c = c_begin; c < c_end; c += 3) {
     step(c, b0, a1, b2, a2);
     if (c + 1 < c_end) step(c + 1, b1, a2, b0, a0);
@@ -243,7 +246,7 @@ __device__ __forceinline__ void skinny_tile(const float* __restrict__ A,
   }
 }
 
-template <typename TW, int MT, int NT, int NW, bool GUARD>
+template <typename TW, int MT, int NT, int NW, bool GUARD, bool LO>
 __global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(const float* __restrict__ A,
                                                               const TW* __restrict__ W,
                                                               float* __restrict__ P,
@@ -266,7 +269,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(const float* __res
   const int C = K / KC;
   const int M = (m_dev ? min(*m_dev, m_cap) : m_cap) - mt * ROWS;
   if (M <= 0) return;
-  skinny_tile<TW, MT, NT, NW, GUARD>(A + (size_t)mt * ROWS * K, nullptr, min(M, ROWS), W, N, K,
+  skinny_tile<TW, MT, NT, NW, GUARD, false, LO>(A + (size_t)mt * ROWS * K, nullptr, min(M, ROWS), W, N, K,
                                      P + ((size_t)split * m_cap + (size_t)mt * ROWS) * N, N,
                                      tile * (16 * NT * NW), (split * C) / S, ((split + 1) * C) / S);
 }
@@ -352,7 +355,7 @@ __global__ __launch_bounds__(256) void pack_kernel(const TW* __restrict__ W, TW*
 }
 
 // ---------------------------------------------------------------------------
-template <typename TW, int MT, int NT, int NW>
+template <typename TW, int MT, int NT, int NW, bool LO>
 hipError_t run_skinny(const GemmPlan& p, const float* A, const void* W, float* out,
                       const int* m_dev, int m_cap, int N, int K, hipStream_t st) {
   const int n_tiles = N / (16 * NT * NW);
@@ -360,11 +363,11 @@ hipError_t run_skinny(const GemmPlan& p, const float* A, const void* W, float* o
   if (m_cap > 16 * MT * mtiles) return hipErrorInvalidValue;
   const dim3 grid((n_tiles * p.splits + 7) / 8 * 8 * mtiles);
   if (p.guard)
-    hipLaunchKernelGGL((gemm_skinny_kernel<TW, MT, NT, NW, true>), grid, dim3(NW * 64), 0, st, A,
+    hipLaunchKernelGGL((gemm_skinny_kernel<TW, MT, NT, NW, true, LO>), grid, dim3(NW * 64), 0, st, A,
                        static_cast<const TW*>(W), out, m_dev, m_cap, N, K, n_tiles, p.splits,
                        mtiles);
   else
-    hipLaunchKernelGGL((gemm_skinny_kernel<TW, MT, NT, NW, false>), grid, dim3(NW * 64), 0, st, A,
+    hipLaunchKernelGGL((gemm_skinny_kernel<TW, MT, NT, NW, false, LO>), grid, dim3(NW * 64), 0, st, A,
                        static_cast<const TW*>(W), out, m_dev, m_cap, N, K, n_tiles, p.splits,
                        mtiles);
   return hipGetLastError();
@@ -422,27 +425,37 @@ hipError_t lmhead_dispatch(const GemmPlan& p, const float* A, const void* W, con
                    : lmhead_mt<TW, 1, 4>(p, A, W, m_dev, m_cap, N, K, e, st);
 }
 
-template <typename TW, int NT, int NW>
+template <typename TW, int NT, int NW, bool LO>
 hipError_t dispatch_mt(const GemmPlan& p, const float* A, const void* W, float* out,
                        const int* m_dev, int m_cap, int N, int K, hipStream_t st) {
   switch (p.mt) {
-    case 1: return run_skinny<TW, 1, NT, NW>(p, A, W, out, m_dev, m_cap, N, K, st);
-    case 2: return run_skinny<TW, 2, NT, NW>(p, A, W, out, m_dev, m_cap, N, K, st);
-    case 3: return run_skinny<TW, 3, NT, NW>(p, A, W, out, m_dev, m_cap, N, K, st);
-    case 4: return run_skinny<TW, 4, NT, NW>(p, A, W, out, m_dev, m_cap, N, K, st);
+    case 1: return run_skinny<TW, 1, NT, NW, LO>(p, A, W, out, m_dev, m_cap, N, K, st);
+    case 2: return run_skinny<TW, 2, NT, NW, LO>(p, A, W, out, m_dev, m_cap, N, K, st);
+    case 3: return run_skinny<TW, 3, NT, NW, LO>(p, A, W, out, m_dev, m_cap, N, K, st);
+    case 4: return run_skinny<TW, 4, NT, NW, LO>(p, A, W, out, m_dev, m_cap, N, K, st);
     default: break;
   }
   if constexpr (NW == 8) {
     return hipErrorInvalidValue;   // 8-wave groups: at most 64 rows
   } else {
     switch (p.mt) {
-      case 5: return run_skinny<TW, 5, NT, NW>(p, A, W, out, m_dev, m_cap, N, K, st);
-      case 6: return run_skinny<TW, 6, NT, NW>(p, A, W, out, m_dev, m_cap, N, K, st);
-      case 7: return run_skinny<TW, 7, NT, NW>(p, A, W, out, m_dev, m_cap, N, K, st);
-      case 8: return run_skinny<TW, 8, NT, NW>(p, A, W, out, m_dev, m_cap, N, K, st);
+      case 5: return run_skinny<TW, 5, NT, NW, LO>(p, A, W, out, m_dev, m_cap, N, K, st);
+      case 6: return run_skinny<TW, 6, NT, NW, LO>(p, A, W, out, m_dev, m_cap, N, K, st);
+      case 7: return run_skinny<TW, 7, NT, NW, LO>(p, A, W, out, m_dev, m_cap, N, K, st);
+      case 8: return run_skinny<TW, 8, NT, NW, LO>(p, A, W, out, m_dev, m_cap, N, K, st);
       default: return hipErrorInvalidValue;
     }
   }
+}
+
+template <typename TW, bool LO>
+hipError_t dispatch_lo(const GemmPlan& p, const float* A, const void* W, float* out,
+                       const int* m_dev, int m_cap, int N, int K, hipStream_t st) {
+  if constexpr (sizeof(TW) == 2) {   // 8-wave groups: bf16 weights only
+    if (p.nw == 8) return dispatch_mt<TW, 2, 8, LO>(p, A, W, out, m_dev, m_cap, N, K, st);
+  }
+  return p.nt == 2 ? dispatch_mt<TW, 2, 4, LO>(p, A, W, out, m_dev, m_cap, N, K, st)
+                   : dispatch_mt<TW, 1, 4, LO>(p, A, W, out, m_dev, m_cap, N, K, st);
 }
 
 template <typename TW>
@@ -450,12 +463,11 @@ hipError_t dispatch(const GemmPlan& p, const float* A, const void* W, float* out
                     const int* m_dev, int m_cap, int N, int K, hipStream_t st) {
   if (p.kind == 1)
     return launch_gemm_fat(sizeof(TW) == 2 ? DType::BF16 : DType::F32, p.nw, p.splits, A, W,
-                           out, m_dev, m_cap, N, K, st);
-  if constexpr (sizeof(TW) == 2) {   // 8-wave groups: bf16 weights only
-    if (p.nw == 8) return dispatch_mt<TW, 2, 8>(p, A, W, out, m_dev, m_cap, N, K, st);
+                           out, m_dev, m_cap, N, K, st, p.lo != 0);
+  if constexpr (sizeof(TW) == 2) {   // activations in bf16 only: a bf16-weight option
+    if (!p.lo) return dispatch_lo<TW, false>(p, A, W, out, m_dev, m_cap, N, K, st);
   }
-  return p.nt == 2 ? dispatch_mt<TW, 2, 4>(p, A, W, out, m_dev, m_cap, N, K, st)
-                   : dispatch_mt<TW, 1, 4>(p, A, W, out, m_dev, m_cap, N, K, st);
+  return dispatch_lo<TW, true>(p, A, W, out, m_dev, m_cap, N, K, st);
 }
 
 }  // namespace
@@ -526,6 +538,7 @@ bool gemm_shape_ok(DType t, int N, int K) {
 // workgroups.
 GemmPlan plan_gemm(DType t, int m_cap, int N, int K, int target_wgs) {
   GemmPlan p{};
+  p.lo = 1;
   if (m_cap > 128) {
     p.kind = 1;
     p.mtiles = 1;

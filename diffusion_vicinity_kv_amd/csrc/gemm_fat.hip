@@ -25,32 +25,47 @@ namespace {
 // columns past N read the last 16-column group (their outputs are not
 // stored).
 constexpr int kFatM = 128;
+// Vector steps per K slab: two (128-byte LDS rows: 64 bf16 / 32 fp32).
+// Measured against one step of 32 bf16 (64-byte rows, 64 KB of slab
+// buffers): 5% slower at the same occupancy, and 35% slower when held to
+// four waves per SIMD so that two workgroups share a CU (the register limit
+// of 128 spills).
+template <typename TW> constexpr int kFatKK = 2;
 
 //
 // VS = true (LM head, one K split): the 128 x 64*WN tile is reduced to vocab
 // records (vocab_common.h) through LDS, 64 rows at a time, instead of being
 // stored (stored as well when ve.logits is set).
-template <typename TW, int WN, bool VS>
-__global__ __launch_bounds__(128 * WN) void gemm_fat_kernel(const float* __restrict__ A,
+// The 128 KB of LDS admit one workgroup per CU (2 x WN / 4 waves per SIMD),
+// which leaves each wave up to 256 registers; saying so keeps the compiler
+// from squeezing into 128 by reloading the prefetched slabs just before use.
+template <typename TW, int WN, bool VS, bool LO>
+__global__ __launch_bounds__(128 * WN)
+__attribute__((amdgpu_waves_per_eu(1, WN / 2))) void gemm_fat_kernel(const float* __restrict__ A,
                                                             const TW* __restrict__ W,
                                                             float* __restrict__ Cout,
                                                             const int* __restrict__ m_dev,
                                                             int m_cap, int N, int K, VocabEpi ve) {
   constexpr int kFatN = 64 * WN, kFatThreads = 128 * WN;
   using MF = Mfma<TW>;
-  using AS = ASplit<TW>;
+  using AS = ASplit<TW, LO>;
   constexpr int PL = AS::PLANES;
   constexpr int VEC = MF::VEC;
   constexpr int KSTEP = MF::KSTEP;
-  constexpr int KK = 2;                        // vector steps per slab
-  constexpr int BK = KK * KSTEP;               // 64 (bf16) / 32 (fp32) elements
-  constexpr int STR = BK;                      // LDS row: 128 bytes, eight 16-byte chunks
+  constexpr int KK = kFatKK<TW>;               // vector steps per slab
+  constexpr int BK = KK * KSTEP;               // K elements per slab
+  constexpr int STR = BK;                      // LDS row: NC 16-byte chunks, unpadded
   constexpr int CH = 16 / sizeof(TW);          // elements per chunk
-  static_assert(BK * sizeof(TW) == 128, "the swizzle assumes eight chunks per row");
-  // Chunk j of row r lives at chunk j ^ ((r >> 1) & 7): the 16 rows of a
-  // fragment read then fall on 16 distinct 16-byte bank groups, and the
-  // rows of a staging write on disjoint halves of the banks.
-  auto sw = [](int r, int e) { return r * STR + ((((e / CH) ^ (r >> 1)) & 7) * CH) + e % CH; };
+  constexpr int NC = BK / CH;                  // chunks per row: 4 or 8
+  static_assert(NC == 4 || NC == 8, "the swizzle takes rows of 64 or 128 bytes");
+  // LDS reads serve 16 lanes (256 bytes, every bank once) at a time.  Chunk j
+  // of row r lives at chunk j ^ ((r / RS) % NC), RS = 256 / row bytes rows
+  // sharing a bank window: the 16 rows of a fragment read then fall on 16
+  // distinct 16-byte bank groups.
+  constexpr int RS = 256 / (NC * 16);
+  auto sw = [](int r, int e) {
+    return r * STR + ((((e / CH) ^ (r / RS)) & (NC - 1)) * CH) + e % CH;
+  };
   constexpr int F4R = BK / 4;                  // float4 of A per slab row
   constexpr int AV = kFatM * F4R / kFatThreads;     // float4 of A per thread per slab
   constexpr int BE = 64 * VEC;                 // elements of one packed weight block
@@ -113,7 +128,8 @@ __global__ __launch_bounds__(128 * WN) void gemm_fat_kernel(const float* __restr
 #pragma unroll
     for (int i = 0; i < BV; ++i) rb[i] = ld16(wrow[i] + kt * wstep[i]);
   };
-  auto sstore = [&](const float4 (&ra)[AV], const V16 (&rb)[BV], int buf) {
+  auto sstore = [&](float4 (&ra)[AV], const V16 (&rb)[BV], int buf) {
+    hold_regs(ra);
 #pragma unroll
     for (int i = 0; i < AV; ++i) {
       const int v = threadIdx.x + kFatThreads * i;
@@ -157,31 +173,42 @@ __global__ __launch_bounds__(128 * WN) void gemm_fat_kernel(const float* __restr
   gload(a1, b1, 1);
   sstore(a0, b0, 0);
   __syncthreads();
-  for (int kt = 0; kt < nk; kt += 3) {
+  // whole groups of three steps unconditionally, the rest after the loop
+  // (conditional steps inside the loop let the compiler sink the prefetch
+  // loads into their use and drain the pipeline at every iteration)
+  int kt = 0;
+  for (; kt + 3 <= nk; kt += 3) {
+    step(kt, a1, b1, a2, b2);
+    step(kt + 1, a2, b2, a0, b0);
+    step(kt + 2, a0, b0, a1, b1);
+  }
+  if (kt < nk) {
     step(kt, a1, b1, a2, b2);
     if (kt + 1 < nk) step(kt + 1, a2, b2, a0, b0);
-    if (kt + 2 < nk) step(kt + 2, a0, b0, a1, b1);
   }
 
   if constexpr (VS) {
     constexpr int LDZ = kFatN + 16;              // padded rows: stores spread over banks
-    static_assert((size_t)64 * LDZ * sizeof(float) <= kAsBytes + kBsBytes, "half tile fits LDS");
+    // rows staged per pass: 64 when they fit the LDS block, else 32
+    constexpr int RP = (size_t)64 * LDZ * sizeof(float) <= kAsBytes + kBsBytes ? 64 : 32;
+    static_assert((size_t)RP * LDZ * sizeof(float) <= kAsBytes + kBsBytes, "pass fits LDS");
     float* zt = reinterpret_cast<float*>(smem);
-    for (int h = 0; h < 2; ++h) {               // row halves: waves wm == h stage theirs
+    for (int h = 0; h < kFatM / RP; ++h) {      // each pass: the waves holding its rows stage them
       __syncthreads();
-      if (wm == h) {
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
+      for (int mt = 0; mt < 4; ++mt) {
+        const int rb = wm * 64 + mt * 16;       // wave-uniform
+        if (rb / RP != h) continue;
 #pragma unroll
-          for (int nt = 0; nt < 4; ++nt)
+        for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-              zt[(mt * 16 + lg * 4 + i) * LDZ + wn * 64 + nt * 16 + lc] = acc[mt][nt][i];
+          for (int i = 0; i < 4; ++i)
+            zt[(rb % RP + lg * 4 + i) * LDZ + wn * 64 + nt * 16 + lc] = acc[mt][nt][i];
       }
       __syncthreads();
-      const int r0 = m0 + h * 64;
+      const int r0 = m0 + h * RP;
       if (r0 < M)
-        vocab::tile_records<kFatN, 2 * WN>(zt, LDZ, min(64, M - r0), r0, n0, N, blockIdx.x,
+        vocab::tile_records<kFatN, 2 * WN>(zt, LDZ, min(RP, M - r0), r0, n0, N, blockIdx.x,
                                            ve.n_tiles, ve.row_plant_id, ve.row_plant_bias,
                                            ve.mask_id, ve.rec_f, ve.rec_i);
     }
@@ -200,26 +227,26 @@ __global__ __launch_bounds__(128 * WN) void gemm_fat_kernel(const float* __restr
       }
 }
 
-template <bool VS>
+template <bool VS, bool LO>
 hipError_t fat_launch(DType t, int wn, int splits, const float* A, const void* W, float* out,
                       const int* m_dev, int m_cap, int N, int K, const VocabEpi& ve,
                       hipStream_t st) {
-  const int bk = t == DType::F32 ? 32 : 64;   // K per slab
+  const int bk = t == DType::F32 ? 16 * kFatKK<float> : 32 * kFatKK<bf16>;   // K per slab
   if ((wn != 2 && wn != 4) || splits < 1 || splits > K / bk) return hipErrorInvalidValue;
   const dim3 grid((N + 64 * wn - 1) / (64 * wn), (m_cap + kFatM - 1) / kFatM, splits);
   if (t == DType::F32) {
     if (wn == 4)
-      hipLaunchKernelGGL((gemm_fat_kernel<float, 4, VS>), grid, dim3(512), 0, st, A,
+      hipLaunchKernelGGL((gemm_fat_kernel<float, 4, VS, true>), grid, dim3(512), 0, st, A,
                          static_cast<const float*>(W), out, m_dev, m_cap, N, K, ve);
     else
-      hipLaunchKernelGGL((gemm_fat_kernel<float, 2, VS>), grid, dim3(256), 0, st, A,
+      hipLaunchKernelGGL((gemm_fat_kernel<float, 2, VS, true>), grid, dim3(256), 0, st, A,
                          static_cast<const float*>(W), out, m_dev, m_cap, N, K, ve);
   } else {
     if (wn == 4)
-      hipLaunchKernelGGL((gemm_fat_kernel<bf16, 4, VS>), grid, dim3(512), 0, st, A,
+      hipLaunchKernelGGL((gemm_fat_kernel<bf16, 4, VS, LO>), grid, dim3(512), 0, st, A,
                          static_cast<const bf16*>(W), out, m_dev, m_cap, N, K, ve);
     else
-      hipLaunchKernelGGL((gemm_fat_kernel<bf16, 2, VS>), grid, dim3(256), 0, st, A,
+      hipLaunchKernelGGL((gemm_fat_kernel<bf16, 2, VS, LO>), grid, dim3(256), 0, st, A,
                          static_cast<const bf16*>(W), out, m_dev, m_cap, N, K, ve);
   }
   return hipGetLastError();
@@ -228,15 +255,18 @@ hipError_t fat_launch(DType t, int wn, int splits, const float* A, const void* W
 }  // namespace
 
 hipError_t launch_gemm_fat(DType t, int wn, int splits, const float* A, const void* W,
-                           float* out, const int* m_dev, int m_cap, int N, int K, hipStream_t st) {
-  return fat_launch<false>(t, wn, splits, A, W, out, m_dev, m_cap, N, K, VocabEpi{}, st);
+                           float* out, const int* m_dev, int m_cap, int N, int K, hipStream_t st,
+                           bool lo) {
+  if (!lo && t == DType::BF16)
+    return fat_launch<false, false>(t, wn, splits, A, W, out, m_dev, m_cap, N, K, VocabEpi{}, st);
+  return fat_launch<false, true>(t, wn, splits, A, W, out, m_dev, m_cap, N, K, VocabEpi{}, st);
 }
 
 hipError_t launch_gemm_fat_lmhead(DType t, int wn, const float* A, const void* W,
                                   const int* m_dev, int m_cap, int N, int K, const VocabEpi& e,
                                   hipStream_t st) {
   if (e.n_tiles != (N + 64 * wn - 1) / (64 * wn)) return hipErrorInvalidValue;
-  return fat_launch<true>(t, wn, 1, A, W, e.logits, m_dev, m_cap, N, K, e, st);
+  return fat_launch<true, true>(t, wn, 1, A, W, e.logits, m_dev, m_cap, N, K, e, st);
 }
 
 }  // namespace dinfer

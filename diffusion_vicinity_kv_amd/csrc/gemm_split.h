@@ -10,9 +10,12 @@
 namespace dinfer {
 namespace {
 
-template <typename TW> struct ASplit;
+// LO = false (bf16 only): the activations enter the MFMA as bf16(a) alone --
+// one plane, one MFMA per weight fragment, the activation's own rounding
+// kept (a per-projection precision option of the library).
+template <typename TW, bool LO = true> struct ASplit;
 // bf16 weights: two LDS planes (hi, lo) of bf16 activations.
-template <> struct ASplit<bf16> {
+template <> struct ASplit<bf16, true> {
   static constexpr int PLANES = 2;
   __device__ __forceinline__ static void store4(bf16* hi, bf16* lo, const float4& x) {
     const float v[4] = {x.x, x.y, x.z, x.w};
@@ -26,8 +29,19 @@ template <> struct ASplit<bf16> {
     *reinterpret_cast<bf16x4*>(lo) = l;
   }
 };
+template <> struct ASplit<bf16, false> {
+  static constexpr int PLANES = 1;
+  __device__ __forceinline__ static void store4(bf16* hi, bf16*, const float4& x) {
+    bf16x4 h;
+    h[0] = static_cast<bf16>(x.x);
+    h[1] = static_cast<bf16>(x.y);
+    h[2] = static_cast<bf16>(x.z);
+    h[3] = static_cast<bf16>(x.w);
+    *reinterpret_cast<bf16x4*>(hi) = h;
+  }
+};
 // fp32 weights: one plane of fp32 activations.
-template <> struct ASplit<float> {
+template <bool LO> struct ASplit<float, LO> {
   static constexpr int PLANES = 1;
   __device__ __forceinline__ static void store4(float* p, float*, const float4& x) {
     *reinterpret_cast<float4*>(p) = x;

@@ -37,6 +37,7 @@ struct GemmPlan {
   int splits;    // K splits (partials out[s][m][n], summed by the consumer)
   int mtiles;    // skinny: row tiles of 16*mt rows per (column group, split); 1 or 2
   int grid;
+  int lo;        // bf16 weights: 1 = activations as hi + lo bf16 halves, 0 = bf16 only
 };
 GemmPlan plan_gemm(DType t, int m_cap, int N, int K, int target_wgs);
 // A is fp32 (split into hi/lo bf16 halves in-kernel for bf16 weights).
@@ -45,7 +46,8 @@ hipError_t launch_gemm(const GemmPlan& p, DType t, const float* A, const void* W
 // The fat kernel alone (M > 128): wn = 2 or 4 column waves (128 x 64*wn
 // tiles), splits K slices (1 .. K/64 bf16, K/32 fp32) writing out[s][m][n].
 hipError_t launch_gemm_fat(DType t, int wn, int splits, const float* A, const void* W,
-                           float* out, const int* m_dev, int m_cap, int N, int K, hipStream_t st);
+                           float* out, const int* m_dev, int m_cap, int N, int K, hipStream_t st,
+                           bool lo = true);
 // n_mats matrices W [N][K] row-major -> the packed block layout every GEMM
 // here reads (gemm_split.h: 16-row groups x one MFMA vector step per 1 KB
 // block, 256-row tiles stored k-step by k-step).  N % 16 == 0, K a multiple

@@ -322,6 +322,9 @@ struct dinfer_ctx {
   int state = 0;                  // 0 init, 1 batch bound
   bool stats_ready = false;
   bool keep_logits = false;       // the LM head also stores the fp32 logits
+  // projections whose activations enter the MFMA in bf16 only (bit 0 QKV,
+  // 1 O, 2 gate|up, 3 down), in steps and in refreshes; 0 = hi + lo everywhere
+  uint32_t hi_only_step = 0, hi_only_refresh = 0;
   // graph
   hipGraphExec_t graph = nullptr;
   int graph_steps = 0;
@@ -388,10 +391,15 @@ dinfer_status run_pass(dinfer_ctx* c, bool step) {
   const int m_cap = step ? L.m_step : c->ref_mcap;
   int* tab = c->at<int>(step ? L.off_tab_step : L.off_tab_ref);
   const PassTable tb = table_view(tab, step ? L.m_step : L.m_ref, L.max_batch);
-  const GemmPlan& gq = step ? L.g_qkv_s : c->ref_q;
-  const GemmPlan& go = step ? L.g_o_s : c->ref_o;
-  const GemmPlan& gg = step ? L.g_gu_s : c->ref_g;
-  const GemmPlan& gd = step ? L.g_d_s : c->ref_d;
+  GemmPlan gq = step ? L.g_qkv_s : c->ref_q;
+  GemmPlan go = step ? L.g_o_s : c->ref_o;
+  GemmPlan gg = step ? L.g_gu_s : c->ref_g;
+  GemmPlan gd = step ? L.g_d_s : c->ref_d;
+  const uint32_t hi_only = step ? c->hi_only_step : c->hi_only_refresh;
+  gq.lo = !(hi_only & 1u);
+  go.lo = !(hi_only & 2u);
+  gg.lo = !(hi_only & 4u);
+  gd.lo = !(hi_only & 8u);
   const AttnPlan& ap = step ? L.a_step : L.a_ref;
   const int d = L.d;
   const int F = L.moe ? L.Fs : L.F;   // dense FFN, or the MoE layer's shared expert
@@ -1328,6 +1336,22 @@ dinfer_status dinfer_expert_cache_report(dinfer_ctx* c, dinfer_expert_cache_stat
     c->bytes_h2d = 0;
     c->placements = 0;
   }
+  return DINFER_OK;
+}
+
+dinfer_status dinfer_set_activation_precision(dinfer_ctx* c, uint32_t step_mask,
+                                              uint32_t refresh_mask) {
+  if (!c) return fail(DINFER_E_ARG, "ctx is null");
+  if ((step_mask | refresh_mask) & ~0xFu) return fail(DINFER_E_ARG, "masks hold bits 0..3 only");
+  if (c->L.dt != DType::BF16 && (step_mask | refresh_mask))
+    return fail(DINFER_E_UNSUPPORTED, "bf16-only activations need bf16 weights");
+  if (c->graph && step_mask != c->hi_only_step) {
+    (void)hipGraphExecDestroy(c->graph);
+    c->graph = nullptr;
+    c->graph_steps = 0;
+  }
+  c->hi_only_step = step_mask;
+  c->hi_only_refresh = refresh_mask;
   return DINFER_OK;
 }
 

@@ -142,6 +142,13 @@ class Engine:
                 "dinfer_expert_cache_report")
         return {k: getattr(r, k) for k, _ in B.ExpertCacheStats._fields_}
 
+    def set_activation_precision(self, step_mask=0, refresh_mask=0):
+        """dinfer_set_activation_precision: bit i (0 QKV, 1 O, 2 gate|up, 3 down)
+        = that projection takes bf16 activations alone instead of hi + lo."""
+        B.check(self.lib.dinfer_set_activation_precision(self.ctx, int(step_mask),
+                                                         int(refresh_mask)),
+                "dinfer_set_activation_precision")
+
     def keep_logits(self, on=True):
         """dinfer_keep_logits: also store the block rows' fp32 logits (inspection)."""
         B.check(self.lib.dinfer_keep_logits(self.ctx, 1 if on else 0), "dinfer_keep_logits")

@@ -369,6 +369,17 @@ dinfer_status dinfer_expert_place(dinfer_ctx* ctx);
 dinfer_status dinfer_expert_cache_report(dinfer_ctx* ctx, dinfer_expert_cache_stats* out,
                                          int32_t reset);
 
+/* Activation precision of the projections (bf16 weights; default 0, 0):
+ * bit i of a mask set means projection i -- 0 QKV, 1 O, 2 gate|up, 3 down
+ * (for an MoE model: the shared expert's gate|up and down) -- takes its fp32
+ * activations into the bf16 MFMA as bf16(a) alone, one MFMA per weight
+ * fragment; clear means as hi = bf16(a) plus lo = bf16(a - hi), two MFMAs, so
+ * that only the weights' rounding remains.  step_mask applies to
+ * denoise_step, refresh_mask to refresh_kv.  DINFER_E_UNSUPPORTED with fp32
+ * weights and a nonzero mask. */
+dinfer_status dinfer_set_activation_precision(dinfer_ctx* ctx, uint32_t step_mask,
+                                              uint32_t refresh_mask);
+
 /* Inspection switch (default off): while on, denoise_step also stores the
  * block rows' fp32 logits into the step view's logits buffer.  The vocab
  * statistics are computed in the LM head's epilogue either way (per row and
