@@ -316,6 +316,47 @@ def run_queue_workload(wc, w, n_requests, unroll, budget=None):
             "max_round_ms": round(1e3 * rnd[-1], 2)}
 
 
+def gemm_shapes(shapes, reps=20, n_weights=4):
+    """Projection kernel timing at the given (M, N, K) shapes: dinfer_linear
+    on random fp32 activations and n_weights packed bf16 weight matrices per
+    shape (rotated, so weights stream from HBM), `reps` launches captured in a
+    graph and replayed twice between events; per shape the average launch
+    time, algorithmic TFLOP/s (2 M N K) and its fraction of the bf16 peak."""
+    import torch
+    from diffusion_vicinity_kv_amd import binding as B
+    lib = B.load()
+    out = []
+    for M, N, K in shapes:
+        g = torch.Generator(device="cuda").manual_seed(M + N + K)
+        A = torch.randn(M, K, device="cuda", generator=g)
+        Ws = [B.pack_linear((torch.randn(N, K, device="cuda", generator=g) * 0.02)
+                            .to(torch.bfloat16)) for _ in range(n_weights)]
+        dst = torch.empty(lib.dinfer_linear_out_elems(M, N, K, B.BF16), device="cuda")
+        S = B.linear(A, Ws[0], dst)
+        torch.cuda.synchronize()
+        cap = torch.cuda.Stream()
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr, stream=cap):
+            for i in range(reps):
+                B.linear(A, Ws[i % n_weights], dst)
+        gr.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        gr.replay()
+        gr.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / (2 * reps)
+        tf = 2.0 * M * N * K / us / 1e6
+        out.append({"M": M, "N": N, "K": K, "splits": S, "us": round(us, 2),
+                    "tflops": round(tf, 1), "frac_bf16_peak": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+                    "weight_gbs": round(N * K * 2 / us / 1e3, 1)})
+        del gr, Ws, A, dst
+        torch.cuda.empty_cache()
+    return out
+
+
 def run_expert_sweep(wc, w, slot_list, intervals, blocks, unroll):
     """TIDE-style expert cache on the MoE workload: the first `blocks` blocks
     of its request with `slots` experts per layer in HBM and the rest read
@@ -408,6 +449,9 @@ def main():
                          "(0: block starts only)")
     ap.add_argument("--expert-blocks", type=int, default=2,
                     help="with --expert-sweep: blocks of the request to run")
+    ap.add_argument("--gemm-shapes", default="",
+                    help="only time the projection kernels at these MxNxK shapes "
+                         "(comma-separated, e.g. 1024x12288x4096,64x12288x4096)")
     ap.add_argument("--kernel-only", action="store_true",
                     help="only the dominant-kernel timing loop (for counter runs)")
     ap.add_argument("--calib-copy", action="store_true",
@@ -426,6 +470,11 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     torch.cuda.set_device(0)
+    if args.gemm_shapes:
+        shapes = [tuple(int(x) for x in t.split("x")) for t in args.gemm_shapes.split(",")]
+        for r in gemm_shapes(shapes):
+            print(json.dumps(r), flush=True)
+        return
     wc = synth.preset(args.workload)
     m = wc.model
 

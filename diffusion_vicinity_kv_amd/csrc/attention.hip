@@ -128,17 +128,19 @@ __global__ __launch_bounds__(256 * kKeyGroups) void attn_kernel(
 
   // fragment f of a step, as lane `lane` holds it: f < NK is K tile t = f /
   // QV, head-dim step kk = f % QV; the rest are V^T row tiles ht = f - NK
+  // The K or V address of a fragment is selected, not branched on: with a
+  // branch per load (the fragment index depends on the wave) every load sits
+  // in a block of its own and the wait counts at the joins drain the whole
+  // prefetch at each step.
   auto load = [&](V16 (&reg)[FW], int i) {     // this group's local step i
     const int kb = k0 + min(kg + i * KG, n_steps - 1) * KS;   // past the end: repeat the last
 #pragma unroll
     for (int i = 0; i < FW; ++i) {
       const int f = wave * FW + i;
-      if (f < NK) {
-        const int key = min(kb + krow0 + 4 * (f / QV), L - 1);   // rows past the range are masked
-        reg[i] = ld16(kbase + (size_t)key * HD + (f % QV) * KS);
-      } else {
-        reg[i] = ld16(vbase + (size_t)(kb >> 5) * HD * 32 + (f - NK) * 16 * 32 + (kb & 31));
-      }
+      const int key = min(kb + krow0 + 4 * (f / QV), L - 1);   // rows past the range are masked
+      const T* kp = kbase + (size_t)key * HD + (f % QV) * KS;
+      const T* vp = vbase + (size_t)(kb >> 5) * HD * 32 + (f - NK) * 16 * 32 + (kb & 31);
+      reg[i] = ld16(f < NK ? kp : vp);
     }
   };
   auto store = [&](const V16 (&reg)[FW], int buf) {
@@ -230,10 +232,18 @@ __global__ __launch_bounds__(256 * kKeyGroups) void attn_kernel(
   load(r1, 1);
   store(r0, 0);
   __syncthreads();
-  for (int i = 0; i < n_local; i += 3) {
+  // whole groups of three steps unconditionally, the rest after the loop
+  // (conditional steps inside the loop let the compiler sink the prefetch
+  // loads into their use and drain the pipeline at every iteration)
+  int i = 0;
+  for (; i + 3 <= n_local; i += 3) {
+    step(i, r1, r2);
+    step(i + 1, r2, r0);
+    step(i + 2, r0, r1);
+  }
+  if (i < n_local) {
     step(i, r1, r2);
     if (i + 1 < n_local) step(i + 1, r2, r0);
-    if (i + 2 < n_local) step(i + 2, r0, r1);
   }
 
   // each lane summed its own keys: total over the query's four lanes
