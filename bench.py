@@ -316,10 +316,11 @@ def run_queue_workload(wc, w, n_requests, unroll, budget=None):
             "max_round_ms": round(1e3 * rnd[-1], 2)}
 
 
-def gemm_shapes(shapes, reps=20, n_weights=4):
+def gemm_shapes(shapes, reps=32):
     """Projection kernel timing at the given (M, N, K) shapes: dinfer_linear
-    on random fp32 activations and n_weights packed bf16 weight matrices per
-    shape (rotated, so weights stream from HBM), `reps` launches captured in a
+    on random fp32 activations and enough packed bf16 weight matrices per
+    shape to span 1 GiB (rotated, so weights stream from HBM rather than the
+    256 MB last-level cache), `reps` launches captured in a
     graph and replayed twice between events; per shape the average launch
     time, algorithmic TFLOP/s (2 M N K) and its fraction of the bf16 peak."""
     import torch
@@ -329,6 +330,7 @@ def gemm_shapes(shapes, reps=20, n_weights=4):
     for M, N, K in shapes:
         g = torch.Generator(device="cuda").manual_seed(M + N + K)
         A = torch.randn(M, K, device="cuda", generator=g)
+        n_weights = min(reps, max(4, -(-(1 << 30) // (N * K * 2))))
         Ws = [B.pack_linear((torch.randn(N, K, device="cuda", generator=g) * 0.02)
                             .to(torch.bfloat16)) for _ in range(n_weights)]
         dst = torch.empty(lib.dinfer_linear_out_elems(M, N, K, B.BF16), device="cuda")
@@ -355,6 +357,74 @@ def gemm_shapes(shapes, reps=20, n_weights=4):
         del gr, Ws, A, dst
         torch.cuda.empty_cache()
     return out
+
+
+def trace_summary(csv_path, top=40):
+    """Per (kernel, grid size) totals of a rocprofv3 kernel-trace CSV, as a
+    markdown table: the same kernel runs with different grids in a block
+    refresh (all prompt rows) and in a denoise step (the window rows), and
+    this is what tells them apart."""
+    import csv
+    import collections
+    agg = collections.defaultdict(lambda: [0, 0.0])
+    def dims(r, stem):
+        xyz = [r.get(f"{stem}_{a}") for a in "XYZ"]
+        if all(xyz):
+            return "x".join(xyz)
+        return r.get(stem, "")
+
+    for r in csv.DictReader(open(csv_path)):
+        name = r["Kernel_Name"].replace("(anonymous namespace)::", "")
+        if name.startswith("void "):
+            name = name[5:]
+        us = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        key = (name.split("(")[0][:110], dims(r, "Grid_Size"), dims(r, "Workgroup_Size"))
+        agg[key][0] += 1
+        agg[key][1] += us
+    total = sum(v[1] for v in agg.values())
+    lines = ["| kernel | grid (work-items x, y, z) | workgroup | calls | total ms | avg us | % |",
+             "|---|---:|---:|---:|---:|---:|---:|"]
+    for (name, grid, wg), (n, us) in sorted(agg.items(), key=lambda kv: -kv[1][1])[:top]:
+        lines.append(f"| `{name}` | {grid} | {wg} | {n} | {us / 1e3:.2f} | {us / n:.2f} | "
+                     f"{100 * us / total:.1f} |")
+    lines.append(f"\nTotal kernel time {total / 1e3:.1f} ms over {sum(v[0] for v in agg.values())} "
+                 "dispatches.")
+    return "\n".join(lines)
+
+
+def traffic_record(k_fetch, k_write, c_fetch, c_write, commands):
+    """The dominant kernel's HBM traffic per launch from two rocprofv3 --pmc
+    runs of --kernel-only (FETCH_SIZE, WRITE_SIZE; KiB per dispatch), each
+    scaled by what the same counter reads for the 1 GiB copy of --calib-copy,
+    keyed on the hash of the kernel's sources."""
+    import csv
+
+    def mean(path, counter, match):
+        vals = [float(r["Counter_Value"]) for r in csv.DictReader(open(path))
+                if r["Counter_Name"] == counter and match in r["Kernel_Name"]]
+        if not vals:
+            raise SystemExit(f"no {counter} rows for {match} in {path}")
+        return sum(vals) / len(vals), len(vals)
+
+    kf, n = mean(k_fetch, "FETCH_SIZE", "gemm_skinny_kernel")
+    kw, _ = mean(k_write, "WRITE_SIZE", "gemm_skinny_kernel")
+    cf, _ = mean(c_fetch, "FETCH_SIZE", "copyBuffer")
+    cw, _ = mean(c_write, "WRITE_SIZE", "copyBuffer")
+    copy_bytes = 1 << 30
+    ff, wf = copy_bytes / 1024 / cf, copy_bytes / 1024 / cw
+    return {"kernel": f"{KERNEL} (QKV and gate|up projections, 64 rows)",
+            "workload": "dense8b_b1 window: 64 rows x d 4096, N = 12288 (QKV) and 24576 (gate|up), "
+                        "alternating; weights packed k-step-major",
+            "source_hash": source_hash(),
+            "source_files": [f"diffusion_vicinity_kv_amd/csrc/{f}"
+                             for f in ("gemm.hip", "gemm_split.h", "common.h")],
+            "dispatches": n, "fetch_kib_per_dispatch": round(kf, 1),
+            "write_kib_per_dispatch": round(kw, 1),
+            "calibration": {"copy_bytes": copy_bytes, "copy_kernel": "__amd_rocclr_copyBuffer",
+                            "copy_fetch_kib": cf, "copy_write_kib": cw,
+                            "fetch_factor": ff, "write_factor": wf},
+            "bytes_per_launch": int(round((kf * ff + kw * wf) * 1024)),
+            "commands": commands}
 
 
 def run_expert_sweep(wc, w, slot_list, intervals, blocks, unroll):
@@ -456,7 +526,26 @@ def main():
                     help="only the dominant-kernel timing loop (for counter runs)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="one plain 1 GiB device copy (counter calibration)")
+    ap.add_argument("--trace-summary", default="",
+                    help="print per-(kernel, grid) totals of this rocprofv3 kernel-trace CSV "
+                         "as a markdown table (no GPU work)")
+    ap.add_argument("--traffic-record", nargs=4, default=None,
+                    metavar=("KERNEL_FETCH_CSV", "KERNEL_WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
+                    help="write the dominant kernel's HBM traffic record from the counter CSVs of "
+                         "--kernel-only and --calib-copy runs (no GPU work)")
+    ap.add_argument("--traffic-out", default=TRAFFIC_FILE)
     args = ap.parse_args()
+    if args.trace_summary:
+        print(trace_summary(args.trace_summary))
+        return
+    if args.traffic_record:
+        cmds = [f"rocprofv3 --pmc {c} --output-format csv -d <dir> -o run -- python3 -u bench.py {m}"
+                for m in ("--kernel-only", "--calib-copy") for c in ("FETCH_SIZE", "WRITE_SIZE")]
+        rec = traffic_record(*args.traffic_record, cmds)
+        with open(args.traffic_out, "w") as f:
+            json.dump(rec, f, indent=1)
+        print(json.dumps({k: rec[k] for k in ("bytes_per_launch", "dispatches", "source_hash")}))
+        return
     if args.gpus != 1:
         print(f"bench.py: this library runs on one GPU; --gpus {args.gpus} is not supported "
               "(the multi-GPU layout is described in the design notes, not built)",
