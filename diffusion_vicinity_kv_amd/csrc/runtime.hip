@@ -284,6 +284,11 @@ struct dinfer_ctx {
   hipStream_t stream = nullptr;   // caller's stream
   hipStream_t st = nullptr;       // stream kernels go to (the capture stream while capturing)
   hipStream_t cap_stream = nullptr;
+  // MoE: the shared expert runs on a second stream beside the routed
+  // experts (forked and joined with events, in eager passes and in the
+  // captured step graph alike)
+  hipStream_t side = nullptr;
+  hipEvent_t ev_fork = nullptr, ev_join = nullptr;
   // weights
   const void* tok_emb = nullptr;
   const void* final_norm = nullptr;
@@ -454,6 +459,15 @@ dinfer_status run_pass(dinfer_ctx* c, bool step) {
     float* egu = c->at<float>(L.off_egu);
     float* eact = c->at<float>(L.off_eact);
     float* ey = c->at<float>(L.off_ey);
+    // the shared expert needs only the normalised input: fork it onto the
+    // side stream, where it overlaps the router, the plan and the routed
+    // experts (it writes part and act, which nothing below touches)
+    HIP_TRY(hipEventRecord(c->ev_fork, st));
+    HIP_TRY(hipStreamWaitEvent(c->side, c->ev_fork, 0));
+    HIP_TRY(launch_gemm(gg, dt, a, c->sgu[l], part, tb.nrows, m_cap, 2 * F, d, c->side));
+    HIP_TRY(launch_swiglu(tb.nrows, m_cap, part, gg.splits, stride_g, F, act, c->side));
+    HIP_TRY(launch_gemm(gd, dt, act, c->sd[l], part, tb.nrows, m_cap, d, F, c->side));
+    HIP_TRY(hipEventRecord(c->ev_join, c->side));
     HIP_TRY(launch_moe_route(dt, tb, m_cap, a, d, c->router[l], E, K8, c->router_bias, L.nl,
                              c->n_bias_blocks, l, sel, gate, c->at<float>(L.off_rlog), st));
     HIP_TRY(launch_moe_plan(tb.nrows, m_cap, sel, E, K8, e_count, e_off, row_of, pos, n_assign, st));
@@ -466,9 +480,7 @@ dinfer_status run_pass(dinfer_ctx* c, bool step) {
     HIP_TRY(launch_swiglu(n_assign, m_cap * K8, egu, 1, 0, Fe, eact, st));
     HIP_TRY(launch_gemm_grouped(dt, eact, nullptr, e_count, e_off, E, m_cap, wt + E, ey, d, Fe,
                                 st));
-    HIP_TRY(launch_gemm(gg, dt, a, c->sgu[l], part, tb.nrows, m_cap, 2 * F, d, st));
-    HIP_TRY(launch_swiglu(tb.nrows, m_cap, part, gg.splits, stride_g, F, act, st));
-    HIP_TRY(launch_gemm(gd, dt, act, c->sd[l], part, tb.nrows, m_cap, d, F, st));
+    HIP_TRY(hipStreamWaitEvent(st, c->ev_join, 0));   // join the shared expert
     HIP_TRY(launch_moe_combine(tb.nrows, m_cap, x, part, gd.splits, stride_d, ey, pos, gate, K8, d,
                                st));
   }
@@ -734,6 +746,10 @@ dinfer_status dinfer_step_init(const dinfer_model_cfg* m, const dinfer_decode_cf
   std::memset(c->h_tab_step, 0, (size_t)L.tab_ints_step * 4);
   std::memset(c->h_tab_ref, 0, (size_t)L.tab_ints_ref * 4);
   if (L.moe) {
+    if (hipStreamCreateWithFlags(&c->side, hipStreamNonBlocking) != hipSuccess ||
+        hipEventCreateWithFlags(&c->ev_fork, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&c->ev_join, hipEventDisableTiming) != hipSuccess)
+      return cleanup(fail(DINFER_E_HIP, "stream or event creation failed"));
     const size_t ne = (size_t)L.nl * L.E;
     if (hipHostMalloc(&c->h_wtab, ne * 2 * sizeof(void*)) != hipSuccess ||
         hipHostMalloc(&c->h_resident, ne * 4) != hipSuccess)
@@ -1508,6 +1524,9 @@ void dinfer_destroy(dinfer_ctx* c) {
   if (!c) return;
   if (c->graph) (void)hipGraphExecDestroy(c->graph);
   if (c->cap_stream) (void)hipStreamDestroy(c->cap_stream);
+  if (c->side) (void)hipStreamDestroy(c->side);
+  if (c->ev_fork) (void)hipEventDestroy(c->ev_fork);
+  if (c->ev_join) (void)hipEventDestroy(c->ev_join);
   if (c->ev_step_upload) (void)hipEventDestroy(c->ev_step_upload);
   if (c->ev_ref_upload) (void)hipEventDestroy(c->ev_ref_upload);
   if (c->ev0) (void)hipEventDestroy(c->ev0);
