@@ -33,9 +33,11 @@ Also reported:
     raised by ln(V-1), so that planted positions pass the threshold gate:
     tokens/s, step latency and the same accounting.  A separate reading of
     the planting, labelled as such; `value` is always the literal workload.
-  cpu_baseline: the CPU oracle on a bounded sample (one layer's refresh and
-    one layer's window step plus the LM head / vocab stats / commit of one
-    step), scaled to the run's layer, refresh and step counts.
+  cpu_baseline: the CPU oracle on a bounded sample -- one full refresh and
+    the median of three full steps (every layer, LM head, vocab stats,
+    commit) when a refresh takes under 25 s on the host, else one layer of
+    each scaled to the model's layers -- scaled to the run's refresh and step
+    counts.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                        [--no-batch16] [--no-cpu-baseline] [--queue Q [--budget T]]
@@ -124,8 +126,18 @@ def dominant_kernel_timing(wc, weights, iters=40):
     return avg_ms, nbytes / len(shapes), nflops / len(shapes), rows
 
 
-def cpu_baseline(wc, gpu_refreshes_per_run, gpu_steps_per_run, committed_per_run):
-    """Oracle timed on a bounded sample of the workload, scaled to one run."""
+def cpu_baseline(wc, gpu_refreshes_per_run, gpu_steps_per_run, committed_per_run,
+                 full_budget_s=25.0):
+    """Oracle timed on a bounded sample of the workload, scaled to one run.
+
+    One layer of the full refresh is timed first.  If a whole refresh of
+    every layer fits full_budget_s, the sample is one full refresh and three
+    full steps (all layers, the LM head, vocab statistics and commit; the
+    step time is their median), on a model whose layers all reuse layer 0's
+    weights -- the oracle's cost depends on the shapes only, and one fp64
+    copy of a layer keeps the host memory small.  Otherwise the one-layer
+    refresh and twelve one-layer window steps are scaled to the model's
+    layers."""
     import numpy as np
     import oracle
     import synth
@@ -136,36 +148,63 @@ def cpu_baseline(wc, gpu_refreshes_per_run, gpu_steps_per_run, committed_per_run
     except Exception:  # pragma: no cover
         threads = os.cpu_count()
     m = wc.model
+    nl = m.n_layers
     w = synth.make_weights(m, wc.seed, device="cpu", layers=[0])
     req = synth.make_requests(wc)
-    om = oracle.OracleModel(m, w, layers=[0])
     rb = req.get("router_bias")
-    run = oracle.OracleRun(om, wc.decode, req["tokens"][0].numpy(), int(req["prompt_len"][0]),
-                           int(req["gen_len"][0]), req["plant_id"][0].numpy(),
-                           float(req["plant_bias"][0]), None if rb is None else rb[0].numpy())
+
+    def new_run(om):
+        return oracle.OracleRun(om, wc.decode, req["tokens"][0].numpy(), int(req["prompt_len"][0]),
+                                int(req["gen_len"][0]), req["plant_id"][0].numpy(),
+                                float(req["plant_bias"][0]), None if rb is None else rb[0].numpy())
+
+    def one_step(om, run, lo, hi):
+        e = run.window_embeddings(lo, hi)
+        t0 = time.perf_counter()
+        h = om.forward_rows(run.cache, np.arange(lo, hi), e, run.L, run._router_bias_block())
+        t_layers = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        st = run.stats(om.logits(h[run.bs - lo: run.be - lo]))
+        run.commit(st)
+        return t_layers, time.perf_counter() - t0
+
+    om = oracle.OracleModel(m, w, layers=[0])
+    run = new_run(om)
     t0 = time.perf_counter()
     run.start_block(0)                           # one layer of the full refresh
     t_ref_layer = time.perf_counter() - t0
     lo, hi = run.window()
-    reps = 12                                    # window steps sampled (averaged)
+    base = {"unit": "tokens/s", "cores": int(threads), "kind": "oracle"}
+    if nl * t_ref_layer <= full_budget_s:
+        om.layer_ids = list(range(nl))            # every layer on layer 0's weights
+        om.layers = {li: om.layers[0] for li in om.layer_ids}
+        run = new_run(om)
+        t0 = time.perf_counter()
+        run.start_block(0)
+        t_refresh = time.perf_counter() - t0
+        steps = [sum(one_step(om, run, lo, hi)) for _ in range(3)]
+        t_step = float(np.median(steps))
+        t_run = gpu_refreshes_per_run * t_refresh + gpu_steps_per_run * t_step
+        return {**base, "value": round(committed_per_run / t_run, 4),
+                "sample": (f"fp64 NumPy oracle, all {nl} layers (sharing one layer's weights): one "
+                           f"full refresh of {run.L} rows ({t_refresh:.2f} s) and the median of 3 "
+                           f"full steps of {hi - lo} window rows with the LM head, vocab stats and "
+                           f"commit ({', '.join(f'{x:.2f}' for x in steps)} s); scaled to "
+                           f"{gpu_refreshes_per_run} refreshes and {gpu_steps_per_run} steps per "
+                           f"run ({t_run:.1f} s; {t_ref_layer + t_refresh + sum(steps):.1f} s "
+                           "measured)"),
+                "step_s": round(t_step, 3), "refresh_s": round(t_refresh, 3)}
+    reps = 12                                    # window steps of one layer (averaged)
     t_step_layer = t_head = 0.0
     for _ in range(reps):
-        t0 = time.perf_counter()
-        e = run.window_embeddings(lo, hi)
-        h = om.forward_rows(run.cache, np.arange(lo, hi), e, run.L, run._router_bias_block())
-        t_step_layer += (time.perf_counter() - t0) / reps
-        t0 = time.perf_counter()
-        logits = om.logits(h[run.bs - lo: run.be - lo])
-        st = run.stats(logits)
-        run.commit(st)
-        t_head += (time.perf_counter() - t0) / reps
-    nl = m.n_layers
+        a, b = one_step(om, run, lo, hi)
+        t_step_layer += a / reps
+        t_head += b / reps
     t_refresh = nl * t_ref_layer
     t_step = nl * t_step_layer + t_head
     t_run = gpu_refreshes_per_run * t_refresh + gpu_steps_per_run * t_step
     sample_s = t_ref_layer + reps * (t_step_layer + t_head)
-    return {"value": round(committed_per_run / t_run, 4), "unit": "tokens/s", "cores": int(threads),
-            "kind": "oracle",
+    return {**base, "value": round(committed_per_run / t_run, 4),
             "sample": (f"fp64 NumPy oracle: 1 of {nl} layers of the full refresh "
                        f"({run.L} rows, {t_ref_layer:.2f} s); {reps} window steps of 1 layer "
                        f"({hi - lo} rows, {t_step_layer:.2f} s each) with the LM head + vocab "
