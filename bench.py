@@ -466,6 +466,40 @@ def traffic_record(k_fetch, k_write, c_fetch, c_write, commands):
             "commands": commands}
 
 
+def step_only(wc, w, req, n_steps):
+    """One block refresh and n_steps eager denoise+commit steps of the
+    workload (no graph), for counter runs: the difference of two such runs
+    with different n_steps is the per-step traffic of the step's kernels."""
+    import torch
+    from diffusion_vicinity_kv_amd.engine import Engine
+    max_len = req["tokens"].shape[1]
+    eng = Engine(wc.model, wc.decode, w, wc.batch, max_len, graph_unroll=0)
+    tokens = req["tokens"].cuda().contiguous()
+    rb = req.get("router_bias")
+    eng.set_batch(tokens, req["prompt_len"].tolist(), req["gen_len"].tolist(),
+                  req["plant_id"].cuda().contiguous(), req["plant_bias"].cuda().contiguous(),
+                  None if rb is None else rb.cuda().contiguous())
+    eng.refresh_kv()
+    for _ in range(n_steps):
+        eng.denoise_step()
+        eng.commit()
+    torch.cuda.synchronize()
+    eng.close()
+
+
+def counter_totals(paths):
+    """Sum of each counter over every dispatch of rocprofv3 counter CSVs
+    (KiB for FETCH_SIZE / WRITE_SIZE), with the dispatch count."""
+    import csv
+    tot, n = {}, {}
+    for path in paths:
+        for r in csv.DictReader(open(path)):
+            c = r["Counter_Name"]
+            tot[c] = tot.get(c, 0.0) + float(r["Counter_Value"])
+            n[c] = n.get(c, 0) + 1
+    return {c: {"sum": tot[c], "dispatches": n[c]} for c in tot}
+
+
 def run_expert_sweep(wc, w, slot_list, intervals, blocks, unroll):
     """TIDE-style expert cache on the MoE workload: the first `blocks` blocks
     of its request with `slots` experts per layer in HBM and the rest read
@@ -573,7 +607,16 @@ def main():
                     help="write the dominant kernel's HBM traffic record from the counter CSVs of "
                          "--kernel-only and --calib-copy runs (no GPU work)")
     ap.add_argument("--traffic-out", default=TRAFFIC_FILE)
+    ap.add_argument("--step-only", type=int, default=0,
+                    help="one block refresh and this many eager denoise+commit steps of the "
+                         "workload, nothing else (counter runs)")
+    ap.add_argument("--counter-totals", nargs="+", default=None,
+                    help="print each counter's sum over every dispatch of these rocprofv3 counter "
+                         "CSVs (no GPU work)")
     args = ap.parse_args()
+    if args.counter_totals:
+        print(json.dumps(counter_totals(args.counter_totals)))
+        return
     if args.trace_summary:
         print(trace_summary(args.trace_summary))
         return
@@ -620,6 +663,12 @@ def main():
     w = synth.make_weights(m, wc.seed, device="cuda")
     req = synth.make_requests(wc)
     torch.cuda.synchronize()
+
+    if args.step_only:
+        log(f"[bench] step-only: refresh + {args.step_only} eager steps")
+        step_only(wc, w, req, args.step_only)
+        log("[bench] step-only done")
+        return
 
     if args.kernel_only:
         avg_ms, avg_bytes, _, rows = dominant_kernel_timing(wc, w, iters=64)
