@@ -38,9 +38,21 @@ namespace dinfer {
 namespace {
 
 constexpr float kSlack = 8.f;
+
+// The probabilities' operand of O^T += V^T P^T: hi + lo halves like the
+// queries (PLO), or bf16(p) alone (a precision option: one MFMA per V
+// fragment instead of two).
+template <typename T, bool PLO> struct ProbOperand : SplitOperand<T> {};
+template <> struct ProbOperand<bf16, false> {
+  static constexpr int PARTS = 1;
+  __device__ __forceinline__ static void make(const float* src, V16* out) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) out[0].b[i] = static_cast<bf16>(src[i]);
+  }
+};
 constexpr int kKeyGroups = 2;   // groups of four waves taking alternate steps
 
-template <typename T, int HD, int QTW>
+template <typename T, int HD, int QTW, bool PLO>
 __global__ __launch_bounds__(256 * kKeyGroups) void attn_kernel(
     PassTable tb, int q_blocks, int keys_per_split, int n_split, int m_cap,
     const float* __restrict__ q, const T* __restrict__ kc, const T* __restrict__ vt, int H,
@@ -48,12 +60,14 @@ __global__ __launch_bounds__(256 * kKeyGroups) void attn_kernel(
     float* __restrict__ out) {
   using MF = Mfma<T>;
   using SO = SplitOperand<T>;
+  using SP = ProbOperand<T, PLO>;
   constexpr int VEC = MF::VEC;
   constexpr int KS = MF::KSTEP;        // keys per step
   constexpr int NTS = KS / 16;         // 16-key score tiles per step
   constexpr int QV = HD / KS;          // vector steps over the head dim
   constexpr int HT = HD / 16;          // 16-row output tiles over the head dim
   constexpr int PL = SO::PARTS;
+  constexpr int PP = SP::PARTS;       // parts of the probabilities (B of O^T)
   constexpr int QB = 64 * QTW;         // queries per workgroup
   constexpr int NK = NTS * QV;         // K fragments per step
   constexpr int NF = NK + HT;          // K and V fragments per step
@@ -170,7 +184,7 @@ __global__ __launch_bounds__(256 * kKeyGroups) void attn_kernel(
 #pragma unroll
           for (int p = 0; p < PL; ++p) MF::mac(sc[u][t], kf, qf[u][kk][p]);
       }
-    V16 pf[QTW][PL];
+    V16 pf[QTW][PP];
 #pragma unroll
     for (int u = 0; u < QTW; ++u) {
       // lane (query lc, group lg) holds keys kb + lg*VEC + e, e = 4t + i
@@ -202,7 +216,7 @@ __global__ __launch_bounds__(256 * kKeyGroups) void attn_kernel(
         pv[e] = exp2f(pv[e] - m_run[u]);
         l_run[u] += pv[e];
       }
-      SO::make(pv, pf[u]);
+      SP::make(pv, pf[u]);
     }
 #pragma unroll
     for (int ht = 0; ht < HT; ++ht) {
@@ -210,7 +224,7 @@ __global__ __launch_bounds__(256 * kKeyGroups) void attn_kernel(
 #pragma unroll
       for (int u = 0; u < QTW; ++u)
 #pragma unroll
-        for (int p = 0; p < PL; ++p) MF::mac(o[u][ht], vf, pf[u][p]);
+        for (int p = 0; p < PP; ++p) MF::mac(o[u][ht], vf, pf[u][p]);
     }
   };
 
@@ -437,13 +451,13 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(PassTable tb, int keys_
   *reinterpret_cast<float4*>(out + (size_t)m * H * HD + i4 * 4) = res;
 }
 
-template <typename T, int HD, int QTW>
+template <typename T, int HD, int QTW, bool PLO>
 hipError_t run(const AttnPlan& p, PassTable tb, int batch, int m_cap, const float* q,
                const void* kc, const void* vt, int H, int Lp, float* o_part, float* ml_part,
                float* o, hipStream_t st) {
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)HD);
   dim3 grid(p.n_split, H, batch * p.q_blocks);
-  hipLaunchKernelGGL((attn_kernel<T, HD, QTW>), grid, dim3(256 * kKeyGroups), 0, st, tb,
+  hipLaunchKernelGGL((attn_kernel<T, HD, QTW, PLO>), grid, dim3(256 * kKeyGroups), 0, st, tb,
                      p.q_blocks,
                      p.keys_per_split, p.n_split, m_cap, q, static_cast<const T*>(kc),
                      static_cast<const T*>(vt), H, Lp, scale_log2, o_part, ml_part, o);
@@ -455,12 +469,12 @@ hipError_t run(const AttnPlan& p, PassTable tb, int batch, int m_cap, const floa
   return hipGetLastError();
 }
 
-template <typename T, int HD>
+template <typename T, int HD, bool PLO>
 hipError_t run_q(const AttnPlan& p, PassTable tb, int batch, int m_cap, const float* q,
                  const void* kc, const void* vt, int H, int Lp, float* o_part, float* ml_part,
                  float* o, hipStream_t st) {
-  if (p.qtw == 1) return run<T, HD, 1>(p, tb, batch, m_cap, q, kc, vt, H, Lp, o_part, ml_part, o, st);
-  if (p.qtw == 2) return run<T, HD, 2>(p, tb, batch, m_cap, q, kc, vt, H, Lp, o_part, ml_part, o, st);
+  if (p.qtw == 1) return run<T, HD, 1, PLO>(p, tb, batch, m_cap, q, kc, vt, H, Lp, o_part, ml_part, o, st);
+  if (p.qtw == 2) return run<T, HD, 2, PLO>(p, tb, batch, m_cap, q, kc, vt, H, Lp, o_part, ml_part, o, st);
   return hipErrorInvalidValue;
 }
 
@@ -495,14 +509,18 @@ AttnPlan plan_attention(int batch, int max_rows_per_req, int max_keys, int H, in
 
 hipError_t launch_attention(DType t, const AttnPlan& p, PassTable tb, int batch, int m_cap,
                             const float* q, const void* kc, const void* vt, int H, int hd,
-                            int Lp, float* o_part, float* ml_part, float* o, hipStream_t st) {
+                            int Lp, float* o_part, float* ml_part, float* o, hipStream_t st,
+                            bool p_lo) {
   if (Lp % 64 != 0 || p.keys_per_split % 32 != 0) return hipErrorInvalidValue;
   if (t == DType::F32) {
-    if (hd == 64) return run_q<float, 64>(p, tb, batch, m_cap, q, kc, vt, H, Lp, o_part, ml_part, o, st);
-    if (hd == 128) return run_q<float, 128>(p, tb, batch, m_cap, q, kc, vt, H, Lp, o_part, ml_part, o, st);
+    if (hd == 64) return run_q<float, 64, true>(p, tb, batch, m_cap, q, kc, vt, H, Lp, o_part, ml_part, o, st);
+    if (hd == 128) return run_q<float, 128, true>(p, tb, batch, m_cap, q, kc, vt, H, Lp, o_part, ml_part, o, st);
+  } else if (p_lo) {
+    if (hd == 64) return run_q<bf16, 64, true>(p, tb, batch, m_cap, q, kc, vt, H, Lp, o_part, ml_part, o, st);
+    if (hd == 128) return run_q<bf16, 128, true>(p, tb, batch, m_cap, q, kc, vt, H, Lp, o_part, ml_part, o, st);
   } else {
-    if (hd == 64) return run_q<bf16, 64>(p, tb, batch, m_cap, q, kc, vt, H, Lp, o_part, ml_part, o, st);
-    if (hd == 128) return run_q<bf16, 128>(p, tb, batch, m_cap, q, kc, vt, H, Lp, o_part, ml_part, o, st);
+    if (hd == 64) return run_q<bf16, 64, false>(p, tb, batch, m_cap, q, kc, vt, H, Lp, o_part, ml_part, o, st);
+    if (hd == 128) return run_q<bf16, 128, false>(p, tb, batch, m_cap, q, kc, vt, H, Lp, o_part, ml_part, o, st);
   }
   return hipErrorInvalidValue;
 }

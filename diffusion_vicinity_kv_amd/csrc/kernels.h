@@ -93,9 +93,12 @@ struct AttnPlan {
 // Padded cache length Lp of K [req][head][Lp][hd] and V^T [req][head][hd][Lp].
 int attn_cache_len(int max_len);
 AttnPlan plan_attention(int batch, int max_rows_per_req, int max_keys, int H, int target_wgs);
+// p_lo (bf16 caches): probabilities into the P V MFMA as hi + lo bf16 halves
+// (default), or as bf16(p) alone.
 hipError_t launch_attention(DType t, const AttnPlan& p, PassTable tb, int batch, int m_cap,
                             const float* q, const void* kc, const void* vt, int H, int hd,
-                            int Lp, float* o_part, float* ml_part, float* o, hipStream_t st);
+                            int Lp, float* o_part, float* ml_part, float* o, hipStream_t st,
+                            bool p_lo = true);
 
 // ---- vocab statistics ---------------------------------------------------------
 struct VocabPlan {

@@ -436,7 +436,8 @@ dinfer_status run_pass(dinfer_ctx* c, bool step) {
                                     c->at<float>(L.off_rope), q, kvk, kvv, L.Lp, st));
     if (!step && last) break;   // a refresh needs only the caches
     HIP_TRY(launch_attention(dt, ap, tb, L.max_batch, m_cap, q, kvk, kvv, L.H, L.hd, L.Lp,
-                             c->at<float>(L.off_ao), c->at<float>(L.off_aml), o, st));
+                             c->at<float>(L.off_ao), c->at<float>(L.off_aml), o, st,
+                             !(hi_only & 16u)));
     HIP_TRY(launch_gemm(go, dt, o, c->wo[l], part, tb.nrows, m_cap, d, d, st));
     HIP_TRY(launch_add_rmsnorm(dt, tb.nrows, m_cap, x, part, go.splits, stride_d, c->ffn_norm[l],
                                c->m.rms_eps, a, d, st));
@@ -1358,7 +1359,7 @@ dinfer_status dinfer_expert_cache_report(dinfer_ctx* c, dinfer_expert_cache_stat
 dinfer_status dinfer_set_activation_precision(dinfer_ctx* c, uint32_t step_mask,
                                               uint32_t refresh_mask) {
   if (!c) return fail(DINFER_E_ARG, "ctx is null");
-  if ((step_mask | refresh_mask) & ~0xFu) return fail(DINFER_E_ARG, "masks hold bits 0..3 only");
+  if ((step_mask | refresh_mask) & ~0x1Fu) return fail(DINFER_E_ARG, "masks hold bits 0..4 only");
   if (c->L.dt != DType::BF16 && (step_mask | refresh_mask))
     return fail(DINFER_E_UNSUPPORTED, "bf16-only activations need bf16 weights");
   if (c->graph && step_mask != c->hi_only_step) {

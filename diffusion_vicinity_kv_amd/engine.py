@@ -144,7 +144,8 @@ class Engine:
 
     def set_activation_precision(self, step_mask=0, refresh_mask=0):
         """dinfer_set_activation_precision: bit i (0 QKV, 1 O, 2 gate|up, 3 down)
-        = that projection takes bf16 activations alone instead of hi + lo."""
+        = that projection takes bf16 activations alone instead of hi + lo; bit
+        4 = the attention's probabilities likewise in its P V product."""
         B.check(self.lib.dinfer_set_activation_precision(self.ctx, int(step_mask),
                                                          int(refresh_mask)),
                 "dinfer_set_activation_precision")

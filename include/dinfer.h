@@ -374,9 +374,11 @@ dinfer_status dinfer_expert_cache_report(dinfer_ctx* ctx, dinfer_expert_cache_st
  * (for an MoE model: the shared expert's gate|up and down) -- takes its fp32
  * activations into the bf16 MFMA as bf16(a) alone, one MFMA per weight
  * fragment; clear means as hi = bf16(a) plus lo = bf16(a - hi), two MFMAs, so
- * that only the weights' rounding remains.  step_mask applies to
- * denoise_step, refresh_mask to refresh_kv.  DINFER_E_UNSUPPORTED with fp32
- * weights and a nonzero mask. */
+ * that only the weights' rounding remains.  Bit 4 does the same for the
+ * attention's probabilities in its P V product (the queries keep both
+ * halves).  step_mask applies to denoise_step, refresh_mask to refresh_kv.
+ * DINFER_E_ARG for bits above 4; DINFER_E_UNSUPPORTED with fp32 weights and
+ * a nonzero mask. */
 dinfer_status dinfer_set_activation_precision(dinfer_ctx* ctx, uint32_t step_mask,
                                               uint32_t refresh_mask);
 
