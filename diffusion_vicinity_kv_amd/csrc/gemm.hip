@@ -56,7 +56,8 @@ namespace {
 // VS = true (LM head): instead of storing the tile (or besides it, when out
 // is not null) the workgroup stages it in LDS and reduces every row of it to
 // its vocab record (vocab_common.h), rows numbered from vrow0.
-template <typename TW, int MT, int NT, int NW, bool GUARD, bool VS = false, bool LO = true>
+template <typename TW, int MT, int NT, int NW, bool GUARD, bool VS = false, bool LO = true,
+          int U = 4>
 __device__ __forceinline__ void skinny_tile(const float* __restrict__ A,
                                             const int* __restrict__ arow, int M,
                                             const TW* __restrict__ W, int N, int K,
@@ -68,14 +69,18 @@ __device__ __forceinline__ void skinny_tile(const float* __restrict__ A,
   constexpr int PL = AS::PLANES;
   constexpr int VEC = MF::VEC;
   constexpr int KSTEP = MF::KSTEP;
-  constexpr int U = 4;                          // vector steps per K chunk
-  constexpr int KC = U * KSTEP;                 // 128 (bf16) / 64 (fp32) K per chunk
+  // U vector steps per K chunk: KC = 128 (bf16, U 4) or 64 (U 2) K per
+  // chunk; the LDS rows keep the 128-element stride (+16 B) either way
+  constexpr int KC = U * KSTEP;
   constexpr int ROWS = 16 * MT;
-  constexpr int STR = KC + 16 / sizeof(TW);     // LDS row stride (+16 B)
+  constexpr int STR = 4 * KSTEP + 16 / sizeof(TW);
   constexpr int NTH = NW * 64;                  // threads per workgroup
   constexpr int F4R = KC / 4;                   // float4 of A per chunk row
-  constexpr int AV = ROWS * F4R / NTH;          // float4 of A per thread per chunk
-  static_assert(ROWS * F4R % NTH == 0, "activation chunk must split evenly");
+  constexpr int AF4 = ROWS * F4R;               // float4 of A per chunk
+  constexpr int AV = (AF4 + NTH - 1) / NTH;     // float4 of A per thread per chunk
+  // (when the threads do not divide the chunk, the surplus ones repeat its
+  // last float4: the same value to the same LDS address)
+  static_assert(U == 2 || U == 4, "two or four vector steps per chunk");
   __shared__ __attribute__((aligned(16))) TW As[2][PL][ROWS * STR];
 
   const int lane = threadIdx.x & 63;
@@ -120,7 +125,7 @@ __device__ __forceinline__ void skinny_tile(const float* __restrict__ A,
   auto load_a = [&](float4 (&areg)[AV], int c) {
 #pragma unroll
     for (int i = 0; i < AV; ++i) {
-      const int v = threadIdx.x + NTH * i;
+      const int v = AF4 % NTH ? min((int)threadIdx.x + NTH * i, AF4 - 1) : threadIdx.x + NTH * i;
       const int r = v / F4R;
       const int cv = v % F4R;
       const size_t ar = arow ? (size_t)arow[GUARD ? min(r, M - 1) : r] : (size_t)r;
@@ -134,7 +139,7 @@ __device__ __forceinline__ void skinny_tile(const float* __restrict__ A,
   auto store_a = [&](const float4 (&areg)[AV], int buf) {
 #pragma unroll
     for (int i = 0; i < AV; ++i) {
-      const int v = threadIdx.x + NTH * i;
+      const int v = AF4 % NTH ? min((int)threadIdx.x + NTH * i, AF4 - 1) : threadIdx.x + NTH * i;
       const int r = v / F4R;
       const int cv = v % F4R;
       AS::store4(&As[buf][0][r * STR + cv * 4], &As[buf][PL - 1][r * STR + cv * 4], areg[i]);
@@ -246,14 +251,14 @@ __device__ __forceinline__ void skinny_tile(const float* __restrict__ A,
   }
 }
 
-template <typename TW, int MT, int NT, int NW, bool GUARD, bool LO>
+template <typename TW, int MT, int NT, int NW, bool GUARD, bool LO, int U>
 __global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(const float* __restrict__ A,
                                                               const TW* __restrict__ W,
                                                               float* __restrict__ P,
                                                               const int* __restrict__ m_dev,
                                                               int m_cap, int N, int K,
                                                               int n_tiles, int S, int m_tiles) {
-  constexpr int KC = 4 * Mfma<TW>::KSTEP;
+  constexpr int KC = U * Mfma<TW>::KSTEP;
   constexpr int ROWS = 16 * MT;
   // work item (split, column group) = split * n_tiles + tile; its m_tiles row
   // tiles get workgroup ids 8 apart, so they run side by side on one XCD and
@@ -269,7 +274,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(const float* __res
   const int C = K / KC;
   const int M = (m_dev ? min(*m_dev, m_cap) : m_cap) - mt * ROWS;
   if (M <= 0) return;
-  skinny_tile<TW, MT, NT, NW, GUARD, false, LO>(A + (size_t)mt * ROWS * K, nullptr, min(M, ROWS), W, N, K,
+  skinny_tile<TW, MT, NT, NW, GUARD, false, LO, U>(A + (size_t)mt * ROWS * K, nullptr, min(M, ROWS), W, N, K,
                                      P + ((size_t)split * m_cap + (size_t)mt * ROWS) * N, N,
                                      tile * (16 * NT * NW), (split * C) / S, ((split + 1) * C) / S);
 }
@@ -355,19 +360,30 @@ __global__ __launch_bounds__(256) void pack_kernel(const TW* __restrict__ W, TW*
 }
 
 // ---------------------------------------------------------------------------
+// Vector steps per K chunk of a skinny projection: 64-element chunks (two
+// 32-element MFMA steps) for the eight-wave bf16 groups -- 32 KB of weights
+// per workgroup and chunk, 64 KB in flight two chunks ahead -- and 128 for
+// the rest.  Measured on the dense 8B window (64 rows): QKV 26.9 -> 24.5 us,
+// gate|up 49.3 -> 47.3 us; the four-wave O and down projections (128-column
+// groups, K 4096 and 12288) were 2% faster and 3% slower.
+template <typename TW, int NW> constexpr int skinny_u() {
+  return sizeof(TW) == 2 && NW == 8 ? 2 : 4;
+}
+
 template <typename TW, int MT, int NT, int NW, bool LO>
 hipError_t run_skinny(const GemmPlan& p, const float* A, const void* W, float* out,
                       const int* m_dev, int m_cap, int N, int K, hipStream_t st) {
+  constexpr int SU = skinny_u<TW, NW>();
   const int n_tiles = N / (16 * NT * NW);
   const int mtiles = p.mtiles > 1 ? p.mtiles : 1;
   if (m_cap > 16 * MT * mtiles) return hipErrorInvalidValue;
   const dim3 grid((n_tiles * p.splits + 7) / 8 * 8 * mtiles);
   if (p.guard)
-    hipLaunchKernelGGL((gemm_skinny_kernel<TW, MT, NT, NW, true, LO>), grid, dim3(NW * 64), 0, st, A,
+    hipLaunchKernelGGL((gemm_skinny_kernel<TW, MT, NT, NW, true, LO, SU>), grid, dim3(NW * 64), 0, st, A,
                        static_cast<const TW*>(W), out, m_dev, m_cap, N, K, n_tiles, p.splits,
                        mtiles);
   else
-    hipLaunchKernelGGL((gemm_skinny_kernel<TW, MT, NT, NW, false, LO>), grid, dim3(NW * 64), 0, st, A,
+    hipLaunchKernelGGL((gemm_skinny_kernel<TW, MT, NT, NW, false, LO, SU>), grid, dim3(NW * 64), 0, st, A,
                        static_cast<const TW*>(W), out, m_dev, m_cap, N, K, n_tiles, p.splits,
                        mtiles);
   return hipGetLastError();
