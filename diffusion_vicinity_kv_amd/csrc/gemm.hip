@@ -279,6 +279,18 @@ __global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(const float* __res
                                      tile * (16 * NT * NW), (split * C) / S, ((split + 1) * C) / S);
 }
 
+// Vector steps per K chunk of a skinny projection: 64-element chunks (two
+// 32-element MFMA steps) for the eight-wave bf16 groups -- 32 KB of weights
+// per workgroup and chunk, 64 KB in flight two chunks ahead -- and 128 for
+// the rest.  Measured on the dense 8B window (64 rows): QKV 26.9 -> 24.5 us,
+// gate|up 49.3 -> 47.3 us; the four-wave O and down projections (128-column
+// groups, K 4096 and 12288) were 2% faster and 3% slower.  The LM head and
+// the MoE grouped experts (eight-wave groups) take the same: dense step
+// 4.78 -> 4.76 ms, MoE step 5.09 -> 5.00 ms.
+template <typename TW, int NW> constexpr int skinny_u() {
+  return sizeof(TW) == 2 && NW == 8 ? 2 : 4;
+}
+
 // LM head: the skinny projection of the block rows over the whole
 // vocabulary (one K slice), each workgroup reducing its tile to vocab
 // records instead of storing logits (also stored when ve.logits is set).
@@ -286,7 +298,8 @@ template <typename TW, int MT, int NT, int NW, bool GUARD>
 __global__ __launch_bounds__(NW * 64) void gemm_skinny_lmhead_kernel(
     const float* __restrict__ A, const TW* __restrict__ W, const int* __restrict__ m_dev,
     int m_cap, int N, int K, int n_tiles, int m_tiles, VocabEpi ve) {
-  constexpr int KC = 4 * Mfma<TW>::KSTEP;
+  constexpr int SU = skinny_u<TW, NW>();
+  constexpr int KC = SU * Mfma<TW>::KSTEP;
   constexpr int ROWS = 16 * MT;
   const int bid = blockIdx.x;
   const int grp = bid / (8 * m_tiles);
@@ -296,7 +309,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_skinny_lmhead_kernel(
   if (tile >= n_tiles) return;
   const int M = (m_dev ? min(*m_dev, m_cap) : m_cap) - mt * ROWS;
   if (M <= 0) return;
-  skinny_tile<TW, MT, NT, NW, GUARD, true>(
+  skinny_tile<TW, MT, NT, NW, GUARD, true, true, SU>(
       A + (size_t)mt * ROWS * K, nullptr, min(M, ROWS), W, N, K,
       ve.logits ? ve.logits + (size_t)mt * ROWS * N : nullptr, N, tile * (16 * NT * NW), 0,
       K / KC, &ve, mt * ROWS);
@@ -317,7 +330,8 @@ __global__ __launch_bounds__(NW * 64) void gemm_grouped_kernel(
     const float* __restrict__ A, const int* __restrict__ row_of, const int* __restrict__ e_count,
     const int* __restrict__ e_off, const TW* const* __restrict__ Wtab, float* __restrict__ out,
     int N, int K, int n_tiles, int m_tiles, int n_pairs) {
-  constexpr int KC = 4 * Mfma<TW>::KSTEP;
+  constexpr int SU = skinny_u<TW, NW>();
+  constexpr int KC = SU * Mfma<TW>::KSTEP;
   const int bid = blockIdx.x;
   const int grp = bid / (8 * m_tiles);
   const int rem = bid % (8 * m_tiles);
@@ -332,7 +346,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_grouped_kernel(
   const int base = e_off[e] + mt * 64;
   const float* a = row_of ? A : A + (size_t)base * K;
   const int* ar = row_of ? row_of + base : nullptr;
-  skinny_tile<TW, 4, NT, NW, true>(a, ar, M, Wtab[e], N, K, out + (size_t)base * N, N,
+  skinny_tile<TW, 4, NT, NW, true, false, true, SU>(a, ar, M, Wtab[e], N, K, out + (size_t)base * N, N,
                                    tile * (16 * NT * NW), 0, K / KC);
 }
 
@@ -360,16 +374,6 @@ __global__ __launch_bounds__(256) void pack_kernel(const TW* __restrict__ W, TW*
 }
 
 // ---------------------------------------------------------------------------
-// Vector steps per K chunk of a skinny projection: 64-element chunks (two
-// 32-element MFMA steps) for the eight-wave bf16 groups -- 32 KB of weights
-// per workgroup and chunk, 64 KB in flight two chunks ahead -- and 128 for
-// the rest.  Measured on the dense 8B window (64 rows): QKV 26.9 -> 24.5 us,
-// gate|up 49.3 -> 47.3 us; the four-wave O and down projections (128-column
-// groups, K 4096 and 12288) were 2% faster and 3% slower.
-template <typename TW, int NW> constexpr int skinny_u() {
-  return sizeof(TW) == 2 && NW == 8 ? 2 : 4;
-}
-
 template <typename TW, int MT, int NT, int NW, bool LO>
 hipError_t run_skinny(const GemmPlan& p, const float* A, const void* W, float* out,
                       const int* m_dev, int m_cap, int N, int K, hipStream_t st) {
