@@ -43,6 +43,12 @@ def test_call_order_errors_leave_the_context_usable(unroll):
     P, G = req["prompt_len"].tolist(), req["gen_len"].tolist()
     pid, pb = req["plant_id"].cuda().contiguous(), req["plant_bias"].cuda().contiguous()
     eng.set_batch(tokens, P, G, pid, pb)
+    # precision options: bits above 4 are rejected; an fp32 model has no
+    # bf16-only option (both leave the default precision in place)
+    assert _status(eng.set_activation_precision, 32, 0) == B.E_ARG
+    assert _status(eng.set_activation_precision, 0, 1 << 31) == B.E_ARG
+    assert _status(eng.set_activation_precision, 16, 16) == B.E_UNSUPPORTED
+    eng.set_activation_precision(0, 0)
     # bound but nothing refreshed
     assert _status(eng.denoise_step) == B.E_STATE
     assert _status(eng.commit) == B.E_STATE
