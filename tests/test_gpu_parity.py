@@ -477,3 +477,28 @@ def test_linear_parity(M, N, K, dt):
     want = A.cpu().double().numpy() @ W.cpu().double().numpy().T
     err = np.max(np.abs(got - want)) / np.sqrt(np.mean(want ** 2))
     assert err < 3e-5, err
+
+
+@pytest.mark.parametrize("unroll", [0, 4])
+def test_empty_prompt_matches_oracle(unroll):
+    """A request with no prompt at all (prompt_len 0: the first block starts
+    at position 0, its vicinity window clipped at the sequence start, and
+    the cache holds only MASK rows at the first refresh), fp32: step by step
+    against the oracle (logits at 1e-5 * RMS, every decision), then a whole
+    run, eager and from step graphs."""
+    note(f"tiny fp32, empty prompt, unroll={unroll}")
+    wc = small_workload(prompt=(0, 0), gen=96, alpha=0.3, seed=21)
+    eng, w, req, tokens = build(wc, graph_unroll=unroll)
+    assert int(req["prompt_len"][0]) == 0
+    if unroll == 0:
+        runs = oracle_runs(wc, w, req)
+        rep = lockstep(wc, eng, tokens, runs, logit_tol=1e-5, check_cache=True)
+        note(f"  {rep}")
+        assert rep["diverged"] is None and all(getattr(r, "_finished", False) for r in runs)
+    else:
+        stats = eng.run_to_completion()
+        torch.cuda.synchronize()
+        run = oracle.run_request(wc.model, wc.decode, w, req)
+        assert np.array_equal(tokens.cpu().numpy()[0][: run.L], run.tokens)
+        assert stats["committed"] == wc.gen_len
+    eng.close()
