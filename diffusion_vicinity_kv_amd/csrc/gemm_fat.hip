@@ -80,8 +80,22 @@ __attribute__((amdgpu_waves_per_eu(1, WN / 2))) void gemm_fat_kernel(const float
   auto& Bs = *reinterpret_cast<TW(*)[2][kFatN * STR]>(smem + kAsBytes);
 
   const int M = m_dev ? min(*m_dev, m_cap) : m_cap;
-  const int m0 = blockIdx.y * kFatM;
-  const int n0 = blockIdx.x * kFatN;
+  // The LM head's grid is one-dimensional: the row tiles of a column tile
+  // get workgroup ids 8 apart, so they run side by side on one XCD and read
+  // the tile's weights from HBM once (its column tiles are not a multiple of
+  // 8: in a 2-D grid the row tiles of a column would fall on different XCDs,
+  // rounds apart, and the 1 GB head would stream once per row tile).
+  int bx = blockIdx.x, by = blockIdx.y;
+  if constexpr (VS) {
+    const int mtiles = (m_cap + kFatM - 1) / kFatM;
+    const int grp = blockIdx.x / (8 * mtiles);
+    const int rem = blockIdx.x % (8 * mtiles);
+    by = rem / 8;
+    bx = grp * 8 + rem % 8;
+    if (bx * kFatN >= N) return;
+  }
+  const int m0 = by * kFatM;
+  const int n0 = bx * kFatN;
   if (m0 >= M) return;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -208,7 +222,7 @@ __attribute__((amdgpu_waves_per_eu(1, WN / 2))) void gemm_fat_kernel(const float
       __syncthreads();
       const int r0 = m0 + h * RP;
       if (r0 < M)
-        vocab::tile_records<kFatN, 2 * WN>(zt, LDZ, min(RP, M - r0), r0, n0, N, blockIdx.x,
+        vocab::tile_records<kFatN, 2 * WN>(zt, LDZ, min(RP, M - r0), r0, n0, N, bx,
                                            ve.n_tiles, ve.row_plant_id, ve.row_plant_bias,
                                            ve.mask_id, ve.rec_f, ve.rec_i);
     }
@@ -233,7 +247,9 @@ hipError_t fat_launch(DType t, int wn, int splits, const float* A, const void* W
                       hipStream_t st) {
   const int bk = t == DType::F32 ? 16 * kFatKK<float> : 32 * kFatKK<bf16>;   // K per slab
   if ((wn != 2 && wn != 4) || splits < 1 || splits > K / bk) return hipErrorInvalidValue;
-  const dim3 grid((N + 64 * wn - 1) / (64 * wn), (m_cap + kFatM - 1) / kFatM, splits);
+  const int n_tiles = (N + 64 * wn - 1) / (64 * wn), m_tiles = (m_cap + kFatM - 1) / kFatM;
+  const dim3 grid = VS ? dim3((n_tiles + 7) / 8 * 8 * m_tiles, 1, 1)   // see the kernel
+                       : dim3(n_tiles, m_tiles, splits);
   if (t == DType::F32) {
     if (wn == 4)
       hipLaunchKernelGGL((gemm_fat_kernel<float, 4, VS, true>), grid, dim3(512), 0, st, A,
