@@ -340,11 +340,14 @@ dinfer_status dinfer_run_to_completion(dinfer_ctx* ctx, int32_t max_steps,
  * afterwards (they may be NULL there, both arrays, if this call follows
  * before the first refresh).  Initially experts 0..slots-1 are resident.
  * Placement: per layer, the `slots` experts with the most row assignments
- * since the last placement (ties: the resident one, then the lower id) are
- * copied into the slots of the experts they replace (on the context's stream,
- * in order with the kernels).  dinfer_run_to_completion places after every
- * block-start refresh and, with interval > 0, every `interval` steps (rounded
- * up to whole graph replays); dinfer_expert_place does it on demand (waits
+ * since the last block-start placement (ties: the resident one, then the
+ * lower id) are copied into the slots of the experts they replace (on the
+ * context's stream, in order with the kernels).  dinfer_run_to_completion
+ * places after every block-start refresh (ranking by that refresh's routing
+ * and the steps before it, then restarting the counts) and, with
+ * interval > 0, every `interval` steps inside a block (rounded up to whole
+ * graph replays; ranking by everything the block has routed so far, counts
+ * kept); dinfer_expert_place does a block-start placement on demand (waits
  * for the stream).  DINFER_E_STATE if called twice; DINFER_E_WORKSPACE for a
  * bad slot buffer; DINFER_E_ARG for a dense model or memory that is not
  * pinned host memory. */
