@@ -39,10 +39,36 @@ namespace {
 
 constexpr float kSlack = 8.f;
 
+// 2^x by the hardware instruction alone; results below 2^-126 come out as
+// zero (exp2f adds a rescaling step per call for them).  A probability that
+// small, next to a row maximum of at least 1, changes no sum in fp32.
+__device__ __forceinline__ float exp2_ftz(float x) { return __builtin_amdgcn_exp2f(x); }
+
 // The probabilities' operand of O^T += V^T P^T: hi + lo halves like the
 // queries (PLO), or bf16(p) alone (a precision option: one MFMA per V
 // fragment instead of two).
 template <typename T, bool PLO> struct ProbOperand : SplitOperand<T> {};
+template <> struct ProbOperand<bf16, true> {
+  static constexpr int PARTS = 2;
+  // per pair of probabilities: one packed conversion gives both hi halves;
+  // each hi half, widened back, leaves the remainder that the second packed
+  // conversion rounds to the lo halves
+  __device__ __forceinline__ static void make(const float* src, V16* out) {
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+    unsigned hw[4], lw[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const f2 x = {src[2 * i], src[2 * i + 1]};
+      hw[i] = __builtin_bit_cast(unsigned, __builtin_convertvector(x, b2));
+      const f2 hx = {__builtin_bit_cast(float, hw[i] << 16),
+                     __builtin_bit_cast(float, hw[i] & 0xffff0000u)};
+      lw[i] = __builtin_bit_cast(unsigned, __builtin_convertvector(x - hx, b2));
+    }
+    out[0].u = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+    out[1].u = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+  }
+};
 template <> struct ProbOperand<bf16, false> {
   static constexpr int PARTS = 1;
   __device__ __forceinline__ static void make(const float* src, V16* out) {
@@ -91,8 +117,11 @@ __global__ __launch_bounds__(256 * kKeyGroups) void attn_kernel(
   const int n_steps = (k1 - k0 + KS - 1) / KS;
 
   const int lane = threadIdx.x & 63;
-  const int kg = threadIdx.x >> 8;             // key group: steps kg, kg + KG, ...
-  const int wave = (threadIdx.x >> 6) & 3;     // query tile(s) within the block
+  // wave-uniform indices read as scalars: the step's key base, its range
+  // test and the fragment addresses then take scalar instructions, not the
+  // vector ALUs the softmax needs
+  const int kg = __builtin_amdgcn_readfirstlane(threadIdx.x >> 8);   // key group: steps kg, kg + KG, ...
+  const int wave = __builtin_amdgcn_readfirstlane((threadIdx.x >> 6) & 3);   // query tile(s)
   const int lc = lane & 15;
   const int lg = lane >> 4;
   const int d = H * HD;
@@ -115,10 +144,11 @@ __global__ __launch_bounds__(256 * kKeyGroups) void attn_kernel(
         const float4 x = qvalid[u] ? *reinterpret_cast<const float4*>(
                                          q + (size_t)qrow[u] * d + h * HD + kk * KS + lg * VEC + e)
                                    : make_float4(0.f, 0.f, 0.f, 0.f);
-        qv[e] = x.x;
-        qv[e + 1] = x.y;
-        qv[e + 2] = x.z;
-        qv[e + 3] = x.w;
+        // scaled into the log2 domain here, once, instead of every score
+        qv[e] = x.x * scale_log2;
+        qv[e + 1] = x.y * scale_log2;
+        qv[e + 2] = x.z * scale_log2;
+        qv[e + 3] = x.w * scale_log2;
       }
       SO::make(qv, qf[u][kk]);
     }
@@ -135,27 +165,37 @@ __global__ __launch_bounds__(256 * kKeyGroups) void attn_kernel(
   }
 
   const size_t head = (size_t)r * H + h;
-  const T* kbase = kc + head * Lp * HD + lg * VEC;
-  const T* vbase = vt + head * Lp * HD + lc * 32 + lg * VEC;   // tile-major V^T
   // score-tile row j of tile t holds key key_of(t, j) of the step
   const int krow0 = NTS == 2 ? 8 * (lc >> 2) + (lc & 3) : lc;
 
   // fragment f of a step, as lane `lane` holds it: f < NK is K tile t = f /
-  // QV, head-dim step kk = f % QV; the rest are V^T row tiles ht = f - NK
-  // The K or V address of a fragment is selected, not branched on: with a
-  // branch per load (the fragment index depends on the wave) every load sits
-  // in a block of its own and the wait counts at the joins drain the whole
-  // prefetch at each step.
+  // QV, head-dim step kk = f % QV; the rest are V^T row tiles ht = f - NK.
+  // A wave loads fragments of one kind only, so its lane's offset within a
+  // fragment is fixed (one register) and each load adds it to a scalar
+  // address.  Keys of the step past the range are read (every row below Lp
+  // is inside the cache, and finite: zeroed at set-up, written with keys
+  // since) and masked out of the scores.
+  static_assert(NK % FW == 0, "a wave's fragments are all K or all V");
+  const bool loads_k = wave * FW < NK;
+  const unsigned lane_off =
+      (unsigned)(loads_k ? krow0 * HD + lg * VEC : lc * 32 + lg * VEC) * sizeof(T);
+  const T* kv_head = (loads_k ? kc : vt) + head * Lp * HD;
+  int frag_off[FW];                            // a fragment's offset within its step
+#pragma unroll
+  for (int j = 0; j < FW; ++j) {
+    const int f = wave * FW + j;
+    frag_off[j] = loads_k ? 4 * (f / QV) * HD + (f % QV) * KS : (f - NK) * 16 * 32;
+  }
   auto load = [&](V16 (&reg)[FW], int i) {     // this group's local step i
     const int kb = k0 + min(kg + i * KG, n_steps - 1) * KS;   // past the end: repeat the last
+    // K rows kb.. start at kb * HD; so does the V^T tile of kb when a step
+    // is a whole tile (KS 32), else (KS 16) it starts inside one
+    const size_t step_off =
+        KS == 32 || loads_k ? (size_t)kb * HD : (size_t)(kb >> 5) * HD * 32 + (kb & 31);
+    const T* sbase = kv_head + step_off;
 #pragma unroll
-    for (int i = 0; i < FW; ++i) {
-      const int f = wave * FW + i;
-      const int key = min(kb + krow0 + 4 * (f / QV), L - 1);   // rows past the range are masked
-      const T* kp = kbase + (size_t)key * HD + (f % QV) * KS;
-      const T* vp = vbase + (size_t)(kb >> 5) * HD * 32 + (f - NK) * 16 * 32 + (kb & 31);
-      reg[i] = ld16(f < NK ? kp : vp);
-    }
+    for (int j = 0; j < FW; ++j)
+      reg[j] = ld16(reinterpret_cast<const char*>(sbase + frag_off[j]) + lane_off);
   };
   auto store = [&](const V16 (&reg)[FW], int buf) {
 #pragma unroll
@@ -184,26 +224,34 @@ __global__ __launch_bounds__(256 * kKeyGroups) void attn_kernel(
 #pragma unroll
           for (int p = 0; p < PL; ++p) MF::mac(sc[u][t], kf, qf[u][kk][p]);
       }
+    // lane (query lc, group lg) holds keys kb + lg*VEC + e, e = 4t + i; keys
+    // past the range occur only in a split's last step
+    if (kb + KS > k1) {
+#pragma unroll
+      for (int u = 0; u < QTW; ++u)
+#pragma unroll
+        for (int t = 0; t < NTS; ++t)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (kb + lg * VEC + 4 * t + i >= k1) sc[u][t][i] = -INFINITY;
+    }
     V16 pf[QTW][PP];
 #pragma unroll
     for (int u = 0; u < QTW; ++u) {
-      // lane (query lc, group lg) holds keys kb + lg*VEC + e, e = 4t + i
       float pv[VEC];
       float mloc = -INFINITY;
 #pragma unroll
       for (int t = 0; t < NTS; ++t)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int e = 4 * t + i;
-          const float v = kb + lg * VEC + e < k1 ? sc[u][t][i] * scale_log2 : -INFINITY;
-          pv[e] = v;
-          mloc = fmaxf(mloc, v);
+          pv[4 * t + i] = sc[u][t][i];
+          mloc = fmaxf(mloc, sc[u][t][i]);
         }
       if (__any(mloc > m_run[u] + kSlack)) {      // wave-uniform: raise the scale
         float mx = fmaxf(mloc, __shfl_xor(mloc, 16, 64));
         mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
         const float m_new = fmaxf(m_run[u], mx);  // finite after the first step
-        const float alpha = exp2f(m_run[u] - m_new);
+        const float alpha = exp2_ftz(m_run[u] - m_new);
         l_run[u] *= alpha;
 #pragma unroll
         for (int ht = 0; ht < HT; ++ht)
@@ -213,7 +261,7 @@ __global__ __launch_bounds__(256 * kKeyGroups) void attn_kernel(
       }
 #pragma unroll
       for (int e = 0; e < VEC; ++e) {
-        pv[e] = exp2f(pv[e] - m_run[u]);
+        pv[e] = exp2_ftz(pv[e] - m_run[u]);
         l_run[u] += pv[e];
       }
       SP::make(pv, pf[u]);
