@@ -83,7 +83,7 @@ __global__ __launch_bounds__(256 * kKeyGroups) void attn_kernel(
     PassTable tb, int q_blocks, int keys_per_split, int n_split, int m_cap,
     const float* __restrict__ q, const T* __restrict__ kc, const T* __restrict__ vt, int H,
     int Lp, float scale_log2, float* __restrict__ o_part, float* __restrict__ ml_part,
-    float* __restrict__ out) {
+    float* __restrict__ out, size_t o_aps) {
   using MF = Mfma<T>;
   using SO = SplitOperand<T>;
   using SP = ProbOperand<T, PLO>;
@@ -365,12 +365,18 @@ __global__ __launch_bounds__(256 * kKeyGroups) void attn_kernel(
     if (!qvalid[u]) continue;
     if (n_split == 1) {
       const float inv = 1.f / l_run[u];
-      float* orow = out + (size_t)qrow[u] * d + h * HD;
+      const size_t ro = (size_t)qrow[u] * d + h * HD;
 #pragma unroll
-      for (int ht = 0; ht < HT; ++ht)
-        *reinterpret_cast<float4*>(orow + ht * 16 + lg * 4) =
-            make_float4(o[u][ht][0] * inv, o[u][ht][1] * inv, o[u][ht][2] * inv,
-                        o[u][ht][3] * inv);
+      for (int ht = 0; ht < HT; ++ht) {
+        const float4 y = make_float4(o[u][ht][0] * inv, o[u][ht][1] * inv, o[u][ht][2] * inv,
+                                     o[u][ht][3] * inv);
+        if (o_aps) {
+          bf16* hi = reinterpret_cast<bf16*>(out) + ro + ht * 16 + lg * 4;
+          store_hi_lo4(hi, hi + o_aps, y);
+        } else {
+          *reinterpret_cast<float4*>(out + ro + ht * 16 + lg * 4) = y;
+        }
+      }
     } else {
       const size_t base = ((size_t)split * m_cap + qrow[u]) * H + h;
       float* op = o_part + base * HD;
@@ -461,7 +467,8 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(PassTable tb, int keys_
                                                          int n_split, int m_cap,
                                                          const float* __restrict__ o_part,
                                                          const float* __restrict__ ml_part,
-                                                         int H, float* __restrict__ out) {
+                                                         int H, float* __restrict__ out,
+                                                         size_t o_aps) {
   const int m = blockIdx.x;                    // < m_cap: every row's records are readable
   const int i4 = blockIdx.y * 256 + threadIdx.x;
   if (i4 * 4 >= H * HD) return;
@@ -496,33 +503,38 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(PassTable tb, int keys_
     }
   }
   if (!valid) return;
-  *reinterpret_cast<float4*>(out + (size_t)m * H * HD + i4 * 4) = res;
+  if (o_aps) {
+    bf16* hi = reinterpret_cast<bf16*>(out) + (size_t)m * H * HD + i4 * 4;
+    store_hi_lo4(hi, hi + o_aps, res);
+  } else {
+    *reinterpret_cast<float4*>(out + (size_t)m * H * HD + i4 * 4) = res;
+  }
 }
 
 template <typename T, int HD, int QTW, bool PLO>
 hipError_t run(const AttnPlan& p, PassTable tb, int batch, int m_cap, const float* q,
                const void* kc, const void* vt, int H, int Lp, float* o_part, float* ml_part,
-               float* o, hipStream_t st) {
+               float* o, hipStream_t st, size_t o_aps) {
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)HD);
   dim3 grid(p.n_split, H, batch * p.q_blocks);
   hipLaunchKernelGGL((attn_kernel<T, HD, QTW, PLO>), grid, dim3(256 * kKeyGroups), 0, st, tb,
                      p.q_blocks,
                      p.keys_per_split, p.n_split, m_cap, q, static_cast<const T*>(kc),
-                     static_cast<const T*>(vt), H, Lp, scale_log2, o_part, ml_part, o);
+                     static_cast<const T*>(vt), H, Lp, scale_log2, o_part, ml_part, o, o_aps);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.n_split == 1) return e;
   const int blocks_y = (H * HD / 4 + 255) / 256;
   hipLaunchKernelGGL((attn_merge_kernel<HD>), dim3(m_cap, blocks_y), dim3(256), 0, st, tb,
-                     p.keys_per_split, p.n_split, m_cap, o_part, ml_part, H, o);
+                     p.keys_per_split, p.n_split, m_cap, o_part, ml_part, H, o, o_aps);
   return hipGetLastError();
 }
 
 template <typename T, int HD, bool PLO>
 hipError_t run_q(const AttnPlan& p, PassTable tb, int batch, int m_cap, const float* q,
                  const void* kc, const void* vt, int H, int Lp, float* o_part, float* ml_part,
-                 float* o, hipStream_t st) {
-  if (p.qtw == 1) return run<T, HD, 1, PLO>(p, tb, batch, m_cap, q, kc, vt, H, Lp, o_part, ml_part, o, st);
-  if (p.qtw == 2) return run<T, HD, 2, PLO>(p, tb, batch, m_cap, q, kc, vt, H, Lp, o_part, ml_part, o, st);
+                 float* o, hipStream_t st, size_t o_aps) {
+  if (p.qtw == 1) return run<T, HD, 1, PLO>(p, tb, batch, m_cap, q, kc, vt, H, Lp, o_part, ml_part, o, st, o_aps);
+  if (p.qtw == 2) return run<T, HD, 2, PLO>(p, tb, batch, m_cap, q, kc, vt, H, Lp, o_part, ml_part, o, st, o_aps);
   return hipErrorInvalidValue;
 }
 
@@ -558,17 +570,17 @@ AttnPlan plan_attention(int batch, int max_rows_per_req, int max_keys, int H, in
 hipError_t launch_attention(DType t, const AttnPlan& p, PassTable tb, int batch, int m_cap,
                             const float* q, const void* kc, const void* vt, int H, int hd,
                             int Lp, float* o_part, float* ml_part, float* o, hipStream_t st,
-                            bool p_lo) {
+                            bool p_lo, size_t o_aps) {
   if (Lp % 64 != 0 || p.keys_per_split % 32 != 0) return hipErrorInvalidValue;
   if (t == DType::F32) {
-    if (hd == 64) return run_q<float, 64, true>(p, tb, batch, m_cap, q, kc, vt, H, Lp, o_part, ml_part, o, st);
-    if (hd == 128) return run_q<float, 128, true>(p, tb, batch, m_cap, q, kc, vt, H, Lp, o_part, ml_part, o, st);
+    if (hd == 64) return run_q<float, 64, true>(p, tb, batch, m_cap, q, kc, vt, H, Lp, o_part, ml_part, o, st, o_aps);
+    if (hd == 128) return run_q<float, 128, true>(p, tb, batch, m_cap, q, kc, vt, H, Lp, o_part, ml_part, o, st, o_aps);
   } else if (p_lo) {
-    if (hd == 64) return run_q<bf16, 64, true>(p, tb, batch, m_cap, q, kc, vt, H, Lp, o_part, ml_part, o, st);
-    if (hd == 128) return run_q<bf16, 128, true>(p, tb, batch, m_cap, q, kc, vt, H, Lp, o_part, ml_part, o, st);
+    if (hd == 64) return run_q<bf16, 64, true>(p, tb, batch, m_cap, q, kc, vt, H, Lp, o_part, ml_part, o, st, o_aps);
+    if (hd == 128) return run_q<bf16, 128, true>(p, tb, batch, m_cap, q, kc, vt, H, Lp, o_part, ml_part, o, st, o_aps);
   } else {
-    if (hd == 64) return run_q<bf16, 64, false>(p, tb, batch, m_cap, q, kc, vt, H, Lp, o_part, ml_part, o, st);
-    if (hd == 128) return run_q<bf16, 128, false>(p, tb, batch, m_cap, q, kc, vt, H, Lp, o_part, ml_part, o, st);
+    if (hd == 64) return run_q<bf16, 64, false>(p, tb, batch, m_cap, q, kc, vt, H, Lp, o_part, ml_part, o, st, o_aps);
+    if (hd == 128) return run_q<bf16, 128, false>(p, tb, batch, m_cap, q, kc, vt, H, Lp, o_part, ml_part, o, st, o_aps);
   }
   return hipErrorInvalidValue;
 }

@@ -90,6 +90,20 @@ template <> struct SplitOperand<bf16> {
     }
   }
 };
+// Four fp32 values stored as bf16 hi halves (hi = bf16(v)) and lo halves
+// (lo = bf16(v - hi)), 8 bytes to each plane: the activation planes that the
+// bf16 GEMMs multiply (in LDS, or in memory when a producer writes them).
+__device__ __forceinline__ void store_hi_lo4(bf16* hi, bf16* lo, const float4& x) {
+  const float v[4] = {x.x, x.y, x.z, x.w};
+  bf16x4 h, l;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    h[i] = static_cast<bf16>(v[i]);
+    l[i] = static_cast<bf16>(v[i] - static_cast<float>(h[i]));
+  }
+  *reinterpret_cast<bf16x4*>(hi) = h;
+  *reinterpret_cast<bf16x4*>(lo) = l;
+}
 template <> struct SplitOperand<float> {
   static constexpr int PARTS = 1;
   __device__ __forceinline__ static void make(const float* src, V16* out) {

@@ -483,7 +483,8 @@ hipError_t dispatch(const GemmPlan& p, const float* A, const void* W, float* out
                     const int* m_dev, int m_cap, int N, int K, hipStream_t st) {
   if (p.kind == 1)
     return launch_gemm_fat(sizeof(TW) == 2 ? DType::BF16 : DType::F32, p.nw, p.splits, A, W,
-                           out, m_dev, m_cap, N, K, st, p.lo != 0);
+                           out, m_dev, m_cap, N, K, st, p.lo != 0, p.ap != 0);
+  if (p.ap) return hipErrorInvalidValue;   // planar activations: fat plans only
   if constexpr (sizeof(TW) == 2) {   // activations in bf16 only: a bf16-weight option
     if (!p.lo) return dispatch_lo<TW, false>(p, A, W, out, m_dev, m_cap, N, K, st);
   }

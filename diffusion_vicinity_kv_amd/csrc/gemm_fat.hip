@@ -3,6 +3,8 @@
 // activations, W [N][K] weights (fp32 or bf16) in the packed block layout of
 // launch_pack_linear, fp32 accumulation.  K splits (grid z) only even out the
 // last round of workgroups; their partials are summed by the consumer.
+#include <type_traits>
+
 #include "common.h"
 #include "gemm_split.h"
 #include "kernels.h"
@@ -39,13 +41,21 @@ template <typename TW> constexpr int kFatKK = 2;
 // The 128 KB of LDS admit one workgroup per CU (2 x WN / 4 waves per SIMD),
 // which leaves each wave up to 256 registers; saying so keeps the compiler
 // from squeezing into 128 by reloading the prefetched slabs just before use.
-template <typename TW, int WN, bool VS, bool LO>
+//
+// AP = true (bf16 weights): A holds the activations already split, as bf16 hi
+// and lo planes of [m_cap][K], the lo plane aps elements after the hi plane
+// (written by the producing kernel with store_hi_lo4: the bits the in-kernel
+// split would make).  Each 16-byte load is then one LDS chunk of a plane and
+// is stored unchanged -- no conversion in the slab loop, which every column
+// tile of a row tile would otherwise repeat.
+template <typename TW, int WN, bool VS, bool LO, bool AP = false>
 __global__ __launch_bounds__(128 * WN)
 __attribute__((amdgpu_waves_per_eu(1, WN / 2))) void gemm_fat_kernel(const float* __restrict__ A,
                                                             const TW* __restrict__ W,
                                                             float* __restrict__ Cout,
                                                             const int* __restrict__ m_dev,
-                                                            int m_cap, int N, int K, VocabEpi ve) {
+                                                            int m_cap, int N, int K, VocabEpi ve,
+                                                            size_t aps) {
   constexpr int kFatN = 64 * WN, kFatThreads = 128 * WN;
   using MF = Mfma<TW>;
   using AS = ASplit<TW, LO>;
@@ -66,8 +76,15 @@ __attribute__((amdgpu_waves_per_eu(1, WN / 2))) void gemm_fat_kernel(const float
   auto sw = [](int r, int e) {
     return r * STR + ((((e / CH) ^ (r / RS)) & (NC - 1)) * CH) + e % CH;
   };
+  static_assert(!AP || (sizeof(TW) == 2 && !VS), "activation planes: bf16 projections only");
   constexpr int F4R = BK / 4;                  // float4 of A per slab row
   constexpr int AV = kFatM * F4R / kFatThreads;     // float4 of A per thread per slab
+  // AP: 16-byte chunks (CH elements) of one plane; PL planes of kFatM rows
+  constexpr int APC = kFatM * NC;              // chunks of one plane per slab
+  constexpr int AU = AP ? PL * APC / kFatThreads : 1;   // chunks per thread per slab
+  static_assert(!AP || PL * APC % kFatThreads == 0, "plane chunks must split evenly");
+  using AReg = std::conditional_t<AP, V16, float4>;
+  constexpr int NA = AP ? AU : AV;             // activation registers per thread per slab
   constexpr int BE = 64 * VEC;                 // elements of one packed weight block
   constexpr int BV = (kFatN / 16) * KK * 64 / kFatThreads;   // W vectors per thread per slab
   static_assert((kFatN / 16) * KK * 64 % kFatThreads == 0, "weight slab must split evenly");
@@ -115,12 +132,24 @@ __attribute__((amdgpu_waves_per_eu(1, WN / 2))) void gemm_fat_kernel(const float
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  // row offsets of this thread's slab elements (fixed over K)
+  // row offsets of this thread's slab elements (fixed over K); with AP the
+  // thread's chunk i is plane v / APC, row (v % APC) / NC, chunk v % NC
   const float* arow[AV];
+  const TW* aprow[AU];
+  if constexpr (AP) {
+    const TW* Ab = reinterpret_cast<const TW*>(A);
 #pragma unroll
-  for (int i = 0; i < AV; ++i) {
-    const int v = threadIdx.x + kFatThreads * i;
-    arow[i] = A + (size_t)min(m0 + v / F4R, M - 1) * K + (v % F4R) * 4;
+    for (int i = 0; i < AU; ++i) {
+      const int v = threadIdx.x + kFatThreads * i;
+      aprow[i] = Ab + (v / APC) * aps + (size_t)min(m0 + (v % APC) / NC, M - 1) * K +
+                 (v % NC) * CH;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < AV; ++i) {
+      const int v = threadIdx.x + kFatThreads * i;
+      arow[i] = A + (size_t)min(m0 + v / F4R, M - 1) * K + (v % F4R) * 4;
+    }
   }
   // weight vector v of a slab: block v / 64 = (16-column group, vector step),
   // lane slot v % 64; the slab's blocks sit in LDS in that order
@@ -135,21 +164,34 @@ __attribute__((amdgpu_waves_per_eu(1, WN / 2))) void gemm_fat_kernel(const float
     wrow[i] = W + packed_block(grp, (v / 64) % KK, KS, NG) * BE + (v % 64) * VEC;
     wstep[i] = (size_t)KK * packed_kstride(grp, NG) * BE;
   }
-  auto gload = [&](float4 (&ra)[AV], V16 (&rb)[BV], int kt) {
+  auto gload = [&](AReg (&ra)[NA], V16 (&rb)[BV], int kt) {
     kt = kb + min(kt, nk - 1);   // past the end: repeat the last slab
+    if constexpr (AP) {
 #pragma unroll
-    for (int i = 0; i < AV; ++i) ra[i] = *reinterpret_cast<const float4*>(arow[i] + kt * BK);
+      for (int i = 0; i < AU; ++i) ra[i] = ld16(aprow[i] + kt * BK);
+    } else {
+#pragma unroll
+      for (int i = 0; i < AV; ++i) ra[i] = *reinterpret_cast<const float4*>(arow[i] + kt * BK);
+    }
 #pragma unroll
     for (int i = 0; i < BV; ++i) rb[i] = ld16(wrow[i] + kt * wstep[i]);
   };
-  auto sstore = [&](float4 (&ra)[AV], const V16 (&rb)[BV], int buf) {
-    hold_regs(ra);
+  auto sstore = [&](AReg (&ra)[NA], const V16 (&rb)[BV], int buf) {
+    if constexpr (AP) {
 #pragma unroll
-    for (int i = 0; i < AV; ++i) {
-      const int v = threadIdx.x + kFatThreads * i;
-      const int r = v / F4R;
-      const int cv = v % F4R;
-      AS::store4(&As[buf][0][sw(r, cv * 4)], &As[buf][PL - 1][sw(r, cv * 4)], ra[i]);
+      for (int i = 0; i < AU; ++i) {
+        const int v = threadIdx.x + kFatThreads * i;
+        st16(&As[buf][v / APC][sw((v % APC) / NC, (v % NC) * CH)], ra[i]);
+      }
+    } else {
+      hold_regs(ra);
+#pragma unroll
+      for (int i = 0; i < AV; ++i) {
+        const int v = threadIdx.x + kFatThreads * i;
+        const int r = v / F4R;
+        const int cv = v % F4R;
+        AS::store4(&As[buf][0][sw(r, cv * 4)], &As[buf][PL - 1][sw(r, cv * 4)], ra[i]);
+      }
     }
 #pragma unroll
     for (int i = 0; i < BV; ++i) st16(&Bs[buf][(threadIdx.x + kFatThreads * i) * VEC], rb[i]);
@@ -175,9 +217,9 @@ __attribute__((amdgpu_waves_per_eu(1, WN / 2))) void gemm_fat_kernel(const float
   };
   // slab kt: issue the loads of kt+2, multiply slab kt from LDS, stage the
   // registers of kt+1 into the other buffer, barrier
-  float4 a0[AV], a1[AV], a2[AV];
+  AReg a0[NA], a1[NA], a2[NA];
   V16 b0[BV], b1[BV], b2[BV];
-  auto step = [&](int kt, float4 (&an)[AV], V16 (&bn)[BV], float4 (&al)[AV], V16 (&bl)[BV]) {
+  auto step = [&](int kt, AReg (&an)[NA], V16 (&bn)[BV], AReg (&al)[NA], V16 (&bl)[BV]) {
     gload(al, bl, kt + 2);
     mma(kt & 1);
     sstore(an, bn, (kt + 1) & 1);
@@ -241,29 +283,31 @@ __attribute__((amdgpu_waves_per_eu(1, WN / 2))) void gemm_fat_kernel(const float
       }
 }
 
-template <bool VS, bool LO>
+template <bool VS, bool LO, bool AP = false>
 hipError_t fat_launch(DType t, int wn, int splits, const float* A, const void* W, float* out,
                       const int* m_dev, int m_cap, int N, int K, const VocabEpi& ve,
                       hipStream_t st) {
+  const size_t aps = AP ? (size_t)m_cap * K : 0;   // plane stride of planar activations
   const int bk = t == DType::F32 ? 16 * kFatKK<float> : 32 * kFatKK<bf16>;   // K per slab
   if ((wn != 2 && wn != 4) || splits < 1 || splits > K / bk) return hipErrorInvalidValue;
   const int n_tiles = (N + 64 * wn - 1) / (64 * wn), m_tiles = (m_cap + kFatM - 1) / kFatM;
   const dim3 grid = VS ? dim3((n_tiles + 7) / 8 * 8 * m_tiles, 1, 1)   // see the kernel
                        : dim3(n_tiles, m_tiles, splits);
   if (t == DType::F32) {
+    if constexpr (AP) return hipErrorInvalidValue;
     if (wn == 4)
       hipLaunchKernelGGL((gemm_fat_kernel<float, 4, VS, true>), grid, dim3(512), 0, st, A,
-                         static_cast<const float*>(W), out, m_dev, m_cap, N, K, ve);
+                         static_cast<const float*>(W), out, m_dev, m_cap, N, K, ve, aps);
     else
       hipLaunchKernelGGL((gemm_fat_kernel<float, 2, VS, true>), grid, dim3(256), 0, st, A,
-                         static_cast<const float*>(W), out, m_dev, m_cap, N, K, ve);
+                         static_cast<const float*>(W), out, m_dev, m_cap, N, K, ve, aps);
   } else {
     if (wn == 4)
-      hipLaunchKernelGGL((gemm_fat_kernel<bf16, 4, VS, LO>), grid, dim3(512), 0, st, A,
-                         static_cast<const bf16*>(W), out, m_dev, m_cap, N, K, ve);
+      hipLaunchKernelGGL((gemm_fat_kernel<bf16, 4, VS, LO, AP>), grid, dim3(512), 0, st, A,
+                         static_cast<const bf16*>(W), out, m_dev, m_cap, N, K, ve, aps);
     else
-      hipLaunchKernelGGL((gemm_fat_kernel<bf16, 2, VS, LO>), grid, dim3(256), 0, st, A,
-                         static_cast<const bf16*>(W), out, m_dev, m_cap, N, K, ve);
+      hipLaunchKernelGGL((gemm_fat_kernel<bf16, 2, VS, LO, AP>), grid, dim3(256), 0, st, A,
+                         static_cast<const bf16*>(W), out, m_dev, m_cap, N, K, ve, aps);
   }
   return hipGetLastError();
 }
@@ -272,10 +316,15 @@ hipError_t fat_launch(DType t, int wn, int splits, const float* A, const void* W
 
 hipError_t launch_gemm_fat(DType t, int wn, int splits, const float* A, const void* W,
                            float* out, const int* m_dev, int m_cap, int N, int K, hipStream_t st,
-                           bool lo) {
+                           bool lo, bool ap) {
+  if (ap && t != DType::BF16) return hipErrorInvalidValue;
   if (!lo && t == DType::BF16)
-    return fat_launch<false, false>(t, wn, splits, A, W, out, m_dev, m_cap, N, K, VocabEpi{}, st);
-  return fat_launch<false, true>(t, wn, splits, A, W, out, m_dev, m_cap, N, K, VocabEpi{}, st);
+    return ap ? fat_launch<false, false, true>(t, wn, splits, A, W, out, m_dev, m_cap, N, K,
+                                               VocabEpi{}, st)
+              : fat_launch<false, false>(t, wn, splits, A, W, out, m_dev, m_cap, N, K, VocabEpi{}, st);
+  return ap ? fat_launch<false, true, true>(t, wn, splits, A, W, out, m_dev, m_cap, N, K,
+                                            VocabEpi{}, st)
+            : fat_launch<false, true>(t, wn, splits, A, W, out, m_dev, m_cap, N, K, VocabEpi{}, st);
 }
 
 hipError_t launch_gemm_fat_lmhead(DType t, int wn, const float* A, const void* W,

@@ -18,15 +18,7 @@ template <typename TW, bool LO = true> struct ASplit;
 template <> struct ASplit<bf16, true> {
   static constexpr int PLANES = 2;
   __device__ __forceinline__ static void store4(bf16* hi, bf16* lo, const float4& x) {
-    const float v[4] = {x.x, x.y, x.z, x.w};
-    bf16x4 h, l;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      h[i] = static_cast<bf16>(v[i]);
-      l[i] = static_cast<bf16>(v[i] - static_cast<float>(h[i]));
-    }
-    *reinterpret_cast<bf16x4*>(hi) = h;
-    *reinterpret_cast<bf16x4*>(lo) = l;
+    store_hi_lo4(hi, lo, x);
   }
 };
 template <> struct ASplit<bf16, false> {

@@ -38,16 +38,21 @@ struct GemmPlan {
   int mtiles;    // skinny: row tiles of 16*mt rows per (column group, split); 1 or 2
   int grid;
   int lo;        // bf16 weights: 1 = activations as hi + lo bf16 halves, 0 = bf16 only
+  int ap;        // fat, bf16 weights: 1 = A given as bf16 hi and lo planes (below)
 };
 GemmPlan plan_gemm(DType t, int m_cap, int N, int K, int target_wgs);
-// A is fp32 (split into hi/lo bf16 halves in-kernel for bf16 weights).
+// A is fp32 (split into hi/lo bf16 halves in-kernel for bf16 weights), or
+// with p.ap the two planes of that split, written by its producer: hi
+// [m_cap][K] bf16 followed by lo [m_cap][K] (store_hi_lo4; the same bits the
+// kernel would make), so the fat kernel stages them without converting.
 hipError_t launch_gemm(const GemmPlan& p, DType t, const float* A, const void* W, float* out,
                        const int* m_dev, int m_cap, int N, int K, hipStream_t st);
 // The fat kernel alone (M > 128): wn = 2 or 4 column waves (128 x 64*wn
-// tiles), splits K slices (1 .. K/64 bf16, K/32 fp32) writing out[s][m][n].
+// tiles), splits K slices (1 .. K/64 bf16, K/32 fp32) writing out[s][m][n];
+// ap: A as bf16 planes (bf16 weights only).
 hipError_t launch_gemm_fat(DType t, int wn, int splits, const float* A, const void* W,
                            float* out, const int* m_dev, int m_cap, int N, int K, hipStream_t st,
-                           bool lo = true);
+                           bool lo = true, bool ap = false);
 // n_mats matrices W [N][K] row-major -> the packed block layout every GEMM
 // here reads (gemm_split.h: 16-row groups x one MFMA vector step per 1 KB
 // block, 256-row tiles stored k-step by k-step).  N % 16 == 0, K a multiple
@@ -69,14 +74,16 @@ hipError_t launch_embed(DType t, PassTable tb, int m_cap, const int* tokens, int
                         const float* smooth_p, const uint8_t* smooth_valid, int B, float* x,
                         hipStream_t st);
 // x[m] += sum_s P[s][m]; a[m] = rmsnorm(x[m]) * g   (S = 0: no partials)
+// aps > 0: a is written as bf16 hi and lo planes (hi [m][d], lo aps elements
+// after it; store_hi_lo4) for a GEMM that reads planes, instead of fp32.
 hipError_t launch_add_rmsnorm(DType t, const int* nrows, int m_cap, float* x, const float* P,
                               int S, size_t p_stride, const void* g, float eps, float* a, int d,
-                              hipStream_t st);
+                              hipStream_t st, size_t aps = 0);
 hipError_t launch_qkv_rope_scatter(DType t, PassTable tb, int m_cap, const float* P, int S,
                                    size_t p_stride, int d, int H, int hd, const float* rope_cs,
                                    float* q_out, void* kc, void* vt, int Lp, hipStream_t st);
 hipError_t launch_swiglu(const int* nrows, int m_cap, const float* P, int S, size_t p_stride,
-                         int F, float* act, hipStream_t st);
+                         int F, float* act, hipStream_t st, size_t aps = 0);   // aps: as above
 // block rows of the window -> x + sum_s P[s] -> rmsnorm * g -> out[r*B + j];
 // also gathers each block row's planting (row_plant_id / row_plant_bias).
 hipError_t launch_final_norm(DType t, PassTable tb, int batch, int B, const float* x,
@@ -94,11 +101,12 @@ struct AttnPlan {
 int attn_cache_len(int max_len);
 AttnPlan plan_attention(int batch, int max_rows_per_req, int max_keys, int H, int target_wgs);
 // p_lo (bf16 caches): probabilities into the P V MFMA as hi + lo bf16 halves
-// (default), or as bf16(p) alone.
+// (default), or as bf16(p) alone.  o_aps > 0: the output o [m][H*hd] is
+// written as bf16 hi and lo planes, o_aps elements apart (store_hi_lo4).
 hipError_t launch_attention(DType t, const AttnPlan& p, PassTable tb, int batch, int m_cap,
                             const float* q, const void* kc, const void* vt, int H, int hd,
                             int Lp, float* o_part, float* ml_part, float* o, hipStream_t st,
-                            bool p_lo = true);
+                            bool p_lo = true, size_t o_aps = 0);
 
 // ---- vocab statistics ---------------------------------------------------------
 struct VocabPlan {

@@ -121,12 +121,30 @@ __device__ __forceinline__ void store_norm(float4* orow, const float4 (&v)[NV], 
   }
 }
 
-// x[m] += sum_s P[s][m] (split order); a[m] = rmsnorm(x[m]) * g.  One row per
+// The same as bf16 hi and lo planes: hi [m][d] at a_hi, lo at a_hi + aps.
+template <typename T, int NV>
+__device__ __forceinline__ void store_norm_planes(bf16* a_hi, size_t aps, const float4 (&v)[NV],
+                                                  float inv, const T* __restrict__ g, int d4) {
+#pragma unroll
+  for (int e = 0; e < NV; ++e) {
+    const int i = threadIdx.x + e * kNormThreads;
+    if (i < d4) {
+      const T* gi = g + 4 * i;
+      store_hi_lo4(a_hi + 4 * i, a_hi + aps + 4 * i,
+                   make_float4(v[e].x * inv * to_f(gi[0]), v[e].y * inv * to_f(gi[1]),
+                               v[e].z * inv * to_f(gi[2]), v[e].w * inv * to_f(gi[3])));
+    }
+  }
+}
+
+// x[m] += sum_s P[s][m] (split order); a[m] = rmsnorm(x[m]) * g, fp32, or
+// (aps > 0) as bf16 hi and lo planes aps elements apart.  One row per
 // workgroup, NV = ceil(d / 4096) float4 per thread.
 template <typename T, int NV>
 __global__ __launch_bounds__(kNormThreads) void add_rmsnorm_kernel(
     const int* __restrict__ nrows, int m_cap, float* __restrict__ x, const float* __restrict__ P,
-    int S, size_t p_stride, const T* __restrict__ g, float eps, float* __restrict__ a, int d) {
+    int S, size_t p_stride, const T* __restrict__ g, float eps, float* __restrict__ a, int d,
+    size_t aps) {
   __shared__ float red[kNormThreads / 64];
   const int m = blockIdx.x;
   // the row count is read together with the row (every row below m_cap is
@@ -144,7 +162,10 @@ __global__ __launch_bounds__(kNormThreads) void add_rmsnorm_kernel(
   }
   const float tot = block_sum<kNormThreads / 64>(ss, red);
   const float inv = 1.f / sqrtf(tot / d + eps);
-  store_norm<T, NV>(reinterpret_cast<float4*>(a + (size_t)m * d), v, inv, g, d4);
+  if (aps)
+    store_norm_planes<T, NV>(reinterpret_cast<bf16*>(a) + (size_t)m * d, aps, v, inv, g, d4);
+  else
+    store_norm<T, NV>(reinterpret_cast<float4*>(a + (size_t)m * d), v, inv, g, d4);
 }
 
 // QKV: sum the split-K partials, rotate q and k (pair (j, j+hd/2) by the
@@ -244,7 +265,7 @@ template <int G>
 __global__ __launch_bounds__(kThreads) void swiglu_kernel(const int* __restrict__ nrows, int m_cap,
                                                           const float* __restrict__ P, int S,
                                                           size_t p_stride, int F,
-                                                          float* __restrict__ act) {
+                                                          float* __restrict__ act, size_t aps) {
   // rows up to m_cap are read (all readable) while the row count loads;
   // only the pass's rows are stored
   const int nr = *nrows;
@@ -260,10 +281,16 @@ __global__ __launch_bounds__(kThreads) void swiglu_kernel(const int* __restrict_
     const float* const pp[2] = {pr + f, pr + F + f};
     add_splits<2, G>(t, pp, p_stride, S);
     const float4 g = t[0], u = t[1];
-    if ((int)m < min(nr, m_cap))
-      *reinterpret_cast<float4*>(act + m * F + f) =
-          make_float4(g.x / (1.f + expf(-g.x)) * u.x, g.y / (1.f + expf(-g.y)) * u.y,
-                      g.z / (1.f + expf(-g.z)) * u.z, g.w / (1.f + expf(-g.w)) * u.w);
+    if ((int)m < min(nr, m_cap)) {
+      const float4 y = make_float4(g.x / (1.f + expf(-g.x)) * u.x, g.y / (1.f + expf(-g.y)) * u.y,
+                                   g.z / (1.f + expf(-g.z)) * u.z, g.w / (1.f + expf(-g.w)) * u.w);
+      if (aps) {
+        bf16* hi = reinterpret_cast<bf16*>(act) + m * F + f;
+        store_hi_lo4(hi, hi + aps, y);
+      } else {
+        *reinterpret_cast<float4*>(act + m * F + f) = y;
+      }
+    }
   }
 }
 
@@ -328,16 +355,16 @@ hipError_t launch_embed(DType t, PassTable tb, int m_cap, const int* tokens, int
 
 hipError_t launch_add_rmsnorm(DType t, const int* nrows, int m_cap, float* x, const float* P,
                               int S, size_t p_stride, const void* g, float eps, float* a, int d,
-                              hipStream_t st) {
+                              hipStream_t st, size_t aps) {
   if (d > 8 * kNormThreads || d % 4 != 0) return hipErrorInvalidValue;
   if (d <= 4 * kNormThreads) {
     DISPATCH_T(t, hipLaunchKernelGGL((add_rmsnorm_kernel<T, 1>), dim3(m_cap), dim3(kNormThreads),
                                      0, st, nrows, m_cap, x, P, S, p_stride,
-                                     static_cast<const T*>(g), eps, a, d));
+                                     static_cast<const T*>(g), eps, a, d, aps));
   } else {
     DISPATCH_T(t, hipLaunchKernelGGL((add_rmsnorm_kernel<T, 2>), dim3(m_cap), dim3(kNormThreads),
                                      0, st, nrows, m_cap, x, P, S, p_stride,
-                                     static_cast<const T*>(g), eps, a, d));
+                                     static_cast<const T*>(g), eps, a, d, aps));
   }
   return hipGetLastError();
 }
@@ -361,17 +388,17 @@ hipError_t launch_qkv_rope_scatter(DType t, PassTable tb, int m_cap, const float
 }
 
 hipError_t launch_swiglu(const int* nrows, int m_cap, const float* P, int S, size_t p_stride,
-                         int F, float* act, hipStream_t st) {
+                         int F, float* act, hipStream_t st, size_t aps) {
   if (F % 4 != 0) return hipErrorInvalidValue;
   size_t total = (size_t)m_cap * F / 4;
   int blocks = (int)((total + kThreads - 1) / kThreads);
   if (blocks > 8192) blocks = 8192;
   if (S <= 1)   // unsplit input (many-row passes): fewer registers, more waves
     hipLaunchKernelGGL(swiglu_kernel<1>, dim3(blocks), dim3(kThreads), 0, st, nrows, m_cap, P, S,
-                       p_stride, F, act);
+                       p_stride, F, act, aps);
   else
     hipLaunchKernelGGL(swiglu_kernel<8>, dim3(blocks), dim3(kThreads), 0, st, nrows, m_cap, P, S,
-                       p_stride, F, act);
+                       p_stride, F, act, aps);
   return hipGetLastError();
 }
 

@@ -405,6 +405,13 @@ dinfer_status run_pass(dinfer_ctx* c, bool step) {
   go.lo = !(hi_only & 2u);
   gg.lo = !(hi_only & 4u);
   gd.lo = !(hi_only & 8u);
+  // A dense bf16 model's many-row passes hand the projections their inputs
+  // as bf16 hi/lo planes, split once by the kernel that produces them (the
+  // norms, the attention, SwiGLU) instead of by every column tile of the fat
+  // projection; the planes take the fp32 buffer's bytes.  (An MoE layer's
+  // router and expert gathers read the fp32 rows.)
+  const bool planes = !L.moe && dt == DType::BF16 && gq.kind == 1;
+  gq.ap = go.ap = gg.ap = gd.ap = planes;
   const AttnPlan& ap = step ? L.a_step : L.a_ref;
   const int d = L.d;
   const int F = L.moe ? L.Fs : L.F;   // dense FFN, or the MoE layer's shared expert
@@ -418,6 +425,7 @@ dinfer_status run_pass(dinfer_ctx* c, bool step) {
   float* part = c->at<float>(L.off_part);
   const size_t stride_q = (size_t)m_cap * 3 * d, stride_d = (size_t)m_cap * d,
                stride_g = (size_t)m_cap * 2 * F;
+  const size_t aps_d = planes ? (size_t)m_cap * d : 0, aps_f = planes ? (size_t)m_cap * F : 0;
 
   if (step)
     HIP_TRY(launch_step_gate(c->batch, tab, tab + 1, const_cast<int*>(tb.req_nrows), tb.req_active,
@@ -428,7 +436,7 @@ dinfer_status run_pass(dinfer_ctx* c, bool step) {
   for (int l = 0; l < L.nl; ++l) {
     const bool last = l == L.nl - 1;
     HIP_TRY(launch_add_rmsnorm(dt, tb.nrows, m_cap, x, part, l == 0 ? 0 : x_splits, stride_d,
-                               c->attn_norm[l], c->m.rms_eps, a, d, st));
+                               c->attn_norm[l], c->m.rms_eps, a, d, st, aps_d));
     HIP_TRY(launch_gemm(gq, dt, a, c->wqkv[l], part, tb.nrows, m_cap, 3 * d, d, st));
     char* kvk = c->at<char>(L.off_kvk) + (size_t)l * L.kv_layer_elems * es;
     char* kvv = c->at<char>(L.off_kvv) + (size_t)l * L.kv_layer_elems * es;
@@ -437,13 +445,13 @@ dinfer_status run_pass(dinfer_ctx* c, bool step) {
     if (!step && last) break;   // a refresh needs only the caches
     HIP_TRY(launch_attention(dt, ap, tb, L.max_batch, m_cap, q, kvk, kvv, L.H, L.hd, L.Lp,
                              c->at<float>(L.off_ao), c->at<float>(L.off_aml), o, st,
-                             !(hi_only & 16u)));
+                             !(hi_only & 16u), aps_d));
     HIP_TRY(launch_gemm(go, dt, o, c->wo[l], part, tb.nrows, m_cap, d, d, st));
     HIP_TRY(launch_add_rmsnorm(dt, tb.nrows, m_cap, x, part, go.splits, stride_d, c->ffn_norm[l],
-                               c->m.rms_eps, a, d, st));
+                               c->m.rms_eps, a, d, st, aps_d));
     if (!L.moe) {
       HIP_TRY(launch_gemm(gg, dt, a, c->wgu[l], part, tb.nrows, m_cap, 2 * F, d, st));
-      HIP_TRY(launch_swiglu(tb.nrows, m_cap, part, gg.splits, stride_g, F, act, st));
+      HIP_TRY(launch_swiglu(tb.nrows, m_cap, part, gg.splits, stride_g, F, act, st, aps_f));
       HIP_TRY(launch_gemm(gd, dt, act, c->wd[l], part, tb.nrows, m_cap, d, F, st));
       continue;
     }

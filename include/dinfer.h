@@ -173,7 +173,11 @@ typedef struct {
   int32_t moe_experts;       /* E                                                */
   float* moe_logits;         /* [rows][E] router logits incl. the block's bias   */
   /* After a step: [rows][d] fp32 normalised FFN input of the last layer, rows
-   * in pass order (after a refresh it holds other intermediate values). */
+   * in pass order (after a refresh it holds other intermediate values).  For
+   * a dense bf16 model whose step row capacity m = max_batch * min(max_len,
+   * block_len + 2 * vicinity_w) exceeds 128 it holds the same values as two
+   * bf16 planes, hi = bf16(a) [m][d] then lo = bf16(a - hi) [m][d], the form
+   * its projections read. */
   float* ffn_in;
   int32_t kv_len;            /* cache positions per head row: max_len rounded up
                                 to a multiple of 64 (padding holds zeros)        */
