@@ -18,10 +18,12 @@ namespace {
 // 64 x 64 as 4 x 4 MFMA tiles; WN = 4: two waves per SIMD, used when the grid
 // still has a workgroup per CU, else WN = 2), K slabs of BK = 64 (bf16)
 // / 32 (fp32) elements double-buffered in LDS with the activations split into
-// hi/lo planes on the way in.  Activation rows in LDS are unpadded 128-byte
-// lines with an XOR swizzle of their 16-byte chunks; the weights keep their
-// packed 1 KB operand blocks, so both are read and written without bank
-// conflicts (LDS traffic, not MFMA, bounds this kernel).  Global loads run
+// hi/lo planes on the way in (or taking planes a producer already split).
+// Activation rows in LDS are unpadded 128-byte lines with an XOR swizzle of
+// their 16-byte chunks; the weights keep their packed 1 KB operand blocks,
+// so both are read and written without bank conflicts (measured: no bank
+// conflicts, matrix cores about 38% and LDS about 23% busy; the waves wait
+// mostly on their global loads, L2 hits for three in four).  Global loads run
 // two slabs ahead through three register sets (a three-times unrolled loop,
 // as in the skinny kernel), all unconditional: rows past M read row M-1 and
 // columns past N read the last 16-column group (their outputs are not
