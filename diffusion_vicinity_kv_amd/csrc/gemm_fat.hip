@@ -50,14 +50,22 @@ template <typename TW> constexpr int kFatKK = 2;
 // split would make).  Each 16-byte load is then one LDS chunk of a plane and
 // is stored unchanged -- no conversion in the slab loop, which every column
 // tile of a row tile would otherwise repeat.
-template <typename TW, int WN, bool VS, bool LO, bool AP = false>
+//
+// SG = true (gate|up projection of a SwiGLU FFN, one K split, WN = 4): the
+// workgroup's 256 columns are the gate columns f0..f0+127 (waves wn 0, 1)
+// and the up columns F+f0..F+f0+127 (waves 2, 3) of W [2F][K], f0 = 128 bx,
+// and its epilogue writes act = silu(gate) * up (the SwiGLU kernel's
+// arithmetic on the same fp32 sums) as bf16 hi/lo planes of [m_cap][F]
+// (lo plane aps_out elements after hi) instead of the [m_cap][2F] product:
+// the up waves hand their tiles to the gate waves through LDS.
+template <typename TW, int WN, bool VS, bool LO, bool AP = false, bool SG = false>
 __global__ __launch_bounds__(128 * WN)
 __attribute__((amdgpu_waves_per_eu(1, WN / 2))) void gemm_fat_kernel(const float* __restrict__ A,
                                                             const TW* __restrict__ W,
                                                             float* __restrict__ Cout,
                                                             const int* __restrict__ m_dev,
                                                             int m_cap, int N, int K, VocabEpi ve,
-                                                            size_t aps) {
+                                                            size_t aps, size_t aps_out) {
   constexpr int kFatN = 64 * WN, kFatThreads = 128 * WN;
   using MF = Mfma<TW>;
   using AS = ASplit<TW, LO>;
@@ -79,6 +87,7 @@ __attribute__((amdgpu_waves_per_eu(1, WN / 2))) void gemm_fat_kernel(const float
     return r * STR + ((((e / CH) ^ (r / RS)) & (NC - 1)) * CH) + e % CH;
   };
   static_assert(!AP || (sizeof(TW) == 2 && !VS), "activation planes: bf16 projections only");
+  static_assert(!SG || (sizeof(TW) == 2 && !VS && WN == 4), "SwiGLU epilogue: bf16, 256 columns");
   constexpr int F4R = BK / 4;                  // float4 of A per slab row
   constexpr int AV = kFatM * F4R / kFatThreads;     // float4 of A per thread per slab
   // AP: 16-byte chunks (CH elements) of one plane; PL planes of kFatM rows
@@ -162,7 +171,10 @@ __attribute__((amdgpu_waves_per_eu(1, WN / 2))) void gemm_fat_kernel(const float
 #pragma unroll
   for (int i = 0; i < BV; ++i) {
     const int v = threadIdx.x + kFatThreads * i;
-    const int grp = min(n0 / 16 + (v / 64) / KK, NG - 1);
+    // SG: groups 0..7 of the tile are gate groups 8 bx.., 8..15 up groups
+    const int j = (v / 64) / KK;
+    const int grp = SG ? (j < 8 ? 8 * bx + j : NG / 2 + 8 * bx + j - 8)
+                       : min(n0 / 16 + j, NG - 1);
     wrow[i] = W + packed_block(grp, (v / 64) % KK, KS, NG) * BE + (v % 64) * VEC;
     wstep[i] = (size_t)KK * packed_kstride(grp, NG) * BE;
   }
@@ -273,6 +285,43 @@ __attribute__((amdgpu_waves_per_eu(1, WN / 2))) void gemm_fat_kernel(const float
     Cout = ve.logits;
     if (Cout == nullptr) return;
   }
+  if constexpr (SG) {
+    // the up waves (wn 2, 3) park their 128 x 128 tile in LDS (free since
+    // the loop's last barrier); the gate waves pair each element with it
+    constexpr int LDU = 128 + 4;
+    static_assert((size_t)128 * LDU * sizeof(float) <= kAsBytes + kBsBytes, "up tile fits LDS");
+    float* ut = reinterpret_cast<float*>(smem);
+    if (wn >= 2) {
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            ut[(wm * 64 + mt * 16 + lg * 4 + i) * LDU + (wn - 2) * 64 + nt * 16 + lc] = acc[mt][nt][i];
+    }
+    __syncthreads();
+    if (wn >= 2) return;
+    const int F = N / 2;
+    bf16* hi = reinterpret_cast<bf16*>(Cout);
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = wm * 64 + mt * 16 + lg * 4 + i;
+          const int c = wn * 64 + nt * 16 + lc;
+          if (m0 + r >= M) continue;
+          const float g = acc[mt][nt][i], u = ut[r * LDU + c];
+          const float y = g / (1.f + expf(-g)) * u;
+          const bf16 h = static_cast<bf16>(y);
+          const size_t at = (size_t)(m0 + r) * F + 128 * bx + c;
+          hi[at] = h;
+          hi[at + aps_out] = static_cast<bf16>(y - static_cast<float>(h));
+        }
+    return;
+  }
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
@@ -285,11 +334,13 @@ __attribute__((amdgpu_waves_per_eu(1, WN / 2))) void gemm_fat_kernel(const float
       }
 }
 
-template <bool VS, bool LO, bool AP = false>
+template <bool VS, bool LO, bool AP = false, bool SG = false>
 hipError_t fat_launch(DType t, int wn, int splits, const float* A, const void* W, float* out,
                       const int* m_dev, int m_cap, int N, int K, const VocabEpi& ve,
                       hipStream_t st) {
   const size_t aps = AP ? (size_t)m_cap * K : 0;   // plane stride of planar activations
+  const size_t aps_out = SG ? (size_t)m_cap * (N / 2) : 0;   // ... of the SwiGLU output
+  if (SG && (wn != 4 || splits != 1 || N % 256 != 0 || t != DType::BF16)) return hipErrorInvalidValue;
   const int bk = t == DType::F32 ? 16 * kFatKK<float> : 32 * kFatKK<bf16>;   // K per slab
   if ((wn != 2 && wn != 4) || splits < 1 || splits > K / bk) return hipErrorInvalidValue;
   const int n_tiles = (N + 64 * wn - 1) / (64 * wn), m_tiles = (m_cap + kFatM - 1) / kFatM;
@@ -299,17 +350,17 @@ hipError_t fat_launch(DType t, int wn, int splits, const float* A, const void* W
     if constexpr (AP) return hipErrorInvalidValue;
     if (wn == 4)
       hipLaunchKernelGGL((gemm_fat_kernel<float, 4, VS, true>), grid, dim3(512), 0, st, A,
-                         static_cast<const float*>(W), out, m_dev, m_cap, N, K, ve, aps);
+                         static_cast<const float*>(W), out, m_dev, m_cap, N, K, ve, aps, aps_out);
     else
       hipLaunchKernelGGL((gemm_fat_kernel<float, 2, VS, true>), grid, dim3(256), 0, st, A,
-                         static_cast<const float*>(W), out, m_dev, m_cap, N, K, ve, aps);
+                         static_cast<const float*>(W), out, m_dev, m_cap, N, K, ve, aps, aps_out);
   } else {
     if (wn == 4)
-      hipLaunchKernelGGL((gemm_fat_kernel<bf16, 4, VS, LO, AP>), grid, dim3(512), 0, st, A,
-                         static_cast<const bf16*>(W), out, m_dev, m_cap, N, K, ve, aps);
-    else
+      hipLaunchKernelGGL((gemm_fat_kernel<bf16, 4, VS, LO, AP, SG>), grid, dim3(512), 0, st, A,
+                         static_cast<const bf16*>(W), out, m_dev, m_cap, N, K, ve, aps, aps_out);
+    else if constexpr (!SG)
       hipLaunchKernelGGL((gemm_fat_kernel<bf16, 2, VS, LO, AP>), grid, dim3(256), 0, st, A,
-                         static_cast<const bf16*>(W), out, m_dev, m_cap, N, K, ve, aps);
+                         static_cast<const bf16*>(W), out, m_dev, m_cap, N, K, ve, aps, aps_out);
   }
   return hipGetLastError();
 }
@@ -327,6 +378,16 @@ hipError_t launch_gemm_fat(DType t, int wn, int splits, const float* A, const vo
   return ap ? fat_launch<false, true, true>(t, wn, splits, A, W, out, m_dev, m_cap, N, K,
                                             VocabEpi{}, st)
             : fat_launch<false, true>(t, wn, splits, A, W, out, m_dev, m_cap, N, K, VocabEpi{}, st);
+}
+
+hipError_t launch_gemm_fat_swiglu(DType t, const float* A, const void* W, float* act,
+                                  const int* m_dev, int m_cap, int N, int K, hipStream_t st,
+                                  bool lo) {
+  if (t != DType::BF16) return hipErrorInvalidValue;
+  return lo ? fat_launch<false, true, true, true>(t, 4, 1, A, W, act, m_dev, m_cap, N, K,
+                                                  VocabEpi{}, st)
+            : fat_launch<false, false, true, true>(t, 4, 1, A, W, act, m_dev, m_cap, N, K,
+                                                   VocabEpi{}, st);
 }
 
 hipError_t launch_gemm_fat_lmhead(DType t, int wn, const float* A, const void* W,

@@ -53,6 +53,14 @@ hipError_t launch_gemm(const GemmPlan& p, DType t, const float* A, const void* W
 hipError_t launch_gemm_fat(DType t, int wn, int splits, const float* A, const void* W,
                            float* out, const int* m_dev, int m_cap, int N, int K, hipStream_t st,
                            bool lo = true, bool ap = false);
+// The fat gate|up projection of a SwiGLU FFN with SwiGLU in its epilogue
+// (bf16, one K split, 256-column tiles): A as bf16 hi/lo planes [m_cap][K],
+// W the packed [N = 2F][K] (gate rows, then up rows); writes act =
+// silu(gate) * up as bf16 hi/lo planes [m_cap][F] (lo m_cap * F elements
+// after hi), the form the down projection reads.  N % 256 == 0.
+hipError_t launch_gemm_fat_swiglu(DType t, const float* A, const void* W, float* act,
+                                  const int* m_dev, int m_cap, int N, int K, hipStream_t st,
+                                  bool lo = true);
 // n_mats matrices W [N][K] row-major -> the packed block layout every GEMM
 // here reads (gemm_split.h: 16-row groups x one MFMA vector step per 1 KB
 // block, 256-row tiles stored k-step by k-step).  N % 16 == 0, K a multiple

@@ -450,8 +450,14 @@ dinfer_status run_pass(dinfer_ctx* c, bool step) {
     HIP_TRY(launch_add_rmsnorm(dt, tb.nrows, m_cap, x, part, go.splits, stride_d, c->ffn_norm[l],
                                c->m.rms_eps, a, d, st, aps_d));
     if (!L.moe) {
-      HIP_TRY(launch_gemm(gg, dt, a, c->wgu[l], part, tb.nrows, m_cap, 2 * F, d, st));
-      HIP_TRY(launch_swiglu(tb.nrows, m_cap, part, gg.splits, stride_g, F, act, st, aps_f));
+      if (planes && gg.splits == 1 && gg.nw == 4 && (2 * F) % 256 == 0) {
+        // one K split: SwiGLU in the projection's epilogue, act as planes
+        HIP_TRY(launch_gemm_fat_swiglu(dt, a, c->wgu[l], act, tb.nrows, m_cap, 2 * F, d, st,
+                                       gg.lo != 0));
+      } else {
+        HIP_TRY(launch_gemm(gg, dt, a, c->wgu[l], part, tb.nrows, m_cap, 2 * F, d, st));
+        HIP_TRY(launch_swiglu(tb.nrows, m_cap, part, gg.splits, stride_g, F, act, st, aps_f));
+      }
       HIP_TRY(launch_gemm(gd, dt, act, c->wd[l], part, tb.nrows, m_cap, d, F, st));
       continue;
     }
