@@ -68,3 +68,33 @@ def test_committed_traffic_record_matches_the_sources():
     assert rec["source_hash"] == bench.source_hash()
     assert rec["bytes_per_launch"] > 0
     assert os.path.basename(bench.TRAFFIC_FILE) == "gemm_skinny_qkv_gateup_dense8b_traffic.json"
+
+
+def test_committed_bench_line_keeps_the_output_contract():
+    """The kept bench line carries every field of the one-line contract, its
+    roofline fraction is achieved / peak, and its CPU baseline is the
+    oracle's."""
+    here = os.path.dirname(os.path.abspath(__file__))
+    path = os.path.join(here, "..", "profiles", "dense8b_b1_bench_line.json")
+    line = json.load(open(path))
+    for k in ("metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step",
+              "higher_is_better", "scaling", "vs_baseline", "dtype", "data", "config",
+              "roofline", "cpu_baseline"):
+        assert k in line, k
+    assert line["n_gpus"] == 1 and line["higher_is_better"] is True
+    assert line["config"]["workload"] == "dense8b_b1"
+    r = line["roofline"]
+    assert r["bound"] in ("hbm", "mfma", "alu") and r["unit"] in ("GB/s", "TFLOP/s")
+    assert abs(r["frac"] - r["achieved"] / r["peak"]) < 1e-3
+    c = line["cpu_baseline"]
+    assert c["kind"] == "oracle" and c["cores"] >= 1 and c["value"] > 0 and c["sample"]
+
+
+def test_more_than_one_gpu_is_refused_with_a_message():
+    import subprocess
+    import sys
+    here = os.path.dirname(os.path.abspath(__file__))
+    r = subprocess.run([sys.executable, os.path.join(here, "..", "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode != 0
+    assert "one GPU" in r.stderr + r.stdout
