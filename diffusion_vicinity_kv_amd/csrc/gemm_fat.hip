@@ -21,9 +21,10 @@ namespace {
 // hi/lo planes on the way in (or taking planes a producer already split).
 // Activation rows in LDS are unpadded 128-byte lines with an XOR swizzle of
 // their 16-byte chunks; the weights keep their packed 1 KB operand blocks,
-// so both are read and written without bank conflicts (measured: no bank
-// conflicts, matrix cores about 38% and LDS about 23% busy; the waves wait
-// mostly on their global loads, L2 hits for three in four).  Global loads run
+// so both are read and written without bank conflicts (measured: matrix
+// cores about 38% busy; a slab takes about twice its MFMA time, spent on the
+// LDS fragment reads, the staging, the barrier and waits on global loads,
+// which hit L2 three times in four).  Global loads run
 // two slabs ahead through three register sets (a three-times unrolled loop,
 // as in the skinny kernel), all unconditional: rows past M read row M-1 and
 // columns past N read the last 16-column group (their outputs are not
