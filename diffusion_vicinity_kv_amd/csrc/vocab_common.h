@@ -19,17 +19,70 @@ __device__ __forceinline__ bool better(float va, int ia, float vb, int ib) {
   return va > vb || (va == vb && ia < ib);
 }
 
-// Wave-wide best (value, id) pair.
-__device__ __forceinline__ void wave_best(float& v, int& id) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const float ov = __shfl_xor(v, o, 64);
-    const int oi = __shfl_xor(id, o, 64);
+// One exchange of a wave-wide reduction: each lane takes the better of its
+// own pair and the partner's.  Within a row of 16 lanes the partner comes
+// from a DPP rotation of the row (row_ror:n, control 0x120 + n); across rows
+// from the gfx950 row swaps (v_permlane16_swap: odd rows of the first
+// operand with even rows of the second; v_permlane32_swap: the upper half of
+// the first with the lower half of the second), which with both operands the
+// same value give each lane its partner row's value in one of the two
+// results.  All of these are vector-ALU moves (no LDS round trip as
+// ds_bpermute takes).  The order is a total order, so any reduction tree
+// gives the same pair.
+template <int CTRL>
+__device__ __forceinline__ void best_rot(float& v, int& id) {
+  const float ov =
+      __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL,
+                                                             0xf, 0xf, false));
+  const int oi = __builtin_amdgcn_update_dpp(0, id, CTRL, 0xf, 0xf, false);
+  if (better(ov, oi, v, id)) {
+    v = ov;
+    id = oi;
+  }
+}
+template <bool HALF>   // false: partner row (lane ^ 16); true: partner half (lane ^ 32)
+__device__ __forceinline__ void best_swap(float& v, int& id) {
+  const unsigned vb = __builtin_bit_cast(unsigned, v), ib = (unsigned)id;
+  const int lane = threadIdx.x & 63;
+  if constexpr (HALF) {
+    const auto sv = __builtin_amdgcn_permlane32_swap(vb, vb, false, false);
+    const auto si = __builtin_amdgcn_permlane32_swap(ib, ib, false, false);
+    const bool lo = lane < 32;
+    const float ov = __builtin_bit_cast(float, lo ? sv[1] : sv[0]);
+    const int oi = (int)(lo ? si[1] : si[0]);
+    if (better(ov, oi, v, id)) {
+      v = ov;
+      id = oi;
+    }
+  } else {
+    const auto sv = __builtin_amdgcn_permlane16_swap(vb, vb, false, false);
+    const auto si = __builtin_amdgcn_permlane16_swap(ib, ib, false, false);
+    const bool even = ((lane >> 4) & 1) == 0;
+    const float ov = __builtin_bit_cast(float, even ? sv[1] : sv[0]);
+    const int oi = (int)(even ? si[1] : si[0]);
     if (better(ov, oi, v, id)) {
       v = ov;
       id = oi;
     }
   }
+}
+
+// Wave-wide best (value, id) pair: rotations by 8, 4, 2, 1 within each row
+// give every lane its row's best, the two swaps combine the rows.
+__device__ __forceinline__ void wave_best(float& v, int& id) {
+  best_rot<0x128>(v, id);
+  best_rot<0x124>(v, id);
+  best_rot<0x122>(v, id);
+  best_rot<0x121>(v, id);
+  best_swap<false>(v, id);
+  best_swap<true>(v, id);
+}
+
+// Wave-wide maximum the same way (exact: max is order-free).
+__device__ __forceinline__ float wave_max_rot(float v) {
+  int id = 0;
+  wave_best(v, id);
+  return v;
 }
 
 // Extract the wave's top-8 from per-lane sorted lists (pop-front on the
@@ -123,7 +176,7 @@ __device__ __forceinline__ void tile_records(const float* z, int ldz, int nrows,
       m = fmaxf(m, x);
       insert_top8(tv, ti, x, id);      // ids increase with j: ties keep the lower id
     }
-    const float wm = wave_max(m);
+    const float wm = wave_max_rot(m);
     float s = 0.f;
     if (wm != -INFINITY) {
 #pragma unroll
