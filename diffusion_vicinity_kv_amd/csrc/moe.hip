@@ -13,6 +13,7 @@
 //            gate * expert output (slot order)
 #include "common.h"
 #include "kernels.h"
+#include "vocab_common.h"
 
 #include <climits>
 
@@ -96,7 +97,7 @@ __global__ __launch_bounds__(64 * kRouteWaves) void moe_route_kernel(PassTable t
       v += router_bias[(((size_t)r * n_layers + layer) * n_blocks + tb.req_blk[r]) * E + lane];
     rlog[(size_t)m * E + lane] = v;
   }
-  const float mx = wave_max(v);
+  const float mx = vocab::wave_max_rot(v);
   // top_k by (value desc, id asc); the selected lanes drop out one by one
   float cand = v;
   int chosen_id[kMaxTopK];
@@ -106,15 +107,7 @@ __global__ __launch_bounds__(64 * kRouteWaves) void moe_route_kernel(PassTable t
     if (k >= top_k) break;
     float bv = cand;
     int bi = lane < E ? lane : INT_MAX;
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      const float ov = __shfl_xor(bv, o, 64);
-      const int oi = __shfl_xor(bi, o, 64);
-      if (ov > bv || (ov == bv && oi < bi)) {
-        bv = ov;
-        bi = oi;
-      }
-    }
+    vocab::wave_best(bv, bi);                  // the whole wave takes part
     chosen_id[k] = bi;
     chosen_v[k] = bv;
     if (lane == bi) cand = -INFINITY;

@@ -1,7 +1,8 @@
 // Device helpers of the vocab statistics shared by the standalone vocab pass
 // (vocab.hip) and the LM-head epilogue of the projection kernels: the order
 // every top-k here uses (larger value first, then smaller id), wave64 best
-// and top-8 extraction, and sorted insertion into a per-thread top-8.
+// and top-8 extraction, and sorted insertion into a per-thread top-8.  The
+// MoE router's top-k takes the same wave64 best (the same order).
 #pragma once
 
 #include <climits>
