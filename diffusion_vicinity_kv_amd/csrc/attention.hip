@@ -128,31 +128,46 @@ __global__ __launch_bounds__(256 * kKeyGroups) void attn_kernel(
   const int n_local = (n_steps + KG - 1) / KG; // steps per group (the last may be empty)
 
   // query fragments (B operand of S^T): query lc of each tile, hd g*VEC..
+  // The raw rows are loaded here, unconditionally (a query past the block
+  // reads the request's first row, zeroed below), and split only after the
+  // first K/V loads are issued: the three reads share one memory round trip
+  // (a conditional load here put each in a branch of its own, with a full
+  // wait at a join, before any K/V load left).
   V16 qf[QTW][QV][PL];
   int qrow[QTW];
   bool qvalid[QTW];
+  float4 qraw[QTW][QV][VEC / 4];
 #pragma unroll
   for (int u = 0; u < QTW; ++u) {
     const int qloc = qb * QB + (wave * QTW + u) * 16 + lc;
     qvalid[u] = qloc < nq;
     qrow[u] = row_off + (qvalid[u] ? qloc : 0);
 #pragma unroll
-    for (int kk = 0; kk < QV; ++kk) {
-      float qv[VEC];
+    for (int kk = 0; kk < QV; ++kk)
 #pragma unroll
-      for (int e = 0; e < VEC; e += 4) {
-        const float4 x = qvalid[u] ? *reinterpret_cast<const float4*>(
-                                         q + (size_t)qrow[u] * d + h * HD + kk * KS + lg * VEC + e)
-                                   : make_float4(0.f, 0.f, 0.f, 0.f);
-        // scaled into the log2 domain here, once, instead of every score
-        qv[e] = x.x * scale_log2;
-        qv[e + 1] = x.y * scale_log2;
-        qv[e + 2] = x.z * scale_log2;
-        qv[e + 3] = x.w * scale_log2;
-      }
-      SO::make(qv, qf[u][kk]);
-    }
+      for (int e = 0; e < VEC; e += 4)
+        qraw[u][kk][e / 4] = *reinterpret_cast<const float4*>(
+            q + (size_t)qrow[u] * d + h * HD + kk * KS + lg * VEC + e);
   }
+  auto split_queries = [&]() {
+#pragma unroll
+    for (int u = 0; u < QTW; ++u)
+#pragma unroll
+      for (int kk = 0; kk < QV; ++kk) {
+        // scaled into the log2 domain here, once, instead of every score
+        const float sc = qvalid[u] ? scale_log2 : 0.f;
+        float qv[VEC];
+#pragma unroll
+        for (int e = 0; e < VEC; e += 4) {
+          const float4 x = qraw[u][kk][e / 4];
+          qv[e] = x.x * sc;
+          qv[e + 1] = x.y * sc;
+          qv[e + 2] = x.z * sc;
+          qv[e + 3] = x.w * sc;
+        }
+        SO::make(qv, qf[u][kk]);
+      }
+  };
 
   floatx4 o[QTW][HT];
   float m_run[QTW], l_run[QTW];
@@ -292,6 +307,7 @@ __global__ __launch_bounds__(256 * kKeyGroups) void attn_kernel(
   };
   load(r0, 0);
   load(r1, 1);
+  split_queries();
   store(r0, 0);
   __syncthreads();
   // whole groups of three steps unconditionally, the rest after the loop
